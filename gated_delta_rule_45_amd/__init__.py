@@ -1,0 +1,25 @@
+"""MI355X-native Kimi Delta Attention (KDA): Python binding of the C ABI.
+
+The computation lives in hand-written HIP kernels for gfx950 behind the C ABI
+declared in ``include/kda.h`` (library ``libkda.so`` in this directory). This
+package only marshals torch tensors into that ABI.
+"""
+from ._binding import (  # noqa: F401
+    KdaError,
+    kda_chunk_prefill,
+    kda_chunk_prefill_workspace_size,
+    kda_decode_packed,
+    kda_mixed_batch,
+    kda_mixed_batch_workspace_size,
+    lib,
+)
+
+__all__ = [
+    "KdaError",
+    "kda_chunk_prefill",
+    "kda_chunk_prefill_workspace_size",
+    "kda_decode_packed",
+    "kda_mixed_batch",
+    "kda_mixed_batch_workspace_size",
+    "lib",
+]

@@ -1,0 +1,286 @@
+"""Python binding of the KDA C ABI (``libkda.so``): argument marshalling only.
+
+Every step of the computation runs in the HIP kernels behind the C ABI. This
+module turns torch tensors into device pointers, strides and sizes, passes the
+caller's current HIP stream, and turns a non-zero status into an exception
+that lists every failed check. There is no fallback: if the library is not
+built, or the tensors are not on a GPU, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkda.so")
+
+KDA_OK = 0
+STATUS_NAMES = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARGUMENT", 2: "KDA_ERR_UNSUPPORTED",
+                3: "KDA_ERR_WORKSPACE", 4: "KDA_ERR_HIP"}
+
+
+class KdaGate(ctypes.Structure):
+    _fields_ = [("A_log", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p),
+                ("has_lower_bound", ctypes.c_int32), ("lower_bound", ctypes.c_float),
+                ("scale", ctypes.c_float)]
+
+
+class KdaState(ctypes.Structure):
+    _fields_ = [("pool", ctypes.c_void_p), ("slot_stride", ctypes.c_int64),
+                ("num_slots", ctypes.c_int64), ("indices", ctypes.c_void_p),
+                ("index_stride", ctypes.c_int64)]
+
+
+class KdaError(ValueError):
+    """A call was rejected. ``status`` is the C status code, ``reasons`` the
+    list of every failed check."""
+
+    def __init__(self, status: int, reasons: list[str]):
+        self.status = status
+        self.reasons = reasons
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: " + "; ".join(reasons))
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Loads libkda.so from the package directory (built by ``build()``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"KDA HIP library not built: {LIB_PATH} is missing "
+                               "(run gated_delta_rule_45_amd.build.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        i32, i64, vp, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+        gp, spn = ctypes.POINTER(KdaGate), ctypes.POINTER(KdaState)
+        L.kda_decode_packed.argtypes = [i32, i32, i32, i32, i32, vp, i64, vp, vp, gp, spn, vp, vp]
+        L.kda_decode_packed.restype = i32
+        L.kda_chunk_prefill_workspace_size.argtypes = [i32, i64, i32, i32, i32]
+        L.kda_chunk_prefill_workspace_size.restype = sz
+        L.kda_chunk_prefill.argtypes = [i32, i64, vp, vp, i32, i32, i32, vp, i64, vp, vp, gp, spn,
+                                        vp, vp, sz, vp]
+        L.kda_chunk_prefill.restype = i32
+        L.kda_mixed_batch_workspace_size.argtypes = [i32, i32, i64, i32, i32, i32]
+        L.kda_mixed_batch_workspace_size.restype = sz
+        L.kda_mixed_batch.argtypes = [i32, i32, i64, vp, vp, i32, i32, i32, vp, i64, vp, vp, gp,
+                                      spn, vp, vp, sz, vp]
+        L.kda_mixed_batch.restype = i32
+        L.kda_status_string.argtypes = [i32]
+        L.kda_status_string.restype = ctypes.c_char_p
+        L.kda_last_error.argtypes = []
+        L.kda_last_error.restype = ctypes.c_char_p
+        L.kda_version.argtypes = []
+        L.kda_version.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _raise_if(status: int) -> None:
+    if status != KDA_OK:
+        detail = lib().kda_last_error().decode()
+        raise KdaError(status, [r for r in detail.split("; ") if r] or [STATUS_NAMES.get(status, "")])
+
+
+# ------------------------------------------------------------ marshalling
+
+class _Marshal:
+    """Collects every marshalling problem before raising once."""
+
+    def __init__(self):
+        self.reasons: list[str] = []
+        self.device = None
+
+    def tensor(self, name, t, dtype, ndim=None, optional=False):
+        if t is None:
+            if not optional:
+                self.reasons.append(f"{name} is required")
+            return
+        if not isinstance(t, torch.Tensor):
+            self.reasons.append(f"{name} must be a torch.Tensor")
+            return
+        if not t.is_cuda:
+            self.reasons.append(f"{name} must be on a GPU (got {t.device})")
+        elif self.device is None:
+            self.device = t.device
+        elif t.device != self.device:
+            self.reasons.append(f"{name} is on {t.device}, expected {self.device}")
+        if t.dtype != dtype:
+            self.reasons.append(f"{name} must be {dtype} (got {t.dtype})")
+        if ndim is not None and t.dim() != ndim:
+            self.reasons.append(f"{name} must be {ndim}-D (got {t.dim()}-D)")
+
+    def check(self, ok, msg):
+        if not ok:
+            self.reasons.append(msg)
+
+    def raise_if_any(self):
+        if self.reasons:
+            raise KdaError(1, self.reasons)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _common(m: _Marshal, mixed_qkv, raw_g, raw_beta, A_log, dt_bias, initial_state, state_indices):
+    m.tensor("mixed_qkv", mixed_qkv, torch.bfloat16, 2)
+    m.tensor("raw_g", raw_g, torch.bfloat16, 2)
+    m.tensor("raw_beta", raw_beta, torch.bfloat16, 2)
+    m.tensor("A_log", A_log, torch.float32, 1)
+    m.tensor("dt_bias", dt_bias, torch.float32, 1)
+    m.tensor("initial_state", initial_state, torch.float32, 4)
+    m.tensor("state_indices", state_indices, torch.int32, 1)
+    if m.reasons:
+        m.raise_if_any()
+    slots, H, K, V = initial_state.shape
+    st = initial_state.stride()
+    m.check(st[1:] == (K * V, V, 1), "initial_state must be contiguous within a slot ([H][K][V])")
+    m.check(mixed_qkv.stride(1) == 1, "mixed_qkv rows must be unit-stride")
+    m.check(raw_g.is_contiguous(), "raw_g must be contiguous")
+    m.check(raw_beta.is_contiguous(), "raw_beta must be contiguous")
+    m.check(A_log.is_contiguous() and dt_bias.is_contiguous(), "A_log and dt_bias must be contiguous")
+    m.check(raw_g.shape[1] == H * K, f"raw_g must have H*K = {H * K} columns")
+    m.check(raw_beta.shape[1] == H, f"raw_beta must have H = {H} columns")
+    m.check(A_log.shape[0] == H, f"A_log must have H = {H} entries")
+    m.check(dt_bias.shape[0] == H * K, f"dt_bias must have H*K = {H * K} entries")
+    m.check(raw_g.shape[0] == mixed_qkv.shape[0] and raw_beta.shape[0] == mixed_qkv.shape[0],
+            "mixed_qkv, raw_g and raw_beta must have the same number of rows")
+    m.raise_if_any()
+    return H, K, V
+
+
+def _gate(A_log, dt_bias, lower_bound, scale) -> KdaGate:
+    has = lower_bound is not None
+    return KdaGate(A_log=A_log.data_ptr(), dt_bias=dt_bias.data_ptr(), has_lower_bound=int(has),
+                   lower_bound=float(lower_bound) if has else 0.0, scale=float(scale))
+
+
+def _state(initial_state, state_indices) -> KdaState:
+    return KdaState(pool=initial_state.data_ptr(), slot_stride=initial_state.stride(0),
+                    num_slots=initial_state.shape[0], indices=state_indices.data_ptr(),
+                    index_stride=state_indices.stride(0))
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _out(out, rows, H, V, device, m: _Marshal):
+    if out is None:
+        return torch.empty(rows, H, V, dtype=torch.bfloat16, device=device)
+    m.tensor("out", out, torch.bfloat16, 3)
+    m.check(tuple(out.shape) == (rows, H, V) and out.is_contiguous(),
+            f"out must be a contiguous [{rows}, {H}, {V}] tensor")
+    m.raise_if_any()
+    return out
+
+
+# ----------------------------------------------------------------- entries
+
+def kda_decode_packed(mixed_qkv, raw_g, raw_beta, A_log, dt_bias, lower_bound, initial_state,
+                      state_indices, *, tokens_per_seq: int = 1, scale: float = 1.0, out=None):
+    """Packed decode / spec-verify. ``initial_state`` (fp32 [slots, H, K, V])
+    is updated in place; ``state_indices`` is a 1-D int32 view, possibly
+    strided, with one entry per request. Returns ``(out, initial_state)``."""
+    m = _Marshal()
+    H, K, V = _common(m, mixed_qkv, raw_g, raw_beta, A_log, dt_bias, initial_state, state_indices)
+    num_seqs = state_indices.shape[0]
+    rows = num_seqs * int(tokens_per_seq)
+    m.check(mixed_qkv.shape[0] == rows,
+            f"mixed_qkv has {mixed_qkv.shape[0]} rows, expected num_seqs*tokens_per_seq = {rows}")
+    m.raise_if_any()
+    out = _out(out, rows, H, V, mixed_qkv.device, m)
+    g, s = _gate(A_log, dt_bias, lower_bound, scale), _state(initial_state, state_indices)
+    st = lib().kda_decode_packed(num_seqs, int(tokens_per_seq), H, K, V, _ptr(mixed_qkv),
+                                 mixed_qkv.stride(0), _ptr(raw_g), _ptr(raw_beta),
+                                 ctypes.byref(g), ctypes.byref(s), _ptr(out),
+                                 _stream(mixed_qkv.device))
+    _raise_if(st)
+    return out, initial_state
+
+
+def kda_chunk_prefill_workspace_size(num_seqs: int, num_tokens: int, H: int, K: int, V: int) -> int:
+    return int(lib().kda_chunk_prefill_workspace_size(num_seqs, num_tokens, H, K, V))
+
+
+def kda_mixed_batch_workspace_size(num_decodes: int, num_prefills: int, num_prefill_tokens: int,
+                                   H: int, K: int, V: int) -> int:
+    return int(lib().kda_mixed_batch_workspace_size(num_decodes, num_prefills, num_prefill_tokens,
+                                                    H, K, V))
+
+
+def _workspace(workspace, need, device, m: _Marshal):
+    if workspace is None:
+        return torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    m.tensor("workspace", workspace, torch.uint8, 1)
+    m.raise_if_any()
+    return workspace
+
+
+def kda_chunk_prefill(mixed_qkv, raw_g, raw_beta, A_log, dt_bias, lower_bound, initial_state,
+                      state_indices, cu_seqlens, *, has_initial_state=None, scale: float = 1.0,
+                      out=None, workspace=None):
+    """Varlen chunked prefill (chunk 64). ``cu_seqlens`` is device int32
+    [num_seqs+1]; the token count is taken from ``mixed_qkv.shape[0]`` (the
+    host never reads ``cu_seqlens``). Without ``workspace`` a scratch tensor of
+    the required size is allocated with torch. Returns ``(out, initial_state)``."""
+    m = _Marshal()
+    H, K, V = _common(m, mixed_qkv, raw_g, raw_beta, A_log, dt_bias, initial_state, state_indices)
+    m.tensor("cu_seqlens", cu_seqlens, torch.int32, 1)
+    m.tensor("has_initial_state", has_initial_state, torch.uint8, 1, optional=True)
+    m.raise_if_any()
+    num_seqs = cu_seqlens.shape[0] - 1
+    num_tokens = mixed_qkv.shape[0]
+    m.check(cu_seqlens.is_contiguous(), "cu_seqlens must be contiguous")
+    m.check(state_indices.shape[0] == num_seqs, "state_indices needs one entry per sequence")
+    if has_initial_state is not None:
+        m.check(has_initial_state.shape[0] == num_seqs and has_initial_state.is_contiguous(),
+                "has_initial_state must be contiguous with one entry per sequence")
+    m.raise_if_any()
+    out = _out(out, num_tokens, H, V, mixed_qkv.device, m)
+    need = kda_chunk_prefill_workspace_size(max(num_seqs, 0), num_tokens, H, K, V)
+    ws = _workspace(workspace, need, mixed_qkv.device, m)
+    g, s = _gate(A_log, dt_bias, lower_bound, scale), _state(initial_state, state_indices)
+    st = lib().kda_chunk_prefill(num_seqs, num_tokens, _ptr(cu_seqlens), _ptr(has_initial_state),
+                                 H, K, V, _ptr(mixed_qkv), mixed_qkv.stride(0), _ptr(raw_g),
+                                 _ptr(raw_beta), ctypes.byref(g), ctypes.byref(s), _ptr(out),
+                                 _ptr(ws), ws.numel(), _stream(mixed_qkv.device))
+    _raise_if(st)
+    return out, initial_state
+
+
+def kda_mixed_batch(mixed_qkv, raw_g, raw_beta, A_log, dt_bias, lower_bound, initial_state,
+                    state_indices, num_decodes: int, prefill_cu_seqlens, *, has_initial_state=None,
+                    scale: float = 1.0, out=None, workspace=None):
+    """Mixed batch: rows [0, num_decodes) are single-token decodes (recurrent
+    kernel), the rest are prefill sequences given by ``prefill_cu_seqlens``
+    (relative to ``num_decodes``; chunk pipeline). ``state_indices`` has the
+    decodes' entries first, then the prefills'. Returns ``(out, initial_state)``."""
+    m = _Marshal()
+    H, K, V = _common(m, mixed_qkv, raw_g, raw_beta, A_log, dt_bias, initial_state, state_indices)
+    m.tensor("prefill_cu_seqlens", prefill_cu_seqlens, torch.int32, 1)
+    m.tensor("has_initial_state", has_initial_state, torch.uint8, 1, optional=True)
+    m.raise_if_any()
+    num_prefills = prefill_cu_seqlens.shape[0] - 1
+    rows = mixed_qkv.shape[0]
+    num_prefill_tokens = rows - int(num_decodes)
+    m.check(prefill_cu_seqlens.is_contiguous(), "prefill_cu_seqlens must be contiguous")
+    m.check(num_prefill_tokens >= 0, "num_decodes exceeds the number of rows")
+    m.check(state_indices.shape[0] == int(num_decodes) + num_prefills,
+            "state_indices needs one entry per decode and per prefill sequence")
+    m.raise_if_any()
+    out = _out(out, rows, H, V, mixed_qkv.device, m)
+    need = kda_mixed_batch_workspace_size(int(num_decodes), max(num_prefills, 0),
+                                          num_prefill_tokens, H, K, V)
+    ws = _workspace(workspace, need, mixed_qkv.device, m)
+    g, s = _gate(A_log, dt_bias, lower_bound, scale), _state(initial_state, state_indices)
+    st = lib().kda_mixed_batch(int(num_decodes), num_prefills, num_prefill_tokens,
+                               _ptr(prefill_cu_seqlens), _ptr(has_initial_state), H, K, V,
+                               _ptr(mixed_qkv), mixed_qkv.stride(0), _ptr(raw_g), _ptr(raw_beta),
+                               ctypes.byref(g), ctypes.byref(s), _ptr(out), _ptr(ws), ws.numel(),
+                               _stream(mixed_qkv.device))
+    _raise_if(st)
+    return out, initial_state

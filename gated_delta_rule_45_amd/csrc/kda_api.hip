@@ -1,0 +1,287 @@
+// kda_api.hip -- C-ABI front end: argument validation, launch planning and the
+// mixed-batch router. Every entry point validates everything on the host
+// first, launches nothing when any check fails, and reports every failed
+// check at once (the all-reasons error convention of vLLM PR #60683, Refusal
+// and steps). No entry point allocates, frees, synchronises or reads device
+// memory from the host.
+#include <cmath>
+#include <cstdio>
+#include <string>
+
+#include "kda.h"
+#include "kda_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+class Checks {
+ public:
+  void require(bool ok, kda_status_t code, const std::string& msg) {
+    if (ok) return;
+    if (!msg_.empty()) msg_ += "; ";
+    msg_ += msg;
+    // The most specific code wins: invalid argument over the others.
+    if (status_ == KDA_OK || code == KDA_ERR_INVALID_ARGUMENT) status_ = code;
+  }
+  kda_status_t finish() {
+    g_last_error = msg_;
+    return status_;
+  }
+  bool ok() const { return status_ == KDA_OK; }
+
+ private:
+  kda_status_t status_ = KDA_OK;
+  std::string msg_;
+};
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Checks shared by all entry points. rows: number of token rows the call reads.
+void check_common(Checks& c, int64_t rows, int32_t H, int32_t K, int32_t V,
+                  const void* mixed_qkv, int64_t qkv_row_stride, const void* raw_g,
+                  const void* raw_beta, const kda_gate_t* gate, const kda_state_t* state,
+                  const void* out) {
+  const auto INV = KDA_ERR_INVALID_ARGUMENT;
+  const auto UNS = KDA_ERR_UNSUPPORTED;
+  c.require(H >= 1, INV, "H must be >= 1");
+  c.require(K >= 1 && V >= 1, INV, "K and V must be >= 1");
+  c.require(K == 64 || K == 128 || K < 1, UNS, "K must be 64 or 128");
+  c.require(V == 64 || V == 128 || V < 1, UNS, "V must be 64 or 128");
+  c.require(gate != nullptr, INV, "gate must not be NULL");
+  c.require(state != nullptr, INV, "state must not be NULL");
+  if (gate) {
+    c.require(gate->A_log != nullptr, INV, "gate->A_log must not be NULL");
+    c.require(gate->dt_bias != nullptr, INV, "gate->dt_bias must not be NULL");
+    c.require(std::isfinite(gate->scale), INV, "gate->scale must be finite");
+    if (gate->has_lower_bound)
+      c.require(std::isfinite(gate->lower_bound) && gate->lower_bound <= 0.0f, INV,
+                "gate->lower_bound must be finite and <= 0");
+  }
+  if (state) {
+    c.require(state->index_stride >= 1, INV,
+              "state->index_stride must be >= 1 (a non-positive stride is rejected)");
+    c.require(state->indices != nullptr, INV, "state->indices must not be NULL");
+    c.require(state->pool != nullptr, INV, "state->pool must not be NULL");
+    c.require(state->num_slots >= 1, INV, "state->num_slots must be >= 1");
+    if (H >= 1 && K >= 1 && V >= 1)
+      c.require(state->slot_stride >= static_cast<int64_t>(H) * K * V, INV,
+                "state->slot_stride must be >= H*K*V");
+    c.require(aligned(state->pool, 16), UNS, "state->pool must be 16-byte aligned");
+    c.require(state->slot_stride % 4 == 0, UNS, "state->slot_stride must be a multiple of 4");
+  }
+  if (rows > 0) {
+    c.require(mixed_qkv != nullptr, INV, "mixed_qkv must not be NULL");
+    c.require(raw_g != nullptr, INV, "raw_g must not be NULL");
+    c.require(raw_beta != nullptr, INV, "raw_beta must not be NULL");
+    c.require(out != nullptr, INV, "out must not be NULL");
+    if (H >= 1 && K >= 1 && V >= 1)
+      c.require(qkv_row_stride >= 2 * static_cast<int64_t>(H) * K + static_cast<int64_t>(H) * V, INV,
+                "qkv_row_stride must be >= 2*H*K + H*V");
+    c.require(qkv_row_stride % 8 == 0, UNS, "qkv_row_stride must be a multiple of 8");
+    c.require(aligned(mixed_qkv, 16), UNS, "mixed_qkv must be 16-byte aligned");
+    c.require(aligned(raw_g, 16), UNS, "raw_g must be 16-byte aligned");
+    c.require(aligned(raw_beta, 2), UNS, "raw_beta must be 2-byte aligned");
+    c.require(aligned(out, 16), UNS, "out must be 16-byte aligned");
+  }
+}
+
+kda::DecodeParams decode_params(int32_t num_seqs, int32_t tps, int32_t H, int32_t V,
+                                const void* mixed_qkv, int64_t qkv_row_stride, const void* raw_g,
+                                const void* raw_beta, const kda_gate_t* gate,
+                                const kda_state_t* state, void* out) {
+  kda::DecodeParams p{};
+  p.qkv = static_cast<const uint16_t*>(mixed_qkv);
+  p.qkv_row_stride = qkv_row_stride;
+  p.raw_g = static_cast<const uint16_t*>(raw_g);
+  p.raw_beta = static_cast<const uint16_t*>(raw_beta);
+  p.A_log = gate->A_log;
+  p.dt_bias = gate->dt_bias;
+  p.has_lb = gate->has_lower_bound ? 1 : 0;
+  p.lower_bound = gate->lower_bound;
+  p.scale = gate->scale;
+  p.pool = state->pool;
+  p.slot_stride = state->slot_stride;
+  p.indices = state->indices;
+  p.index_stride = state->index_stride;
+  p.out = static_cast<uint16_t*>(out);
+  p.num_seqs = num_seqs;
+  p.tokens_per_seq = tps;
+  p.H = H;
+  p.V = V;
+  return p;
+}
+
+kda_status_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) {
+    g_last_error.clear();
+    return KDA_OK;
+  }
+  g_last_error = std::string(what) + ": " + hipGetErrorString(e);
+  return KDA_ERR_HIP;
+}
+
+kda::PrefillParams prefill_params(int32_t num_seqs, int64_t num_tokens, const int32_t* cu_seqlens,
+                                  const uint8_t* has_initial_state, int32_t H, int32_t K,
+                                  int32_t V, const void* mixed_qkv, int64_t qkv_row_stride,
+                                  const void* raw_g, const void* raw_beta,
+                                  const kda_gate_t* gate, const kda_state_t* state, void* out,
+                                  void* workspace, size_t workspace_bytes) {
+  kda::PrefillParams p{};
+  p.qkv = static_cast<const uint16_t*>(mixed_qkv);
+  p.qkv_row_stride = qkv_row_stride;
+  p.raw_g = static_cast<const uint16_t*>(raw_g);
+  p.raw_beta = static_cast<const uint16_t*>(raw_beta);
+  p.A_log = gate->A_log;
+  p.dt_bias = gate->dt_bias;
+  p.has_lb = gate->has_lower_bound ? 1 : 0;
+  p.lower_bound = gate->lower_bound;
+  p.scale = gate->scale;
+  p.pool = state->pool;
+  p.slot_stride = state->slot_stride;
+  p.indices = state->indices;
+  p.index_stride = state->index_stride;
+  p.out = static_cast<uint16_t*>(out);
+  p.cu_seqlens = cu_seqlens;
+  p.has_initial_state = has_initial_state;
+  p.num_seqs = num_seqs;
+  p.num_tokens = num_tokens;
+  p.H = H;
+  p.K = K;
+  p.V = V;
+  p.workspace = workspace;
+  p.workspace_bytes = workspace_bytes;
+  return p;
+}
+
+void check_prefill_specific(Checks& c, int32_t num_seqs, int64_t num_tokens,
+                            const int32_t* cu_seqlens, int32_t H, int32_t K, int32_t V,
+                            void* workspace, size_t workspace_bytes) {
+  const auto INV = KDA_ERR_INVALID_ARGUMENT;
+  c.require(num_seqs >= 0, INV, "num_seqs must be >= 0");
+  c.require(num_tokens >= 0, INV, "num_tokens must be >= 0");
+  c.require(num_tokens <= 0x7fffffffLL, INV, "num_tokens must fit in int32");
+  if (num_seqs > 0) c.require(cu_seqlens != nullptr, INV, "cu_seqlens must not be NULL");
+  c.require(num_tokens == 0 || num_seqs > 0, INV, "num_tokens > 0 needs num_seqs > 0");
+  if (num_seqs > 0 && num_tokens > 0 && H >= 1 && (K == 64 || K == 128) && (V == 64 || V == 128)) {
+    const size_t need = kda::prefill_workspace_bytes(num_seqs, num_tokens, H, K, V);
+    c.require(workspace != nullptr && workspace_bytes >= need, KDA_ERR_WORKSPACE,
+              "workspace must be at least kda_chunk_prefill_workspace_size() bytes (" +
+                  std::to_string(need) + ")");
+    c.require(aligned(workspace, 256), KDA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status_t kda_decode_packed(int32_t num_seqs, int32_t tokens_per_seq, int32_t H, int32_t K,
+                               int32_t V, const void* mixed_qkv, int64_t qkv_row_stride,
+                               const void* raw_g, const void* raw_beta, const kda_gate_t* gate,
+                               const kda_state_t* state, void* out, hipStream_t stream) {
+  Checks c;
+  const auto INV = KDA_ERR_INVALID_ARGUMENT;
+  c.require(num_seqs >= 0, INV, "num_seqs must be >= 0");
+  c.require(tokens_per_seq >= 1 && tokens_per_seq <= 8, INV,
+            "tokens_per_seq must be in 1..8 (spec-verify steps have at most 8 rows per request)");
+  const int64_t rows = static_cast<int64_t>(num_seqs) * tokens_per_seq;
+  c.require(rows <= 0x7fffffffLL, INV, "num_seqs * tokens_per_seq must fit in int32");
+  check_common(c, rows, H, K, V, mixed_qkv, qkv_row_stride, raw_g, raw_beta, gate, state, out);
+  if (!c.ok()) return c.finish();
+  if (num_seqs == 0) return c.finish();
+  kda::DecodeParams p = decode_params(num_seqs, tokens_per_seq, H, V, mixed_qkv, qkv_row_stride,
+                                      raw_g, raw_beta, gate, state, out);
+  return hip_status(kda::launch_decode(p, K, stream), "decode launch");
+}
+
+size_t kda_chunk_prefill_workspace_size(int32_t num_seqs, int64_t num_tokens, int32_t H, int32_t K,
+                                        int32_t V) {
+  if (num_seqs < 0 || num_tokens < 0 || H < 1 || !(K == 64 || K == 128) || !(V == 64 || V == 128))
+    return 0;
+  return kda::prefill_workspace_bytes(num_seqs, num_tokens, H, K, V);
+}
+
+kda_status_t kda_chunk_prefill(int32_t num_seqs, int64_t num_tokens, const int32_t* cu_seqlens,
+                               const uint8_t* has_initial_state, int32_t H, int32_t K, int32_t V,
+                               const void* mixed_qkv, int64_t qkv_row_stride, const void* raw_g,
+                               const void* raw_beta, const kda_gate_t* gate,
+                               const kda_state_t* state, void* out, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+  Checks c;
+  check_common(c, num_tokens, H, K, V, mixed_qkv, qkv_row_stride, raw_g, raw_beta, gate, state, out);
+  check_prefill_specific(c, num_seqs, num_tokens, cu_seqlens, H, K, V, workspace, workspace_bytes);
+  if (!c.ok()) return c.finish();
+  if (num_seqs == 0 || num_tokens == 0) return c.finish();
+  kda::PrefillParams p =
+      prefill_params(num_seqs, num_tokens, cu_seqlens, has_initial_state, H, K, V, mixed_qkv,
+                     qkv_row_stride, raw_g, raw_beta, gate, state, out, workspace, workspace_bytes);
+  return hip_status(kda::launch_prefill(p, stream), "prefill launch");
+}
+
+size_t kda_mixed_batch_workspace_size(int32_t num_decodes, int32_t num_prefills,
+                                      int64_t num_prefill_tokens, int32_t H, int32_t K,
+                                      int32_t V) {
+  if (num_decodes < 0) return 0;
+  return kda_chunk_prefill_workspace_size(num_prefills, num_prefill_tokens, H, K, V);
+}
+
+kda_status_t kda_mixed_batch(int32_t num_decodes, int32_t num_prefills, int64_t num_prefill_tokens,
+                             const int32_t* prefill_cu_seqlens, const uint8_t* has_initial_state,
+                             int32_t H, int32_t K, int32_t V, const void* mixed_qkv,
+                             int64_t qkv_row_stride, const void* raw_g, const void* raw_beta,
+                             const kda_gate_t* gate, const kda_state_t* state, void* out,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Checks c;
+  const auto INV = KDA_ERR_INVALID_ARGUMENT;
+  c.require(num_decodes >= 0, INV, "num_decodes must be >= 0");
+  const int64_t rows = static_cast<int64_t>(num_decodes) + num_prefill_tokens;
+  c.require(rows <= 0x7fffffffLL, INV, "num_decodes + num_prefill_tokens must fit in int32");
+  check_common(c, rows, H, K, V, mixed_qkv, qkv_row_stride, raw_g, raw_beta, gate, state, out);
+  check_prefill_specific(c, num_prefills, num_prefill_tokens, prefill_cu_seqlens, H, K, V,
+                         workspace, workspace_bytes);
+  if (!c.ok()) return c.finish();
+
+  // Decode rows [0, D): recurrent kernel, one token per request.
+  if (num_decodes > 0) {
+    kda::DecodeParams p = decode_params(num_decodes, 1, H, V, mixed_qkv, qkv_row_stride, raw_g,
+                                        raw_beta, gate, state, out);
+    hipError_t e = kda::launch_decode(p, K, stream);
+    if (e != hipSuccess) return hip_status(e, "mixed batch: decode launch");
+  }
+  // Prefill rows [D, D + P): the chunk pipeline on the shifted views. Only
+  // host pointer arithmetic; device data is never read here.
+  if (num_prefills > 0 && num_prefill_tokens > 0) {
+    const int64_t D = num_decodes;
+    const uint16_t* qkv = static_cast<const uint16_t*>(mixed_qkv) + D * qkv_row_stride;
+    const uint16_t* rg = static_cast<const uint16_t*>(raw_g) + D * H * K;
+    const uint16_t* rb = static_cast<const uint16_t*>(raw_beta) + D * H;
+    uint16_t* o = static_cast<uint16_t*>(out) + D * H * V;
+    kda_state_t st = *state;
+    st.indices = state->indices + D * state->index_stride;
+    kda::PrefillParams p =
+        prefill_params(num_prefills, num_prefill_tokens, prefill_cu_seqlens, has_initial_state, H,
+                       K, V, qkv, qkv_row_stride, rg, rb, gate, &st, o, workspace, workspace_bytes);
+    hipError_t e = kda::launch_prefill(p, stream);
+    if (e != hipSuccess) return hip_status(e, "mixed batch: prefill launch");
+  }
+  g_last_error.clear();
+  return KDA_OK;
+}
+
+const char* kda_status_string(kda_status_t status) {
+  switch (status) {
+    case KDA_OK: return "KDA_OK";
+    case KDA_ERR_INVALID_ARGUMENT: return "KDA_ERR_INVALID_ARGUMENT";
+    case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
+    case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE";
+    case KDA_ERR_HIP: return "KDA_ERR_HIP";
+  }
+  return "KDA_ERR_UNKNOWN";
+}
+
+const char* kda_last_error(void) { return g_last_error.c_str(); }
+
+const char* kda_version(void) { return "kda-mi355x 0.1 (gfx950)"; }
+
+}  // extern "C"

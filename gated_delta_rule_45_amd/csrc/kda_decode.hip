@@ -1,0 +1,219 @@
+// kda_decode.hip -- packed single-token decode and <=8-token spec-verify.
+//
+// Packed decode (vLLM PR #51682 report, Key source excerpts): one state slot
+// per request, addressed through a possibly strided index view; spec-verify
+// (vLLM PR #60683, Refusal and steps): whole requests of tokens_per_seq rows,
+// padded requests on a null slot.
+//
+// Work split. The V columns of a state evolve independently (u_j depends only
+// on column j), so a workgroup owns a (request, head, VT-column) tile of the
+// fp32 K x V state and needs no other workgroup. Its four waves split the K
+// rows: wave w owns rows [w*K/4, (w+1)*K/4). Inside a wave, lane
+// (rg, cg) = (lane / CG, lane % CG) holds the RPL consecutive rows
+// w*K/4 + rg*RPL + r of columns 4cg..4cg+3 as float4s. With VT = 128 one
+// wave-wide load covers RG whole 512-byte rows, and every wave streams a
+// contiguous 16 KiB block of the state; a lane's rows are addressed from one
+// base with immediate offsets. The tile is read once and written once; all tokens of a request are
+// applied in registers in between. Bound by HBM bandwidth (about 0.9 flop per
+// state byte), so no MFMA.
+//
+// The per-token inputs (q, k, the decay alpha = exp(g) from the fused gate,
+// v, beta) for all tokens of the request are staged in LDS up front, while
+// the state loads are in flight, so the token loop never waits on memory.
+//
+// Per token, with S' = diag(alpha) S:
+//   u = beta (v - S'^T k),   o = scale (S'^T q + u (k.q)),   S = S' + k u^T
+// which is the decay / delta-write / readout order in one pass over the tile.
+// The K-reductions are a per-lane partial, a butterfly over the wave's row
+// groups, and a sum of the four waves' partials through LDS (one barrier per
+// token; the partial buffer alternates between tokens).
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kMaxTokens = 8;
+
+}  // namespace
+
+template <int K, int V, int VT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8)))
+void decode_kernel(const DecodeParams p) {
+  constexpr int RW = K / kWaves;   // rows per wave
+  constexpr int CG = VT / 4;       // column groups of 4 columns
+  constexpr int RG = 64 / CG;      // row groups per wave
+  constexpr int RPL = RW / RG;     // rows per lane
+  static_assert(CG * RG == 64 && RPL * RG == RW && RPL >= 1, "tile does not fit");
+
+  __shared__ float s_q[kMaxTokens][K];
+  __shared__ float s_k[kMaxTokens][K];
+  __shared__ float s_a[kMaxTokens][K];
+  __shared__ float s_v[kMaxTokens][VT];
+  __shared__ float s_b[kMaxTokens];
+  __shared__ float s_red[2][kWaves][2 * VT + 4];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int H = p.H;
+  const int tps = p.tokens_per_seq;
+  constexpr int tiles = V / VT;
+  const int64_t bid = blockIdx.x;
+  const int tile = static_cast<int>(bid % tiles);
+  const int64_t nh = bid / tiles;
+  const int h = static_cast<int>(nh % H);
+  const int n = static_cast<int>(nh / H);
+  const int64_t row0 = static_cast<int64_t>(n) * tps;
+  const int cg = lane % CG;
+  const int rg = lane / CG;
+  const int col = tile * VT + cg * 4;
+
+  // State slot of this request: a strided 1-D view, widened to 64 bits.
+  const int64_t slot = static_cast<int64_t>(p.indices[static_cast<int64_t>(n) * p.index_stride]);
+
+  if (slot < 0) {
+    // Null slot (the same for the whole workgroup): no state traffic, zero rows.
+    for (int e = tid; e < tps * VT; e += blockDim.x) {
+      const int t = e / VT, j = e % VT;
+      p.out[((row0 + t) * H + h) * static_cast<int64_t>(V) + tile * VT + j] = 0;
+    }
+    return;
+  }
+
+  // 1. Issue the state loads first: one buffer resource over this head's
+  //    K x V tile, a per-lane offset, and per-row scalar offsets.
+  const __amdgpu_buffer_rsrc_t tile_rsrc =
+      make_rsrc(p.pool + slot * p.slot_stride + static_cast<int64_t>(h) * K * V, K * V * 4);
+  const int voff = ((w * RW + rg * RPL) * V + col) * 4;
+  f32x4 S[RPL];
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) S[r] = buffer_load_f32x4<kStreamPolicy>(tile_rsrc, voff, r * V * 4);
+
+  // 2. Stage every token's q, k, alpha, v-tile and beta in LDS.
+  {
+    const float a = __expf(p.A_log[h]);
+    const bool has_lb = p.has_lb != 0;
+    for (int e = tid; e < tps * K; e += blockDim.x) {
+      const int t = e / K, i = e % K;
+      const int64_t row = row0 + t;
+      const uint16_t* qkv = p.qkv + row * p.qkv_row_stride;
+      s_q[t][i] = bf16_to_f32(qkv[h * K + i]);
+      s_k[t][i] = bf16_to_f32(qkv[H * K + h * K + i]);
+      const float g = gate_log_decay(bf16_to_f32(p.raw_g[row * (H * K) + h * K + i]),
+                                     p.dt_bias[h * K + i], a, has_lb, p.lower_bound);
+      s_a[t][i] = __expf(g);
+    }
+    for (int e = tid; e < tps * VT; e += blockDim.x) {
+      const int t = e / VT, j = e % VT;
+      s_v[t][j] = bf16_to_f32(p.qkv[(row0 + t) * p.qkv_row_stride + 2 * H * K + h * V + tile * VT + j]);
+    }
+    if (tid < tps) s_b[tid] = sigmoid_f32(bf16_to_f32(p.raw_beta[(row0 + tid) * H + h]));
+  }
+  __syncthreads();
+
+  // 3. Token loop, all in registers.
+  for (int t = 0; t < tps; ++t) {
+    f32x4 kS = {0.f, 0.f, 0.f, 0.f};
+    f32x4 qS = {0.f, 0.f, 0.f, 0.f};
+    float kq = 0.f;
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+      const int row = w * RW + rg * RPL + r;
+      const float alpha = s_a[t][row];
+      const float kk = s_k[t][row];
+      const float qq = s_q[t][row];
+      S[r] *= alpha;
+      kS += kk * S[r];
+      qS += qq * S[r];
+      kq = fmaf(kk, qq, kq);
+    }
+#pragma unroll
+    for (int off = CG; off < 64; off <<= 1) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        kS[c] += __shfl_xor(kS[c], off);
+        qS[c] += __shfl_xor(qS[c], off);
+      }
+      kq += __shfl_xor(kq, off);
+    }
+    float(*red)[2 * VT + 4] = s_red[t & 1];
+    if (rg == 0) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        red[w][cg * 4 + c] = kS[c];
+        red[w][VT + cg * 4 + c] = qS[c];
+      }
+      if (cg == 0) red[w][2 * VT] = kq;
+    }
+    __syncthreads();
+    kS = f32x4{0.f, 0.f, 0.f, 0.f};
+    qS = f32x4{0.f, 0.f, 0.f, 0.f};
+    kq = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        kS[c] += red[ww][cg * 4 + c];
+        qS[c] += red[ww][VT + cg * 4 + c];
+      }
+      kq += red[ww][2 * VT];
+    }
+    const float beta = s_b[t];
+    f32x4 u;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) u[c] = beta * (s_v[t][cg * 4 + c] - kS[c]);
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) S[r] += s_k[t][w * RW + rg * RPL + r] * u;
+    if (w == 0 && rg == 0) {
+      const float s = p.scale;
+      uint16_t* o = p.out + ((row0 + t) * H + h) * static_cast<int64_t>(V) + col;
+      *reinterpret_cast<uint2*>(o) =
+          make_uint2(pack_bf16x2(s * fmaf(u[0], kq, qS[0]), s * fmaf(u[1], kq, qS[1])),
+                     pack_bf16x2(s * fmaf(u[2], kq, qS[2]), s * fmaf(u[3], kq, qS[3])));
+    }
+  }
+
+  // 4. Store the final state.
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) buffer_store_f32x4<kStreamPolicy>(S[r], tile_rsrc, voff, r * V * 4);
+}
+
+template <int K, int V>
+static hipError_t launch_kv(const DecodeParams& p, int vt, hipStream_t stream) {
+  const int64_t blocks = static_cast<int64_t>(p.num_seqs) * p.H * (V / vt);
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  dim3 grid(static_cast<unsigned>(blocks)), block(64 * kWaves);
+  switch (vt) {
+    case 16: decode_kernel<K, V, 16><<<grid, block, 0, stream>>>(p); break;
+    case 32: decode_kernel<K, V, 32><<<grid, block, 0, stream>>>(p); break;
+    case 64: decode_kernel<K, V, 64><<<grid, block, 0, stream>>>(p); break;
+    default:
+      if constexpr (V == 128) decode_kernel<K, V, 128><<<grid, block, 0, stream>>>(p);
+      break;
+  }
+  return hipGetLastError();
+}
+
+// Column-tile choice: whole rows (VT = V) when there are enough (request,
+// head) pairs to fill the chip; narrower tiles for small batches, so that a
+// spec-verify step of a single request still spreads over the 256 CUs.
+hipError_t launch_decode(DecodeParams p, int K, hipStream_t stream) {
+  const int64_t pairs = static_cast<int64_t>(p.num_seqs) * p.H;
+  int vt = 128;
+  if (pairs < 512) vt = 64;
+  if (pairs < 256) vt = 32;
+  if (pairs < 128) vt = 16;
+  if (vt > p.V) vt = p.V;
+  p.num_tiles = pairs * (p.V / vt);
+  if (K == 64) {
+    if (p.V == 64) return launch_kv<64, 64>(p, vt, stream);
+    return launch_kv<64, 128>(p, vt, stream);
+  }
+  if (p.V == 64) return launch_kv<128, 64>(p, vt, stream);
+  return launch_kv<128, 128>(p, vt, stream);
+}
+
+}  // namespace kda

@@ -1,0 +1,68 @@
+// kda_internal.h -- launch descriptors shared between the C-ABI front end and
+// the kernel translation units. Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+// One packed-decode / spec-verify launch.
+struct DecodeParams {
+  const uint16_t* qkv;      // bf16 [rows][qkv_row_stride]
+  int64_t qkv_row_stride;   // elements
+  const uint16_t* raw_g;    // bf16 [rows][H*K]
+  const uint16_t* raw_beta; // bf16 [rows][H]
+  const float* A_log;       // [H]
+  const float* dt_bias;     // [H*K]
+  float lower_bound;
+  float scale;
+  int32_t has_lb;
+  float* pool;
+  int64_t slot_stride;
+  const int32_t* indices;
+  int64_t index_stride;
+  uint16_t* out;            // bf16 [rows][H][V]
+  int32_t num_seqs;
+  int32_t tokens_per_seq;
+  int32_t H;
+  int32_t V;
+  int64_t num_tiles;        // num_seqs * H * (V / VT)
+};
+
+// Picks the column-tile width for a decode launch and launches it.
+hipError_t launch_decode(DecodeParams p, int K, hipStream_t stream);
+
+// One chunked-prefill call (all sequences of one varlen batch).
+struct PrefillParams {
+  const uint16_t* qkv;
+  int64_t qkv_row_stride;
+  const uint16_t* raw_g;
+  const uint16_t* raw_beta;
+  const float* A_log;
+  const float* dt_bias;
+  float lower_bound;
+  float scale;
+  int32_t has_lb;
+  float* pool;
+  int64_t slot_stride;
+  const int32_t* indices;
+  int64_t index_stride;
+  uint16_t* out;
+  const int32_t* cu_seqlens;
+  const uint8_t* has_initial_state;  // may be null
+  int32_t num_seqs;
+  int64_t num_tokens;
+  int32_t H;
+  int32_t K;
+  int32_t V;
+  void* workspace;
+  size_t workspace_bytes;
+};
+
+size_t prefill_workspace_bytes(int32_t num_seqs, int64_t num_tokens, int32_t H,
+                               int32_t K, int32_t V);
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
+
+}  // namespace kda

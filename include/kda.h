@@ -1,0 +1,185 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention (KDA) library.
+ *
+ * KDA keeps, per sequence and head, an fp32 K x V state S. Per token it decays
+ * S per key channel by alpha = exp(g), writes the value with a beta-scaled
+ * delta rule, and reads out o = scale * S^T q (decay, write, readout):
+ *     S <- diag(alpha) S ;  u = beta (v - S^T k) ;  S <- S + k u^T ;  o = scale S^T q
+ * The gate g and beta are fused from raw inputs inside the kernels:
+ *     x = raw_g + dt_bias ,  a = exp(A_log[h])
+ *     g = -a * softplus(x)              (no lower bound)
+ *     g = lower_bound * sigmoid(a * x)  (with a lower bound)
+ *     beta = sigmoid(raw_beta)
+ * Sources: vLLM PR #51682 (prhub report), "Key source excerpts" and
+ * "Implementation breakdown" give the packed-decode argument set and the
+ * strided slot addressing; vLLM PR #50649, "Purpose", gives the chunked prefill
+ * with its WY recompute_w_u step and the rule that decode rows of a mixed
+ * batch never go through the chunk path; vLLM PR #60683, "Purpose" and
+ * "Refusal and steps", gives spec-verify steps of at most 8 rows with padded
+ * requests on a null state slot. The gate formula is a reading of the argument
+ * names (the pages print no formula).
+ *
+ * Conventions for every entry point:
+ *  - All data pointers are DEVICE pointers owned by the caller. Inputs are only
+ *    read, the state pool is read and written in place, outputs are written.
+ *  - No call allocates or frees memory, synchronises the host, or reads device
+ *    memory from the host; every launch goes on `stream` (NULL = the default
+ *    stream). Calls can therefore be captured in a HIP graph.
+ *  - Arguments are validated on the host before anything is launched. On any
+ *    failed check nothing is launched, the call returns a non-zero status, and
+ *    kda_last_error() lists every failed check (not just the first).
+ *  - Device-side values are the caller's guarantee and are not checked: slot
+ *    numbers must be < num_slots, slots must be unique within one call, and
+ *    cu_seqlens must start at 0, be non-decreasing and end at num_tokens.
+ *  - bf16 outputs are rounded to nearest even; the state stays fp32.
+ *  - Supported head dims: K, V in {64, 128}. Layout alignment: mixed_qkv, raw_g,
+ *    out and the pool must be 16-byte aligned, qkv_row_stride a multiple of 8
+ *    and slot_stride a multiple of 4 elements.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size or stride, bad value */
+  KDA_ERR_UNSUPPORTED = 2,      /* valid but not built: head dim, alignment   */
+  KDA_ERR_WORKSPACE = 3,        /* workspace missing or too small             */
+  KDA_ERR_HIP = 4               /* a HIP launch reported an error             */
+} kda_status_t;
+
+/* Gate and readout parameters (vLLM PR #51682 report, Key source excerpts:
+ * A_log, dt_bias, lower_bound). */
+typedef struct {
+  const float* A_log;      /* device fp32 [H]                                   */
+  const float* dt_bias;    /* device fp32 [H*K]                                 */
+  int32_t has_lower_bound; /* 0: no lower bound ("None")                        */
+  float lower_bound;       /* used when has_lower_bound; must be <= 0, finite   */
+  float scale;             /* o = scale * S^T q; finite                         */
+} kda_gate_t;
+
+/* State pool, updated in place (vLLM PR #51682 report, Implementation
+ * breakdown: the slot of sequence i is state_indices[i * stride], read as a
+ * 64-bit offset; the slot stride comes from the pool tensor). */
+typedef struct {
+  float* pool;             /* device fp32; slot s, head h at
+                              pool + s*slot_stride + h*K*V, [K][V] row-major    */
+  int64_t slot_stride;     /* elements between slots, >= H*K*V                  */
+  int64_t num_slots;       /* >= 1                                              */
+  const int32_t* indices;  /* device int32; entry i at indices[i*index_stride];
+                              a negative entry is a null slot                   */
+  int64_t index_stride;    /* elements, >= 1 (a strided view such as column 0
+                              of a block table is accepted without a copy)      */
+} kda_state_t;
+
+/*
+ * Packed decode and spec-verify (vLLM PR #51682 report, Key source excerpts:
+ * fused_recurrent_kda_packed_decode; vLLM PR #60683, Refusal and steps).
+ *
+ * num_seqs sequences of tokens_per_seq (1..8) consecutive rows each; rows =
+ * num_seqs * tokens_per_seq. Sequence n uses slot indices[n*index_stride]: its
+ * state is read, the tokens are applied in order, and only the state after the
+ * last token is written back. A null slot (negative entry) reads and writes no
+ * state and yields zero output rows.
+ *   mixed_qkv  bf16 [rows][qkv_row_stride]; per row [q | k | v], each
+ *              head-major: q of head h at h*K, k at H*K + h*K, v at 2*H*K + h*V.
+ *              qkv_row_stride >= 2*H*K + H*V.
+ *   raw_g      bf16 [rows][H*K], contiguous.
+ *   raw_beta   bf16 [rows][H], contiguous.
+ *   out        bf16 [rows][H][V], contiguous.
+ * Errors: KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED, KDA_ERR_HIP.
+ */
+kda_status_t kda_decode_packed(int32_t num_seqs, int32_t tokens_per_seq,
+                               int32_t H, int32_t K, int32_t V,
+                               const void* mixed_qkv, int64_t qkv_row_stride,
+                               const void* raw_g, const void* raw_beta,
+                               const kda_gate_t* gate, const kda_state_t* state,
+                               void* out, hipStream_t stream);
+
+/* Bytes of device workspace kda_chunk_prefill needs for these sizes (a pure
+ * host computation; returns 0 for invalid sizes). */
+size_t kda_chunk_prefill_workspace_size(int32_t num_seqs, int64_t num_tokens,
+                                        int32_t H, int32_t K, int32_t V);
+
+/*
+ * Chunked prefill at chunk size 64 (vLLM PR #50649, Purpose:
+ * chunk_kda_with_fused_gate and recompute_w_u).
+ *
+ * Varlen: sequence i covers rows cu_seqlens[i] .. cu_seqlens[i+1]-1 (device
+ * int32 [num_seqs+1], cu_seqlens[num_seqs] == num_tokens) and uses slot
+ * indices[i*index_stride]. Its initial state is read from the slot unless
+ * has_initial_state[i] == 0 (device uint8 [num_seqs]; NULL means all 1), in
+ * which case it starts from zero. The final state is written to the slot. A
+ * zero-length sequence or a null slot touches no state (null: zero output).
+ * Chunks never cross sequences; the last chunk of a sequence may be partial.
+ * Row formats as for kda_decode_packed; out is bf16 [num_tokens][H][V].
+ * workspace: device scratch of at least kda_chunk_prefill_workspace_size()
+ * bytes, 256-byte aligned, owned by the caller; its contents are not needed
+ * before or after the call.
+ * Errors: KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE,
+ * KDA_ERR_HIP.
+ */
+kda_status_t kda_chunk_prefill(int32_t num_seqs, int64_t num_tokens,
+                               const int32_t* cu_seqlens,
+                               const uint8_t* has_initial_state,
+                               int32_t H, int32_t K, int32_t V,
+                               const void* mixed_qkv, int64_t qkv_row_stride,
+                               const void* raw_g, const void* raw_beta,
+                               const kda_gate_t* gate, const kda_state_t* state,
+                               void* out, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/* Bytes of device workspace kda_mixed_batch needs. */
+size_t kda_mixed_batch_workspace_size(int32_t num_decodes, int32_t num_prefills,
+                                      int64_t num_prefill_tokens, int32_t H,
+                                      int32_t K, int32_t V);
+
+/*
+ * Mixed decode + prefill batch in one call (vLLM PR #50649, Purpose: the
+ * decode rows of a mixed non-speculative batch go to the recurrent kernel,
+ * never to the chunk kernel, which returned NaN for them).
+ *
+ * Rows [0, num_decodes) are single-token decodes; decode d uses slot
+ * indices[d*index_stride]. Rows [num_decodes, num_decodes+num_prefill_tokens)
+ * are num_prefills prefill sequences described by prefill_cu_seqlens (device
+ * int32 [num_prefills+1], relative to row num_decodes); prefill i uses slot
+ * indices[(num_decodes+i)*index_stride] and has_initial_state[i] (NULL = all
+ * 1). Decode rows go to the recurrent decode kernel, prefill rows to the chunk
+ * pipeline, all on `stream` with no host synchronisation. out is bf16
+ * [num_decodes+num_prefill_tokens][H][V].
+ * Errors: as kda_chunk_prefill.
+ */
+kda_status_t kda_mixed_batch(int32_t num_decodes, int32_t num_prefills,
+                             int64_t num_prefill_tokens,
+                             const int32_t* prefill_cu_seqlens,
+                             const uint8_t* has_initial_state,
+                             int32_t H, int32_t K, int32_t V,
+                             const void* mixed_qkv, int64_t qkv_row_stride,
+                             const void* raw_g, const void* raw_beta,
+                             const kda_gate_t* gate, const kda_state_t* state,
+                             void* out, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
+/* Static name of a status code. */
+const char* kda_status_string(kda_status_t status);
+
+/* Detail of the last failed call on the calling thread: every failed check,
+ * separated by "; ". Empty after a successful call. The pointer stays valid
+ * until the next call on the same thread. */
+const char* kda_last_error(void);
+
+/* Library version string. */
+const char* kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KDA_H */

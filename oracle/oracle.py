@@ -194,14 +194,35 @@ def _pool2d(pool: torch.Tensor) -> np.ndarray:
     return np.array(pool.reshape(pool.shape[0], -1).numpy(), dtype=np.float32, copy=True)
 
 
+def _compact(pool: torch.Tensor, idx: np.ndarray):
+    """Gathers the slots the call references into a small pool and remaps the
+    index buffer to it (plumbing only: the oracle sees the same slot contents,
+    and untouched slots cannot change). Returns (pool2d, idx_remapped)."""
+    refs = sorted({int(x) for x in np.unique(idx) if x >= 0})
+    pool = pool.detach().cpu()
+    if not refs:
+        return np.zeros((1, int(np.prod(pool.shape[1:]))), dtype=np.float32), idx
+    sel = pool[torch.tensor(refs, dtype=torch.long)]
+    comp = np.array(sel.reshape(len(refs), -1).numpy(), dtype=np.float32, copy=True)
+    remap = {s: i for i, s in enumerate(refs)}
+    idx2 = np.array([remap.get(int(x), int(x)) if x >= 0 else int(x) for x in idx], dtype=np.int32)
+    return comp, idx2
+
+
 def decode_packed(inp: dict, pool: torch.Tensor, state_indices: torch.Tensor,
                   H: int, K: int, V: int, tokens_per_seq: int = 1,
-                  lower_bound=None, scale: float = 1.0, form: int = 0):
+                  lower_bound=None, scale: float = 1.0, form: int = 0,
+                  return_pool: bool = True):
     """Packed decode / spec-verify. Returns (out [rows,H,V], final_state
-    [seqs,H,K,V] (zeros for null slots), pool_after [slots, slot_stride])."""
+    [seqs,H,K,V] (zeros for null slots), pool_after [slots, slot_stride]).
+    With ``return_pool=False`` only the referenced slots are copied and
+    pool_after is None (much faster on GiB-sized pools)."""
     idx, ist = _indices(state_indices)
     num_seqs = state_indices.shape[0]
-    P = _pool2d(pool)
+    if return_pool:
+        P = _pool2d(pool)
+    else:
+        P, idx = _compact(pool, idx)
     keep: list = []
     a = _args(inp, P, idx, ist, lower_bound, scale, keep)
     rows = num_seqs * tokens_per_seq
@@ -211,12 +232,13 @@ def decode_packed(inp: dict, pool: torch.Tensor, state_indices: torch.Tensor,
                                         int(form), _ptr(out), _ptr(fs))
     if rc != 0:
         raise ValueError("oracle rejected the decode arguments")
-    return out, fs, P
+    return out, fs, (P if return_pool else None)
 
 
 def prefill(inp: dict, pool: torch.Tensor, state_indices: torch.Tensor,
             cu_seqlens, H: int, K: int, V: int, has_initial_state=None,
-            lower_bound=None, scale: float = 1.0, form: int = 0):
+            lower_bound=None, scale: float = 1.0, form: int = 0,
+            return_pool: bool = True):
     """Varlen prefill over rows 0..cu_seqlens[-1]-1 of ``inp``.
     Returns (out [rows,H,V], final_state [seqs,H,K,V], pool_after)."""
     cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
@@ -225,7 +247,10 @@ def prefill(inp: dict, pool: torch.Tensor, state_indices: torch.Tensor,
     if has_initial_state is not None:
         hs = np.ascontiguousarray(np.asarray(has_initial_state, dtype=np.uint8))
     idx, ist = _indices(state_indices)
-    P = _pool2d(pool)
+    if return_pool:
+        P = _pool2d(pool)
+    else:
+        P, idx = _compact(pool, idx)
     keep: list = []
     a = _args(inp, P, idx, ist, lower_bound, scale, keep)
     rows = int(cu[-1]) if num_seqs >= 0 else 0
@@ -235,13 +260,13 @@ def prefill(inp: dict, pool: torch.Tensor, state_indices: torch.Tensor,
                                   H, K, V, ctypes.byref(a), int(form), _ptr(out), _ptr(fs))
     if rc != 0:
         raise ValueError("oracle rejected the prefill arguments")
-    return out, fs, P
+    return out, fs, (P if return_pool else None)
 
 
 def mixed_batch(inp: dict, pool: torch.Tensor, state_indices: torch.Tensor,
                 num_decodes: int, prefill_cu_seqlens, H: int, K: int, V: int,
                 has_initial_state=None, lower_bound=None, scale: float = 1.0,
-                form: int = 0):
+                form: int = 0, return_pool: bool = True):
     """Decode rows [0, D) then prefill sequences over rows D.. (cu_seqlens
     relative to D); slot entries: the D decodes first, then the prefills.
     Every sequence is independent, so this is one call over all of them with
@@ -253,4 +278,4 @@ def mixed_batch(inp: dict, pool: torch.Tensor, state_indices: torch.Tensor,
         hs = np.concatenate([np.ones(num_decodes, dtype=np.uint8),
                              np.asarray(has_initial_state, dtype=np.uint8)])
     return prefill(inp, pool, state_indices, cu, H, K, V, has_initial_state=hs,
-                   lower_bound=lower_bound, scale=scale, form=form)
+                   lower_bound=lower_bound, scale=scale, form=form, return_pool=return_pool)

@@ -1,0 +1,153 @@
+"""CPU checks of the C ABI: the library loads, exports every symbol the header
+declares, and rejects bad arguments on the host before launching anything
+(every failed check is reported at once). No call here reaches a kernel."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import gated_delta_rule_45_amd as kda
+from gated_delta_rule_45_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_three_entry_points():
+    names = declared_functions()
+    for n in ("kda_decode_packed", "kda_chunk_prefill", "kda_mixed_batch"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = kda.lib()
+    missing = [n for n in declared_functions() if not hasattr(L, n)]
+    assert not missing, f"not exported: {missing}"
+
+
+def test_status_strings_and_version():
+    L = kda.lib()
+    assert L.kda_status_string(0) == b"KDA_OK"
+    assert L.kda_status_string(3) == b"KDA_ERR_WORKSPACE"
+    assert b"gfx950" in L.kda_version()
+
+
+FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation first
+
+
+def _gate(**kw):
+    d = dict(A_log=FAKE, dt_bias=FAKE, has_lower_bound=1, lower_bound=-5.0, scale=1.0)
+    d.update(kw)
+    return B.KdaGate(**d)
+
+
+def _state(**kw):
+    d = dict(pool=FAKE, slot_stride=32 * 128 * 128, num_slots=4, indices=FAKE, index_stride=8)
+    d.update(kw)
+    return B.KdaState(**d)
+
+
+def _decode(num_seqs=4, tps=1, H=32, K=128, V=128, qkv=FAKE, stride=3 * 32 * 128, g=None, s=None,
+            out=FAKE):
+    L = kda.lib()
+    g = g or _gate()
+    s = s or _state()
+    st = L.kda_decode_packed(num_seqs, tps, H, K, V, qkv, stride, FAKE, FAKE, ctypes.byref(g),
+                             ctypes.byref(s), out, None)
+    return st, L.kda_last_error().decode()
+
+
+def test_decode_rejects_and_lists_every_reason():
+    st, msg = _decode(tps=9, K=96, s=_state(index_stride=0, pool=None), out=None)
+    assert st == 1
+    for frag in ("tokens_per_seq must be in 1..8", "K must be 64 or 128",
+                 "index_stride must be >= 1", "pool must not be NULL", "out must not be NULL"):
+        assert frag in msg, msg
+
+
+def test_negative_index_stride_rejected():
+    st, msg = _decode(s=_state(index_stride=-8))
+    assert st == 1 and "index_stride" in msg
+
+
+def test_bad_gate_values_rejected():
+    st, msg = _decode(g=_gate(lower_bound=float("nan")))
+    assert st == 1 and "lower_bound" in msg
+    st, msg = _decode(g=_gate(lower_bound=0.5))
+    assert st == 1 and "lower_bound" in msg
+    st, msg = _decode(g=_gate(scale=float("inf")))
+    assert st == 1 and "scale" in msg
+    st, msg = _decode(g=_gate(A_log=None))
+    assert st == 1 and "A_log" in msg
+
+
+def test_alignment_and_strides_are_unsupported_not_invalid():
+    st, msg = _decode(qkv=FAKE + 2)
+    assert st == 2 and "mixed_qkv must be 16-byte aligned" in msg
+    st, msg = _decode(stride=3 * 32 * 128 + 4)
+    assert st == 2 and "multiple of 8" in msg
+    st, msg = _decode(stride=100)
+    assert st == 1 and "qkv_row_stride" in msg
+
+
+def test_slot_stride_too_small():
+    st, msg = _decode(s=_state(slot_stride=100))
+    assert st == 1 and "slot_stride" in msg
+
+
+def test_empty_decode_is_a_no_op():
+    st, msg = _decode(num_seqs=0)
+    assert st == 0 and msg == ""
+
+
+def test_workspace_size_query():
+    L = kda.lib()
+    a = L.kda_chunk_prefill_workspace_size(1, 8192, 32, 128, 128)
+    b = L.kda_chunk_prefill_workspace_size(64, 8192, 32, 128, 128)
+    c = L.kda_chunk_prefill_workspace_size(1, 65536, 32, 128, 128)
+    assert 0 < a < b and a < c
+    assert L.kda_chunk_prefill_workspace_size(1, 10, 32, 96, 128) == 0
+    assert L.kda_chunk_prefill_workspace_size(-1, 10, 32, 128, 128) == 0
+    assert L.kda_mixed_batch_workspace_size(96, 5, 4000, 32, 128, 128) == \
+        L.kda_chunk_prefill_workspace_size(5, 4000, 32, 128, 128)
+
+
+def test_prefill_rejects_missing_workspace_and_cu_seqlens():
+    L = kda.lib()
+    g, s = _gate(), _state(index_stride=1)
+    st = L.kda_chunk_prefill(2, 100, None, None, 32, 128, 128, FAKE, 3 * 32 * 128, FAKE, FAKE,
+                             ctypes.byref(g), ctypes.byref(s), FAKE, None, 0, None)
+    msg = L.kda_last_error().decode()
+    assert st == 1
+    assert "cu_seqlens must not be NULL" in msg and "workspace" in msg
+    need = L.kda_chunk_prefill_workspace_size(2, 100, 32, 128, 128)
+    st = L.kda_chunk_prefill(2, 100, FAKE, None, 32, 128, 128, FAKE, 3 * 32 * 128, FAKE, FAKE,
+                             ctypes.byref(g), ctypes.byref(s), FAKE, FAKE, need - 1, None)
+    assert st == 3 and "workspace" in L.kda_last_error().decode()
+
+
+def test_mixed_rejects_negative_decodes():
+    L = kda.lib()
+    g, s = _gate(), _state()
+    st = L.kda_mixed_batch(-1, 0, 0, None, None, 32, 128, 128, FAKE, 3 * 32 * 128, FAKE, FAKE,
+                           ctypes.byref(g), ctypes.byref(s), FAKE, None, 0, None)
+    assert st == 1 and "num_decodes" in L.kda_last_error().decode()
+
+
+def test_binding_refuses_host_tensors_listing_each():
+    t = torch.zeros(4, 3 * 4 * 64, dtype=torch.bfloat16)
+    with pytest.raises(kda.KdaError) as ei:
+        kda.kda_decode_packed(t, torch.zeros(4, 256, dtype=torch.bfloat16),
+                              torch.zeros(4, 4, dtype=torch.bfloat16), torch.zeros(4),
+                              torch.zeros(256), -5.0, torch.zeros(8, 4, 64, 64),
+                              torch.zeros(4, dtype=torch.int32))
+    reasons = ei.value.reasons
+    assert sum("must be on a GPU" in r for r in reasons) == 7

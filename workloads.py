@@ -19,7 +19,7 @@ distributions are this project's choice, since the pages give none):
 from __future__ import annotations
 
 import dataclasses
-import math
+import functools
 
 import torch
 
@@ -52,10 +52,12 @@ def make_token_inputs(rows: int, H: int, K: int, V: int, seed: int) -> dict:
     }
 
 
+@functools.lru_cache(maxsize=2)
 def make_pool(num_slots: int, H: int, K: int, V: int, std: float, seed: int,
               slot_pad: int = 0) -> torch.Tensor:
     """fp32 state pool [slots, H, K, V] (CPU). With ``slot_pad`` > 0 the
-    result is a view of a larger buffer whose slot stride is H*K*V + slot_pad."""
+    result is a view of a larger buffer whose slot stride is H*K*V + slot_pad.
+    The result is cached (pools reach 2 GiB): callers must not modify it."""
     g = _gen(seed)
     per = H * K * V
     buf = torch.randn(num_slots, per + slot_pad, generator=g).mul_(std)
@@ -132,11 +134,13 @@ class Case:
 
 
 def decode_case(name, H, K, V, num_seqs, tokens_per_seq, num_slots, index_stride,
-                lower_bound, seed, std=0.05, null_rows=(), slot_pad=0, scale=1.0) -> Case:
+                lower_bound, seed, std=0.05, null_rows=(), slot_pad=0, scale=1.0,
+                pool_seed=None) -> Case:
     rows = num_seqs * tokens_per_seq
     return Case(name=name, kind="decode", H=H, K=K, V=V,
                 inputs=make_token_inputs(rows, H, K, V, seed),
-                pool=make_pool(num_slots, H, K, V, std, seed + 1, slot_pad),
+                pool=make_pool(num_slots, H, K, V, std,
+                               seed + 1 if pool_seed is None else pool_seed, slot_pad),
                 block_table=make_block_table(num_seqs, index_stride, num_slots, seed + 2, null_rows),
                 tokens_per_seq=tokens_per_seq, lower_bound=lower_bound, scale=scale)
 
@@ -176,10 +180,10 @@ def batched_decode(index_stride: int = 8, lower_bound: float | None = -5.0,
                    num_seqs: int = 32) -> Case:
     """32 single-token sequences, H=32, K=V=128, 512-slot pool (1 GiB) of
     0.05*randn, unique random slots at index stride 1 or 8."""
-    variant = (index_stride == 8) * 2 + (lower_bound is None)
+    variant = (index_stride == 8) * 2 + (lower_bound is None) + 4 * (num_seqs != 32)
     return decode_case(f"batched_decode_h32_k128_n{num_seqs}_s{index_stride}_lb{lower_bound}",
                        32, 128, 128, num_seqs, 1, 512, index_stride, lower_bound,
-                       1000 + variant)
+                       1000 + 10 * variant + num_seqs % 10, pool_seed=1999)
 
 
 SPEC_LAYOUTS = {  # name -> (real sequences, tokens per sequence, padded null requests)
@@ -197,7 +201,8 @@ def spec_verify(layout: str, lower_bound: float | None = -5.0) -> Case:
     variant = list(SPEC_LAYOUTS).index(layout)
     n = real + nulls
     return decode_case(f"spec_verify_{layout}_h32_k128", 32, 128, 128, n, tps, 512, 8,
-                       lower_bound, 2000 + variant, null_rows=tuple(range(real, n)))
+                       lower_bound, 2000 + variant, null_rows=tuple(range(real, n)),
+                       pool_seed=2999)
 
 
 def prefill_8192(lower_bound: float | None = -5.0) -> Case:
