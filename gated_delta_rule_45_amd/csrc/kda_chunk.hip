@@ -1,18 +1,732 @@
-// kda_chunk.hip -- chunked prefill (placeholder until the chunk kernels land).
+// kda_chunk.hip -- chunked prefill at chunk size 64 (chunk_kda_with_fused_gate
+// with its WY recompute_w_u step, vLLM PR #50649, Purpose).
+//
+// Within a chunk of n <= 64 tokens of one (sequence, head) that starts from
+// state S, with gam_t = sum_{s<=t} g_s (per key channel), the recurrence is
+// reached exactly by
+//   A[t][s] = beta_t sum_i k_ti k_si e^{gam_ti - gam_si}   (s < t)
+//   T       = (I + A)^{-1}
+//   W       = T diag(beta) (K o e^gam),   U = T diag(beta) V     (recompute_w_u)
+//   V'      = U - W S                                              (delta writes)
+//   P[t][s] = sum_i q_ti k_si e^{gam_ti - gam_si}          (s <= t)
+//   O       = scale [ (Q o e^gam) S + P V' ]
+//   S      <- diag(e^{gam_last}) S + (K o e^{gam_last - gam})^T V'
+//
+// Three launches on one stream, no host synchronisation:
+//  1. plan:  chunk offsets per sequence from the device cu_seqlens.
+//  2. intra: one workgroup per (chunk, head), all chunks in parallel. Builds
+//            gam, A and P (off-diagonal 16x16 blocks on bf16 MFMA with a
+//            reference point between the two blocks so both factors stay <= 1;
+//            diagonal blocks pairwise in fp32 so nothing can overflow for any
+//            gate), T by blocked forward substitution in fp32, then W and U on
+//            MFMA. It stores -W, Q o e^gam, P, (K o e^{gam_last-gam})^T (bf16,
+//            laid out as MFMA A operands), e^{gam_last} and U (fp32, in
+//            accumulator fragment order) in the workspace.
+//  3. state: one workgroup per (sequence, head, 64 value columns), looping over
+//            the sequence's chunks in order. The state lives in MFMA
+//            accumulators (fp32) for the whole sequence; each chunk's A
+//            operands are double-buffered in LDS, and the next chunk's are
+//            fetched while the current one computes.
+//
+// Accumulator reuse. The bf16 16x16x32 MFMA leaves lane l with rows
+// 4(l/16)+j (j < 4) of column l%16; its B operand wants rows 8(l/16)+j
+// (j < 8). Two accumulator tiles (rows r0..r0+15 and r0+16..r0+31) therefore
+// form a B operand directly if the contraction index is permuted within each
+// 32-block: storage slot 8g+j holds index 4g+j (j < 4) or 16+4g+j-4 (j >= 4).
+// The A operands that meet such a B operand (-W and Q o e^gam along channels,
+// P and K^T along positions) are stored in that permuted order, so S and V'
+// never leave registers.
+#include "kda_device.h"
 #include "kda_internal.h"
 
 namespace kda {
 
+namespace {
+
+constexpr int C = 64;          // chunk size
+constexpr int kThreads = 256;  // 4 waves per workgroup
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Index held in permuted storage slot s (0..31) of a 32-block.
+__device__ __forceinline__ int perm_phys(int s) {
+  const int g = s >> 3, j = s & 7;
+  return j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4);
+}
+
+// Storage slot of index p (0..31) in a permuted 32-block.
+__device__ __forceinline__ int perm_slot(int p) {
+  const int hi = p >> 4, r = p & 15;
+  return ((r >> 2) << 3) + (hi << 2) + (r & 3);
+}
+
+__device__ __forceinline__ uint16_t bf16_bits(float f) { return f32_to_bf16_rne(f); }
+
+__device__ __forceinline__ bf16x8 to_bf16x8(const float* v) {
+  bf16x8 r;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = static_cast<__bf16>(v[j]);
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 pack_acc(f32x4 lo, f32x4 hi) {
+  bf16x8 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    r[j] = static_cast<__bf16>(lo[j]);
+    r[4 + j] = static_cast<__bf16>(hi[j]);
+  }
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 lds_frag(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+}
+
+// Per-(chunk, head) record in the workspace. The first five fields are
+// copied to LDS as one contiguous block by the state kernel.
+template <int K, int V>
+struct Rec {
+  static constexpr size_t Wn = 0;                      // bf16 [C][K], -W, channels permuted
+  static constexpr size_t Qg = Wn + C * K * 2;         // bf16 [C][K], Q o e^gam, channels permuted
+  static constexpr size_t Pm = Qg + C * K * 2;         // bf16 [C][C], positions permuted
+  static constexpr size_t KgT = Pm + C * C * 2;        // bf16 [K][C], positions permuted
+  static constexpr size_t Eg = KgT + K * C * 2;        // fp32 [K], e^{gam_last}
+  static constexpr size_t lds_part = Eg + K * 4;       // bytes copied to LDS
+  static constexpr size_t Uf = (lds_part + 255) / 256 * 256;  // fp32 fragments [C/16][V/16][64][4]
+  static constexpr size_t bytes = (Uf + C * V * 4 + 255) / 256 * 256;
+};
+
+size_t header_bytes(int32_t num_seqs) {
+  return (static_cast<size_t>(num_seqs + 1) * 4 + 255) / 256 * 256;
+}
+
+__host__ __device__ inline int64_t max_chunks_for(int64_t num_tokens, int32_t num_seqs) {
+  return num_tokens / C + num_seqs;
+}
+
+// ------------------------------------------------------------------ plan --
+
+// chunk_start[i] = sum_{j<i} ceil(len_j / 64); chunk_start[N] = total chunks.
+__global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t* cu, int32_t N,
+                                                         int32_t* chunk_start) {
+  __shared__ int part[kThreads];
+  const int tid = threadIdx.x;
+  const int per = (N + kThreads - 1) / kThreads;
+  const int b = tid * per;
+  const int e = min(N, b + per);
+  int cnt = 0;
+  for (int i = b; i < e; ++i) cnt += (max(cu[i + 1] - cu[i], 0) + C - 1) / C;
+  part[tid] = cnt;
+  __syncthreads();
+  if (tid == 0) {
+    int acc = 0;
+    for (int k = 0; k < kThreads; ++k) {
+      const int x = part[k];
+      part[k] = acc;
+      acc += x;
+    }
+    chunk_start[N] = acc;
+  }
+  __syncthreads();
+  int acc = part[tid];
+  for (int i = b; i < e; ++i) {
+    chunk_start[i] = acc;
+    acc += (max(cu[i + 1] - cu[i], 0) + C - 1) / C;
+  }
+}
+
+// --------------------------------------------------------------- intra --
+
+template <int K, int V>
+struct IntraSmem {
+  static constexpr int KP = K + 8;   // padded bf16 row (breaks LDS bank conflicts)
+  static constexpr int VP = V + 8;
+  static constexpr int GP = K + 4;   // padded fp32 row
+  static constexpr int MP = C + 1;   // padded fp32 64x64 row
+  uint16_t k[C][KP];
+  uint16_t q[C][KP];                 // later: staging of -W for the copy-out
+  uint16_t v[C][VP];
+  float gam[C][GP];
+  float beta[C];
+  float A[C][MP];
+  float T[C][MP];
+  float P[C][MP];                    // later: scratch of the blocked inverse
+};
+
+template <int K, int V>
+__global__ __launch_bounds__(kThreads) void chunk_intra_kernel(const PrefillParams p,
+                                                               const int32_t* chunk_start,
+                                                               char* recs) {
+  using R = Rec<K, V>;
+  using SM = IntraSmem<K, V>;
+  __shared__ SM sm;
+
+  const int H = p.H;
+  const int c = static_cast<int>(blockIdx.x / H);
+  const int h = static_cast<int>(blockIdx.x % H);
+  const int N = p.num_seqs;
+  if (c >= chunk_start[N]) return;  // uniform: past the last chunk
+
+  // Which sequence owns chunk slot c: the last i with chunk_start[i] <= c.
+  int lo = 0, hi = N;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (chunk_start[mid] <= c) lo = mid; else hi = mid;
+  }
+  const int seq = lo;
+  const int64_t bos = p.cu_seqlens[seq];
+  const int64_t eos = p.cu_seqlens[seq + 1];
+  const int64_t t0 = bos + static_cast<int64_t>(C) * (c - chunk_start[seq]);
+  if (eos > p.num_tokens || t0 >= eos) return;  // malformed cu_seqlens: touch nothing
+  const int n = static_cast<int>(min<int64_t>(C, eos - t0));
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int m = lane & 15;
+  const int g = lane >> 4;
+
+  char* rec = recs + (static_cast<int64_t>(c) * H + h) * static_cast<int64_t>(R::bytes);
+
+  // ---- 1. inputs: k, q, v (bf16), beta, gate + cumulative sum ----------
+  for (int e = tid; e < C * (K / 8); e += kThreads) {
+    const int t = e / (K / 8), pc = e % (K / 8);
+    uint4 kv = make_uint4(0, 0, 0, 0), qv = make_uint4(0, 0, 0, 0);
+    if (t < n) {
+      const uint16_t* row = p.qkv + (t0 + t) * p.qkv_row_stride;
+      qv = *reinterpret_cast<const uint4*>(row + h * K + pc * 8);
+      kv = *reinterpret_cast<const uint4*>(row + H * K + h * K + pc * 8);
+    }
+    *reinterpret_cast<uint4*>(&sm.q[t][pc * 8]) = qv;
+    *reinterpret_cast<uint4*>(&sm.k[t][pc * 8]) = kv;
+  }
+  for (int e = tid; e < C * (V / 8); e += kThreads) {
+    const int t = e / (V / 8), pc = e % (V / 8);
+    uint4 vv = make_uint4(0, 0, 0, 0);
+    if (t < n)
+      vv = *reinterpret_cast<const uint4*>(p.qkv + (t0 + t) * p.qkv_row_stride + 2 * H * K + h * V + pc * 8);
+    *reinterpret_cast<uint4*>(&sm.v[t][pc * 8]) = vv;
+  }
+  if (tid < C)
+    sm.beta[tid] = tid < n ? sigmoid_f32(bf16_to_f32(p.raw_beta[(t0 + tid) * H + h])) : 0.f;
+  for (int e = tid; e < C * SM::MP; e += kThreads) {
+    (&sm.A[0][0])[e] = 0.f;
+    (&sm.T[0][0])[e] = 0.f;
+    (&sm.P[0][0])[e] = 0.f;
+  }
+  {
+    // Gate and inclusive cumulative sum along positions: thread (ch, part)
+    // scans PP positions; partial totals are then added across parts.
+    constexpr int PARTS = kThreads / K;
+    constexpr int PP = C / PARTS;
+    const int ch = tid % K, part = tid / K;
+    const float a = __expf(p.A_log[h]);
+    const float dtb = p.dt_bias[h * K + ch];
+    const bool has_lb = p.has_lb != 0;
+    float acc = 0.f;
+    for (int i = 0; i < PP; ++i) {
+      const int t = part * PP + i;
+      float gv = 0.f;  // padded positions do not decay, so row 63 holds gam_last
+      if (t < n)
+        gv = gate_log_decay(bf16_to_f32(p.raw_g[(t0 + t) * (H * K) + h * K + ch]), dtb, a,
+                            has_lb, p.lower_bound);
+      acc += gv;
+      sm.gam[t][ch] = acc;
+    }
+    __syncthreads();
+    float before = 0.f;
+    for (int q2 = 0; q2 < part; ++q2) before += sm.gam[(q2 + 1) * PP - 1][ch];
+    __syncthreads();
+    if (part > 0)
+      for (int i = 0; i < PP; ++i) sm.gam[part * PP + i][ch] += before;
+  }
+  __syncthreads();
+
+  // ---- 2. elementwise outputs: e^{gam_last}, Q o e^gam, (K o e^{gl-gam})^T
+  {
+    float* eg = reinterpret_cast<float*>(rec + R::Eg);
+    for (int ch = tid; ch < K; ch += kThreads) eg[ch] = __expf(sm.gam[C - 1][ch]);
+    uint16_t* qg = reinterpret_cast<uint16_t*>(rec + R::Qg);
+    for (int e = tid; e < C * (K / 8); e += kThreads) {
+      const int t = e / (K / 8), pc = e % (K / 8);
+      const int base = (pc >> 2) * 32;
+      float vals[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int ch = base + perm_phys((pc & 3) * 8 + j);
+        vals[j] = bf16_to_f32(sm.q[t][ch]) * __expf(sm.gam[t][ch]);
+      }
+      uint4 o;
+      o.x = pack_bf16x2(vals[0], vals[1]); o.y = pack_bf16x2(vals[2], vals[3]);
+      o.z = pack_bf16x2(vals[4], vals[5]); o.w = pack_bf16x2(vals[6], vals[7]);
+      *reinterpret_cast<uint4*>(qg + t * K + pc * 8) = o;
+    }
+    uint16_t* kgt = reinterpret_cast<uint16_t*>(rec + R::KgT);
+    for (int e = tid; e < K * (C / 8); e += kThreads) {
+      const int ch = e / (C / 8), pc = e % (C / 8);
+      const int base = (pc >> 2) * 32;
+      const float gl = sm.gam[C - 1][ch];
+      float vals[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int t = base + perm_phys((pc & 3) * 8 + j);
+        vals[j] = bf16_to_f32(sm.k[t][ch]) * __expf(gl - sm.gam[t][ch]);
+      }
+      uint4 o;
+      o.x = pack_bf16x2(vals[0], vals[1]); o.y = pack_bf16x2(vals[2], vals[3]);
+      o.z = pack_bf16x2(vals[4], vals[5]); o.w = pack_bf16x2(vals[6], vals[7]);
+      *reinterpret_cast<uint4*>(kgt + ch * C + pc * 8) = o;
+    }
+  }
+
+  // ---- 3a. diagonal 16x16 blocks of A and P, pairwise in fp32 ----------
+  {
+    constexpr int CQ = K / 4;   // channels per lane quarter
+    const int blk = w;          // wave w: diagonal block w
+    const int t = m;            // row within the block
+    const int cq = g;           // channel quarter
+    const int row = 16 * blk + t;
+    float gt[CQ], kt[CQ], qt[CQ];
+#pragma unroll
+    for (int i = 0; i < CQ; ++i) {
+      const int ch = cq * CQ + i;
+      gt[i] = sm.gam[row][ch];
+      kt[i] = bf16_to_f32(sm.k[row][ch]);
+      qt[i] = bf16_to_f32(sm.q[row][ch]);
+    }
+    float ares[16], pres[16];
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      const int srow = 16 * blk + s;
+      float av = 0.f, pv = 0.f;
+#pragma unroll
+      for (int i = 0; i < CQ; ++i) {
+        const int ch = cq * CQ + i;
+        // gam is non-increasing, so for s <= t the exponent is <= 0; the min
+        // only keeps the masked s > t entries finite.
+        const float e = __expf(fminf(gt[i] - sm.gam[srow][ch], 0.f));
+        const float ke = bf16_to_f32(sm.k[srow][ch]) * e;
+        av = fmaf(kt[i], ke, av);
+        pv = fmaf(qt[i], ke, pv);
+      }
+      ares[s] = av;
+      pres[s] = pv;
+    }
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      ares[s] += __shfl_xor(ares[s], 16);
+      ares[s] += __shfl_xor(ares[s], 32);
+      pres[s] += __shfl_xor(pres[s], 16);
+      pres[s] += __shfl_xor(pres[s], 32);
+    }
+    if (cq == 0) {
+      const float bt = sm.beta[row];
+#pragma unroll
+      for (int s = 0; s < 16; ++s) {
+        if (s < t) sm.A[row][16 * blk + s] = bt * ares[s];
+        if (s <= t) sm.P[row][16 * blk + s] = pres[s];
+      }
+    }
+  }
+
+  // ---- 3b. off-diagonal blocks (I > J) of A and P on MFMA --------------
+  // Reference r = 16 I: for t in block I and s in block J < I both factors
+  // e^{gam_t - gam_r} and e^{gam_r - gam_s} are <= 1.
+  {
+    const int pairs[4][2][2] = {{{1, 0}, {2, 1}}, {{2, 0}, {3, 2}}, {{3, 0}, {-1, -1}},
+                                {{3, 1}, {-1, -1}}};
+    for (int pi = 0; pi < 2; ++pi) {
+      const int I = pairs[w][pi][0], J = pairs[w][pi][1];
+      if (I < 0) break;
+      const int r = 16 * I;
+      f32x4 dA = {0.f, 0.f, 0.f, 0.f}, dP = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < K / 32; ++kb) {
+        float ak[8], aq[8], bk[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int ch = 32 * kb + 8 * g + j;
+          const float gr = sm.gam[r][ch];
+          const float ea = __expf(sm.gam[16 * I + m][ch] - gr);
+          ak[j] = bf16_to_f32(sm.k[16 * I + m][ch]) * ea;
+          aq[j] = bf16_to_f32(sm.q[16 * I + m][ch]) * ea;
+          bk[j] = bf16_to_f32(sm.k[16 * J + m][ch]) * __expf(gr - sm.gam[16 * J + m][ch]);
+        }
+        const bf16x8 b = to_bf16x8(bk);
+        dA = mfma16(to_bf16x8(ak), b, dA);
+        dP = mfma16(to_bf16x8(aq), b, dP);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = 16 * I + 4 * g + j;
+        sm.A[row][16 * J + m] = sm.beta[row] * dA[j];
+        sm.P[row][16 * J + m] = dP[j];
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- 4a. P -> workspace (bf16, positions permuted) --------------------
+  {
+    uint16_t* pm = reinterpret_cast<uint16_t*>(rec + R::Pm);
+    for (int e = tid; e < C * (C / 8); e += kThreads) {
+      const int t = e / (C / 8), pc = e % (C / 8);
+      const int base = (pc >> 2) * 32;
+      float vals[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) vals[j] = sm.P[t][base + perm_phys((pc & 3) * 8 + j)];
+      uint4 o;
+      o.x = pack_bf16x2(vals[0], vals[1]); o.y = pack_bf16x2(vals[2], vals[3]);
+      o.z = pack_bf16x2(vals[4], vals[5]); o.w = pack_bf16x2(vals[6], vals[7]);
+      *reinterpret_cast<uint4*>(pm + t * C + pc * 8) = o;
+    }
+  }
+  // ---- 4b. T = (I + A)^{-1}: diagonal blocks by forward substitution ----
+  if (lane < 16) {
+    const int blk = w, jc = lane;
+    float x[16];
+#pragma unroll
+    for (int tt = 0; tt < 16; ++tt) {
+      float v = (tt == jc) ? 1.f : 0.f;
+#pragma unroll
+      for (int s = 0; s < tt; ++s) v = fmaf(-sm.A[16 * blk + tt][16 * blk + s], x[s], v);
+      x[tt] = v;
+    }
+#pragma unroll
+    for (int tt = 0; tt < 16; ++tt) sm.T[16 * blk + tt][16 * blk + jc] = x[tt];
+  }
+  __syncthreads();
+  // ---- 4c. off-diagonal blocks of T, by distance from the diagonal -------
+  //   T_IJ = -T_II sum_{J<=L<I} A_IL T_LJ
+  {
+    float(*Y)[SM::MP] = sm.P;  // scratch: up to three 16x16 blocks side by side
+    const int rr = tid >> 4, cc = tid & 15;
+    for (int d = 1; d < 4; ++d) {
+      for (int I = d; I < 4; ++I) {
+        const int J = I - d;
+        float y = 0.f;
+        for (int L = J; L < I; ++L)
+#pragma unroll
+          for (int k2 = 0; k2 < 16; ++k2)
+            y = fmaf(sm.A[16 * I + rr][16 * L + k2], sm.T[16 * L + k2][16 * J + cc], y);
+        Y[rr][16 * (I - d) + cc] = y;
+      }
+      __syncthreads();
+      for (int I = d; I < 4; ++I) {
+        const int J = I - d;
+        float t2 = 0.f;
+#pragma unroll
+        for (int k2 = 0; k2 < 16; ++k2)
+          t2 = fmaf(sm.T[16 * I + rr][16 * I + k2], Y[k2][16 * (I - d) + cc], t2);
+        sm.T[16 * I + rr][16 * J + cc] = -t2;
+      }
+      __syncthreads();
+    }
+  }
+
+  // ---- 5. W = T diag(beta)(K o e^gam), U = T diag(beta) V on MFMA -------
+  // T is lower triangular, so rows 0..31 need only positions 0..31.
+  {
+    bf16x8 Tf[4][2];
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        float tv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) tv[j] = sm.T[16 * pb + m][32 * kb + 8 * g + j];
+        Tf[pb][kb] = to_bf16x8(tv);
+      }
+    // -W staged in sm.q (no longer read) with the channel permutation.
+    for (int nb = w; nb < K / 16; nb += 4) {
+      const int ch = 16 * nb + m;
+      bf16x8 Bf[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        float bv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int t = 32 * kb + 8 * g + j;
+          bv[j] = sm.beta[t] * bf16_to_f32(sm.k[t][ch]) * __expf(sm.gam[t][ch]);
+        }
+        Bf[kb] = to_bf16x8(bv);
+      }
+#pragma unroll
+      for (int pb = 0; pb < 4; ++pb) {
+        f32x4 D = mfma16(Tf[pb][0], Bf[0], f32x4{0.f, 0.f, 0.f, 0.f});
+        if (pb >= 2) D = mfma16(Tf[pb][1], Bf[1], D);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int row = 16 * pb + 4 * g + j;
+          const int col = 32 * (nb >> 1) + perm_slot(16 * (nb & 1) + m);
+          sm.q[row][col] = bf16_bits(-D[j]);
+        }
+      }
+    }
+    // U written straight out in accumulator fragment order.
+    f32x4* uf = reinterpret_cast<f32x4*>(rec + R::Uf);
+    for (int nb = w; nb < V / 16; nb += 4) {
+      const int col = 16 * nb + m;
+      bf16x8 Bv[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        float bv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int t = 32 * kb + 8 * g + j;
+          bv[j] = sm.beta[t] * bf16_to_f32(sm.v[t][col]);
+        }
+        Bv[kb] = to_bf16x8(bv);
+      }
+#pragma unroll
+      for (int pb = 0; pb < 4; ++pb) {
+        f32x4 D = mfma16(Tf[pb][0], Bv[0], f32x4{0.f, 0.f, 0.f, 0.f});
+        if (pb >= 2) D = mfma16(Tf[pb][1], Bv[1], D);
+        uf[(pb * (V / 16) + nb) * 64 + lane] = D;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- 6. -W -> workspace ----------------------------------------------
+  {
+    uint16_t* wn = reinterpret_cast<uint16_t*>(rec + R::Wn);
+    for (int e = tid; e < C * (K / 8); e += kThreads) {
+      const int t = e / (K / 8), pc = e % (K / 8);
+      *reinterpret_cast<uint4*>(wn + t * K + pc * 8) = *reinterpret_cast<const uint4*>(&sm.q[t][pc * 8]);
+    }
+  }
+}
+
+// --------------------------------------------------------------- state --
+
+template <int K, int V>
+struct StateBuf {
+  static constexpr int KP = K + 8;
+  static constexpr int CP = C + 8;
+  uint16_t wn[C][KP];
+  uint16_t qg[C][KP];
+  uint16_t pm[C][CP];
+  uint16_t kgt[K][CP];
+  float eg[K];
+};
+
+// Direct global -> LDS copy of chunk record c's LDS part into a padded
+// buffer. Each wave's global_load_lds_dwordx4 writes lane l's 16 bytes at
+// M0 + 16 l, so the buffer is walked slot by slot (64 slots per wave per
+// round) and every slot picks its source piece; padding slots read a valid
+// dummy piece. No registers hold the data, and the copy overlaps compute
+// until the next s_waitcnt vmcnt.
+template <int K, int V>
+__device__ __forceinline__ void dma_chunk(const char* rec, StateBuf<K, V>& b, int tid) {
+  using Bf = StateBuf<K, V>;
+  constexpr int KS = Bf::KP / 8, CS = Bf::CP / 8;  // 16-byte slots per padded row
+  constexpr int sW = C * KS, sQ = C * KS, sP = C * CS, sK = K * CS, sE = K / 4;
+  constexpr int total = sW + sQ + sP + sK + sE;
+  static_assert(sizeof(Bf) == static_cast<size_t>(total) * 16, "padded buffer must be whole slots");
+  const uint4* src = reinterpret_cast<const uint4*>(rec);
+  uint4* base = reinterpret_cast<uint4*>(&b);
+  const int wbase = tid & ~63;
+#pragma unroll 4
+  for (int r = 0; r < (total + kThreads - 1) / kThreads; ++r) {
+    const int slot = r * kThreads + tid;
+    if (slot < total) {
+      int piece = 0;  // dummy source for padding slots
+      int e = slot;
+      if (e < sW) {
+        if (e % KS < K / 8) piece = (e / KS) * (K / 8) + e % KS;
+      } else if ((e -= sW) < sQ) {
+        if (e % KS < K / 8) piece = C * K / 8 + (e / KS) * (K / 8) + e % KS;
+      } else if ((e -= sQ) < sP) {
+        if (e % CS < C / 8) piece = 2 * C * K / 8 + (e / CS) * (C / 8) + e % CS;
+      } else if ((e -= sP) < sK) {
+        if (e % CS < C / 8) piece = 2 * C * K / 8 + C * C / 8 + (e / CS) * (C / 8) + e % CS;
+      } else {
+        e -= sK;
+        piece = 2 * C * K / 8 + C * C / 8 + K * C / 8 + e;
+      }
+      __builtin_amdgcn_global_load_lds(src + piece, base + r * kThreads + wbase, 16, 0, 0);
+    }
+  }
+}
+
+// Waits until this wave's outstanding vector-memory operations (including
+// LDS DMA) have completed: vmcnt = 0, other counters unconstrained.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+template <int K, int V>
+__global__ __launch_bounds__(kThreads) void chunk_state_kernel(const PrefillParams p,
+                                                               const int32_t* chunk_start,
+                                                               const char* recs) {
+  using R = Rec<K, V>;
+  using B = StateBuf<K, V>;
+  static_assert(R::lds_part % 16 == 0, "record LDS part must be whole 16-byte pieces");
+  constexpr int NVH = V / 64;  // workgroups per (sequence, head): 64 columns each
+  __shared__ B buf[2];
+
+  // The NVH workgroups of one (sequence, head) read the same records: give
+  // them indices that are equal modulo 8 so they run on the same XCD (one L2).
+  const int bidx = blockIdx.x;
+  int pair, vh;
+  if constexpr (NVH == 2) {
+    pair = (bidx / 16) * 8 + (bidx % 8);
+    vh = (bidx / 8) % 2;
+  } else {
+    pair = bidx;
+    vh = 0;
+  }
+  const int H = p.H;
+  if (pair >= p.num_seqs * H) return;
+  const int seq = pair / H, h = pair % H;
+  const int64_t bos = p.cu_seqlens[seq];
+  const int64_t eos = p.cu_seqlens[seq + 1];
+  const int c0 = chunk_start[seq];
+  const int nch = chunk_start[seq + 1] - c0;
+  if (nch <= 0 || eos > p.num_tokens || bos < 0) return;
+  // Records exist for at most max_chunks chunks (sized from the host's token
+  // count); inconsistent cu_seqlens must not send us past them.
+  if (chunk_start[p.num_seqs] > max_chunks_for(p.num_tokens, p.num_seqs)) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int m = lane & 15;
+  const int g = lane >> 4;
+  const int col0 = vh * 64 + 16 * w;
+  const int64_t HV = static_cast<int64_t>(H) * V;
+
+  const int64_t slot = static_cast<int64_t>(p.indices[static_cast<int64_t>(seq) * p.index_stride]);
+  if (slot < 0) {
+    // Null slot: zero output rows, no state traffic.
+    for (int64_t t = bos; t < eos; ++t)
+      if (tid < 64) p.out[t * HV + h * V + vh * 64 + tid] = 0;
+    return;
+  }
+
+  float* st = p.pool + slot * p.slot_stride + static_cast<int64_t>(h) * K * V;
+  const bool init = p.has_initial_state == nullptr || p.has_initial_state[seq] != 0;
+  f32x4 S[K / 16];
+#pragma unroll
+  for (int cb = 0; cb < K / 16; ++cb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      S[cb][j] = init ? st[(16 * cb + 4 * g + j) * V + col0 + m] : 0.f;
+
+  f32x4 Upre[4];
+  auto rec_of = [&](int cc) {
+    return recs + (static_cast<int64_t>(c0 + cc) * H + h) * static_cast<int64_t>(R::bytes);
+  };
+  auto load_u = [&](int cc) {
+    const f32x4* uf = reinterpret_cast<const f32x4*>(rec_of(cc) + R::Uf);
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb) Upre[pb] = uf[(pb * (V / 16) + col0 / 16) * 64 + lane];
+  };
+  dma_chunk<K, V>(rec_of(0), buf[0], tid);
+  load_u(0);
+  const float scale = p.scale;
+  for (int cc = 0; cc < nch; ++cc) {
+    B& bf = buf[cc & 1];
+    // Chunk cc's buffer is complete once every wave's copy has landed; the
+    // barrier also means every wave is done with chunk cc-1's buffer, which
+    // the next copy overwrites.
+    wait_vmem();
+    __syncthreads();
+    f32x4 Vp[4];
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb) Vp[pb] = Upre[pb];
+    if (cc + 1 < nch) {
+      dma_chunk<K, V>(rec_of(cc + 1), buf[(cc + 1) & 1], tid);
+      load_u(cc + 1);
+    }
+
+    const int64_t t0 = bos + static_cast<int64_t>(C) * cc;
+    const int n = static_cast<int>(min<int64_t>(C, eos - t0));
+
+    // V' = U - W S and Q o e^gam S, contracting over channels.
+    bf16x8 Sb[K / 32];
+#pragma unroll
+    for (int kb = 0; kb < K / 32; ++kb) Sb[kb] = pack_acc(S[2 * kb], S[2 * kb + 1]);
+    f32x4 Ob[4];
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb) {
+      Ob[pb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < K / 32; ++kb) {
+        Vp[pb] = mfma16(lds_frag(&bf.wn[16 * pb + m][32 * kb + 8 * g]), Sb[kb], Vp[pb]);
+        Ob[pb] = mfma16(lds_frag(&bf.qg[16 * pb + m][32 * kb + 8 * g]), Sb[kb], Ob[pb]);
+      }
+    }
+    // V' as a B operand over positions.
+    const bf16x8 Vb0 = pack_acc(Vp[0], Vp[1]);
+    const bf16x8 Vb1 = pack_acc(Vp[2], Vp[3]);
+    // O += P V' (P is lower triangular: rows 0..31 need positions 0..31 only).
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb) {
+      Ob[pb] = mfma16(lds_frag(&bf.pm[16 * pb + m][8 * g]), Vb0, Ob[pb]);
+      if (pb >= 2) Ob[pb] = mfma16(lds_frag(&bf.pm[16 * pb + m][32 + 8 * g]), Vb1, Ob[pb]);
+    }
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int pos = 16 * pb + 4 * g + j;
+        if (pos < n) p.out[(t0 + pos) * HV + h * V + col0 + m] = f32_to_bf16_rne(scale * Ob[pb][j]);
+      }
+    // S <- diag(e^{gam_last}) S + (K o e^{gam_last - gam})^T V'.
+#pragma unroll
+    for (int cb = 0; cb < K / 16; ++cb) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) S[cb][j] *= bf.eg[16 * cb + 4 * g + j];
+      S[cb] = mfma16(lds_frag(&bf.kgt[16 * cb + m][8 * g]), Vb0, S[cb]);
+      S[cb] = mfma16(lds_frag(&bf.kgt[16 * cb + m][32 + 8 * g]), Vb1, S[cb]);
+    }
+  }
+
+#pragma unroll
+  for (int cb = 0; cb < K / 16; ++cb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) st[(16 * cb + 4 * g + j) * V + col0 + m] = S[cb][j];
+}
+
+template <int K, int V>
+hipError_t launch_kv(const PrefillParams& p, int32_t* chunk_start, char* recs, hipStream_t stream) {
+  const int64_t maxc = max_chunks_for(p.num_tokens, p.num_seqs);
+  const int64_t intra_blocks = maxc * p.H;
+  const int64_t pairs = static_cast<int64_t>(p.num_seqs) * p.H;
+  const int64_t state_blocks = (V / 64 == 2) ? (pairs + 7) / 8 * 16 : pairs;
+  if (intra_blocks > 0x7fffffff || state_blocks > 0x7fffffff) return hipErrorInvalidValue;
+  chunk_intra_kernel<K, V><<<dim3(static_cast<unsigned>(intra_blocks)), dim3(kThreads), 0, stream>>>(
+      p, chunk_start, recs);
+  chunk_state_kernel<K, V><<<dim3(static_cast<unsigned>(state_blocks)), dim3(kThreads), 0, stream>>>(
+      p, chunk_start, recs);
+  return hipGetLastError();
+}
+
+}  // namespace
+
 size_t prefill_workspace_bytes(int32_t num_seqs, int64_t num_tokens, int32_t H, int32_t K,
                                int32_t V) {
-  (void)K; (void)V;
-  const int64_t chunks = num_tokens / 64 + num_seqs;
-  return static_cast<size_t>(chunks) * H * 256 + 256;
+  size_t rec = 0;
+  if (K == 64 && V == 64) rec = Rec<64, 64>::bytes;
+  if (K == 64 && V == 128) rec = Rec<64, 128>::bytes;
+  if (K == 128 && V == 64) rec = Rec<128, 64>::bytes;
+  if (K == 128 && V == 128) rec = Rec<128, 128>::bytes;
+  return header_bytes(num_seqs) + static_cast<size_t>(max_chunks_for(num_tokens, num_seqs)) * H * rec;
 }
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
-  (void)p; (void)stream;
-  return hipErrorNotSupported;
+  int32_t* chunk_start = static_cast<int32_t*>(p.workspace);
+  char* recs = static_cast<char*>(p.workspace) + header_bytes(p.num_seqs);
+  plan_kernel<<<1, kThreads, 0, stream>>>(p.cu_seqlens, p.num_seqs, chunk_start);
+  if (p.K == 64 && p.V == 64) return launch_kv<64, 64>(p, chunk_start, recs, stream);
+  if (p.K == 64 && p.V == 128) return launch_kv<64, 128>(p, chunk_start, recs, stream);
+  if (p.K == 128 && p.V == 64) return launch_kv<128, 64>(p, chunk_start, recs, stream);
+  return launch_kv<128, 128>(p, chunk_start, recs, stream);
 }
 
 }  // namespace kda

@@ -257,16 +257,18 @@ static void gather_head(int32_t row0, int32_t n, int32_t h, int32_t H,
   }
 }
 
-/* One sequence of n rows starting at row0, on slot `slot` (< 0: null slot). */
-static void run_sequence(int32_t row0, int32_t n, int64_t slot, int32_t read_initial,
-                         int32_t H, int32_t K, int32_t V, const kda_oracle_args_t* a,
-                         int32_t form, double* out, double* final_state) {
+/* One (sequence, head) pair: n rows starting at row0, slot `slot` (< 0: null
+ * slot), head h. */
+static void run_sequence_head(int32_t row0, int32_t n, int64_t slot, int32_t read_initial,
+                              int32_t h, int32_t H, int32_t K, int32_t V,
+                              const kda_oracle_args_t* a, int32_t form, double* out,
+                              double* final_state) {
   if (n <= 0) return;
   if (slot < 0) {
     /* Null slot ([P3] Refusal and steps: padded requests): no pool access,
      * zero output rows. */
     for (int32_t t = 0; t < n; ++t)
-      for (int32_t x = 0; x < H * V; ++x) out[(int64_t)(row0 + t) * H * V + x] = 0.0;
+      for (int32_t j = 0; j < V; ++j) out[(int64_t)(row0 + t) * H * V + (int64_t)h * V + j] = 0.0;
     return;
   }
   double* q = (double*)malloc(sizeof(double) * (size_t)n * K);
@@ -276,23 +278,21 @@ static void run_sequence(int32_t row0, int32_t n, int64_t slot, int32_t read_ini
   double* o = (double*)malloc(sizeof(double) * (size_t)n * V);
   double* beta = (double*)malloc(sizeof(double) * (size_t)n);
   double* S = (double*)malloc(sizeof(double) * (size_t)K * V);
-  for (int32_t h = 0; h < H; ++h) {
-    float* tile = a->pool + slot * a->slot_stride + (int64_t)h * K * V;
-    for (int64_t x = 0; x < (int64_t)K * V; ++x) S[x] = read_initial ? (double)tile[x] : 0.0;
-    gather_head(row0, n, h, H, K, V, a->mixed_qkv, a->qkv_row_stride, a->raw_g,
-                a->raw_beta, a->A_log, a->dt_bias, a->has_lower_bound,
-                a->lower_bound, q, k, v, g, beta);
-    if (form <= 0)
-      kda_oracle_recurrent_pregated(n, K, V, q, k, v, g, beta, a->scale, S, o);
-    else
-      kda_oracle_chunked_pregated(n, K, V, form, q, k, v, g, beta, a->scale, S, o);
-    for (int32_t t = 0; t < n; ++t)
-      for (int32_t j = 0; j < V; ++j)
-        out[(int64_t)(row0 + t) * H * V + (int64_t)h * V + j] = o[(size_t)t * V + j];
-    for (int64_t x = 0; x < (int64_t)K * V; ++x) tile[x] = (float)S[x];
-    if (final_state)
-      memcpy(final_state + (int64_t)h * K * V, S, sizeof(double) * (size_t)K * V);
-  }
+  float* tile = a->pool + slot * a->slot_stride + (int64_t)h * K * V;
+  for (int64_t x = 0; x < (int64_t)K * V; ++x) S[x] = read_initial ? (double)tile[x] : 0.0;
+  gather_head(row0, n, h, H, K, V, a->mixed_qkv, a->qkv_row_stride, a->raw_g,
+              a->raw_beta, a->A_log, a->dt_bias, a->has_lower_bound,
+              a->lower_bound, q, k, v, g, beta);
+  if (form <= 0)
+    kda_oracle_recurrent_pregated(n, K, V, q, k, v, g, beta, a->scale, S, o);
+  else
+    kda_oracle_chunked_pregated(n, K, V, form, q, k, v, g, beta, a->scale, S, o);
+  for (int32_t t = 0; t < n; ++t)
+    for (int32_t j = 0; j < V; ++j)
+      out[(int64_t)(row0 + t) * H * V + (int64_t)h * V + j] = o[(size_t)t * V + j];
+  for (int64_t x = 0; x < (int64_t)K * V; ++x) tile[x] = (float)S[x];
+  if (final_state)
+    memcpy(final_state + (int64_t)h * K * V, S, sizeof(double) * (size_t)K * V);
   free(q); free(k); free(g); free(v); free(o); free(beta); free(S);
 }
 
@@ -321,13 +321,14 @@ int32_t kda_oracle_decode_packed(int32_t num_seqs, int32_t tokens_per_seq,
                                  const kda_oracle_args_t* a, int32_t form,
                                  double* out, double* final_state) {
   if (num_seqs < 0 || tokens_per_seq < 1 || H < 1 || K < 1 || V < 1) return 1;
+  if (final_state)
+    for (int64_t x = 0; x < (int64_t)num_seqs * H * K * V; ++x) final_state[x] = 0.0;
 #pragma omp parallel for schedule(dynamic, 1)
-  for (int32_t n = 0; n < num_seqs; ++n) {
+  for (int64_t nh = 0; nh < (int64_t)num_seqs * H; ++nh) {
+    int32_t n = (int32_t)(nh / H), h = (int32_t)(nh % H);
     int64_t slot = (int64_t)a->state_indices[(int64_t)n * a->index_stride];
     double* fs = final_state ? final_state + (int64_t)n * H * K * V : NULL;
-    if (fs && slot < 0)
-      for (int64_t x = 0; x < (int64_t)H * K * V; ++x) fs[x] = 0.0;
-    run_sequence(n * tokens_per_seq, tokens_per_seq, slot, 1, H, K, V, a, form, out, fs);
+    run_sequence_head(n * tokens_per_seq, tokens_per_seq, slot, 1, h, H, K, V, a, form, out, fs);
   }
   return 0;
 }
@@ -343,15 +344,16 @@ int32_t kda_oracle_prefill(int32_t num_seqs, const int32_t* cu_seqlens,
   if (num_seqs < 0 || H < 1 || K < 1 || V < 1) return 1;
   for (int32_t i = 0; i < num_seqs; ++i)
     if (cu_seqlens[i + 1] < cu_seqlens[i]) return 1;
+  if (final_state)
+    for (int64_t x = 0; x < (int64_t)num_seqs * H * K * V; ++x) final_state[x] = 0.0;
 #pragma omp parallel for schedule(dynamic, 1)
-  for (int32_t i = 0; i < num_seqs; ++i) {
+  for (int64_t ih = 0; ih < (int64_t)num_seqs * H; ++ih) {
+    int32_t i = (int32_t)(ih / H), h = (int32_t)(ih % H);
     int64_t slot = (int64_t)a->state_indices[(int64_t)i * a->index_stride];
     int32_t n = cu_seqlens[i + 1] - cu_seqlens[i];
     int32_t read_initial = has_initial_state ? (has_initial_state[i] != 0) : 1;
     double* fs = final_state ? final_state + (int64_t)i * H * K * V : NULL;
-    if (fs && (slot < 0 || n == 0))
-      for (int64_t x = 0; x < (int64_t)H * K * V; ++x) fs[x] = 0.0;
-    run_sequence(cu_seqlens[i], n, slot, read_initial, H, K, V, a, form, out, fs);
+    run_sequence_head(cu_seqlens[i], n, slot, read_initial, h, H, K, V, a, form, out, fs);
   }
   return 0;
 }

@@ -1,0 +1,182 @@
+"""GPU parity of the chunked prefill (chunk 64) and the mixed-batch router
+against the fp64 oracle.
+
+Chunked prefill with the WY recompute_w_u step and the rule that decode rows
+of a mixed batch go to the recurrent kernel come from vLLM PR #50649
+(Purpose); the length-1 cases target the NaN that page describes for
+length-1 sequences in the chunk kernel, and every output is scanned for
+non-finite or garbage-sized values (the ~1e38 values of its racy config).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_45_amd as kda
+import workloads as W
+from kda_testlib import (DECODE_TOL_O, DECODE_TOL_S, PREFILL_TOL_O, PREFILL_TOL_S, check_case, log,
+                         rel_err, run_gpu, to_device)
+from oracle import oracle as O
+
+pytestmark = pytest.mark.gpu
+
+RAGGED = [1, 5, 63, 64, 65, 130, 200, 1]
+
+
+@pytest.mark.parametrize("K,V", [(128, 128), (64, 64), (64, 128), (128, 64)])
+@pytest.mark.parametrize("lower_bound", [-5.0, None])
+def test_ragged_prefill(K, V, lower_bound):
+    case = W.prefill_case(f"ragged_k{K}_v{V}_lb{lower_bound}", 3, K, V, RAGGED, 16, lower_bound,
+                          seed=601 + K + V, std=0.1, scale=1.0 / math.sqrt(K))
+    check_case(case, PREFILL_TOL_O, PREFILL_TOL_S)
+
+
+def test_prefill_initial_state_flags_null_slot_and_empty_sequence():
+    lens = [70, 0, 33, 1, 128]
+    case = W.prefill_case("flags", 4, 128, 128, lens, 12, -5.0, seed=611, std=0.2,
+                          has_initial=[1, 1, 0, 1, 0], index_stride=3)
+    case.block_table[3, 0] = -1   # a padded request on the null slot
+    check_case(case, PREFILL_TOL_O, PREFILL_TOL_S)
+
+
+def test_prefill_single_long_sequence_8192():
+    check_case(W.prefill_8192(), PREFILL_TOL_O, PREFILL_TOL_S)
+
+
+def test_prefill_varlen_64_sequences():
+    check_case(W.prefill_varlen(), PREFILL_TOL_O, PREFILL_TOL_S)
+
+
+def test_prefill_varlen_no_lower_bound():
+    case = W.prefill_varlen(None)
+    check_case(case, PREFILL_TOL_O, PREFILL_TOL_S)
+
+
+def test_prefill_is_deterministic():
+    case = W.prefill_case("det", 8, 128, 128, [300, 77, 1], 8, -5.0, seed=621)
+    results = []
+    for _ in range(3):
+        dc = to_device(case)
+        out = run_gpu(dc).cpu()
+        results.append((out, dc.pool.cpu()))
+    for out, pool in results[1:]:
+        assert torch.equal(out, results[0][0]) and torch.equal(pool, results[0][1])
+    log("[case] prefill determinism: 3 runs bit-identical")
+
+
+def test_mixed_batch_4096():
+    check_case(W.mixed_4096(), PREFILL_TOL_O, PREFILL_TOL_S)
+
+
+def test_mixed_batch_decode_rows_match_decode_kernel():
+    """The decode rows of a mixed batch are bit-identical to a plain decode
+    call on the same rows (they take the recurrent kernel, not the chunk path)."""
+    case = W.mixed_case("mixed_vs_decode", 4, 128, 128, 9, [40, 1, 90], 40, -5.0, seed=631)
+    dc = to_device(case)
+    out_mixed = run_gpu(dc)
+    D = case.num_decodes
+    dc2 = to_device(case)
+    i = dc2.inputs
+    out_dec, _ = kda.kda_decode_packed(i["mixed_qkv"][:D], i["raw_g"][:D], i["raw_beta"][:D],
+                                       i["A_log"], i["dt_bias"], -5.0, dc2.pool,
+                                       dc2.state_indices[:D])
+    assert torch.equal(out_mixed[:D], out_dec)
+
+
+def _head_slice(case: W.Case, heads):
+    """The same case restricted to a subset of heads (heads are independent)."""
+    H, K, V = case.H, case.K, case.V
+    qkv = case.inputs["mixed_qkv"]
+    cols = ([h * K + i for h in heads for i in range(K)] +
+            [H * K + h * K + i for h in heads for i in range(K)] +
+            [2 * H * K + h * V + j for h in heads for j in range(V)])
+    inp = {
+        "mixed_qkv": qkv[:, cols].contiguous(),
+        "raw_g": case.inputs["raw_g"].view(-1, H, K)[:, heads].reshape(qkv.shape[0], -1).contiguous(),
+        "raw_beta": case.inputs["raw_beta"][:, heads].contiguous(),
+        "A_log": case.inputs["A_log"][heads].contiguous(),
+        "dt_bias": case.inputs["dt_bias"].view(H, K)[heads].reshape(-1).contiguous(),
+    }
+    return inp, case.pool[:, heads].contiguous()
+
+
+def test_prefill_65536_sampled_heads():
+    """One 65 536-token sequence at full size (all 32 heads on the GPU, as the
+    benchmark launches it); the oracle checks a sample of heads."""
+    case = W.prefill_65536()
+    dc = to_device(case)
+    out = run_gpu(dc)
+    heads = [0, 21]
+    inp, pool = _head_slice(case, heads)
+    ref_out, ref_fs, _ = O.prefill(inp, pool, case.state_indices, case.cu_seqlens.tolist(), len(heads),
+                                   case.K, case.V, lower_bound=case.lower_bound, return_pool=False)
+    got = out[:, heads].float().cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got))
+    e_o = rel_err(got, ref_out)
+    slot = int(case.state_indices[0])
+    got_s = dc.pool[slot, heads].cpu().numpy().astype(np.float64)
+    e_s = rel_err(got_s, ref_fs[0])
+    log(f"[case] prefill_t65536 heads {heads}: e_o={e_o:.3e} e_S={e_s:.3e}")
+    assert e_o <= PREFILL_TOL_O and e_s <= PREFILL_TOL_S
+
+
+@pytest.mark.parametrize("T", [1, 3, 8])
+def test_cross_path_decodes_prefill_spec_verify(T):
+    """T single-token decodes = one prefill of T = one spec-verify call of T
+    tokens (each against the oracle, and against each other)."""
+    case = W.prefill_case(f"cross_{T}", 8, 128, 128, [T], 4, -5.0, seed=641 + T, std=0.1)
+    dc = to_device(case)
+    out_pre = run_gpu(dc)
+    pool_pre = dc.pool.clone()
+    dc2 = to_device(case)
+    i = dc2.inputs
+    out_spec, _ = kda.kda_decode_packed(i["mixed_qkv"], i["raw_g"], i["raw_beta"], i["A_log"],
+                                        i["dt_bias"], -5.0, dc2.pool, dc2.state_indices,
+                                        tokens_per_seq=T)
+    dc3 = to_device(case)
+    i = dc3.inputs
+    outs = []
+    for t in range(T):
+        o, _ = kda.kda_decode_packed(i["mixed_qkv"][t:t + 1], i["raw_g"][t:t + 1],
+                                     i["raw_beta"][t:t + 1], i["A_log"], i["dt_bias"], -5.0,
+                                     dc3.pool, dc3.state_indices)
+        outs.append(o)
+    out_dec = torch.cat(outs)
+    torch.cuda.synchronize()
+    ref, ref_fs, _ = O.prefill(case.inputs, case.pool, case.state_indices, [0, T], 8, 128, 128,
+                               lower_bound=-5.0, return_pool=False)
+    slot = int(case.state_indices[0])
+    for name, o, pool, tol in (("prefill", out_pre, pool_pre, PREFILL_TOL_O),
+                               ("spec", out_spec, dc2.pool, DECODE_TOL_O * 2),
+                               ("decodes", out_dec, dc3.pool, DECODE_TOL_O * 2)):
+        e = rel_err(o.float().cpu().numpy(), ref)
+        es = rel_err(pool[slot].cpu().numpy().astype(np.float64), ref_fs[0])
+        log(f"[case] cross T={T} {name}: e_o={e:.3e} e_S={es:.3e}")
+        assert e <= tol and es <= PREFILL_TOL_S
+    # Spec-verify and T single decodes run the same recurrence in fp32.
+    e = rel_err(out_spec.float().cpu().numpy(), out_dec.float().cpu().numpy().astype(np.float64))
+    assert e <= DECODE_TOL_O * 2
+
+
+def test_prefill_split_equals_whole():
+    T1, T2 = 100, 93
+    case = W.prefill_case("split", 4, 128, 128, [T1 + T2], 4, -5.0, seed=651)
+    dc = to_device(case)
+    out_whole = run_gpu(dc)
+    pool_whole = dc.pool.clone()
+    dc2 = to_device(case)
+    i = dc2.inputs
+    cu1 = torch.tensor([0, T1], dtype=torch.int32, device="cuda")
+    cu2 = torch.tensor([0, T2], dtype=torch.int32, device="cuda")
+    o1, _ = kda.kda_chunk_prefill(i["mixed_qkv"][:T1], i["raw_g"][:T1], i["raw_beta"][:T1],
+                                  i["A_log"], i["dt_bias"], -5.0, dc2.pool, dc2.state_indices, cu1)
+    o2, _ = kda.kda_chunk_prefill(i["mixed_qkv"][T1:].contiguous(), i["raw_g"][T1:].contiguous(),
+                                  i["raw_beta"][T1:].contiguous(), i["A_log"], i["dt_bias"], -5.0,
+                                  dc2.pool, dc2.state_indices, cu2)
+    torch.cuda.synchronize()
+    e = rel_err(torch.cat([o1, o2]).float().cpu().numpy(), out_whole.float().cpu().numpy().astype(np.float64))
+    slot = int(case.state_indices[0])
+    es = rel_err(dc2.pool[slot].cpu().numpy(), pool_whole[slot].cpu().numpy().astype(np.float64))
+    log(f"[case] split vs whole: e_o={e:.3e} e_S={es:.3e}")
+    assert e <= PREFILL_TOL_O and es <= PREFILL_TOL_S
