@@ -193,18 +193,26 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_kernel(const PrefillPara
 
   char* rec = recs + (static_cast<int64_t>(c) * H + h) * static_cast<int64_t>(R::bytes);
 
-  // ---- 1. inputs: k, q, v (bf16), beta, gate + cumulative sum ----------
+  // ---- 1. inputs: k, q, v, raw_g (bf16), beta; gate + cumulative sum ----
+  // All global loads are issued back to back; raw_g is staged in the P
+  // region (free until the A/P phase) as bf16 [C][K].
+  uint16_t* rawg = reinterpret_cast<uint16_t*>(&sm.P[0][0]);
+  static_assert(sizeof(sm.P) >= sizeof(uint16_t) * C * K, "raw_g staging must fit in P");
+#pragma unroll
   for (int e = tid; e < C * (K / 8); e += kThreads) {
     const int t = e / (K / 8), pc = e % (K / 8);
-    uint4 kv = make_uint4(0, 0, 0, 0), qv = make_uint4(0, 0, 0, 0);
+    uint4 kv = make_uint4(0, 0, 0, 0), qv = kv, gv = kv;
     if (t < n) {
       const uint16_t* row = p.qkv + (t0 + t) * p.qkv_row_stride;
       qv = *reinterpret_cast<const uint4*>(row + h * K + pc * 8);
       kv = *reinterpret_cast<const uint4*>(row + H * K + h * K + pc * 8);
+      gv = *reinterpret_cast<const uint4*>(p.raw_g + (t0 + t) * (H * K) + h * K + pc * 8);
     }
     *reinterpret_cast<uint4*>(&sm.q[t][pc * 8]) = qv;
     *reinterpret_cast<uint4*>(&sm.k[t][pc * 8]) = kv;
+    *reinterpret_cast<uint4*>(&rawg[t * K + pc * 8]) = gv;
   }
+#pragma unroll
   for (int e = tid; e < C * (V / 8); e += kThreads) {
     const int t = e / (V / 8), pc = e % (V / 8);
     uint4 vv = make_uint4(0, 0, 0, 0);
@@ -217,8 +225,8 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_kernel(const PrefillPara
   for (int e = tid; e < C * SM::MP; e += kThreads) {
     (&sm.A[0][0])[e] = 0.f;
     (&sm.T[0][0])[e] = 0.f;
-    (&sm.P[0][0])[e] = 0.f;
   }
+  __syncthreads();
   {
     // Gate and inclusive cumulative sum along positions: thread (ch, part)
     // scans PP positions; partial totals are then added across parts.
@@ -229,18 +237,19 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_kernel(const PrefillPara
     const float dtb = p.dt_bias[h * K + ch];
     const bool has_lb = p.has_lb != 0;
     float acc = 0.f;
+#pragma unroll 8
     for (int i = 0; i < PP; ++i) {
       const int t = part * PP + i;
       float gv = 0.f;  // padded positions do not decay, so row 63 holds gam_last
-      if (t < n)
-        gv = gate_log_decay(bf16_to_f32(p.raw_g[(t0 + t) * (H * K) + h * K + ch]), dtb, a,
-                            has_lb, p.lower_bound);
+      if (t < n) gv = gate_log_decay(bf16_to_f32(rawg[t * K + ch]), dtb, a, has_lb, p.lower_bound);
       acc += gv;
       sm.gam[t][ch] = acc;
     }
     __syncthreads();
     float before = 0.f;
     for (int q2 = 0; q2 < part; ++q2) before += sm.gam[(q2 + 1) * PP - 1][ch];
+    // raw_g has been consumed: the P region becomes P (zeroed).
+    for (int e = tid; e < C * SM::MP; e += kThreads) (&sm.P[0][0])[e] = 0.f;
     __syncthreads();
     if (part > 0)
       for (int i = 0; i < PP; ++i) sm.gam[part * PP + i][ch] += before;
