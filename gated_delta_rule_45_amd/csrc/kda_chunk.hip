@@ -83,6 +83,18 @@ __device__ __forceinline__ bf16x8 pack_acc(f32x4 lo, f32x4 hi) {
   return r;
 }
 
+// Residual of pack_acc: the bf16 rounding of (acc - hi), so hi + lo carries
+// about 16 significant bits of the fp32 accumulators.
+__device__ __forceinline__ bf16x8 pack_lo(f32x4 lo, f32x4 hi, bf16x8 h) {
+  bf16x8 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    r[j] = static_cast<__bf16>(lo[j] - static_cast<float>(h[j]));
+    r[4 + j] = static_cast<__bf16>(hi[j] - static_cast<float>(h[4 + j]));
+  }
+  return r;
+}
+
 __device__ __forceinline__ bf16x8 lds_frag(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
 }
@@ -100,6 +112,10 @@ struct Rec {
   static constexpr size_t Uf = (lds_part + 255) / 256 * 256;  // fp32 fragments [C/16][V/16][64][4]
   static constexpr size_t bytes = (Uf + C * V * 4 + 255) / 256 * 256;
 };
+
+// Waits until this wave's outstanding vector-memory operations (including
+// LDS DMA) have completed: vmcnt = 0, other counters unconstrained.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 size_t header_bytes(int32_t num_seqs) {
   return (static_cast<size_t>(num_seqs + 1) * 4 + 255) / 256 * 256;
@@ -142,26 +158,41 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t* cu, int32
 
 // --------------------------------------------------------------- intra --
 
+// Element offsets in XOR-swizzled row-major LDS tiles: the 16-byte pieces of
+// row t are permuted by t, so the 16 rows an MFMA fragment touches fall in
+// different banks (no padding, which keeps two workgroups per CU).
+template <int N>  // bf16 tile [C][N]: 8 elements per piece
+__device__ __forceinline__ int sw16(int t, int c) {
+  constexpr int PM = (N / 8 > 16 ? 16 : N / 8) - 1;
+  return t * N + ((((c >> 3) ^ (t & PM)) << 3) | (c & 7));
+}
+template <int N>  // fp32 tile [C][N]: 4 elements per piece
+__device__ __forceinline__ int sw32(int t, int c) {
+  constexpr int PM = (N / 4 > 16 ? 16 : N / 4) - 1;
+  return t * N + ((((c >> 2) ^ (t & PM)) << 2) | (c & 3));
+}
+
+// Intra-kernel LDS: 80 KiB at K = 128, so two workgroups share a CU.
+//  k    bf16 [C][K]  keys of the chunk (zero rows past its end)
+//  q    bf16 [C][K]  queries; after the A/P phase: scratch of the blocked
+//                    inverse, then -W for the coalesced copy-out
+//  gam  fp32 [C][K]  cumulative log-decay
+//  at   fp32 [C][C]  raw_g (bf16 [C][K]) at load time; then A^T strictly
+//                    above the diagonal (at(s,t) = A[t][s]), T = (I + A)^{-1}
+//                    strictly below it (unit diagonal implicit), beta on it
 template <int K, int V>
 struct IntraSmem {
-  static constexpr int KP = K + 8;   // padded bf16 row (breaks LDS bank conflicts)
-  static constexpr int VP = V + 8;
-  static constexpr int GP = K + 4;   // padded fp32 row
-  static constexpr int MP = C + 1;   // padded fp32 64x64 row
-  uint16_t k[C][KP];
-  uint16_t q[C][KP];                 // later: staging of -W for the copy-out
-  uint16_t v[C][VP];
-  float gam[C][GP];
-  float beta[C];
-  float A[C][MP];
-  float T[C][MP];
-  float P[C][MP];                    // later: scratch of the blocked inverse
+  uint16_t k[C * K];
+  uint16_t q[C * K];
+  float gam[C * K];
+  float at[C * C];
+  static_assert(sizeof(float) * C * C >= sizeof(uint16_t) * C * K, "raw_g staging must fit in at");
 };
 
 template <int K, int V>
-__global__ __launch_bounds__(kThreads) void chunk_intra_kernel(const PrefillParams p,
-                                                               const int32_t* chunk_start,
-                                                               char* recs) {
+__global__ __launch_bounds__(kThreads, 2) void chunk_intra_kernel(const PrefillParams p,
+                                                                  const int32_t* chunk_start,
+                                                                  char* recs) {
   using R = Rec<K, V>;
   using SM = IntraSmem<K, V>;
   __shared__ SM sm;
@@ -190,42 +221,30 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_kernel(const PrefillPara
   const int w = tid >> 6;
   const int m = lane & 15;
   const int g = lane >> 4;
+  constexpr int KP8 = K / 8;                     // 16-byte pieces per bf16 row
+  constexpr int KPM = (KP8 > 16 ? 16 : KP8) - 1;
 
   char* rec = recs + (static_cast<int64_t>(c) * H + h) * static_cast<int64_t>(R::bytes);
 
-  // ---- 1. inputs: k, q, v, raw_g (bf16), beta; gate + cumulative sum ----
-  // All global loads are issued back to back; raw_g is staged in the P
-  // region (free until the A/P phase) as bf16 [C][K].
-  uint16_t* rawg = reinterpret_cast<uint16_t*>(&sm.P[0][0]);
-  static_assert(sizeof(sm.P) >= sizeof(uint16_t) * C * K, "raw_g staging must fit in P");
+  // ---- 1. k, q and raw_g tiles by LDS DMA; rows past the chunk end read 0
+  uint16_t* rawg = reinterpret_cast<uint16_t*>(sm.at);
+  {
+    const int64_t rs = p.qkv_row_stride * 2;  // bytes per mixed_qkv row
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.qkv + t0 * p.qkv_row_stride, static_cast<uint32_t>(n * rs));
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.raw_g + t0 * (H * K), static_cast<uint32_t>(n * H * K * 2));
 #pragma unroll
-  for (int e = tid; e < C * (K / 8); e += kThreads) {
-    const int t = e / (K / 8), pc = e % (K / 8);
-    uint4 kv = make_uint4(0, 0, 0, 0), qv = kv, gv = kv;
-    if (t < n) {
-      const uint16_t* row = p.qkv + (t0 + t) * p.qkv_row_stride;
-      qv = *reinterpret_cast<const uint4*>(row + h * K + pc * 8);
-      kv = *reinterpret_cast<const uint4*>(row + H * K + h * K + pc * 8);
-      gv = *reinterpret_cast<const uint4*>(p.raw_g + (t0 + t) * (H * K) + h * K + pc * 8);
+    for (int r = 0; r < C * KP8 / kThreads; ++r) {
+      const int ps = r * kThreads + tid;          // physical piece in the tile
+      const int t = ps / KP8;
+      const int pl = (ps % KP8) ^ (t & KPM);      // logical piece stored there
+      const int slot = r * kThreads + (tid & ~63);
+      const int qoff = static_cast<int>(t * rs) + (h * K + pl * 8) * 2;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, reinterpret_cast<uint4*>(sm.q) + slot, 16, qoff, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, reinterpret_cast<uint4*>(sm.k) + slot, 16, qoff + H * K * 2, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rg, reinterpret_cast<uint4*>(rawg) + slot, 16, (t * H * K + h * K + pl * 8) * 2, 0, 0, 0);
     }
-    *reinterpret_cast<uint4*>(&sm.q[t][pc * 8]) = qv;
-    *reinterpret_cast<uint4*>(&sm.k[t][pc * 8]) = kv;
-    *reinterpret_cast<uint4*>(&rawg[t * K + pc * 8]) = gv;
   }
-#pragma unroll
-  for (int e = tid; e < C * (V / 8); e += kThreads) {
-    const int t = e / (V / 8), pc = e % (V / 8);
-    uint4 vv = make_uint4(0, 0, 0, 0);
-    if (t < n)
-      vv = *reinterpret_cast<const uint4*>(p.qkv + (t0 + t) * p.qkv_row_stride + 2 * H * K + h * V + pc * 8);
-    *reinterpret_cast<uint4*>(&sm.v[t][pc * 8]) = vv;
-  }
-  if (tid < C)
-    sm.beta[tid] = tid < n ? sigmoid_f32(bf16_to_f32(p.raw_beta[(t0 + tid) * H + h])) : 0.f;
-  for (int e = tid; e < C * SM::MP; e += kThreads) {
-    (&sm.A[0][0])[e] = 0.f;
-    (&sm.T[0][0])[e] = 0.f;
-  }
+  wait_vmem();
   __syncthreads();
   {
     // Gate and inclusive cumulative sum along positions: thread (ch, part)
@@ -241,34 +260,44 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_kernel(const PrefillPara
     for (int i = 0; i < PP; ++i) {
       const int t = part * PP + i;
       float gv = 0.f;  // padded positions do not decay, so row 63 holds gam_last
-      if (t < n) gv = gate_log_decay(bf16_to_f32(rawg[t * K + ch]), dtb, a, has_lb, p.lower_bound);
+      if (t < n) gv = gate_log_decay(bf16_to_f32(rawg[sw16<K>(t, ch)]), dtb, a, has_lb, p.lower_bound);
       acc += gv;
-      sm.gam[t][ch] = acc;
+      sm.gam[sw32<K>(t, ch)] = acc;
     }
-    __syncthreads();
+    const float beta_t = (tid < n) ? sigmoid_f32(bf16_to_f32(p.raw_beta[(t0 + tid) * H + h])) : 0.f;
+    lds_barrier();  // raw_g fully consumed; partial sums visible
     float before = 0.f;
-    for (int q2 = 0; q2 < part; ++q2) before += sm.gam[(q2 + 1) * PP - 1][ch];
-    // raw_g has been consumed: the P region becomes P (zeroed).
-    for (int e = tid; e < C * SM::MP; e += kThreads) (&sm.P[0][0])[e] = 0.f;
-    __syncthreads();
+    for (int q2 = 0; q2 < part; ++q2) before += sm.gam[sw32<K>((q2 + 1) * PP - 1, ch)];
+    if (tid < C) sm.at[sw32<C>(tid, tid)] = beta_t;  // beta on the diagonal of at
+    lds_barrier();
     if (part > 0)
-      for (int i = 0; i < PP; ++i) sm.gam[part * PP + i][ch] += before;
+      for (int i = 0; i < PP; ++i) sm.gam[sw32<K>(part * PP + i, ch)] += before;
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- 2. elementwise outputs: e^{gam_last}, Q o e^gam, (K o e^{gl-gam})^T
   {
     float* eg = reinterpret_cast<float*>(rec + R::Eg);
-    for (int ch = tid; ch < K; ch += kThreads) eg[ch] = __expf(sm.gam[C - 1][ch]);
+    for (int ch = tid; ch < K; ch += kThreads) eg[ch] = __expf(sm.gam[sw32<K>(C - 1, ch)]);
     uint16_t* qg = reinterpret_cast<uint16_t*>(rec + R::Qg);
-    for (int e = tid; e < C * (K / 8); e += kThreads) {
-      const int t = e / (K / 8), pc = e % (K / 8);
-      const int base = (pc >> 2) * 32;
-      float vals[8];
+    for (int e = tid; e < C * KP8; e += kThreads) {
+      const int t = e / KP8, pc = e % KP8;
+      const int cb = (pc >> 2) * 32 + 4 * (pc & 3);  // storage piece pc holds channels cb..cb+3, cb+16..cb+19
+      float qv[8], vals[8];
+      {
+        const uint2 w0 = *reinterpret_cast<const uint2*>(&sm.q[sw16<K>(t, cb)]);
+        const uint2 w1 = *reinterpret_cast<const uint2*>(&sm.q[sw16<K>(t, cb + 16)]);
+        qv[0] = __uint_as_float(w0.x << 16); qv[1] = __uint_as_float(w0.x & 0xffff0000u);
+        qv[2] = __uint_as_float(w0.y << 16); qv[3] = __uint_as_float(w0.y & 0xffff0000u);
+        qv[4] = __uint_as_float(w1.x << 16); qv[5] = __uint_as_float(w1.x & 0xffff0000u);
+        qv[6] = __uint_as_float(w1.y << 16); qv[7] = __uint_as_float(w1.y & 0xffff0000u);
+      }
+      const f32x4 g0 = *reinterpret_cast<const f32x4*>(&sm.gam[sw32<K>(t, cb)]);
+      const f32x4 g1 = *reinterpret_cast<const f32x4*>(&sm.gam[sw32<K>(t, cb + 16)]);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int ch = base + perm_phys((pc & 3) * 8 + j);
-        vals[j] = bf16_to_f32(sm.q[t][ch]) * __expf(sm.gam[t][ch]);
+      for (int j = 0; j < 4; ++j) {
+        vals[j] = qv[j] * __expf(g0[j]);
+        vals[4 + j] = qv[4 + j] * __expf(g1[j]);
       }
       uint4 o;
       o.x = pack_bf16x2(vals[0], vals[1]); o.y = pack_bf16x2(vals[2], vals[3]);
@@ -279,12 +308,12 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_kernel(const PrefillPara
     for (int e = tid; e < K * (C / 8); e += kThreads) {
       const int ch = e / (C / 8), pc = e % (C / 8);
       const int base = (pc >> 2) * 32;
-      const float gl = sm.gam[C - 1][ch];
+      const float gl = sm.gam[sw32<K>(C - 1, ch)];
       float vals[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int t = base + perm_phys((pc & 3) * 8 + j);
-        vals[j] = bf16_to_f32(sm.k[t][ch]) * __expf(gl - sm.gam[t][ch]);
+        vals[j] = bf16_to_f32(sm.k[sw16<K>(t, ch)]) * __expf(gl - sm.gam[sw32<K>(t, ch)]);
       }
       uint4 o;
       o.x = pack_bf16x2(vals[0], vals[1]); o.y = pack_bf16x2(vals[2], vals[3]);
@@ -293,109 +322,155 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_kernel(const PrefillPara
     }
   }
 
-  // ---- 3a. diagonal 16x16 blocks of A and P, pairwise in fp32 ----------
-  {
-    constexpr int CQ = K / 4;   // channels per lane quarter
-    const int blk = w;          // wave w: diagonal block w
-    const int t = m;            // row within the block
-    const int cq = g;           // channel quarter
-    const int row = 16 * blk + t;
-    float gt[CQ], kt[CQ], qt[CQ];
-#pragma unroll
-    for (int i = 0; i < CQ; ++i) {
-      const int ch = cq * CQ + i;
-      gt[i] = sm.gam[row][ch];
-      kt[i] = bf16_to_f32(sm.k[row][ch]);
-      qt[i] = bf16_to_f32(sm.q[row][ch]);
-    }
-    float ares[16], pres[16];
-#pragma unroll
-    for (int s = 0; s < 16; ++s) {
-      const int srow = 16 * blk + s;
-      float av = 0.f, pv = 0.f;
-#pragma unroll
-      for (int i = 0; i < CQ; ++i) {
-        const int ch = cq * CQ + i;
-        // gam is non-increasing, so for s <= t the exponent is <= 0; the min
-        // only keeps the masked s > t entries finite.
-        const float e = __expf(fminf(gt[i] - sm.gam[srow][ch], 0.f));
-        const float ke = bf16_to_f32(sm.k[srow][ch]) * e;
-        av = fmaf(kt[i], ke, av);
-        pv = fmaf(qt[i], ke, pv);
-      }
-      ares[s] = av;
-      pres[s] = pv;
-    }
-#pragma unroll
-    for (int s = 0; s < 16; ++s) {
-      ares[s] += __shfl_xor(ares[s], 16);
-      ares[s] += __shfl_xor(ares[s], 32);
-      pres[s] += __shfl_xor(pres[s], 16);
-      pres[s] += __shfl_xor(pres[s], 32);
-    }
-    if (cq == 0) {
-      const float bt = sm.beta[row];
-#pragma unroll
-      for (int s = 0; s < 16; ++s) {
-        if (s < t) sm.A[row][16 * blk + s] = bt * ares[s];
-        if (s <= t) sm.P[row][16 * blk + s] = pres[s];
-      }
-    }
-  }
-
-  // ---- 3b. off-diagonal blocks (I > J) of A and P on MFMA --------------
-  // Reference r = 16 I: for t in block I and s in block J < I both factors
-  // e^{gam_t - gam_r} and e^{gam_r - gam_s} are <= 1.
-  {
-    const int pairs[4][2][2] = {{{1, 0}, {2, 1}}, {{2, 0}, {3, 2}}, {{3, 0}, {-1, -1}},
-                                {{3, 1}, {-1, -1}}};
-    for (int pi = 0; pi < 2; ++pi) {
-      const int I = pairs[w][pi][0], J = pairs[w][pi][1];
-      if (I < 0) break;
-      const int r = 16 * I;
-      f32x4 dA = {0.f, 0.f, 0.f, 0.f}, dP = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < K / 32; ++kb) {
-        float ak[8], aq[8], bk[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int ch = 32 * kb + 8 * g + j;
-          const float gr = sm.gam[r][ch];
-          const float ea = __expf(sm.gam[16 * I + m][ch] - gr);
-          ak[j] = bf16_to_f32(sm.k[16 * I + m][ch]) * ea;
-          aq[j] = bf16_to_f32(sm.q[16 * I + m][ch]) * ea;
-          bk[j] = bf16_to_f32(sm.k[16 * J + m][ch]) * __expf(gr - sm.gam[16 * J + m][ch]);
-        }
-        const bf16x8 b = to_bf16x8(bk);
-        dA = mfma16(to_bf16x8(ak), b, dA);
-        dP = mfma16(to_bf16x8(aq), b, dP);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = 16 * I + 4 * g + j;
-        sm.A[row][16 * J + m] = sm.beta[row] * dA[j];
-        sm.P[row][16 * J + m] = dP[j];
-      }
-    }
-  }
-  __syncthreads();
-
-  // ---- 4a. P -> workspace (bf16, positions permuted) --------------------
+  // ---- 3. A and P by 16x16 blocks (I, J), J <= I --------------------------
+  // Fast path for block-row I: one reference row r = 16 I + 7. For s in an
+  // earlier block e^{gam_r - gam_s} <= 1; inside block I every factor lies
+  // within e^{+-D}, D = the block's largest decay range over channels. If
+  // D <= 80 every factor fits bf16 and every product with s <= t equals
+  // e^{gam_t - gam_s} <= 1, so the whole block-row runs on MFMA. Otherwise
+  // the exact scheme: reference 16 I for J < I (both factors <= 1) and
+  // pairwise fp32 exponentials on the diagonal block.
+  // A goes transposed into at (strictly above the diagonal); P goes straight
+  // to the workspace (bf16, positions permuted), including the zero blocks
+  // above the diagonal that the state kernel reads.
   {
     uint16_t* pm = reinterpret_cast<uint16_t*>(rec + R::Pm);
-    for (int e = tid; e < C * (C / 8); e += kThreads) {
-      const int t = e / (C / 8), pc = e % (C / 8);
-      const int base = (pc >> 2) * 32;
-      float vals[8];
+    const int blocks[4][3][2] = {{{3, 3}, {3, 0}, {0, 0}},
+                                 {{2, 2}, {3, 1}, {1, 0}},
+                                 {{1, 1}, {3, 2}, {-1, -1}},
+                                 {{2, 1}, {2, 0}, {-1, -1}}};
+    for (int bi = 0; bi < 3; ++bi) {
+      const int I = blocks[w][bi][0], J = blocks[w][bi][1];
+      if (I < 0) break;
+      float dloc = 0.f;
+      for (int ch = lane; ch < K; ch += 64)
+        dloc = fmaxf(dloc, sm.gam[sw32<K>(16 * I, ch)] - sm.gam[sw32<K>(16 * I + 15, ch)]);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) vals[j] = sm.P[t][base + perm_phys((pc & 3) * 8 + j)];
-      uint4 o;
-      o.x = pack_bf16x2(vals[0], vals[1]); o.y = pack_bf16x2(vals[2], vals[3]);
-      o.z = pack_bf16x2(vals[4], vals[5]); o.w = pack_bf16x2(vals[6], vals[7]);
-      *reinterpret_cast<uint4*>(pm + t * C + pc * 8) = o;
+      for (int off = 32; off > 0; off >>= 1) dloc = fmaxf(dloc, __shfl_xor(dloc, off));
+      const bool fast = dloc <= 80.f;  // wave-uniform after the butterfly
+      if (J < I || fast) {
+        const int r = fast ? 16 * I + 7 : 16 * I;
+        f32x4 dA = {0.f, 0.f, 0.f, 0.f}, dP = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < K / 32; ++kb) {
+          const int c0 = 32 * kb + 8 * g;
+          const uint4 ka = *reinterpret_cast<const uint4*>(&sm.k[sw16<K>(16 * I + m, c0)]);
+          const uint4 kbv = *reinterpret_cast<const uint4*>(&sm.k[sw16<K>(16 * J + m, c0)]);
+          const uint4 qav = *reinterpret_cast<const uint4*>(&sm.q[sw16<K>(16 * I + m, c0)]);
+          const uint32_t qaw[4] = {qav.x, qav.y, qav.z, qav.w};
+          const f32x4 gt0 = *reinterpret_cast<const f32x4*>(&sm.gam[sw32<K>(16 * I + m, c0)]);
+          const f32x4 gt1 = *reinterpret_cast<const f32x4*>(&sm.gam[sw32<K>(16 * I + m, c0 + 4)]);
+          const f32x4 gr0 = *reinterpret_cast<const f32x4*>(&sm.gam[sw32<K>(r, c0)]);
+          const f32x4 gr1 = *reinterpret_cast<const f32x4*>(&sm.gam[sw32<K>(r, c0 + 4)]);
+          const f32x4 gs0 = *reinterpret_cast<const f32x4*>(&sm.gam[sw32<K>(16 * J + m, c0)]);
+          const f32x4 gs1 = *reinterpret_cast<const f32x4*>(&sm.gam[sw32<K>(16 * J + m, c0 + 4)]);
+          const uint32_t kaw[4] = {ka.x, ka.y, ka.z, ka.w};
+          const uint32_t kbw[4] = {kbv.x, kbv.y, kbv.z, kbv.w};
+          float ak[8], aq[8], bk[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float gt = j < 4 ? gt0[j] : gt1[j - 4];
+            const float gr = j < 4 ? gr0[j] : gr1[j - 4];
+            const float gs = j < 4 ? gs0[j] : gs1[j - 4];
+            const float kav = __uint_as_float(j & 1 ? (kaw[j >> 1] & 0xffff0000u) : (kaw[j >> 1] << 16));
+            const float kbf = __uint_as_float(j & 1 ? (kbw[j >> 1] & 0xffff0000u) : (kbw[j >> 1] << 16));
+            const float ea = __expf(gt - gr);
+            ak[j] = kav * ea;
+            aq[j] = __uint_as_float(j & 1 ? (qaw[j >> 1] & 0xffff0000u) : (qaw[j >> 1] << 16)) * ea;
+            bk[j] = kbf * __expf(gr - gs);
+          }
+          const bf16x8 b = to_bf16x8(bk);
+          dA = mfma16(to_bf16x8(ak), b, dA);
+          dP = mfma16(to_bf16x8(aq), b, dP);
+        }
+        // Lane holds rows 16 I + 4 g + j of column s = 16 J + m. Entries
+        // above the diagonal are dropped (they may be huge or non-finite).
+        const int s2 = 16 * J + m;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int row = 16 * I + 4 * g + j;
+          if (s2 < row) sm.at[sw32<C>(s2, row)] = sm.at[sw32<C>(row, row)] * dA[j];
+          pm[row * C + 32 * (s2 >> 5) + perm_slot(s2 & 31)] = bf16_bits(s2 <= row ? dP[j] : 0.f);
+        }
+      } else {
+        // Diagonal block pairwise: lane (t, cq) = (m, g) covers row t and a
+        // quarter of the channels; partial sums are reduced over quarters.
+        constexpr int CQ = K / 4;
+        const int t = m, cq = g, row = 16 * I + t;
+        float ares[16], pres[16];
+#pragma unroll
+        for (int s3 = 0; s3 < 16; ++s3) {
+          ares[s3] = 0.f;
+          pres[s3] = 0.f;
+        }
+        for (int i8 = 0; i8 < CQ; i8 += 8) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int ch = cq * CQ + i8 + i;
+            const float gt = sm.gam[sw32<K>(row, ch)];
+            const float kt = bf16_to_f32(sm.k[sw16<K>(row, ch)]);
+            const float qti = bf16_to_f32(sm.q[sw16<K>(row, ch)]);
+#pragma unroll
+            for (int s3 = 0; s3 < 16; ++s3) {
+              const int srow = 16 * I + s3;
+              // gam is non-increasing, so for s <= t the exponent is <= 0;
+              // the min only keeps the masked s > t entries finite.
+              const float ke = bf16_to_f32(sm.k[sw16<K>(srow, ch)]) *
+                               __expf(fminf(gt - sm.gam[sw32<K>(srow, ch)], 0.f));
+              ares[s3] = fmaf(kt, ke, ares[s3]);
+              pres[s3] = fmaf(qti, ke, pres[s3]);
+            }
+          }
+        }
+#pragma unroll
+        for (int s3 = 0; s3 < 16; ++s3) {
+          ares[s3] += __shfl_xor(ares[s3], 16);
+          ares[s3] += __shfl_xor(ares[s3], 32);
+          pres[s3] += __shfl_xor(pres[s3], 16);
+          pres[s3] += __shfl_xor(pres[s3], 32);
+        }
+        if (cq == 0) {
+          const float bt = sm.at[sw32<C>(row, row)];
+#pragma unroll
+          for (int s3 = 0; s3 < 16; ++s3) {
+            const int col = 16 * I + s3;
+            if (s3 < t) sm.at[sw32<C>(col, row)] = bt * ares[s3];
+            pm[row * C + 32 * (col >> 5) + perm_slot(col & 31)] = bf16_bits(s3 <= t ? pres[s3] : 0.f);
+          }
+        }
+      }
+    }
+    if (w == 3) {
+      // Zero P blocks above the diagonal that the state kernel reads:
+      // rows 0..15 x cols 16..31 and rows 32..47 x cols 48..63.
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = 4 * g + j;
+        pm[row * C + perm_slot(16 + m)] = 0;
+        pm[(32 + row) * C + 32 + perm_slot(16 + m)] = 0;
+      }
     }
   }
-  // ---- 4b. T = (I + A)^{-1}: diagonal blocks by forward substitution ----
+  // v for the U phase, fetched now so its latency hides behind the inverse:
+  // lane (m, g) needs v[t][16 nb + m] for t = 32 kb + 8 g + j, nb = w, w + 4.
+  constexpr int NBU = (V / 16 + 3) / 4;
+  uint16_t vpre[NBU][2][8];
+#pragma unroll
+  for (int u = 0; u < NBU; ++u)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int t = 32 * kb + 8 * g + j;
+        const int nb = w + 4 * u;
+        vpre[u][kb][j] = (t < n && nb < V / 16)
+                             ? p.qkv[(t0 + t) * p.qkv_row_stride + 2 * H * K + h * V + 16 * nb + m]
+                             : static_cast<uint16_t>(0);
+      }
+  lds_barrier();
+
+  // ---- 4a. T = (I + A)^{-1}: diagonal blocks by forward substitution ----
+  // at(s, t) = A[t][s] for s < t; T strictly below the diagonal of at.
   if (lane < 16) {
     const int blk = w, jc = lane;
     float x[16];
@@ -403,43 +478,49 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_kernel(const PrefillPara
     for (int tt = 0; tt < 16; ++tt) {
       float v = (tt == jc) ? 1.f : 0.f;
 #pragma unroll
-      for (int s = 0; s < tt; ++s) v = fmaf(-sm.A[16 * blk + tt][16 * blk + s], x[s], v);
+      for (int s3 = 0; s3 < tt; ++s3) v = fmaf(-sm.at[sw32<C>(16 * blk + s3, 16 * blk + tt)], x[s3], v);
       x[tt] = v;
     }
 #pragma unroll
-    for (int tt = 0; tt < 16; ++tt) sm.T[16 * blk + tt][16 * blk + jc] = x[tt];
+    for (int tt = 0; tt < 16; ++tt)
+      if (tt > jc) sm.at[sw32<C>(16 * blk + tt, 16 * blk + jc)] = x[tt];
   }
-  __syncthreads();
-  // ---- 4c. off-diagonal blocks of T, by distance from the diagonal -------
-  //   T_IJ = -T_II sum_{J<=L<I} A_IL T_LJ
+  lds_barrier();
+  // ---- 4b. off-diagonal blocks of T, by distance from the diagonal -------
+  //   T_IJ = -T_II sum_{J<=L<I} A_IL T_LJ,  A_IL[r][c] = at(16L + c, 16I + r)
   {
-    float(*Y)[SM::MP] = sm.P;  // scratch: up to three 16x16 blocks side by side
+    float* Y = reinterpret_cast<float*>(sm.q);  // q is no longer read: three 16x16 blocks
     const int rr = tid >> 4, cc = tid & 15;
     for (int d = 1; d < 4; ++d) {
       for (int I = d; I < 4; ++I) {
         const int J = I - d;
-        float y = 0.f;
-        for (int L = J; L < I; ++L)
+        // L = J: T_JJ[k2][cc] is 1 at k2 = cc, at(16J + k2, 16J + cc) below.
+        float y = sm.at[sw32<C>(16 * J + cc, 16 * I + rr)];
+        for (int k2 = cc + 1; k2 < 16; ++k2)
+          y = fmaf(sm.at[sw32<C>(16 * J + k2, 16 * I + rr)], sm.at[sw32<C>(16 * J + k2, 16 * J + cc)], y);
+        for (int L = J + 1; L < I; ++L)
 #pragma unroll
           for (int k2 = 0; k2 < 16; ++k2)
-            y = fmaf(sm.A[16 * I + rr][16 * L + k2], sm.T[16 * L + k2][16 * J + cc], y);
-        Y[rr][16 * (I - d) + cc] = y;
+            y = fmaf(sm.at[sw32<C>(16 * L + k2, 16 * I + rr)], sm.at[sw32<C>(16 * L + k2, 16 * J + cc)], y);
+        Y[(I - d) * 256 + rr * 16 + cc] = y;
       }
-      __syncthreads();
+      lds_barrier();
       for (int I = d; I < 4; ++I) {
         const int J = I - d;
-        float t2 = 0.f;
-#pragma unroll
-        for (int k2 = 0; k2 < 16; ++k2)
-          t2 = fmaf(sm.T[16 * I + rr][16 * I + k2], Y[k2][16 * (I - d) + cc], t2);
-        sm.T[16 * I + rr][16 * J + cc] = -t2;
+        // T_II[rr][k2]: at(16I + rr, 16I + k2) for k2 < rr, 1 at k2 = rr.
+        float t2 = Y[(I - d) * 256 + rr * 16 + cc];
+        for (int k2 = 0; k2 < rr; ++k2)
+          t2 = fmaf(sm.at[sw32<C>(16 * I + rr, 16 * I + k2)], Y[(I - d) * 256 + k2 * 16 + cc], t2);
+        sm.at[sw32<C>(16 * I + rr, 16 * J + cc)] = -t2;
       }
-      __syncthreads();
+      lds_barrier();
     }
   }
 
   // ---- 5. W = T diag(beta)(K o e^gam), U = T diag(beta) V on MFMA -------
-  // T is lower triangular, so rows 0..31 need only positions 0..31.
+  // beta is folded into the fp32 columns of T before the bf16 cast, so V
+  // enters the product exactly as given. T is lower triangular, so rows
+  // 0..31 need only positions 0..31.
   {
     bf16x8 Tf[4][2];
 #pragma unroll
@@ -447,11 +528,16 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_kernel(const PrefillPara
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         float tv[8];
+        const int row = 16 * pb + m;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) tv[j] = sm.T[16 * pb + m][32 * kb + 8 * g + j];
+        for (int j = 0; j < 8; ++j) {
+          const int col = 32 * kb + 8 * g + j;
+          const float bcol = sm.at[sw32<C>(col, col)];
+          tv[j] = (col < row ? sm.at[sw32<C>(row, col)] : (col == row ? 1.f : 0.f)) * bcol;
+        }
         Tf[pb][kb] = to_bf16x8(tv);
       }
-    // -W staged in sm.q (no longer read) with the channel permutation.
+    // -W staged in sm.q (plain row-major, channels permuted).
     for (int nb = w; nb < K / 16; nb += 4) {
       const int ch = 16 * nb + m;
       bf16x8 Bf[2];
@@ -461,7 +547,7 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_kernel(const PrefillPara
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int t = 32 * kb + 8 * g + j;
-          bv[j] = sm.beta[t] * bf16_to_f32(sm.k[t][ch]) * __expf(sm.gam[t][ch]);
+          bv[j] = bf16_to_f32(sm.k[sw16<K>(t, ch)]) * __expf(sm.gam[sw32<K>(t, ch)]);
         }
         Bf[kb] = to_bf16x8(bv);
       }
@@ -473,25 +559,21 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_kernel(const PrefillPara
         for (int j = 0; j < 4; ++j) {
           const int row = 16 * pb + 4 * g + j;
           const int col = 32 * (nb >> 1) + perm_slot(16 * (nb & 1) + m);
-          sm.q[row][col] = bf16_bits(-D[j]);
+          sm.q[row * K + col] = bf16_bits(-D[j]);
         }
       }
     }
     // U written straight out in accumulator fragment order.
     f32x4* uf = reinterpret_cast<f32x4*>(rec + R::Uf);
-    for (int nb = w; nb < V / 16; nb += 4) {
-      const int col = 16 * nb + m;
+#pragma unroll
+    for (int u = 0; u < NBU; ++u) {
+      const int nb = w + 4 * u;
+      if (nb >= V / 16) break;
       bf16x8 Bv[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        float bv[8];
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int t = 32 * kb + 8 * g + j;
-          bv[j] = sm.beta[t] * bf16_to_f32(sm.v[t][col]);
-        }
-        Bv[kb] = to_bf16x8(bv);
-      }
+        for (int j = 0; j < 8; ++j) Bv[kb][j] = __builtin_bit_cast(__bf16, vpre[u][kb][j]);
 #pragma unroll
       for (int pb = 0; pb < 4; ++pb) {
         f32x4 D = mfma16(Tf[pb][0], Bv[0], f32x4{0.f, 0.f, 0.f, 0.f});
@@ -500,15 +582,13 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_kernel(const PrefillPara
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- 6. -W -> workspace ----------------------------------------------
   {
     uint16_t* wn = reinterpret_cast<uint16_t*>(rec + R::Wn);
-    for (int e = tid; e < C * (K / 8); e += kThreads) {
-      const int t = e / (K / 8), pc = e % (K / 8);
-      *reinterpret_cast<uint4*>(wn + t * K + pc * 8) = *reinterpret_cast<const uint4*>(&sm.q[t][pc * 8]);
-    }
+    for (int e = tid; e < C * KP8; e += kThreads)
+      *reinterpret_cast<uint4*>(wn + e * 8) = *reinterpret_cast<const uint4*>(&sm.q[e * 8]);
   }
 }
 
@@ -563,10 +643,6 @@ __device__ __forceinline__ void dma_chunk(const char* rec, StateBuf<K, V>& b, in
     }
   }
 }
-
-// Waits until this wave's outstanding vector-memory operations (including
-// LDS DMA) have completed: vmcnt = 0, other counters unconstrained.
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 template <int K, int V>
 __global__ __launch_bounds__(kThreads) void chunk_state_kernel(const PrefillParams p,
@@ -670,14 +746,24 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(const PrefillPara
         Ob[pb] = mfma16(lds_frag(&bf.qg[16 * pb + m][32 * kb + 8 * g]), Sb[kb], Ob[pb]);
       }
     }
-    // V' as a B operand over positions.
+    // V' as a B operand over positions. The output product takes it as
+    // hi + lo bf16 parts (the rounding of V' would otherwise dominate the
+    // output error); the state update takes the hi part.
     const bf16x8 Vb0 = pack_acc(Vp[0], Vp[1]);
     const bf16x8 Vb1 = pack_acc(Vp[2], Vp[3]);
+    const bf16x8 Vl0 = pack_lo(Vp[0], Vp[1], Vb0);
+    const bf16x8 Vl1 = pack_lo(Vp[2], Vp[3], Vb1);
     // O += P V' (P is lower triangular: rows 0..31 need positions 0..31 only).
 #pragma unroll
     for (int pb = 0; pb < 4; ++pb) {
-      Ob[pb] = mfma16(lds_frag(&bf.pm[16 * pb + m][8 * g]), Vb0, Ob[pb]);
-      if (pb >= 2) Ob[pb] = mfma16(lds_frag(&bf.pm[16 * pb + m][32 + 8 * g]), Vb1, Ob[pb]);
+      const bf16x8 P0 = lds_frag(&bf.pm[16 * pb + m][8 * g]);
+      Ob[pb] = mfma16(P0, Vb0, Ob[pb]);
+      Ob[pb] = mfma16(P0, Vl0, Ob[pb]);
+      if (pb >= 2) {
+        const bf16x8 P1 = lds_frag(&bf.pm[16 * pb + m][32 + 8 * g]);
+        Ob[pb] = mfma16(P1, Vb1, Ob[pb]);
+        Ob[pb] = mfma16(P1, Vl1, Ob[pb]);
+      }
     }
 #pragma unroll
     for (int pb = 0; pb < 4; ++pb)

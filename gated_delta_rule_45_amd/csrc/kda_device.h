@@ -79,17 +79,30 @@ __device__ __forceinline__ void load_bf16(const uint16_t* p, float* out) {
   }
 }
 
-__device__ __forceinline__ float sigmoid_f32(float z) { return 1.0f / (1.0f + __expf(-z)); }
+// 1 / (1 + e^-z) with the hardware exponential and reciprocal (about 1 ulp
+// each; the result is within a few ulp of the correctly rounded value).
+__device__ __forceinline__ float sigmoid_f32(float z) {
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
 
 // Per-channel log-decay from the raw gate input (same reading as the header):
 //   x = raw_g + dt_bias, a = exp(A_log[h]);
 //   g = -a * softplus(x)  or  g = lower_bound * sigmoid(a * x).
-// softplus is evaluated as max(x, 0) + log1p(exp(-|x|)), which cannot overflow.
+// softplus is evaluated as max(x, 0) + log(1 + exp(-|x|)), which cannot
+// overflow; for large |x| the log term is below fp32 resolution of the sum.
 __device__ __forceinline__ float gate_log_decay(float raw_g, float dt_bias, float a,
                                                 bool has_lb, float lb) {
   const float x = raw_g + dt_bias;
   if (has_lb) return lb * sigmoid_f32(a * x);
-  return -a * (fmaxf(x, 0.0f) + log1pf(__expf(-fabsf(x))));
+  return -a * (fmaxf(x, 0.0f) + __logf(1.0f + __expf(-fabsf(x))));
+}
+
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS
+// operations (lgkmcnt = 0) and meets the other waves, but leaves global loads
+// and stores in flight (unlike __syncthreads, whose fence drains them).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt = 63, expcnt = 7, lgkmcnt = 0
+  __builtin_amdgcn_s_barrier();
 }
 
 }  // namespace kda
