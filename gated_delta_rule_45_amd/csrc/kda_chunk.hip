@@ -99,8 +99,28 @@ __device__ __forceinline__ bf16x8 lds_frag(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
 }
 
+// Piece swizzle of the record's bf16 tiles. A row of N bf16 elements is
+// N/8 16-byte pieces; piece p of row r is stored at piece p ^ swz<N>(r). The
+// state kernel copies the record to LDS byte for byte and reads MFMA
+// fragments of 16 consecutive rows at one logical piece: the swizzle puts
+// those 16 reads in 16 different 16-byte bank groups (and any 8 consecutive
+// rows in 8), for 256-byte rows (r & 15) and for 128-byte rows, whose odd
+// rows start half way round the banks (r ^ r >> 3) & 7.
+template <int N>
+__device__ __forceinline__ int swz(int r) {
+  static_assert(N / 8 >= 8, "rows of at least 8 pieces");
+  if constexpr (N / 8 >= 16) return r & 15;
+  else return (r ^ (r >> 3)) & 7;
+}
+// Element offset of logical (row, col) in a swizzled [rows][N] bf16 tile.
+template <int N>
+__device__ __forceinline__ int rec_elem(int r, int c) {
+  return r * N + ((((c >> 3) ^ swz<N>(r)) << 3) | (c & 7));
+}
+
 // Per-(chunk, head) record in the workspace. The first five fields are
-// copied to LDS as one contiguous block by the state kernel.
+// copied to LDS as one contiguous block by the state kernel; its bf16 tiles
+// are stored with the swizzle above.
 template <int K, int V>
 struct Rec {
   static constexpr size_t Wn = 0;                      // bf16 [C][K], -W, channels permuted
@@ -302,7 +322,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_intra_kernel(const PrefillP
       uint4 o;
       o.x = pack_bf16x2(vals[0], vals[1]); o.y = pack_bf16x2(vals[2], vals[3]);
       o.z = pack_bf16x2(vals[4], vals[5]); o.w = pack_bf16x2(vals[6], vals[7]);
-      *reinterpret_cast<uint4*>(qg + t * K + pc * 8) = o;
+      *reinterpret_cast<uint4*>(qg + rec_elem<K>(t, pc * 8)) = o;
     }
     uint16_t* kgt = reinterpret_cast<uint16_t*>(rec + R::KgT);
     for (int e = tid; e < K * (C / 8); e += kThreads) {
@@ -318,7 +338,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_intra_kernel(const PrefillP
       uint4 o;
       o.x = pack_bf16x2(vals[0], vals[1]); o.y = pack_bf16x2(vals[2], vals[3]);
       o.z = pack_bf16x2(vals[4], vals[5]); o.w = pack_bf16x2(vals[6], vals[7]);
-      *reinterpret_cast<uint4*>(kgt + ch * C + pc * 8) = o;
+      *reinterpret_cast<uint4*>(kgt + rec_elem<C>(ch, pc * 8)) = o;
     }
   }
 
@@ -390,7 +410,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_intra_kernel(const PrefillP
         for (int j = 0; j < 4; ++j) {
           const int row = 16 * I + 4 * g + j;
           if (s2 < row) sm.at[sw32<C>(s2, row)] = sm.at[sw32<C>(row, row)] * dA[j];
-          pm[row * C + 32 * (s2 >> 5) + perm_slot(s2 & 31)] = bf16_bits(s2 <= row ? dP[j] : 0.f);
+          pm[rec_elem<C>(row, 32 * (s2 >> 5) + perm_slot(s2 & 31))] = bf16_bits(s2 <= row ? dP[j] : 0.f);
         }
       } else {
         // Diagonal block pairwise: lane (t, cq) = (m, g) covers row t and a
@@ -435,7 +455,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_intra_kernel(const PrefillP
           for (int s3 = 0; s3 < 16; ++s3) {
             const int col = 16 * I + s3;
             if (s3 < t) sm.at[sw32<C>(col, row)] = bt * ares[s3];
-            pm[row * C + 32 * (col >> 5) + perm_slot(col & 31)] = bf16_bits(s3 <= t ? pres[s3] : 0.f);
+            pm[rec_elem<C>(row, 32 * (col >> 5) + perm_slot(col & 31))] = bf16_bits(s3 <= t ? pres[s3] : 0.f);
           }
         }
       }
@@ -446,8 +466,8 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_intra_kernel(const PrefillP
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int row = 4 * g + j;
-        pm[row * C + perm_slot(16 + m)] = 0;
-        pm[(32 + row) * C + 32 + perm_slot(16 + m)] = 0;
+        pm[rec_elem<C>(row, perm_slot(16 + m))] = 0;
+        pm[rec_elem<C>(32 + row, 32 + perm_slot(16 + m))] = 0;
       }
     }
   }
@@ -588,68 +608,70 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_intra_kernel(const PrefillP
   {
     uint16_t* wn = reinterpret_cast<uint16_t*>(rec + R::Wn);
     for (int e = tid; e < C * KP8; e += kThreads)
-      *reinterpret_cast<uint4*>(wn + e * 8) = *reinterpret_cast<const uint4*>(&sm.q[e * 8]);
+      *reinterpret_cast<uint4*>(wn + rec_elem<K>(e / KP8, (e % KP8) * 8)) = *reinterpret_cast<const uint4*>(&sm.q[e * 8]);
   }
 }
 
 // --------------------------------------------------------------- state --
 
+// The LDS image of one record: the record's first lds_part bytes, byte for
+// byte (tiles swizzled as written by the intra kernel).
 template <int K, int V>
 struct StateBuf {
-  static constexpr int KP = K + 8;
-  static constexpr int CP = C + 8;
-  uint16_t wn[C][KP];
-  uint16_t qg[C][KP];
-  uint16_t pm[C][CP];
-  uint16_t kgt[K][CP];
+  uint16_t wn[C * K];
+  uint16_t qg[C * K];
+  uint16_t pm[C * C];
+  uint16_t kgt[K * C];
   float eg[K];
 };
 
-// Direct global -> LDS copy of chunk record c's LDS part into a padded
-// buffer. Each wave's global_load_lds_dwordx4 writes lane l's 16 bytes at
-// M0 + 16 l, so the buffer is walked slot by slot (64 slots per wave per
-// round) and every slot picks its source piece; padding slots read a valid
-// dummy piece. No registers hold the data, and the copy overlaps compute
-// until the next s_waitcnt vmcnt.
+// Copy record `rec`'s LDS part into `b` by LDS DMA: lane l of a wave writes
+// its 16 bytes at the wave's base + 16 l, so slot i takes piece i. Nothing
+// passes through registers; the copy runs until the next vmcnt wait.
 template <int K, int V>
-__device__ __forceinline__ void dma_chunk(const char* rec, StateBuf<K, V>& b, int tid) {
-  using Bf = StateBuf<K, V>;
-  constexpr int KS = Bf::KP / 8, CS = Bf::CP / 8;  // 16-byte slots per padded row
-  constexpr int sW = C * KS, sQ = C * KS, sP = C * CS, sK = K * CS, sE = K / 4;
-  constexpr int total = sW + sQ + sP + sK + sE;
-  static_assert(sizeof(Bf) == static_cast<size_t>(total) * 16, "padded buffer must be whole slots");
+__device__ __forceinline__ void dma_chunk(const char* rec, StateBuf<K, V>* b, int tid) {
+  constexpr int total = static_cast<int>(sizeof(StateBuf<K, V>) / 16);
+  constexpr int full = total / kThreads, rem = total % kThreads;
   const uint4* src = reinterpret_cast<const uint4*>(rec);
-  uint4* base = reinterpret_cast<uint4*>(&b);
+  uint4* dst = reinterpret_cast<uint4*>(b);
   const int wbase = tid & ~63;
-#pragma unroll 4
-  for (int r = 0; r < (total + kThreads - 1) / kThreads; ++r) {
-    const int slot = r * kThreads + tid;
-    if (slot < total) {
-      int piece = 0;  // dummy source for padding slots
-      int e = slot;
-      if (e < sW) {
-        if (e % KS < K / 8) piece = (e / KS) * (K / 8) + e % KS;
-      } else if ((e -= sW) < sQ) {
-        if (e % KS < K / 8) piece = C * K / 8 + (e / KS) * (K / 8) + e % KS;
-      } else if ((e -= sQ) < sP) {
-        if (e % CS < C / 8) piece = 2 * C * K / 8 + (e / CS) * (C / 8) + e % CS;
-      } else if ((e -= sP) < sK) {
-        if (e % CS < C / 8) piece = 2 * C * K / 8 + C * C / 8 + (e / CS) * (C / 8) + e % CS;
-      } else {
-        e -= sK;
-        piece = 2 * C * K / 8 + C * C / 8 + K * C / 8 + e;
-      }
-      __builtin_amdgcn_global_load_lds(src + piece, base + r * kThreads + wbase, 16, 0, 0);
-    }
+#pragma unroll
+  for (int r = 0; r < full; ++r)
+    __builtin_amdgcn_global_load_lds(src + r * kThreads + tid, dst + r * kThreads + wbase, 16, 0, 0);
+  if constexpr (rem > 0) {
+    if (tid < rem)
+      __builtin_amdgcn_global_load_lds(src + full * kThreads + tid, dst + full * kThreads + wbase, 16, 0, 0);
   }
 }
 
+// Output stores per lane per chunk: one 8-byte store per 16-position block.
+constexpr int kOutStores = C / 16;
+
+// Top of a chunk: this wave's copies and U loads for the chunk have landed
+// (every vector-memory operation except the kOutStores output stores issued
+// after them; they complete in order), its LDS reads are done, and all waves
+// meet. Unlike __syncthreads this leaves the output stores in flight.
+__device__ __forceinline__ void chunk_barrier() {
+  static_assert(kOutStores < 16, "vmcnt field");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0070 | kOutStores);  // vmcnt = kOutStores, expcnt = 7, lgkmcnt = 0
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// MFMA fragment (8 bf16) at logical (row, col) of a swizzled [rows][N] tile.
+template <int N>
+__device__ __forceinline__ bf16x8 frag(const uint16_t* tile, int r, int c) {
+  return lds_frag(tile + rec_elem<N>(r, c));
+}
+
 template <int K, int V>
-__global__ __launch_bounds__(kThreads) void chunk_state_kernel(const PrefillParams p,
-                                                               const int32_t* chunk_start,
-                                                               const char* recs) {
+__global__ __launch_bounds__(kThreads, 1) void chunk_state_kernel(const PrefillParams p,
+                                                                  const int32_t* chunk_start,
+                                                                  const char* recs) {
   using R = Rec<K, V>;
   using B = StateBuf<K, V>;
+  static_assert(sizeof(B) == R::lds_part, "LDS image is the record's first lds_part bytes");
   static_assert(R::lds_part % 16 == 0, "record LDS part must be whole 16-byte pieces");
   constexpr int NVH = V / 64;  // workgroups per (sequence, head): 64 columns each
   __shared__ B buf[2];
@@ -695,12 +717,16 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(const PrefillPara
 
   float* st = p.pool + slot * p.slot_stride + static_cast<int64_t>(h) * K * V;
   const bool init = p.has_initial_state == nullptr || p.has_initial_state[seq] != 0;
+  // Without an initial state the range is empty and every load reads zero;
+  // all loads are issued before the first use.
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(st, init ? static_cast<uint32_t>(K * V * 4) : 0u);
   f32x4 S[K / 16];
 #pragma unroll
   for (int cb = 0; cb < K / 16; ++cb)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      S[cb][j] = init ? st[(16 * cb + 4 * g + j) * V + col0 + m] : 0.f;
+      S[cb][j] = __builtin_bit_cast(
+          float, __builtin_amdgcn_raw_buffer_load_b32(rs, ((16 * cb + 4 * g + j) * V + col0 + m) * 4, 0, 0));
 
   f32x4 Upre[4];
   auto rec_of = [&](int cc) {
@@ -711,74 +737,113 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(const PrefillPara
 #pragma unroll
     for (int pb = 0; pb < 4; ++pb) Upre[pb] = uf[(pb * (V / 16) + col0 / 16) * 64 + lane];
   };
-  dma_chunk<K, V>(rec_of(0), buf[0], tid);
+  dma_chunk<K, V>(rec_of(0), &buf[0], tid);
   load_u(0);
   const float scale = p.scale;
+  // Lane (m, g) of the transposed output tile of position block pb holds
+  // channels col0 + 4 g .. + 3 of position 16 pb + m: 8 contiguous bytes.
+  const int out_lane = static_cast<int>(m * HV + h * V + col0 + 4 * g) * 2;
   for (int cc = 0; cc < nch; ++cc) {
-    B& bf = buf[cc & 1];
+    const B& bf = buf[cc & 1];
     // Chunk cc's buffer is complete once every wave's copy has landed; the
     // barrier also means every wave is done with chunk cc-1's buffer, which
     // the next copy overwrites.
-    wait_vmem();
-    __syncthreads();
+    chunk_barrier();
     f32x4 Vp[4];
 #pragma unroll
     for (int pb = 0; pb < 4; ++pb) Vp[pb] = Upre[pb];
     if (cc + 1 < nch) {
-      dma_chunk<K, V>(rec_of(cc + 1), buf[(cc + 1) & 1], tid);
+      dma_chunk<K, V>(rec_of(cc + 1), &buf[(cc + 1) & 1], tid);
       load_u(cc + 1);
     }
 
     const int64_t t0 = bos + static_cast<int64_t>(C) * cc;
     const int n = static_cast<int>(min<int64_t>(C, eos - t0));
 
-    // V' = U - W S and Q o e^gam S, contracting over channels.
+    // V' = U - W S (rows: positions) and O^T = S^T (Q o e^gam)^T (rows:
+    // value channels), both contracting over key channels. S as a bf16
+    // fragment is the B operand of the first and the A operand of the second.
     bf16x8 Sb[K / 32];
 #pragma unroll
     for (int kb = 0; kb < K / 32; ++kb) Sb[kb] = pack_acc(S[2 * kb], S[2 * kb + 1]);
-    f32x4 Ob[4];
+    // Fragments are read one position block ahead of the MFMAs that use
+    // them (the scheduling barriers keep that order), so LDS latency hides
+    // behind the previous block's MFMAs.
+    bf16x8 wf[2][K / 32], qf[2][K / 32];
+#pragma unroll
+    for (int kb = 0; kb < K / 32; ++kb) {
+      wf[0][kb] = frag<K>(bf.wn, m, 32 * kb + 8 * g);
+      qf[0][kb] = frag<K>(bf.qg, m, 32 * kb + 8 * g);
+    }
+    bf16x8 pf[4][2];
+    f32x4 Ot[4];
 #pragma unroll
     for (int pb = 0; pb < 4; ++pb) {
-      Ob[pb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      __builtin_amdgcn_sched_barrier(0);
+      if (pb + 1 < 4) {
+#pragma unroll
+        for (int kb = 0; kb < K / 32; ++kb) {
+          wf[(pb + 1) & 1][kb] = frag<K>(bf.wn, 16 * (pb + 1) + m, 32 * kb + 8 * g);
+          qf[(pb + 1) & 1][kb] = frag<K>(bf.qg, 16 * (pb + 1) + m, 32 * kb + 8 * g);
+        }
+      } else {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          pf[b][0] = frag<C>(bf.pm, 16 * b + m, 8 * g);
+          if (b >= 2) pf[b][1] = frag<C>(bf.pm, 16 * b + m, 32 + 8 * g);
+        }
+      }
+      Ot[pb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < K / 32; ++kb) {
-        Vp[pb] = mfma16(lds_frag(&bf.wn[16 * pb + m][32 * kb + 8 * g]), Sb[kb], Vp[pb]);
-        Ob[pb] = mfma16(lds_frag(&bf.qg[16 * pb + m][32 * kb + 8 * g]), Sb[kb], Ob[pb]);
+        Vp[pb] = mfma16(wf[pb & 1][kb], Sb[kb], Vp[pb]);
+        Ot[pb] = mfma16(Sb[kb], qf[pb & 1][kb], Ot[pb]);
       }
     }
-    // V' as a B operand over positions. The output product takes it as
-    // hi + lo bf16 parts (the rounding of V' would otherwise dominate the
-    // output error); the state update takes the hi part.
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 kf[K / 16][2];
+#pragma unroll
+    for (int cb = 0; cb < K / 16; ++cb) {
+      kf[cb][0] = frag<C>(bf.kgt, 16 * cb + m, 8 * g);
+      kf[cb][1] = frag<C>(bf.kgt, 16 * cb + m, 32 + 8 * g);
+    }
+    // V' over positions: the output product takes it as hi + lo bf16 parts
+    // (the rounding of V' would otherwise dominate the output error); the
+    // state update takes the hi part.
     const bf16x8 Vb0 = pack_acc(Vp[0], Vp[1]);
     const bf16x8 Vb1 = pack_acc(Vp[2], Vp[3]);
     const bf16x8 Vl0 = pack_lo(Vp[0], Vp[1], Vb0);
     const bf16x8 Vl1 = pack_lo(Vp[2], Vp[3], Vb1);
-    // O += P V' (P is lower triangular: rows 0..31 need positions 0..31 only).
+    // O^T += V'^T P^T (P is lower triangular: positions 0..31 see only
+    // positions 0..31).
 #pragma unroll
     for (int pb = 0; pb < 4; ++pb) {
-      const bf16x8 P0 = lds_frag(&bf.pm[16 * pb + m][8 * g]);
-      Ob[pb] = mfma16(P0, Vb0, Ob[pb]);
-      Ob[pb] = mfma16(P0, Vl0, Ob[pb]);
+      Ot[pb] = mfma16(Vb0, pf[pb][0], Ot[pb]);
+      Ot[pb] = mfma16(Vl0, pf[pb][0], Ot[pb]);
       if (pb >= 2) {
-        const bf16x8 P1 = lds_frag(&bf.pm[16 * pb + m][32 + 8 * g]);
-        Ob[pb] = mfma16(P1, Vb1, Ob[pb]);
-        Ob[pb] = mfma16(P1, Vl1, Ob[pb]);
+        Ot[pb] = mfma16(Vb1, pf[pb][1], Ot[pb]);
+        Ot[pb] = mfma16(Vl1, pf[pb][1], Ot[pb]);
       }
     }
+    // Rows of the chunk as one buffer range: positions past its end fall
+    // outside and their stores are dropped, so every lane issues exactly
+    // kOutStores stores.
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.out + t0 * HV, static_cast<uint32_t>(n * HV * 2));
 #pragma unroll
-    for (int pb = 0; pb < 4; ++pb)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int pos = 16 * pb + 4 * g + j;
-        if (pos < n) p.out[(t0 + pos) * HV + h * V + col0 + m] = f32_to_bf16_rne(scale * Ob[pb][j]);
-      }
+    for (int pb = 0; pb < 4; ++pb) {
+      const uint32_t lo = pack_bf16x2(scale * Ot[pb][0], scale * Ot[pb][1]);
+      const uint32_t hi = pack_bf16x2(scale * Ot[pb][2], scale * Ot[pb][3]);
+      typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2{lo, hi}, ro, out_lane + static_cast<int>(16 * pb * HV * 2), 0, 0);
+    }
     // S <- diag(e^{gam_last}) S + (K o e^{gam_last - gam})^T V'.
 #pragma unroll
     for (int cb = 0; cb < K / 16; ++cb) {
+      const f32x4 e = *reinterpret_cast<const f32x4*>(&bf.eg[16 * cb + 4 * g]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) S[cb][j] *= bf.eg[16 * cb + 4 * g + j];
-      S[cb] = mfma16(lds_frag(&bf.kgt[16 * cb + m][8 * g]), Vb0, S[cb]);
-      S[cb] = mfma16(lds_frag(&bf.kgt[16 * cb + m][32 + 8 * g]), Vb1, S[cb]);
+      for (int j = 0; j < 4; ++j) S[cb][j] *= e[j];
+      S[cb] = mfma16(kf[cb][0], Vb0, S[cb]);
+      S[cb] = mfma16(kf[cb][1], Vb1, S[cb]);
     }
   }
 

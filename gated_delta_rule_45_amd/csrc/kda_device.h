@@ -100,9 +100,13 @@ __device__ __forceinline__ float gate_log_decay(float raw_g, float dt_bias, floa
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS
 // operations (lgkmcnt = 0) and meets the other waves, but leaves global loads
 // and stores in flight (unlike __syncthreads, whose fence drains them).
+// The empty asm statements keep the compiler from moving memory accesses
+// across the barrier.
 __device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt = 63, expcnt = 7, lgkmcnt = 0
   __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 }  // namespace kda
