@@ -16,6 +16,9 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # Packed-fp32 instructions are kept out of every kernel on purpose.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: the state pass reads and rescales
+    # its accumulators every chunk, which in AGPRs costs a move each way.
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
 ]
 

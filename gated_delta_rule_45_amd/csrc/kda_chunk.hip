@@ -19,7 +19,7 @@
 //            reference point between the two blocks so both factors stay <= 1;
 //            diagonal blocks pairwise in fp32 so nothing can overflow for any
 //            gate), T by blocked forward substitution in fp32, then W and U on
-//            MFMA. It stores -W, Q o e^gam, P, (K o e^{gam_last-gam})^T (bf16,
+//            MFMA. It stores -W, scale Q o e^gam, scale P, (K o e^{gam_last-gam})^T (bf16,
 //            laid out as MFMA A operands), e^{gam_last} and U (fp32, in
 //            accumulator fragment order) in the workspace.
 //  3. state: one workgroup per (sequence, head, 64 value columns), looping over
@@ -124,8 +124,8 @@ __device__ __forceinline__ int rec_elem(int r, int c) {
 template <int K, int V>
 struct Rec {
   static constexpr size_t Wn = 0;                      // bf16 [C][K], -W, channels permuted
-  static constexpr size_t Qg = Wn + C * K * 2;         // bf16 [C][K], Q o e^gam, channels permuted
-  static constexpr size_t Pm = Qg + C * K * 2;         // bf16 [C][C], positions permuted
+  static constexpr size_t Qg = Wn + C * K * 2;         // bf16 [C][K], scale Q o e^gam, channels permuted
+  static constexpr size_t Pm = Qg + C * K * 2;         // bf16 [C][C], scale P, positions permuted
   static constexpr size_t KgT = Pm + C * C * 2;        // bf16 [K][C], positions permuted
   static constexpr size_t Eg = KgT + K * C * 2;        // fp32 [K], e^{gam_last}
   static constexpr size_t lds_part = Eg + K * 4;       // bytes copied to LDS
@@ -316,8 +316,8 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_intra_kernel(const PrefillP
       const f32x4 g1 = *reinterpret_cast<const f32x4*>(&sm.gam[sw32<K>(t, cb + 16)]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        vals[j] = qv[j] * __expf(g0[j]);
-        vals[4 + j] = qv[4 + j] * __expf(g1[j]);
+        vals[j] = p.scale * qv[j] * __expf(g0[j]);
+        vals[4 + j] = p.scale * qv[4 + j] * __expf(g1[j]);
       }
       uint4 o;
       o.x = pack_bf16x2(vals[0], vals[1]); o.y = pack_bf16x2(vals[2], vals[3]);
@@ -410,7 +410,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_intra_kernel(const PrefillP
         for (int j = 0; j < 4; ++j) {
           const int row = 16 * I + 4 * g + j;
           if (s2 < row) sm.at[sw32<C>(s2, row)] = sm.at[sw32<C>(row, row)] * dA[j];
-          pm[rec_elem<C>(row, 32 * (s2 >> 5) + perm_slot(s2 & 31))] = bf16_bits(s2 <= row ? dP[j] : 0.f);
+          pm[rec_elem<C>(row, 32 * (s2 >> 5) + perm_slot(s2 & 31))] = bf16_bits(s2 <= row ? p.scale * dP[j] : 0.f);
         }
       } else {
         // Diagonal block pairwise: lane (t, cq) = (m, g) covers row t and a
@@ -455,7 +455,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_intra_kernel(const PrefillP
           for (int s3 = 0; s3 < 16; ++s3) {
             const int col = 16 * I + s3;
             if (s3 < t) sm.at[sw32<C>(col, row)] = bt * ares[s3];
-            pm[rec_elem<C>(row, 32 * (col >> 5) + perm_slot(col & 31))] = bf16_bits(s3 <= t ? pres[s3] : 0.f);
+            pm[rec_elem<C>(row, 32 * (col >> 5) + perm_slot(col & 31))] = bf16_bits(s3 <= t ? p.scale * pres[s3] : 0.f);
           }
         }
       }
@@ -625,22 +625,26 @@ struct StateBuf {
   float eg[K];
 };
 
-// Copy record `rec`'s LDS part into `b` by LDS DMA: lane l of a wave writes
-// its 16 bytes at the wave's base + 16 l, so slot i takes piece i. Nothing
-// passes through registers; the copy runs until the next vmcnt wait.
+// Copy record `rec`'s LDS part into `b` by buffer-to-LDS DMA: lane l of a
+// wave writes its 16 bytes at the wave's LDS base + 16 l, so slot i takes
+// piece i. Nothing passes through registers and no per-lane address math is
+// needed; the copy runs until the next vmcnt wait. `wave` is the wave index
+// in a scalar register.
 template <int K, int V>
-__device__ __forceinline__ void dma_chunk(const char* rec, StateBuf<K, V>* b, int tid) {
+__device__ __forceinline__ void dma_chunk(const char* rec, StateBuf<K, V>* b, int tid, int wave) {
   constexpr int total = static_cast<int>(sizeof(StateBuf<K, V>) / 16);
   constexpr int full = total / kThreads, rem = total % kThreads;
-  const uint4* src = reinterpret_cast<const uint4*>(rec);
-  uint4* dst = reinterpret_cast<uint4*>(b);
-  const int wbase = tid & ~63;
+  const __amdgpu_buffer_rsrc_t rr = make_rsrc(rec, static_cast<uint32_t>(sizeof(StateBuf<K, V>)));
+  uint4* dst = reinterpret_cast<uint4*>(b) + wave * 64;
+  const int voff = tid * 16;
 #pragma unroll
   for (int r = 0; r < full; ++r)
-    __builtin_amdgcn_global_load_lds(src + r * kThreads + tid, dst + r * kThreads + wbase, 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, dst + r * kThreads, 16, voff, r * kThreads * 16, 0, 0);
   if constexpr (rem > 0) {
+    // Only lanes whose slot lies inside the record take part (inactive lanes
+    // write nothing).
     if (tid < rem)
-      __builtin_amdgcn_global_load_lds(src + full * kThreads + tid, dst + full * kThreads + wbase, 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, dst + full * kThreads, 16, voff, full * kThreads * 16, 0, 0);
   }
 }
 
@@ -690,10 +694,11 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_state_kernel(const PrefillP
   const int H = p.H;
   if (pair >= p.num_seqs * H) return;
   const int seq = pair / H, h = pair % H;
-  const int64_t bos = p.cu_seqlens[seq];
-  const int64_t eos = p.cu_seqlens[seq + 1];
-  const int c0 = chunk_start[seq];
-  const int nch = chunk_start[seq + 1] - c0;
+  // Values loaded from wave-uniform addresses, kept in scalar registers.
+  const int64_t bos = uniform(static_cast<int64_t>(p.cu_seqlens[seq]));
+  const int64_t eos = uniform(static_cast<int64_t>(p.cu_seqlens[seq + 1]));
+  const int c0 = uniform(chunk_start[seq]);
+  const int nch = uniform(chunk_start[seq + 1]) - c0;
   if (nch <= 0 || eos > p.num_tokens || bos < 0) return;
   // Records exist for at most max_chunks chunks (sized from the host's token
   // count); inconsistent cu_seqlens must not send us past them.
@@ -702,12 +707,13 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_state_kernel(const PrefillP
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
+  const int wave = uniform(w);
   const int m = lane & 15;
   const int g = lane >> 4;
   const int col0 = vh * 64 + 16 * w;
   const int64_t HV = static_cast<int64_t>(H) * V;
 
-  const int64_t slot = static_cast<int64_t>(p.indices[static_cast<int64_t>(seq) * p.index_stride]);
+  const int64_t slot = uniform(static_cast<int64_t>(p.indices[static_cast<int64_t>(seq) * p.index_stride]));
   if (slot < 0) {
     // Null slot: zero output rows, no state traffic.
     for (int64_t t = bos; t < eos; ++t)
@@ -716,7 +722,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_state_kernel(const PrefillP
   }
 
   float* st = p.pool + slot * p.slot_stride + static_cast<int64_t>(h) * K * V;
-  const bool init = p.has_initial_state == nullptr || p.has_initial_state[seq] != 0;
+  const bool init = p.has_initial_state == nullptr || uniform(static_cast<int32_t>(p.has_initial_state[seq])) != 0;
   // Without an initial state the range is empty and every load reads zero;
   // all loads are issued before the first use.
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(st, init ? static_cast<uint32_t>(K * V * 4) : 0u);
@@ -732,14 +738,15 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_state_kernel(const PrefillP
   auto rec_of = [&](int cc) {
     return recs + (static_cast<int64_t>(c0 + cc) * H + h) * static_cast<int64_t>(R::bytes);
   };
+  // U fragments: lane's 16 bytes of tile (pb, col0 / 16) at a fixed offset.
+  const int u_lane = ((col0 / 16) * 64 + lane) * 16;
   auto load_u = [&](int cc) {
-    const f32x4* uf = reinterpret_cast<const f32x4*>(rec_of(cc) + R::Uf);
+    const __amdgpu_buffer_rsrc_t ru = make_rsrc(rec_of(cc) + R::Uf, static_cast<uint32_t>(C * V * 4));
 #pragma unroll
-    for (int pb = 0; pb < 4; ++pb) Upre[pb] = uf[(pb * (V / 16) + col0 / 16) * 64 + lane];
+    for (int pb = 0; pb < 4; ++pb) Upre[pb] = buffer_load_f32x4<0>(ru, u_lane, pb * (V / 16) * 64 * 16);
   };
-  dma_chunk<K, V>(rec_of(0), &buf[0], tid);
+  dma_chunk<K, V>(rec_of(0), &buf[0], tid, wave);
   load_u(0);
-  const float scale = p.scale;
   // Lane (m, g) of the transposed output tile of position block pb holds
   // channels col0 + 4 g .. + 3 of position 16 pb + m: 8 contiguous bytes.
   const int out_lane = static_cast<int>(m * HV + h * V + col0 + 4 * g) * 2;
@@ -753,7 +760,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_state_kernel(const PrefillP
 #pragma unroll
     for (int pb = 0; pb < 4; ++pb) Vp[pb] = Upre[pb];
     if (cc + 1 < nch) {
-      dma_chunk<K, V>(rec_of(cc + 1), &buf[(cc + 1) & 1], tid);
+      dma_chunk<K, V>(rec_of(cc + 1), &buf[(cc + 1) & 1], tid, wave);
       load_u(cc + 1);
     }
 
@@ -831,8 +838,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_state_kernel(const PrefillP
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.out + t0 * HV, static_cast<uint32_t>(n * HV * 2));
 #pragma unroll
     for (int pb = 0; pb < 4; ++pb) {
-      const uint32_t lo = pack_bf16x2(scale * Ot[pb][0], scale * Ot[pb][1]);
-      const uint32_t hi = pack_bf16x2(scale * Ot[pb][2], scale * Ot[pb][3]);
+      const uint32_t lo = pack_bf16x2(Ot[pb][0], Ot[pb][1]);
+      const uint32_t hi = pack_bf16x2(Ot[pb][2], Ot[pb][3]);
       typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
       __builtin_amdgcn_raw_buffer_store_b64(u32x2{lo, hi}, ro, out_lane + static_cast<int>(16 * pb * HV * 2), 0, 0);
     }
