@@ -118,6 +118,12 @@ __device__ __forceinline__ int rec_elem(int r, int c) {
   return r * N + ((((c >> 3) ^ swz<N>(r)) << 3) | (c & 7));
 }
 
+// MFMA fragment (8 bf16) at logical (row, col) of a swizzled [rows][N] tile.
+template <int N>
+__device__ __forceinline__ bf16x8 frag(const uint16_t* tile, int r, int c) {
+  return lds_frag(tile + rec_elem<N>(r, c));
+}
+
 // Per-(chunk, head) record in the workspace. The first five fields are
 // copied to LDS as one contiguous block by the state kernel; its bf16 tiles
 // are stored with the swizzle above.
@@ -193,21 +199,54 @@ __device__ __forceinline__ int sw32(int t, int c) {
 }
 
 // Intra-kernel LDS: 80 KiB at K = 128, so two workgroups share a CU.
-//  k    bf16 [C][K]  keys of the chunk (zero rows past its end)
-//  q    bf16 [C][K]  queries; after the A/P phase: scratch of the blocked
-//                    inverse, then -W for the coalesced copy-out
-//  gam  fp32 [C][K]  cumulative log-decay
-//  at   fp32 [C][C]  raw_g (bf16 [C][K]) at load time; then A^T strictly
-//                    above the diagonal (at(s,t) = A[t][s]), T = (I + A)^{-1}
-//                    strictly below it (unit diagonal implicit), beta on it
+//  k   bf16 [C][K] (sw16)  keys (zero rows past the chunk end); on the
+//                          factored path overwritten by K o R
+//  q   bf16 [C][K] (sw16)  queries; factored path: Q o R. After A/P:
+//                          -W staging for the coalesced copy-out
+//  u   union of
+//        gam  fp32 [C][K] (sw32)  cumulative log-decay (exact path)
+//        kf   bf16 [C][K] (sw16)  K o F (factored path), and
+//        x    fp32 scratch: part totals, gam at block starts, per-block
+//             decay ranges and the channel factors c_IJ until A/P is done;
+//             then (K o e^gam)^T, bf16 [K][C] (swz<C>), the B operand of W
+//  at  fp32 [C][C] (sw32)  raw_g (bf16 [C][K]) at load time; then A^T
+//                          strictly above the diagonal (at(s,t) = A[t][s]),
+//                          T = (I + A)^{-1} strictly below it (unit
+//                          diagonal implicit), beta on it
 template <int K, int V>
 struct IntraSmem {
   uint16_t k[C * K];
   uint16_t q[C * K];
-  float gam[C * K];
+  union {
+    float gam[C * K];
+    struct {
+      uint16_t kf[C * K];
+      float x[C * K / 2];
+    } f;
+  } u;
   float at[C * C];
   static_assert(sizeof(float) * C * C >= sizeof(uint16_t) * C * K, "raw_g staging must fit in at");
 };
+
+// Layout of the x scratch (in floats).
+template <int K>
+struct XLayout {
+  static constexpr int PARTS = kThreads / K;  // threads per channel in the gate scan
+  static constexpr int tot = 0;               // [PARTS][K] partial sums of the gate scan
+  static constexpr int bnd = tot + PARTS * K; // [4][K] gam at rows 16 I
+  static constexpr int dmax = bnd + 4 * K;    // [4 blocks][2] largest decay range per wave
+  static constexpr int cij = dmax + 16;       // [10][K] e^{gam(16 I) - gam(16 J)}, J <= I
+  static constexpr int end = cij + 10 * K;
+  static_assert(end <= C * K / 2, "x scratch overflows its area");
+};
+
+// Factored-path bound on a 16-row block's decay range: every factored
+// operand then lies in [e^-80, e^80], inside bf16/fp32 range.
+constexpr float kMaxBlockDecay = 80.f;
+
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
 
 template <int K, int V>
 __global__ __launch_bounds__(kThreads, 2) void chunk_intra_kernel(const PrefillParams p,
@@ -215,6 +254,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_intra_kernel(const PrefillP
                                                                   char* recs) {
   using R = Rec<K, V>;
   using SM = IntraSmem<K, V>;
+  using XL = XLayout<K>;
   __shared__ SM sm;
 
   const int H = p.H;
@@ -230,9 +270,9 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_intra_kernel(const PrefillP
     if (chunk_start[mid] <= c) lo = mid; else hi = mid;
   }
   const int seq = lo;
-  const int64_t bos = p.cu_seqlens[seq];
-  const int64_t eos = p.cu_seqlens[seq + 1];
-  const int64_t t0 = bos + static_cast<int64_t>(C) * (c - chunk_start[seq]);
+  const int64_t bos = uniform(static_cast<int64_t>(p.cu_seqlens[seq]));
+  const int64_t eos = uniform(static_cast<int64_t>(p.cu_seqlens[seq + 1]));
+  const int64_t t0 = bos + static_cast<int64_t>(C) * (c - uniform(chunk_start[seq]));
   if (eos > p.num_tokens || t0 >= eos) return;  // malformed cu_seqlens: touch nothing
   const int n = static_cast<int>(min<int64_t>(C, eos - t0));
 
@@ -245,8 +285,10 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_intra_kernel(const PrefillP
   constexpr int KPM = (KP8 > 16 ? 16 : KP8) - 1;
 
   char* rec = recs + (static_cast<int64_t>(c) * H + h) * static_cast<int64_t>(R::bytes);
+  float* x = sm.u.f.x;
+  uint16_t* wkt = reinterpret_cast<uint16_t*>(sm.u.f.x);
 
-  // ---- 1. k, q and raw_g tiles by LDS DMA; rows past the chunk end read 0
+  // ---- 1. raw_g, k and q tiles by LDS DMA; rows past the chunk end read 0
   uint16_t* rawg = reinterpret_cast<uint16_t*>(sm.at);
   {
     const int64_t rs = p.qkv_row_stride * 2;  // bytes per mixed_qkv row
@@ -258,153 +300,172 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_intra_kernel(const PrefillP
       const int t = ps / KP8;
       const int pl = (ps % KP8) ^ (t & KPM);      // logical piece stored there
       const int slot = r * kThreads + (tid & ~63);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rg, reinterpret_cast<uint4*>(rawg) + slot, 16, (t * H * K + h * K + pl * 8) * 2, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < C * KP8 / kThreads; ++r) {
+      const int ps = r * kThreads + tid;
+      const int t = ps / KP8;
+      const int pl = (ps % KP8) ^ (t & KPM);
+      const int slot = r * kThreads + (tid & ~63);
       const int qoff = static_cast<int>(t * rs) + (h * K + pl * 8) * 2;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, reinterpret_cast<uint4*>(sm.q) + slot, 16, qoff, 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, reinterpret_cast<uint4*>(sm.k) + slot, 16, qoff + H * K * 2, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rg, reinterpret_cast<uint4*>(rawg) + slot, 16, (t * H * K + h * K + pl * 8) * 2, 0, 0, 0);
     }
   }
   wait_vmem();
   __syncthreads();
+
+  // ---- 2. gate and cumulative log-decay, in registers ---------------------
+  // Thread (ch, part) scans PP consecutive positions of channel ch; partial
+  // totals are added across parts through x.
+  constexpr int PARTS = XL::PARTS;
+  constexpr int PP = C / PARTS;          // 32 at K = 128, 16 at K = 64
+  constexpr int NBP = PP / 16;           // 16-row blocks per part
+  constexpr int WPP = K / 64;            // waves per part
+  static_assert(PP % 16 == 0, "parts hold whole blocks");
+  const int ch = tid % K, part = tid / K;
+  float gm[PP];
+  float before = 0.f, gl = 0.f;
   {
-    // Gate and inclusive cumulative sum along positions: thread (ch, part)
-    // scans PP positions; partial totals are then added across parts.
-    constexpr int PARTS = kThreads / K;
-    constexpr int PP = C / PARTS;
-    const int ch = tid % K, part = tid / K;
     const float a = __expf(p.A_log[h]);
     const float dtb = p.dt_bias[h * K + ch];
     const bool has_lb = p.has_lb != 0;
     float acc = 0.f;
-#pragma unroll 8
+#pragma unroll
     for (int i = 0; i < PP; ++i) {
       const int t = part * PP + i;
       float gv = 0.f;  // padded positions do not decay, so row 63 holds gam_last
       if (t < n) gv = gate_log_decay(bf16_to_f32(rawg[sw16<K>(t, ch)]), dtb, a, has_lb, p.lower_bound);
       acc += gv;
-      sm.gam[sw32<K>(t, ch)] = acc;
+      gm[i] = acc;
     }
+    x[XL::tot + part * K + ch] = acc;
     const float beta_t = (tid < n) ? sigmoid_f32(bf16_to_f32(p.raw_beta[(t0 + tid) * H + h])) : 0.f;
-    lds_barrier();  // raw_g fully consumed; partial sums visible
-    float before = 0.f;
-    for (int q2 = 0; q2 < part; ++q2) before += sm.gam[sw32<K>((q2 + 1) * PP - 1, ch)];
+    lds_barrier();  // raw_g consumed; partial totals visible
+#pragma unroll
+    for (int q2 = 0; q2 < PARTS; ++q2) {
+      const float tq = x[XL::tot + q2 * K + ch];
+      if (q2 < part) before += tq;
+      gl += tq;
+    }
     if (tid < C) sm.at[sw32<C>(tid, tid)] = beta_t;  // beta on the diagonal of at
-    lds_barrier();
-    if (part > 0)
-      for (int i = 0; i < PP; ++i) sm.gam[sw32<K>(part * PP + i, ch)] += before;
+#pragma unroll
+    for (int i = 0; i < PP; ++i) gm[i] += before;
+    // Block bounds and decay ranges (a range is the same before and after
+    // adding the offset of earlier parts).
+#pragma unroll
+    for (int b = 0; b < NBP; ++b) {
+      const int I = part * NBP + b;
+      x[XL::bnd + I * K + ch] = gm[16 * b];
+      float d = gm[16 * b] - gm[16 * b + 15];
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) d = fmaxf(d, __shfl_xor(d, off));
+      if (lane == 0) x[XL::dmax + 2 * I + (w % WPP)] = d;
+    }
+    if (part == 0) reinterpret_cast<float*>(rec + R::Eg)[ch] = __expf(gl);
   }
   lds_barrier();
+  bool fast = true;
+#pragma unroll
+  for (int I = 0; I < 4; ++I)
+#pragma unroll
+    for (int v = 0; v < WPP; ++v) fast = fast && x[XL::dmax + 2 * I + v] <= kMaxBlockDecay;
 
-  // ---- 2. elementwise outputs: e^{gam_last}, Q o e^gam, (K o e^{gl-gam})^T
-  {
-    float* eg = reinterpret_cast<float*>(rec + R::Eg);
-    for (int ch = tid; ch < K; ch += kThreads) eg[ch] = __expf(sm.gam[sw32<K>(C - 1, ch)]);
+  // K o e^gam of this thread's positions, as bf16 pairs, kept in registers
+  // until x is free.
+  uint32_t wkp[PP / 2];
+
+  if (fast) {
+    // ---- 3f. factored operands -------------------------------------------
+    // With the reference rho_I = gam(16 I) of each 16-row block,
+    //   e^{gam_t - gam_s} = R_t F_s c_IJ,  R_t = e^{gam_t - rho_I},
+    //   F_s = e^{rho_J - gam_s},  c_IJ = e^{rho_I - rho_J},
+    // for t in block I and s in block J <= I (c_II = 1). Under the
+    // decay-range bound R lies in [e^-80, 1] and F in [1, e^80]; for J < I,
+    // F_s c_IJ = e^{rho_I - gam_s} <= 1. Nothing overflows, and the diagonal
+    // blocks take their operands as stored (one bf16 rounding each).
+    // Q o e^gam = (Q o R) e^{rho_I} and K o e^{gl - gam} = (K o F) e^{gl - rho_I}
+    // need no further exponential.
+    for (int e = tid; e < 10 * K; e += kThreads) {
+      const int pr = e / K, cc = e % K;
+      const int I = pr < 1 ? 0 : pr < 3 ? 1 : pr < 6 ? 2 : 3;
+      const int J = pr - I * (I + 1) / 2;
+      x[XL::cij + e] = __expf(x[XL::bnd + I * K + cc] - x[XL::bnd + J * K + cc]);
+    }
     uint16_t* qg = reinterpret_cast<uint16_t*>(rec + R::Qg);
-    for (int e = tid; e < C * KP8; e += kThreads) {
-      const int t = e / KP8, pc = e % KP8;
-      const int cb = (pc >> 2) * 32 + 4 * (pc & 3);  // storage piece pc holds channels cb..cb+3, cb+16..cb+19
-      float qv[8], vals[8];
-      {
-        const uint2 w0 = *reinterpret_cast<const uint2*>(&sm.q[sw16<K>(t, cb)]);
-        const uint2 w1 = *reinterpret_cast<const uint2*>(&sm.q[sw16<K>(t, cb + 16)]);
-        qv[0] = __uint_as_float(w0.x << 16); qv[1] = __uint_as_float(w0.x & 0xffff0000u);
-        qv[2] = __uint_as_float(w0.y << 16); qv[3] = __uint_as_float(w0.y & 0xffff0000u);
-        qv[4] = __uint_as_float(w1.x << 16); qv[5] = __uint_as_float(w1.x & 0xffff0000u);
-        qv[6] = __uint_as_float(w1.y << 16); qv[7] = __uint_as_float(w1.y & 0xffff0000u);
-      }
-      const f32x4 g0 = *reinterpret_cast<const f32x4*>(&sm.gam[sw32<K>(t, cb)]);
-      const f32x4 g1 = *reinterpret_cast<const f32x4*>(&sm.gam[sw32<K>(t, cb + 16)]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        vals[j] = p.scale * qv[j] * __expf(g0[j]);
-        vals[4 + j] = p.scale * qv[4 + j] * __expf(g1[j]);
-      }
-      uint4 o;
-      o.x = pack_bf16x2(vals[0], vals[1]); o.y = pack_bf16x2(vals[2], vals[3]);
-      o.z = pack_bf16x2(vals[4], vals[5]); o.w = pack_bf16x2(vals[6], vals[7]);
-      *reinterpret_cast<uint4*>(qg + rec_elem<K>(t, pc * 8)) = o;
-    }
     uint16_t* kgt = reinterpret_cast<uint16_t*>(rec + R::KgT);
-    for (int e = tid; e < K * (C / 8); e += kThreads) {
-      const int ch = e / (C / 8), pc = e % (C / 8);
-      const int base = (pc >> 2) * 32;
-      const float gl = sm.gam[sw32<K>(C - 1, ch)];
-      float vals[8];
+    const int qcol = 32 * (ch >> 5) + perm_slot(ch & 31);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int t = base + perm_phys((pc & 3) * 8 + j);
-        vals[j] = bf16_to_f32(sm.k[sw16<K>(t, ch)]) * __expf(gl - sm.gam[sw32<K>(t, ch)]);
+    for (int b = 0; b < NBP; ++b) {
+      const float rho = gm[16 * b];
+      const float E = __expf(rho), G = __expf(gl - rho);
+#pragma unroll
+      for (int u4 = 0; u4 < 4; ++u4) {
+        float kgv[4];
+#pragma unroll
+        for (int i3 = 0; i3 < 4; ++i3) {
+          const int i = 16 * b + 4 * u4 + i3;
+          const int t = part * PP + i;
+          const int o = sw16<K>(t, ch);
+          const float kv = bf16_to_f32(sm.k[o]), qv = bf16_to_f32(sm.q[o]);
+          const float Rt = __expf(gm[i] - rho), Ft = __expf(rho - gm[i]);
+          const float kr = kv * Rt, qr = qv * Rt, kf = kv * Ft;
+          sm.k[o] = bf16_bits(kr);
+          sm.q[o] = bf16_bits(qr);
+          sm.u.f.kf[o] = bf16_bits(kf);
+          qg[rec_elem<K>(t, qcol)] = bf16_bits(p.scale * qr * E);
+          kgv[i3] = kf * G;
+          const uint32_t wk = bf16_bits(kr * E);
+          if (i & 1) wkp[i >> 1] |= wk << 16;
+          else wkp[i >> 1] = wk;
+        }
+        // (K o e^{gl - gam})^T: 4 consecutive positions are 8 contiguous
+        // bytes of the permuted order.
+        const int tp = part * PP + 16 * b + 4 * u4;
+        const int pin = tp & 31;
+        const int slot0 = pin < 16 ? 2 * pin : 2 * (pin - 16) + 4;
+        uint2 v;
+        v.x = pack_bf16x2(kgv[0], kgv[1]);
+        v.y = pack_bf16x2(kgv[2], kgv[3]);
+        *reinterpret_cast<uint2*>(kgt + rec_elem<C>(ch, 32 * (tp >> 5) + slot0)) = v;
       }
-      uint4 o;
-      o.x = pack_bf16x2(vals[0], vals[1]); o.y = pack_bf16x2(vals[2], vals[3]);
-      o.z = pack_bf16x2(vals[4], vals[5]); o.w = pack_bf16x2(vals[6], vals[7]);
-      *reinterpret_cast<uint4*>(kgt + rec_elem<C>(ch, pc * 8)) = o;
     }
-  }
+    lds_barrier();
 
-  // ---- 3. A and P by 16x16 blocks (I, J), J <= I --------------------------
-  // Fast path for block-row I: one reference row r = 16 I + 7. For s in an
-  // earlier block e^{gam_r - gam_s} <= 1; inside block I every factor lies
-  // within e^{+-D}, D = the block's largest decay range over channels. If
-  // D <= 80 every factor fits bf16 and every product with s <= t equals
-  // e^{gam_t - gam_s} <= 1, so the whole block-row runs on MFMA. Otherwise
-  // the exact scheme: reference 16 I for J < I (both factors <= 1) and
-  // pairwise fp32 exponentials on the diagonal block.
-  // A goes transposed into at (strictly above the diagonal); P goes straight
-  // to the workspace (bf16, positions permuted), including the zero blocks
-  // above the diagonal that the state kernel reads.
-  {
-    uint16_t* pm = reinterpret_cast<uint16_t*>(rec + R::Pm);
-    const int blocks[4][3][2] = {{{3, 3}, {3, 0}, {0, 0}},
-                                 {{2, 2}, {3, 1}, {1, 0}},
-                                 {{1, 1}, {3, 2}, {-1, -1}},
-                                 {{2, 1}, {2, 0}, {-1, -1}}};
-    for (int bi = 0; bi < 3; ++bi) {
-      const int I = blocks[w][bi][0], J = blocks[w][bi][1];
-      if (I < 0) break;
-      float dloc = 0.f;
-      for (int ch = lane; ch < K; ch += 64)
-        dloc = fmaxf(dloc, sm.gam[sw32<K>(16 * I, ch)] - sm.gam[sw32<K>(16 * I + 15, ch)]);
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) dloc = fmaxf(dloc, __shfl_xor(dloc, off));
-      const bool fast = dloc <= 80.f;  // wave-uniform after the butterfly
-      if (J < I || fast) {
-        const int r = fast ? 16 * I + 7 : 16 * I;
+    // ---- 4f. A and P by 16x16 blocks on MFMA ------------------------------
+    // A goes transposed into at (strictly above the diagonal); scale P goes
+    // straight to the workspace (bf16, positions permuted), including the
+    // zero blocks above the diagonal that the state kernel reads.
+    {
+      uint16_t* pm = reinterpret_cast<uint16_t*>(rec + R::Pm);
+      const int blocks[4][3][2] = {{{3, 3}, {3, 0}, {0, 0}},
+                                   {{2, 2}, {3, 1}, {1, 0}},
+                                   {{1, 1}, {3, 2}, {-1, -1}},
+                                   {{2, 1}, {2, 0}, {-1, -1}}};
+      for (int bi = 0; bi < 3; ++bi) {
+        const int I = blocks[w][bi][0], J = blocks[w][bi][1];
+        if (I < 0) break;
+        const float* cv = x + XL::cij + (I * (I + 1) / 2 + J) * K;
         f32x4 dA = {0.f, 0.f, 0.f, 0.f}, dP = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < K / 32; ++kb) {
           const int c0 = 32 * kb + 8 * g;
-          const uint4 ka = *reinterpret_cast<const uint4*>(&sm.k[sw16<K>(16 * I + m, c0)]);
-          const uint4 kbv = *reinterpret_cast<const uint4*>(&sm.k[sw16<K>(16 * J + m, c0)]);
-          const uint4 qav = *reinterpret_cast<const uint4*>(&sm.q[sw16<K>(16 * I + m, c0)]);
-          const uint32_t qaw[4] = {qav.x, qav.y, qav.z, qav.w};
-          const f32x4 gt0 = *reinterpret_cast<const f32x4*>(&sm.gam[sw32<K>(16 * I + m, c0)]);
-          const f32x4 gt1 = *reinterpret_cast<const f32x4*>(&sm.gam[sw32<K>(16 * I + m, c0 + 4)]);
-          const f32x4 gr0 = *reinterpret_cast<const f32x4*>(&sm.gam[sw32<K>(r, c0)]);
-          const f32x4 gr1 = *reinterpret_cast<const f32x4*>(&sm.gam[sw32<K>(r, c0 + 4)]);
-          const f32x4 gs0 = *reinterpret_cast<const f32x4*>(&sm.gam[sw32<K>(16 * J + m, c0)]);
-          const f32x4 gs1 = *reinterpret_cast<const f32x4*>(&sm.gam[sw32<K>(16 * J + m, c0 + 4)]);
-          const uint32_t kaw[4] = {ka.x, ka.y, ka.z, ka.w};
-          const uint32_t kbw[4] = {kbv.x, kbv.y, kbv.z, kbv.w};
-          float ak[8], aq[8], bk[8];
+          const bf16x8 ak = lds_frag(&sm.k[sw16<K>(16 * I + m, c0)]);
+          const bf16x8 aq = lds_frag(&sm.q[sw16<K>(16 * I + m, c0)]);
+          const bf16x8 bk = lds_frag(&sm.u.f.kf[sw16<K>(16 * J + m, c0)]);
+          const f32x4 c0v = *reinterpret_cast<const f32x4*>(cv + c0);
+          const f32x4 c1v = *reinterpret_cast<const f32x4*>(cv + c0 + 4);
+          bf16x8 b = bk;
+          if (J < I) {
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const float gt = j < 4 ? gt0[j] : gt1[j - 4];
-            const float gr = j < 4 ? gr0[j] : gr1[j - 4];
-            const float gs = j < 4 ? gs0[j] : gs1[j - 4];
-            const float kav = __uint_as_float(j & 1 ? (kaw[j >> 1] & 0xffff0000u) : (kaw[j >> 1] << 16));
-            const float kbf = __uint_as_float(j & 1 ? (kbw[j >> 1] & 0xffff0000u) : (kbw[j >> 1] << 16));
-            const float ea = __expf(gt - gr);
-            ak[j] = kav * ea;
-            aq[j] = __uint_as_float(j & 1 ? (qaw[j >> 1] & 0xffff0000u) : (qaw[j >> 1] << 16)) * ea;
-            bk[j] = kbf * __expf(gr - gs);
+            for (int j = 0; j < 8; ++j)
+              b[j] = static_cast<__bf16>(static_cast<float>(bk[j]) * (j < 4 ? c0v[j] : c1v[j - 4]));
           }
-          const bf16x8 b = to_bf16x8(bk);
-          dA = mfma16(to_bf16x8(ak), b, dA);
-          dP = mfma16(to_bf16x8(aq), b, dP);
+          dA = mfma16(ak, b, dA);
+          dP = mfma16(aq, b, dP);
         }
-        // Lane holds rows 16 I + 4 g + j of column s = 16 J + m. Entries
-        // above the diagonal are dropped (they may be huge or non-finite).
+        // Lane holds rows 16 I + 4 g + j of column s = 16 J + m.
         const int s2 = 16 * J + m;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -412,63 +473,207 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_intra_kernel(const PrefillP
           if (s2 < row) sm.at[sw32<C>(s2, row)] = sm.at[sw32<C>(row, row)] * dA[j];
           pm[rec_elem<C>(row, 32 * (s2 >> 5) + perm_slot(s2 & 31))] = bf16_bits(s2 <= row ? p.scale * dP[j] : 0.f);
         }
-      } else {
-        // Diagonal block pairwise: lane (t, cq) = (m, g) covers row t and a
-        // quarter of the channels; partial sums are reduced over quarters.
-        constexpr int CQ = K / 4;
-        const int t = m, cq = g, row = 16 * I + t;
-        float ares[16], pres[16];
+      }
+      if (w == 3) {
+        // Zero P blocks above the diagonal that the state kernel reads:
+        // rows 0..15 x cols 16..31 and rows 32..47 x cols 48..63.
 #pragma unroll
-        for (int s3 = 0; s3 < 16; ++s3) {
-          ares[s3] = 0.f;
-          pres[s3] = 0.f;
-        }
-        for (int i8 = 0; i8 < CQ; i8 += 8) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int ch = cq * CQ + i8 + i;
-            const float gt = sm.gam[sw32<K>(row, ch)];
-            const float kt = bf16_to_f32(sm.k[sw16<K>(row, ch)]);
-            const float qti = bf16_to_f32(sm.q[sw16<K>(row, ch)]);
-#pragma unroll
-            for (int s3 = 0; s3 < 16; ++s3) {
-              const int srow = 16 * I + s3;
-              // gam is non-increasing, so for s <= t the exponent is <= 0;
-              // the min only keeps the masked s > t entries finite.
-              const float ke = bf16_to_f32(sm.k[sw16<K>(srow, ch)]) *
-                               __expf(fminf(gt - sm.gam[sw32<K>(srow, ch)], 0.f));
-              ares[s3] = fmaf(kt, ke, ares[s3]);
-              pres[s3] = fmaf(qti, ke, pres[s3]);
-            }
-          }
-        }
-#pragma unroll
-        for (int s3 = 0; s3 < 16; ++s3) {
-          ares[s3] += __shfl_xor(ares[s3], 16);
-          ares[s3] += __shfl_xor(ares[s3], 32);
-          pres[s3] += __shfl_xor(pres[s3], 16);
-          pres[s3] += __shfl_xor(pres[s3], 32);
-        }
-        if (cq == 0) {
-          const float bt = sm.at[sw32<C>(row, row)];
-#pragma unroll
-          for (int s3 = 0; s3 < 16; ++s3) {
-            const int col = 16 * I + s3;
-            if (s3 < t) sm.at[sw32<C>(col, row)] = bt * ares[s3];
-            pm[rec_elem<C>(row, 32 * (col >> 5) + perm_slot(col & 31))] = bf16_bits(s3 <= t ? p.scale * pres[s3] : 0.f);
-          }
+        for (int j = 0; j < 4; ++j) {
+          const int row = 4 * g + j;
+          pm[rec_elem<C>(row, perm_slot(16 + m))] = 0;
+          pm[rec_elem<C>(32 + row, 32 + perm_slot(16 + m))] = 0;
         }
       }
     }
-    if (w == 3) {
-      // Zero P blocks above the diagonal that the state kernel reads:
-      // rows 0..15 x cols 16..31 and rows 32..47 x cols 48..63.
+  } else {
+    // ---- 3e/4e. exact path (a block decays by more than the bound) --------
+    lds_barrier();  // every thread has read the decay ranges (gam overlays x)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = 4 * g + j;
-        pm[rec_elem<C>(row, perm_slot(16 + m))] = 0;
-        pm[rec_elem<C>(32 + row, 32 + perm_slot(16 + m))] = 0;
+    for (int i = 0; i < PP; ++i) sm.u.gam[sw32<K>(part * PP + i, ch)] = gm[i];
+    lds_barrier();
+    // Exact path, elementwise outputs: Q o e^gam and (K o e^{gl-gam})^T.
+    {
+      uint16_t* qg = reinterpret_cast<uint16_t*>(rec + R::Qg);
+      for (int e = tid; e < C * KP8; e += kThreads) {
+        const int t = e / KP8, pc = e % KP8;
+        const int cb = (pc >> 2) * 32 + 4 * (pc & 3);  // storage piece pc holds channels cb..cb+3, cb+16..cb+19
+        float qv[8], vals[8];
+        {
+          const uint2 w0 = *reinterpret_cast<const uint2*>(&sm.q[sw16<K>(t, cb)]);
+          const uint2 w1 = *reinterpret_cast<const uint2*>(&sm.q[sw16<K>(t, cb + 16)]);
+          qv[0] = __uint_as_float(w0.x << 16); qv[1] = __uint_as_float(w0.x & 0xffff0000u);
+          qv[2] = __uint_as_float(w0.y << 16); qv[3] = __uint_as_float(w0.y & 0xffff0000u);
+          qv[4] = __uint_as_float(w1.x << 16); qv[5] = __uint_as_float(w1.x & 0xffff0000u);
+          qv[6] = __uint_as_float(w1.y << 16); qv[7] = __uint_as_float(w1.y & 0xffff0000u);
+        }
+        const f32x4 g0 = *reinterpret_cast<const f32x4*>(&sm.u.gam[sw32<K>(t, cb)]);
+        const f32x4 g1 = *reinterpret_cast<const f32x4*>(&sm.u.gam[sw32<K>(t, cb + 16)]);
+  #pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          vals[j] = p.scale * qv[j] * __expf(g0[j]);
+          vals[4 + j] = p.scale * qv[4 + j] * __expf(g1[j]);
+        }
+        uint4 o;
+        o.x = pack_bf16x2(vals[0], vals[1]); o.y = pack_bf16x2(vals[2], vals[3]);
+        o.z = pack_bf16x2(vals[4], vals[5]); o.w = pack_bf16x2(vals[6], vals[7]);
+        *reinterpret_cast<uint4*>(qg + rec_elem<K>(t, pc * 8)) = o;
       }
+      uint16_t* kgt = reinterpret_cast<uint16_t*>(rec + R::KgT);
+      for (int e = tid; e < K * (C / 8); e += kThreads) {
+        const int ch = e / (C / 8), pc = e % (C / 8);
+        const int base = (pc >> 2) * 32;
+        const float gl = sm.u.gam[sw32<K>(C - 1, ch)];
+        float vals[8];
+  #pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int t = base + perm_phys((pc & 3) * 8 + j);
+          vals[j] = bf16_to_f32(sm.k[sw16<K>(t, ch)]) * __expf(gl - sm.u.gam[sw32<K>(t, ch)]);
+        }
+        uint4 o;
+        o.x = pack_bf16x2(vals[0], vals[1]); o.y = pack_bf16x2(vals[2], vals[3]);
+        o.z = pack_bf16x2(vals[4], vals[5]); o.w = pack_bf16x2(vals[6], vals[7]);
+        *reinterpret_cast<uint4*>(kgt + rec_elem<C>(ch, pc * 8)) = o;
+      }
+    }
+
+
+    // Exact path, A and P by 16x16 blocks (I, J), J <= I.
+    // Fast path for block-row I: one reference row r = 16 I + 7. For s in an
+    // earlier block e^{gam_r - gam_s} <= 1; inside block I every factor lies
+    // within e^{+-D}, D = the block's largest decay range over channels. If
+    // D <= 80 every factor fits bf16 and every product with s <= t equals
+    // e^{gam_t - gam_s} <= 1, so the whole block-row runs on MFMA. Otherwise
+    // the exact scheme: reference 16 I for J < I (both factors <= 1) and
+    // pairwise fp32 exponentials on the diagonal block.
+    // A goes transposed into at (strictly above the diagonal); P goes straight
+    // to the workspace (bf16, positions permuted), including the zero blocks
+    // above the diagonal that the state kernel reads.
+    {
+      uint16_t* pm = reinterpret_cast<uint16_t*>(rec + R::Pm);
+      const int blocks[4][3][2] = {{{3, 3}, {3, 0}, {0, 0}},
+                                   {{2, 2}, {3, 1}, {1, 0}},
+                                   {{1, 1}, {3, 2}, {-1, -1}},
+                                   {{2, 1}, {2, 0}, {-1, -1}}};
+      for (int bi = 0; bi < 3; ++bi) {
+        const int I = blocks[w][bi][0], J = blocks[w][bi][1];
+        if (I < 0) break;
+        float dloc = 0.f;
+        for (int ch = lane; ch < K; ch += 64)
+          dloc = fmaxf(dloc, sm.u.gam[sw32<K>(16 * I, ch)] - sm.u.gam[sw32<K>(16 * I + 15, ch)]);
+  #pragma unroll
+        for (int off = 32; off > 0; off >>= 1) dloc = fmaxf(dloc, __shfl_xor(dloc, off));
+        const bool fast = dloc <= 80.f;  // wave-uniform after the butterfly
+        if (J < I || fast) {
+          const int r = fast ? 16 * I + 7 : 16 * I;
+          f32x4 dA = {0.f, 0.f, 0.f, 0.f}, dP = {0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+          for (int kb = 0; kb < K / 32; ++kb) {
+            const int c0 = 32 * kb + 8 * g;
+            const uint4 ka = *reinterpret_cast<const uint4*>(&sm.k[sw16<K>(16 * I + m, c0)]);
+            const uint4 kbv = *reinterpret_cast<const uint4*>(&sm.k[sw16<K>(16 * J + m, c0)]);
+            const uint4 qav = *reinterpret_cast<const uint4*>(&sm.q[sw16<K>(16 * I + m, c0)]);
+            const uint32_t qaw[4] = {qav.x, qav.y, qav.z, qav.w};
+            const f32x4 gt0 = *reinterpret_cast<const f32x4*>(&sm.u.gam[sw32<K>(16 * I + m, c0)]);
+            const f32x4 gt1 = *reinterpret_cast<const f32x4*>(&sm.u.gam[sw32<K>(16 * I + m, c0 + 4)]);
+            const f32x4 gr0 = *reinterpret_cast<const f32x4*>(&sm.u.gam[sw32<K>(r, c0)]);
+            const f32x4 gr1 = *reinterpret_cast<const f32x4*>(&sm.u.gam[sw32<K>(r, c0 + 4)]);
+            const f32x4 gs0 = *reinterpret_cast<const f32x4*>(&sm.u.gam[sw32<K>(16 * J + m, c0)]);
+            const f32x4 gs1 = *reinterpret_cast<const f32x4*>(&sm.u.gam[sw32<K>(16 * J + m, c0 + 4)]);
+            const uint32_t kaw[4] = {ka.x, ka.y, ka.z, ka.w};
+            const uint32_t kbw[4] = {kbv.x, kbv.y, kbv.z, kbv.w};
+            float ak[8], aq[8], bk[8];
+  #pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const float gt = j < 4 ? gt0[j] : gt1[j - 4];
+              const float gr = j < 4 ? gr0[j] : gr1[j - 4];
+              const float gs = j < 4 ? gs0[j] : gs1[j - 4];
+              const float kav = __uint_as_float(j & 1 ? (kaw[j >> 1] & 0xffff0000u) : (kaw[j >> 1] << 16));
+              const float kbf = __uint_as_float(j & 1 ? (kbw[j >> 1] & 0xffff0000u) : (kbw[j >> 1] << 16));
+              const float ea = __expf(gt - gr);
+              ak[j] = kav * ea;
+              aq[j] = __uint_as_float(j & 1 ? (qaw[j >> 1] & 0xffff0000u) : (qaw[j >> 1] << 16)) * ea;
+              bk[j] = kbf * __expf(gr - gs);
+            }
+            const bf16x8 b = to_bf16x8(bk);
+            dA = mfma16(to_bf16x8(ak), b, dA);
+            dP = mfma16(to_bf16x8(aq), b, dP);
+          }
+          // Lane holds rows 16 I + 4 g + j of column s = 16 J + m. Entries
+          // above the diagonal are dropped (they may be huge or non-finite).
+          const int s2 = 16 * J + m;
+  #pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int row = 16 * I + 4 * g + j;
+            if (s2 < row) sm.at[sw32<C>(s2, row)] = sm.at[sw32<C>(row, row)] * dA[j];
+            pm[rec_elem<C>(row, 32 * (s2 >> 5) + perm_slot(s2 & 31))] = bf16_bits(s2 <= row ? p.scale * dP[j] : 0.f);
+          }
+        } else {
+          // Diagonal block pairwise: lane (t, cq) = (m, g) covers row t and a
+          // quarter of the channels; partial sums are reduced over quarters.
+          constexpr int CQ = K / 4;
+          const int t = m, cq = g, row = 16 * I + t;
+          float ares[16], pres[16];
+  #pragma unroll
+          for (int s3 = 0; s3 < 16; ++s3) {
+            ares[s3] = 0.f;
+            pres[s3] = 0.f;
+          }
+          for (int i8 = 0; i8 < CQ; i8 += 8) {
+  #pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const int ch = cq * CQ + i8 + i;
+              const float gt = sm.u.gam[sw32<K>(row, ch)];
+              const float kt = bf16_to_f32(sm.k[sw16<K>(row, ch)]);
+              const float qti = bf16_to_f32(sm.q[sw16<K>(row, ch)]);
+  #pragma unroll
+              for (int s3 = 0; s3 < 16; ++s3) {
+                const int srow = 16 * I + s3;
+                // gam is non-increasing, so for s <= t the exponent is <= 0;
+                // the min only keeps the masked s > t entries finite.
+                const float ke = bf16_to_f32(sm.k[sw16<K>(srow, ch)]) *
+                                 __expf(fminf(gt - sm.u.gam[sw32<K>(srow, ch)], 0.f));
+                ares[s3] = fmaf(kt, ke, ares[s3]);
+                pres[s3] = fmaf(qti, ke, pres[s3]);
+              }
+            }
+          }
+  #pragma unroll
+          for (int s3 = 0; s3 < 16; ++s3) {
+            ares[s3] += __shfl_xor(ares[s3], 16);
+            ares[s3] += __shfl_xor(ares[s3], 32);
+            pres[s3] += __shfl_xor(pres[s3], 16);
+            pres[s3] += __shfl_xor(pres[s3], 32);
+          }
+          if (cq == 0) {
+            const float bt = sm.at[sw32<C>(row, row)];
+  #pragma unroll
+            for (int s3 = 0; s3 < 16; ++s3) {
+              const int col = 16 * I + s3;
+              if (s3 < t) sm.at[sw32<C>(col, row)] = bt * ares[s3];
+              pm[rec_elem<C>(row, 32 * (col >> 5) + perm_slot(col & 31))] = bf16_bits(s3 <= t ? p.scale * pres[s3] : 0.f);
+            }
+          }
+        }
+      }
+      if (w == 3) {
+        // Zero P blocks above the diagonal that the state kernel reads:
+        // rows 0..15 x cols 16..31 and rows 32..47 x cols 48..63.
+  #pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int row = 4 * g + j;
+          pm[rec_elem<C>(row, perm_slot(16 + m))] = 0;
+          pm[rec_elem<C>(32 + row, 32 + perm_slot(16 + m))] = 0;
+        }
+      }
+    }
+
+    // K o e^gam from the LDS tiles (k is unchanged on this path).
+#pragma unroll
+    for (int i = 0; i < PP; ++i) {
+      const int t = part * PP + i;
+      const uint32_t wk = bf16_bits(bf16_to_f32(sm.k[sw16<K>(t, ch)]) * __expf(sm.u.gam[sw32<K>(t, ch)]));
+      if (i & 1) wkp[i >> 1] |= wk << 16;
+      else wkp[i >> 1] = wk;
     }
   }
   // v for the U phase, fetched now so its latency hides behind the inverse:
@@ -487,9 +692,17 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_intra_kernel(const PrefillP
                              ? p.qkv[(t0 + t) * p.qkv_row_stride + 2 * H * K + h * V + 16 * nb + m]
                              : static_cast<uint16_t>(0);
       }
-  lds_barrier();
 
-  // ---- 4a. T = (I + A)^{-1}: diagonal blocks by forward substitution ----
+
+  lds_barrier();  // A^T complete; x (or gam) no longer read
+
+  // ---- 4. (K o e^gam)^T into x: 16-byte pieces of 8 positions -----------
+#pragma unroll
+  for (int u8 = 0; u8 < PP / 8; ++u8)
+    *reinterpret_cast<uint4*>(wkt + rec_elem<C>(ch, part * PP + 8 * u8)) =
+        uint4{wkp[4 * u8], wkp[4 * u8 + 1], wkp[4 * u8 + 2], wkp[4 * u8 + 3]};
+
+  // ---- 5. T = (I + A)^{-1}: diagonal blocks by forward substitution -----
   // at(s, t) = A[t][s] for s < t; T strictly below the diagonal of at.
   if (lane < 16) {
     const int blk = w, jc = lane;
@@ -506,38 +719,51 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_intra_kernel(const PrefillP
       if (tt > jc) sm.at[sw32<C>(16 * blk + tt, 16 * blk + jc)] = x[tt];
   }
   lds_barrier();
-  // ---- 4b. off-diagonal blocks of T, by distance from the diagonal -------
-  //   T_IJ = -T_II sum_{J<=L<I} A_IL T_LJ,  A_IL[r][c] = at(16L + c, 16I + r)
+
+  // ---- 6. off-diagonal blocks of T on fp32 MFMA ---------------------------
+  // With the 32-row halves t (blocks 0, 1) and b (blocks 2, 3):
+  //   T_10 = -T_11 A_10 T_00,  T_32 = -T_33 A_32 T_22,  T_bt = -T_bb (A_bt T_tt).
+  // The 16x16x4 product pairs lane group g of step kk with contraction index
+  // 4 g + kk, so an accumulator tile (rows 4 g + j) is the B operand of the
+  // next product as it stands: step kk takes its element j = kk.
   {
-    float* Y = reinterpret_cast<float*>(sm.q);  // q is no longer read: three 16x16 blocks
-    const int rr = tid >> 4, cc = tid & 15;
-    for (int d = 1; d < 4; ++d) {
-      for (int I = d; I < 4; ++I) {
-        const int J = I - d;
-        // L = J: T_JJ[k2][cc] is 1 at k2 = cc, at(16J + k2, 16J + cc) below.
-        float y = sm.at[sw32<C>(16 * J + cc, 16 * I + rr)];
-        for (int k2 = cc + 1; k2 < 16; ++k2)
-          y = fmaf(sm.at[sw32<C>(16 * J + k2, 16 * I + rr)], sm.at[sw32<C>(16 * J + k2, 16 * J + cc)], y);
-        for (int L = J + 1; L < I; ++L)
+    auto Tget = [&](int r, int cc) { return r > cc ? sm.at[sw32<C>(r, cc)] : (r == cc ? 1.f : 0.f); };
+    auto Aget = [&](int t, int s) { return s < t ? sm.at[sw32<C>(s, t)] : 0.f; };  // A[t][s]
+    if (w < 2) {
+      const int I = 1 + 2 * w, J = 2 * w;
+      f32x4 z = {0.f, 0.f, 0.f, 0.f}, tij = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int k2 = 0; k2 < 16; ++k2)
-            y = fmaf(sm.at[sw32<C>(16 * L + k2, 16 * I + rr)], sm.at[sw32<C>(16 * L + k2, 16 * J + cc)], y);
-        Y[(I - d) * 256 + rr * 16 + cc] = y;
-      }
-      lds_barrier();
-      for (int I = d; I < 4; ++I) {
-        const int J = I - d;
-        // T_II[rr][k2]: at(16I + rr, 16I + k2) for k2 < rr, 1 at k2 = rr.
-        float t2 = Y[(I - d) * 256 + rr * 16 + cc];
-        for (int k2 = 0; k2 < rr; ++k2)
-          t2 = fmaf(sm.at[sw32<C>(16 * I + rr, 16 * I + k2)], Y[(I - d) * 256 + k2 * 16 + cc], t2);
-        sm.at[sw32<C>(16 * I + rr, 16 * J + cc)] = -t2;
-      }
-      lds_barrier();
+      for (int kk = 0; kk < 4; ++kk)
+        z = mfma4(Aget(16 * I + m, 16 * J + 4 * g + kk), Tget(16 * J + 4 * g + kk, 16 * J + m), z);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) tij = mfma4(Tget(16 * I + m, 16 * I + 4 * g + kk), z[kk], tij);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sm.at[sw32<C>(16 * I + 4 * g + j, 16 * J + m)] = -tij[j];
     }
+    lds_barrier();
+    {
+      const int I = 2 + (w >> 1), J = w & 1;
+      f32x4 y2 = {0.f, 0.f, 0.f, 0.f}, y3 = {0.f, 0.f, 0.f, 0.f}, tij = {0.f, 0.f, 0.f, 0.f};
+      for (int M = J; M < 2; ++M)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const float b = Tget(16 * M + 4 * g + kk, 16 * J + m);
+          y2 = mfma4(Aget(32 + m, 16 * M + 4 * g + kk), b, y2);
+          if (I == 3) y3 = mfma4(Aget(48 + m, 16 * M + 4 * g + kk), b, y3);
+        }
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) tij = mfma4(Tget(16 * I + m, 32 + 4 * g + kk), y2[kk], tij);
+      if (I == 3) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) tij = mfma4(Tget(48 + m, 48 + 4 * g + kk), y3[kk], tij);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sm.at[sw32<C>(16 * I + 4 * g + j, 16 * J + m)] = -tij[j];
+    }
+    lds_barrier();
   }
 
-  // ---- 5. W = T diag(beta)(K o e^gam), U = T diag(beta) V on MFMA -------
+  // ---- 7. W = T diag(beta)(K o e^gam), U = T diag(beta) V on MFMA -------
   // beta is folded into the fp32 columns of T before the bf16 cast, so V
   // enters the product exactly as given. T is lower triangular, so rows
   // 0..31 need only positions 0..31.
@@ -559,18 +785,10 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_intra_kernel(const PrefillP
       }
     // -W staged in sm.q (plain row-major, channels permuted).
     for (int nb = w; nb < K / 16; nb += 4) {
-      const int ch = 16 * nb + m;
+      const int wch = 16 * nb + m;
       bf16x8 Bf[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        float bv[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int t = 32 * kb + 8 * g + j;
-          bv[j] = bf16_to_f32(sm.k[sw16<K>(t, ch)]) * __expf(sm.gam[sw32<K>(t, ch)]);
-        }
-        Bf[kb] = to_bf16x8(bv);
-      }
+      for (int kb = 0; kb < 2; ++kb) Bf[kb] = frag<C>(wkt, wch, 32 * kb + 8 * g);
 #pragma unroll
       for (int pb = 0; pb < 4; ++pb) {
         f32x4 D = mfma16(Tf[pb][0], Bf[0], f32x4{0.f, 0.f, 0.f, 0.f});
@@ -604,13 +822,14 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_intra_kernel(const PrefillP
   }
   lds_barrier();
 
-  // ---- 6. -W -> workspace ----------------------------------------------
+  // ---- 8. -W -> workspace ----------------------------------------------
   {
     uint16_t* wn = reinterpret_cast<uint16_t*>(rec + R::Wn);
     for (int e = tid; e < C * KP8; e += kThreads)
       *reinterpret_cast<uint4*>(wn + rec_elem<K>(e / KP8, (e % KP8) * 8)) = *reinterpret_cast<const uint4*>(&sm.q[e * 8]);
   }
 }
+
 
 // --------------------------------------------------------------- state --
 
@@ -661,12 +880,6 @@ __device__ __forceinline__ void chunk_barrier() {
   __builtin_amdgcn_s_waitcnt(0x0070 | kOutStores);  // vmcnt = kOutStores, expcnt = 7, lgkmcnt = 0
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
-}
-
-// MFMA fragment (8 bf16) at logical (row, col) of a swizzled [rows][N] tile.
-template <int N>
-__device__ __forceinline__ bf16x8 frag(const uint16_t* tile, int r, int c) {
-  return lds_frag(tile + rec_elem<N>(r, c));
 }
 
 template <int K, int V>
