@@ -258,10 +258,17 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_intra_kernel(const PrefillP
   __shared__ SM sm;
 
   const int H = p.H;
-  const int c = static_cast<int>(blockIdx.x / H);
-  const int h = static_cast<int>(blockIdx.x % H);
   const int N = p.num_seqs;
-  if (c >= chunk_start[N]) return;  // uniform: past the last chunk
+  // Chunks are taken last to first: the state pass reads them first to
+  // last, so its early chunks are the most recently written (still in the
+  // memory-side cache when the records outgrow it).
+  const int nchunks = uniform(chunk_start[N]);
+  const int c = nchunks - 1 - static_cast<int>(blockIdx.x / H);
+  const int h = static_cast<int>(blockIdx.x % H);
+  if (c < 0) return;  // uniform: past the last chunk
+  // Records exist for at most max_chunks chunks (sized from the host's token
+  // count); inconsistent cu_seqlens must not send us past them.
+  if (nchunks > max_chunks_for(p.num_tokens, N)) return;
 
   // Which sequence owns chunk slot c: the last i with chunk_start[i] <= c.
   int lo = 0, hi = N;
@@ -313,23 +320,26 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_intra_kernel(const PrefillP
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, reinterpret_cast<uint4*>(sm.k) + slot, 16, qoff + H * K * 2, 0, 0, 0);
     }
   }
+  // Per-head gate parameters and beta, loaded while the copies are in flight.
+  constexpr int PARTS = XLayout<K>::PARTS;
+  const int ch = tid % K, part = tid / K;
+  const float a_h = __expf(p.A_log[h]);
+  const float dtb = p.dt_bias[h * K + ch];
+  const float beta_t = (tid < n) ? sigmoid_f32(bf16_to_f32(p.raw_beta[(t0 + tid) * H + h])) : 0.f;
   wait_vmem();
   __syncthreads();
 
   // ---- 2. gate and cumulative log-decay, in registers ---------------------
   // Thread (ch, part) scans PP consecutive positions of channel ch; partial
   // totals are added across parts through x.
-  constexpr int PARTS = XL::PARTS;
   constexpr int PP = C / PARTS;          // 32 at K = 128, 16 at K = 64
   constexpr int NBP = PP / 16;           // 16-row blocks per part
   constexpr int WPP = K / 64;            // waves per part
   static_assert(PP % 16 == 0, "parts hold whole blocks");
-  const int ch = tid % K, part = tid / K;
   float gm[PP];
   float before = 0.f, gl = 0.f;
   {
-    const float a = __expf(p.A_log[h]);
-    const float dtb = p.dt_bias[h * K + ch];
+    const float a = a_h;
     const bool has_lb = p.has_lb != 0;
     float acc = 0.f;
 #pragma unroll
@@ -341,7 +351,6 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_intra_kernel(const PrefillP
       gm[i] = acc;
     }
     x[XL::tot + part * K + ch] = acc;
-    const float beta_t = (tid < n) ? sigmoid_f32(bf16_to_f32(p.raw_beta[(t0 + tid) * H + h])) : 0.f;
     lds_barrier();  // raw_g consumed; partial totals visible
 #pragma unroll
     for (int q2 = 0; q2 < PARTS; ++q2) {
