@@ -131,9 +131,15 @@ def token_io_bytes(rows, H, K, V):
     return rows * H * (2 * K * 2 + V * 2 + K * 2 + 2 + V * 2)
 
 
+DECODE_SOURCES = ("kda_decode.hip", "kda_device.h", "kda_internal.h")
+
+
 def decode_kernel_hash() -> str:
-    src = os.path.join(ROOT, "gated_delta_rule_45_amd", "csrc", "kda_decode.hip")
-    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    """Hash of every source the decode kernel is compiled from."""
+    h = hashlib.sha256()
+    for name in DECODE_SOURCES:
+        h.update(open(os.path.join(ROOT, "gated_delta_rule_45_amd", "csrc", name), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic():

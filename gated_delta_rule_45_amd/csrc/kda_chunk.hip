@@ -14,19 +14,20 @@
 //
 // Three launches on one stream, no host synchronisation:
 //  1. plan:  chunk offsets per sequence from the device cu_seqlens.
-//  2. intra: one workgroup per (chunk, head), all chunks in parallel. Builds
-//            gam, A and P (off-diagonal 16x16 blocks on bf16 MFMA with a
-//            reference point between the two blocks so both factors stay <= 1;
-//            diagonal blocks pairwise in fp32 so nothing can overflow for any
-//            gate), T by blocked forward substitution in fp32, then W and U on
-//            MFMA. It stores -W, scale Q o e^gam, scale P, (K o e^{gam_last-gam})^T (bf16,
-//            laid out as MFMA A operands), e^{gam_last} and U (fp32, in
-//            accumulator fragment order) in the workspace.
+//  2. intra: one workgroup per (chunk, head), all chunks in parallel (last
+//            to first). Builds gam in registers, then A and P on bf16 MFMA
+//            from factored operand tiles (or, for a chunk with a block that
+//            decays too steeply, with pairwise fp32 exponentials on the
+//            diagonal blocks), T by forward substitution plus fp32-MFMA block
+//            products, then W and U on MFMA. It stores -W, scale Q o e^gam,
+//            scale P, (K o e^{gam_last-gam})^T (bf16, laid out as MFMA A
+//            operands), e^{gam_last} and U (fp32, in accumulator fragment
+//            order) in the workspace.
 //  3. state: one workgroup per (sequence, head, 64 value columns), looping over
 //            the sequence's chunks in order. The state lives in MFMA
 //            accumulators (fp32) for the whole sequence; each chunk's A
 //            operands are double-buffered in LDS, and the next chunk's are
-//            fetched while the current one computes.
+//            copied in while the current one computes.
 //
 // Accumulator reuse. The bf16 16x16x32 MFMA leaves lane l with rows
 // 4(l/16)+j (j < 4) of column l%16; its B operand wants rows 8(l/16)+j
