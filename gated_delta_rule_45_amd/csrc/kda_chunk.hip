@@ -152,6 +152,11 @@ __host__ __device__ inline int64_t max_chunks_for(int64_t num_tokens, int32_t nu
   return num_tokens / C + num_seqs;
 }
 
+// One byte per (chunk slot, head): 1 when the chunk needs the exact path.
+size_t flag_bytes(int64_t num_tokens, int32_t num_seqs, int32_t H) {
+  return (static_cast<size_t>(max_chunks_for(num_tokens, num_seqs)) * H + 255) / 256 * 256;
+}
+
 // ------------------------------------------------------------------ plan --
 
 // chunk_start[i] = sum_{j<i} ceil(len_j / 64); chunk_start[N] = total chunks.
@@ -249,10 +254,14 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-template <int K, int V>
-__global__ __launch_bounds__(kThreads, 2) void chunk_intra_kernel(const PrefillParams p,
-                                                                  const int32_t* chunk_start,
-                                                                  char* recs) {
+// One intra workgroup. The factored instantiation (kExact = false) handles
+// every chunk whose blocks all decay by at most kMaxBlockDecay and flags the
+// others; the exact instantiation, launched after it on the same grid,
+// handles only the flagged chunks. Separate kernels keep the factored path's
+// registers free of the exact path's.
+template <int K, int V, bool kExact>
+__device__ __forceinline__ void intra_body(const PrefillParams& p, const int32_t* chunk_start,
+                                           char* recs, uint8_t* exact_flags) {
   using R = Rec<K, V>;
   using SM = IntraSmem<K, V>;
   using XL = XLayout<K>;
@@ -270,6 +279,10 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_intra_kernel(const PrefillP
   // Records exist for at most max_chunks chunks (sized from the host's token
   // count); inconsistent cu_seqlens must not send us past them.
   if (nchunks > max_chunks_for(p.num_tokens, N)) return;
+  uint8_t* flag = exact_flags + static_cast<int64_t>(c) * H + h;
+  if constexpr (kExact) {
+    if (*flag == 0) return;  // uniform: the factored kernel took this chunk
+  }
 
   // Which sequence owns chunk slot c: the last i with chunk_start[i] <= c.
   int lo = 0, hi = N;
@@ -286,7 +299,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_intra_kernel(const PrefillP
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = uniform(tid >> 6);  // wave index, in a scalar register
   const int m = lane & 15;
   const int g = lane >> 4;
   constexpr int KP8 = K / 8;                     // 16-byte pieces per bf16 row
@@ -342,14 +355,27 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_intra_kernel(const PrefillP
   {
     const float a = a_h;
     const bool has_lb = p.has_lb != 0;
-    float acc = 0.f;
+    // All reads first (rows past the chunk end hold zeros), then a
+    // branch-free scan; padded positions do not decay, so row 63 holds
+    // gam_last.
+    float rg[PP];
 #pragma unroll
-    for (int i = 0; i < PP; ++i) {
-      const int t = part * PP + i;
-      float gv = 0.f;  // padded positions do not decay, so row 63 holds gam_last
-      if (t < n) gv = gate_log_decay(bf16_to_f32(rawg[sw16<K>(t, ch)]), dtb, a, has_lb, p.lower_bound);
-      acc += gv;
-      gm[i] = acc;
+    for (int i = 0; i < PP; ++i) rg[i] = bf16_to_f32(rawg[sw16<K>(part * PP + i, ch)]);
+    float acc = 0.f;
+    if (has_lb) {
+#pragma unroll
+      for (int i = 0; i < PP; ++i) {
+        const float gv = p.lower_bound * sigmoid_f32(a * (rg[i] + dtb));
+        acc += part * PP + i < n ? gv : 0.f;
+        gm[i] = acc;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < PP; ++i) {
+        const float gv = -a * softplus_f32(rg[i] + dtb);
+        acc += part * PP + i < n ? gv : 0.f;
+        gm[i] = acc;
+      }
     }
     x[XL::tot + part * K + ch] = acc;
     lds_barrier();  // raw_g consumed; partial totals visible
@@ -386,7 +412,9 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_intra_kernel(const PrefillP
   // until x is free.
   uint32_t wkp[PP / 2];
 
-  if (fast) {
+  if constexpr (!kExact) {
+    if (tid == 0) *flag = fast ? 0 : 1;
+    if (!fast) return;  // uniform: left to the exact kernel
     // ---- 3f. factored operands -------------------------------------------
     // With the reference rho_I = gam(16 I) of each 16-row block,
     //   e^{gam_t - gam_s} = R_t F_s c_IJ,  R_t = e^{gam_t - rho_I},
@@ -410,6 +438,15 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_intra_kernel(const PrefillP
     for (int b = 0; b < NBP; ++b) {
       const float rho = gm[16 * b];
       const float E = __expf(rho), G = __expf(gl - rho);
+      // The block's k and q first: the in-place writes below would otherwise
+      // keep the compiler from moving later reads ahead of them.
+      uint16_t kb16[16], qb16[16];
+#pragma unroll
+      for (int i2 = 0; i2 < 16; ++i2) {
+        const int o = sw16<K>(part * PP + 16 * b + i2, ch);
+        kb16[i2] = sm.k[o];
+        qb16[i2] = sm.q[o];
+      }
 #pragma unroll
       for (int u4 = 0; u4 < 4; ++u4) {
         float kgv[4];
@@ -418,7 +455,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_intra_kernel(const PrefillP
           const int i = 16 * b + 4 * u4 + i3;
           const int t = part * PP + i;
           const int o = sw16<K>(t, ch);
-          const float kv = bf16_to_f32(sm.k[o]), qv = bf16_to_f32(sm.q[o]);
+          const float kv = bf16_to_f32(kb16[4 * u4 + i3]), qv = bf16_to_f32(qb16[4 * u4 + i3]);
           const float Rt = __expf(gm[i] - rho), Ft = __expf(rho - gm[i]);
           const float kr = kv * Rt, qr = qv * Rt, kf = kv * Ft;
           sm.k[o] = bf16_bits(kr);
@@ -497,6 +534,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_intra_kernel(const PrefillP
     }
   } else {
     // ---- 3e/4e. exact path (a block decays by more than the bound) --------
+    (void)fast;
     lds_barrier();  // every thread has read the decay ranges (gam overlays x)
 #pragma unroll
     for (int i = 0; i < PP; ++i) sm.u.gam[sw32<K>(part * PP + i, ch)] = gm[i];
@@ -623,19 +661,19 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_intra_kernel(const PrefillP
           constexpr int CQ = K / 4;
           const int t = m, cq = g, row = 16 * I + t;
           float ares[16], pres[16];
-  #pragma unroll
+#pragma unroll
           for (int s3 = 0; s3 < 16; ++s3) {
             ares[s3] = 0.f;
             pres[s3] = 0.f;
           }
           for (int i8 = 0; i8 < CQ; i8 += 8) {
-  #pragma unroll
+#pragma unroll
             for (int i = 0; i < 8; ++i) {
               const int ch = cq * CQ + i8 + i;
               const float gt = sm.u.gam[sw32<K>(row, ch)];
               const float kt = bf16_to_f32(sm.k[sw16<K>(row, ch)]);
               const float qti = bf16_to_f32(sm.q[sw16<K>(row, ch)]);
-  #pragma unroll
+#pragma unroll
               for (int s3 = 0; s3 < 16; ++s3) {
                 const int srow = 16 * I + s3;
                 // gam is non-increasing, so for s <= t the exponent is <= 0;
@@ -647,7 +685,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_intra_kernel(const PrefillP
               }
             }
           }
-  #pragma unroll
+#pragma unroll
           for (int s3 = 0; s3 < 16; ++s3) {
             ares[s3] += __shfl_xor(ares[s3], 16);
             ares[s3] += __shfl_xor(ares[s3], 32);
@@ -656,7 +694,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_intra_kernel(const PrefillP
           }
           if (cq == 0) {
             const float bt = sm.at[sw32<C>(row, row)];
-  #pragma unroll
+#pragma unroll
             for (int s3 = 0; s3 < 16; ++s3) {
               const int col = 16 * I + s3;
               if (s3 < t) sm.at[sw32<C>(col, row)] = bt * ares[s3];
@@ -839,6 +877,21 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_intra_kernel(const PrefillP
       *reinterpret_cast<uint4*>(wn + rec_elem<K>(e / KP8, (e % KP8) * 8)) = *reinterpret_cast<const uint4*>(&sm.q[e * 8]);
   }
 }
+
+template <int K, int V>
+__global__ __launch_bounds__(kThreads, 2) void chunk_intra_kernel(const PrefillParams p,
+                                                                  const int32_t* chunk_start,
+                                                                  char* recs, uint8_t* exact_flags) {
+  intra_body<K, V, false>(p, chunk_start, recs, exact_flags);
+}
+
+template <int K, int V>
+__global__ __launch_bounds__(kThreads, 2) void chunk_intra_exact_kernel(const PrefillParams p,
+                                                                        const int32_t* chunk_start,
+                                                                        char* recs, uint8_t* exact_flags) {
+  intra_body<K, V, true>(p, chunk_start, recs, exact_flags);
+}
+
 
 
 // --------------------------------------------------------------- state --
@@ -1084,14 +1137,17 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_state_kernel(const PrefillP
 }
 
 template <int K, int V>
-hipError_t launch_kv(const PrefillParams& p, int32_t* chunk_start, char* recs, hipStream_t stream) {
+hipError_t launch_kv(const PrefillParams& p, int32_t* chunk_start, uint8_t* exact_flags, char* recs,
+                     hipStream_t stream) {
   const int64_t maxc = max_chunks_for(p.num_tokens, p.num_seqs);
   const int64_t intra_blocks = maxc * p.H;
   const int64_t pairs = static_cast<int64_t>(p.num_seqs) * p.H;
   const int64_t state_blocks = (V / 64 == 2) ? (pairs + 7) / 8 * 16 : pairs;
   if (intra_blocks > 0x7fffffff || state_blocks > 0x7fffffff) return hipErrorInvalidValue;
   chunk_intra_kernel<K, V><<<dim3(static_cast<unsigned>(intra_blocks)), dim3(kThreads), 0, stream>>>(
-      p, chunk_start, recs);
+      p, chunk_start, recs, exact_flags);
+  chunk_intra_exact_kernel<K, V><<<dim3(static_cast<unsigned>(intra_blocks)), dim3(kThreads), 0, stream>>>(
+      p, chunk_start, recs, exact_flags);
   chunk_state_kernel<K, V><<<dim3(static_cast<unsigned>(state_blocks)), dim3(kThreads), 0, stream>>>(
       p, chunk_start, recs);
   return hipGetLastError();
@@ -1106,17 +1162,19 @@ size_t prefill_workspace_bytes(int32_t num_seqs, int64_t num_tokens, int32_t H, 
   if (K == 64 && V == 128) rec = Rec<64, 128>::bytes;
   if (K == 128 && V == 64) rec = Rec<128, 64>::bytes;
   if (K == 128 && V == 128) rec = Rec<128, 128>::bytes;
-  return header_bytes(num_seqs) + static_cast<size_t>(max_chunks_for(num_tokens, num_seqs)) * H * rec;
+  return header_bytes(num_seqs) + flag_bytes(num_tokens, num_seqs, H) +
+         static_cast<size_t>(max_chunks_for(num_tokens, num_seqs)) * H * rec;
 }
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   int32_t* chunk_start = static_cast<int32_t*>(p.workspace);
-  char* recs = static_cast<char*>(p.workspace) + header_bytes(p.num_seqs);
+  uint8_t* flags = static_cast<uint8_t*>(p.workspace) + header_bytes(p.num_seqs);
+  char* recs = reinterpret_cast<char*>(flags) + flag_bytes(p.num_tokens, p.num_seqs, p.H);
   plan_kernel<<<1, kThreads, 0, stream>>>(p.cu_seqlens, p.num_seqs, chunk_start);
-  if (p.K == 64 && p.V == 64) return launch_kv<64, 64>(p, chunk_start, recs, stream);
-  if (p.K == 64 && p.V == 128) return launch_kv<64, 128>(p, chunk_start, recs, stream);
-  if (p.K == 128 && p.V == 64) return launch_kv<128, 64>(p, chunk_start, recs, stream);
-  return launch_kv<128, 128>(p, chunk_start, recs, stream);
+  if (p.K == 64 && p.V == 64) return launch_kv<64, 64>(p, chunk_start, flags, recs, stream);
+  if (p.K == 64 && p.V == 128) return launch_kv<64, 128>(p, chunk_start, flags, recs, stream);
+  if (p.K == 128 && p.V == 64) return launch_kv<128, 64>(p, chunk_start, flags, recs, stream);
+  return launch_kv<128, 128>(p, chunk_start, flags, recs, stream);
 }
 
 }  // namespace kda

@@ -95,6 +95,12 @@ __device__ __forceinline__ float sigmoid_f32(float z) {
   return __builtin_amdgcn_rcpf(1.0f + __expf(-z));
 }
 
+// softplus(x) = max(x, 0) + ln(1 + e^-|x|). The log argument lies in
+// (1, 2], where the hardware log2 (about 1 ulp) needs no range reduction.
+__device__ __forceinline__ float softplus_f32(float x) {
+  return fmaxf(x, 0.0f) + 0.693147180559945f * __builtin_amdgcn_logf(1.0f + __expf(-fabsf(x)));
+}
+
 // Per-channel log-decay from the raw gate input (same reading as the header):
 //   x = raw_g + dt_bias, a = exp(A_log[h]);
 //   g = -a * softplus(x)  or  g = lower_bound * sigmoid(a * x).
@@ -104,7 +110,7 @@ __device__ __forceinline__ float gate_log_decay(float raw_g, float dt_bias, floa
                                                 bool has_lb, float lb) {
   const float x = raw_g + dt_bias;
   if (has_lb) return lb * sigmoid_f32(a * x);
-  return -a * (fmaxf(x, 0.0f) + __logf(1.0f + __expf(-fabsf(x))));
+  return -a * softplus_f32(x);
 }
 
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS
