@@ -431,8 +431,10 @@ __device__ __forceinline__ void intra_body(const PrefillParams& p, const int32_t
       const int J = pr - I * (I + 1) / 2;
       x[XL::cij + e] = __expf(x[XL::bnd + I * K + cc] - x[XL::bnd + J * K + cc]);
     }
-    uint16_t* qg = reinterpret_cast<uint16_t*>(rec + R::Qg);
-    uint16_t* kgt = reinterpret_cast<uint16_t*>(rec + R::KgT);
+    // Record tiles written through buffer resources: 32-bit offsets, no
+    // per-store 64-bit address arithmetic.
+    const __amdgpu_buffer_rsrc_t rqg = make_rsrc(rec + R::Qg, static_cast<uint32_t>(C * K * 2));
+    const __amdgpu_buffer_rsrc_t rkg = make_rsrc(rec + R::KgT, static_cast<uint32_t>(K * C * 2));
     const int qcol = 32 * (ch >> 5) + perm_slot(ch & 31);
 #pragma unroll
     for (int b = 0; b < NBP; ++b) {
@@ -461,7 +463,7 @@ __device__ __forceinline__ void intra_body(const PrefillParams& p, const int32_t
           sm.k[o] = bf16_bits(kr);
           sm.q[o] = bf16_bits(qr);
           sm.u.f.kf[o] = bf16_bits(kf);
-          qg[rec_elem<K>(t, qcol)] = bf16_bits(p.scale * qr * E);
+          __builtin_amdgcn_raw_buffer_store_b16(bf16_bits(p.scale * qr * E), rqg, rec_elem<K>(t, qcol) * 2, 0, 0);
           kgv[i3] = kf * G;
           const uint32_t wk = bf16_bits(kr * E);
           if (i & 1) wkp[i >> 1] |= wk << 16;
@@ -472,10 +474,9 @@ __device__ __forceinline__ void intra_body(const PrefillParams& p, const int32_t
         const int tp = part * PP + 16 * b + 4 * u4;
         const int pin = tp & 31;
         const int slot0 = pin < 16 ? 2 * pin : 2 * (pin - 16) + 4;
-        uint2 v;
-        v.x = pack_bf16x2(kgv[0], kgv[1]);
-        v.y = pack_bf16x2(kgv[2], kgv[3]);
-        *reinterpret_cast<uint2*>(kgt + rec_elem<C>(ch, 32 * (tp >> 5) + slot0)) = v;
+        typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 v = {pack_bf16x2(kgv[0], kgv[1]), pack_bf16x2(kgv[2], kgv[3])};
+        __builtin_amdgcn_raw_buffer_store_b64(v, rkg, rec_elem<C>(ch, 32 * (tp >> 5) + slot0) * 2, 0, 0);
       }
     }
     lds_barrier();
@@ -485,7 +486,7 @@ __device__ __forceinline__ void intra_body(const PrefillParams& p, const int32_t
     // straight to the workspace (bf16, positions permuted), including the
     // zero blocks above the diagonal that the state kernel reads.
     {
-      uint16_t* pm = reinterpret_cast<uint16_t*>(rec + R::Pm);
+      const __amdgpu_buffer_rsrc_t rpm = make_rsrc(rec + R::Pm, static_cast<uint32_t>(C * C * 2));
       const int blocks[4][3][2] = {{{3, 3}, {3, 0}, {0, 0}},
                                    {{2, 2}, {3, 1}, {1, 0}},
                                    {{1, 1}, {3, 2}, {-1, -1}},
@@ -494,6 +495,9 @@ __device__ __forceinline__ void intra_body(const PrefillParams& p, const int32_t
         const int I = blocks[w][bi][0], J = blocks[w][bi][1];
         if (I < 0) break;
         const float* cv = x + XL::cij + (I * (I + 1) / 2 + J) * K;
+        float bt[4];  // beta of the lane's rows (on the diagonal of at)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bt[j] = sm.at[sw32<C>(16 * I + 4 * g + j, 16 * I + 4 * g + j)];
         f32x4 dA = {0.f, 0.f, 0.f, 0.f}, dP = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < K / 32; ++kb) {
@@ -512,13 +516,17 @@ __device__ __forceinline__ void intra_body(const PrefillParams& p, const int32_t
           dA = mfma16(ak, b, dA);
           dP = mfma16(aq, b, dP);
         }
-        // Lane holds rows 16 I + 4 g + j of column s = 16 J + m.
+        // Lane holds rows 16 I + 4 g + j of column s = 16 J + m. Every entry
+        // is written without a branch: beta stays on the diagonal, and the
+        // entries below it (junk from the masked s > t products) are
+        // overwritten by T before anything reads them.
         const int s2 = 16 * J + m;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int row = 16 * I + 4 * g + j;
-          if (s2 < row) sm.at[sw32<C>(s2, row)] = sm.at[sw32<C>(row, row)] * dA[j];
-          pm[rec_elem<C>(row, 32 * (s2 >> 5) + perm_slot(s2 & 31))] = bf16_bits(s2 <= row ? p.scale * dP[j] : 0.f);
+          sm.at[sw32<C>(s2, row)] = s2 == row ? bt[j] : bt[j] * dA[j];
+          __builtin_amdgcn_raw_buffer_store_b16(bf16_bits(s2 <= row ? p.scale * dP[j] : 0.f), rpm,
+                                                rec_elem<C>(row, 32 * (s2 >> 5) + perm_slot(s2 & 31)) * 2, 0, 0);
         }
       }
       if (w == 3) {
@@ -527,8 +535,8 @@ __device__ __forceinline__ void intra_body(const PrefillParams& p, const int32_t
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int row = 4 * g + j;
-          pm[rec_elem<C>(row, perm_slot(16 + m))] = 0;
-          pm[rec_elem<C>(32 + row, 32 + perm_slot(16 + m))] = 0;
+          __builtin_amdgcn_raw_buffer_store_b16(0, rpm, rec_elem<C>(row, perm_slot(16 + m)) * 2, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b16(0, rpm, rec_elem<C>(32 + row, 32 + perm_slot(16 + m)) * 2, 0, 0);
         }
       }
     }
@@ -726,20 +734,25 @@ __device__ __forceinline__ void intra_body(const PrefillParams& p, const int32_t
   }
   // v for the U phase, fetched now so its latency hides behind the inverse:
   // lane (m, g) needs v[t][16 nb + m] for t = 32 kb + 8 g + j, nb = w, w + 4.
+  // 16-bit buffer loads over the chunk's rows: rows past its end read zero,
+  // the lane part of the offset is fixed and the row part is scalar.
   constexpr int NBU = (V / 16 + 3) / 4;
+  static_assert(V / 16 <= 4 * NBU && V / 16 > 4 * (NBU - 1), "every wave has NBU column blocks");
   uint16_t vpre[NBU][2][8];
+  {
+    const int rs = static_cast<int>(p.qkv_row_stride * 2);  // bytes per mixed_qkv row
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.qkv + t0 * p.qkv_row_stride, static_cast<uint32_t>(n * rs));
+    const int vlane = (2 * H * K + h * V + m) * 2 + 8 * g * rs;
 #pragma unroll
-  for (int u = 0; u < NBU; ++u)
+    for (int u = 0; u < NBU; ++u)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int t = 32 * kb + 8 * g + j;
-        const int nb = w + 4 * u;
-        vpre[u][kb][j] = (t < n && nb < V / 16)
-                             ? p.qkv[(t0 + t) * p.qkv_row_stride + 2 * H * K + h * V + 16 * nb + m]
-                             : static_cast<uint16_t>(0);
-      }
+        for (int j = 0; j < 8; ++j) {
+          const int nb = w + 4 * u;
+          vpre[u][kb][j] = __builtin_amdgcn_raw_buffer_load_b16(rv, vlane + 32 * nb, (32 * kb + j) * rs, 0);
+        }
+  }
 
 
   lds_barrier();  // A^T complete; x (or gam) no longer read
@@ -777,33 +790,55 @@ __device__ __forceinline__ void intra_body(const PrefillParams& p, const int32_t
   {
     auto Tget = [&](int r, int cc) { return r > cc ? sm.at[sw32<C>(r, cc)] : (r == cc ? 1.f : 0.f); };
     auto Aget = [&](int t, int s) { return s < t ? sm.at[sw32<C>(s, t)] : 0.f; };  // A[t][s]
+    // Operands are read into registers before their products (no LDS
+    // writes intervene), so the reads overlap.
     if (w < 2) {
       const int I = 1 + 2 * w, J = 2 * w;
+      float a[4], b[4], t[4];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        a[kk] = Aget(16 * I + m, 16 * J + 4 * g + kk);
+        b[kk] = Tget(16 * J + 4 * g + kk, 16 * J + m);
+        t[kk] = Tget(16 * I + m, 16 * I + 4 * g + kk);
+      }
       f32x4 z = {0.f, 0.f, 0.f, 0.f}, tij = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        z = mfma4(Aget(16 * I + m, 16 * J + 4 * g + kk), Tget(16 * J + 4 * g + kk, 16 * J + m), z);
+      for (int kk = 0; kk < 4; ++kk) z = mfma4(a[kk], b[kk], z);
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) tij = mfma4(Tget(16 * I + m, 16 * I + 4 * g + kk), z[kk], tij);
+      for (int kk = 0; kk < 4; ++kk) tij = mfma4(t[kk], z[kk], tij);
 #pragma unroll
       for (int j = 0; j < 4; ++j) sm.at[sw32<C>(16 * I + 4 * g + j, 16 * J + m)] = -tij[j];
     }
     lds_barrier();
     {
       const int I = 2 + (w >> 1), J = w & 1;
-      f32x4 y2 = {0.f, 0.f, 0.f, 0.f}, y3 = {0.f, 0.f, 0.f, 0.f}, tij = {0.f, 0.f, 0.f, 0.f};
-      for (int M = J; M < 2; ++M)
+      float a2[2][4], a3[2][4], b[2][4], t2[4], t3[4];
+#pragma unroll
+      for (int M = 0; M < 2; ++M)
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-          const float b = Tget(16 * M + 4 * g + kk, 16 * J + m);
-          y2 = mfma4(Aget(32 + m, 16 * M + 4 * g + kk), b, y2);
-          if (I == 3) y3 = mfma4(Aget(48 + m, 16 * M + 4 * g + kk), b, y3);
+          b[M][kk] = Tget(16 * M + 4 * g + kk, 16 * J + m);  // zero for M < J
+          a2[M][kk] = Aget(32 + m, 16 * M + 4 * g + kk);
+          a3[M][kk] = Aget(48 + m, 16 * M + 4 * g + kk);
         }
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) tij = mfma4(Tget(16 * I + m, 32 + 4 * g + kk), y2[kk], tij);
+      for (int kk = 0; kk < 4; ++kk) {
+        t2[kk] = Tget(16 * I + m, 32 + 4 * g + kk);
+        t3[kk] = Tget(48 + m, 48 + 4 * g + kk);
+      }
+      f32x4 y2 = {0.f, 0.f, 0.f, 0.f}, y3 = {0.f, 0.f, 0.f, 0.f}, tij = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int M = 0; M < 2; ++M)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          y2 = mfma4(a2[M][kk], b[M][kk], y2);
+          y3 = mfma4(a3[M][kk], b[M][kk], y3);
+        }
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) tij = mfma4(t2[kk], y2[kk], tij);
       if (I == 3) {
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) tij = mfma4(Tget(48 + m, 48 + 4 * g + kk), y3[kk], tij);
+        for (int kk = 0; kk < 4; ++kk) tij = mfma4(t3[kk], y3[kk], tij);
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) sm.at[sw32<C>(16 * I + 4 * g + j, 16 * J + m)] = -tij[j];
