@@ -333,6 +333,69 @@ int32_t kda_oracle_decode_packed(int32_t num_seqs, int32_t tokens_per_seq,
   return 0;
 }
 
+/* Speculative decoding with a state per token ([P2] Purpose: with speculative
+ * decoding the KDA state slot is column 0 of a block table that has
+ * 1 + num_speculative_blocks columns; [P3] Refusal and steps: a padded
+ * request carries a null slot and one accepted token). Reading taken here:
+ * request n owns tokens_per_seq consecutive rows and block-table row
+ * table[n * index_stride + c * col_stride]. Its initial state is the slot in
+ * column num_accepted[n] - 1 (clamped to 0 .. tokens_per_seq - 1); after its
+ * token t the state is stored into the slot in column t, unless that entry
+ * is < 0. A request whose initial entry is < 0 reads and writes no slot and
+ * outputs zeros. states (optional): fp64 [num_seqs][tokens_per_seq][H][K][V],
+ * the state after every token (zeros for such a request). */
+int32_t kda_oracle_spec_decode(int32_t num_seqs, int32_t tokens_per_seq,
+                               int32_t H, int32_t K, int32_t V,
+                               const kda_oracle_args_t* a, int64_t col_stride,
+                               const int32_t* num_accepted, double* out,
+                               double* states) {
+  if (num_seqs < 0 || tokens_per_seq < 1 || H < 1 || K < 1 || V < 1 || col_stride < 1) return 1;
+  const int32_t T = tokens_per_seq;
+  const int64_t KV = (int64_t)K * V;
+  if (states)
+    for (int64_t x = 0; x < (int64_t)num_seqs * T * H * KV; ++x) states[x] = 0.0;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t nh = 0; nh < (int64_t)num_seqs * H; ++nh) {
+    const int32_t n = (int32_t)(nh / H), h = (int32_t)(nh % H);
+    const int32_t* row = a->state_indices + (int64_t)n * a->index_stride;
+    int32_t acc = num_accepted[n];
+    if (acc < 1) acc = 1;
+    if (acc > T) acc = T;
+    const int64_t s0 = (int64_t)row[(int64_t)(acc - 1) * col_stride];
+    const int32_t row0 = n * T;
+    if (s0 < 0) {
+      for (int32_t t = 0; t < T; ++t)
+        for (int32_t j = 0; j < V; ++j) out[(int64_t)(row0 + t) * H * V + (int64_t)h * V + j] = 0.0;
+      continue;
+    }
+    double* q = (double*)malloc(sizeof(double) * (size_t)T * K);
+    double* k = (double*)malloc(sizeof(double) * (size_t)T * K);
+    double* g = (double*)malloc(sizeof(double) * (size_t)T * K);
+    double* v = (double*)malloc(sizeof(double) * (size_t)T * V);
+    double* o = (double*)malloc(sizeof(double) * (size_t)V);
+    double* beta = (double*)malloc(sizeof(double) * (size_t)T);
+    double* S = (double*)malloc(sizeof(double) * (size_t)KV);
+    const float* init = a->pool + s0 * a->slot_stride + (int64_t)h * KV;
+    for (int64_t x = 0; x < KV; ++x) S[x] = (double)init[x];
+    gather_head(row0, T, h, H, K, V, a->mixed_qkv, a->qkv_row_stride, a->raw_g, a->raw_beta,
+                a->A_log, a->dt_bias, a->has_lower_bound, a->lower_bound, q, k, v, g, beta);
+    for (int32_t t = 0; t < T; ++t) {
+      /* one token of the recurrence, then its state goes to column t */
+      kda_oracle_recurrent_pregated(1, K, V, q + (size_t)t * K, k + (size_t)t * K,
+                                    v + (size_t)t * V, g + (size_t)t * K, beta + t, a->scale, S, o);
+      for (int32_t j = 0; j < V; ++j) out[(int64_t)(row0 + t) * H * V + (int64_t)h * V + j] = o[j];
+      if (states) memcpy(states + (((int64_t)n * T + t) * H + h) * KV, S, sizeof(double) * (size_t)KV);
+      const int64_t st = (int64_t)row[(int64_t)t * col_stride];
+      if (st >= 0) {
+        float* tile = a->pool + st * a->slot_stride + (int64_t)h * KV;
+        for (int64_t x = 0; x < KV; ++x) tile[x] = (float)S[x];
+      }
+    }
+    free(q); free(k); free(g); free(v); free(o); free(beta); free(S);
+  }
+  return 0;
+}
+
 /* Varlen prefill: sequence i covers rows cu_seqlens[i] .. cu_seqlens[i+1]-1
  * and uses slot state_indices[i * index_stride]. The initial state is read from
  * the slot unless has_initial_state[i] == 0 (then it is zero). A zero-length

@@ -54,6 +54,14 @@ int32_t kda_oracle_decode_packed(int32_t num_seqs, int32_t tokens_per_seq,
                                  int32_t H, int32_t K, int32_t V,
                                  const kda_oracle_args_t* a, int32_t form,
                                  double* out, double* final_state);
+/* Spec decode with a state per token: initial state from block-table column
+ * num_accepted[n] - 1, the state after token t stored into column t.
+ * states (optional): fp64 [seqs][tokens_per_seq][H][K][V]. */
+int32_t kda_oracle_spec_decode(int32_t num_seqs, int32_t tokens_per_seq,
+                               int32_t H, int32_t K, int32_t V,
+                               const kda_oracle_args_t* a, int64_t col_stride,
+                               const int32_t* num_accepted, double* out,
+                               double* states);
 int32_t kda_oracle_prefill(int32_t num_seqs, const int32_t* cu_seqlens,
                            const uint8_t* has_initial_state, int32_t H,
                            int32_t K, int32_t V, const kda_oracle_args_t* a,

@@ -82,6 +82,9 @@ def lib():
         L.kda_oracle_decode_packed.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(_Args), i32, vp, vp]
         L.kda_oracle_decode_packed.restype = i32
         L.kda_oracle_prefill.argtypes = [i32, vp, vp, i32, i32, i32, ctypes.POINTER(_Args), i32, vp, vp]
+        L.kda_oracle_spec_decode.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(_Args), ctypes.c_int64,
+                                             vp, vp, vp]
+        L.kda_oracle_spec_decode.restype = i32
         L.kda_oracle_prefill.restype = i32
         _lib = L
     return _lib
@@ -233,6 +236,37 @@ def decode_packed(inp: dict, pool: torch.Tensor, state_indices: torch.Tensor,
     if rc != 0:
         raise ValueError("oracle rejected the decode arguments")
     return out, fs, (P if return_pool else None)
+
+
+def spec_decode(inp: dict, pool: torch.Tensor, block_table: torch.Tensor, num_accepted,
+                H: int, K: int, V: int, tokens_per_seq: int, lower_bound=None,
+                scale: float = 1.0, return_pool: bool = True):
+    """Speculative decoding with a state per token: request n reads its
+    initial state from block-table column num_accepted[n] - 1 and stores the
+    state after its token t into column t (entries < 0 are skipped; a request
+    whose initial entry is < 0 touches nothing and outputs zeros).
+    ``block_table``: int32 [num_seqs, >= tokens_per_seq] (any strides; the
+    oracle gets the same entries, packed). Returns (out [rows,H,V],
+    states [seqs,tokens,H,K,V], pool_after)."""
+    num_seqs = block_table.shape[0]
+    T = int(tokens_per_seq)
+    tab = np.ascontiguousarray(block_table[:, :T].cpu().numpy().astype(np.int32))
+    acc = np.ascontiguousarray(np.asarray(num_accepted, dtype=np.int32))
+    if return_pool:
+        P = _pool2d(pool)
+        flat = tab.reshape(-1)
+    else:
+        P, flat = _compact(pool, tab.reshape(-1))
+    flat = np.ascontiguousarray(flat.astype(np.int32))
+    keep: list = []
+    a = _args(inp, P, flat, T, lower_bound, scale, keep)
+    out = np.zeros((num_seqs * T, H, V), dtype=np.float64)
+    states = np.zeros((num_seqs, T, H, K, V), dtype=np.float64)
+    rc = lib().kda_oracle_spec_decode(num_seqs, T, H, K, V, ctypes.byref(a), 1, _ptr(acc),
+                                      _ptr(out), _ptr(states))
+    if rc != 0:
+        raise ValueError("oracle rejected the spec-decode arguments")
+    return out, states, (P if return_pool else None)
 
 
 def prefill(inp: dict, pool: torch.Tensor, state_indices: torch.Tensor,

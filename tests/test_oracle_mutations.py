@@ -42,6 +42,12 @@ MUTANTS = {
                            "x += Tm[(size_t)t * C + s] * bc[t] * kc[(size_t)s * K + i] *"),
     "chunk_cumsum_exclusive": ("acc += gc[(size_t)t * K + i];\n        gam[(size_t)t * K + i] = acc;",
                                "gam[(size_t)t * K + i] = acc;\n        acc += gc[(size_t)t * K + i];"),
+    "spec_initial_column_fixed": ("const int64_t s0 = (int64_t)row[(int64_t)(acc - 1) * col_stride];",
+                                  "const int64_t s0 = (int64_t)row[0];"),
+    "spec_write_column_reversed": ("const int64_t st = (int64_t)row[(int64_t)t * col_stride];",
+                                   "const int64_t st = (int64_t)row[(int64_t)(T - 1 - t) * col_stride];"),
+    "spec_only_final_state_written": ("      if (st >= 0) {\n        float* tile",
+                                      "      if (st >= 0 && t == T - 1) {\n        float* tile"),
 }
 
 

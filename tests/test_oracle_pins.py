@@ -143,6 +143,79 @@ def test_decode_matches_brute_force(K, V, H, lower_bound):
     assert np.all(out[6:9] == 0.0)  # null slot rows
 
 
+def _spec_brute(case: W.Case, lower_bound, scale):
+    """Per-token states of the spec-decode reading through the dense brute
+    force: request n starts from the slot in column num_accepted[n]-1 and its
+    state after token t is the brute-force state after t+1 tokens."""
+    T = case.tokens_per_seq
+    tab = case.block_table.tolist()
+    acc = case.num_accepted.tolist()
+    N = len(tab)
+    out = np.zeros((case.rows, case.H, case.V))
+    states = np.zeros((N, T, case.H, case.K, case.V))
+    for n in range(N):
+        s0 = tab[n][acc[n] - 1]
+        for t in range(T):
+            o, st = brute_force(case, [(n * T, t + 1, s0, True)], lower_bound, scale)
+            out[n * T + t] = o[n * T + t]
+            states[n, t] = st[0] if s0 >= 0 else 0.0
+    return out, states
+
+
+@pytest.mark.parametrize("lower_bound", [None, -5.0])
+@pytest.mark.parametrize("T", [1, 3, 4])
+def test_spec_decode_states_match_brute_force(T, lower_bound):
+    """Initial state from column num_accepted-1, the state after token t in
+    column t, a padded request (null slots) touching nothing."""
+    H, K, V, N = 2, 4, 5, 4
+    case = W.spec_decode_case("sd", H, K, V, N, T, num_slots=N * 4 + 3, lower_bound=lower_bound,
+                              seed=71 + T, width=4, std=0.3, null_rows=(2,))
+    out, states, pool_after = O.spec_decode(case.inputs, case.pool, case.block_table, case.num_accepted,
+                                            H, K, V, T, lower_bound=lower_bound, scale=0.6)
+    ref_out, ref_states = _spec_brute(case, lower_bound, 0.6)
+    assert _rel(out, ref_out) < 1e-12
+    assert _rel(states, ref_states) < 1e-12
+    tab = case.block_table.tolist()
+    written = set()
+    for n in range(N):
+        for t in range(T):
+            sl = tab[n][t]
+            if sl >= 0 and n != 2:
+                written.add(sl)
+                np.testing.assert_array_equal(pool_after[sl].reshape(H, K, V),
+                                              ref_states[n, t].astype(np.float32))
+    before = case.pool.reshape(case.pool.shape[0], -1).numpy()
+    for sl in range(case.pool.shape[0]):
+        if sl not in written:
+            np.testing.assert_array_equal(pool_after[sl], before[sl])
+    assert np.all(out[2 * T:3 * T] == 0.0)
+
+
+def test_spec_decode_skips_null_columns_and_selects_by_accepted_count():
+    H, K, V, N, T = 1, 4, 4, 3, 4
+    case = W.spec_decode_case("sdn", H, K, V, N, T, num_slots=N * 4, lower_bound=-5.0, seed=91,
+                              width=4, std=0.3, null_cols=((0, 1), (1, 3)), accepted=[3, 2, 1])
+    out, states, pool_after = O.spec_decode(case.inputs, case.pool, case.block_table, case.num_accepted,
+                                            H, K, V, T, lower_bound=-5.0)
+    tab = case.block_table.tolist()
+    before = case.pool.reshape(N * 4, -1).numpy()
+    # The null entries are skipped; every other column holds its token's state.
+    for n in range(N):
+        for t in range(T):
+            sl = tab[n][t]
+            if sl >= 0:
+                np.testing.assert_array_equal(pool_after[sl], states[n, t].reshape(-1).astype(np.float32))
+    # Request 0 started from column 2: its first output equals a one-token
+    # decode from that slot's original state.
+    single = W.decode_case("one", H, K, V, 1, 1, N * 4, 1, -5.0, seed=91)
+    single.inputs = {k: (v[0:1] if v.dim() and v.shape[0] == N * T else v) for k, v in case.inputs.items()}
+    single.pool = case.pool
+    single.block_table = torch.tensor([[tab[0][2]]], dtype=torch.int32)
+    o1, _ = brute_force(single, [(0, 1, tab[0][2], True)], -5.0, 1.0)
+    np.testing.assert_allclose(out[0], o1[0], rtol=0, atol=1e-12)
+    assert np.isfinite(before).all()
+
+
 @pytest.mark.parametrize("lower_bound", [None, -5.0])
 def test_prefill_matches_brute_force(lower_bound):
     lens = [1, 9, 0, 23, 40]

@@ -123,6 +123,7 @@ class Case:
     has_initial_state: torch.Tensor | None = None
     lower_bound: float | None = -5.0
     scale: float = 1.0
+    num_accepted: torch.Tensor | None = None  # spec decode with a state per token
 
     @property
     def state_indices(self) -> torch.Tensor:
@@ -143,6 +144,32 @@ def decode_case(name, H, K, V, num_seqs, tokens_per_seq, num_slots, index_stride
                                seed + 1 if pool_seed is None else pool_seed, slot_pad),
                 block_table=make_block_table(num_seqs, index_stride, num_slots, seed + 2, null_rows),
                 tokens_per_seq=tokens_per_seq, lower_bound=lower_bound, scale=scale)
+
+
+def spec_decode_case(name, H, K, V, num_seqs, tokens_per_seq, num_slots, lower_bound, seed,
+                     width=8, std=0.05, null_rows=(), null_cols=(), accepted=None,
+                     pool_seed=None) -> Case:
+    """Spec decode with a state per token: a [num_seqs, width] block table of
+    distinct slots (width >= tokens_per_seq; needs num_slots >= num_seqs *
+    width), requests in ``null_rows`` padded (null slot in every column they
+    use, one accepted token), (row, col) pairs in ``null_cols`` set to -1,
+    and num_accepted drawn uniformly from 1..tokens_per_seq unless given."""
+    assert width >= tokens_per_seq and num_slots >= num_seqs * width
+    rows = num_seqs * tokens_per_seq
+    table = make_block_table(num_seqs, width, num_slots, seed + 2)
+    g = _gen(seed + 3)
+    acc = (torch.randint(1, tokens_per_seq + 1, (num_seqs,), generator=g).to(torch.int32)
+           if accepted is None else torch.tensor(accepted, dtype=torch.int32))
+    for r in null_rows:
+        table[r, :] = -1
+        acc[r] = 1
+    for r, c in null_cols:
+        table[r, c] = -1
+    return Case(name=name, kind="spec", H=H, K=K, V=V,
+                inputs=make_token_inputs(rows, H, K, V, seed),
+                pool=make_pool(num_slots, H, K, V, std, seed + 1 if pool_seed is None else pool_seed),
+                block_table=table, tokens_per_seq=tokens_per_seq, lower_bound=lower_bound,
+                num_accepted=acc)
 
 
 def prefill_case(name, H, K, V, lens, num_slots, lower_bound, seed, std=0.05,
