@@ -14,7 +14,8 @@ and never synchronise) and the graph is replayed; HIP events on the replay
 stream bracket the timed region. Eager (Python-launched) times are reported
 next to them. The same JSON line carries the other legs of the hot path:
 spec-verify (8 rows), chunked prefill (one 8192-token sequence; 64 varlen
-sequences) and the mixed 4096-token batch.
+sequences), the mixed 4096-token batch and spec decode with a state per
+token.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs ...]
 """
@@ -224,6 +225,46 @@ def leg_spec(steps, warmup):
     return res
 
 
+def leg_spec_states(steps, warmup):
+    """Spec decode with a state per token (kda_spec_decode): each request
+    reads one state and writes one per token; a random accepted count picks
+    the column the state is read from."""
+    import torch
+
+    import gated_delta_rule_45_amd as kda
+    import workloads as W
+
+    dev = torch.device("cuda")
+    H, K, V = 32, 128, 128
+    res = {}
+    pool = _device_pool(512, H, K, V, 0.05, 2999, dev)
+    for name, (real, tps, nulls) in W.SPEC_LAYOUTS.items():
+        n = real + nulls
+        inp = _device_token_inputs(n * tps, H, K, V, 2200, dev)
+        perm = torch.randperm(512, generator=W._gen(2201)).to(torch.int32)
+        sets = 512 // (n * 8)  # disjoint tables of 8 columns per request
+        tables, accs = [], []
+        for s_ in range(sets):
+            t = perm[s_ * n * 8:(s_ + 1) * n * 8].view(n, 8).clone()
+            t[real:, :] = -1
+            tables.append(t.to(dev))
+            a = torch.randint(1, tps + 1, (n,), generator=W._gen(2202 + s_)).to(torch.int32)
+            a[real:] = 1
+            accs.append(a.to(dev))
+        out = torch.empty(n * tps, H, V, dtype=torch.bfloat16, device=dev)
+
+        def step(i):
+            kda.kda_spec_decode(inp["mixed_qkv"], inp["raw_g"], inp["raw_beta"], inp["A_log"],
+                                inp["dt_bias"], -5.0, pool, tables[i % sets], accs[i % sets],
+                                tokens_per_seq=tps, out=out)
+
+        ms, _ = graph_time(step, sets, steps, warmup)
+        state_bytes = (1 + tps) * real * H * K * V * 4
+        res[name] = {"us_per_step": round(ms * 1e3, 3),
+                     "state_gbs": round(state_bytes / (ms * 1e-3) / 1e9, 1)}
+    return res
+
+
 def prefill_flops(lens, H, K, V, C=64):
     """Useful flops of the chunked algorithm, causal triangles counted once.
     Per chunk of n tokens and head:
@@ -366,6 +407,7 @@ def main():
     extra = {}
     if "spec" in legs:
         extra["spec_verify"] = leg_spec(max(args.steps // 4, 64), 16)
+        extra["spec_decode_per_token_states"] = leg_spec_states(max(args.steps // 4, 64), 16)
     if "prefill" in legs:
         import workloads as W
 

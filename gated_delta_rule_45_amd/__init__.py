@@ -11,6 +11,7 @@ from ._binding import (  # noqa: F401
     kda_decode_packed,
     kda_mixed_batch,
     kda_mixed_batch_workspace_size,
+    kda_spec_decode,
     lib,
 )
 
@@ -21,5 +22,6 @@ __all__ = [
     "kda_decode_packed",
     "kda_mixed_batch",
     "kda_mixed_batch_workspace_size",
+    "kda_spec_decode",
     "lib",
 ]

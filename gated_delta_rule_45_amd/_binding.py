@@ -58,6 +58,8 @@ def lib() -> ctypes.CDLL:
         gp, spn = ctypes.POINTER(KdaGate), ctypes.POINTER(KdaState)
         L.kda_decode_packed.argtypes = [i32, i32, i32, i32, i32, vp, i64, vp, vp, gp, spn, vp, vp]
         L.kda_decode_packed.restype = i32
+        L.kda_spec_decode.argtypes = [i32, i32, i32, i32, i32, vp, i64, vp, vp, gp, spn, i64, vp, vp, vp]
+        L.kda_spec_decode.restype = i32
         L.kda_chunk_prefill_workspace_size.argtypes = [i32, i64, i32, i32, i32]
         L.kda_chunk_prefill_workspace_size.restype = sz
         L.kda_chunk_prefill.argtypes = [i32, i64, vp, vp, i32, i32, i32, vp, i64, vp, vp, gp, spn,
@@ -198,6 +200,42 @@ def kda_decode_packed(mixed_qkv, raw_g, raw_beta, A_log, dt_bias, lower_bound, i
                                  mixed_qkv.stride(0), _ptr(raw_g), _ptr(raw_beta),
                                  ctypes.byref(g), ctypes.byref(s), _ptr(out),
                                  _stream(mixed_qkv.device))
+    _raise_if(st)
+    return out, initial_state
+
+
+def kda_spec_decode(mixed_qkv, raw_g, raw_beta, A_log, dt_bias, lower_bound, initial_state,
+                    block_table, num_accepted_tokens, *, tokens_per_seq: int, scale: float = 1.0,
+                    out=None):
+    """Speculative decoding with a state per token. ``block_table`` is an
+    int32 [num_seqs, >= tokens_per_seq] view (any strides): request n starts
+    from the slot in column num_accepted_tokens[n] - 1 and the state after
+    its token t is written to the slot in column t (null entries skipped).
+    ``initial_state`` (fp32 [slots, H, K, V]) is updated in place. Returns
+    ``(out, initial_state)``."""
+    m = _Marshal()
+    m.tensor("block_table", block_table, torch.int32, 2)
+    m.tensor("num_accepted_tokens", num_accepted_tokens, torch.int32, 1)
+    m.raise_if_any()
+    tps = int(tokens_per_seq)
+    num_seqs = block_table.shape[0]
+    m.check(block_table.shape[1] >= tps,
+            f"block_table has {block_table.shape[1]} columns, needs tokens_per_seq = {tps}")
+    m.raise_if_any()
+    col0 = block_table[:, 0]
+    H, K, V = _common(m, mixed_qkv, raw_g, raw_beta, A_log, dt_bias, initial_state, col0)
+    rows = num_seqs * tps
+    m.check(mixed_qkv.shape[0] == rows,
+            f"mixed_qkv has {mixed_qkv.shape[0]} rows, expected num_seqs*tokens_per_seq = {rows}")
+    m.check(num_accepted_tokens.shape[0] == num_seqs and num_accepted_tokens.is_contiguous(),
+            f"num_accepted_tokens must be a contiguous [{num_seqs}] tensor")
+    m.raise_if_any()
+    out = _out(out, rows, H, V, mixed_qkv.device, m)
+    g, s = _gate(A_log, dt_bias, lower_bound, scale), _state(initial_state, col0)
+    st = lib().kda_spec_decode(num_seqs, tps, H, K, V, _ptr(mixed_qkv), mixed_qkv.stride(0),
+                               _ptr(raw_g), _ptr(raw_beta), ctypes.byref(g), ctypes.byref(s),
+                               block_table.stride(1), _ptr(num_accepted_tokens), _ptr(out),
+                               _stream(mixed_qkv.device))
     _raise_if(st)
     return out, initial_state
 

@@ -195,6 +195,30 @@ kda_status_t kda_decode_packed(int32_t num_seqs, int32_t tokens_per_seq, int32_t
   return hip_status(kda::launch_decode(p, K, stream), "decode launch");
 }
 
+kda_status_t kda_spec_decode(int32_t num_seqs, int32_t tokens_per_seq, int32_t H, int32_t K,
+                             int32_t V, const void* mixed_qkv, int64_t qkv_row_stride,
+                             const void* raw_g, const void* raw_beta, const kda_gate_t* gate,
+                             const kda_state_t* state, int64_t index_col_stride,
+                             const int32_t* num_accepted_tokens, void* out, hipStream_t stream) {
+  Checks c;
+  const auto INV = KDA_ERR_INVALID_ARGUMENT;
+  c.require(num_seqs >= 0, INV, "num_seqs must be >= 0");
+  c.require(tokens_per_seq >= 1 && tokens_per_seq <= 8, INV,
+            "tokens_per_seq must be in 1..8 (spec-verify steps have at most 8 rows per request)");
+  const int64_t rows = static_cast<int64_t>(num_seqs) * tokens_per_seq;
+  c.require(rows <= 0x7fffffffLL, INV, "num_seqs * tokens_per_seq must fit in int32");
+  c.require(index_col_stride >= 1, INV, "index_col_stride must be >= 1");
+  c.require(num_accepted_tokens != nullptr, INV, "num_accepted_tokens must not be NULL");
+  check_common(c, rows, H, K, V, mixed_qkv, qkv_row_stride, raw_g, raw_beta, gate, state, out);
+  if (!c.ok()) return c.finish();
+  if (num_seqs == 0) return c.finish();
+  kda::DecodeParams p = decode_params(num_seqs, tokens_per_seq, H, V, mixed_qkv, qkv_row_stride,
+                                      raw_g, raw_beta, gate, state, out);
+  p.num_accepted = num_accepted_tokens;
+  p.index_col_stride = index_col_stride;
+  return hip_status(kda::launch_decode(p, K, stream), "spec decode launch");
+}
+
 size_t kda_chunk_prefill_workspace_size(int32_t num_seqs, int64_t num_tokens, int32_t H, int32_t K,
                                         int32_t V) {
   if (num_seqs < 0 || num_tokens < 0 || H < 1 || !(K == 64 || K == 128) || !(V == 64 || V == 128))

@@ -3,7 +3,10 @@
 // Packed decode (vLLM PR #51682 report, Key source excerpts): one state slot
 // per request, addressed through a possibly strided index view; spec-verify
 // (vLLM PR #60683, Refusal and steps): whole requests of tokens_per_seq rows,
-// padded requests on a null slot.
+// padded requests on a null slot. Spec decode with a state per token (vLLM
+// PR #51682 report, Purpose: the state slot is column 0 of a block table with
+// 1 + num_speculative_blocks columns): the initial state comes from column
+// num_accepted-1 and the state after token t is stored into column t.
 //
 // Work split. The V columns of a state evolve independently (u_j depends only
 // on column j), so a workgroup owns a (request, head, VT-column) tile of the
@@ -71,8 +74,14 @@ void decode_kernel(const DecodeParams p) {
   const int rg = lane / CG;
   const int col = tile * VT + cg * 4;
 
-  // State slot of this request: a strided 1-D view, widened to 64 bits.
-  const int64_t slot = static_cast<int64_t>(p.indices[static_cast<int64_t>(n) * p.index_stride]);
+  // State slot of this request: a strided 1-D view, widened to 64 bits. With
+  // a state per token, the initial slot is the one in column num_accepted-1
+  // (clamped to the request's columns) and every token's slot is read now.
+  const int32_t* irow = p.indices + static_cast<int64_t>(n) * p.index_stride;
+  const bool per_token = p.num_accepted != nullptr;
+  int init_col = 0;
+  if (per_token) init_col = min(max(uniform(p.num_accepted[n]), 1), tps) - 1;
+  const int64_t slot = uniform(static_cast<int64_t>(irow[init_col * p.index_col_stride]));
 
   if (slot < 0) {
     // Null slot (the same for the whole workgroup): no state traffic, zero rows.
@@ -167,6 +176,16 @@ void decode_kernel(const DecodeParams p) {
     for (int c = 0; c < 4; ++c) u[c] = beta * (s_v[t][cg * 4 + c] - kS[c]);
 #pragma unroll
     for (int r = 0; r < RPL; ++r) S[r] += s_k[t][w * RW + rg * RPL + r] * u;
+    if (per_token) {
+      // The state after token t goes to column t's slot (none when null).
+      const int64_t st = uniform(static_cast<int64_t>(irow[t * p.index_col_stride]));
+      if (st >= 0) {
+        const __amdgpu_buffer_rsrc_t tr =
+            make_rsrc(p.pool + st * p.slot_stride + static_cast<int64_t>(h) * K * V, K * V * 4);
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) buffer_store_f32x4<kStreamPolicy>(S[r], tr, voff, r * V * 4);
+      }
+    }
     if (w == 0 && rg == 0) {
       const float s = p.scale;
       uint16_t* o = p.out + ((row0 + t) * H + h) * static_cast<int64_t>(V) + col;
@@ -176,9 +195,11 @@ void decode_kernel(const DecodeParams p) {
     }
   }
 
-  // 4. Store the final state.
+  // 4. Store the final state (with a state per token it is already stored).
+  if (!per_token) {
 #pragma unroll
-  for (int r = 0; r < RPL; ++r) buffer_store_f32x4<kStreamPolicy>(S[r], tile_rsrc, voff, r * V * 4);
+    for (int r = 0; r < RPL; ++r) buffer_store_f32x4<kStreamPolicy>(S[r], tile_rsrc, voff, r * V * 4);
+  }
 }
 
 template <int K, int V>

@@ -23,6 +23,12 @@ struct DecodeParams {
   int64_t slot_stride;
   const int32_t* indices;
   int64_t index_stride;
+  // Spec decode with a state per token (null for plain decode): request n
+  // starts from the slot in column num_accepted[n]-1 of its index row and
+  // stores its state after token t into column t (entry n*index_stride +
+  // c*index_col_stride).
+  const int32_t* num_accepted;
+  int64_t index_col_stride;
   uint16_t* out;            // bf16 [rows][H][V]
   int32_t num_seqs;
   int32_t tokens_per_seq;

@@ -104,6 +104,35 @@ kda_status_t kda_decode_packed(int32_t num_seqs, int32_t tokens_per_seq,
                                const kda_gate_t* gate, const kda_state_t* state,
                                void* out, hipStream_t stream);
 
+/*
+ * Speculative decoding with a state per token (vLLM PR #51682 report,
+ * Purpose: with speculative decoding the KDA state slot is column 0 of a
+ * block table with 1 + num_speculative_blocks columns; vLLM PR #60683,
+ * Refusal and steps: a padded request carries a null slot and one accepted
+ * token).
+ *
+ * As kda_decode_packed, except for the state slots. state->indices is a
+ * device int32 block table: request n's column c is
+ * indices[n*index_stride + c*index_col_stride], and every request must have
+ * tokens_per_seq columns. The initial state is read from the slot in column
+ * num_accepted_tokens[n] - 1 (device int32 [num_seqs]; values outside
+ * 1..tokens_per_seq are clamped into it), and the state after the request's
+ * token t is written to the slot in column t; a null entry there skips that
+ * write. A request whose initial entry is null reads and writes no state and
+ * yields zero output rows. Slots of different requests must be distinct
+ * (caller's guarantee, as for the other entry points).
+ * Errors: KDA_ERR_INVALID_ARGUMENT (also for index_col_stride < 1 or a NULL
+ * num_accepted_tokens), KDA_ERR_UNSUPPORTED, KDA_ERR_HIP.
+ */
+kda_status_t kda_spec_decode(int32_t num_seqs, int32_t tokens_per_seq,
+                             int32_t H, int32_t K, int32_t V,
+                             const void* mixed_qkv, int64_t qkv_row_stride,
+                             const void* raw_g, const void* raw_beta,
+                             const kda_gate_t* gate, const kda_state_t* state,
+                             int64_t index_col_stride,
+                             const int32_t* num_accepted_tokens,
+                             void* out, hipStream_t stream);
+
 /* Bytes of device workspace kda_chunk_prefill needs for these sizes (a pure
  * host computation; returns 0 for invalid sizes). */
 size_t kda_chunk_prefill_workspace_size(int32_t num_seqs, int64_t num_tokens,

@@ -73,6 +73,18 @@ def test_decode_rejects_and_lists_every_reason():
         assert frag in msg, msg
 
 
+def test_spec_decode_rejects_and_lists_every_reason():
+    L = kda.lib()
+    g, s = _gate(), _state()
+    st = L.kda_spec_decode(4, 9, 32, 128, 128, FAKE, 3 * 32 * 128, FAKE, FAKE, ctypes.byref(g),
+                           ctypes.byref(s), 0, None, FAKE, None)
+    msg = L.kda_last_error().decode()
+    assert st == 1
+    for frag in ("tokens_per_seq must be in 1..8", "index_col_stride must be >= 1",
+                 "num_accepted_tokens must not be NULL"):
+        assert frag in msg, msg
+
+
 def test_negative_index_stride_rejected():
     st, msg = _decode(s=_state(index_stride=-8))
     assert st == 1 and "index_stride" in msg
