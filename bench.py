@@ -14,8 +14,8 @@ and never synchronise) and the graph is replayed; HIP events on the replay
 stream bracket the timed region. Eager (Python-launched) times are reported
 next to them. The same JSON line carries the other legs of the hot path:
 spec-verify (8 rows), chunked prefill (one 8192-token sequence; 64 varlen
-sequences), the mixed 4096-token batch and spec decode with a state per
-token.
+sequences; one 65536-token sequence), the mixed 4096-token batch and spec
+decode with a state per token.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs ...]
 """
@@ -415,6 +415,7 @@ def main():
         extra["prefill_t8192"] = leg_prefill(pf_steps, 2, [8192], "prefill_t8192_h32_k128", 3000)
         extra["prefill_varlen64"] = leg_prefill(pf_steps, 2, W.random_lengths(64, 1, 256, 3001, force_ones=2),
                                                 "prefill_varlen64_h32_k128", 3002)
+        extra["prefill_t65536"] = leg_prefill(max(pf_steps // 2, 4), 1, [65536], "prefill_t65536_h32_k128", 3004)
     if "mixed" in legs:
         extra["mixed_4096"] = leg_mixed(max(args.steps // 16, 9), 9)
 

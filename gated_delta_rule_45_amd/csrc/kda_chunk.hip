@@ -37,6 +37,8 @@
 // The A operands that meet such a B operand (-W and Q o e^gam along channels,
 // P and K^T along positions) are stored in that permuted order, so S and V'
 // never leave registers.
+#include <algorithm>
+
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -144,47 +146,204 @@ struct Rec {
 // LDS DMA) have completed: vmcnt = 0, other counters unconstrained.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-size_t header_bytes(int32_t num_seqs) {
-  return (static_cast<size_t>(num_seqs + 1) * 4 + 255) / 256 * 256;
-}
-
 __host__ __device__ inline int64_t max_chunks_for(int64_t num_tokens, int32_t num_seqs) {
   return num_tokens / C + num_seqs;
 }
 
-// One byte per (chunk slot, head): 1 when the chunk needs the exact path.
-size_t flag_bytes(int64_t num_tokens, int32_t num_seqs, int32_t H) {
-  return (static_cast<size_t>(max_chunks_for(num_tokens, num_seqs)) * H + 255) / 256 * 256;
+// Records, maps and starting states are laid out head-major: the chunks of
+// one head follow each other, so a workgroup walking a head's chunks reads
+// one contiguous stream.
+__device__ __forceinline__ int64_t rec_index(int h, int c, const PrefillParams& p) {
+  return static_cast<int64_t>(h) * max_chunks_for(p.num_tokens, p.num_seqs) + c;
+}
+
+// ------------------------------------------------------------- segments --
+//
+// The inter-chunk pass carries one state per (sequence, head) through the
+// sequence's chunks, so a long sequence is a chain of dependent steps on a
+// few workgroups. The chunk recurrence is affine in the state: after a run
+// of chunks, S_out = M S_in + B with
+//   M = prod_c (diag(e^{gam_last}) - (K o e^{gam_last - gam})^T W)   (K x K)
+//   B = the state reached from S_in = 0                                (K x V)
+// so a long sequence is cut into segments: a map pass computes (M, B) of
+// every segment but the last in parallel, a combine pass walks the segments
+// in order (S_{j+1} = M_j S_j + B_j, a K x K by K x V product per step),
+// and the state pass then runs all segments in parallel from their true
+// starting states.
+//
+// A sequence is cut into at most ceil(chunks / kSegMinChunks) segments of
+// equal length (the last may be shorter), into no more segments than it
+// takes for the cut sequences' state-pass workgroups to occupy kChipSlots
+// slots (one per compute unit: its LDS image allows one workgroup per CU),
+// and only into kMinCut segments or more: a map chunk costs about as much as
+// a state chunk, so two segments would not shorten the chain.
+constexpr int kSegMinChunks = 16;
+constexpr int kMaxSegs = 16;  // <= kSegMinChunks: keeps the last segment non-empty
+constexpr int kMinCut = 3;
+constexpr int kChipSlots = 256;
+static_assert(kMaxSegs <= kSegMinChunks, "segment count bound");
+
+// Device-side plan of one prefill call, written by plan_kernel.
+struct SegPlan {
+  int32_t* chunk_start;  // [N+1] first chunk slot of each sequence
+  int32_t* seg_start;    // [N+1] first segment of each sequence
+  int32_t* counts;       // [4]: segments, maps, long sequences, plan fits its bounds
+  int32_t* seg_seq;      // [seg_bound] sequence of each segment
+  int32_t* seg_buf;      // [seg_bound] start-state buffer of a cut sequence's segment, else -1
+  int32_t* map_seg;      // [map_bound] segment of each map item (a non-final segment)
+  int32_t* long_seq;     // [long_bound] the cut sequences
+  float* maps;           // [H][map_bound]: M (fp32 [K][K]) then B (fp32 [K][V])
+  float* starts;         // [H][map_bound + long_bound]: fp32 [K][V] starting states
+  int32_t seg_bound, map_bound, long_bound;
+  int32_t max_segs;      // segments per sequence at most (host bound)
+  int32_t fill_units;    // state-pass workgroups per segment (H * V / 64)
+};
+
+__device__ __forceinline__ int64_t map_index(int h, int mi, const SegPlan& pl) {
+  return static_cast<int64_t>(h) * pl.map_bound + mi;
+}
+__device__ __forceinline__ int64_t start_index(int h, int sb, const SegPlan& pl) {
+  return static_cast<int64_t>(h) * (pl.map_bound + pl.long_bound) + sb;
+}
+
+// Workspace layout (byte offsets) for one call's sizes. Bounds: a cut
+// sequence of len tokens has fewer than len / (64 kSegMinChunks) non-final
+// segments, so a call has at most num_tokens / (64 kSegMinChunks) of them
+// (and at most num_seqs (max_segs - 1)); each cut sequence has at least one.
+struct Layout {
+  int64_t seg_bound, map_bound, long_bound, max_segs, fill_units;
+  size_t chunk_start, seg_start, counts, seg_seq, seg_buf, map_seg, long_seq;
+  size_t flags, recs, maps, starts, total;
+};
+
+inline size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+inline size_t rec_bytes_for(int32_t K, int32_t V) {
+  if (K == 64 && V == 64) return Rec<64, 64>::bytes;
+  if (K == 64 && V == 128) return Rec<64, 128>::bytes;
+  if (K == 128 && V == 64) return Rec<128, 64>::bytes;
+  return Rec<128, 128>::bytes;
+}
+
+inline Layout layout_for(int32_t num_seqs, int64_t num_tokens, int32_t H, int32_t K, int32_t V) {
+  Layout L{};
+  const int64_t N = num_seqs;
+  L.fill_units = static_cast<int64_t>(H) * (V / 64);
+  L.max_segs = std::min<int64_t>(kMaxSegs, std::max<int64_t>(1, (kChipSlots + L.fill_units - 1) / L.fill_units));
+  L.map_bound = L.max_segs < kMinCut ? 0 : std::min<int64_t>(num_tokens / (C * kSegMinChunks), N * (L.max_segs - 1));
+  L.long_bound = L.map_bound;
+  L.seg_bound = N + L.map_bound;
+  size_t o = 0;
+  L.chunk_start = o; o += (N + 1) * 4;
+  L.seg_start = o;   o += (N + 1) * 4;
+  L.counts = o;      o += 16;
+  L.seg_seq = o;     o += L.seg_bound * 4;
+  L.seg_buf = o;     o += L.seg_bound * 4;
+  L.map_seg = o;     o += L.map_bound * 4;
+  L.long_seq = o;    o += L.long_bound * 4;
+  L.flags = round256(o);
+  const int64_t maxc = max_chunks_for(num_tokens, num_seqs);
+  L.recs = L.flags + round256(static_cast<size_t>(maxc) * H);
+  L.maps = L.recs + static_cast<size_t>(maxc) * H * rec_bytes_for(K, V);
+  L.starts = L.maps + static_cast<size_t>(L.map_bound) * H * (static_cast<size_t>(K) * K + static_cast<size_t>(K) * V) * 4;
+  L.total = L.starts + static_cast<size_t>(L.map_bound + L.long_bound) * H * static_cast<size_t>(K) * V * 4;
+  return L;
 }
 
 // ------------------------------------------------------------------ plan --
 
-// chunk_start[i] = sum_{j<i} ceil(len_j / 64); chunk_start[N] = total chunks.
-__global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t* cu, int32_t N,
-                                                         int32_t* chunk_start) {
-  __shared__ int part[kThreads];
+// Exclusive prefix sum of x over the workgroup (kThreads threads, 64-lane
+// waves); `total` receives the sum. Every thread must call it.
+__device__ __forceinline__ int block_exclusive_scan(int x, int* part, int& total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int inc = x;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(inc, d, 64);
+    if (lane >= d) inc += y;
+  }
+  if (lane == 63) part[w] = inc;
+  __syncthreads();
+  int before = 0;
+  total = 0;
+#pragma unroll
+  for (int k = 0; k < kThreads / 64; ++k) {
+    const int t = part[k];
+    if (k < w) before += t;
+    total += t;
+  }
+  __syncthreads();
+  return before + inc - x;
+}
+
+__device__ __forceinline__ int chunks_of(const int32_t* cu, int i) {
+  return (max(cu[i + 1] - cu[i], 0) + C - 1) / C;
+}
+
+__device__ __forceinline__ int segments_of(int nch, int target) {
+  const int ns = min((nch + kSegMinChunks - 1) / kSegMinChunks, target);
+  return ns >= kMinCut ? ns : 1;
+}
+
+// Chunk slots and segments of every sequence. The segment target is the
+// number of segments each cut sequence needs for the cut sequences together
+// to occupy the chip.
+__global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t* cu, int32_t N, SegPlan pl) {
+  __shared__ int part[kThreads / 64];
   const int tid = threadIdx.x;
   const int per = (N + kThreads - 1) / kThreads;
   const int b = tid * per;
   const int e = min(N, b + per);
-  int cnt = 0;
-  for (int i = b; i < e; ++i) cnt += (max(cu[i + 1] - cu[i], 0) + C - 1) / C;
-  part[tid] = cnt;
-  __syncthreads();
-  if (tid == 0) {
-    int acc = 0;
-    for (int k = 0; k < kThreads; ++k) {
-      const int x = part[k];
-      part[k] = acc;
-      acc += x;
-    }
-    chunk_start[N] = acc;
-  }
-  __syncthreads();
-  int acc = part[tid];
+  int nl = 0;
+  for (int i = b; i < e; ++i) nl += chunks_of(cu, i) > (kMinCut - 1) * kSegMinChunks;  // can be cut
+  int n_long;
+  block_exclusive_scan(nl, part, n_long);
+  const int units = pl.fill_units * max(n_long, 1);
+  const int target = min(pl.max_segs, max(1, (kChipSlots + units - 1) / units));
+
+  int cc = 0, sc = 0, lc = 0;
   for (int i = b; i < e; ++i) {
-    chunk_start[i] = acc;
-    acc += (max(cu[i + 1] - cu[i], 0) + C - 1) / C;
+    const int nch = chunks_of(cu, i);
+    const int ns = segments_of(nch, target);
+    cc += nch;
+    sc += ns;
+    lc += ns > 1;
+  }
+  int ctot, stot, ltot;
+  int cb = block_exclusive_scan(cc, part, ctot);
+  int sb = block_exclusive_scan(sc, part, stot);
+  int lb = block_exclusive_scan(lc, part, ltot);
+  const int mtot = stot - N;
+  // Holds for cu_seqlens that keep to the contract; otherwise no segment
+  // tables are written and the state pass does nothing.
+  const bool fits = stot <= pl.seg_bound && mtot <= pl.map_bound && ltot <= pl.long_bound;
+  for (int i = b; i < e; ++i) {
+    const int nch = chunks_of(cu, i);
+    const int ns = segments_of(nch, target);
+    pl.chunk_start[i] = cb;
+    pl.seg_start[i] = sb;
+    if (fits) {
+      // Map items of sequence i start at sb - i (each earlier sequence has
+      // one fewer than its segments); its start-state buffers at sb - i + lb
+      // (each earlier cut sequence has one per segment).
+      for (int s = 0; s < ns; ++s) {
+        pl.seg_seq[sb + s] = i;
+        pl.seg_buf[sb + s] = ns > 1 ? sb - i + lb + s : -1;
+      }
+      for (int s = 0; s + 1 < ns; ++s) pl.map_seg[sb - i + s] = sb + s;
+      if (ns > 1) pl.long_seq[lb] = i;
+    }
+    cb += nch;
+    sb += ns;
+    lb += ns > 1;
+  }
+  if (tid == 0) {
+    pl.chunk_start[N] = ctot;
+    pl.seg_start[N] = stot;
+    pl.counts[0] = stot;
+    pl.counts[1] = mtot;
+    pl.counts[2] = ltot;
+    pl.counts[3] = fits ? 1 : 0;
   }
 }
 
@@ -305,7 +464,7 @@ __device__ __forceinline__ void intra_body(const PrefillParams& p, const int32_t
   constexpr int KP8 = K / 8;                     // 16-byte pieces per bf16 row
   constexpr int KPM = (KP8 > 16 ? 16 : KP8) - 1;
 
-  char* rec = recs + (static_cast<int64_t>(c) * H + h) * static_cast<int64_t>(R::bytes);
+  char* rec = recs + rec_index(h, c, p) * static_cast<int64_t>(R::bytes);
   float* x = sm.u.f.x;
   uint16_t* wkt = reinterpret_cast<uint16_t*>(sm.u.f.x);
 
@@ -942,27 +1101,34 @@ struct StateBuf {
   float eg[K];
 };
 
-// Copy record `rec`'s LDS part into `b` by buffer-to-LDS DMA: lane l of a
-// wave writes its 16 bytes at the wave's LDS base + 16 l, so slot i takes
-// piece i. Nothing passes through registers and no per-lane address math is
-// needed; the copy runs until the next vmcnt wait. `wave` is the wave index
-// in a scalar register.
-template <int K, int V>
-__device__ __forceinline__ void dma_chunk(const char* rec, StateBuf<K, V>* b, int tid, int wave) {
-  constexpr int total = static_cast<int>(sizeof(StateBuf<K, V>) / 16);
-  constexpr int full = total / kThreads, rem = total % kThreads;
-  const __amdgpu_buffer_rsrc_t rr = make_rsrc(rec, static_cast<uint32_t>(sizeof(StateBuf<K, V>)));
-  uint4* dst = reinterpret_cast<uint4*>(b) + wave * 64;
+// Copy `Bytes` bytes (whole 16-byte pieces) from `src` to LDS at `dst` by
+// buffer-to-LDS DMA: lane l of a wave writes its 16 bytes at the wave's LDS
+// base + 16 l, so slot i takes piece i. Nothing passes through registers and
+// no per-lane address math is needed; the copy runs until the next vmcnt
+// wait. `wave` is the wave index in a scalar register.
+template <int Bytes, int NT>
+__device__ __forceinline__ void dma_copy(const char* src, void* dst_lds, int tid, int wave) {
+  static_assert(Bytes % 16 == 0, "whole 16-byte pieces");
+  constexpr int total = Bytes / 16;
+  constexpr int full = total / NT, rem = total % NT;
+  const __amdgpu_buffer_rsrc_t rr = make_rsrc(src, static_cast<uint32_t>(Bytes));
+  uint4* dst = reinterpret_cast<uint4*>(dst_lds) + wave * 64;
   const int voff = tid * 16;
 #pragma unroll
   for (int r = 0; r < full; ++r)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, dst + r * kThreads, 16, voff, r * kThreads * 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, dst + r * NT, 16, voff, r * NT * 16, 0, 0);
   if constexpr (rem > 0) {
-    // Only lanes whose slot lies inside the record take part (inactive lanes
+    // Only lanes whose slot lies inside the range take part (inactive lanes
     // write nothing).
     if (tid < rem)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, dst + full * kThreads, 16, voff, full * kThreads * 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, dst + full * NT, 16, voff, full * NT * 16, 0, 0);
   }
+}
+
+// Copy record `rec`'s LDS part into `b` with NT threads.
+template <int K, int V, int NT>
+__device__ __forceinline__ void dma_chunk(const char* rec, StateBuf<K, V>* b, int tid, int wave) {
+  dma_copy<static_cast<int>(sizeof(StateBuf<K, V>)), NT>(rec, b, tid, wave);
 }
 
 // Output stores per lane per chunk: one 8-byte store per 16-position block.
@@ -982,17 +1148,20 @@ __device__ __forceinline__ void chunk_barrier() {
 
 template <int K, int V>
 __global__ __launch_bounds__(kThreads, 1) void chunk_state_kernel(const PrefillParams p,
-                                                                  const int32_t* chunk_start,
+                                                                  const SegPlan pl,
                                                                   const char* recs) {
   using R = Rec<K, V>;
   using B = StateBuf<K, V>;
   static_assert(sizeof(B) == R::lds_part, "LDS image is the record's first lds_part bytes");
   static_assert(R::lds_part % 16 == 0, "record LDS part must be whole 16-byte pieces");
-  constexpr int NVH = V / 64;  // workgroups per (sequence, head): 64 columns each
+  constexpr int NVH = V / 64;  // workgroups per (segment, head): 64 columns each
   __shared__ B buf[2];
 
-  // The NVH workgroups of one (sequence, head) read the same records: give
+  // The NVH workgroups of one (segment, head) read the same records: give
   // them indices that are equal modulo 8 so they run on the same XCD (one L2).
+  // (Four waves per workgroup: every wave reads the whole of each record's
+  // tiles from LDS, so more waves per workgroup would make LDS reads, not
+  // the record copies, the bound.)
   const int bidx = blockIdx.x;
   int pair, vh;
   if constexpr (NVH == 2) {
@@ -1003,17 +1172,29 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_state_kernel(const PrefillP
     vh = 0;
   }
   const int H = p.H;
-  if (pair >= p.num_seqs * H) return;
-  const int seq = pair / H, h = pair % H;
-  // Values loaded from wave-uniform addresses, kept in scalar registers.
-  const int64_t bos = uniform(static_cast<int64_t>(p.cu_seqlens[seq]));
-  const int64_t eos = uniform(static_cast<int64_t>(p.cu_seqlens[seq + 1]));
-  const int c0 = uniform(chunk_start[seq]);
-  const int nch = uniform(chunk_start[seq + 1]) - c0;
-  if (nch <= 0 || eos > p.num_tokens || bos < 0) return;
+  if (uniform(pl.counts[3]) == 0) return;  // cu_seqlens outside the contract
+  const int gs = pair / H, h = pair % H;
+  if (gs >= uniform(pl.counts[0])) return;
   // Records exist for at most max_chunks chunks (sized from the host's token
   // count); inconsistent cu_seqlens must not send us past them.
-  if (chunk_start[p.num_seqs] > max_chunks_for(p.num_tokens, p.num_seqs)) return;
+  if (pl.chunk_start[p.num_seqs] > max_chunks_for(p.num_tokens, p.num_seqs)) return;
+  // Values loaded from wave-uniform addresses, kept in scalar registers.
+  const int seq = uniform(pl.seg_seq[gs]);
+  const int seg0 = uniform(pl.seg_start[seq]);
+  const int nseg = uniform(pl.seg_start[seq + 1]) - seg0;
+  const int sg = gs - seg0;
+  const int cbase = uniform(pl.chunk_start[seq]);
+  const int nch_seq = uniform(pl.chunk_start[seq + 1]) - cbase;
+  const int seg_len = (nch_seq + nseg - 1) / nseg;
+  const int cfirst = sg * seg_len;
+  const int nch = min(nch_seq, cfirst + seg_len) - cfirst;
+  const int c0 = cbase + cfirst;
+  const bool last_seg = sg == nseg - 1;
+  const int64_t bos = uniform(static_cast<int64_t>(p.cu_seqlens[seq]));
+  const int64_t eos = uniform(static_cast<int64_t>(p.cu_seqlens[seq + 1]));
+  if (nch <= 0 || eos > p.num_tokens || bos < 0) return;
+  const int64_t tfirst = bos + static_cast<int64_t>(C) * cfirst;
+  const int64_t tend = min<int64_t>(eos, tfirst + static_cast<int64_t>(C) * nch);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1027,16 +1208,22 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_state_kernel(const PrefillP
   const int64_t slot = uniform(static_cast<int64_t>(p.indices[static_cast<int64_t>(seq) * p.index_stride]));
   if (slot < 0) {
     // Null slot: zero output rows, no state traffic.
-    for (int64_t t = bos; t < eos; ++t)
+    for (int64_t t = tfirst; t < tend; ++t)
       if (tid < 64) p.out[t * HV + h * V + vh * 64 + tid] = 0;
     return;
   }
 
   float* st = p.pool + slot * p.slot_stride + static_cast<int64_t>(h) * K * V;
-  const bool init = p.has_initial_state == nullptr || uniform(static_cast<int32_t>(p.has_initial_state[seq])) != 0;
+  // A segment of a cut sequence starts from the state the combine pass
+  // stored for it (the first segment too: the slot is written by the last
+  // segment of this same launch); an uncut sequence from its slot.
+  const int sbuf = uniform(pl.seg_buf[gs]);
+  const float* s_in = sbuf >= 0 ? pl.starts + start_index(h, sbuf, pl) * K * V : st;
+  const bool init = sbuf >= 0 || p.has_initial_state == nullptr ||
+                    uniform(static_cast<int32_t>(p.has_initial_state[seq])) != 0;
   // Without an initial state the range is empty and every load reads zero;
   // all loads are issued before the first use.
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(st, init ? static_cast<uint32_t>(K * V * 4) : 0u);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(s_in, init ? static_cast<uint32_t>(K * V * 4) : 0u);
   f32x4 S[K / 16];
 #pragma unroll
   for (int cb = 0; cb < K / 16; ++cb)
@@ -1047,7 +1234,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_state_kernel(const PrefillP
 
   f32x4 Upre[4];
   auto rec_of = [&](int cc) {
-    return recs + (static_cast<int64_t>(c0 + cc) * H + h) * static_cast<int64_t>(R::bytes);
+    return recs + rec_index(h, c0 + cc, p) * static_cast<int64_t>(R::bytes);
   };
   // U fragments: lane's 16 bytes of tile (pb, col0 / 16) at a fixed offset.
   const int u_lane = ((col0 / 16) * 64 + lane) * 16;
@@ -1056,7 +1243,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_state_kernel(const PrefillP
 #pragma unroll
     for (int pb = 0; pb < 4; ++pb) Upre[pb] = buffer_load_f32x4<0>(ru, u_lane, pb * (V / 16) * 64 * 16);
   };
-  dma_chunk<K, V>(rec_of(0), &buf[0], tid, wave);
+  dma_chunk<K, V, kThreads>(rec_of(0), &buf[0], tid, wave);
   load_u(0);
   // Lane (m, g) of the transposed output tile of position block pb holds
   // channels col0 + 4 g .. + 3 of position 16 pb + m: 8 contiguous bytes.
@@ -1071,11 +1258,11 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_state_kernel(const PrefillP
 #pragma unroll
     for (int pb = 0; pb < 4; ++pb) Vp[pb] = Upre[pb];
     if (cc + 1 < nch) {
-      dma_chunk<K, V>(rec_of(cc + 1), &buf[(cc + 1) & 1], tid, wave);
+      dma_chunk<K, V, kThreads>(rec_of(cc + 1), &buf[(cc + 1) & 1], tid, wave);
       load_u(cc + 1);
     }
 
-    const int64_t t0 = bos + static_cast<int64_t>(C) * cc;
+    const int64_t t0 = tfirst + static_cast<int64_t>(C) * cc;
     const int n = static_cast<int>(min<int64_t>(C, eos - t0));
 
     // V' = U - W S (rows: positions) and O^T = S^T (Q o e^gam)^T (rows:
@@ -1165,26 +1352,335 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_state_kernel(const PrefillP
     }
   }
 
+  if (!last_seg) return;
 #pragma unroll
   for (int cb = 0; cb < K / 16; ++cb)
 #pragma unroll
     for (int j = 0; j < 4; ++j) st[(16 * cb + 4 * g + j) * V + col0 + m] = S[cb][j];
 }
 
+// ----------------------------------------------------------------- map --
+
+// LDS image of the record parts the map pass reads: -W, and the
+// contiguous (K o e^{gam_last - gam})^T and e^{gam_last}.
 template <int K, int V>
-hipError_t launch_kv(const PrefillParams& p, int32_t* chunk_start, uint8_t* exact_flags, char* recs,
-                     hipStream_t stream) {
+struct MapBuf {
+  uint16_t wn[C * K];
+  uint16_t kgt[K * C];
+  float eg[K];
+};
+
+// One workgroup per (map item, head, 128 columns of [M | B]), 32 columns
+// (two MFMA column tiles) per wave, so that each operand fragment read from
+// LDS feeds two MFMAs: runs the chunk recurrence of one non-final segment
+// (all of its chunks are full) from S = the identity's columns with U = 0
+// (columns of M) or from S = 0 with the chunk's U (columns of B). There is
+// no output; the rounding is the state pass's (bf16 S into W S, bf16 V' into
+// the update, fp32 accumulation). Waves past column K + V only take part in
+// the copies and barriers (K and V are multiples of 64, so a wave's columns
+// all belong to M or all to B).
+constexpr int kMapWaves = 4;
+constexpr int kMapThreads = kMapWaves * 64;
+constexpr int kMapCT = 2;  // 16-column tiles per wave
+
+template <int K, int V>
+__global__ __launch_bounds__(kMapThreads, 2) void chunk_map_kernel(const PrefillParams p,
+                                                                   const SegPlan pl,
+                                                                   const char* recs) {
+  using R = Rec<K, V>;
+  using B = MapBuf<K, V>;
+  static_assert(R::Eg == R::KgT + static_cast<size_t>(K) * C * 2, "e^{gam_last} follows K^T in the record");
+  static_assert(sizeof(B) == static_cast<size_t>(C) * K * 2 + static_cast<size_t>(K) * C * 2 + K * 4, "packed");
+  constexpr int WCOLS = 16 * kMapCT;                                   // columns per wave
+  constexpr int NW = (K + V + kMapWaves * WCOLS - 1) / (kMapWaves * WCOLS);  // workgroups per (item, head)
+  constexpr int kKgtBytes = K * C * 2 + K * 4;
+  __shared__ B buf[2];
+
+  // The NW workgroups of one (item, head) read the same records: indices
+  // equal modulo 8 put them on one XCD.
+  const int bidx = blockIdx.x;
+  const int pair = (bidx / (8 * NW)) * 8 + bidx % 8;
+  const int sub = (bidx / 8) % NW;
+  const int H = p.H;
+  if (uniform(pl.counts[3]) == 0) return;
+  const int mi = pair / H, h = pair % H;
+  if (mi >= uniform(pl.counts[1])) return;
+  if (pl.chunk_start[p.num_seqs] > max_chunks_for(p.num_tokens, p.num_seqs)) return;
+  const int gs = uniform(pl.map_seg[mi]);
+  const int seq = uniform(pl.seg_seq[gs]);
+  const int seg0 = uniform(pl.seg_start[seq]);
+  const int nseg = uniform(pl.seg_start[seq + 1]) - seg0;
+  const int cbase = uniform(pl.chunk_start[seq]);
+  const int nch_seq = uniform(pl.chunk_start[seq + 1]) - cbase;
+  const int nch = (nch_seq + nseg - 1) / nseg;  // a non-final segment is full length
+  const int c0 = cbase + (gs - seg0) * nch;
+  const int64_t eos = uniform(static_cast<int64_t>(p.cu_seqlens[seq + 1]));
+  if (eos > p.num_tokens) return;
+  const int64_t slot = uniform(static_cast<int64_t>(p.indices[static_cast<int64_t>(seq) * p.index_stride]));
+  if (slot < 0) return;  // a null slot carries no state
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int wave = uniform(w);
+  const int m = lane & 15;
+  const int g = lane >> 4;
+  const int gcol = sub * kMapWaves * WCOLS + WCOLS * wave;  // this wave's first column of [M | B]
+  const bool active = gcol < K + V;
+  const bool is_m = gcol < K;
+  const int col0 = is_m ? gcol : gcol - K;
+
+  f32x4 S[kMapCT][K / 16];
+#pragma unroll
+  for (int ct = 0; ct < kMapCT; ++ct)
+#pragma unroll
+    for (int cb = 0; cb < K / 16; ++cb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) S[ct][cb][j] = (is_m && 16 * cb + 4 * g + j == col0 + 16 * ct + m) ? 1.f : 0.f;
+
+  auto rec_of = [&](int cc) {
+    return recs + rec_index(h, c0 + cc, p) * static_cast<int64_t>(R::bytes);
+  };
+  auto dma = [&](int cc, B* b) {
+    dma_copy<C * K * 2, kMapThreads>(rec_of(cc) + R::Wn, b->wn, tid, wave);
+    dma_copy<kKgtBytes, kMapThreads>(rec_of(cc) + R::KgT, b->kgt, tid, wave);
+  };
+  f32x4 Upre[kMapCT][4];
+  auto load_u = [&](int cc) {
+    const __amdgpu_buffer_rsrc_t ru = make_rsrc(rec_of(cc) + R::Uf, static_cast<uint32_t>(C * V * 4));
+#pragma unroll
+    for (int ct = 0; ct < kMapCT; ++ct)
+#pragma unroll
+      for (int pb = 0; pb < 4; ++pb)
+        Upre[ct][pb] = buffer_load_f32x4<0>(ru, (((col0 + 16 * ct) / 16) * 64 + lane) * 16, pb * (V / 16) * 64 * 16);
+  };
+  const bool takes_u = active && !is_m;
+  dma(0, &buf[0]);
+  if (takes_u) load_u(0);
+  for (int cc = 0; cc < nch; ++cc) {
+    const B& bf = buf[cc & 1];
+    // Chunk cc's copy and U have landed in every wave, every wave's LDS
+    // reads of chunk cc-1's buffer (which the next copy overwrites) are done,
+    // and all waves meet.
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt = 0, expcnt = 7, lgkmcnt = 0
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    f32x4 Vp[kMapCT][4];
+#pragma unroll
+    for (int ct = 0; ct < kMapCT; ++ct)
+#pragma unroll
+      for (int pb = 0; pb < 4; ++pb) Vp[ct][pb] = is_m ? f32x4{0.f, 0.f, 0.f, 0.f} : Upre[ct][pb];
+    if (cc + 1 < nch) {
+      dma(cc + 1, &buf[(cc + 1) & 1]);
+      if (takes_u) load_u(cc + 1);
+    }
+    if (!active) continue;
+    // V' = U - W S over positions.
+    bf16x8 Sh[kMapCT][K / 32];
+#pragma unroll
+    for (int ct = 0; ct < kMapCT; ++ct)
+#pragma unroll
+      for (int kb = 0; kb < K / 32; ++kb) Sh[ct][kb] = pack_acc(S[ct][2 * kb], S[ct][2 * kb + 1]);
+    // Fragments are read one position block (or channel block) ahead of the
+    // MFMAs that use them; the scheduling barriers keep that order, so LDS
+    // latency hides behind the previous block's MFMAs.
+    bf16x8 wf[2][K / 32];
+#pragma unroll
+    for (int kb = 0; kb < K / 32; ++kb) wf[0][kb] = frag<K>(bf.wn, m, 32 * kb + 8 * g);
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (pb + 1 < 4) {
+#pragma unroll
+        for (int kb = 0; kb < K / 32; ++kb) wf[(pb + 1) & 1][kb] = frag<K>(bf.wn, 16 * (pb + 1) + m, 32 * kb + 8 * g);
+      }
+#pragma unroll
+      for (int kb = 0; kb < K / 32; ++kb)
+#pragma unroll
+        for (int ct = 0; ct < kMapCT; ++ct) Vp[ct][pb] = mfma16(wf[pb & 1][kb], Sh[ct][kb], Vp[ct][pb]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 Vb[kMapCT][2];
+#pragma unroll
+    for (int ct = 0; ct < kMapCT; ++ct) {
+      Vb[ct][0] = pack_acc(Vp[ct][0], Vp[ct][1]);
+      Vb[ct][1] = pack_acc(Vp[ct][2], Vp[ct][3]);
+    }
+    // S <- diag(e^{gam_last}) S + (K o e^{gam_last - gam})^T V'.
+    bf16x8 kf[2][2];
+    f32x4 ef[2];
+    kf[0][0] = frag<C>(bf.kgt, m, 8 * g);
+    kf[0][1] = frag<C>(bf.kgt, m, 32 + 8 * g);
+    ef[0] = *reinterpret_cast<const f32x4*>(&bf.eg[4 * g]);
+#pragma unroll
+    for (int cb = 0; cb < K / 16; ++cb) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (cb + 1 < K / 16) {
+        kf[(cb + 1) & 1][0] = frag<C>(bf.kgt, 16 * (cb + 1) + m, 8 * g);
+        kf[(cb + 1) & 1][1] = frag<C>(bf.kgt, 16 * (cb + 1) + m, 32 + 8 * g);
+        ef[(cb + 1) & 1] = *reinterpret_cast<const f32x4*>(&bf.eg[16 * (cb + 1) + 4 * g]);
+      }
+#pragma unroll
+      for (int ct = 0; ct < kMapCT; ++ct) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) S[ct][cb][j] *= ef[cb & 1][j];
+        S[ct][cb] = mfma16(kf[cb & 1][0], Vb[ct][0], S[ct][cb]);
+        S[ct][cb] = mfma16(kf[cb & 1][1], Vb[ct][1], S[ct][cb]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (!active) return;
+  const int64_t item = map_index(h, mi, pl) * (static_cast<int64_t>(K) * K + static_cast<int64_t>(K) * V);
+  float* dst = pl.maps + item + (is_m ? 0 : K * K);
+  const int ld = is_m ? K : V;
+#pragma unroll
+  for (int ct = 0; ct < kMapCT; ++ct)
+#pragma unroll
+    for (int cb = 0; cb < K / 16; ++cb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dst[(16 * cb + 4 * g + j) * ld + col0 + 16 * ct + m] = S[ct][cb][j];
+}
+
+// ------------------------------------------------------------- combine --
+
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// One workgroup per (cut sequence, head, 16 value columns): S_0 = the slot's
+// state (or zero), S_{j+1} = M_j S_j + B_j, each S_j stored as segment j's
+// starting state. fp32 MFMA (16x16x4): in the MFMA that takes contraction
+// indices 16 cb + 4 g + kk (lane group g), lane (m, g) supplies
+// M[row m][16 cb + 4 g + kk] and S[16 cb + 4 g + kk][col m]: four
+// consecutive M entries per lane (one 16-byte load), and four consecutive
+// S entries of one column, read from LDS where S is kept transposed.
+// Wave w owns output row tiles w*RT .. w*RT + RT - 1.
+template <int K, int V>
+__global__ __launch_bounds__(kThreads) void chunk_combine_kernel(const PrefillParams p,
+                                                                 const SegPlan pl) {
+  constexpr int NB = V / 16;   // workgroups per (sequence, head)
+  constexpr int RT = K / 64;   // 16-row tiles per wave
+  constexpr int KB = K / 16;   // 16-index contraction blocks
+  constexpr int LD = K + 4;    // padded row of the transposed state (floats)
+  __shared__ float sT[2][16 * LD];
+
+  const int bidx = blockIdx.x;
+  const int pair = (bidx / (8 * NB)) * 8 + bidx % 8;
+  const int sub = (bidx / 8) % NB;
+  const int H = p.H;
+  if (uniform(pl.counts[3]) == 0) return;
+  const int li = pair / H, h = pair % H;
+  if (li >= uniform(pl.counts[2])) return;
+  const int seq = uniform(pl.long_seq[li]);
+  const int seg0 = uniform(pl.seg_start[seq]);
+  const int nseg = uniform(pl.seg_start[seq + 1]) - seg0;
+  const int mi0 = seg0 - seq;
+  const int sb0 = uniform(pl.seg_buf[seg0]);
+  const int64_t eos = uniform(static_cast<int64_t>(p.cu_seqlens[seq + 1]));
+  if (eos > p.num_tokens || sb0 < 0) return;
+  const int64_t slot = uniform(static_cast<int64_t>(p.indices[static_cast<int64_t>(seq) * p.index_stride]));
+  if (slot < 0) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int m = lane & 15;
+  const int g = lane >> 4;
+  const int c = 16 * sub + m;  // this lane's value column
+  const int64_t KV = static_cast<int64_t>(K) * V;
+  const int64_t item = static_cast<int64_t>(K) * K + KV;
+
+  // Operands of step j: this lane's M entries and B accumulator seeds.
+  f32x4 Ma[RT][KB], Bs[RT];
+  auto load_map = [&](int j, f32x4 (&a)[RT][KB], f32x4 (&bs)[RT]) {
+    const float* M = pl.maps + map_index(h, mi0 + j, pl) * item;
+    const float* Bm = M + static_cast<int64_t>(K) * K;
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        a[r][kb] = *reinterpret_cast<const f32x4*>(M + (16 * (w * RT + r) + m) * K + 16 * kb + 4 * g);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) bs[r][jj] = Bm[(16 * (w * RT + r) + 4 * g + jj) * V + c];
+    }
+  };
+  load_map(0, Ma, Bs);  // nseg > 1 for a cut sequence; issued before the slot's state is read
+  const bool init = p.has_initial_state == nullptr || uniform(static_cast<int32_t>(p.has_initial_state[seq])) != 0;
+  const float* st = p.pool + slot * p.slot_stride + static_cast<int64_t>(h) * KV;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(st, init ? static_cast<uint32_t>(KV * 4) : 0u);
+  f32x4 S[RT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      S[r][j] = __builtin_bit_cast(
+          float, __builtin_amdgcn_raw_buffer_load_b32(rs, ((16 * (w * RT + r) + 4 * g + j) * V + c) * 4, 0, 0));
+  auto store_start = [&](int j) {
+    float* dst = pl.starts + start_index(h, sb0 + j, pl) * KV;
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) dst[(16 * (w * RT + r) + 4 * g + jj) * V + c] = S[r][jj];
+  };
+  store_start(0);
+  for (int j = 0; j + 1 < nseg; ++j) {
+    float* t = sT[j & 1];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) *reinterpret_cast<f32x4*>(&t[m * LD + 16 * (w * RT + r) + 4 * g]) = S[r];
+    // One barrier per step: the other buffer, written next step, was last
+    // read before this barrier.
+    lds_barrier();
+    f32x4 Mn[RT][KB], Bn[RT];
+    if (j + 2 < nseg) load_map(j + 1, Mn, Bn);
+    f32x4 acc[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) acc[r] = Bs[r];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const f32x4 sv = *reinterpret_cast<const f32x4*>(&t[m * LD + 16 * kb + 4 * g]);
+#pragma unroll
+      for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) acc[r] = mfma_f32(Ma[r][kb][kk], sv[kk], acc[r]);
+    }
+#pragma unroll
+    for (int r = 0; r < RT; ++r) S[r] = acc[r];
+    store_start(j + 1);
+    if (j + 2 < nseg) {
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        Bs[r] = Bn[r];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) Ma[r][kb] = Mn[r][kb];
+      }
+    }
+  }
+}
+
+template <int K, int V>
+hipError_t launch_kv(const PrefillParams& p, const Layout& L, const SegPlan& pl, uint8_t* exact_flags,
+                     char* recs, hipStream_t stream) {
   const int64_t maxc = max_chunks_for(p.num_tokens, p.num_seqs);
   const int64_t intra_blocks = maxc * p.H;
-  const int64_t pairs = static_cast<int64_t>(p.num_seqs) * p.H;
-  const int64_t state_blocks = (V / 64 == 2) ? (pairs + 7) / 8 * 16 : pairs;
-  if (intra_blocks > 0x7fffffff || state_blocks > 0x7fffffff) return hipErrorInvalidValue;
+  const int64_t seg_pairs = L.seg_bound * p.H;
+  const int64_t state_blocks = (V / 64 == 2) ? (seg_pairs + 7) / 8 * 16 : seg_pairs;
+  const int64_t map_blocks = (L.map_bound * p.H + 7) / 8 * 8 * ((K + V + 16 * kMapCT * kMapWaves - 1) / (16 * kMapCT * kMapWaves));
+  const int64_t combine_blocks = (L.long_bound * p.H + 7) / 8 * 8 * (V / 16);
+  if (intra_blocks > 0x7fffffff || state_blocks > 0x7fffffff || map_blocks > 0x7fffffff ||
+      combine_blocks > 0x7fffffff)
+    return hipErrorInvalidValue;
   chunk_intra_kernel<K, V><<<dim3(static_cast<unsigned>(intra_blocks)), dim3(kThreads), 0, stream>>>(
-      p, chunk_start, recs, exact_flags);
+      p, pl.chunk_start, recs, exact_flags);
   chunk_intra_exact_kernel<K, V><<<dim3(static_cast<unsigned>(intra_blocks)), dim3(kThreads), 0, stream>>>(
-      p, chunk_start, recs, exact_flags);
+      p, pl.chunk_start, recs, exact_flags);
+  if (L.map_bound > 0) {
+    chunk_map_kernel<K, V><<<dim3(static_cast<unsigned>(map_blocks)), dim3(kMapThreads), 0, stream>>>(p, pl, recs);
+    chunk_combine_kernel<K, V><<<dim3(static_cast<unsigned>(combine_blocks)), dim3(kThreads), 0, stream>>>(p, pl);
+  }
   chunk_state_kernel<K, V><<<dim3(static_cast<unsigned>(state_blocks)), dim3(kThreads), 0, stream>>>(
-      p, chunk_start, recs);
+      p, pl, recs);
   return hipGetLastError();
 }
 
@@ -1192,24 +1688,35 @@ hipError_t launch_kv(const PrefillParams& p, int32_t* chunk_start, uint8_t* exac
 
 size_t prefill_workspace_bytes(int32_t num_seqs, int64_t num_tokens, int32_t H, int32_t K,
                                int32_t V) {
-  size_t rec = 0;
-  if (K == 64 && V == 64) rec = Rec<64, 64>::bytes;
-  if (K == 64 && V == 128) rec = Rec<64, 128>::bytes;
-  if (K == 128 && V == 64) rec = Rec<128, 64>::bytes;
-  if (K == 128 && V == 128) rec = Rec<128, 128>::bytes;
-  return header_bytes(num_seqs) + flag_bytes(num_tokens, num_seqs, H) +
-         static_cast<size_t>(max_chunks_for(num_tokens, num_seqs)) * H * rec;
+  return layout_for(num_seqs, num_tokens, H, K, V).total;
 }
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
-  int32_t* chunk_start = static_cast<int32_t*>(p.workspace);
-  uint8_t* flags = static_cast<uint8_t*>(p.workspace) + header_bytes(p.num_seqs);
-  char* recs = reinterpret_cast<char*>(flags) + flag_bytes(p.num_tokens, p.num_seqs, p.H);
-  plan_kernel<<<1, kThreads, 0, stream>>>(p.cu_seqlens, p.num_seqs, chunk_start);
-  if (p.K == 64 && p.V == 64) return launch_kv<64, 64>(p, chunk_start, flags, recs, stream);
-  if (p.K == 64 && p.V == 128) return launch_kv<64, 128>(p, chunk_start, flags, recs, stream);
-  if (p.K == 128 && p.V == 64) return launch_kv<128, 64>(p, chunk_start, flags, recs, stream);
-  return launch_kv<128, 128>(p, chunk_start, flags, recs, stream);
+  const Layout L = layout_for(p.num_seqs, p.num_tokens, p.H, p.K, p.V);
+  if (L.seg_bound > 0x7fffffff) return hipErrorInvalidValue;
+  char* ws = static_cast<char*>(p.workspace);
+  SegPlan pl;
+  pl.chunk_start = reinterpret_cast<int32_t*>(ws + L.chunk_start);
+  pl.seg_start = reinterpret_cast<int32_t*>(ws + L.seg_start);
+  pl.counts = reinterpret_cast<int32_t*>(ws + L.counts);
+  pl.seg_seq = reinterpret_cast<int32_t*>(ws + L.seg_seq);
+  pl.seg_buf = reinterpret_cast<int32_t*>(ws + L.seg_buf);
+  pl.map_seg = reinterpret_cast<int32_t*>(ws + L.map_seg);
+  pl.long_seq = reinterpret_cast<int32_t*>(ws + L.long_seq);
+  pl.maps = reinterpret_cast<float*>(ws + L.maps);
+  pl.starts = reinterpret_cast<float*>(ws + L.starts);
+  pl.seg_bound = static_cast<int32_t>(L.seg_bound);
+  pl.map_bound = static_cast<int32_t>(L.map_bound);
+  pl.long_bound = static_cast<int32_t>(L.long_bound);
+  pl.max_segs = static_cast<int32_t>(L.max_segs);
+  pl.fill_units = static_cast<int32_t>(L.fill_units);
+  uint8_t* flags = reinterpret_cast<uint8_t*>(ws + L.flags);
+  char* recs = ws + L.recs;
+  plan_kernel<<<1, kThreads, 0, stream>>>(p.cu_seqlens, p.num_seqs, pl);
+  if (p.K == 64 && p.V == 64) return launch_kv<64, 64>(p, L, pl, flags, recs, stream);
+  if (p.K == 64 && p.V == 128) return launch_kv<64, 128>(p, L, pl, flags, recs, stream);
+  if (p.K == 128 && p.V == 64) return launch_kv<128, 64>(p, L, pl, flags, recs, stream);
+  return launch_kv<128, 128>(p, L, pl, flags, recs, stream);
 }
 
 }  // namespace kda

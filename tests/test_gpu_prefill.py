@@ -53,6 +53,44 @@ def test_prefill_varlen_no_lower_bound():
     check_case(case, PREFILL_TOL_O, PREFILL_TOL_S)
 
 
+# Long sequences are cut into segments whose states are composed
+# (S_out = M S_in + B per segment) before every segment runs in parallel. At
+# H=3 these lengths cut three sequences into 3, 5 and 3 segments (shorter
+# than 16 chunks, the last ones ragged); the 1100-token sequence (18 chunks)
+# and the short ones stay whole.
+CUT = [2100, 5, 1100, 1, 4200, 64, 2500]
+
+
+@pytest.mark.parametrize("K,V", [(128, 128), (64, 64), (64, 128), (128, 64)])
+@pytest.mark.parametrize("lower_bound", [-5.0, None])
+def test_prefill_cut_sequences(K, V, lower_bound):
+    case = W.prefill_case(f"cut_k{K}_v{V}_lb{lower_bound}", 3, K, V, CUT, 16, lower_bound,
+                          seed=651 + K + V, std=0.1, scale=1.0 / math.sqrt(K))
+    check_case(case, PREFILL_TOL_O, PREFILL_TOL_S)
+
+
+def test_prefill_cut_sequences_with_flags_and_null_slot():
+    """Cut sequences without an initial state and on the null slot (zero
+    output, no state traffic), beside an uncut one, at index stride 3."""
+    lens = [1500, 2500, 2200, 70, 3000]
+    case = W.prefill_case("cut_flags", 4, 128, 128, lens, 12, -5.0, seed=661, std=0.2,
+                          has_initial=[1, 1, 0, 1, 0], index_stride=3)
+    case.block_table[1, 0] = -1
+    check_case(case, PREFILL_TOL_O, PREFILL_TOL_S)
+
+
+def test_prefill_cut_sequence_is_deterministic():
+    case = W.prefill_case("det_cut", 2, 128, 128, [4000, 40], 4, -5.0, seed=671)
+    results = []
+    for _ in range(3):
+        dc = to_device(case)
+        out = run_gpu(dc).cpu()
+        results.append((out, dc.pool.cpu()))
+    for out, pool in results[1:]:
+        assert torch.equal(out, results[0][0]) and torch.equal(pool, results[0][1])
+    log("[case] cut-sequence prefill determinism: 3 runs bit-identical")
+
+
 def test_prefill_is_deterministic():
     case = W.prefill_case("det", 8, 128, 128, [300, 77, 1], 8, -5.0, seed=621)
     results = []

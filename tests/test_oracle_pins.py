@@ -328,6 +328,30 @@ def test_linear_in_initial_state_and_values():
     np.testing.assert_allclose(S_full, S_s + S_v, rtol=0, atol=1e-13)
 
 
+def test_segment_maps_compose_to_the_whole_sequence():
+    """A run of tokens maps the state affinely: S_out = M S_in + B, with M the
+    end state reached from the identity with zero values and B the end state
+    reached from zero. Walking S_{j+1} = M_j S_j + B_j over consecutive
+    segments reproduces the uncut end state, and rerunning each segment from
+    its S_j reproduces the uncut outputs (the segment-parallel inter-chunk
+    pass relies on both)."""
+    T, K, V = 150, 8, 6
+    q, k, v, g, b, S0 = _rand_pregated(T, K, V, seed=17)
+    o_all, S_all = O.recurrent_pregated(q, k, v, g, b, S0)
+    S = S0.copy()
+    outs = []
+    for a, e in [(0, 64), (64, 128), (128, 150)]:
+        M = O.recurrent_pregated(q[a:e], k[a:e], np.zeros((e - a, K)), g[a:e], b[a:e], np.eye(K))[1]
+        B = O.recurrent_pregated(q[a:e], k[a:e], v[a:e], g[a:e], b[a:e], np.zeros((K, V)))[1]
+        o_seg, S_seg = O.recurrent_pregated(q[a:e], k[a:e], v[a:e], g[a:e], b[a:e], S)
+        np.testing.assert_allclose(S_seg, M @ S + B, rtol=0, atol=1e-13)
+        assert np.abs(M - np.eye(K)).max() > 1e-3   # the segment does change the state
+        outs.append(o_seg)
+        S = M @ S + B
+    np.testing.assert_allclose(S, S_all, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(np.concatenate(outs), o_all, rtol=0, atol=1e-13)
+
+
 # ------------------------------------------------------ equivariance (P-f)
 
 def test_value_columns_permute_and_heads_are_independent():
