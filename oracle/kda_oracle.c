@@ -420,3 +420,30 @@ int32_t kda_oracle_prefill(int32_t num_seqs, const int32_t* cu_seqlens,
   }
   return 0;
 }
+
+/* Gated RMSNorm output epilogue. [P3] Purpose lists "gated RMSNorm" as the
+ * step after the KDA recurrence inside one decode kernel, with no formula.
+ * Reading: per token row and head, over the head's V output channels,
+ *   y_j = o_j / sqrt(mean_j' o_j'^2 + eps) * w_j * act(z_j)
+ * with a per-channel weight w shared by the heads, a gate input z (bf16, laid
+ * out head-major like the output: channel j of head h at h*V + j) and
+ * act(z) = sigmoid(z) (activation 0) or z * sigmoid(z) (activation 1).
+ * o is updated in place. */
+void kda_oracle_gated_rmsnorm(int64_t rows, int32_t H, int32_t V, double* o,
+                              const uint16_t* z, int64_t z_row_stride,
+                              const float* w, double eps, int32_t activation) {
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int32_t h = 0; h < H; ++h) {
+      double* oh = o + ((size_t)r * H + h) * V;
+      const uint16_t* zh = z + (size_t)r * z_row_stride + (size_t)h * V;
+      double ss = 0.0;
+      for (int32_t j = 0; j < V; ++j) ss += oh[j] * oh[j];
+      const double inv = 1.0 / sqrt(ss / V + eps);
+      for (int32_t j = 0; j < V; ++j) {
+        const double zv = kda_oracle_bf16_to_double(zh[j]);
+        const double act = activation == 1 ? zv * sigmoid(zv) : sigmoid(zv);
+        oh[j] = oh[j] * inv * (double)w[j] * act;
+      }
+    }
+  }
+}

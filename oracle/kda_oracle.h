@@ -67,6 +67,13 @@ int32_t kda_oracle_prefill(int32_t num_seqs, const int32_t* cu_seqlens,
                            int32_t K, int32_t V, const kda_oracle_args_t* a,
                            int32_t form, double* out, double* final_state);
 
+/* Gated RMSNorm epilogue (reading R20), in place on fp64 outputs:
+ * o: [rows][H][V]; z: bf16 bits, row r at z + r*z_row_stride, head h at h*V;
+ * w: fp32 [V]; activation 0 = sigmoid(z), 1 = z*sigmoid(z). */
+void kda_oracle_gated_rmsnorm(int64_t rows, int32_t H, int32_t V, double* o,
+                              const uint16_t* z, int64_t z_row_stride,
+                              const float* w, double eps, int32_t activation);
+
 #ifdef __cplusplus
 }
 #endif

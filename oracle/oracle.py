@@ -86,6 +86,8 @@ def lib():
                                              vp, vp, vp]
         L.kda_oracle_spec_decode.restype = i32
         L.kda_oracle_prefill.restype = i32
+        L.kda_oracle_gated_rmsnorm.argtypes = [ctypes.c_int64, i32, i32, vp, vp, ctypes.c_int64, vp, d, i32]
+        L.kda_oracle_gated_rmsnorm.restype = None
         _lib = L
     return _lib
 
@@ -313,3 +315,29 @@ def mixed_batch(inp: dict, pool: torch.Tensor, state_indices: torch.Tensor,
                              np.asarray(has_initial_state, dtype=np.uint8)])
     return prefill(inp, pool, state_indices, cu, H, K, V, has_initial_state=hs,
                    lower_bound=lower_bound, scale=scale, form=form, return_pool=return_pool)
+
+
+# ---------------------------------------------------------- output epilogue
+
+ACTIVATIONS = {"sigmoid": 0, "silu": 1}
+
+
+def gated_rmsnorm(out: np.ndarray, gate: torch.Tensor, weight: torch.Tensor, eps: float,
+                  activation: str = "sigmoid") -> np.ndarray:
+    """Gated RMSNorm of KDA outputs (reading R20 of the design notes; the
+    pages name the step after the recurrence, vLLM PR #60683 Purpose, but
+    print no formula): per row and head, over the head's V channels,
+    y = o / sqrt(mean(o^2) + eps) * w * act(z), act = sigmoid or z*sigmoid(z).
+    out: fp64 [rows, H, V] (not modified); gate: bf16 [rows, >= H*V] (its
+    first H*V columns are the gate input); weight: fp32 [V]. Returns a new
+    fp64 array."""
+    y = np.ascontiguousarray(np.array(out, dtype=np.float64))
+    rows, H, V = y.shape
+    g = gate.detach().cpu()
+    assert g.dtype == torch.bfloat16 and g.dim() == 2 and g.shape[0] == rows and g.shape[1] >= H * V
+    bits = _bits(g[:, :H * V].contiguous()) if rows else np.zeros(1, dtype=np.uint16)
+    w = np.ascontiguousarray(weight.detach().cpu().float().numpy())
+    assert w.shape == (V,)
+    lib().kda_oracle_gated_rmsnorm(rows, H, V, _ptr(y), _ptr(bits), H * V, _ptr(w), float(eps),
+                                   ACTIVATIONS[activation])
+    return y

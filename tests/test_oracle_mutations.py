@@ -48,6 +48,14 @@ MUTANTS = {
                                    "const int64_t st = (int64_t)row[(int64_t)(T - 1 - t) * col_stride];"),
     "spec_only_final_state_written": ("      if (st >= 0) {\n        float* tile",
                                       "      if (st >= 0 && t == T - 1) {\n        float* tile"),
+    "norm_sum_not_mean": ("const double inv = 1.0 / sqrt(ss / V + eps);", "const double inv = 1.0 / sqrt(ss + eps);"),
+    "norm_eps_outside_root": ("const double inv = 1.0 / sqrt(ss / V + eps);",
+                              "const double inv = 1.0 / (sqrt(ss / V) + eps);"),
+    "norm_gate_of_head_0": ("const uint16_t* zh = z + (size_t)r * z_row_stride + (size_t)h * V;",
+                            "const uint16_t* zh = z + (size_t)r * z_row_stride;"),
+    "norm_silu_as_sigmoid": ("const double act = activation == 1 ? zv * sigmoid(zv) : sigmoid(zv);",
+                             "const double act = sigmoid(zv);"),
+    "norm_weight_dropped": ("oh[j] = oh[j] * inv * (double)w[j] * act;", "oh[j] = oh[j] * inv * act;"),
 }
 
 

@@ -481,3 +481,82 @@ def test_padded_slot_stride_is_honoured():
     out_b, fs_b, _ = O.decode_packed(case.inputs, dense, case.state_indices, 2, 4, 4, 1, -5.0)
     np.testing.assert_array_equal(out_a, out_b)
     np.testing.assert_array_equal(fs_a, fs_b)
+
+
+# ------------------------------------------------ gated RMSNorm epilogue (R20)
+
+def _bf16_rows(vals):
+    return torch.tensor(vals, dtype=torch.float32).to(torch.bfloat16)
+
+
+def _norm_inputs(rows=3, H=2, V=8, seed=71):
+    rng = np.random.default_rng(seed)
+    o = rng.standard_normal((rows, H, V))
+    z = _bf16_rows(rng.standard_normal((rows, H * V)).tolist())
+    w = torch.tensor(rng.uniform(0.5, 1.5, V), dtype=torch.float32)
+    return o, z, w
+
+
+def _rms(y):
+    return np.sqrt((y ** 2).mean(axis=-1))
+
+
+def test_gated_rmsnorm_unit_rms_and_direction():
+    """eps = 0, unit weights and an activation of 1 (sigmoid of a large gate):
+    every head's output has RMS 1 and points along o."""
+    o, _, _ = _norm_inputs()
+    z = _bf16_rows([[88.0] * 16] * 3)   # sigmoid(88) = 1 in fp64
+    y = O.gated_rmsnorm(o, z, torch.ones(8), 0.0, "sigmoid")
+    np.testing.assert_allclose(_rms(y), 1.0, rtol=1e-14)
+    ratio = y / o
+    np.testing.assert_allclose(ratio, ratio[..., :1] * np.ones_like(ratio), rtol=1e-13)
+    assert np.all(ratio > 0)
+
+
+def test_gated_rmsnorm_activation_special_values():
+    """sigmoid(0) = 1/2 halves the RMS; z sigmoid(z) is 0 at z = 0 and about
+    z for a large gate."""
+    o, _, _ = _norm_inputs()
+    zeros = _bf16_rows([[0.0] * 16] * 3)
+    big = _bf16_rows([[88.0] * 16] * 3)
+    w = torch.ones(8)
+    np.testing.assert_allclose(_rms(O.gated_rmsnorm(o, zeros, w, 0.0, "sigmoid")), 0.5, rtol=1e-14)
+    assert np.all(O.gated_rmsnorm(o, zeros, w, 0.0, "silu") == 0.0)
+    np.testing.assert_allclose(_rms(O.gated_rmsnorm(o, big, w, 0.0, "silu")), 88.0, rtol=1e-14)
+
+
+def test_gated_rmsnorm_scaling_identity_fixes_eps():
+    """Scaling o by lambda equals dividing eps by lambda^2:
+    y(lambda o; eps) = y(o; eps / lambda^2) (eps sits under the root, beside
+    the mean square); with eps = 0 the output is scale-invariant and odd."""
+    o, z, w = _norm_inputs(seed=73)
+    for lam in (0.01, 3.0, 250.0):
+        np.testing.assert_allclose(O.gated_rmsnorm(lam * o, z, w, 0.3),
+                                   O.gated_rmsnorm(o, z, w, 0.3 / lam ** 2), rtol=1e-12)
+        np.testing.assert_allclose(O.gated_rmsnorm(lam * o, z, w, 0.0), O.gated_rmsnorm(o, z, w, 0.0),
+                                   rtol=1e-12)
+    np.testing.assert_allclose(O.gated_rmsnorm(-o, z, w, 0.3), -O.gated_rmsnorm(o, z, w, 0.3), rtol=1e-15)
+    # eps > 0 shrinks the output of a small row well below unit RMS.
+    tiny = 1e-3 * o
+    assert np.all(_rms(O.gated_rmsnorm(tiny, _bf16_rows([[88.0] * 16] * 3), torch.ones(8), 1.0)) < 2e-3)
+
+
+def test_gated_rmsnorm_weight_is_per_channel_and_gate_per_head():
+    o, _, _ = _norm_inputs(seed=75)
+    H, V = 2, 8
+    onehot = torch.zeros(V)
+    onehot[5] = 2.0
+    big = _bf16_rows([[88.0] * 16] * 3)
+    y = O.gated_rmsnorm(o, big, onehot, 0.0)
+    assert np.count_nonzero(y[..., [0, 1, 2, 3, 4, 6, 7]]) == 0
+    assert np.all(y[..., 5] != 0)
+    # Head 0's gate 0 (sigmoid 1/2), head 1's gate large (sigmoid 1).
+    z = _bf16_rows([[0.0] * V + [88.0] * V] * 3)
+    y = O.gated_rmsnorm(o, z, torch.ones(V), 0.0)
+    np.testing.assert_allclose(_rms(y)[:, 0], 0.5, rtol=1e-14)
+    np.testing.assert_allclose(_rms(y)[:, 1], 1.0, rtol=1e-14)
+    # Heads are independent: changing head 1's outputs leaves head 0's alone.
+    o2 = o.copy()
+    o2[:, 1] *= -7.0
+    y2 = O.gated_rmsnorm(o2, z, torch.ones(V), 0.1)
+    np.testing.assert_array_equal(y2[:, 0], O.gated_rmsnorm(o, z, torch.ones(V), 0.1)[:, 0])
