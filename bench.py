@@ -43,7 +43,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=320)
     ap.add_argument("--warmup", type=int, default=32)
-    ap.add_argument("--legs", default="decode,spec,prefill,mixed")
+    ap.add_argument("--legs", default="decode,spec,prefill,mixed,norm")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -155,7 +155,7 @@ def measured_traffic():
     return d.get("hbm_bytes_per_launch")
 
 
-def leg_decode(steps, warmup):
+def leg_decode(steps, warmup, with_norm=False):
     import torch
 
     import gated_delta_rule_45_amd as kda
@@ -172,17 +172,21 @@ def leg_decode(steps, warmup):
         t[:, 0] = perm[s * N:(s + 1) * N]
         tables.append(t.to(dev))
     out = torch.empty(N, H, V, dtype=torch.bfloat16, device=dev)
+    norm = None
+    if with_norm:
+        nm = W.make_norm(N, H, V, 1022)
+        norm = kda.GatedRMSNorm(nm["gate"].to(dev), nm["weight"].to(dev), nm["eps"])
 
     def step(i):
         kda.kda_decode_packed(inp["mixed_qkv"], inp["raw_g"], inp["raw_beta"], inp["A_log"],
-                              inp["dt_bias"], -5.0, pool, tables[i % SETS][:, 0], out=out)
+                              inp["dt_bias"], -5.0, pool, tables[i % SETS][:, 0], out=out, norm=norm)
 
     eager_ms = eager_time(step, steps, warmup)
     ms, timed = graph_time(step, SETS, steps, warmup)
     state_bytes = 2 * N * H * K * V * 4
-    alg_bytes = state_bytes + token_io_bytes(N, H, K, V)
+    alg_bytes = state_bytes + token_io_bytes(N, H, K, V) + (N * H * V * 2 if with_norm else 0)
     return {
-        "workload": "batched_decode_h32_k128_n32_stride8_lb-5",
+        "workload": "batched_decode_h32_k128_n32_stride8_lb-5" + ("_gated_rmsnorm" if with_norm else ""),
         "ms_per_step": ms, "eager_ms_per_step": eager_ms, "steps_timed": timed,
         "state_gbs": state_bytes / (ms * 1e-3) / 1e9,
         "alg_bytes_per_launch": alg_bytes,
@@ -287,7 +291,7 @@ def prefill_io_bytes(T, H, K, V, seqs):
     return token_io_bytes(T, H, K, V) + 2 * seqs * H * K * V * 4
 
 
-def leg_prefill(steps, warmup, lens, name, seed):
+def leg_prefill(steps, warmup, lens, name, seed, with_norm=False):
     import torch
 
     import gated_delta_rule_45_amd as kda
@@ -304,11 +308,16 @@ def leg_prefill(steps, warmup, lens, name, seed):
     cu = W.cu_from_lengths(lens).to(dev)
     out = torch.empty(T, H, V, dtype=torch.bfloat16, device=dev)
     ws = torch.empty(kda.kda_chunk_prefill_workspace_size(n, T, H, K, V), dtype=torch.uint8, device=dev)
+    norm = None
+    if with_norm:
+        nm = W.make_norm(T, H, V, seed + 20)
+        norm = kda.GatedRMSNorm(nm["gate"].to(dev), nm["weight"].to(dev), nm["eps"])
 
     def step(i):
         inp = inps[i % copies]
         kda.kda_chunk_prefill(inp["mixed_qkv"], inp["raw_g"], inp["raw_beta"], inp["A_log"],
-                              inp["dt_bias"], -5.0, pool, idx[i % 2], cu, out=out, workspace=ws)
+                              inp["dt_bias"], -5.0, pool, idx[i % 2], cu, out=out, workspace=ws,
+                              norm=norm)
 
     ms, _ = graph_time(step, copies, steps, warmup)
     flops = prefill_flops(lens, H, K, V)
@@ -418,6 +427,15 @@ def main():
         extra["prefill_t65536"] = leg_prefill(max(pf_steps // 2, 4), 1, [65536], "prefill_t65536_h32_k128", 3004)
     if "mixed" in legs:
         extra["mixed_4096"] = leg_mixed(max(args.steps // 16, 9), 9)
+    if "norm" in legs:
+        # Gated RMSNorm output epilogue: inside the decode kernel (whole-row
+        # tiles), and as a pass after the prefill state pass.
+        d = leg_decode(args.steps, args.warmup, with_norm=True)
+        extra["decode_gated_rmsnorm"] = {k: (round(v, 5) if isinstance(v, float) else v)
+                                         for k, v in d.items() if k != "steps_timed"}
+        extra["prefill_t8192_gated_rmsnorm"] = leg_prefill(max(args.steps // 32, 6), 2, [8192],
+                                                           "prefill_t8192_h32_k128_gated_rmsnorm",
+                                                           3000, with_norm=True)
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -5,6 +5,7 @@ declared in ``include/kda.h`` (library ``libkda.so`` in this directory). This
 package only marshals torch tensors into that ABI.
 """
 from ._binding import (  # noqa: F401
+    GatedRMSNorm,
     KdaError,
     kda_chunk_prefill,
     kda_chunk_prefill_workspace_size,
@@ -16,6 +17,7 @@ from ._binding import (  # noqa: F401
 )
 
 __all__ = [
+    "GatedRMSNorm",
     "KdaError",
     "kda_chunk_prefill",
     "kda_chunk_prefill_workspace_size",

@@ -33,6 +33,24 @@ class KdaState(ctypes.Structure):
                 ("index_stride", ctypes.c_int64)]
 
 
+class KdaOutNorm(ctypes.Structure):
+    _fields_ = [("gate", ctypes.c_void_p), ("gate_row_stride", ctypes.c_int64),
+                ("weight", ctypes.c_void_p), ("eps", ctypes.c_float), ("activation", ctypes.c_int32)]
+
+
+NORM_ACTIVATIONS = {"sigmoid": 0, "silu": 1}
+
+
+class GatedRMSNorm:
+    """Optional output epilogue of every entry point: per row and head,
+    y = o / sqrt(mean(o^2) + eps) * weight * act(gate) over the head's V
+    channels, act = sigmoid or z*sigmoid(z). ``gate`` is bf16 [rows, >= H*V]
+    (unit-stride rows, head h at h*V), ``weight`` fp32 [V]."""
+
+    def __init__(self, gate, weight, eps: float = 1e-6, activation: str = "sigmoid"):
+        self.gate, self.weight, self.eps, self.activation = gate, weight, float(eps), activation
+
+
 class KdaError(ValueError):
     """A call was rejected. ``status`` is the C status code, ``reasons`` the
     list of every failed check."""
@@ -55,20 +73,21 @@ def lib() -> ctypes.CDLL:
                                "(run gated_delta_rule_45_amd.build.build())")
         L = ctypes.CDLL(LIB_PATH)
         i32, i64, vp, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
-        gp, spn = ctypes.POINTER(KdaGate), ctypes.POINTER(KdaState)
-        L.kda_decode_packed.argtypes = [i32, i32, i32, i32, i32, vp, i64, vp, vp, gp, spn, vp, vp]
+        gp, spn, npn = ctypes.POINTER(KdaGate), ctypes.POINTER(KdaState), ctypes.POINTER(KdaOutNorm)
+        L.kda_decode_packed.argtypes = [i32, i32, i32, i32, i32, vp, i64, vp, vp, gp, spn, npn, vp, vp]
         L.kda_decode_packed.restype = i32
-        L.kda_spec_decode.argtypes = [i32, i32, i32, i32, i32, vp, i64, vp, vp, gp, spn, i64, vp, vp, vp]
+        L.kda_spec_decode.argtypes = [i32, i32, i32, i32, i32, vp, i64, vp, vp, gp, spn, i64, vp, npn,
+                                      vp, vp]
         L.kda_spec_decode.restype = i32
         L.kda_chunk_prefill_workspace_size.argtypes = [i32, i64, i32, i32, i32]
         L.kda_chunk_prefill_workspace_size.restype = sz
         L.kda_chunk_prefill.argtypes = [i32, i64, vp, vp, i32, i32, i32, vp, i64, vp, vp, gp, spn,
-                                        vp, vp, sz, vp]
+                                        npn, vp, vp, sz, vp]
         L.kda_chunk_prefill.restype = i32
         L.kda_mixed_batch_workspace_size.argtypes = [i32, i32, i64, i32, i32, i32]
         L.kda_mixed_batch_workspace_size.restype = sz
         L.kda_mixed_batch.argtypes = [i32, i32, i64, vp, vp, i32, i32, i32, vp, i64, vp, vp, gp,
-                                      spn, vp, vp, sz, vp]
+                                      spn, npn, vp, vp, sz, vp]
         L.kda_mixed_batch.restype = i32
         L.kda_status_string.argtypes = [i32]
         L.kda_status_string.restype = ctypes.c_char_p
@@ -180,13 +199,41 @@ def _out(out, rows, H, V, device, m: _Marshal):
     return out
 
 
+def _norm(norm, rows, H, V, m: _Marshal):
+    """The optional epilogue as a C struct (None when absent)."""
+    if norm is None:
+        return None
+    if not isinstance(norm, GatedRMSNorm):
+        m.check(False, "norm must be a GatedRMSNorm or None")
+        m.raise_if_any()
+    m.tensor("norm.gate", norm.gate, torch.bfloat16, 2)
+    m.tensor("norm.weight", norm.weight, torch.float32, 1)
+    m.raise_if_any()
+    m.check(norm.activation in NORM_ACTIVATIONS,
+            f"norm.activation must be one of {sorted(NORM_ACTIVATIONS)}")
+    m.check(norm.gate.shape[0] == rows and norm.gate.shape[1] >= H * V and norm.gate.stride(1) == 1,
+            f"norm.gate must be [{rows}, >= {H * V}] with unit-stride rows")
+    m.check(norm.weight.shape[0] == V and norm.weight.is_contiguous(),
+            f"norm.weight must be a contiguous [{V}] tensor")
+    m.raise_if_any()
+    return KdaOutNorm(gate=norm.gate.data_ptr(), gate_row_stride=norm.gate.stride(0),
+                      weight=norm.weight.data_ptr(), eps=norm.eps,
+                      activation=NORM_ACTIVATIONS[norm.activation])
+
+
+def _byref(x):
+    return ctypes.byref(x) if x is not None else None
+
+
 # ----------------------------------------------------------------- entries
 
 def kda_decode_packed(mixed_qkv, raw_g, raw_beta, A_log, dt_bias, lower_bound, initial_state,
-                      state_indices, *, tokens_per_seq: int = 1, scale: float = 1.0, out=None):
+                      state_indices, *, tokens_per_seq: int = 1, scale: float = 1.0, out=None,
+                      norm: GatedRMSNorm | None = None):
     """Packed decode / spec-verify. ``initial_state`` (fp32 [slots, H, K, V])
     is updated in place; ``state_indices`` is a 1-D int32 view, possibly
-    strided, with one entry per request. Returns ``(out, initial_state)``."""
+    strided, with one entry per request; ``norm`` an optional output
+    epilogue. Returns ``(out, initial_state)``."""
     m = _Marshal()
     H, K, V = _common(m, mixed_qkv, raw_g, raw_beta, A_log, dt_bias, initial_state, state_indices)
     num_seqs = state_indices.shape[0]
@@ -195,10 +242,11 @@ def kda_decode_packed(mixed_qkv, raw_g, raw_beta, A_log, dt_bias, lower_bound, i
             f"mixed_qkv has {mixed_qkv.shape[0]} rows, expected num_seqs*tokens_per_seq = {rows}")
     m.raise_if_any()
     out = _out(out, rows, H, V, mixed_qkv.device, m)
+    nm = _norm(norm, rows, H, V, m)
     g, s = _gate(A_log, dt_bias, lower_bound, scale), _state(initial_state, state_indices)
     st = lib().kda_decode_packed(num_seqs, int(tokens_per_seq), H, K, V, _ptr(mixed_qkv),
                                  mixed_qkv.stride(0), _ptr(raw_g), _ptr(raw_beta),
-                                 ctypes.byref(g), ctypes.byref(s), _ptr(out),
+                                 ctypes.byref(g), ctypes.byref(s), _byref(nm), _ptr(out),
                                  _stream(mixed_qkv.device))
     _raise_if(st)
     return out, initial_state
@@ -206,7 +254,7 @@ def kda_decode_packed(mixed_qkv, raw_g, raw_beta, A_log, dt_bias, lower_bound, i
 
 def kda_spec_decode(mixed_qkv, raw_g, raw_beta, A_log, dt_bias, lower_bound, initial_state,
                     block_table, num_accepted_tokens, *, tokens_per_seq: int, scale: float = 1.0,
-                    out=None):
+                    out=None, norm: GatedRMSNorm | None = None):
     """Speculative decoding with a state per token. ``block_table`` is an
     int32 [num_seqs, >= tokens_per_seq] view (any strides): request n starts
     from the slot in column num_accepted_tokens[n] - 1 and the state after
@@ -231,11 +279,12 @@ def kda_spec_decode(mixed_qkv, raw_g, raw_beta, A_log, dt_bias, lower_bound, ini
             f"num_accepted_tokens must be a contiguous [{num_seqs}] tensor")
     m.raise_if_any()
     out = _out(out, rows, H, V, mixed_qkv.device, m)
+    nm = _norm(norm, rows, H, V, m)
     g, s = _gate(A_log, dt_bias, lower_bound, scale), _state(initial_state, col0)
     st = lib().kda_spec_decode(num_seqs, tps, H, K, V, _ptr(mixed_qkv), mixed_qkv.stride(0),
                                _ptr(raw_g), _ptr(raw_beta), ctypes.byref(g), ctypes.byref(s),
-                               block_table.stride(1), _ptr(num_accepted_tokens), _ptr(out),
-                               _stream(mixed_qkv.device))
+                               block_table.stride(1), _ptr(num_accepted_tokens), _byref(nm),
+                               _ptr(out), _stream(mixed_qkv.device))
     _raise_if(st)
     return out, initial_state
 
@@ -260,7 +309,7 @@ def _workspace(workspace, need, device, m: _Marshal):
 
 def kda_chunk_prefill(mixed_qkv, raw_g, raw_beta, A_log, dt_bias, lower_bound, initial_state,
                       state_indices, cu_seqlens, *, has_initial_state=None, scale: float = 1.0,
-                      out=None, workspace=None):
+                      out=None, workspace=None, norm: GatedRMSNorm | None = None):
     """Varlen chunked prefill (chunk 64). ``cu_seqlens`` is device int32
     [num_seqs+1]; the token count is taken from ``mixed_qkv.shape[0]`` (the
     host never reads ``cu_seqlens``). Without ``workspace`` a scratch tensor of
@@ -281,18 +330,19 @@ def kda_chunk_prefill(mixed_qkv, raw_g, raw_beta, A_log, dt_bias, lower_bound, i
     out = _out(out, num_tokens, H, V, mixed_qkv.device, m)
     need = kda_chunk_prefill_workspace_size(max(num_seqs, 0), num_tokens, H, K, V)
     ws = _workspace(workspace, need, mixed_qkv.device, m)
+    nm = _norm(norm, num_tokens, H, V, m)
     g, s = _gate(A_log, dt_bias, lower_bound, scale), _state(initial_state, state_indices)
     st = lib().kda_chunk_prefill(num_seqs, num_tokens, _ptr(cu_seqlens), _ptr(has_initial_state),
                                  H, K, V, _ptr(mixed_qkv), mixed_qkv.stride(0), _ptr(raw_g),
-                                 _ptr(raw_beta), ctypes.byref(g), ctypes.byref(s), _ptr(out),
-                                 _ptr(ws), ws.numel(), _stream(mixed_qkv.device))
+                                 _ptr(raw_beta), ctypes.byref(g), ctypes.byref(s), _byref(nm),
+                                 _ptr(out), _ptr(ws), ws.numel(), _stream(mixed_qkv.device))
     _raise_if(st)
     return out, initial_state
 
 
 def kda_mixed_batch(mixed_qkv, raw_g, raw_beta, A_log, dt_bias, lower_bound, initial_state,
                     state_indices, num_decodes: int, prefill_cu_seqlens, *, has_initial_state=None,
-                    scale: float = 1.0, out=None, workspace=None):
+                    scale: float = 1.0, out=None, workspace=None, norm: GatedRMSNorm | None = None):
     """Mixed batch: rows [0, num_decodes) are single-token decodes (recurrent
     kernel), the rest are prefill sequences given by ``prefill_cu_seqlens``
     (relative to ``num_decodes``; chunk pipeline). ``state_indices`` has the
@@ -314,11 +364,12 @@ def kda_mixed_batch(mixed_qkv, raw_g, raw_beta, A_log, dt_bias, lower_bound, ini
     need = kda_mixed_batch_workspace_size(int(num_decodes), max(num_prefills, 0),
                                           num_prefill_tokens, H, K, V)
     ws = _workspace(workspace, need, mixed_qkv.device, m)
+    nm = _norm(norm, rows, H, V, m)
     g, s = _gate(A_log, dt_bias, lower_bound, scale), _state(initial_state, state_indices)
     st = lib().kda_mixed_batch(int(num_decodes), num_prefills, num_prefill_tokens,
                                _ptr(prefill_cu_seqlens), _ptr(has_initial_state), H, K, V,
                                _ptr(mixed_qkv), mixed_qkv.stride(0), _ptr(raw_g), _ptr(raw_beta),
-                               ctypes.byref(g), ctypes.byref(s), _ptr(out), _ptr(ws), ws.numel(),
-                               _stream(mixed_qkv.device))
+                               ctypes.byref(g), ctypes.byref(s), _byref(nm), _ptr(out), _ptr(ws),
+                               ws.numel(), _stream(mixed_qkv.device))
     _raise_if(st)
     return out, initial_state

@@ -86,6 +86,37 @@ void check_common(Checks& c, int64_t rows, int32_t H, int32_t K, int32_t V,
   }
 }
 
+// The optional output epilogue: rows gate rows pair with the call's output rows.
+void check_norm(Checks& c, int64_t rows, int32_t H, int32_t V, const kda_out_norm_t* norm) {
+  if (norm == nullptr) return;
+  const auto INV = KDA_ERR_INVALID_ARGUMENT;
+  const auto UNS = KDA_ERR_UNSUPPORTED;
+  c.require(norm->activation == KDA_NORM_SIGMOID || norm->activation == KDA_NORM_SILU, INV,
+            "norm->activation must be KDA_NORM_SIGMOID or KDA_NORM_SILU");
+  c.require(std::isfinite(norm->eps) && norm->eps > 0.0f, INV, "norm->eps must be finite and > 0");
+  if (rows > 0) {
+    c.require(norm->gate != nullptr, INV, "norm->gate must not be NULL");
+    c.require(norm->weight != nullptr, INV, "norm->weight must not be NULL");
+    if (H >= 1 && V >= 1)
+      c.require(norm->gate_row_stride >= static_cast<int64_t>(H) * V, INV,
+                "norm->gate_row_stride must be >= H*V");
+    c.require(norm->gate_row_stride % 8 == 0, UNS, "norm->gate_row_stride must be a multiple of 8");
+    c.require(aligned(norm->gate, 16), UNS, "norm->gate must be 16-byte aligned");
+    c.require(aligned(norm->weight, 16), UNS, "norm->weight must be 16-byte aligned");
+  }
+}
+
+kda::OutNorm out_norm(const kda_out_norm_t* norm, int64_t first_row) {
+  kda::OutNorm n{};
+  if (norm == nullptr) return n;
+  n.gate = static_cast<const uint16_t*>(norm->gate) + first_row * norm->gate_row_stride;
+  n.gate_row_stride = norm->gate_row_stride;
+  n.weight = norm->weight;
+  n.eps = norm->eps;
+  n.activation = norm->activation;
+  return n;
+}
+
 kda::DecodeParams decode_params(int32_t num_seqs, int32_t tps, int32_t H, int32_t V,
                                 const void* mixed_qkv, int64_t qkv_row_stride, const void* raw_g,
                                 const void* raw_beta, const kda_gate_t* gate,
@@ -179,7 +210,8 @@ extern "C" {
 kda_status_t kda_decode_packed(int32_t num_seqs, int32_t tokens_per_seq, int32_t H, int32_t K,
                                int32_t V, const void* mixed_qkv, int64_t qkv_row_stride,
                                const void* raw_g, const void* raw_beta, const kda_gate_t* gate,
-                               const kda_state_t* state, void* out, hipStream_t stream) {
+                               const kda_state_t* state, const kda_out_norm_t* norm, void* out,
+                               hipStream_t stream) {
   Checks c;
   const auto INV = KDA_ERR_INVALID_ARGUMENT;
   c.require(num_seqs >= 0, INV, "num_seqs must be >= 0");
@@ -188,10 +220,12 @@ kda_status_t kda_decode_packed(int32_t num_seqs, int32_t tokens_per_seq, int32_t
   const int64_t rows = static_cast<int64_t>(num_seqs) * tokens_per_seq;
   c.require(rows <= 0x7fffffffLL, INV, "num_seqs * tokens_per_seq must fit in int32");
   check_common(c, rows, H, K, V, mixed_qkv, qkv_row_stride, raw_g, raw_beta, gate, state, out);
+  check_norm(c, rows, H, V, norm);
   if (!c.ok()) return c.finish();
   if (num_seqs == 0) return c.finish();
   kda::DecodeParams p = decode_params(num_seqs, tokens_per_seq, H, V, mixed_qkv, qkv_row_stride,
                                       raw_g, raw_beta, gate, state, out);
+  p.norm = out_norm(norm, 0);
   return hip_status(kda::launch_decode(p, K, stream), "decode launch");
 }
 
@@ -199,7 +233,8 @@ kda_status_t kda_spec_decode(int32_t num_seqs, int32_t tokens_per_seq, int32_t H
                              int32_t V, const void* mixed_qkv, int64_t qkv_row_stride,
                              const void* raw_g, const void* raw_beta, const kda_gate_t* gate,
                              const kda_state_t* state, int64_t index_col_stride,
-                             const int32_t* num_accepted_tokens, void* out, hipStream_t stream) {
+                             const int32_t* num_accepted_tokens, const kda_out_norm_t* norm,
+                             void* out, hipStream_t stream) {
   Checks c;
   const auto INV = KDA_ERR_INVALID_ARGUMENT;
   c.require(num_seqs >= 0, INV, "num_seqs must be >= 0");
@@ -210,10 +245,12 @@ kda_status_t kda_spec_decode(int32_t num_seqs, int32_t tokens_per_seq, int32_t H
   c.require(index_col_stride >= 1, INV, "index_col_stride must be >= 1");
   c.require(num_accepted_tokens != nullptr, INV, "num_accepted_tokens must not be NULL");
   check_common(c, rows, H, K, V, mixed_qkv, qkv_row_stride, raw_g, raw_beta, gate, state, out);
+  check_norm(c, rows, H, V, norm);
   if (!c.ok()) return c.finish();
   if (num_seqs == 0) return c.finish();
   kda::DecodeParams p = decode_params(num_seqs, tokens_per_seq, H, V, mixed_qkv, qkv_row_stride,
                                       raw_g, raw_beta, gate, state, out);
+  p.norm = out_norm(norm, 0);
   p.num_accepted = num_accepted_tokens;
   p.index_col_stride = index_col_stride;
   return hip_status(kda::launch_decode(p, K, stream), "spec decode launch");
@@ -230,16 +267,18 @@ kda_status_t kda_chunk_prefill(int32_t num_seqs, int64_t num_tokens, const int32
                                const uint8_t* has_initial_state, int32_t H, int32_t K, int32_t V,
                                const void* mixed_qkv, int64_t qkv_row_stride, const void* raw_g,
                                const void* raw_beta, const kda_gate_t* gate,
-                               const kda_state_t* state, void* out, void* workspace,
-                               size_t workspace_bytes, hipStream_t stream) {
+                               const kda_state_t* state, const kda_out_norm_t* norm, void* out,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
   Checks c;
   check_common(c, num_tokens, H, K, V, mixed_qkv, qkv_row_stride, raw_g, raw_beta, gate, state, out);
   check_prefill_specific(c, num_seqs, num_tokens, cu_seqlens, H, K, V, workspace, workspace_bytes);
+  check_norm(c, num_tokens, H, V, norm);
   if (!c.ok()) return c.finish();
   if (num_seqs == 0 || num_tokens == 0) return c.finish();
   kda::PrefillParams p =
       prefill_params(num_seqs, num_tokens, cu_seqlens, has_initial_state, H, K, V, mixed_qkv,
                      qkv_row_stride, raw_g, raw_beta, gate, state, out, workspace, workspace_bytes);
+  p.norm = out_norm(norm, 0);
   return hip_status(kda::launch_prefill(p, stream), "prefill launch");
 }
 
@@ -254,8 +293,9 @@ kda_status_t kda_mixed_batch(int32_t num_decodes, int32_t num_prefills, int64_t 
                              const int32_t* prefill_cu_seqlens, const uint8_t* has_initial_state,
                              int32_t H, int32_t K, int32_t V, const void* mixed_qkv,
                              int64_t qkv_row_stride, const void* raw_g, const void* raw_beta,
-                             const kda_gate_t* gate, const kda_state_t* state, void* out,
-                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                             const kda_gate_t* gate, const kda_state_t* state,
+                             const kda_out_norm_t* norm, void* out, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
   Checks c;
   const auto INV = KDA_ERR_INVALID_ARGUMENT;
   c.require(num_decodes >= 0, INV, "num_decodes must be >= 0");
@@ -264,12 +304,14 @@ kda_status_t kda_mixed_batch(int32_t num_decodes, int32_t num_prefills, int64_t 
   check_common(c, rows, H, K, V, mixed_qkv, qkv_row_stride, raw_g, raw_beta, gate, state, out);
   check_prefill_specific(c, num_prefills, num_prefill_tokens, prefill_cu_seqlens, H, K, V,
                          workspace, workspace_bytes);
+  check_norm(c, rows, H, V, norm);
   if (!c.ok()) return c.finish();
 
   // Decode rows [0, D): recurrent kernel, one token per request.
   if (num_decodes > 0) {
     kda::DecodeParams p = decode_params(num_decodes, 1, H, V, mixed_qkv, qkv_row_stride, raw_g,
                                         raw_beta, gate, state, out);
+    p.norm = out_norm(norm, 0);
     hipError_t e = kda::launch_decode(p, K, stream);
     if (e != hipSuccess) return hip_status(e, "mixed batch: decode launch");
   }
@@ -286,6 +328,7 @@ kda_status_t kda_mixed_batch(int32_t num_decodes, int32_t num_prefills, int64_t 
     kda::PrefillParams p =
         prefill_params(num_prefills, num_prefill_tokens, prefill_cu_seqlens, has_initial_state, H,
                        K, V, qkv, qkv_row_stride, rg, rb, gate, &st, o, workspace, workspace_bytes);
+    p.norm = out_norm(norm, D);
     hipError_t e = kda::launch_prefill(p, stream);
     if (e != hipSuccess) return hip_status(e, "mixed batch: prefill launch");
   }

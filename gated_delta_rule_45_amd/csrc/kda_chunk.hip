@@ -1713,10 +1713,16 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   uint8_t* flags = reinterpret_cast<uint8_t*>(ws + L.flags);
   char* recs = ws + L.recs;
   plan_kernel<<<1, kThreads, 0, stream>>>(p.cu_seqlens, p.num_seqs, pl);
-  if (p.K == 64 && p.V == 64) return launch_kv<64, 64>(p, L, pl, flags, recs, stream);
-  if (p.K == 64 && p.V == 128) return launch_kv<64, 128>(p, L, pl, flags, recs, stream);
-  if (p.K == 128 && p.V == 64) return launch_kv<128, 64>(p, L, pl, flags, recs, stream);
-  return launch_kv<128, 128>(p, L, pl, flags, recs, stream);
+  hipError_t e;
+  if (p.K == 64 && p.V == 64) e = launch_kv<64, 64>(p, L, pl, flags, recs, stream);
+  else if (p.K == 64 && p.V == 128) e = launch_kv<64, 128>(p, L, pl, flags, recs, stream);
+  else if (p.K == 128 && p.V == 64) e = launch_kv<128, 64>(p, L, pl, flags, recs, stream);
+  else e = launch_kv<128, 128>(p, L, pl, flags, recs, stream);
+  // Output epilogue: a head's columns are spread over the state pass's waves
+  // (and, at V = 128, over two workgroups), so the norm is a pass over the
+  // output.
+  if (e != hipSuccess || p.norm.gate == nullptr) return e;
+  return launch_gated_rmsnorm(p.norm, p.out, p.num_tokens, p.H, p.V, stream);
 }
 
 }  // namespace kda

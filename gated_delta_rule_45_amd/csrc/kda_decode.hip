@@ -57,6 +57,10 @@ void decode_kernel(const DecodeParams p) {
   __shared__ float s_v[kMaxTokens][VT];
   __shared__ float s_b[kMaxTokens];
   __shared__ float s_red[2][kWaves][2 * VT + 4];
+  // Gated RMSNorm epilogue operands (only a whole-row tile can apply it).
+  constexpr bool kRow = VT == V;
+  __shared__ float s_z[kRow ? kMaxTokens : 1][kRow ? VT : 1];
+  __shared__ float s_w[kRow ? VT : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -120,6 +124,15 @@ void decode_kernel(const DecodeParams p) {
       s_v[t][j] = bf16_to_f32(p.qkv[(row0 + t) * p.qkv_row_stride + 2 * H * K + h * V + tile * VT + j]);
     }
     if (tid < tps) s_b[tid] = sigmoid_f32(bf16_to_f32(p.raw_beta[(row0 + tid) * H + h]));
+    if constexpr (kRow) {
+      if (p.norm.gate != nullptr) {
+        for (int e = tid; e < tps * VT; e += blockDim.x) {
+          const int t = e / VT, j = e % VT;
+          s_z[t][j] = bf16_to_f32(p.norm.gate[(row0 + t) * p.norm.gate_row_stride + h * V + j]);
+        }
+        if (tid < VT) s_w[tid] = p.norm.weight[tid];
+      }
+    }
   }
   __syncthreads();
 
@@ -186,12 +199,32 @@ void decode_kernel(const DecodeParams p) {
         for (int r = 0; r < RPL; ++r) buffer_store_f32x4<kStreamPolicy>(S[r], tr, voff, r * V * 4);
       }
     }
-    if (w == 0 && rg == 0) {
+    if (w == 0) {
       const float s = p.scale;
-      uint16_t* o = p.out + ((row0 + t) * H + h) * static_cast<int64_t>(V) + col;
-      *reinterpret_cast<uint2*>(o) =
-          make_uint2(pack_bf16x2(s * fmaf(u[0], kq, qS[0]), s * fmaf(u[1], kq, qS[1])),
-                     pack_bf16x2(s * fmaf(u[2], kq, qS[2]), s * fmaf(u[3], kq, qS[3])));
+      f32x4 ov;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) ov[c] = s * fmaf(u[c], kq, qS[c]);
+      if constexpr (kRow) {
+        // Gated RMSNorm over the head's V outputs: every row group of wave 0
+        // holds the whole row (4 columns per lane), so a butterfly over the
+        // CG lanes of a group gives the sum of squares.
+        if (p.norm.gate != nullptr) {
+          float ss = ov[0] * ov[0] + ov[1] * ov[1] + ov[2] * ov[2] + ov[3] * ov[3];
+#pragma unroll
+          for (int off = 1; off < CG; off <<= 1) ss += __shfl_xor(ss, off);
+          const float inv = 1.0f / sqrtf(ss * (1.0f / V) + p.norm.eps);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const float zv = s_z[t][cg * 4 + c];
+            const float sg = sigmoid_f32(zv);
+            ov[c] *= inv * s_w[cg * 4 + c] * (p.norm.activation == 1 ? zv * sg : sg);
+          }
+        }
+      }
+      if (rg == 0) {
+        uint16_t* o = p.out + ((row0 + t) * H + h) * static_cast<int64_t>(V) + col;
+        *reinterpret_cast<uint2*>(o) = make_uint2(pack_bf16x2(ov[0], ov[1]), pack_bf16x2(ov[2], ov[3]));
+      }
     }
   }
 
@@ -229,12 +262,19 @@ hipError_t launch_decode(DecodeParams p, int K, hipStream_t stream) {
   if (pairs < 128) vt = 16;
   if (vt > p.V) vt = p.V;
   p.num_tiles = pairs * (p.V / vt);
-  if (K == 64) {
-    if (p.V == 64) return launch_kv<64, 64>(p, vt, stream);
-    return launch_kv<64, 128>(p, vt, stream);
-  }
-  if (p.V == 64) return launch_kv<128, 64>(p, vt, stream);
-  return launch_kv<128, 128>(p, vt, stream);
+  // The output epilogue runs inside the kernel when a workgroup holds whole
+  // rows; otherwise as a pass over the output after it.
+  const OutNorm norm = p.norm;
+  const bool separate = norm.gate != nullptr && vt != p.V;
+  if (separate) p.norm.gate = nullptr;
+  hipError_t e;
+  if (K == 64)
+    e = p.V == 64 ? launch_kv<64, 64>(p, vt, stream) : launch_kv<64, 128>(p, vt, stream);
+  else
+    e = p.V == 64 ? launch_kv<128, 64>(p, vt, stream) : launch_kv<128, 128>(p, vt, stream);
+  if (e != hipSuccess || !separate) return e;
+  return launch_gated_rmsnorm(norm, p.out, static_cast<int64_t>(p.num_seqs) * p.tokens_per_seq, p.H,
+                              p.V, stream);
 }
 
 }  // namespace kda

@@ -8,6 +8,20 @@
 
 namespace kda {
 
+// Gated RMSNorm output epilogue (gate == nullptr: none):
+// y = o / sqrt(mean(o^2) + eps) * weight * act(gate) per row and head.
+struct OutNorm {
+  const uint16_t* gate;     // bf16 [rows][gate_row_stride], head h at h*V
+  int64_t gate_row_stride;  // elements
+  const float* weight;      // [V]
+  float eps;
+  int32_t activation;       // 0: sigmoid(z), 1: z * sigmoid(z)
+};
+
+// Applies the epilogue in place to bf16 out [rows][H][V].
+hipError_t launch_gated_rmsnorm(const OutNorm& n, uint16_t* out, int64_t rows, int32_t H,
+                                int32_t V, hipStream_t stream);
+
 // One packed-decode / spec-verify launch.
 struct DecodeParams {
   const uint16_t* qkv;      // bf16 [rows][qkv_row_stride]
@@ -30,6 +44,7 @@ struct DecodeParams {
   const int32_t* num_accepted;
   int64_t index_col_stride;
   uint16_t* out;            // bf16 [rows][H][V]
+  OutNorm norm;             // fused into the kernel when a workgroup holds whole rows
   int32_t num_seqs;
   int32_t tokens_per_seq;
   int32_t H;
@@ -56,6 +71,7 @@ struct PrefillParams {
   const int32_t* indices;
   int64_t index_stride;
   uint16_t* out;
+  OutNorm norm;             // applied to out after the state pass
   const int32_t* cu_seqlens;
   const uint8_t* has_initial_state;  // may be null
   int32_t num_seqs;

@@ -80,6 +80,27 @@ typedef struct {
                               of a block table is accepted without a copy)      */
 } kda_state_t;
 
+/* Gated RMSNorm output epilogue (vLLM PR #60683, Purpose: in the decode
+ * kernels a gated RMSNorm follows the KDA recurrence; the page prints no
+ * formula, so this is a reading). With norm != NULL a call writes, per output
+ * row and head, over the head's V channels,
+ *     y_j = o_j / sqrt(mean_j' o_j'^2 + eps) * weight[j] * act(gate_j)
+ * instead of o, where act(z) = sigmoid(z) (KDA_NORM_SIGMOID) or
+ * z * sigmoid(z) (KDA_NORM_SILU). Null-slot rows stay zero. The norm is taken
+ * over o in fp32 inside the decode kernel when one workgroup holds a head's
+ * whole row of V channels; otherwise (narrow decode column tiles, prefill)
+ * one more pass applies it to the call's bf16 output in place. */
+enum { KDA_NORM_SIGMOID = 0, KDA_NORM_SILU = 1 };
+typedef struct {
+  const void* gate;        /* device bf16 [rows][gate_row_stride]; gate input of
+                              head h, channel j at h*V + j; row r pairs with
+                              output row r of the call                        */
+  int64_t gate_row_stride; /* elements, >= H*V, a multiple of 8               */
+  const float* weight;     /* device fp32 [V], shared by the heads            */
+  float eps;               /* > 0, finite                                     */
+  int32_t activation;      /* KDA_NORM_SIGMOID or KDA_NORM_SILU               */
+} kda_out_norm_t;
+
 /*
  * Packed decode and spec-verify (vLLM PR #51682 report, Key source excerpts:
  * fused_recurrent_kda_packed_decode; vLLM PR #60683, Refusal and steps).
@@ -94,6 +115,8 @@ typedef struct {
  *              qkv_row_stride >= 2*H*K + H*V.
  *   raw_g      bf16 [rows][H*K], contiguous.
  *   raw_beta   bf16 [rows][H], contiguous.
+ *   norm       optional output epilogue (NULL: none); gate and weight
+ *              16-byte aligned.
  *   out        bf16 [rows][H][V], contiguous.
  * Errors: KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED, KDA_ERR_HIP.
  */
@@ -102,7 +125,8 @@ kda_status_t kda_decode_packed(int32_t num_seqs, int32_t tokens_per_seq,
                                const void* mixed_qkv, int64_t qkv_row_stride,
                                const void* raw_g, const void* raw_beta,
                                const kda_gate_t* gate, const kda_state_t* state,
-                               void* out, hipStream_t stream);
+                               const kda_out_norm_t* norm, void* out,
+                               hipStream_t stream);
 
 /*
  * Speculative decoding with a state per token (vLLM PR #51682 report,
@@ -131,7 +155,8 @@ kda_status_t kda_spec_decode(int32_t num_seqs, int32_t tokens_per_seq,
                              const kda_gate_t* gate, const kda_state_t* state,
                              int64_t index_col_stride,
                              const int32_t* num_accepted_tokens,
-                             void* out, hipStream_t stream);
+                             const kda_out_norm_t* norm, void* out,
+                             hipStream_t stream);
 
 /* Bytes of device workspace kda_chunk_prefill needs for these sizes (a pure
  * host computation; returns 0 for invalid sizes). */
@@ -149,7 +174,7 @@ size_t kda_chunk_prefill_workspace_size(int32_t num_seqs, int64_t num_tokens,
  * which case it starts from zero. The final state is written to the slot. A
  * zero-length sequence or a null slot touches no state (null: zero output).
  * Chunks never cross sequences; the last chunk of a sequence may be partial.
- * Row formats as for kda_decode_packed; out is bf16 [num_tokens][H][V].
+ * Row formats and norm as for kda_decode_packed; out is bf16 [num_tokens][H][V].
  * workspace: device scratch of at least kda_chunk_prefill_workspace_size()
  * bytes, 256-byte aligned, owned by the caller; its contents are not needed
  * before or after the call.
@@ -163,7 +188,8 @@ kda_status_t kda_chunk_prefill(int32_t num_seqs, int64_t num_tokens,
                                const void* mixed_qkv, int64_t qkv_row_stride,
                                const void* raw_g, const void* raw_beta,
                                const kda_gate_t* gate, const kda_state_t* state,
-                               void* out, void* workspace, size_t workspace_bytes,
+                               const kda_out_norm_t* norm, void* out,
+                               void* workspace, size_t workspace_bytes,
                                hipStream_t stream);
 
 /* Bytes of device workspace kda_mixed_batch needs. */
@@ -183,7 +209,8 @@ size_t kda_mixed_batch_workspace_size(int32_t num_decodes, int32_t num_prefills,
  * indices[(num_decodes+i)*index_stride] and has_initial_state[i] (NULL = all
  * 1). Decode rows go to the recurrent decode kernel, prefill rows to the chunk
  * pipeline, all on `stream` with no host synchronisation. out is bf16
- * [num_decodes+num_prefill_tokens][H][V].
+ * [num_decodes+num_prefill_tokens][H][V]; norm (optional) as for
+ * kda_decode_packed, its gate rows paired with the output rows.
  * Errors: as kda_chunk_prefill.
  */
 kda_status_t kda_mixed_batch(int32_t num_decodes, int32_t num_prefills,
@@ -194,7 +221,8 @@ kda_status_t kda_mixed_batch(int32_t num_decodes, int32_t num_prefills,
                              const void* mixed_qkv, int64_t qkv_row_stride,
                              const void* raw_g, const void* raw_beta,
                              const kda_gate_t* gate, const kda_state_t* state,
-                             void* out, void* workspace, size_t workspace_bytes,
+                             const kda_out_norm_t* norm, void* out,
+                             void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
 
 /* Static name of a status code. */

@@ -56,12 +56,12 @@ def _state(**kw):
 
 
 def _decode(num_seqs=4, tps=1, H=32, K=128, V=128, qkv=FAKE, stride=3 * 32 * 128, g=None, s=None,
-            out=FAKE):
+            out=FAKE, norm=None):
     L = kda.lib()
     g = g or _gate()
     s = s or _state()
     st = L.kda_decode_packed(num_seqs, tps, H, K, V, qkv, stride, FAKE, FAKE, ctypes.byref(g),
-                             ctypes.byref(s), out, None)
+                             ctypes.byref(s), ctypes.byref(norm) if norm is not None else None, out, None)
     return st, L.kda_last_error().decode()
 
 
@@ -77,12 +77,24 @@ def test_spec_decode_rejects_and_lists_every_reason():
     L = kda.lib()
     g, s = _gate(), _state()
     st = L.kda_spec_decode(4, 9, 32, 128, 128, FAKE, 3 * 32 * 128, FAKE, FAKE, ctypes.byref(g),
-                           ctypes.byref(s), 0, None, FAKE, None)
+                           ctypes.byref(s), 0, None, None, FAKE, None)
     msg = L.kda_last_error().decode()
     assert st == 1
     for frag in ("tokens_per_seq must be in 1..8", "index_col_stride must be >= 1",
                  "num_accepted_tokens must not be NULL"):
         assert frag in msg, msg
+
+
+def test_output_norm_rejects_and_lists_every_reason():
+    bad = B.KdaOutNorm(gate=None, gate_row_stride=100, weight=FAKE + 4, eps=0.0, activation=7)
+    st, msg = _decode(norm=bad)
+    assert st == 1
+    for frag in ("norm->activation", "norm->eps must be finite and > 0", "norm->gate must not be NULL",
+                 "norm->gate_row_stride must be >= H*V", "norm->weight must be 16-byte aligned"):
+        assert frag in msg, msg
+    ok = B.KdaOutNorm(gate=FAKE, gate_row_stride=32 * 128 + 8, weight=FAKE, eps=1e-6, activation=1)
+    st, msg = _decode(norm=ok, out=None)
+    assert st == 1 and "norm" not in msg and "out must not be NULL" in msg
 
 
 def test_negative_index_stride_rejected():
@@ -136,13 +148,13 @@ def test_prefill_rejects_missing_workspace_and_cu_seqlens():
     L = kda.lib()
     g, s = _gate(), _state(index_stride=1)
     st = L.kda_chunk_prefill(2, 100, None, None, 32, 128, 128, FAKE, 3 * 32 * 128, FAKE, FAKE,
-                             ctypes.byref(g), ctypes.byref(s), FAKE, None, 0, None)
+                             ctypes.byref(g), ctypes.byref(s), None, FAKE, None, 0, None)
     msg = L.kda_last_error().decode()
     assert st == 1
     assert "cu_seqlens must not be NULL" in msg and "workspace" in msg
     need = L.kda_chunk_prefill_workspace_size(2, 100, 32, 128, 128)
     st = L.kda_chunk_prefill(2, 100, FAKE, None, 32, 128, 128, FAKE, 3 * 32 * 128, FAKE, FAKE,
-                             ctypes.byref(g), ctypes.byref(s), FAKE, FAKE, need - 1, None)
+                             ctypes.byref(g), ctypes.byref(s), None, FAKE, FAKE, need - 1, None)
     assert st == 3 and "workspace" in L.kda_last_error().decode()
 
 
@@ -150,7 +162,7 @@ def test_mixed_rejects_negative_decodes():
     L = kda.lib()
     g, s = _gate(), _state()
     st = L.kda_mixed_batch(-1, 0, 0, None, None, 32, 128, 128, FAKE, 3 * 32 * 128, FAKE, FAKE,
-                           ctypes.byref(g), ctypes.byref(s), FAKE, None, 0, None)
+                           ctypes.byref(g), ctypes.byref(s), None, FAKE, None, 0, None)
     assert st == 1 and "num_decodes" in L.kda_last_error().decode()
 
 

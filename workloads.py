@@ -15,6 +15,8 @@ distributions are this project's choice, since the pages give none):
   pool       fp32 [slots, H, K, V] = std * randn (optionally padded slots).
   state_indices: column 0 of an int32 block table [seqs, width] of unique
              random slots; the other columns hold other slots (never read).
+  output-norm epilogue: gate bf16 [rows, H*V (+ pad)] randn, weight fp32 [V]
+             = 1 + 0.1 * randn, eps 1e-6.
 """
 from __future__ import annotations
 
@@ -99,6 +101,16 @@ def split_total(total: int, parts: int, seed: int) -> list[int]:
     return [bounds[i + 1] - bounds[i] for i in range(parts)]
 
 
+def make_norm(rows: int, H: int, V: int, seed: int, activation: str = "sigmoid",
+              row_pad: int = 0, eps: float = 1e-6) -> dict:
+    """Gate input and weight of the output epilogue. With ``row_pad`` the gate
+    rows sit inside a wider buffer (row stride H*V + row_pad)."""
+    g = _gen(seed)
+    wide = torch.randn(rows, H * V + row_pad, generator=g).to(torch.bfloat16)
+    weight = 1.0 + 0.1 * torch.randn(V, generator=g)
+    return {"gate": wide[:, :H * V], "weight": weight, "eps": eps, "activation": activation}
+
+
 def cu_from_lengths(lens) -> torch.Tensor:
     cu = [0]
     for n in lens:
@@ -124,6 +136,7 @@ class Case:
     lower_bound: float | None = -5.0
     scale: float = 1.0
     num_accepted: torch.Tensor | None = None  # spec decode with a state per token
+    norm: dict | None = None  # output epilogue: gate, weight, eps, activation
 
     @property
     def state_indices(self) -> torch.Tensor:
