@@ -447,3 +447,69 @@ void kda_oracle_gated_rmsnorm(int64_t rows, int32_t H, int32_t V, double* o,
     }
   }
 }
+
+/* Short causal conv prologue. [P3] Purpose lists a "spec conv" step before
+ * the KDA recurrence, with no formula. Reading: a depthwise causal
+ * convolution of width W along each sequence, per channel of the [q | k | v]
+ * pre-activations (D = 2*H*K + H*V channels, head-major as in mixed_qkv):
+ *   a[t][c] = bias[c] + sum_{i<W} w[c][i] * x[t - (W-1) + i][c]
+ * where inputs before the sequence's first row come from its conv state
+ * (the W-1 previous inputs, oldest first; zero without an initial state or
+ * on a null slot), then y = silu(a) = a * sigmoid(a), then q and k of each
+ * head are divided by sqrt(sum of squares over the head + l2_eps). The new
+ * conv state is the last W-1 inputs of the sequence (older ones from the old
+ * state when the sequence is shorter than W-1); it is written back unless
+ * the slot is null or the sequence is empty.
+ *   x: bf16 bits [rows][D]; w: fp32 [D][W]; bias: fp32 [D] or NULL;
+ *   state: fp64 [slots][W-1][D] (in/out, indexed like the KDA pool);
+ *   y: fp64 [rows][D]. */
+void kda_oracle_short_conv(int32_t num_seqs, const int32_t* cu_seqlens,
+                           const uint8_t* has_initial_state, int32_t H,
+                           int32_t K, int32_t V, int32_t W, const uint16_t* x,
+                           const float* w, const float* bias, double l2_eps,
+                           double* state, const int32_t* indices,
+                           int64_t index_stride, double* y) {
+  const int32_t D = 2 * H * K + H * V;
+  const int32_t P = W - 1;
+  double* hist = (double*)malloc(sizeof(double) * (size_t)(P + 1));
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int32_t bos = cu_seqlens[s], len = cu_seqlens[s + 1] - cu_seqlens[s];
+    const int64_t slot = (int64_t)indices[(int64_t)s * index_stride];
+    const int init = slot >= 0 && (has_initial_state == NULL || has_initial_state[s] != 0);
+    double* st = slot >= 0 ? state + (size_t)slot * P * D : NULL;
+    for (int32_t c = 0; c < D; ++c) {
+      /* hist[j] = input at relative position j - P, j < P */
+      for (int32_t j = 0; j < P; ++j) hist[j] = init ? st[(size_t)j * D + c] : 0.0;
+      for (int32_t t = 0; t < len; ++t) {
+        double a = bias ? (double)bias[c] : 0.0;
+        for (int32_t i = 0; i < W; ++i) {
+          const int32_t pos = t - P + i;
+          const double xv = pos >= 0 ? kda_oracle_bf16_to_double(x[(size_t)(bos + pos) * D + c])
+                                     : hist[P + pos];
+          a += (double)w[(size_t)c * W + i] * xv;
+        }
+        y[(size_t)(bos + t) * D + c] = a * sigmoid(a);
+      }
+      if (slot >= 0 && len > 0) {
+        for (int32_t j = 0; j < P; ++j) {
+          const int32_t pos = len - P + j;
+          st[(size_t)j * D + c] = pos >= 0 ? kda_oracle_bf16_to_double(x[(size_t)(bos + pos) * D + c])
+                                           : hist[P + pos];
+        }
+      }
+    }
+    /* L2 norm of q and k per head. */
+    for (int32_t t = 0; t < len; ++t) {
+      double* yr = y + (size_t)(bos + t) * D;
+      for (int32_t part = 0; part < 2; ++part)
+        for (int32_t h = 0; h < H; ++h) {
+          double* v = yr + (size_t)part * H * K + (size_t)h * K;
+          double ss = 0.0;
+          for (int32_t i = 0; i < K; ++i) ss += v[i] * v[i];
+          const double inv = 1.0 / sqrt(ss + l2_eps);
+          for (int32_t i = 0; i < K; ++i) v[i] *= inv;
+        }
+    }
+  }
+  free(hist);
+}

@@ -74,6 +74,17 @@ void kda_oracle_gated_rmsnorm(int64_t rows, int32_t H, int32_t V, double* o,
                               const uint16_t* z, int64_t z_row_stride,
                               const float* w, double eps, int32_t activation);
 
+/* Short causal conv prologue (reading R22), varlen over cu_seqlens:
+ * x: bf16 bits [rows][D] (D = 2HK + HV); w: fp32 [D][W]; bias: fp32 [D] or
+ * NULL; state: fp64 [slots][W-1][D] (in/out; entry i of indices at
+ * i*index_stride, negative = null); y: fp64 [rows][D]. */
+void kda_oracle_short_conv(int32_t num_seqs, const int32_t* cu_seqlens,
+                           const uint8_t* has_initial_state, int32_t H,
+                           int32_t K, int32_t V, int32_t W, const uint16_t* x,
+                           const float* w, const float* bias, double l2_eps,
+                           double* state, const int32_t* indices,
+                           int64_t index_stride, double* y);
+
 #ifdef __cplusplus
 }
 #endif

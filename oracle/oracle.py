@@ -88,6 +88,9 @@ def lib():
         L.kda_oracle_prefill.restype = i32
         L.kda_oracle_gated_rmsnorm.argtypes = [ctypes.c_int64, i32, i32, vp, vp, ctypes.c_int64, vp, d, i32]
         L.kda_oracle_gated_rmsnorm.restype = None
+        L.kda_oracle_short_conv.argtypes = [i32, vp, vp, i32, i32, i32, i32, vp, vp, vp, d, vp, vp,
+                                            ctypes.c_int64, vp]
+        L.kda_oracle_short_conv.restype = None
         _lib = L
     return _lib
 
@@ -341,3 +344,36 @@ def gated_rmsnorm(out: np.ndarray, gate: torch.Tensor, weight: torch.Tensor, eps
     lib().kda_oracle_gated_rmsnorm(rows, H, V, _ptr(y), _ptr(bits), H * V, _ptr(w), float(eps),
                                    ACTIVATIONS[activation])
     return y
+
+
+# --------------------------------------------------------- input prologue
+
+def short_conv(x: torch.Tensor, weight: torch.Tensor, bias, conv_state: torch.Tensor,
+               state_indices: torch.Tensor, cu_seqlens, H: int, K: int, V: int,
+               has_initial_state=None, l2_eps: float = 1e-6):
+    """Short causal conv prologue (reading R22 of the design notes; vLLM PR
+    #60683 Purpose names a conv step before the recurrence but prints no
+    formula): per sequence and channel of the [q | k | v] pre-activations,
+    a = bias + sum_i w[c][i] x[t - (W-1) + i] with earlier inputs from the
+    conv state, y = silu(a), then q and k of each head L2-normalised.
+    x: bf16 [rows, >= D]; weight: fp32 [D, W]; bias: fp32 [D] or None;
+    conv_state: [slots, W-1, D] (any float dtype; read as given);
+    state_indices: int32 1-D (strides honoured). Returns (y fp64 [rows, D],
+    new conv state fp64 [slots, W-1, D])."""
+    D = 2 * H * K + H * V
+    Wd = int(weight.shape[1])
+    rows = x.shape[0]
+    xb = _bits(x[:, :D].contiguous()) if rows else np.zeros(1, dtype=np.uint16)
+    w = np.ascontiguousarray(weight.detach().cpu().float().numpy())
+    assert w.shape == (D, Wd)
+    b = None if bias is None else np.ascontiguousarray(bias.detach().cpu().float().numpy())
+    st = np.array(conv_state.detach().cpu().double().numpy(), dtype=np.float64, copy=True)  # never the caller's buffer
+    assert st.shape[1:] == (Wd - 1, D)
+    idx, stride = _indices(state_indices)
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+    hs = None if has_initial_state is None else np.ascontiguousarray(np.asarray(has_initial_state, dtype=np.uint8))
+    y = np.zeros((max(rows, 1), D), dtype=np.float64)
+    lib().kda_oracle_short_conv(len(cu) - 1, _ptr(cu), _ptr(hs) if hs is not None else None, H, K, V, Wd,
+                                _ptr(xb), _ptr(w), _ptr(b) if b is not None else None, float(l2_eps),
+                                _ptr(st), _ptr(idx), stride, _ptr(y))
+    return y[:rows], st

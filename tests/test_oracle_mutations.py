@@ -56,6 +56,12 @@ MUTANTS = {
     "norm_silu_as_sigmoid": ("const double act = activation == 1 ? zv * sigmoid(zv) : sigmoid(zv);",
                              "const double act = sigmoid(zv);"),
     "norm_weight_dropped": ("oh[j] = oh[j] * inv * (double)w[j] * act;", "oh[j] = oh[j] * inv * act;"),
+    "conv_taps_reversed": ("a += (double)w[(size_t)c * W + i] * xv;", "a += (double)w[(size_t)c * W + (W - 1 - i)] * xv;"),
+    "conv_history_off_by_one": (": hist[P + pos];\n          a +=", ": hist[P + pos - (pos > -P)];\n          a +="),
+    "conv_sigmoid_not_silu": ("y[(size_t)(bos + t) * D + c] = a * sigmoid(a);", "y[(size_t)(bos + t) * D + c] = sigmoid(a);"),
+    "conv_state_keeps_first_inputs": ("const int32_t pos = len - P + j;", "const int32_t pos = j;"),
+    "conv_q_not_normalised": ("for (int32_t part = 0; part < 2; ++part)", "for (int32_t part = 1; part < 2; ++part)"),
+    "conv_bias_dropped": ("double a = bias ? (double)bias[c] : 0.0;", "double a = 0.0;"),
 }
 
 

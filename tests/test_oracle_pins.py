@@ -560,3 +560,103 @@ def test_gated_rmsnorm_weight_is_per_channel_and_gate_per_head():
     o2[:, 1] *= -7.0
     y2 = O.gated_rmsnorm(o2, z, torch.ones(V), 0.1)
     np.testing.assert_array_equal(y2[:, 0], O.gated_rmsnorm(o, z, torch.ones(V), 0.1)[:, 0])
+
+
+# ------------------------------------------------ short conv prologue (R22)
+
+def _conv_setup(lens, H=2, K=4, V=3, Wd=4, slots=6, seed=81, bias=True):
+    g = torch.Generator().manual_seed(seed)
+    D = 2 * H * K + H * V
+    rows = sum(lens)
+    x = torch.randn(rows, D, generator=g).to(torch.bfloat16)
+    w = torch.randn(D, Wd, generator=g) * 0.5
+    b = torch.randn(D, generator=g) * 0.1 if bias else None
+    state = torch.randn(slots, Wd - 1, D, generator=g).to(torch.bfloat16).double()
+    idx = torch.randperm(slots, generator=g)[:len(lens)].to(torch.int32)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    return D, x, w, b, state, idx, cu
+
+
+def _silu(a):
+    return torch.nn.functional.silu(torch.as_tensor(a, dtype=torch.float64)).numpy()
+
+
+def test_short_conv_matches_numpy_convolution_per_channel():
+    """Pre-activation = numpy's convolution of [history; inputs] with the
+    flipped taps, then torch's silu; q and k of each head are then unit
+    vectors along the same direction."""
+    H, K, V, Wd = 2, 4, 3, 4
+    lens = [5, 1, 9]
+    D, x, w, b, state, idx, cu = _conv_setup(lens, H, K, V, Wd)
+    y, _ = O.short_conv(x, w, b, state, idx, cu, H, K, V, l2_eps=1e-300)
+    xf = x.double().numpy()
+    raw = np.zeros_like(y)
+    for s in range(len(lens)):
+        hist = state[int(idx[s])].numpy()          # [W-1, D], oldest first
+        seq = np.concatenate([hist, xf[cu[s]:cu[s + 1]]])
+        for c in range(D):
+            a = np.convolve(seq[:, c], w[c].double().numpy()[::-1], mode="valid") + float(b[c])
+            raw[cu[s]:cu[s + 1], c] = _silu(a)
+    np.testing.assert_allclose(y[:, 2 * H * K:], raw[:, 2 * H * K:], rtol=1e-13, atol=1e-15)
+    for part in range(2):
+        for h in range(H):
+            sl = slice(part * H * K + h * K, part * H * K + (h + 1) * K)
+            ref = raw[:, sl] / np.linalg.norm(raw[:, sl], axis=1, keepdims=True)
+            np.testing.assert_allclose(y[:, sl], ref, rtol=1e-12, atol=1e-14)
+
+
+def test_short_conv_single_taps_are_shifts():
+    """One-hot taps: the last tap passes the current input, the first passes
+    the input W-1 rows back (from the conv state for the first rows)."""
+    H, K, V, Wd = 1, 4, 4, 4
+    D, x, _, _, state, idx, cu = _conv_setup([6], H, K, V, Wd, seed=83)
+    for tap, back in ((Wd - 1, 0), (0, Wd - 1)):
+        w = torch.zeros(D, Wd)
+        w[:, tap] = 1.0
+        y, _ = O.short_conv(x, w, None, state, idx, cu, H, K, V)
+        v = y[:, 2 * H * K:]
+        hist = state[int(idx[0])].numpy()
+        seq = np.concatenate([hist, x.double().numpy()])[:, 2 * H * K:]
+        np.testing.assert_allclose(v, _silu(seq[Wd - 1 - back: Wd - 1 - back + 6]), rtol=1e-14)
+
+
+def test_short_conv_state_carries_across_calls():
+    """One call over a sequence equals two calls with the conv state carried
+    between them, and T one-row calls equal one T-row call; a sequence
+    shorter than W-1 shifts the old state."""
+    H, K, V, Wd = 2, 4, 3, 4
+    D, x, w, b, state, idx, cu = _conv_setup([7], H, K, V, Wd, seed=85)
+    y_all, st_all = O.short_conv(x, w, b, state, idx, cu, H, K, V)
+    cuts = [0, 2, 3, 7]
+    st = state.clone()
+    ys = []
+    for a, e in zip(cuts[:-1], cuts[1:]):
+        y, st_np = O.short_conv(x[a:e], w, b, st, idx, [0, e - a], H, K, V)
+        st = torch.from_numpy(st_np)
+        ys.append(y)
+    np.testing.assert_allclose(np.concatenate(ys), y_all, rtol=1e-14, atol=1e-15)
+    np.testing.assert_array_equal(st.numpy(), st_all)
+    # The new state is the last W-1 inputs of the sequence.
+    np.testing.assert_array_equal(st_all[int(idx[0])], x[-(Wd - 1):].double().numpy())
+    # A 1-row call shifts the old state by one row and appends the input.
+    _, st1 = O.short_conv(x[:1], w, b, state, idx, [0, 1], H, K, V)
+    old = state[int(idx[0])].numpy()
+    np.testing.assert_array_equal(st1[int(idx[0])], np.concatenate([old[1:], x[:1].double().numpy()]))
+
+
+def test_short_conv_null_slot_and_no_initial_state():
+    H, K, V, Wd = 2, 4, 3, 3
+    D, x, w, b, state, idx, cu = _conv_setup([4, 3], H, K, V, Wd, seed=87)
+    null = idx.clone()
+    null[0] = -1
+    y_null, st_null = O.short_conv(x, w, b, state, null, cu, H, K, V)
+    y_zero, st_zero = O.short_conv(x, w, b, state, idx, cu, H, K, V, has_initial_state=[0, 1])
+    # Both read zeros before the first row; the null slot writes no state
+    # (only the second sequence's slot changes).
+    np.testing.assert_array_equal(y_null, y_zero)
+    others = [s for s in range(state.shape[0]) if s != int(idx[1])]
+    np.testing.assert_array_equal(st_null[others], state.numpy()[others])
+    assert not np.array_equal(st_zero[int(idx[0])], state[int(idx[0])].numpy())
+    y_init, _ = O.short_conv(x, w, b, state, idx, cu, H, K, V)
+    assert not np.allclose(y_init[:Wd - 1], y_zero[:Wd - 1])
+    np.testing.assert_array_equal(y_init[Wd - 1:4], y_zero[Wd - 1:4])   # history no longer reached
