@@ -14,8 +14,9 @@ and never synchronise) and the graph is replayed; HIP events on the replay
 stream bracket the timed region. Eager (Python-launched) times are reported
 next to them. The same JSON line carries the other legs of the hot path:
 spec-verify (8 rows), chunked prefill (one 8192-token sequence; 64 varlen
-sequences; one 65536-token sequence), the mixed 4096-token batch and spec
-decode with a state per token.
+sequences; one 65536-token sequence), the mixed 4096-token batch, spec
+decode with a state per token, the gated RMSNorm output epilogue and the
+short-conv input prologue.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs ...]
 """
@@ -43,7 +44,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=320)
     ap.add_argument("--warmup", type=int, default=32)
-    ap.add_argument("--legs", default="decode,spec,prefill,mixed,norm")
+    ap.add_argument("--legs", default="decode,spec,prefill,mixed,norm,conv")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -335,6 +336,34 @@ def leg_prefill(steps, warmup, lens, name, seed, with_norm=False):
     }
 
 
+def leg_conv(steps, warmup, lens, name, seed):
+    """Short causal conv prologue (width 4) producing mixed_qkv for a batch:
+    reads x and the conv states, writes mixed_qkv and the new conv states."""
+    import torch
+
+    import gated_delta_rule_45_amd as kda
+    import workloads as W
+
+    dev = torch.device("cuda")
+    H, K, V, Wd = 32, 128, 128, 4
+    D = 2 * H * K + H * V
+    rows, n = sum(lens), len(lens)
+    ci = W.make_conv(rows, H, K, V, Wd, 2 * n, seed)
+    x, w, b = ci["x"].to(dev), ci["weight"].to(dev), ci["bias"].to(dev)
+    state = ci["conv_state"].to(dev)
+    idx = [torch.arange(c * n, (c + 1) * n, dtype=torch.int32, device=dev) for c in range(2)]
+    cu = W.cu_from_lengths(lens).to(dev)
+    out = torch.empty(rows, D, dtype=torch.bfloat16, device=dev)
+
+    def step(i):
+        kda.kda_short_conv(x, w, b, state, idx[i % 2], cu, H=H, K=K, V=V, out=out)
+
+    ms, _ = graph_time(step, 2, steps, warmup)
+    io = rows * D * 2 * 2 + 2 * n * (Wd - 1) * D * 2
+    return {"workload": name, "ms_per_step": round(ms, 5), "rows_per_s": round(rows / (ms * 1e-3), 1),
+            "io_gbs": round(io / (ms * 1e-3) / 1e9, 1), "io_bytes_per_step": io}
+
+
 def leg_mixed(steps, warmup):
     import torch
 
@@ -427,6 +456,12 @@ def main():
         extra["prefill_t65536"] = leg_prefill(max(pf_steps // 2, 4), 1, [65536], "prefill_t65536_h32_k128", 3004)
     if "mixed" in legs:
         extra["mixed_4096"] = leg_mixed(max(args.steps // 16, 9), 9)
+    if "conv" in legs:
+        # Short causal conv prologue: the decode batch and one 8192-token sequence.
+        extra["conv_prologue_decode_n32"] = leg_conv(args.steps, args.warmup, [1] * 32,
+                                                     "conv_prologue_decode_h32_k128_n32_w4", 3100)
+        extra["conv_prologue_t8192"] = leg_conv(max(args.steps // 8, 16), 4, [8192],
+                                                "conv_prologue_t8192_h32_k128_w4", 3101)
     if "norm" in legs:
         # Gated RMSNorm output epilogue: inside the decode kernel (whole-row
         # tiles), and as a pass after the prefill state pass.

@@ -12,6 +12,7 @@ from ._binding import (  # noqa: F401
     kda_decode_packed,
     kda_mixed_batch,
     kda_mixed_batch_workspace_size,
+    kda_short_conv,
     kda_spec_decode,
     lib,
 )
@@ -24,6 +25,7 @@ __all__ = [
     "kda_decode_packed",
     "kda_mixed_batch",
     "kda_mixed_batch_workspace_size",
+    "kda_short_conv",
     "kda_spec_decode",
     "lib",
 ]

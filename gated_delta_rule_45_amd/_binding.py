@@ -51,6 +51,12 @@ class GatedRMSNorm:
         self.gate, self.weight, self.eps, self.activation = gate, weight, float(eps), activation
 
 
+class KdaShortConv(ctypes.Structure):
+    _fields_ = [("weight", ctypes.c_void_p), ("bias", ctypes.c_void_p), ("width", ctypes.c_int32),
+                ("l2_eps", ctypes.c_float), ("conv_state", ctypes.c_void_p),
+                ("conv_slot_stride", ctypes.c_int64), ("num_slots", ctypes.c_int64)]
+
+
 class KdaError(ValueError):
     """A call was rejected. ``status`` is the C status code, ``reasons`` the
     list of every failed check."""
@@ -89,6 +95,9 @@ def lib() -> ctypes.CDLL:
         L.kda_mixed_batch.argtypes = [i32, i32, i64, vp, vp, i32, i32, i32, vp, i64, vp, vp, gp,
                                       spn, npn, vp, vp, sz, vp]
         L.kda_mixed_batch.restype = i32
+        L.kda_short_conv.argtypes = [i32, i64, vp, vp, i32, i32, i32, vp, i64,
+                                     ctypes.POINTER(KdaShortConv), vp, i64, vp, i64, vp]
+        L.kda_short_conv.restype = i32
         L.kda_status_string.argtypes = [i32]
         L.kda_status_string.restype = ctypes.c_char_p
         L.kda_last_error.argtypes = []
@@ -373,3 +382,56 @@ def kda_mixed_batch(mixed_qkv, raw_g, raw_beta, A_log, dt_bias, lower_bound, ini
                                ws.numel(), _stream(mixed_qkv.device))
     _raise_if(st)
     return out, initial_state
+
+
+def kda_short_conv(x, weight, bias, conv_state, state_indices, cu_seqlens, *, H: int, K: int, V: int,
+                   has_initial_state=None, l2_eps: float = 1e-6, out=None):
+    """Short causal conv prologue: mixed_qkv from the [q | k | v]
+    pre-activations ``x`` (bf16 [rows, >= D], D = 2*H*K + H*V, unit-stride
+    rows). ``weight`` fp32 [D, width], ``bias`` fp32 [D] or None,
+    ``conv_state`` bf16 [slots, width-1, D] (updated in place; rows of a slot
+    contiguous), ``state_indices`` int32 1-D (possibly strided),
+    ``cu_seqlens`` device int32 [num_seqs+1]. Returns ``(out, conv_state)``
+    with ``out`` bf16 [rows, D] (or the given ``out``, any unit-stride rows)."""
+    m = _Marshal()
+    m.tensor("x", x, torch.bfloat16, 2)
+    m.tensor("weight", weight, torch.float32, 2)
+    m.tensor("bias", bias, torch.float32, 1, optional=True)
+    m.tensor("conv_state", conv_state, torch.bfloat16, 3)
+    m.tensor("state_indices", state_indices, torch.int32, 1)
+    m.tensor("cu_seqlens", cu_seqlens, torch.int32, 1)
+    m.tensor("has_initial_state", has_initial_state, torch.uint8, 1, optional=True)
+    m.raise_if_any()
+    D = 2 * H * K + H * V
+    width = weight.shape[1]
+    num_seqs = cu_seqlens.shape[0] - 1
+    rows = x.shape[0]
+    m.check(x.shape[1] >= D and x.stride(1) == 1, f"x must be [rows, >= {D}] with unit-stride rows")
+    m.check(tuple(weight.shape) == (D, width) and weight.is_contiguous(),
+            f"weight must be a contiguous [{D}, width] tensor")
+    if bias is not None:
+        m.check(tuple(bias.shape) == (D,) and bias.is_contiguous(), f"bias must be a contiguous [{D}] tensor")
+    m.check(conv_state.shape[1:] == (width - 1, D) and conv_state.stride(1) == D and conv_state.stride(2) == 1,
+            f"conv_state must be [slots, {width - 1}, {D}] with contiguous slots")
+    m.check(cu_seqlens.is_contiguous(), "cu_seqlens must be contiguous")
+    m.check(state_indices.shape[0] == num_seqs, "state_indices needs one entry per sequence")
+    if has_initial_state is not None:
+        m.check(has_initial_state.shape[0] == num_seqs and has_initial_state.is_contiguous(),
+                "has_initial_state must be contiguous with one entry per sequence")
+    m.raise_if_any()
+    if out is None:
+        out = torch.empty(rows, D, dtype=torch.bfloat16, device=x.device)
+    else:
+        m.tensor("out", out, torch.bfloat16, 2)
+        m.raise_if_any()
+        m.check(out.shape[0] == rows and out.shape[1] >= D and out.stride(1) == 1,
+                f"out must be [{rows}, >= {D}] with unit-stride rows")
+        m.raise_if_any()
+    cv = KdaShortConv(weight=weight.data_ptr(), bias=bias.data_ptr() if bias is not None else None,
+                      width=int(width), l2_eps=float(l2_eps), conv_state=conv_state.data_ptr(),
+                      conv_slot_stride=conv_state.stride(0), num_slots=conv_state.shape[0])
+    st = lib().kda_short_conv(num_seqs, rows, _ptr(cu_seqlens), _ptr(has_initial_state), H, K, V,
+                              _ptr(x), x.stride(0), ctypes.byref(cv), _ptr(state_indices),
+                              state_indices.stride(0), _ptr(out), out.stride(0), _stream(x.device))
+    _raise_if(st)
+    return out, conv_state

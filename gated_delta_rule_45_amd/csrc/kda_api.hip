@@ -336,6 +336,81 @@ kda_status_t kda_mixed_batch(int32_t num_decodes, int32_t num_prefills, int64_t 
   return KDA_OK;
 }
 
+kda_status_t kda_short_conv(int32_t num_seqs, int64_t num_rows, const int32_t* cu_seqlens,
+                            const uint8_t* has_initial_state, int32_t H, int32_t K, int32_t V,
+                            const void* x, int64_t x_row_stride, const kda_short_conv_t* conv,
+                            const int32_t* indices, int64_t index_stride, void* mixed_qkv,
+                            int64_t qkv_row_stride, hipStream_t stream) {
+  Checks c;
+  const auto INV = KDA_ERR_INVALID_ARGUMENT;
+  const auto UNS = KDA_ERR_UNSUPPORTED;
+  c.require(num_seqs >= 0, INV, "num_seqs must be >= 0");
+  c.require(num_rows >= 0 && num_rows <= 0x7fffffffLL, INV, "num_rows must be in 0..2^31-1");
+  c.require(num_rows == 0 || num_seqs > 0, INV, "num_rows > 0 needs num_seqs > 0");
+  if (num_seqs > 0) c.require(cu_seqlens != nullptr, INV, "cu_seqlens must not be NULL");
+  c.require(H >= 1, INV, "H must be >= 1");
+  c.require(K == 64 || K == 128, UNS, "K must be 64 or 128");
+  c.require(V == 64 || V == 128, UNS, "V must be 64 or 128");
+  c.require(conv != nullptr, INV, "conv must not be NULL");
+  c.require(indices != nullptr || num_seqs == 0, INV, "indices must not be NULL");
+  c.require(index_stride >= 1, INV, "index_stride must be >= 1 (a non-positive stride is rejected)");
+  const int64_t D = 2 * static_cast<int64_t>(H) * K + static_cast<int64_t>(H) * V;
+  if (conv) {
+    c.require(conv->width >= 2 && conv->width <= 4, UNS, "conv->width must be 2, 3 or 4");
+    c.require(std::isfinite(conv->l2_eps) && conv->l2_eps > 0.0f, INV, "conv->l2_eps must be finite and > 0");
+    c.require(conv->weight != nullptr, INV, "conv->weight must not be NULL");
+    c.require(aligned(conv->weight, 16), UNS, "conv->weight must be 16-byte aligned");
+    c.require(conv->bias == nullptr || aligned(conv->bias, 16), UNS, "conv->bias must be 16-byte aligned");
+    c.require(conv->conv_state != nullptr, INV, "conv->conv_state must not be NULL");
+    c.require(aligned(conv->conv_state, 16), UNS, "conv->conv_state must be 16-byte aligned");
+    c.require(conv->num_slots >= 1, INV, "conv->num_slots must be >= 1");
+    if (H >= 1)
+      c.require(conv->conv_slot_stride >= (conv->width - 1) * D, INV,
+                "conv->conv_slot_stride must be >= (width-1)*D");
+    c.require(conv->conv_slot_stride % 8 == 0, UNS, "conv->conv_slot_stride must be a multiple of 8");
+  }
+  if (num_rows > 0) {
+    c.require(x != nullptr, INV, "x must not be NULL");
+    c.require(mixed_qkv != nullptr, INV, "mixed_qkv must not be NULL");
+    if (H >= 1) {
+      c.require(x_row_stride >= D, INV, "x_row_stride must be >= 2*H*K + H*V");
+      c.require(qkv_row_stride >= D, INV, "qkv_row_stride must be >= 2*H*K + H*V");
+    }
+    c.require(x_row_stride % 8 == 0 && qkv_row_stride % 8 == 0, UNS,
+              "x_row_stride and qkv_row_stride must be multiples of 8");
+    c.require(aligned(x, 16) && aligned(mixed_qkv, 16), UNS, "x and mixed_qkv must be 16-byte aligned");
+    if (x && mixed_qkv && x_row_stride >= 1 && qkv_row_stride >= 1) {
+      const auto xa = reinterpret_cast<uintptr_t>(x), oa = reinterpret_cast<uintptr_t>(mixed_qkv);
+      const uintptr_t xe = xa + static_cast<uintptr_t>(num_rows * x_row_stride * 2);
+      const uintptr_t oe = oa + static_cast<uintptr_t>(num_rows * qkv_row_stride * 2);
+      c.require(xe <= oa || oe <= xa, INV, "mixed_qkv must not overlap x");
+    }
+  }
+  if (!c.ok()) return c.finish();
+  if (num_seqs == 0) return c.finish();
+  kda::ConvParams p{};
+  p.x = static_cast<const uint16_t*>(x);
+  p.x_row_stride = x_row_stride;
+  p.weight = conv->weight;
+  p.bias = conv->bias;
+  p.width = conv->width;
+  p.l2_eps = conv->l2_eps;
+  p.conv_state = static_cast<uint16_t*>(conv->conv_state);
+  p.conv_slot_stride = conv->conv_slot_stride;
+  p.indices = indices;
+  p.index_stride = index_stride;
+  p.cu_seqlens = cu_seqlens;
+  p.has_initial_state = has_initial_state;
+  p.out = static_cast<uint16_t*>(mixed_qkv);
+  p.out_row_stride = qkv_row_stride;
+  p.num_seqs = num_seqs;
+  p.num_rows = num_rows;
+  p.H = H;
+  p.K = K;
+  p.V = V;
+  return hip_status(kda::launch_short_conv(p, stream), "short conv launch");
+}
+
 const char* kda_status_string(kda_status_t status) {
   switch (status) {
     case KDA_OK: return "KDA_OK";

@@ -52,6 +52,31 @@ struct DecodeParams {
   int64_t num_tiles;        // num_seqs * H * (V / VT)
 };
 
+// One short-conv prologue call (varlen over cu_seqlens).
+struct ConvParams {
+  const uint16_t* x;            // bf16 [rows][x_row_stride], channels [q | k | v]
+  int64_t x_row_stride;         // elements
+  const float* weight;          // [D][width]
+  const float* bias;            // [D] or null
+  int32_t width;                // 2..4
+  float l2_eps;
+  uint16_t* conv_state;         // bf16 pool; slot s at s*conv_slot_stride: [width-1][D]
+  int64_t conv_slot_stride;     // elements
+  const int32_t* indices;       // entry i at indices[i*index_stride]; < 0: null
+  int64_t index_stride;
+  const int32_t* cu_seqlens;    // [num_seqs+1]
+  const uint8_t* has_initial_state;  // may be null (all 1)
+  uint16_t* out;                // bf16 [rows][out_row_stride] (mixed_qkv)
+  int64_t out_row_stride;       // elements
+  int32_t num_seqs;
+  int64_t num_rows;
+  int32_t H;
+  int32_t K;
+  int32_t V;
+};
+
+hipError_t launch_short_conv(const ConvParams& p, hipStream_t stream);
+
 // Picks the column-tile width for a decode launch and launches it.
 hipError_t launch_decode(DecodeParams p, int K, hipStream_t stream);
 

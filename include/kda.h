@@ -225,6 +225,51 @@ kda_status_t kda_mixed_batch(int32_t num_decodes, int32_t num_prefills,
                              void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
 
+/* Short causal conv prologue (vLLM PR #60683, Purpose: in the decode
+ * kernels a conv step precedes the KDA recurrence; the page prints no
+ * formula, so this is a reading). It produces mixed_qkv from the [q | k | v]
+ * pre-activations x (D = 2*H*K + H*V channels, head-major as in mixed_qkv).
+ * Per sequence and channel c:
+ *     a[t][c] = bias[c] + sum_{i<width} weight[c*width + i] * x[t-(width-1)+i][c]
+ * where the inputs before the sequence's first row come from its conv state
+ * (the width-1 previous inputs, oldest first), read as zero on a null slot
+ * or when has_initial_state[i] == 0. Then y = silu(a) = a*sigmoid(a), and q
+ * and k of each head are divided by sqrt(sum of squares + l2_eps). The new
+ * conv state, the sequence's last width-1 inputs (older ones from the old
+ * state for a shorter sequence), is written back bit for bit unless the
+ * slot is null or the sequence empty. */
+typedef struct {
+  const float* weight;      /* device fp32 [D][width], 16-byte aligned          */
+  const float* bias;        /* device fp32 [D] (16-byte aligned), or NULL       */
+  int32_t width;            /* 2..4                                             */
+  float l2_eps;             /* > 0, finite                                      */
+  void* conv_state;         /* device bf16 pool, 16-byte aligned; slot s at
+                               conv_state + s*conv_slot_stride: [width-1][D]    */
+  int64_t conv_slot_stride; /* elements, >= (width-1)*D, a multiple of 8        */
+  int64_t num_slots;        /* >= 1                                             */
+} kda_short_conv_t;
+
+/*
+ * Varlen: sequence i covers rows cu_seqlens[i] .. cu_seqlens[i+1]-1 (device
+ * int32 [num_seqs+1], cu_seqlens[num_seqs] == num_rows; a decode batch is
+ * sequences of one row, a spec-verify step sequences of tokens_per_seq rows)
+ * and uses conv-state slot indices[i*index_stride] (the same slot numbers as
+ * the KDA state pool). has_initial_state: device uint8 [num_seqs] or NULL.
+ *   x          bf16 [num_rows][x_row_stride], x_row_stride >= D, multiple of 8.
+ *   mixed_qkv  bf16 [num_rows][qkv_row_stride] output, qkv_row_stride >= D,
+ *              multiple of 8; must not overlap x.
+ * Errors: KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED, KDA_ERR_HIP.
+ */
+kda_status_t kda_short_conv(int32_t num_seqs, int64_t num_rows,
+                            const int32_t* cu_seqlens,
+                            const uint8_t* has_initial_state,
+                            int32_t H, int32_t K, int32_t V,
+                            const void* x, int64_t x_row_stride,
+                            const kda_short_conv_t* conv,
+                            const int32_t* indices, int64_t index_stride,
+                            void* mixed_qkv, int64_t qkv_row_stride,
+                            hipStream_t stream);
+
 /* Static name of a status code. */
 const char* kda_status_string(kda_status_t status);
 

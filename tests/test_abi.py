@@ -97,6 +97,26 @@ def test_output_norm_rejects_and_lists_every_reason():
     assert st == 1 and "norm" not in msg and "out must not be NULL" in msg
 
 
+def test_short_conv_rejects_and_lists_every_reason():
+    L = kda.lib()
+    cv = B.KdaShortConv(weight=None, bias=FAKE + 4, width=5, l2_eps=float("nan"), conv_state=FAKE,
+                        conv_slot_stride=10, num_slots=0)
+    st = L.kda_short_conv(2, 10, None, None, 32, 96, 128, FAKE, 100, ctypes.byref(cv), FAKE, 0,
+                          FAKE, 3 * 32 * 128, None)
+    msg = L.kda_last_error().decode()
+    assert st == 1
+    for frag in ("cu_seqlens must not be NULL", "K must be 64 or 128", "index_stride must be >= 1",
+                 "conv->width must be 2, 3 or 4", "conv->l2_eps", "conv->weight must not be NULL",
+                 "conv->bias must be 16-byte aligned", "conv->num_slots", "x_row_stride must be >="):
+        assert frag in msg, msg
+    # Output overlapping the input is refused.
+    cv = B.KdaShortConv(weight=FAKE, bias=None, width=4, l2_eps=1e-6, conv_state=FAKE,
+                        conv_slot_stride=3 * 3 * 32 * 128, num_slots=4)
+    st = L.kda_short_conv(2, 10, FAKE, None, 32, 128, 128, FAKE, 3 * 32 * 128, ctypes.byref(cv), FAKE, 1,
+                          FAKE + 3 * 32 * 128 * 2, 3 * 32 * 128, None)
+    assert st == 1 and "must not overlap x" in L.kda_last_error().decode()
+
+
 def test_negative_index_stride_rejected():
     st, msg = _decode(s=_state(index_stride=-8))
     assert st == 1 and "index_stride" in msg

@@ -17,6 +17,9 @@ distributions are this project's choice, since the pages give none):
              random slots; the other columns hold other slots (never read).
   output-norm epilogue: gate bf16 [rows, H*V (+ pad)] randn, weight fp32 [V]
              = 1 + 0.1 * randn, eps 1e-6.
+  conv prologue: x bf16 [rows, D (+ pad)] randn (D = 2*H*K + H*V); weight
+             fp32 [D, W] = 0.5 * randn; bias fp32 [D] = 0.1 * randn; conv
+             state bf16 [slots, W-1, D] randn.
 """
 from __future__ import annotations
 
@@ -109,6 +112,19 @@ def make_norm(rows: int, H: int, V: int, seed: int, activation: str = "sigmoid",
     wide = torch.randn(rows, H * V + row_pad, generator=g).to(torch.bfloat16)
     weight = 1.0 + 0.1 * torch.randn(V, generator=g)
     return {"gate": wide[:, :H * V], "weight": weight, "eps": eps, "activation": activation}
+
+
+def make_conv(rows: int, H: int, K: int, V: int, width: int, num_slots: int, seed: int,
+              bias: bool = True, x_row_pad: int = 0) -> dict:
+    """Inputs of the conv prologue; x rows sit inside a wider buffer when
+    ``x_row_pad`` > 0."""
+    g = _gen(seed)
+    D = 2 * H * K + H * V
+    x = torch.randn(rows, D + x_row_pad, generator=g).to(torch.bfloat16)[:, :D]
+    weight = 0.5 * torch.randn(D, width, generator=g)
+    b = 0.1 * torch.randn(D, generator=g) if bias else None
+    state = torch.randn(num_slots, width - 1, D, generator=g).to(torch.bfloat16)
+    return {"x": x, "weight": weight, "bias": b, "conv_state": state}
 
 
 def cu_from_lengths(lens) -> torch.Tensor:
