@@ -12,8 +12,10 @@
 //   O       = scale [ (Q o e^gam) S + P V' ]
 //   S      <- diag(e^{gam_last}) S + (K o e^{gam_last - gam})^T V'
 //
-// Three launches on one stream, no host synchronisation:
-//  1. plan:  chunk offsets per sequence from the device cu_seqlens.
+// Launches on one stream, no host synchronisation (the map pass only when a
+// call of these sizes can cut a sequence; see "segments" below):
+//  1. plan:  chunk offsets and segments per sequence from the device
+//            cu_seqlens.
 //  2. intra: one workgroup per (chunk, head), all chunks in parallel (last
 //            to first). Builds gam in registers, then A and P on bf16 MFMA
 //            from factored operand tiles (or, for a chunk with a block that
@@ -23,8 +25,10 @@
 //            scale P, (K o e^{gam_last-gam})^T (bf16, laid out as MFMA A
 //            operands), e^{gam_last} and U (fp32, in accumulator fragment
 //            order) in the workspace.
-//  3. state: one workgroup per (sequence, head, 64 value columns), looping over
-//            the sequence's chunks in order. The state lives in MFMA
+//  3. map:   per non-final segment of a cut sequence, the affine map of
+//            its chunks (below).
+//  4. state: one workgroup per (segment, head, 64 value columns), looping over
+//            the segment's chunks in order. The state lives in MFMA
 //            accumulators (fp32) for the whole sequence; each chunk's A
 //            operands are double-buffered in LDS, and the next chunk's are
 //            copied in while the current one computes.
@@ -166,10 +170,10 @@ __device__ __forceinline__ int64_t rec_index(int h, int c, const PrefillParams& 
 //   M = prod_c (diag(e^{gam_last}) - (K o e^{gam_last - gam})^T W)   (K x K)
 //   B = the state reached from S_in = 0                                (K x V)
 // so a long sequence is cut into segments: a map pass computes (M, B) of
-// every segment but the last in parallel, a combine pass walks the segments
-// in order (S_{j+1} = M_j S_j + B_j, a K x K by K x V product per step),
-// and the state pass then runs all segments in parallel from their true
-// starting states.
+// every segment but the last in parallel, and in the state pass every
+// segment first walks the maps of the segments before it
+// (S_{j+1} = M_j S_j + B_j, a K x K by K x 16 product per wave and step)
+// and then runs its own chunks, all segments in parallel.
 //
 // A sequence is cut into at most ceil(chunks / kSegMinChunks) segments of
 // equal length (the last may be shorter), into no more segments than it
@@ -189,11 +193,10 @@ struct SegPlan {
   int32_t* seg_start;    // [N+1] first segment of each sequence
   int32_t* counts;       // [4]: segments, maps, long sequences, plan fits its bounds
   int32_t* seg_seq;      // [seg_bound] sequence of each segment
-  int32_t* seg_buf;      // [seg_bound] start-state buffer of a cut sequence's segment, else -1
+  int32_t* seg_long;     // [seg_bound] index of a cut sequence among the cut ones, else -1
   int32_t* map_seg;      // [map_bound] segment of each map item (a non-final segment)
-  int32_t* long_seq;     // [long_bound] the cut sequences
   float* maps;           // [H][map_bound]: M (fp32 [K][K]) then B (fp32 [K][V])
-  float* starts;         // [H][map_bound + long_bound]: fp32 [K][V] starting states
+  float* s0;             // [H][long_bound]: fp32 [K][V] initial state of each cut sequence
   int32_t seg_bound, map_bound, long_bound;
   int32_t max_segs;      // segments per sequence at most (host bound)
   int32_t fill_units;    // state-pass workgroups per segment (H * V / 64)
@@ -202,8 +205,8 @@ struct SegPlan {
 __device__ __forceinline__ int64_t map_index(int h, int mi, const SegPlan& pl) {
   return static_cast<int64_t>(h) * pl.map_bound + mi;
 }
-__device__ __forceinline__ int64_t start_index(int h, int sb, const SegPlan& pl) {
-  return static_cast<int64_t>(h) * (pl.map_bound + pl.long_bound) + sb;
+__device__ __forceinline__ int64_t s0_index(int h, int li, const SegPlan& pl) {
+  return static_cast<int64_t>(h) * pl.long_bound + li;
 }
 
 // Workspace layout (byte offsets) for one call's sizes. Bounds: a cut
@@ -212,8 +215,8 @@ __device__ __forceinline__ int64_t start_index(int h, int sb, const SegPlan& pl)
 // (and at most num_seqs (max_segs - 1)); each cut sequence has at least one.
 struct Layout {
   int64_t seg_bound, map_bound, long_bound, max_segs, fill_units;
-  size_t chunk_start, seg_start, counts, seg_seq, seg_buf, map_seg, long_seq;
-  size_t flags, recs, maps, starts, total;
+  size_t chunk_start, seg_start, counts, seg_seq, seg_long, map_seg;
+  size_t flags, recs, maps, s0, total;
 };
 
 inline size_t round256(size_t x) { return (x + 255) / 256 * 256; }
@@ -238,15 +241,14 @@ inline Layout layout_for(int32_t num_seqs, int64_t num_tokens, int32_t H, int32_
   L.seg_start = o;   o += (N + 1) * 4;
   L.counts = o;      o += 16;
   L.seg_seq = o;     o += L.seg_bound * 4;
-  L.seg_buf = o;     o += L.seg_bound * 4;
+  L.seg_long = o;    o += L.seg_bound * 4;
   L.map_seg = o;     o += L.map_bound * 4;
-  L.long_seq = o;    o += L.long_bound * 4;
   L.flags = round256(o);
   const int64_t maxc = max_chunks_for(num_tokens, num_seqs);
   L.recs = L.flags + round256(static_cast<size_t>(maxc) * H);
   L.maps = L.recs + static_cast<size_t>(maxc) * H * rec_bytes_for(K, V);
-  L.starts = L.maps + static_cast<size_t>(L.map_bound) * H * (static_cast<size_t>(K) * K + static_cast<size_t>(K) * V) * 4;
-  L.total = L.starts + static_cast<size_t>(L.map_bound + L.long_bound) * H * static_cast<size_t>(K) * V * 4;
+  L.s0 = L.maps + static_cast<size_t>(L.map_bound) * H * (static_cast<size_t>(K) * K + static_cast<size_t>(K) * V) * 4;
+  L.total = L.s0 + static_cast<size_t>(L.long_bound) * H * static_cast<size_t>(K) * V * 4;
   return L;
 }
 
@@ -324,14 +326,12 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t* cu, int32
     pl.seg_start[i] = sb;
     if (fits) {
       // Map items of sequence i start at sb - i (each earlier sequence has
-      // one fewer than its segments); its start-state buffers at sb - i + lb
-      // (each earlier cut sequence has one per segment).
+      // one fewer than its segments); lb counts the earlier cut sequences.
       for (int s = 0; s < ns; ++s) {
         pl.seg_seq[sb + s] = i;
-        pl.seg_buf[sb + s] = ns > 1 ? sb - i + lb + s : -1;
+        pl.seg_long[sb + s] = ns > 1 ? lb : -1;
       }
       for (int s = 0; s + 1 < ns; ++s) pl.map_seg[sb - i + s] = sb + s;
-      if (ns > 1) pl.long_seq[lb] = i;
     }
     cb += nch;
     sb += ns;
@@ -1214,12 +1214,12 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_state_kernel(const PrefillP
   }
 
   float* st = p.pool + slot * p.slot_stride + static_cast<int64_t>(h) * K * V;
-  // A segment of a cut sequence starts from the state the combine pass
-  // stored for it (the first segment too: the slot is written by the last
-  // segment of this same launch); an uncut sequence from its slot.
-  const int sbuf = uniform(pl.seg_buf[gs]);
-  const float* s_in = sbuf >= 0 ? pl.starts + start_index(h, sbuf, pl) * K * V : st;
-  const bool init = sbuf >= 0 || p.has_initial_state == nullptr ||
+  // Every segment of a cut sequence starts from the copy of the slot's state
+  // that the map pass made (the slot itself is written by the last segment
+  // of this same launch); an uncut sequence from its slot.
+  const int li = uniform(pl.seg_long[gs]);
+  const float* s_in = li >= 0 ? pl.s0 + s0_index(h, li, pl) * K * V : st;
+  const bool init = li >= 0 || p.has_initial_state == nullptr ||
                     uniform(static_cast<int32_t>(p.has_initial_state[seq])) != 0;
   // Without an initial state the range is empty and every load reads zero;
   // all loads are issued before the first use.
@@ -1231,7 +1231,6 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_state_kernel(const PrefillP
     for (int j = 0; j < 4; ++j)
       S[cb][j] = __builtin_bit_cast(
           float, __builtin_amdgcn_raw_buffer_load_b32(rs, ((16 * cb + 4 * g + j) * V + col0 + m) * 4, 0, 0));
-
   f32x4 Upre[4];
   auto rec_of = [&](int cc) {
     return recs + rec_index(h, c0 + cc, p) * static_cast<int64_t>(R::bytes);
@@ -1243,8 +1242,75 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_state_kernel(const PrefillP
 #pragma unroll
     for (int pb = 0; pb < 4; ++pb) Upre[pb] = buffer_load_f32x4<0>(ru, u_lane, pb * (V / 16) * 64 * 16);
   };
+  // The first chunk's copy and U loads go out first, so the walk below
+  // hides their latency.
   dma_chunk<K, V, kThreads>(rec_of(0), &buf[0], tid, wave);
   load_u(0);
+  // Segment sg > 0 of a cut sequence walks the maps of the segments before
+  // it: S <- M_j S + B_j. The wave holds all K rows of its 16 columns, so
+  // two accumulator tiles form a bf16 B operand as in the chunk loop (the
+  // contraction index permuted within each 32-block); lane (m, g)'s A
+  // operand is then M[row m][32 kb + 4 g .. +3] and M[row m][32 kb + 16 +
+  // 4 g .. +3], two float4s of the row-major fp32 M. Both operands are split
+  // into bf16 hi + lo parts and the product is hi*hi + hi*lo + lo*hi (about
+  // 16 significant bits, fp32 accumulation).
+  if (li >= 0 && sg > 0) {
+    // Flattened over (step j, row tile rt); tile i + 1's operands are loaded
+    // while tile i computes (the scheduling barriers keep that order).
+    const int mi0 = seg0 - seq;  // the sequence's first map item
+    const int64_t item = static_cast<int64_t>(K) * K + static_cast<int64_t>(K) * V;
+    constexpr int RT = K / 16, KB = K / 32;
+    auto load_tile = [&](int i, f32x4 (&a)[KB][2], f32x4& b) {
+      const float* M = pl.maps + map_index(h, mi0 + i / RT, pl) * item;
+      const int rt = i % RT;
+      const float* row = M + (16 * rt + m) * K + 4 * g;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        a[kb][0] = *reinterpret_cast<const f32x4*>(row + 32 * kb);
+        a[kb][1] = *reinterpret_cast<const f32x4*>(row + 32 * kb + 16);
+      }
+      const float* Bm = M + static_cast<int64_t>(K) * K;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) b[jj] = Bm[(16 * rt + 4 * g + jj) * V + col0 + m];
+    };
+    f32x4 a_cur[KB][2], a_nxt[KB][2], b_cur, b_nxt;
+    bf16x8 Sh[KB], Sl[KB];
+    load_tile(0, a_cur, b_cur);
+    const int tiles = sg * RT;
+    for (int i = 0; i < tiles; ++i) {
+      const int rt = i % RT;
+      if (rt == 0) {
+        // Operands of this step: the state before it, as bf16 hi + lo.
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          Sh[kb] = pack_acc(S[2 * kb], S[2 * kb + 1]);
+          Sl[kb] = pack_lo(S[2 * kb], S[2 * kb + 1], Sh[kb]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + 1 < tiles) load_tile(i + 1, a_nxt, b_nxt);
+      __builtin_amdgcn_sched_barrier(0);
+      f32x4 acc = b_cur;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const bf16x8 ah = pack_acc(a_cur[kb][0], a_cur[kb][1]);
+        const bf16x8 al = pack_lo(a_cur[kb][0], a_cur[kb][1], ah);
+        acc = mfma16(ah, Sh[kb], acc);
+        acc = mfma16(ah, Sl[kb], acc);
+        acc = mfma16(al, Sh[kb], acc);
+      }
+      // Row tile rt of the new state (the old tiles live on in Sh/Sl).
+#pragma unroll
+      for (int r2 = 0; r2 < RT; ++r2)
+        if (r2 == rt) S[r2] = acc;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        a_cur[kb][0] = a_nxt[kb][0];
+        a_cur[kb][1] = a_nxt[kb][1];
+      }
+      b_cur = b_nxt;
+    }
+  }
   // Lane (m, g) of the transposed output tile of position block pb holds
   // channels col0 + 4 g .. + 3 of position 16 pb + m: 8 contiguous bytes.
   const int out_lane = static_cast<int>(m * HV + h * V + col0 + 4 * g) * 2;
@@ -1455,6 +1521,25 @@ __global__ __launch_bounds__(kMapThreads, 2) void chunk_map_kernel(const Prefill
         Upre[ct][pb] = buffer_load_f32x4<0>(ru, (((col0 + 16 * ct) / 16) * 64 + lane) * 16, pb * (V / 16) * 64 * 16);
   };
   const bool takes_u = active && !is_m;
+  // The first map item of a cut sequence copies the slot's initial state
+  // (zero without one) for the state pass: its segments then never read the
+  // slot that the last of them writes. The waves with columns of B cover
+  // every value column once.
+  if (takes_u && mi == seg0 - seq) {
+    // Lane l copies 4 consecutive columns of rows l/8, l/8 + 8, ... of the
+    // wave's 32 columns; every load is issued before the first store.
+    const int li = uniform(pl.seg_long[gs]);
+    const bool init = p.has_initial_state == nullptr || uniform(static_cast<int32_t>(p.has_initial_state[seq])) != 0;
+    const float* src = p.pool + slot * p.slot_stride + static_cast<int64_t>(h) * K * V;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, init ? static_cast<uint32_t>(K * V * 4) : 0u);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(pl.s0 + s0_index(h, li, pl) * K * V, static_cast<uint32_t>(K * V * 4));
+    const int lane_off = ((lane >> 3) * V + col0 + 4 * (lane & 7)) * 4;
+    f32x4 cp[K / 8];
+#pragma unroll
+    for (int i = 0; i < K / 8; ++i) cp[i] = buffer_load_f32x4<0>(rs, lane_off, i * 8 * V * 4);
+#pragma unroll
+    for (int i = 0; i < K / 8; ++i) buffer_store_f32x4<0>(cp[i], rd, lane_off, i * 8 * V * 4);
+  }
   dma(0, &buf[0]);
   if (takes_u) load_u(0);
   for (int cc = 0; cc < nch; ++cc) {
@@ -1543,122 +1628,6 @@ __global__ __launch_bounds__(kMapThreads, 2) void chunk_map_kernel(const Prefill
       for (int j = 0; j < 4; ++j) dst[(16 * cb + 4 * g + j) * ld + col0 + 16 * ct + m] = S[ct][cb][j];
 }
 
-// ------------------------------------------------------------- combine --
-
-__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
-// One workgroup per (cut sequence, head, 16 value columns): S_0 = the slot's
-// state (or zero), S_{j+1} = M_j S_j + B_j, each S_j stored as segment j's
-// starting state. fp32 MFMA (16x16x4): in the MFMA that takes contraction
-// indices 16 cb + 4 g + kk (lane group g), lane (m, g) supplies
-// M[row m][16 cb + 4 g + kk] and S[16 cb + 4 g + kk][col m]: four
-// consecutive M entries per lane (one 16-byte load), and four consecutive
-// S entries of one column, read from LDS where S is kept transposed.
-// Wave w owns output row tiles w*RT .. w*RT + RT - 1.
-template <int K, int V>
-__global__ __launch_bounds__(kThreads) void chunk_combine_kernel(const PrefillParams p,
-                                                                 const SegPlan pl) {
-  constexpr int NB = V / 16;   // workgroups per (sequence, head)
-  constexpr int RT = K / 64;   // 16-row tiles per wave
-  constexpr int KB = K / 16;   // 16-index contraction blocks
-  constexpr int LD = K + 4;    // padded row of the transposed state (floats)
-  __shared__ float sT[2][16 * LD];
-
-  const int bidx = blockIdx.x;
-  const int pair = (bidx / (8 * NB)) * 8 + bidx % 8;
-  const int sub = (bidx / 8) % NB;
-  const int H = p.H;
-  if (uniform(pl.counts[3]) == 0) return;
-  const int li = pair / H, h = pair % H;
-  if (li >= uniform(pl.counts[2])) return;
-  const int seq = uniform(pl.long_seq[li]);
-  const int seg0 = uniform(pl.seg_start[seq]);
-  const int nseg = uniform(pl.seg_start[seq + 1]) - seg0;
-  const int mi0 = seg0 - seq;
-  const int sb0 = uniform(pl.seg_buf[seg0]);
-  const int64_t eos = uniform(static_cast<int64_t>(p.cu_seqlens[seq + 1]));
-  if (eos > p.num_tokens || sb0 < 0) return;
-  const int64_t slot = uniform(static_cast<int64_t>(p.indices[static_cast<int64_t>(seq) * p.index_stride]));
-  if (slot < 0) return;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = tid >> 6;
-  const int m = lane & 15;
-  const int g = lane >> 4;
-  const int c = 16 * sub + m;  // this lane's value column
-  const int64_t KV = static_cast<int64_t>(K) * V;
-  const int64_t item = static_cast<int64_t>(K) * K + KV;
-
-  // Operands of step j: this lane's M entries and B accumulator seeds.
-  f32x4 Ma[RT][KB], Bs[RT];
-  auto load_map = [&](int j, f32x4 (&a)[RT][KB], f32x4 (&bs)[RT]) {
-    const float* M = pl.maps + map_index(h, mi0 + j, pl) * item;
-    const float* Bm = M + static_cast<int64_t>(K) * K;
-#pragma unroll
-    for (int r = 0; r < RT; ++r) {
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-        a[r][kb] = *reinterpret_cast<const f32x4*>(M + (16 * (w * RT + r) + m) * K + 16 * kb + 4 * g);
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) bs[r][jj] = Bm[(16 * (w * RT + r) + 4 * g + jj) * V + c];
-    }
-  };
-  load_map(0, Ma, Bs);  // nseg > 1 for a cut sequence; issued before the slot's state is read
-  const bool init = p.has_initial_state == nullptr || uniform(static_cast<int32_t>(p.has_initial_state[seq])) != 0;
-  const float* st = p.pool + slot * p.slot_stride + static_cast<int64_t>(h) * KV;
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(st, init ? static_cast<uint32_t>(KV * 4) : 0u);
-  f32x4 S[RT];
-#pragma unroll
-  for (int r = 0; r < RT; ++r)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      S[r][j] = __builtin_bit_cast(
-          float, __builtin_amdgcn_raw_buffer_load_b32(rs, ((16 * (w * RT + r) + 4 * g + j) * V + c) * 4, 0, 0));
-  auto store_start = [&](int j) {
-    float* dst = pl.starts + start_index(h, sb0 + j, pl) * KV;
-#pragma unroll
-    for (int r = 0; r < RT; ++r)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) dst[(16 * (w * RT + r) + 4 * g + jj) * V + c] = S[r][jj];
-  };
-  store_start(0);
-  for (int j = 0; j + 1 < nseg; ++j) {
-    float* t = sT[j & 1];
-#pragma unroll
-    for (int r = 0; r < RT; ++r) *reinterpret_cast<f32x4*>(&t[m * LD + 16 * (w * RT + r) + 4 * g]) = S[r];
-    // One barrier per step: the other buffer, written next step, was last
-    // read before this barrier.
-    lds_barrier();
-    f32x4 Mn[RT][KB], Bn[RT];
-    if (j + 2 < nseg) load_map(j + 1, Mn, Bn);
-    f32x4 acc[RT];
-#pragma unroll
-    for (int r = 0; r < RT; ++r) acc[r] = Bs[r];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      const f32x4 sv = *reinterpret_cast<const f32x4*>(&t[m * LD + 16 * kb + 4 * g]);
-#pragma unroll
-      for (int r = 0; r < RT; ++r)
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) acc[r] = mfma_f32(Ma[r][kb][kk], sv[kk], acc[r]);
-    }
-#pragma unroll
-    for (int r = 0; r < RT; ++r) S[r] = acc[r];
-    store_start(j + 1);
-    if (j + 2 < nseg) {
-#pragma unroll
-      for (int r = 0; r < RT; ++r) {
-        Bs[r] = Bn[r];
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) Ma[r][kb] = Mn[r][kb];
-      }
-    }
-  }
-}
-
 template <int K, int V>
 hipError_t launch_kv(const PrefillParams& p, const Layout& L, const SegPlan& pl, uint8_t* exact_flags,
                      char* recs, hipStream_t stream) {
@@ -1667,9 +1636,7 @@ hipError_t launch_kv(const PrefillParams& p, const Layout& L, const SegPlan& pl,
   const int64_t seg_pairs = L.seg_bound * p.H;
   const int64_t state_blocks = (V / 64 == 2) ? (seg_pairs + 7) / 8 * 16 : seg_pairs;
   const int64_t map_blocks = (L.map_bound * p.H + 7) / 8 * 8 * ((K + V + 16 * kMapCT * kMapWaves - 1) / (16 * kMapCT * kMapWaves));
-  const int64_t combine_blocks = (L.long_bound * p.H + 7) / 8 * 8 * (V / 16);
-  if (intra_blocks > 0x7fffffff || state_blocks > 0x7fffffff || map_blocks > 0x7fffffff ||
-      combine_blocks > 0x7fffffff)
+  if (intra_blocks > 0x7fffffff || state_blocks > 0x7fffffff || map_blocks > 0x7fffffff)
     return hipErrorInvalidValue;
   chunk_intra_kernel<K, V><<<dim3(static_cast<unsigned>(intra_blocks)), dim3(kThreads), 0, stream>>>(
       p, pl.chunk_start, recs, exact_flags);
@@ -1677,7 +1644,6 @@ hipError_t launch_kv(const PrefillParams& p, const Layout& L, const SegPlan& pl,
       p, pl.chunk_start, recs, exact_flags);
   if (L.map_bound > 0) {
     chunk_map_kernel<K, V><<<dim3(static_cast<unsigned>(map_blocks)), dim3(kMapThreads), 0, stream>>>(p, pl, recs);
-    chunk_combine_kernel<K, V><<<dim3(static_cast<unsigned>(combine_blocks)), dim3(kThreads), 0, stream>>>(p, pl);
   }
   chunk_state_kernel<K, V><<<dim3(static_cast<unsigned>(state_blocks)), dim3(kThreads), 0, stream>>>(
       p, pl, recs);
@@ -1700,11 +1666,10 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   pl.seg_start = reinterpret_cast<int32_t*>(ws + L.seg_start);
   pl.counts = reinterpret_cast<int32_t*>(ws + L.counts);
   pl.seg_seq = reinterpret_cast<int32_t*>(ws + L.seg_seq);
-  pl.seg_buf = reinterpret_cast<int32_t*>(ws + L.seg_buf);
+  pl.seg_long = reinterpret_cast<int32_t*>(ws + L.seg_long);
   pl.map_seg = reinterpret_cast<int32_t*>(ws + L.map_seg);
-  pl.long_seq = reinterpret_cast<int32_t*>(ws + L.long_seq);
   pl.maps = reinterpret_cast<float*>(ws + L.maps);
-  pl.starts = reinterpret_cast<float*>(ws + L.starts);
+  pl.s0 = reinterpret_cast<float*>(ws + L.s0);
   pl.seg_bound = static_cast<int32_t>(L.seg_bound);
   pl.map_bound = static_cast<int32_t>(L.map_bound);
   pl.long_bound = static_cast<int32_t>(L.long_bound);
