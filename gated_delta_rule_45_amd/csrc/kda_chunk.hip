@@ -916,6 +916,11 @@ __device__ __forceinline__ void intra_body(const PrefillParams& p, const int32_t
 
   lds_barrier();  // A^T complete; x (or gam) no longer read
 
+  // beta of every position as a plain array in the first bytes of the kf
+  // area (dead on both paths from here), for 16-byte reads in step 7.
+  float* beta_l = reinterpret_cast<float*>(sm.u.f.kf);
+  if (tid < C) beta_l[tid] = beta_t;
+
   // ---- 4. (K o e^gam)^T into x: 16-byte pieces of 8 positions -----------
 #pragma unroll
   for (int u8 = 0; u8 < PP / 8; ++u8)
@@ -1010,36 +1015,48 @@ __device__ __forceinline__ void intra_body(const PrefillParams& p, const int32_t
   // enters the product exactly as given. T is lower triangular, so rows
   // 0..31 need only positions 0..31.
   {
+    // T diag(beta) as bf16 fragments: row 16 pb + m, positions 32 kb + 8 g
+    // .. +7, read as two 16-byte pieces of at (T strictly below the
+    // diagonal; the diagonal and above are masked by index).
     bf16x8 Tf[4][2];
 #pragma unroll
     for (int pb = 0; pb < 4; ++pb)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        float tv[8];
         const int row = 16 * pb + m;
+        const int c0 = 32 * kb + 8 * g;
+        const f32x4 t0 = *reinterpret_cast<const f32x4*>(&sm.at[sw32<C>(row, c0)]);
+        const f32x4 t1 = *reinterpret_cast<const f32x4*>(&sm.at[sw32<C>(row, c0 + 4)]);
+        const f32x4 b0 = *reinterpret_cast<const f32x4*>(&beta_l[c0]);
+        const f32x4 b1 = *reinterpret_cast<const f32x4*>(&beta_l[c0 + 4]);
+        float tv[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const int col = 32 * kb + 8 * g + j;
-          const float bcol = sm.at[sw32<C>(col, col)];
-          tv[j] = (col < row ? sm.at[sw32<C>(row, col)] : (col == row ? 1.f : 0.f)) * bcol;
+          const int col = c0 + j;
+          const float tval = j < 4 ? t0[j] : t1[j - 4];
+          const float bcol = j < 4 ? b0[j] : b1[j - 4];
+          tv[j] = (col < row ? tval : (col == row ? 1.f : 0.f)) * bcol;
         }
         Tf[pb][kb] = to_bf16x8(tv);
       }
-    // -W staged in sm.q (plain row-major, channels permuted).
-    for (int nb = w; nb < K / 16; nb += 4) {
-      const int wch = 16 * nb + m;
-      bf16x8 Bf[2];
+    // -W^T = -(K o e^gam)^T (T diag(beta))^T: the same fragments with the
+    // operands swapped leave lane (m, g) four consecutive channels
+    // 16 nb + 4 g .. +3 of position 16 pb + m, which are four consecutive
+    // slots of the record's permuted channel order: one 8-byte store each.
+    {
+      const __amdgpu_buffer_rsrc_t rwn = make_rsrc(rec + R::Wn, static_cast<uint32_t>(C * K * 2));
+      typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+      for (int nb = w; nb < K / 16; nb += 4) {
+        bf16x8 Bf[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) Bf[kb] = frag<C>(wkt, wch, 32 * kb + 8 * g);
+        for (int kb = 0; kb < 2; ++kb) Bf[kb] = frag<C>(wkt, 16 * nb + m, 32 * kb + 8 * g);
+        const int col = 32 * (nb >> 1) + 8 * g + 4 * (nb & 1);
 #pragma unroll
-      for (int pb = 0; pb < 4; ++pb) {
-        f32x4 D = mfma16(Tf[pb][0], Bf[0], f32x4{0.f, 0.f, 0.f, 0.f});
-        if (pb >= 2) D = mfma16(Tf[pb][1], Bf[1], D);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int row = 16 * pb + 4 * g + j;
-          const int col = 32 * (nb >> 1) + perm_slot(16 * (nb & 1) + m);
-          sm.q[row * K + col] = bf16_bits(-D[j]);
+        for (int pb = 0; pb < 4; ++pb) {
+          f32x4 D = mfma16(Bf[0], Tf[pb][0], f32x4{0.f, 0.f, 0.f, 0.f});
+          if (pb >= 2) D = mfma16(Bf[1], Tf[pb][1], D);
+          const u32x2 v = {pack_bf16x2(-D[0], -D[1]), pack_bf16x2(-D[2], -D[3])};
+          __builtin_amdgcn_raw_buffer_store_b64(v, rwn, rec_elem<K>(16 * pb + m, col) * 2, 0, 0);
         }
       }
     }
@@ -1061,14 +1078,6 @@ __device__ __forceinline__ void intra_body(const PrefillParams& p, const int32_t
         uf[(pb * (V / 16) + nb) * 64 + lane] = D;
       }
     }
-  }
-  lds_barrier();
-
-  // ---- 8. -W -> workspace ----------------------------------------------
-  {
-    uint16_t* wn = reinterpret_cast<uint16_t*>(rec + R::Wn);
-    for (int e = tid; e < C * KP8; e += kThreads)
-      *reinterpret_cast<uint4*>(wn + rec_elem<K>(e / KP8, (e % KP8) * 8)) = *reinterpret_cast<const uint4*>(&sm.q[e * 8]);
   }
 }
 
