@@ -1155,16 +1155,22 @@ __device__ __forceinline__ void chunk_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int K, int V>
-__global__ __launch_bounds__(kThreads, 1) void chunk_state_kernel(const PrefillParams p,
-                                                                  const SegPlan pl,
-                                                                  const char* recs) {
+// NB = 2: the next chunk's record is copied into the second LDS buffer while
+// the current one computes (one workgroup per CU at K = V = 128). NB = 1: one
+// buffer, refilled once every wave has read it, so two workgroups share a CU
+// and each one's copies overlap the other's MFMA phases; the host takes it
+// when there are enough workgroups to give every CU two.
+template <int K, int V, int NB>
+__global__ __launch_bounds__(kThreads, NB == 1 ? 2 : 1) void chunk_state_kernel(const PrefillParams p,
+                                                                                const SegPlan pl,
+                                                                                const char* recs) {
   using R = Rec<K, V>;
   using B = StateBuf<K, V>;
   static_assert(sizeof(B) == R::lds_part, "LDS image is the record's first lds_part bytes");
   static_assert(R::lds_part % 16 == 0, "record LDS part must be whole 16-byte pieces");
+  static_assert(NB == 1 || NB == 2, "one or two record buffers");
   constexpr int NVH = V / 64;  // workgroups per (segment, head): 64 columns each
-  __shared__ B buf[2];
+  __shared__ B buf[NB];
 
   // The NVH workgroups of one (segment, head) read the same records: give
   // them indices that are equal modulo 8 so they run on the same XCD (one L2).
@@ -1324,15 +1330,15 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_state_kernel(const PrefillP
   // channels col0 + 4 g .. + 3 of position 16 pb + m: 8 contiguous bytes.
   const int out_lane = static_cast<int>(m * HV + h * V + col0 + 4 * g) * 2;
   for (int cc = 0; cc < nch; ++cc) {
-    const B& bf = buf[cc & 1];
-    // Chunk cc's buffer is complete once every wave's copy has landed; the
-    // barrier also means every wave is done with chunk cc-1's buffer, which
-    // the next copy overwrites.
+    const B& bf = buf[NB == 2 ? (cc & 1) : 0];
+    // Chunk cc's buffer is complete once every wave's copy has landed; with
+    // two buffers the barrier also means every wave is done with chunk
+    // cc-1's buffer, which the next copy overwrites.
     chunk_barrier();
     f32x4 Vp[4];
 #pragma unroll
     for (int pb = 0; pb < 4; ++pb) Vp[pb] = Upre[pb];
-    if (cc + 1 < nch) {
+    if (NB == 2 && cc + 1 < nch) {
       dma_chunk<K, V, kThreads>(rec_of(cc + 1), &buf[(cc + 1) & 1], tid, wave);
       load_u(cc + 1);
     }
@@ -1407,15 +1413,18 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_state_kernel(const PrefillP
     }
     // Rows of the chunk as one buffer range: positions past its end fall
     // outside and their stores are dropped, so every lane issues exactly
-    // kOutStores stores.
-    const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.out + t0 * HV, static_cast<uint32_t>(n * HV * 2));
+    // kOutStores stores, the last vector-memory operations of the chunk.
+    auto store_out = [&]() {
+      const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.out + t0 * HV, static_cast<uint32_t>(n * HV * 2));
 #pragma unroll
-    for (int pb = 0; pb < 4; ++pb) {
-      const uint32_t lo = pack_bf16x2(Ot[pb][0], Ot[pb][1]);
-      const uint32_t hi = pack_bf16x2(Ot[pb][2], Ot[pb][3]);
-      typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-      __builtin_amdgcn_raw_buffer_store_b64(u32x2{lo, hi}, ro, out_lane + static_cast<int>(16 * pb * HV * 2), 0, 0);
-    }
+      for (int pb = 0; pb < 4; ++pb) {
+        const uint32_t lo = pack_bf16x2(Ot[pb][0], Ot[pb][1]);
+        const uint32_t hi = pack_bf16x2(Ot[pb][2], Ot[pb][3]);
+        typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{lo, hi}, ro, out_lane + static_cast<int>(16 * pb * HV * 2), 0, 0);
+      }
+    };
+    if constexpr (NB == 2) store_out();
     // S <- diag(e^{gam_last}) S + (K o e^{gam_last - gam})^T V'.
 #pragma unroll
     for (int cb = 0; cb < K / 16; ++cb) {
@@ -1424,6 +1433,16 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_state_kernel(const PrefillP
       for (int j = 0; j < 4; ++j) S[cb][j] *= e[j];
       S[cb] = mfma16(kf[cb][0], Vb0, S[cb]);
       S[cb] = mfma16(kf[cb][1], Vb1, S[cb]);
+    }
+    if constexpr (NB == 1) {
+      // Every wave's reads of the buffer are done: refill it with the next
+      // chunk, then store this chunk's output rows.
+      if (cc + 1 < nch) {
+        lds_barrier();
+        dma_chunk<K, V, kThreads>(rec_of(cc + 1), &buf[0], tid, wave);
+        load_u(cc + 1);
+      }
+      store_out();
     }
   }
 
@@ -1654,8 +1673,15 @@ hipError_t launch_kv(const PrefillParams& p, const Layout& L, const SegPlan& pl,
   if (L.map_bound > 0) {
     chunk_map_kernel<K, V><<<dim3(static_cast<unsigned>(map_blocks)), dim3(kMapThreads), 0, stream>>>(p, pl, recs);
   }
-  chunk_state_kernel<K, V><<<dim3(static_cast<unsigned>(state_blocks)), dim3(kThreads), 0, stream>>>(
-      p, pl, recs);
+  // Every sequence is at least one segment: with enough of them for two
+  // state workgroups per CU, one record buffer per workgroup lets two share
+  // a CU.
+  if (static_cast<int64_t>(p.num_seqs) * p.H * (V / 64) >= 2 * kChipSlots)
+    chunk_state_kernel<K, V, 1><<<dim3(static_cast<unsigned>(state_blocks)), dim3(kThreads), 0, stream>>>(
+        p, pl, recs);
+  else
+    chunk_state_kernel<K, V, 2><<<dim3(static_cast<unsigned>(state_blocks)), dim3(kThreads), 0, stream>>>(
+        p, pl, recs);
   return hipGetLastError();
 }
 

@@ -79,6 +79,15 @@ def test_prefill_cut_sequences_with_flags_and_null_slot():
     check_case(case, PREFILL_TOL_O, PREFILL_TOL_S)
 
 
+def test_prefill_many_sequences_with_a_cut_one():
+    """Enough sequences for the one-buffer state pass (16 sequences x 16
+    heads x 2 column halves = 512 workgroups, two per CU), one of them long
+    enough (47 chunks) to be cut into three segments."""
+    lens = [3000, 1, 64, 65, 17, 130, 2, 90, 33, 127, 5, 64, 200, 1, 48, 77]
+    case = W.prefill_case("one_buffer_cut", 16, 128, 128, lens, 24, -5.0, seed=681, std=0.1)
+    check_case(case, PREFILL_TOL_O, PREFILL_TOL_S)
+
+
 def test_prefill_cut_sequence_is_deterministic():
     case = W.prefill_case("det_cut", 2, 128, 128, [4000, 40], 4, -5.0, seed=671)
     results = []
