@@ -1464,9 +1464,10 @@ struct MapBuf {
   float eg[K];
 };
 
-// One workgroup per (map item, head, 128 columns of [M | B]), 32 columns
-// (two MFMA column tiles) per wave, so that each operand fragment read from
-// LDS feeds two MFMAs: runs the chunk recurrence of one non-final segment
+// One workgroup per (map item, head, 64 columns of [M | B]), one 16-column
+// MFMA tile per wave. (Two tiles per wave, each LDS fragment feeding two
+// MFMAs, measured 5 % slower: half as many workgroups, each with longer
+// chains per chunk.) Runs the chunk recurrence of one non-final segment
 // (all of its chunks are full) from S = the identity's columns with U = 0
 // (columns of M) or from S = 0 with the chunk's U (columns of B). There is
 // no output; the rounding is the state pass's (bf16 S into W S, bf16 V' into
@@ -1475,7 +1476,7 @@ struct MapBuf {
 // all belong to M or all to B).
 constexpr int kMapWaves = 4;
 constexpr int kMapThreads = kMapWaves * 64;
-constexpr int kMapCT = 2;  // 16-column tiles per wave
+constexpr int kMapCT = 1;  // 16-column tiles per wave
 
 template <int K, int V>
 __global__ __launch_bounds__(kMapThreads, 2) void chunk_map_kernel(const PrefillParams p,
@@ -1554,19 +1555,23 @@ __global__ __launch_bounds__(kMapThreads, 2) void chunk_map_kernel(const Prefill
   // slot that the last of them writes. The waves with columns of B cover
   // every value column once.
   if (takes_u && mi == seg0 - seq) {
-    // Lane l copies 4 consecutive columns of rows l/8, l/8 + 8, ... of the
-    // wave's 32 columns; every load is issued before the first store.
+    // Lane l copies 4 consecutive columns of the wave's WCOLS columns in
+    // every 64 / (WCOLS / 4)-th row; every load is issued before the first
+    // store.
     const int li = uniform(pl.seg_long[gs]);
     const bool init = p.has_initial_state == nullptr || uniform(static_cast<int32_t>(p.has_initial_state[seq])) != 0;
     const float* src = p.pool + slot * p.slot_stride + static_cast<int64_t>(h) * K * V;
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, init ? static_cast<uint32_t>(K * V * 4) : 0u);
     const __amdgpu_buffer_rsrc_t rd = make_rsrc(pl.s0 + s0_index(h, li, pl) * K * V, static_cast<uint32_t>(K * V * 4));
-    const int lane_off = ((lane >> 3) * V + col0 + 4 * (lane & 7)) * 4;
-    f32x4 cp[K / 8];
+    constexpr int LPR = WCOLS / 4;  // lanes per row
+    constexpr int RPP = 64 / LPR;   // rows per pass
+    static_assert(K % RPP == 0, "whole passes");
+    const int lane_off = ((lane / LPR) * V + col0 + 4 * (lane % LPR)) * 4;
+    f32x4 cp[K / RPP];
 #pragma unroll
-    for (int i = 0; i < K / 8; ++i) cp[i] = buffer_load_f32x4<0>(rs, lane_off, i * 8 * V * 4);
+    for (int i = 0; i < K / RPP; ++i) cp[i] = buffer_load_f32x4<0>(rs, lane_off, i * RPP * V * 4);
 #pragma unroll
-    for (int i = 0; i < K / 8; ++i) buffer_store_f32x4<0>(cp[i], rd, lane_off, i * 8 * V * 4);
+    for (int i = 0; i < K / RPP; ++i) buffer_store_f32x4<0>(cp[i], rd, lane_off, i * RPP * V * 4);
   }
   dma(0, &buf[0]);
   if (takes_u) load_u(0);
