@@ -79,6 +79,8 @@ void check_common(Checks& c, int64_t rows, int32_t H, int32_t K, int32_t V,
       c.require(qkv_row_stride >= 2 * static_cast<int64_t>(H) * K + static_cast<int64_t>(H) * V, INV,
                 "qkv_row_stride must be >= 2*H*K + H*V");
     c.require(qkv_row_stride % 8 == 0, UNS, "qkv_row_stride must be a multiple of 8");
+    c.require(qkv_row_stride <= (int64_t{1} << 24), UNS,
+              "qkv_row_stride must be <= 2^24 (kernels address 64 rows with 32-bit offsets)");
     c.require(aligned(mixed_qkv, 16), UNS, "mixed_qkv must be 16-byte aligned");
     c.require(aligned(raw_g, 16), UNS, "raw_g must be 16-byte aligned");
     c.require(aligned(raw_beta, 2), UNS, "raw_beta must be 2-byte aligned");

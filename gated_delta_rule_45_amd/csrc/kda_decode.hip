@@ -28,8 +28,9 @@
 //   u = beta (v - S'^T k),   o = scale (S'^T q + u (k.q)),   S = S' + k u^T
 // which is the decay / delta-write / readout order in one pass over the tile.
 // The K-reductions are a per-lane partial, a butterfly over the wave's row
-// groups, and a sum of the four waves' partials through LDS (one barrier per
-// token; the partial buffer alternates between tokens).
+// groups (DPP rotations and lane swaps, no LDS traffic), and a sum of the
+// four waves' partials through LDS (one barrier per token; the partial
+// buffer alternates between tokens).
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -39,6 +40,27 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kMaxTokens = 8;
+
+// Sum of x over the lanes that share lane % CG (CG = 4, 8, 16 or 32): a
+// butterfly on VALU lane permutations, no LDS traffic. Inside a 16-lane row
+// the lanes l, l + CG, ... mod 16 are summed by DPP rotations of the row;
+// the rows are then combined by swaps of rows 1, 3 with rows 0, 2
+// (v_permlane16_swap) and of the two halves (v_permlane32_swap). Every
+// lane must be active.
+template <int CG>
+__device__ __forceinline__ float sum_row_groups(float x) {
+  static_assert(CG == 4 || CG == 8 || CG == 16 || CG == 32, "column groups");
+  if constexpr (CG == 4)
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xf, 0xf, false));  // row_ror:4
+  if constexpr (CG <= 8)
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false));  // row_ror:8
+  if constexpr (CG <= 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 }  // namespace
 
@@ -153,14 +175,11 @@ void decode_kernel(const DecodeParams p) {
       kq = fmaf(kk, qq, kq);
     }
 #pragma unroll
-    for (int off = CG; off < 64; off <<= 1) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        kS[c] += __shfl_xor(kS[c], off);
-        qS[c] += __shfl_xor(qS[c], off);
-      }
-      kq += __shfl_xor(kq, off);
+    for (int c = 0; c < 4; ++c) {
+      kS[c] = sum_row_groups<CG>(kS[c]);
+      qS[c] = sum_row_groups<CG>(qS[c]);
     }
+    kq = sum_row_groups<CG>(kq);
     float(*red)[2 * VT + 4] = s_red[t & 1];
     if (rg == 0) {
 #pragma unroll

@@ -34,7 +34,8 @@
  *  - bf16 outputs are rounded to nearest even; the state stays fp32.
  *  - Supported head dims: K, V in {64, 128}. Layout alignment: mixed_qkv, raw_g,
  *    out and the pool must be 16-byte aligned, qkv_row_stride a multiple of 8
- *    and slot_stride a multiple of 4 elements.
+ *    and at most 2^24 elements (kernels address up to 64 rows with 32-bit
+ *    byte offsets), and slot_stride a multiple of 4 elements.
  */
 #ifndef KDA_H
 #define KDA_H

@@ -140,6 +140,8 @@ def test_alignment_and_strides_are_unsupported_not_invalid():
     assert st == 2 and "multiple of 8" in msg
     st, msg = _decode(stride=100)
     assert st == 1 and "qkv_row_stride" in msg
+    st, msg = _decode(stride=(1 << 24) + 8)
+    assert st == 2 and "qkv_row_stride must be <= 2^24" in msg
 
 
 def test_slot_stride_too_small():
