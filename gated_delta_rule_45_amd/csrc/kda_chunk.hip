@@ -595,6 +595,7 @@ __device__ __forceinline__ void intra_body(const PrefillParams& p, const int32_t
     const __amdgpu_buffer_rsrc_t rqg = make_rsrc(rec + R::Qg, static_cast<uint32_t>(C * K * 2));
     const __amdgpu_buffer_rsrc_t rkg = make_rsrc(rec + R::KgT, static_cast<uint32_t>(K * C * 2));
     const int qcol = 32 * (ch >> 5) + perm_slot(ch & 31);
+    float wk_even = 0.f;
 #pragma unroll
     for (int b = 0; b < NBP; ++b) {
       const float rho = gm[16 * b];
@@ -624,9 +625,9 @@ __device__ __forceinline__ void intra_body(const PrefillParams& p, const int32_t
           sm.u.f.kf[o] = bf16_bits(kf);
           __builtin_amdgcn_raw_buffer_store_b16(bf16_bits(p.scale * qr * E), rqg, rec_elem<K>(t, qcol) * 2, 0, 0);
           kgv[i3] = kf * G;
-          const uint32_t wk = bf16_bits(kr * E);
-          if (i & 1) wkp[i >> 1] |= wk << 16;
-          else wkp[i >> 1] = wk;
+          // Position pairs share one conversion.
+          if (i & 1) wkp[i >> 1] = pack_bf16x2(wk_even, kr * E);
+          else wk_even = kr * E;
         }
         // (K o e^{gl - gam})^T: 4 consecutive positions are 8 contiguous
         // bytes of the permuted order.
@@ -657,23 +658,36 @@ __device__ __forceinline__ void intra_body(const PrefillParams& p, const int32_t
         float bt[4];  // beta of the lane's rows (on the diagonal of at)
 #pragma unroll
         for (int j = 0; j < 4; ++j) bt[j] = sm.at[sw32<C>(16 * I + 4 * g + j, 16 * I + 4 * g + j)];
-        f32x4 dA = {0.f, 0.f, 0.f, 0.f}, dP = {0.f, 0.f, 0.f, 0.f};
+        // Every fragment of the block is read before the first product, so
+        // the reads overlap instead of waiting one channel slice at a time.
+        bf16x8 ak[K / 32], aq[K / 32], b[K / 32];
 #pragma unroll
         for (int kb = 0; kb < K / 32; ++kb) {
           const int c0 = 32 * kb + 8 * g;
-          const bf16x8 ak = lds_frag(&sm.k[sw16<K>(16 * I + m, c0)]);
-          const bf16x8 aq = lds_frag(&sm.q[sw16<K>(16 * I + m, c0)]);
-          const bf16x8 bk = lds_frag(&sm.u.f.kf[sw16<K>(16 * J + m, c0)]);
-          const f32x4 c0v = *reinterpret_cast<const f32x4*>(cv + c0);
-          const f32x4 c1v = *reinterpret_cast<const f32x4*>(cv + c0 + 4);
-          bf16x8 b = bk;
-          if (J < I) {
+          ak[kb] = lds_frag(&sm.k[sw16<K>(16 * I + m, c0)]);
+          aq[kb] = lds_frag(&sm.q[sw16<K>(16 * I + m, c0)]);
+          b[kb] = lds_frag(&sm.u.f.kf[sw16<K>(16 * J + m, c0)]);
+        }
+        if (J < I) {  // wave-uniform
+          f32x4 cf[K / 32][2];
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-              b[j] = static_cast<__bf16>(static_cast<float>(bk[j]) * (j < 4 ? c0v[j] : c1v[j - 4]));
+          for (int kb = 0; kb < K / 32; ++kb) {
+            cf[kb][0] = *reinterpret_cast<const f32x4*>(cv + 32 * kb + 8 * g);
+            cf[kb][1] = *reinterpret_cast<const f32x4*>(cv + 32 * kb + 8 * g + 4);
           }
-          dA = mfma16(ak, b, dA);
-          dP = mfma16(aq, b, dP);
+#pragma unroll
+          for (int kb = 0; kb < K / 32; ++kb) {
+            float sc[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) sc[j] = static_cast<float>(b[kb][j]) * cf[kb][j >> 2][j & 3];
+            b[kb] = to_bf16x8(sc);
+          }
+        }
+        f32x4 dA = {0.f, 0.f, 0.f, 0.f}, dP = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < K / 32; ++kb) {
+          dA = mfma16(ak[kb], b[kb], dA);
+          dP = mfma16(aq[kb], b[kb], dP);
         }
         // Lane holds rows 16 I + 4 g + j of column s = 16 J + m. Every entry
         // is written without a branch: beta stays on the diagonal, and the
@@ -1673,8 +1687,14 @@ hipError_t launch_kv(const PrefillParams& p, const Layout& L, const SegPlan& pl,
     return hipErrorInvalidValue;
   chunk_intra_kernel<K, V><<<dim3(static_cast<unsigned>(intra_blocks)), dim3(kThreads), 0, stream>>>(
       p, pl.chunk_start, recs, exact_flags);
-  chunk_intra_exact_kernel<K, V><<<dim3(static_cast<unsigned>(intra_blocks)), dim3(kThreads), 0, stream>>>(
-      p, pl.chunk_start, recs, exact_flags);
+  // With a lower bound lb every per-token log-decay lies in [lb, 0], so a
+  // 16-row block decays by at most 15 |lb| and the factored kernel takes
+  // every chunk once 15 |lb| <= kMaxBlockDecay: the exact kernel would only
+  // read its flags and return.
+  const bool all_factored = p.has_lb != 0 && 15.f * -p.lower_bound <= kMaxBlockDecay - 1.f;
+  if (!all_factored)
+    chunk_intra_exact_kernel<K, V><<<dim3(static_cast<unsigned>(intra_blocks)), dim3(kThreads), 0, stream>>>(
+        p, pl.chunk_start, recs, exact_flags);
   if (L.map_bound > 0) {
     chunk_map_kernel<K, V><<<dim3(static_cast<unsigned>(map_blocks)), dim3(kMapThreads), 0, stream>>>(p, pl, recs);
   }

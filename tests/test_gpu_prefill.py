@@ -32,6 +32,16 @@ def test_ragged_prefill(K, V, lower_bound):
     check_case(case, PREFILL_TOL_O, PREFILL_TOL_S)
 
 
+@pytest.mark.parametrize("lower_bound", [-5.3, -12.0])
+def test_prefill_steep_lower_bound(lower_bound):
+    """A bound steep enough that a 16-row block can decay by more than the
+    factored path allows (15 |lb| > 79): the host must still launch the
+    exact-path kernel for the chunks the factored one hands over."""
+    case = W.prefill_case(f"steep_lb{lower_bound}", 3, 128, 128, RAGGED, 16, lower_bound,
+                          seed=607, std=0.1, scale=1.0 / math.sqrt(128))
+    check_case(case, PREFILL_TOL_O, PREFILL_TOL_S)
+
+
 def test_prefill_initial_state_flags_null_slot_and_empty_sequence():
     lens = [70, 0, 33, 1, 128]
     case = W.prefill_case("flags", 4, 128, 128, lens, 12, -5.0, seed=611, std=0.2,
