@@ -396,10 +396,10 @@ struct IntraSmem {
 // Layout of the x scratch (in floats).
 template <int K>
 struct XLayout {
-  static constexpr int PARTS = kThreads / K;  // threads per channel in the gate scan
+  static constexpr int PARTS = kThreads / (K / 4);  // threads per channel quad in the gate scan
   static constexpr int tot = 0;               // [PARTS][K] partial sums of the gate scan
   static constexpr int bnd = tot + PARTS * K; // [4][K] gam at rows 16 I
-  static constexpr int dmax = bnd + 4 * K;    // [4 blocks][2] largest decay range per wave
+  static constexpr int dmax = bnd + 4 * K;    // [4 blocks] largest decay range
   static constexpr int cij = dmax + 16;       // [10][K] e^{gam(16 I) - gam(16 J)}, J <= I
   static constexpr int end = cij + 10 * K;
   static_assert(end <= C * K / 2, "x scratch overflows its area");
@@ -494,82 +494,113 @@ __device__ __forceinline__ void intra_body(const PrefillParams& p, const int32_t
     }
   }
   // Per-head gate parameters and beta, loaded while the copies are in flight.
-  constexpr int PARTS = XLayout<K>::PARTS;
-  const int ch = tid % K, part = tid / K;
+  // Thread (q4, part) owns channels 4 q4 .. 4 q4 + 3 at positions
+  // part PP .. part PP + PP - 1: its tile reads and writes are 8 bytes wide,
+  // and wave w holds exactly the 16-row block w.
+  constexpr int NQ = K / 4;              // channel quads
+  constexpr int NPART = XL::PARTS;       // 8 at K = 128, 16 at K = 64
+  constexpr int PP = C / NPART;          // positions per thread: 8 or 4
+  static_assert(NPART * PP == C && (64 / NQ) * PP == 16 && PP % 4 == 0, "a wave holds one 16-row block");
+  const int q4 = tid % NQ, part = tid / NQ;
+  const int c4 = 4 * q4;                 // the thread's first channel
   const float a_h = __expf(p.A_log[h]);
-  const float dtb = p.dt_bias[h * K + ch];
+  float dtb[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) dtb[j] = p.dt_bias[h * K + c4 + j];
   const float beta_t = (tid < n) ? sigmoid_f32(bf16_to_f32(p.raw_beta[(t0 + tid) * H + h])) : 0.f;
   wait_vmem();
   __syncthreads();
 
   // ---- 2. gate and cumulative log-decay, in registers ---------------------
-  // Thread (ch, part) scans PP consecutive positions of channel ch; partial
-  // totals are added across parts through x.
-  constexpr int PP = C / PARTS;          // 32 at K = 128, 16 at K = 64
-  constexpr int NBP = PP / 16;           // 16-row blocks per part
-  constexpr int WPP = K / 64;            // waves per part
-  static_assert(PP % 16 == 0, "parts hold whole blocks");
-  float gm[PP];
-  float before = 0.f, gl = 0.f;
+  // Each thread scans its PP positions; partial totals are added across
+  // parts through x.
+  float gm[PP][4];
+  float gl[4] = {0.f, 0.f, 0.f, 0.f};
   {
     const float a = a_h;
     const bool has_lb = p.has_lb != 0;
     // All reads first (rows past the chunk end hold zeros), then a
     // branch-free scan; padded positions do not decay, so row 63 holds
     // gam_last.
-    float rg[PP];
+    float rg[PP][4];
 #pragma unroll
-    for (int i = 0; i < PP; ++i) rg[i] = bf16_to_f32(rawg[sw16<K>(part * PP + i, ch)]);
-    float acc = 0.f;
+    for (int i = 0; i < PP; ++i) {
+      const uint2 wv = *reinterpret_cast<const uint2*>(&rawg[sw16<K>(part * PP + i, c4)]);
+      rg[i][0] = __uint_as_float(wv.x << 16);
+      rg[i][1] = __uint_as_float(wv.x & 0xffff0000u);
+      rg[i][2] = __uint_as_float(wv.y << 16);
+      rg[i][3] = __uint_as_float(wv.y & 0xffff0000u);
+    }
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
     if (has_lb) {
 #pragma unroll
       for (int i = 0; i < PP; ++i) {
-        const float gv = p.lower_bound * sigmoid_f32(a * (rg[i] + dtb));
-        acc += part * PP + i < n ? gv : 0.f;
-        gm[i] = acc;
+        const bool live = part * PP + i < n;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float gv = p.lower_bound * sigmoid_f32(a * (rg[i][j] + dtb[j]));
+          acc[j] += live ? gv : 0.f;
+          gm[i][j] = acc[j];
+        }
       }
     } else {
 #pragma unroll
       for (int i = 0; i < PP; ++i) {
-        const float gv = -a * softplus_f32(rg[i] + dtb);
-        acc += part * PP + i < n ? gv : 0.f;
-        gm[i] = acc;
+        const bool live = part * PP + i < n;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float gv = -a * softplus_f32(rg[i][j] + dtb[j]);
+          acc[j] += live ? gv : 0.f;
+          gm[i][j] = acc[j];
+        }
       }
     }
-    x[XL::tot + part * K + ch] = acc;
+    *reinterpret_cast<f32x4*>(&x[XL::tot + part * K + c4]) = f32x4{acc[0], acc[1], acc[2], acc[3]};
     lds_barrier();  // raw_g consumed; partial totals visible
+    float before[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int q2 = 0; q2 < PARTS; ++q2) {
-      const float tq = x[XL::tot + q2 * K + ch];
-      if (q2 < part) before += tq;
-      gl += tq;
+    for (int q2 = 0; q2 < NPART; ++q2) {
+      const f32x4 tq = *reinterpret_cast<const f32x4*>(&x[XL::tot + q2 * K + c4]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (q2 < part) before[j] += tq[j];
+        gl[j] += tq[j];
+      }
     }
     if (tid < C) sm.at[sw32<C>(tid, tid)] = beta_t;  // beta on the diagonal of at
 #pragma unroll
-    for (int i = 0; i < PP; ++i) gm[i] += before;
-    // Block bounds and decay ranges (a range is the same before and after
-    // adding the offset of earlier parts).
+    for (int i = 0; i < PP; ++i)
 #pragma unroll
-    for (int b = 0; b < NBP; ++b) {
-      const int I = part * NBP + b;
-      x[XL::bnd + I * K + ch] = gm[16 * b];
-      float d = gm[16 * b] - gm[16 * b + 15];
+      for (int j = 0; j < 4; ++j) gm[i][j] += before[j];
+    // Block w's bound gam(16 w) is row 0 of the wave's first part (lanes
+    // 0 .. NQ-1); its row 15 is the last row of the wave's last part, in
+    // lane + 64 - NQ. The decay range is gam(16 w) - gam(16 w + 15).
+    float d = 0.f;
+    {
+      float last[4];
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) d = fmaxf(d, __shfl_xor(d, off));
-      if (lane == 0) x[XL::dmax + 2 * I + (w % WPP)] = d;
+      for (int j = 0; j < 4; ++j) last[j] = __shfl_xor(gm[PP - 1][j], 64 - NQ);
+      if (lane < NQ) {
+        *reinterpret_cast<f32x4*>(&x[XL::bnd + w * K + c4]) = f32x4{gm[0][0], gm[0][1], gm[0][2], gm[0][3]};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) d = fmaxf(d, gm[0][j] - last[j]);
+      }
     }
-    if (part == 0) reinterpret_cast<float*>(rec + R::Eg)[ch] = __expf(gl);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) d = fmaxf(d, __shfl_xor(d, off));
+    if (lane == 0) x[XL::dmax + w] = d;
+    if (part == 0)
+      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(rec + R::Eg) + c4) =
+          f32x4{__expf(gl[0]), __expf(gl[1]), __expf(gl[2]), __expf(gl[3])};
   }
   lds_barrier();
   bool fast = true;
 #pragma unroll
-  for (int I = 0; I < 4; ++I)
-#pragma unroll
-    for (int v = 0; v < WPP; ++v) fast = fast && x[XL::dmax + 2 * I + v] <= kMaxBlockDecay;
+  for (int I = 0; I < 4; ++I) fast = fast && x[XL::dmax + I] <= kMaxBlockDecay;
 
-  // K o e^gam of this thread's positions, as bf16 pairs, kept in registers
-  // until x is free.
-  uint32_t wkp[PP / 2];
+  // K o e^gam of this thread's channels and positions, as bf16 pairs, kept
+  // in registers until x is free.
+  uint32_t wkp[4][PP / 2];
 
   if constexpr (!kExact) {
     if (tid == 0) *flag = fast ? 0 : 1;
@@ -594,49 +625,70 @@ __device__ __forceinline__ void intra_body(const PrefillParams& p, const int32_t
     // per-store 64-bit address arithmetic.
     const __amdgpu_buffer_rsrc_t rqg = make_rsrc(rec + R::Qg, static_cast<uint32_t>(C * K * 2));
     const __amdgpu_buffer_rsrc_t rkg = make_rsrc(rec + R::KgT, static_cast<uint32_t>(K * C * 2));
-    const int qcol = 32 * (ch >> 5) + perm_slot(ch & 31);
-    float wk_even = 0.f;
+    // The thread's block is the wave's: rho = gam(16 w) per channel.
+    const f32x4 rho = *reinterpret_cast<const f32x4*>(&x[XL::bnd + w * K + c4]);
+    float E[4], sE[4], G[4];
 #pragma unroll
-    for (int b = 0; b < NBP; ++b) {
-      const float rho = gm[16 * b];
-      const float E = __expf(rho), G = __expf(gl - rho);
-      // The block's k and q first: the in-place writes below would otherwise
-      // keep the compiler from moving later reads ahead of them.
-      uint16_t kb16[16], qb16[16];
+    for (int j = 0; j < 4; ++j) {
+      E[j] = __expf(rho[j]);
+      sE[j] = p.scale * E[j];
+      G[j] = __expf(gl[j] - rho[j]);
+    }
+    // The four channels are four consecutive slots of the record's permuted
+    // channel order.
+    const int r8 = (c4 & 31) >> 2;
+    const int qcol = 32 * (c4 >> 5) + 8 * (r8 & 3) + 4 * (r8 >> 2);
+    // Every k and q read first: the in-place writes below would otherwise
+    // keep the compiler from moving later reads ahead of them.
+    uint2 kq[PP], qq[PP];
 #pragma unroll
-      for (int i2 = 0; i2 < 16; ++i2) {
-        const int o = sw16<K>(part * PP + 16 * b + i2, ch);
-        kb16[i2] = sm.k[o];
-        qb16[i2] = sm.q[o];
-      }
+    for (int i = 0; i < PP; ++i) {
+      const int o = sw16<K>(part * PP + i, c4);
+      kq[i] = *reinterpret_cast<const uint2*>(&sm.k[o]);
+      qq[i] = *reinterpret_cast<const uint2*>(&sm.q[o]);
+    }
+    float wk_even[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int u4 = 0; u4 < 4; ++u4) {
-        float kgv[4];
+    for (int u4 = 0; u4 < PP / 4; ++u4) {
+      float kgv[4][4];  // [channel][position]
 #pragma unroll
-        for (int i3 = 0; i3 < 4; ++i3) {
-          const int i = 16 * b + 4 * u4 + i3;
-          const int t = part * PP + i;
-          const int o = sw16<K>(t, ch);
-          const float kv = bf16_to_f32(kb16[4 * u4 + i3]), qv = bf16_to_f32(qb16[4 * u4 + i3]);
-          const float Rt = __expf(gm[i] - rho), Ft = __expf(rho - gm[i]);
-          const float kr = kv * Rt, qr = qv * Rt, kf = kv * Ft;
-          sm.k[o] = bf16_bits(kr);
-          sm.q[o] = bf16_bits(qr);
-          sm.u.f.kf[o] = bf16_bits(kf);
-          __builtin_amdgcn_raw_buffer_store_b16(bf16_bits(p.scale * qr * E), rqg, rec_elem<K>(t, qcol) * 2, 0, 0);
-          kgv[i3] = kf * G;
+      for (int i3 = 0; i3 < 4; ++i3) {
+        const int i = 4 * u4 + i3;
+        const int t = part * PP + i;
+        const int o = sw16<K>(t, c4);
+        const float kv[4] = {__uint_as_float(kq[i].x << 16), __uint_as_float(kq[i].x & 0xffff0000u),
+                             __uint_as_float(kq[i].y << 16), __uint_as_float(kq[i].y & 0xffff0000u)};
+        const float qv[4] = {__uint_as_float(qq[i].x << 16), __uint_as_float(qq[i].x & 0xffff0000u),
+                             __uint_as_float(qq[i].y << 16), __uint_as_float(qq[i].y & 0xffff0000u)};
+        float kr[4], qr[4], kf[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float Rt = __expf(gm[i][j] - rho[j]), Ft = __expf(rho[j] - gm[i][j]);
+          kr[j] = kv[j] * Rt;
+          qr[j] = qv[j] * Rt;
+          kf[j] = kv[j] * Ft;
+          kgv[j][i3] = kf[j] * G[j];
           // Position pairs share one conversion.
-          if (i & 1) wkp[i >> 1] = pack_bf16x2(wk_even, kr * E);
-          else wk_even = kr * E;
+          if (i & 1) wkp[j][i >> 1] = pack_bf16x2(wk_even[j], kr[j] * E[j]);
+          else wk_even[j] = kr[j] * E[j];
         }
-        // (K o e^{gl - gam})^T: 4 consecutive positions are 8 contiguous
-        // bytes of the permuted order.
-        const int tp = part * PP + 16 * b + 4 * u4;
-        const int pin = tp & 31;
-        const int slot0 = pin < 16 ? 2 * pin : 2 * (pin - 16) + 4;
+        *reinterpret_cast<uint2*>(&sm.k[o]) = uint2{pack_bf16x2(kr[0], kr[1]), pack_bf16x2(kr[2], kr[3])};
+        *reinterpret_cast<uint2*>(&sm.q[o]) = uint2{pack_bf16x2(qr[0], qr[1]), pack_bf16x2(qr[2], qr[3])};
+        *reinterpret_cast<uint2*>(&sm.u.f.kf[o]) = uint2{pack_bf16x2(kf[0], kf[1]), pack_bf16x2(kf[2], kf[3])};
         typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-        const u32x2 v = {pack_bf16x2(kgv[0], kgv[1]), pack_bf16x2(kgv[2], kgv[3])};
-        __builtin_amdgcn_raw_buffer_store_b64(v, rkg, rec_elem<C>(ch, 32 * (tp >> 5) + slot0) * 2, 0, 0);
+        const u32x2 qs = {pack_bf16x2(qr[0] * sE[0], qr[1] * sE[1]), pack_bf16x2(qr[2] * sE[2], qr[3] * sE[3])};
+        __builtin_amdgcn_raw_buffer_store_b64(qs, rqg, rec_elem<K>(t, qcol) * 2, 0, 0);
+      }
+      // (K o e^{gl - gam})^T: 4 consecutive positions are 8 contiguous
+      // bytes of the permuted order.
+      const int tp = part * PP + 4 * u4;
+      const int pin = tp & 31;
+      const int slot0 = pin < 16 ? 2 * pin : 2 * (pin - 16) + 4;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 v = {pack_bf16x2(kgv[j][0], kgv[j][1]), pack_bf16x2(kgv[j][2], kgv[j][3])};
+        __builtin_amdgcn_raw_buffer_store_b64(v, rkg, rec_elem<C>(c4 + j, 32 * (tp >> 5) + slot0) * 2, 0, 0);
       }
     }
     lds_barrier();
@@ -718,7 +770,8 @@ __device__ __forceinline__ void intra_body(const PrefillParams& p, const int32_t
     (void)fast;
     lds_barrier();  // every thread has read the decay ranges (gam overlays x)
 #pragma unroll
-    for (int i = 0; i < PP; ++i) sm.u.gam[sw32<K>(part * PP + i, ch)] = gm[i];
+    for (int i = 0; i < PP; ++i)
+      *reinterpret_cast<f32x4*>(&sm.u.gam[sw32<K>(part * PP + i, c4)]) = f32x4{gm[i][0], gm[i][1], gm[i][2], gm[i][3]};
     lds_barrier();
     // Exact path, elementwise outputs: Q o e^gam and (K o e^{gl-gam})^T.
     {
@@ -897,12 +950,20 @@ __device__ __forceinline__ void intra_body(const PrefillParams& p, const int32_t
     }
 
     // K o e^gam from the LDS tiles (k is unchanged on this path).
+    float wk_even[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < PP; ++i) {
       const int t = part * PP + i;
-      const uint32_t wk = bf16_bits(bf16_to_f32(sm.k[sw16<K>(t, ch)]) * __expf(sm.u.gam[sw32<K>(t, ch)]));
-      if (i & 1) wkp[i >> 1] |= wk << 16;
-      else wkp[i >> 1] = wk;
+      const uint2 kv = *reinterpret_cast<const uint2*>(&sm.k[sw16<K>(t, c4)]);
+      const f32x4 gv = *reinterpret_cast<const f32x4*>(&sm.u.gam[sw32<K>(t, c4)]);
+      const float kf[4] = {__uint_as_float(kv.x << 16), __uint_as_float(kv.x & 0xffff0000u),
+                           __uint_as_float(kv.y << 16), __uint_as_float(kv.y & 0xffff0000u)};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float val = kf[j] * __expf(gv[j]);
+        if (i & 1) wkp[j][i >> 1] = pack_bf16x2(wk_even[j], val);
+        else wk_even[j] = val;
+      }
     }
   }
   // v for the U phase, fetched now so its latency hides behind the inverse:
@@ -937,9 +998,12 @@ __device__ __forceinline__ void intra_body(const PrefillParams& p, const int32_t
 
   // ---- 4. (K o e^gam)^T into x: 16-byte pieces of 8 positions -----------
 #pragma unroll
-  for (int u8 = 0; u8 < PP / 8; ++u8)
-    *reinterpret_cast<uint4*>(wkt + rec_elem<C>(ch, part * PP + 8 * u8)) =
-        uint4{wkp[4 * u8], wkp[4 * u8 + 1], wkp[4 * u8 + 2], wkp[4 * u8 + 3]};
+  for (int j = 0; j < 4; ++j) {
+    if constexpr (PP == 8)
+      *reinterpret_cast<uint4*>(wkt + rec_elem<C>(c4 + j, part * PP)) = uint4{wkp[j][0], wkp[j][1], wkp[j][2], wkp[j][3]};
+    else
+      *reinterpret_cast<uint2*>(wkt + rec_elem<C>(c4 + j, part * PP)) = uint2{wkp[j][0], wkp[j][1]};
+  }
 
   // ---- 5. T = (I + A)^{-1}: diagonal blocks by forward substitution -----
   // at(s, t) = A[t][s] for s < t; T strictly below the diagonal of at.
