@@ -374,7 +374,7 @@ __device__ __forceinline__ int sw32(int t, int c) {
 //        x    fp32 scratch: part totals, gam at block starts, per-block
 //             decay ranges and the channel factors c_IJ until A/P is done;
 //             then (K o e^gam)^T, bf16 [K][C] (swz<C>), the B operand of W
-//  at  fp32 [C][C] (sw32)  raw_g (bf16 [C][K]) at load time; then A^T
+//  at  fp32 [C][C] (sw32)  A^T
 //                          strictly above the diagonal (at(s,t) = A[t][s]),
 //                          T = (I + A)^{-1} strictly below it (unit
 //                          diagonal implicit), beta on it
@@ -390,7 +390,6 @@ struct IntraSmem {
     } f;
   } u;
   float at[C * C];
-  static_assert(sizeof(float) * C * C >= sizeof(uint16_t) * C * K, "raw_g staging must fit in at");
 };
 
 // Layout of the x scratch (in floats).
@@ -468,32 +467,10 @@ __device__ __forceinline__ void intra_body(const PrefillParams& p, const int32_t
   float* x = sm.u.f.x;
   uint16_t* wkt = reinterpret_cast<uint16_t*>(sm.u.f.x);
 
-  // ---- 1. raw_g, k and q tiles by LDS DMA; rows past the chunk end read 0
-  uint16_t* rawg = reinterpret_cast<uint16_t*>(sm.at);
-  {
-    const int64_t rs = p.qkv_row_stride * 2;  // bytes per mixed_qkv row
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.qkv + t0 * p.qkv_row_stride, static_cast<uint32_t>(n * rs));
-    const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.raw_g + t0 * (H * K), static_cast<uint32_t>(n * H * K * 2));
-#pragma unroll
-    for (int r = 0; r < C * KP8 / kThreads; ++r) {
-      const int ps = r * kThreads + tid;          // physical piece in the tile
-      const int t = ps / KP8;
-      const int pl = (ps % KP8) ^ (t & KPM);      // logical piece stored there
-      const int slot = r * kThreads + (tid & ~63);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rg, reinterpret_cast<uint4*>(rawg) + slot, 16, (t * H * K + h * K + pl * 8) * 2, 0, 0, 0);
-    }
-#pragma unroll
-    for (int r = 0; r < C * KP8 / kThreads; ++r) {
-      const int ps = r * kThreads + tid;
-      const int t = ps / KP8;
-      const int pl = (ps % KP8) ^ (t & KPM);
-      const int slot = r * kThreads + (tid & ~63);
-      const int qoff = static_cast<int>(t * rs) + (h * K + pl * 8) * 2;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, reinterpret_cast<uint4*>(sm.q) + slot, 16, qoff, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, reinterpret_cast<uint4*>(sm.k) + slot, 16, qoff + H * K * 2, 0, 0, 0);
-    }
-  }
-  // Per-head gate parameters and beta, loaded while the copies are in flight.
+  // ---- 1. raw_g into registers, k and q tiles by LDS DMA -----------------
+  // Rows past the chunk end read 0. The thread's raw_g arrives in its own
+  // registers, so the gate scan waits only for those loads while the k and
+  // q copies keep landing under it.
   // Thread (q4, part) owns channels 4 q4 .. 4 q4 + 3 at positions
   // part PP .. part PP + PP - 1: its tile reads and writes are 8 bytes wide,
   // and wave w holds exactly the 16-row block w.
@@ -503,15 +480,41 @@ __device__ __forceinline__ void intra_body(const PrefillParams& p, const int32_t
   static_assert(NPART * PP == C && (64 / NQ) * PP == 16 && PP % 4 == 0, "a wave holds one 16-row block");
   const int q4 = tid % NQ, part = tid / NQ;
   const int c4 = 4 * q4;                 // the thread's first channel
-  const float a_h = __expf(p.A_log[h]);
-  float dtb[4];
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  u32x2 rgw[PP];
+  float a_h, dtb[4];
+  uint16_t rb_bits = 0;
+  {
+    const int64_t rs = p.qkv_row_stride * 2;  // bytes per mixed_qkv row
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.qkv + t0 * p.qkv_row_stride, static_cast<uint32_t>(n * rs));
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.raw_g + t0 * (H * K), static_cast<uint32_t>(n * H * K * 2));
 #pragma unroll
-  for (int j = 0; j < 4; ++j) dtb[j] = p.dt_bias[h * K + c4 + j];
-  const float beta_t = (tid < n) ? sigmoid_f32(bf16_to_f32(p.raw_beta[(t0 + tid) * H + h])) : 0.f;
-  wait_vmem();
-  __syncthreads();
+    for (int i = 0; i < PP; ++i)
+      rgw[i] = __builtin_amdgcn_raw_buffer_load_b64(rg, ((part * PP + i) * H * K + h * K + c4) * 2, 0, 0);
+    // Per-head gate parameters and beta.
+    a_h = __expf(p.A_log[h]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dtb[j] = p.dt_bias[h * K + c4 + j];
+    // beta of position tid (rows past the chunk end read 0; only tid < n is used).
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.raw_beta + t0 * H, static_cast<uint32_t>(n * H * 2));
+    rb_bits = __builtin_amdgcn_raw_buffer_load_b16(rb, (tid * H + h) * 2, 0, 0);
+    // Keep these loads ahead of the copies: loads complete in issue order,
+    // so anything issued after the copies would wait for them.
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int r = 0; r < C * KP8 / kThreads; ++r) {
+      const int ps = r * kThreads + tid;          // physical piece in the tile
+      const int t = ps / KP8;
+      const int pl = (ps % KP8) ^ (t & KPM);      // logical piece stored there
+      const int slot = r * kThreads + (tid & ~63);
+      const int qoff = static_cast<int>(t * rs) + (h * K + pl * 8) * 2;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, reinterpret_cast<uint4*>(sm.q) + slot, 16, qoff, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, reinterpret_cast<uint4*>(sm.k) + slot, 16, qoff + H * K * 2, 0, 0, 0);
+    }
+  }
 
   // ---- 2. gate and cumulative log-decay, in registers ---------------------
+  const float beta_t = (tid < n) ? sigmoid_f32(bf16_to_f32(rb_bits)) : 0.f;
   // Each thread scans its PP positions; partial totals are added across
   // parts through x.
   float gm[PP][4];
@@ -525,11 +528,10 @@ __device__ __forceinline__ void intra_body(const PrefillParams& p, const int32_t
     float rg[PP][4];
 #pragma unroll
     for (int i = 0; i < PP; ++i) {
-      const uint2 wv = *reinterpret_cast<const uint2*>(&rawg[sw16<K>(part * PP + i, c4)]);
-      rg[i][0] = __uint_as_float(wv.x << 16);
-      rg[i][1] = __uint_as_float(wv.x & 0xffff0000u);
-      rg[i][2] = __uint_as_float(wv.y << 16);
-      rg[i][3] = __uint_as_float(wv.y & 0xffff0000u);
+      rg[i][0] = __uint_as_float(rgw[i][0] << 16);
+      rg[i][1] = __uint_as_float(rgw[i][0] & 0xffff0000u);
+      rg[i][2] = __uint_as_float(rgw[i][1] << 16);
+      rg[i][3] = __uint_as_float(rgw[i][1] & 0xffff0000u);
     }
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     if (has_lb) {
@@ -556,7 +558,7 @@ __device__ __forceinline__ void intra_body(const PrefillParams& p, const int32_t
       }
     }
     *reinterpret_cast<f32x4*>(&x[XL::tot + part * K + c4]) = f32x4{acc[0], acc[1], acc[2], acc[3]};
-    lds_barrier();  // raw_g consumed; partial totals visible
+    lds_barrier();  // partial totals visible
     float before[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int q2 = 0; q2 < NPART; ++q2) {
@@ -593,6 +595,7 @@ __device__ __forceinline__ void intra_body(const PrefillParams& p, const int32_t
       *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(rec + R::Eg) + c4) =
           f32x4{__expf(gl[0]), __expf(gl[1]), __expf(gl[2]), __expf(gl[3])};
   }
+  wait_vmem();  // this thread's k and q copies (and every load before them) have landed
   lds_barrier();
   bool fast = true;
 #pragma unroll
@@ -663,7 +666,7 @@ __device__ __forceinline__ void intra_body(const PrefillParams& p, const int32_t
         float kr[4], qr[4], kf[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float Rt = __expf(gm[i][j] - rho[j]), Ft = __expf(rho[j] - gm[i][j]);
+          const float Rt = __expf(gm[i][j] - rho[j]), Ft = __builtin_amdgcn_rcpf(Rt);  // Rt >= e^-80
           kr[j] = kv[j] * Rt;
           qr[j] = qv[j] * Rt;
           kf[j] = kv[j] * Ft;
@@ -735,34 +738,45 @@ __device__ __forceinline__ void intra_body(const PrefillParams& p, const int32_t
             b[kb] = to_bf16x8(sc);
           }
         }
-        f32x4 dA = {0.f, 0.f, 0.f, 0.f}, dP = {0.f, 0.f, 0.f, 0.f};
+        // A with block I's positions as rows; P transposed (block J's
+        // positions as rows), so a lane holds four consecutive columns of
+        // one row of P.
+        f32x4 dA = {0.f, 0.f, 0.f, 0.f}, dPt = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < K / 32; ++kb) {
           dA = mfma16(ak[kb], b[kb], dA);
-          dP = mfma16(aq[kb], b[kb], dP);
+          dPt = mfma16(b[kb], aq[kb], dPt);
         }
-        // Lane holds rows 16 I + 4 g + j of column s = 16 J + m. Every entry
-        // is written without a branch: beta stays on the diagonal, and the
-        // entries below it (junk from the masked s > t products) are
+        // dA: lane holds rows 16 I + 4 g + j of column s = 16 J + m. Every
+        // entry is written without a branch: beta stays on the diagonal, and
+        // the entries below it (junk from the masked s > t products) are
         // overwritten by T before anything reads them.
         const int s2 = 16 * J + m;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int row = 16 * I + 4 * g + j;
           sm.at[sw32<C>(s2, row)] = s2 == row ? bt[j] : bt[j] * dA[j];
-          __builtin_amdgcn_raw_buffer_store_b16(bf16_bits(s2 <= row ? p.scale * dP[j] : 0.f), rpm,
-                                                rec_elem<C>(row, 32 * (s2 >> 5) + perm_slot(s2 & 31)) * 2, 0, 0);
+        }
+        // dPt: lane holds P[16 I + m][16 J + 4 g + j], j < 4: four
+        // consecutive slots of the permuted position order, one 8-byte store.
+        {
+          const int prow = 16 * I + m;
+          float pv[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) pv[j] = 16 * J + 4 * g + j <= prow ? p.scale * dPt[j] : 0.f;
+          typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+          const u32x2 v = {pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])};
+          __builtin_amdgcn_raw_buffer_store_b64(v, rpm, rec_elem<C>(prow, 32 * (J >> 1) + 8 * g + 4 * (J & 1)) * 2, 0, 0);
         }
       }
       if (w == 3) {
         // Zero P blocks above the diagonal that the state kernel reads:
-        // rows 0..15 x cols 16..31 and rows 32..47 x cols 48..63.
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int row = 4 * g + j;
-          __builtin_amdgcn_raw_buffer_store_b16(0, rpm, rec_elem<C>(row, perm_slot(16 + m)) * 2, 0, 0);
-          __builtin_amdgcn_raw_buffer_store_b16(0, rpm, rec_elem<C>(32 + row, 32 + perm_slot(16 + m)) * 2, 0, 0);
-        }
+        // rows 0..15 x cols 16..31 and rows 32..47 x cols 48..63 (column
+        // 16 + 4 g + j sits in slot 8 g + 4 + j of its 32-block).
+        typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 z = {0u, 0u};
+        __builtin_amdgcn_raw_buffer_store_b64(z, rpm, rec_elem<C>(m, 8 * g + 4) * 2, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(z, rpm, rec_elem<C>(32 + m, 32 + 8 * g + 4) * 2, 0, 0);
       }
     }
   } else {
