@@ -190,6 +190,8 @@ static_assert(kMaxSegs <= kSegMinChunks, "segment count bound");
 // Device-side plan of one prefill call, written by plan_kernel.
 struct SegPlan {
   int32_t* chunk_start;  // [N+1] first chunk slot of each sequence
+  int4* chunk_info;      // [max_chunks] per intra workgroup row j: {chunk slot, first token, tokens, 0}
+                         // of chunk slot (chunks - 1 - j); tokens = 0 past the last chunk
   int32_t* seg_start;    // [N+1] first segment of each sequence
   int32_t* counts;       // [4]: segments, maps, long sequences, plan fits its bounds
   int32_t* seg_seq;      // [seg_bound] sequence of each segment
@@ -200,6 +202,8 @@ struct SegPlan {
   int32_t seg_bound, map_bound, long_bound;
   int32_t max_segs;      // segments per sequence at most (host bound)
   int32_t fill_units;    // state-pass workgroups per segment (H * V / 64)
+  int32_t max_chunks;    // chunk slots the records are sized for
+  int32_t num_tokens;    // rows of the call (validated to fit in int32)
 };
 
 __device__ __forceinline__ int64_t map_index(int h, int mi, const SegPlan& pl) {
@@ -215,7 +219,7 @@ __device__ __forceinline__ int64_t s0_index(int h, int li, const SegPlan& pl) {
 // (and at most num_seqs (max_segs - 1)); each cut sequence has at least one.
 struct Layout {
   int64_t seg_bound, map_bound, long_bound, max_segs, fill_units;
-  size_t chunk_start, seg_start, counts, seg_seq, seg_long, map_seg;
+  size_t chunk_start, seg_start, counts, seg_seq, seg_long, map_seg, chunk_info;
   size_t flags, recs, maps, s0, total;
 };
 
@@ -243,8 +247,10 @@ inline Layout layout_for(int32_t num_seqs, int64_t num_tokens, int32_t H, int32_
   L.seg_seq = o;     o += L.seg_bound * 4;
   L.seg_long = o;    o += L.seg_bound * 4;
   L.map_seg = o;     o += L.map_bound * 4;
-  L.flags = round256(o);
   const int64_t maxc = max_chunks_for(num_tokens, num_seqs);
+  L.chunk_info = (o + 15) / 16 * 16;
+  o = L.chunk_info + static_cast<size_t>(maxc) * 16;
+  L.flags = round256(o);
   L.recs = L.flags + round256(static_cast<size_t>(maxc) * H);
   L.maps = L.recs + static_cast<size_t>(maxc) * H * rec_bytes_for(K, V);
   L.s0 = L.maps + static_cast<size_t>(L.map_bound) * H * (static_cast<size_t>(K) * K + static_cast<size_t>(K) * V) * 4;
@@ -319,6 +325,10 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t* cu, int32
   // Holds for cu_seqlens that keep to the contract; otherwise no segment
   // tables are written and the state pass does nothing.
   const bool fits = stot <= pl.seg_bound && mtot <= pl.map_bound && ltot <= pl.long_bound;
+  // Intra rows past the last chunk do nothing (so do all rows if the
+  // chunks outgrow the records).
+  for (int jj = (ctot <= pl.max_chunks ? ctot : 0) + tid; jj < pl.max_chunks; jj += kThreads)
+    pl.chunk_info[jj] = int4{0, 0, 0, 0};
   for (int i = b; i < e; ++i) {
     const int nch = chunks_of(cu, i);
     const int ns = segments_of(nch, target);
@@ -336,6 +346,22 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t* cu, int32
     cb += nch;
     sb += ns;
     lb += ns > 1;
+  }
+  __syncthreads();  // chunk_start[0 .. N-1] visible to every thread
+  if (ctot <= pl.max_chunks) {
+    // Intra row j takes chunk slot ctot - 1 - j (the chunks last to first);
+    // slot c belongs to the last sequence whose first slot is <= c.
+    for (int c = tid; c < ctot; c += kThreads) {
+      int lo = 0, hi = N;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (pl.chunk_start[mid] <= c) lo = mid; else hi = mid;
+      }
+      const int k = c - pl.chunk_start[lo];
+      const int bos = cu[lo], eos = cu[lo + 1];
+      const bool ok = bos >= 0 && eos <= pl.num_tokens;
+      pl.chunk_info[ctot - 1 - c] = ok ? int4{c, bos + C * k, min(C, eos - bos - C * k), 0} : int4{0, 0, 0, 0};
+    }
   }
   if (tid == 0) {
     pl.chunk_start[N] = ctot;
@@ -418,7 +444,7 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
 // handles only the flagged chunks. Separate kernels keep the factored path's
 // registers free of the exact path's.
 template <int K, int V, bool kExact>
-__device__ __forceinline__ void intra_body(const PrefillParams& p, const int32_t* chunk_start,
+__device__ __forceinline__ void intra_body(const PrefillParams& p, const int4* chunk_info,
                                            char* recs, uint8_t* exact_flags) {
   using R = Rec<K, V>;
   using SM = IntraSmem<K, V>;
@@ -426,34 +452,22 @@ __device__ __forceinline__ void intra_body(const PrefillParams& p, const int32_t
   __shared__ SM sm;
 
   const int H = p.H;
-  const int N = p.num_seqs;
   // Chunks are taken last to first: the state pass reads them first to
   // last, so its early chunks are the most recently written (still in the
-  // memory-side cache when the records outgrow it).
-  const int nchunks = uniform(chunk_start[N]);
-  const int c = nchunks - 1 - static_cast<int>(blockIdx.x / H);
+  // memory-side cache when the records outgrow it). The plan gives row j
+  // its chunk slot, first token and token count in one load (zero tokens
+  // past the last chunk, or for cu_seqlens outside the contract).
+  const int j = static_cast<int>(blockIdx.x / H);
   const int h = static_cast<int>(blockIdx.x % H);
-  if (c < 0) return;  // uniform: past the last chunk
-  // Records exist for at most max_chunks chunks (sized from the host's token
-  // count); inconsistent cu_seqlens must not send us past them.
-  if (nchunks > max_chunks_for(p.num_tokens, N)) return;
+  const int4 info = chunk_info[j];
+  const int n = uniform(info.z);
+  if (n <= 0) return;  // uniform
+  const int c = uniform(info.x);
+  const int64_t t0 = uniform(info.y);
   uint8_t* flag = exact_flags + static_cast<int64_t>(c) * H + h;
   if constexpr (kExact) {
     if (*flag == 0) return;  // uniform: the factored kernel took this chunk
   }
-
-  // Which sequence owns chunk slot c: the last i with chunk_start[i] <= c.
-  int lo = 0, hi = N;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (chunk_start[mid] <= c) lo = mid; else hi = mid;
-  }
-  const int seq = lo;
-  const int64_t bos = uniform(static_cast<int64_t>(p.cu_seqlens[seq]));
-  const int64_t eos = uniform(static_cast<int64_t>(p.cu_seqlens[seq + 1]));
-  const int64_t t0 = bos + static_cast<int64_t>(C) * (c - uniform(chunk_start[seq]));
-  if (eos > p.num_tokens || t0 >= eos) return;  // malformed cu_seqlens: touch nothing
-  const int n = static_cast<int>(min<int64_t>(C, eos - t0));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1175,16 +1189,16 @@ __device__ __forceinline__ void intra_body(const PrefillParams& p, const int32_t
 
 template <int K, int V>
 __global__ __launch_bounds__(kThreads, 2) void chunk_intra_kernel(const PrefillParams p,
-                                                                  const int32_t* chunk_start,
+                                                                  const int4* chunk_info,
                                                                   char* recs, uint8_t* exact_flags) {
-  intra_body<K, V, false>(p, chunk_start, recs, exact_flags);
+  intra_body<K, V, false>(p, chunk_info, recs, exact_flags);
 }
 
 template <int K, int V>
 __global__ __launch_bounds__(kThreads, 2) void chunk_intra_exact_kernel(const PrefillParams p,
-                                                                        const int32_t* chunk_start,
+                                                                        const int4* chunk_info,
                                                                         char* recs, uint8_t* exact_flags) {
-  intra_body<K, V, true>(p, chunk_start, recs, exact_flags);
+  intra_body<K, V, true>(p, chunk_info, recs, exact_flags);
 }
 
 
@@ -1764,7 +1778,7 @@ hipError_t launch_kv(const PrefillParams& p, const Layout& L, const SegPlan& pl,
   if (intra_blocks > 0x7fffffff || state_blocks > 0x7fffffff || map_blocks > 0x7fffffff)
     return hipErrorInvalidValue;
   chunk_intra_kernel<K, V><<<dim3(static_cast<unsigned>(intra_blocks)), dim3(kThreads), 0, stream>>>(
-      p, pl.chunk_start, recs, exact_flags);
+      p, pl.chunk_info, recs, exact_flags);
   // With a lower bound lb every per-token log-decay lies in [lb, 0], so a
   // 16-row block decays by at most 15 |lb| and the factored kernel takes
   // every chunk once 15 |lb| <= kMaxBlockDecay: the exact kernel would only
@@ -1772,7 +1786,7 @@ hipError_t launch_kv(const PrefillParams& p, const Layout& L, const SegPlan& pl,
   const bool all_factored = p.has_lb != 0 && 15.f * -p.lower_bound <= kMaxBlockDecay - 1.f;
   if (!all_factored)
     chunk_intra_exact_kernel<K, V><<<dim3(static_cast<unsigned>(intra_blocks)), dim3(kThreads), 0, stream>>>(
-        p, pl.chunk_start, recs, exact_flags);
+        p, pl.chunk_info, recs, exact_flags);
   if (L.map_bound > 0) {
     chunk_map_kernel<K, V><<<dim3(static_cast<unsigned>(map_blocks)), dim3(kMapThreads), 0, stream>>>(p, pl, recs);
   }
@@ -1813,6 +1827,9 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   pl.long_bound = static_cast<int32_t>(L.long_bound);
   pl.max_segs = static_cast<int32_t>(L.max_segs);
   pl.fill_units = static_cast<int32_t>(L.fill_units);
+  pl.chunk_info = reinterpret_cast<int4*>(ws + L.chunk_info);
+  pl.max_chunks = static_cast<int32_t>(max_chunks_for(p.num_tokens, p.num_seqs));
+  pl.num_tokens = static_cast<int32_t>(p.num_tokens);
   uint8_t* flags = reinterpret_cast<uint8_t*>(ws + L.flags);
   char* recs = ws + L.recs;
   plan_kernel<<<1, kThreads, 0, stream>>>(p.cu_seqlens, p.num_seqs, pl);
