@@ -131,21 +131,69 @@ void decode_kernel(const DecodeParams p) {
   {
     const float a = __expf(p.A_log[h]);
     const bool has_lb = p.has_lb != 0;
-    for (int e = tid; e < tps * K; e += blockDim.x) {
-      const int t = e / K, i = e % K;
-      const int64_t row = row0 + t;
-      const uint16_t* qkv = p.qkv + row * p.qkv_row_stride;
-      s_q[t][i] = bf16_to_f32(qkv[h * K + i]);
-      s_k[t][i] = bf16_to_f32(qkv[H * K + h * K + i]);
-      const float g = gate_log_decay(bf16_to_f32(p.raw_g[row * (H * K) + h * K + i]),
-                                     p.dt_bias[h * K + i], a, has_lb, p.lower_bound);
-      s_a[t][i] = __expf(g);
+    if (tps >= 3) {
+      // Long requests: every load is issued before the first use (buffer
+      // loads over the request's rows; elements past its tokens read zero
+      // and are not stored), one memory round trip instead of one per pass.
+      constexpr int NE = (kMaxTokens * K + 255) / 256;   // q/k/raw_g elements per thread
+      constexpr int NV = (kMaxTokens * VT + 255) / 256;  // v elements per thread
+      const int rs = static_cast<int>(p.qkv_row_stride) * 2;  // bytes per mixed_qkv row
+      const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.qkv + row0 * p.qkv_row_stride, static_cast<uint32_t>(tps * rs));
+      const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.raw_g + row0 * (H * K), static_cast<uint32_t>(tps * H * K * 2));
+      const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.raw_beta + row0 * H, static_cast<uint32_t>(tps * H * 2));
+      uint16_t qb[NE], kb[NE], gb[NE], vb[NV];
+      float db[NE];
+#pragma unroll
+      for (int u = 0; u < NE; ++u) {
+        const int e = tid + 256 * u;
+        const int t = e / K, i = e % K;
+        qb[u] = __builtin_amdgcn_raw_buffer_load_b16(rq, t * rs + (h * K + i) * 2, 0, 0);
+        kb[u] = __builtin_amdgcn_raw_buffer_load_b16(rq, t * rs + (H * K + h * K + i) * 2, 0, 0);
+        gb[u] = __builtin_amdgcn_raw_buffer_load_b16(rg, (t * H * K + h * K + i) * 2, 0, 0);
+        db[u] = p.dt_bias[h * K + i];
+      }
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        const int e = tid + 256 * u;
+        const int t = e / VT, j = e % VT;
+        vb[u] = __builtin_amdgcn_raw_buffer_load_b16(rq, t * rs + (2 * H * K + h * V + tile * VT + j) * 2, 0, 0);
+      }
+      const uint16_t bb = __builtin_amdgcn_raw_buffer_load_b16(rb, (tid * H + h) * 2, 0, 0);
+#pragma unroll
+      for (int u = 0; u < NE; ++u) {
+        const int e = tid + 256 * u;
+        if (e < tps * K) {
+          const int t = e / K, i = e % K;
+          s_q[t][i] = bf16_to_f32(qb[u]);
+          s_k[t][i] = bf16_to_f32(kb[u]);
+          s_a[t][i] = __expf(gate_log_decay(bf16_to_f32(gb[u]), db[u], a, has_lb, p.lower_bound));
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        const int e = tid + 256 * u;
+        if (e < tps * VT) s_v[e / VT][e % VT] = bf16_to_f32(vb[u]);
+      }
+      if (tid < tps) s_b[tid] = sigmoid_f32(bf16_to_f32(bb));
+    } else {
+      // One or two tokens: a single pass, with fewer instructions in the
+      // way of the state loads.
+      for (int e = tid; e < tps * K; e += blockDim.x) {
+        const int t = e / K, i = e % K;
+        const int64_t row = row0 + t;
+        const uint16_t* qkv = p.qkv + row * p.qkv_row_stride;
+        s_q[t][i] = bf16_to_f32(qkv[h * K + i]);
+        s_k[t][i] = bf16_to_f32(qkv[H * K + h * K + i]);
+        const float g = gate_log_decay(bf16_to_f32(p.raw_g[row * (H * K) + h * K + i]),
+                                       p.dt_bias[h * K + i], a, has_lb, p.lower_bound);
+        s_a[t][i] = __expf(g);
+      }
+      for (int e = tid; e < tps * VT; e += blockDim.x) {
+        const int t = e / VT, j = e % VT;
+        s_v[t][j] = bf16_to_f32(p.qkv[(row0 + t) * p.qkv_row_stride + 2 * H * K + h * V + tile * VT + j]);
+      }
+      if (tid < tps) s_b[tid] = sigmoid_f32(bf16_to_f32(p.raw_beta[(row0 + tid) * H + h]));
     }
-    for (int e = tid; e < tps * VT; e += blockDim.x) {
-      const int t = e / VT, j = e % VT;
-      s_v[t][j] = bf16_to_f32(p.qkv[(row0 + t) * p.qkv_row_stride + 2 * H * K + h * V + tile * VT + j]);
-    }
-    if (tid < tps) s_b[tid] = sigmoid_f32(bf16_to_f32(p.raw_beta[(row0 + tid) * H + h]));
     if constexpr (kRow) {
       if (p.norm.gate != nullptr) {
         for (int e = tid; e < tps * VT; e += blockDim.x) {
