@@ -6,6 +6,8 @@
 // memory from the host.
 #include <cmath>
 #include <cstdio>
+#include <map>
+#include <mutex>
 #include <string>
 
 #include "kda.h"
@@ -36,6 +38,34 @@ class Checks {
 };
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Per-device side stream of the mixed-batch router, with the two events that
+// fork it from the caller's stream and join it back. Created on a device's
+// first mixed batch with decode and prefill rows, kept until the process
+// ends, and used under g_side_mu so that concurrent callers cannot interleave
+// their records and waits.
+struct SideStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_side_mu;
+std::map<int, SideStream> g_side;
+
+hipError_t side_stream_locked(SideStream** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  SideStream& ss = g_side[dev];
+  if (ss.stream == nullptr) {
+    SideStream fresh;
+    if ((e = hipStreamCreateWithFlags(&fresh.stream, hipStreamNonBlocking)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&fresh.fork, hipEventDisableTiming)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&fresh.join, hipEventDisableTiming)) != hipSuccess) return e;
+    ss = fresh;
+  }
+  *out = &ss;
+  return hipSuccess;
+}
 
 // Checks shared by all entry points. rows: number of token rows the call reads.
 void check_common(Checks& c, int64_t rows, int32_t H, int32_t K, int32_t V,
@@ -309,17 +339,23 @@ kda_status_t kda_mixed_batch(int32_t num_decodes, int32_t num_prefills, int64_t 
   check_norm(c, rows, H, V, norm);
   if (!c.ok()) return c.finish();
 
-  // Decode rows [0, D): recurrent kernel, one token per request.
-  if (num_decodes > 0) {
+  // Decode rows [0, D) go to the recurrent kernel, one token per request;
+  // prefill rows [D, D + P) to the chunk pipeline on the shifted views (only
+  // host pointer arithmetic; device data is never read here). The two parts
+  // touch disjoint slots and rows, so with both present the decode rows run
+  // on a side stream forked from `stream` once the prefill's intra-chunk
+  // kernels are launched, and joined back after its last kernel: the
+  // HBM-bound decode kernel overlaps the latency-bound map and state passes,
+  // which leave LDS free beside their one workgroup per CU.
+  const bool has_decode = num_decodes > 0;
+  const bool has_prefill = num_prefills > 0 && num_prefill_tokens > 0;
+  auto launch_decode_rows = [&](hipStream_t s) -> hipError_t {
     kda::DecodeParams p = decode_params(num_decodes, 1, H, V, mixed_qkv, qkv_row_stride, raw_g,
                                         raw_beta, gate, state, out);
     p.norm = out_norm(norm, 0);
-    hipError_t e = kda::launch_decode(p, K, stream);
-    if (e != hipSuccess) return hip_status(e, "mixed batch: decode launch");
-  }
-  // Prefill rows [D, D + P): the chunk pipeline on the shifted views. Only
-  // host pointer arithmetic; device data is never read here.
-  if (num_prefills > 0 && num_prefill_tokens > 0) {
+    return kda::launch_decode(p, K, s);
+  };
+  auto launch_prefill_rows = [&](hipStream_t s, hipEvent_t after_intra) -> hipError_t {
     const int64_t D = num_decodes;
     const uint16_t* qkv = static_cast<const uint16_t*>(mixed_qkv) + D * qkv_row_stride;
     const uint16_t* rg = static_cast<const uint16_t*>(raw_g) + D * H * K;
@@ -331,7 +367,30 @@ kda_status_t kda_mixed_batch(int32_t num_decodes, int32_t num_prefills, int64_t 
         prefill_params(num_prefills, num_prefill_tokens, prefill_cu_seqlens, has_initial_state, H,
                        K, V, qkv, qkv_row_stride, rg, rb, gate, &st, o, workspace, workspace_bytes);
     p.norm = out_norm(norm, D);
-    hipError_t e = kda::launch_prefill(p, stream);
+    return kda::launch_prefill(p, s, after_intra);
+  };
+  if (has_decode && has_prefill) {
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    SideStream* side = nullptr;
+    hipError_t e = side_stream_locked(&side);
+    if (e != hipSuccess) return hip_status(e, "mixed batch: side stream");
+    // The fork is recorded inside the prefill launch, after its intra
+    // kernels; once the side stream waits on it, it is joined back whatever
+    // fails in between, so it never outlives the call's work on `stream`
+    // (and a capture of `stream` stays joined).
+    const hipError_t ep = launch_prefill_rows(stream, side->fork);
+    if (ep != hipSuccess) return hip_status(ep, "mixed batch: prefill launch");
+    if ((e = hipStreamWaitEvent(side->stream, side->fork, 0)) != hipSuccess)
+      return hip_status(e, "mixed batch: fork");
+    const hipError_t ed = launch_decode_rows(side->stream);
+    if ((e = hipEventRecord(side->join, side->stream)) != hipSuccess) return hip_status(e, "mixed batch: join");
+    if ((e = hipStreamWaitEvent(stream, side->join, 0)) != hipSuccess) return hip_status(e, "mixed batch: join");
+    if (ed != hipSuccess) return hip_status(ed, "mixed batch: decode launch");
+  } else if (has_decode) {
+    const hipError_t e = launch_decode_rows(stream);
+    if (e != hipSuccess) return hip_status(e, "mixed batch: decode launch");
+  } else if (has_prefill) {
+    const hipError_t e = launch_prefill_rows(stream, nullptr);
     if (e != hipSuccess) return hip_status(e, "mixed batch: prefill launch");
   }
   g_last_error.clear();

@@ -1769,7 +1769,7 @@ __global__ __launch_bounds__(kMapThreads, 2) void chunk_map_kernel(const Prefill
 
 template <int K, int V>
 hipError_t launch_kv(const PrefillParams& p, const Layout& L, const SegPlan& pl, uint8_t* exact_flags,
-                     char* recs, hipStream_t stream) {
+                     char* recs, hipStream_t stream, hipEvent_t after_intra) {
   const int64_t maxc = max_chunks_for(p.num_tokens, p.num_seqs);
   const int64_t intra_blocks = maxc * p.H;
   const int64_t seg_pairs = L.seg_bound * p.H;
@@ -1787,6 +1787,10 @@ hipError_t launch_kv(const PrefillParams& p, const Layout& L, const SegPlan& pl,
   if (!all_factored)
     chunk_intra_exact_kernel<K, V><<<dim3(static_cast<unsigned>(intra_blocks)), dim3(kThreads), 0, stream>>>(
         p, pl.chunk_info, recs, exact_flags);
+  if (after_intra != nullptr) {
+    const hipError_t e = hipEventRecord(after_intra, stream);
+    if (e != hipSuccess) return e;
+  }
   if (L.map_bound > 0) {
     chunk_map_kernel<K, V><<<dim3(static_cast<unsigned>(map_blocks)), dim3(kMapThreads), 0, stream>>>(p, pl, recs);
   }
@@ -1809,7 +1813,7 @@ size_t prefill_workspace_bytes(int32_t num_seqs, int64_t num_tokens, int32_t H, 
   return layout_for(num_seqs, num_tokens, H, K, V).total;
 }
 
-hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream, hipEvent_t after_intra) {
   const Layout L = layout_for(p.num_seqs, p.num_tokens, p.H, p.K, p.V);
   if (L.seg_bound > 0x7fffffff) return hipErrorInvalidValue;
   char* ws = static_cast<char*>(p.workspace);
@@ -1834,10 +1838,10 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   char* recs = ws + L.recs;
   plan_kernel<<<1, kThreads, 0, stream>>>(p.cu_seqlens, p.num_seqs, pl);
   hipError_t e;
-  if (p.K == 64 && p.V == 64) e = launch_kv<64, 64>(p, L, pl, flags, recs, stream);
-  else if (p.K == 64 && p.V == 128) e = launch_kv<64, 128>(p, L, pl, flags, recs, stream);
-  else if (p.K == 128 && p.V == 64) e = launch_kv<128, 64>(p, L, pl, flags, recs, stream);
-  else e = launch_kv<128, 128>(p, L, pl, flags, recs, stream);
+  if (p.K == 64 && p.V == 64) e = launch_kv<64, 64>(p, L, pl, flags, recs, stream, after_intra);
+  else if (p.K == 64 && p.V == 128) e = launch_kv<64, 128>(p, L, pl, flags, recs, stream, after_intra);
+  else if (p.K == 128 && p.V == 64) e = launch_kv<128, 64>(p, L, pl, flags, recs, stream, after_intra);
+  else e = launch_kv<128, 128>(p, L, pl, flags, recs, stream, after_intra);
   // Output epilogue: a head's columns are spread over the state pass's waves
   // (and, at V = 128, over two workgroups), so the norm is a pass over the
   // output.

@@ -209,7 +209,16 @@ size_t kda_mixed_batch_workspace_size(int32_t num_decodes, int32_t num_prefills,
  * int32 [num_prefills+1], relative to row num_decodes); prefill i uses slot
  * indices[(num_decodes+i)*index_stride] and has_initial_state[i] (NULL = all
  * 1). Decode rows go to the recurrent decode kernel, prefill rows to the chunk
- * pipeline, all on `stream` with no host synchronisation. out is bf16
+ * pipeline, with no host synchronisation. The call is ordered on `stream` as
+ * a whole; when it has both kinds of rows, the decode kernel runs on a
+ * library-owned side stream (one per device, created with two events on the
+ * device's first such call and kept until the process ends) that is forked
+ * from `stream` after the prefill's intra-chunk kernels and joined back
+ * before the call's work on `stream` ends, so it overlaps the prefill's
+ * state pass. A capture of `stream` captures both branches; make the first
+ * such call on a device outside capture, since it creates the side stream.
+ * Calls on one device from several host threads are serialised while they
+ * enqueue. out is bf16
  * [num_decodes+num_prefill_tokens][H][V]; norm (optional) as for
  * kda_decode_packed, its gate rows paired with the output rows.
  * Errors: as kda_chunk_prefill.
