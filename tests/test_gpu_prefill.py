@@ -16,7 +16,7 @@ import torch
 import gated_delta_rule_45_amd as kda
 import workloads as W
 from kda_testlib import (DECODE_TOL_O, DECODE_TOL_S, PREFILL_TOL_O, PREFILL_TOL_S, check_case, log,
-                         rel_err, run_gpu, to_device)
+                         rel_err, run_gpu, run_oracle, to_device)
 from oracle import oracle as O
 
 pytestmark = pytest.mark.gpu
@@ -237,3 +237,51 @@ def test_prefill_split_equals_whole():
     es = rel_err(dc2.pool[slot].cpu().numpy(), pool_whole[slot].cpu().numpy().astype(np.float64))
     log(f"[case] split vs whole: e_o={e:.3e} e_S={es:.3e}")
     assert e <= PREFILL_TOL_O and es <= PREFILL_TOL_S
+
+
+def test_mixed_batches_from_two_host_threads():
+    """The router runs a batch's decode rows on a side stream forked from the
+    caller's stream and joined back. Two host threads, each on its own
+    stream with its own pool, call it repeatedly at the same time; every
+    output and final state must still match the oracle."""
+    import threading
+
+    cases = [W.mixed_case(f"threads_{n}", 4, 128, 128, 7, [90, 1, 40], 16, -5.0, seed=671 + n)
+             for n in range(2)]
+    refs = [run_oracle(c) for c in cases]
+    results = [None, None]
+    errors = []
+
+    def worker(n):
+        try:
+            c = cases[n]
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                outs = []
+                for _ in range(4):
+                    dc = to_device(c)
+                    i = dc.inputs
+                    o, _ = kda.kda_mixed_batch(i["mixed_qkv"], i["raw_g"], i["raw_beta"], i["A_log"],
+                                               i["dt_bias"], -5.0, dc.pool, dc.state_indices,
+                                               c.num_decodes, dc.cu_seqlens)
+                    outs.append((o, dc))
+                s.synchronize()
+            results[n] = outs
+        except Exception as exc:  # reported on the main thread
+            errors.append(repr(exc))
+
+    threads = [threading.Thread(target=worker, args=(n,)) for n in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not errors, errors
+    for n, c in enumerate(cases):
+        ref_out, ref_fs = refs[n]
+        idx = c.state_indices.tolist()
+        for o, dc in results[n]:
+            e = rel_err(o.float().cpu().numpy().astype(np.float64), ref_out)
+            es = max(rel_err(dc.pool[s].cpu().numpy().astype(np.float64), ref_fs[i])
+                     for i, s in enumerate(idx) if s >= 0)
+            log(f"[case] thread {n}: e_o={e:.3e} e_S={es:.3e}")
+            assert e <= PREFILL_TOL_O and es <= PREFILL_TOL_S
