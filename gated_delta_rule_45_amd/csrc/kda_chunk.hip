@@ -18,9 +18,10 @@
 //            cu_seqlens.
 //  2. intra: one workgroup per (chunk, head), all chunks in parallel (last
 //            to first). Builds gam in registers, then A and P on bf16 MFMA
-//            from factored operand tiles (or, for a chunk with a block that
-//            decays too steeply, with pairwise fp32 exponentials on the
-//            diagonal blocks), T by forward substitution plus fp32-MFMA block
+//            from factored operand tiles, the key channels in halves of 64
+//            (or, in a second kernel for a chunk with a block that decays
+//            too steeply, with pairwise fp32 exponentials on the diagonal
+//            blocks), T by forward substitution plus fp32-MFMA block
 //            products, then W and U on MFMA. It stores -W, scale Q o e^gam,
 //            scale P, (K o e^{gam_last-gam})^T (bf16, laid out as MFMA A
 //            operands), e^{gam_last} and U (fp32, in accumulator fragment
@@ -389,17 +390,16 @@ __device__ __forceinline__ int sw32(int t, int c) {
   return t * N + ((((c >> 2) ^ (t & PM)) << 2) | (c & 3));
 }
 
-// Intra-kernel LDS: 80 KiB at K = 128, so two workgroups share a CU.
-//  k   bf16 [C][K] (sw16)  keys (zero rows past the chunk end); on the
-//                          factored path overwritten by K o R
-//  q   bf16 [C][K] (sw16)  queries; factored path: Q o R. After A/P:
-//                          -W staging for the coalesced copy-out
+// Exact intra kernel LDS: 80 KiB at K = 128, two workgroups per CU.
+//  k   bf16 [C][K] (sw16)  keys (zero rows past the chunk end)
+//  q   bf16 [C][K] (sw16)  queries
 //  u   union of
-//        gam  fp32 [C][K] (sw32)  cumulative log-decay (exact path)
-//        kf   bf16 [C][K] (sw16)  K o F (factored path), and
-//        x    fp32 scratch: part totals, gam at block starts, per-block
-//             decay ranges and the channel factors c_IJ until A/P is done;
-//             then (K o e^gam)^T, bf16 [K][C] (swz<C>), the B operand of W
+//        gam  fp32 [C][K] (sw32)  cumulative log-decay, and
+//        kf   bf16 [C][K] space, placing x over gam's second half; its
+//             first bytes hold beta after A/P, and
+//        x    fp32 scratch: part totals, gam at block starts and per-block
+//             decay ranges until gam is written; then (K o e^gam)^T, bf16
+//             [K][C] (swz<C>), the B operand of W
 //  at  fp32 [C][C] (sw32)  A^T
 //                          strictly above the diagonal (at(s,t) = A[t][s]),
 //                          T = (I + A)^{-1} strictly below it (unit
@@ -438,14 +438,180 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// One intra workgroup. The factored instantiation (kExact = false) handles
-// every chunk whose blocks all decay by at most kMaxBlockDecay and flags the
-// others; the exact instantiation, launched after it on the same grid,
-// handles only the flagged chunks. Separate kernels keep the factored path's
-// registers free of the exact path's.
-template <int K, int V, bool kExact>
-__device__ __forceinline__ void intra_body(const PrefillParams& p, const int4* chunk_info,
-                                           char* recs, uint8_t* exact_flags) {
+// Steps common to both intra kernels once A^T (with beta on its diagonal)
+// is in at, (K o e^gam)^T in wkt, beta in beta_l and the lane's v operands
+// in vpre: T = (I + A)^{-1} in at, then W and U into the record.
+template <int K, int V>
+__device__ __forceinline__ void intra_inverse_wu(const PrefillParams& p, float* at, const uint16_t* wkt,
+                                                 const float* beta_l,
+                                                 const uint16_t (&vpre)[(V / 16 + 3) / 4][2][8],
+                                                 char* rec, int w, int lane) {
+  using R = Rec<K, V>;
+  constexpr int NBU = (V / 16 + 3) / 4;
+  const int m = lane & 15;
+  const int g = lane >> 4;
+  // ---- 5. T = (I + A)^{-1}: diagonal blocks by forward substitution -----
+  // at(s, t) = A[t][s] for s < t; T strictly below the diagonal of at.
+  if (lane < 16) {
+    const int blk = w, jc = lane;
+    float x[16];
+#pragma unroll
+    for (int tt = 0; tt < 16; ++tt) {
+      float v = (tt == jc) ? 1.f : 0.f;
+#pragma unroll
+      for (int s3 = 0; s3 < tt; ++s3) v = fmaf(-at[sw32<C>(16 * blk + s3, 16 * blk + tt)], x[s3], v);
+      x[tt] = v;
+    }
+#pragma unroll
+    for (int tt = 0; tt < 16; ++tt)
+      if (tt > jc) at[sw32<C>(16 * blk + tt, 16 * blk + jc)] = x[tt];
+  }
+  lds_barrier();
+
+  // ---- 6. off-diagonal blocks of T on fp32 MFMA ---------------------------
+  // With the 32-row halves t (blocks 0, 1) and b (blocks 2, 3):
+  //   T_10 = -T_11 A_10 T_00,  T_32 = -T_33 A_32 T_22,  T_bt = -T_bb (A_bt T_tt).
+  // The 16x16x4 product pairs lane group g of step kk with contraction index
+  // 4 g + kk, so an accumulator tile (rows 4 g + j) is the B operand of the
+  // next product as it stands: step kk takes its element j = kk.
+  {
+    auto Tget = [&](int r, int cc) { return r > cc ? at[sw32<C>(r, cc)] : (r == cc ? 1.f : 0.f); };
+    auto Aget = [&](int t, int s) { return s < t ? at[sw32<C>(s, t)] : 0.f; };  // A[t][s]
+    // Operands are read into registers before their products (no LDS
+    // writes intervene), so the reads overlap.
+    if (w < 2) {
+      const int I = 1 + 2 * w, J = 2 * w;
+      float a[4], b[4], t[4];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        a[kk] = Aget(16 * I + m, 16 * J + 4 * g + kk);
+        b[kk] = Tget(16 * J + 4 * g + kk, 16 * J + m);
+        t[kk] = Tget(16 * I + m, 16 * I + 4 * g + kk);
+      }
+      f32x4 z = {0.f, 0.f, 0.f, 0.f}, tij = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) z = mfma4(a[kk], b[kk], z);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) tij = mfma4(t[kk], z[kk], tij);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) at[sw32<C>(16 * I + 4 * g + j, 16 * J + m)] = -tij[j];
+    }
+    lds_barrier();
+    {
+      const int I = 2 + (w >> 1), J = w & 1;
+      float a2[2][4], a3[2][4], b[2][4], t2[4], t3[4];
+#pragma unroll
+      for (int M = 0; M < 2; ++M)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          b[M][kk] = Tget(16 * M + 4 * g + kk, 16 * J + m);  // zero for M < J
+          a2[M][kk] = Aget(32 + m, 16 * M + 4 * g + kk);
+          a3[M][kk] = Aget(48 + m, 16 * M + 4 * g + kk);
+        }
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        t2[kk] = Tget(16 * I + m, 32 + 4 * g + kk);
+        t3[kk] = Tget(48 + m, 48 + 4 * g + kk);
+      }
+      f32x4 y2 = {0.f, 0.f, 0.f, 0.f}, y3 = {0.f, 0.f, 0.f, 0.f}, tij = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int M = 0; M < 2; ++M)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          y2 = mfma4(a2[M][kk], b[M][kk], y2);
+          y3 = mfma4(a3[M][kk], b[M][kk], y3);
+        }
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) tij = mfma4(t2[kk], y2[kk], tij);
+      if (I == 3) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) tij = mfma4(t3[kk], y3[kk], tij);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) at[sw32<C>(16 * I + 4 * g + j, 16 * J + m)] = -tij[j];
+    }
+    lds_barrier();
+  }
+
+  // ---- 7. W = T diag(beta)(K o e^gam), U = T diag(beta) V on MFMA -------
+  // beta is folded into the fp32 columns of T before the bf16 cast, so V
+  // enters the product exactly as given. T is lower triangular, so rows
+  // 0..31 need only positions 0..31.
+  {
+    // T diag(beta) as bf16 fragments: row 16 pb + m, positions 32 kb + 8 g
+    // .. +7, read as two 16-byte pieces of at (T strictly below the
+    // diagonal; the diagonal and above are masked by index).
+    bf16x8 Tf[4][2];
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int row = 16 * pb + m;
+        const int c0 = 32 * kb + 8 * g;
+        const f32x4 t0 = *reinterpret_cast<const f32x4*>(&at[sw32<C>(row, c0)]);
+        const f32x4 t1 = *reinterpret_cast<const f32x4*>(&at[sw32<C>(row, c0 + 4)]);
+        const f32x4 b0 = *reinterpret_cast<const f32x4*>(&beta_l[c0]);
+        const f32x4 b1 = *reinterpret_cast<const f32x4*>(&beta_l[c0 + 4]);
+        float tv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int col = c0 + j;
+          const float tval = j < 4 ? t0[j] : t1[j - 4];
+          const float bcol = j < 4 ? b0[j] : b1[j - 4];
+          tv[j] = (col < row ? tval : (col == row ? 1.f : 0.f)) * bcol;
+        }
+        Tf[pb][kb] = to_bf16x8(tv);
+      }
+    // -W^T = -(K o e^gam)^T (T diag(beta))^T: the same fragments with the
+    // operands swapped leave lane (m, g) four consecutive channels
+    // 16 nb + 4 g .. +3 of position 16 pb + m, which are four consecutive
+    // slots of the record's permuted channel order: one 8-byte store each.
+    {
+      const __amdgpu_buffer_rsrc_t rwn = make_rsrc(rec + R::Wn, static_cast<uint32_t>(C * K * 2));
+      typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+      for (int nb = w; nb < K / 16; nb += 4) {
+        bf16x8 Bf[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) Bf[kb] = frag<C>(wkt, 16 * nb + m, 32 * kb + 8 * g);
+        const int col = 32 * (nb >> 1) + 8 * g + 4 * (nb & 1);
+#pragma unroll
+        for (int pb = 0; pb < 4; ++pb) {
+          f32x4 D = mfma16(Bf[0], Tf[pb][0], f32x4{0.f, 0.f, 0.f, 0.f});
+          if (pb >= 2) D = mfma16(Bf[1], Tf[pb][1], D);
+          const u32x2 v = {pack_bf16x2(-D[0], -D[1]), pack_bf16x2(-D[2], -D[3])};
+          __builtin_amdgcn_raw_buffer_store_b64(v, rwn, rec_elem<K>(16 * pb + m, col) * 2, 0, 0);
+        }
+      }
+    }
+    // U written straight out in accumulator fragment order.
+    f32x4* uf = reinterpret_cast<f32x4*>(rec + R::Uf);
+#pragma unroll
+    for (int u = 0; u < NBU; ++u) {
+      const int nb = w + 4 * u;
+      if (nb >= V / 16) break;
+      bf16x8 Bv[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) Bv[kb][j] = __builtin_bit_cast(__bf16, vpre[u][kb][j]);
+#pragma unroll
+      for (int pb = 0; pb < 4; ++pb) {
+        f32x4 D = mfma16(Tf[pb][0], Bv[0], f32x4{0.f, 0.f, 0.f, 0.f});
+        if (pb >= 2) D = mfma16(Tf[pb][1], Bv[1], D);
+        uf[(pb * (V / 16) + nb) * 64 + lane] = D;
+      }
+    }
+  }
+}
+
+// One workgroup of the exact intra kernel, launched after the factored one
+// on the same grid: it takes only the chunks the factored kernel flagged
+// (some 16-row block decays by more than kMaxBlockDecay), with gam in LDS
+// and pairwise exponentials on the diagonal blocks. Separate kernels keep
+// the factored path's registers and LDS free of the exact path's.
+template <int K, int V>
+__device__ __forceinline__ void intra_exact(const PrefillParams& p, const int4* chunk_info,
+                                            char* recs, uint8_t* exact_flags) {
   using R = Rec<K, V>;
   using SM = IntraSmem<K, V>;
   using XL = XLayout<K>;
@@ -465,9 +631,7 @@ __device__ __forceinline__ void intra_body(const PrefillParams& p, const int4* c
   const int c = uniform(info.x);
   const int64_t t0 = uniform(info.y);
   uint8_t* flag = exact_flags + static_cast<int64_t>(c) * H + h;
-  if constexpr (kExact) {
-    if (*flag == 0) return;  // uniform: the factored kernel took this chunk
-  }
+  if (*flag == 0) return;  // uniform: the factored kernel took this chunk
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -619,181 +783,7 @@ __device__ __forceinline__ void intra_body(const PrefillParams& p, const int4* c
   // in registers until x is free.
   uint32_t wkp[4][PP / 2];
 
-  if constexpr (!kExact) {
-    if (tid == 0) *flag = fast ? 0 : 1;
-    if (!fast) return;  // uniform: left to the exact kernel
-    // ---- 3f. factored operands -------------------------------------------
-    // With the reference rho_I = gam(16 I) of each 16-row block,
-    //   e^{gam_t - gam_s} = R_t F_s c_IJ,  R_t = e^{gam_t - rho_I},
-    //   F_s = e^{rho_J - gam_s},  c_IJ = e^{rho_I - rho_J},
-    // for t in block I and s in block J <= I (c_II = 1). Under the
-    // decay-range bound R lies in [e^-80, 1] and F in [1, e^80]; for J < I,
-    // F_s c_IJ = e^{rho_I - gam_s} <= 1. Nothing overflows, and the diagonal
-    // blocks take their operands as stored (one bf16 rounding each).
-    // Q o e^gam = (Q o R) e^{rho_I} and K o e^{gl - gam} = (K o F) e^{gl - rho_I}
-    // need no further exponential.
-    for (int e = tid; e < 10 * K; e += kThreads) {
-      const int pr = e / K, cc = e % K;
-      const int I = pr < 1 ? 0 : pr < 3 ? 1 : pr < 6 ? 2 : 3;
-      const int J = pr - I * (I + 1) / 2;
-      x[XL::cij + e] = __expf(x[XL::bnd + I * K + cc] - x[XL::bnd + J * K + cc]);
-    }
-    // Record tiles written through buffer resources: 32-bit offsets, no
-    // per-store 64-bit address arithmetic.
-    const __amdgpu_buffer_rsrc_t rqg = make_rsrc(rec + R::Qg, static_cast<uint32_t>(C * K * 2));
-    const __amdgpu_buffer_rsrc_t rkg = make_rsrc(rec + R::KgT, static_cast<uint32_t>(K * C * 2));
-    // The thread's block is the wave's: rho = gam(16 w) per channel.
-    const f32x4 rho = *reinterpret_cast<const f32x4*>(&x[XL::bnd + w * K + c4]);
-    float E[4], sE[4], G[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      E[j] = __expf(rho[j]);
-      sE[j] = p.scale * E[j];
-      G[j] = __expf(gl[j] - rho[j]);
-    }
-    // The four channels are four consecutive slots of the record's permuted
-    // channel order.
-    const int r8 = (c4 & 31) >> 2;
-    const int qcol = 32 * (c4 >> 5) + 8 * (r8 & 3) + 4 * (r8 >> 2);
-    // Every k and q read first: the in-place writes below would otherwise
-    // keep the compiler from moving later reads ahead of them.
-    uint2 kq[PP], qq[PP];
-#pragma unroll
-    for (int i = 0; i < PP; ++i) {
-      const int o = sw16<K>(part * PP + i, c4);
-      kq[i] = *reinterpret_cast<const uint2*>(&sm.k[o]);
-      qq[i] = *reinterpret_cast<const uint2*>(&sm.q[o]);
-    }
-    float wk_even[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int u4 = 0; u4 < PP / 4; ++u4) {
-      float kgv[4][4];  // [channel][position]
-#pragma unroll
-      for (int i3 = 0; i3 < 4; ++i3) {
-        const int i = 4 * u4 + i3;
-        const int t = part * PP + i;
-        const int o = sw16<K>(t, c4);
-        const float kv[4] = {__uint_as_float(kq[i].x << 16), __uint_as_float(kq[i].x & 0xffff0000u),
-                             __uint_as_float(kq[i].y << 16), __uint_as_float(kq[i].y & 0xffff0000u)};
-        const float qv[4] = {__uint_as_float(qq[i].x << 16), __uint_as_float(qq[i].x & 0xffff0000u),
-                             __uint_as_float(qq[i].y << 16), __uint_as_float(qq[i].y & 0xffff0000u)};
-        float kr[4], qr[4], kf[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float Rt = __expf(gm[i][j] - rho[j]), Ft = __builtin_amdgcn_rcpf(Rt);  // Rt >= e^-80
-          kr[j] = kv[j] * Rt;
-          qr[j] = qv[j] * Rt;
-          kf[j] = kv[j] * Ft;
-          kgv[j][i3] = kf[j] * G[j];
-          // Position pairs share one conversion.
-          if (i & 1) wkp[j][i >> 1] = pack_bf16x2(wk_even[j], kr[j] * E[j]);
-          else wk_even[j] = kr[j] * E[j];
-        }
-        *reinterpret_cast<uint2*>(&sm.k[o]) = uint2{pack_bf16x2(kr[0], kr[1]), pack_bf16x2(kr[2], kr[3])};
-        *reinterpret_cast<uint2*>(&sm.q[o]) = uint2{pack_bf16x2(qr[0], qr[1]), pack_bf16x2(qr[2], qr[3])};
-        *reinterpret_cast<uint2*>(&sm.u.f.kf[o]) = uint2{pack_bf16x2(kf[0], kf[1]), pack_bf16x2(kf[2], kf[3])};
-        typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-        const u32x2 qs = {pack_bf16x2(qr[0] * sE[0], qr[1] * sE[1]), pack_bf16x2(qr[2] * sE[2], qr[3] * sE[3])};
-        __builtin_amdgcn_raw_buffer_store_b64(qs, rqg, rec_elem<K>(t, qcol) * 2, 0, 0);
-      }
-      // (K o e^{gl - gam})^T: 4 consecutive positions are 8 contiguous
-      // bytes of the permuted order.
-      const int tp = part * PP + 4 * u4;
-      const int pin = tp & 31;
-      const int slot0 = pin < 16 ? 2 * pin : 2 * (pin - 16) + 4;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-        const u32x2 v = {pack_bf16x2(kgv[j][0], kgv[j][1]), pack_bf16x2(kgv[j][2], kgv[j][3])};
-        __builtin_amdgcn_raw_buffer_store_b64(v, rkg, rec_elem<C>(c4 + j, 32 * (tp >> 5) + slot0) * 2, 0, 0);
-      }
-    }
-    lds_barrier();
-
-    // ---- 4f. A and P by 16x16 blocks on MFMA ------------------------------
-    // A goes transposed into at (strictly above the diagonal); scale P goes
-    // straight to the workspace (bf16, positions permuted), including the
-    // zero blocks above the diagonal that the state kernel reads.
-    {
-      const __amdgpu_buffer_rsrc_t rpm = make_rsrc(rec + R::Pm, static_cast<uint32_t>(C * C * 2));
-      const int blocks[4][3][2] = {{{3, 3}, {3, 0}, {0, 0}},
-                                   {{2, 2}, {3, 1}, {1, 0}},
-                                   {{1, 1}, {3, 2}, {-1, -1}},
-                                   {{2, 1}, {2, 0}, {-1, -1}}};
-      for (int bi = 0; bi < 3; ++bi) {
-        const int I = blocks[w][bi][0], J = blocks[w][bi][1];
-        if (I < 0) break;
-        const float* cv = x + XL::cij + (I * (I + 1) / 2 + J) * K;
-        float bt[4];  // beta of the lane's rows (on the diagonal of at)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) bt[j] = sm.at[sw32<C>(16 * I + 4 * g + j, 16 * I + 4 * g + j)];
-        // Every fragment of the block is read before the first product, so
-        // the reads overlap instead of waiting one channel slice at a time.
-        bf16x8 ak[K / 32], aq[K / 32], b[K / 32];
-#pragma unroll
-        for (int kb = 0; kb < K / 32; ++kb) {
-          const int c0 = 32 * kb + 8 * g;
-          ak[kb] = lds_frag(&sm.k[sw16<K>(16 * I + m, c0)]);
-          aq[kb] = lds_frag(&sm.q[sw16<K>(16 * I + m, c0)]);
-          b[kb] = lds_frag(&sm.u.f.kf[sw16<K>(16 * J + m, c0)]);
-        }
-        if (J < I) {  // wave-uniform
-          f32x4 cf[K / 32][2];
-#pragma unroll
-          for (int kb = 0; kb < K / 32; ++kb) {
-            cf[kb][0] = *reinterpret_cast<const f32x4*>(cv + 32 * kb + 8 * g);
-            cf[kb][1] = *reinterpret_cast<const f32x4*>(cv + 32 * kb + 8 * g + 4);
-          }
-#pragma unroll
-          for (int kb = 0; kb < K / 32; ++kb) {
-            float sc[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) sc[j] = static_cast<float>(b[kb][j]) * cf[kb][j >> 2][j & 3];
-            b[kb] = to_bf16x8(sc);
-          }
-        }
-        // A with block I's positions as rows; P transposed (block J's
-        // positions as rows), so a lane holds four consecutive columns of
-        // one row of P.
-        f32x4 dA = {0.f, 0.f, 0.f, 0.f}, dPt = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < K / 32; ++kb) {
-          dA = mfma16(ak[kb], b[kb], dA);
-          dPt = mfma16(b[kb], aq[kb], dPt);
-        }
-        // dA: lane holds rows 16 I + 4 g + j of column s = 16 J + m. Every
-        // entry is written without a branch: beta stays on the diagonal, and
-        // the entries below it (junk from the masked s > t products) are
-        // overwritten by T before anything reads them.
-        const int s2 = 16 * J + m;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int row = 16 * I + 4 * g + j;
-          sm.at[sw32<C>(s2, row)] = s2 == row ? bt[j] : bt[j] * dA[j];
-        }
-        // dPt: lane holds P[16 I + m][16 J + 4 g + j], j < 4: four
-        // consecutive slots of the permuted position order, one 8-byte store.
-        {
-          const int prow = 16 * I + m;
-          float pv[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) pv[j] = 16 * J + 4 * g + j <= prow ? p.scale * dPt[j] : 0.f;
-          typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-          const u32x2 v = {pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])};
-          __builtin_amdgcn_raw_buffer_store_b64(v, rpm, rec_elem<C>(prow, 32 * (J >> 1) + 8 * g + 4 * (J & 1)) * 2, 0, 0);
-        }
-      }
-      if (w == 3) {
-        // Zero P blocks above the diagonal that the state kernel reads:
-        // rows 0..15 x cols 16..31 and rows 32..47 x cols 48..63 (column
-        // 16 + 4 g + j sits in slot 8 g + 4 + j of its 32-block).
-        typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-        const u32x2 z = {0u, 0u};
-        __builtin_amdgcn_raw_buffer_store_b64(z, rpm, rec_elem<C>(m, 8 * g + 4) * 2, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b64(z, rpm, rec_elem<C>(32 + m, 32 + 8 * g + 4) * 2, 0, 0);
-      }
-    }
-  } else {
+  {
     // ---- 3e/4e. exact path (a block decays by more than the bound) --------
     (void)fast;
     lds_barrier();  // every thread has read the decay ranges (gam overlays x)
@@ -1020,7 +1010,7 @@ __device__ __forceinline__ void intra_body(const PrefillParams& p, const int4* c
   lds_barrier();  // A^T complete; x (or gam) no longer read
 
   // beta of every position as a plain array in the first bytes of the kf
-  // area (dead on both paths from here), for 16-byte reads in step 7.
+  // area (dead from here), for 16-byte reads in the W/U step.
   float* beta_l = reinterpret_cast<float*>(sm.u.f.kf);
   if (tid < C) beta_l[tid] = beta_t;
 
@@ -1033,172 +1023,368 @@ __device__ __forceinline__ void intra_body(const PrefillParams& p, const int4* c
       *reinterpret_cast<uint2*>(wkt + rec_elem<C>(c4 + j, part * PP)) = uint2{wkp[j][0], wkp[j][1]};
   }
 
-  // ---- 5. T = (I + A)^{-1}: diagonal blocks by forward substitution -----
-  // at(s, t) = A[t][s] for s < t; T strictly below the diagonal of at.
-  if (lane < 16) {
-    const int blk = w, jc = lane;
-    float x[16];
-#pragma unroll
-    for (int tt = 0; tt < 16; ++tt) {
-      float v = (tt == jc) ? 1.f : 0.f;
-#pragma unroll
-      for (int s3 = 0; s3 < tt; ++s3) v = fmaf(-sm.at[sw32<C>(16 * blk + s3, 16 * blk + tt)], x[s3], v);
-      x[tt] = v;
-    }
-#pragma unroll
-    for (int tt = 0; tt < 16; ++tt)
-      if (tt > jc) sm.at[sw32<C>(16 * blk + tt, 16 * blk + jc)] = x[tt];
-  }
-  lds_barrier();
+  intra_inverse_wu<K, V>(p, sm.at, wkt, beta_l, vpre, rec, w, lane);
+}
 
-  // ---- 6. off-diagonal blocks of T on fp32 MFMA ---------------------------
-  // With the 32-row halves t (blocks 0, 1) and b (blocks 2, 3):
-  //   T_10 = -T_11 A_10 T_00,  T_32 = -T_33 A_32 T_22,  T_bt = -T_bb (A_bt T_tt).
-  // The 16x16x4 product pairs lane group g of step kk with contraction index
-  // 4 g + kk, so an accumulator tile (rows 4 g + j) is the B operand of the
-  // next product as it stands: step kk takes its element j = kk.
+
+// ------------------------------------------------------ intra, factored --
+//
+// The factored path works through the key channels in halves of 64, so one
+// half's k, q and K o F tiles (24 KiB) are all the tile space it needs: 47
+// KiB of LDS in all, three workgroups per CU. A and P accumulate over the
+// halves in registers; after the last half the tile space holds
+// (K o e^gam)^T for W. Chunks with a block that decays too steeply are
+// flagged for the exact kernel (which recomputes the whole chunk).
+constexpr int kHalf = 64;  // channels per half
+
+template <int K, int V>
+struct IntraHalfSmem {
+  union {
+    struct {
+      uint16_t k[C * kHalf];   // keys, then K o R (sw16<kHalf>)
+      uint16_t q[C * kHalf];   // queries, then Q o R
+      uint16_t kf[C * kHalf];  // K o F
+    } t;
+    uint16_t wkt[K * C];       // (K o e^gam)^T, bf16 [K][C] (swz<C>), after A/P
+  } u;
+  float x[XLayout<kHalf>::end];  // one half's scan totals, bounds, ranges, c_IJ; then beta
+  float at[C * C];               // as in the exact kernel: A^T, T, beta on the diagonal
+};
+
+template <int K, int V>
+__device__ __forceinline__ void intra_factored(const PrefillParams& p, const int4* chunk_info,
+                                               char* recs, uint8_t* exact_flags) {
+  using R = Rec<K, V>;
+  using SM = IntraHalfSmem<K, V>;
+  using XL = XLayout<kHalf>;
+  constexpr int NH = K / kHalf;  // halves
+  __shared__ SM sm;
+
+  const int H = p.H;
+  const int j = static_cast<int>(blockIdx.x / H);
+  const int h = static_cast<int>(blockIdx.x % H);
+  const int4 info = chunk_info[j];
+  const int n = uniform(info.z);
+  if (n <= 0) return;  // uniform
+  const int c = uniform(info.x);
+  const int64_t t0 = uniform(info.y);
+  uint8_t* flag = exact_flags + static_cast<int64_t>(c) * H + h;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = uniform(tid >> 6);
+  const int m = lane & 15;
+  const int g = lane >> 4;
+  char* rec = recs + rec_index(h, c, p) * static_cast<int64_t>(R::bytes);
+
+  // Thread (q4, part) owns channels ch0 + 4 q4 .. + 3 of each half at
+  // positions part PP .. part PP + PP - 1; wave w holds the 16-row block w.
+  constexpr int NQ = kHalf / 4;         // 16 channel quads per half
+  constexpr int NPART = XL::PARTS;      // 16 parts
+  constexpr int PP = C / NPART;         // 4 positions per thread
+  static_assert(NPART * PP == C && (64 / NQ) * PP == 16 && PP == 4, "a wave holds one 16-row block");
+  constexpr int KP8 = kHalf / 8;        // 16-byte pieces per tile row
+  const int q4 = tid % NQ, part = tid / NQ;
+  const int c4 = 4 * q4;
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+  // raw_g of both halves, gate parameters and beta into registers first.
+  const int rs = static_cast<int>(p.qkv_row_stride * 2);  // bytes per mixed_qkv row
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.qkv + t0 * p.qkv_row_stride, static_cast<uint32_t>(n * rs));
+  u32x2 rgw[NH][PP];
+  float dtb[NH][4];
   {
-    auto Tget = [&](int r, int cc) { return r > cc ? sm.at[sw32<C>(r, cc)] : (r == cc ? 1.f : 0.f); };
-    auto Aget = [&](int t, int s) { return s < t ? sm.at[sw32<C>(s, t)] : 0.f; };  // A[t][s]
-    // Operands are read into registers before their products (no LDS
-    // writes intervene), so the reads overlap.
-    if (w < 2) {
-      const int I = 1 + 2 * w, J = 2 * w;
-      float a[4], b[4], t[4];
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.raw_g + t0 * (H * K), static_cast<uint32_t>(n * H * K * 2));
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        a[kk] = Aget(16 * I + m, 16 * J + 4 * g + kk);
-        b[kk] = Tget(16 * J + 4 * g + kk, 16 * J + m);
-        t[kk] = Tget(16 * I + m, 16 * I + 4 * g + kk);
+    for (int hf = 0; hf < NH; ++hf)
+#pragma unroll
+      for (int i = 0; i < PP; ++i)
+        rgw[hf][i] = __builtin_amdgcn_raw_buffer_load_b64(rg, ((part * PP + i) * H * K + h * K + kHalf * hf + c4) * 2, 0, 0);
+#pragma unroll
+    for (int hf = 0; hf < NH; ++hf)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) dtb[hf][jj] = p.dt_bias[h * K + kHalf * hf + c4 + jj];
+  }
+  const float a_h = __expf(p.A_log[h]);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.raw_beta + t0 * H, static_cast<uint32_t>(n * H * 2));
+  const uint16_t rb_bits = __builtin_amdgcn_raw_buffer_load_b16(rb, (tid * H + h) * 2, 0, 0);
+  auto copy_tiles = [&](int hf) {  // one half's q and k columns by LDS DMA
+#pragma unroll
+    for (int r = 0; r < C * KP8 / kThreads; ++r) {
+      const int ps = r * kThreads + tid;
+      const int t = ps / KP8;
+      const int pl = (ps % KP8) ^ (t & (KP8 - 1));
+      const int slot = r * kThreads + (tid & ~63);
+      const int qoff = t * rs + (h * K + kHalf * hf + pl * 8) * 2;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, reinterpret_cast<uint4*>(sm.u.t.q) + slot, 16, qoff, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, reinterpret_cast<uint4*>(sm.u.t.k) + slot, 16, qoff + H * K * 2, 0, 0, 0);
+    }
+  };
+  __builtin_amdgcn_sched_barrier(0);
+  copy_tiles(0);
+  const float beta_t = (tid < n) ? sigmoid_f32(bf16_to_f32(rb_bits)) : 0.f;
+
+  // The blocks (I, J), J <= I, of A and P each wave computes, with their
+  // accumulators kept over the halves.
+  const int blocks[4][3][2] = {{{3, 3}, {3, 0}, {0, 0}},
+                               {{2, 2}, {3, 1}, {1, 0}},
+                               {{1, 1}, {3, 2}, {-1, -1}},
+                               {{2, 1}, {2, 0}, {-1, -1}}};
+  f32x4 dA[3], dPt[3];
+#pragma unroll
+  for (int bi = 0; bi < 3; ++bi) {
+    dA[bi] = f32x4{0.f, 0.f, 0.f, 0.f};
+    dPt[bi] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  uint32_t wkp[NH][4][PP / 2];  // K o e^gam of the thread's channels, bf16 pairs
+  const __amdgpu_buffer_rsrc_t rqg = make_rsrc(rec + R::Qg, static_cast<uint32_t>(C * K * 2));
+  const __amdgpu_buffer_rsrc_t rkg = make_rsrc(rec + R::KgT, static_cast<uint32_t>(K * C * 2));
+
+#pragma unroll
+  for (int hf = 0; hf < NH; ++hf) {
+    const int ch0 = kHalf * hf;
+    if (hf > 0) {
+      // Every wave is done with the previous half's tiles.
+      lds_barrier();
+      copy_tiles(hf);
+    }
+    // ---- gate and cumulative log-decay of the half, in registers ---------
+    float gm[PP][4];
+    float gl[4] = {0.f, 0.f, 0.f, 0.f};
+    {
+      const bool has_lb = p.has_lb != 0;
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < PP; ++i) {
+        const bool live = part * PP + i < n;
+        const float rg4[4] = {__uint_as_float(rgw[hf][i][0] << 16), __uint_as_float(rgw[hf][i][0] & 0xffff0000u),
+                              __uint_as_float(rgw[hf][i][1] << 16), __uint_as_float(rgw[hf][i][1] & 0xffff0000u)};
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const float gv = gate_log_decay(rg4[jj], dtb[hf][jj], a_h, has_lb, p.lower_bound);
+          acc[jj] += live ? gv : 0.f;
+          gm[i][jj] = acc[jj];
+        }
       }
-      f32x4 z = {0.f, 0.f, 0.f, 0.f}, tij = {0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<f32x4*>(&sm.x[XL::tot + part * kHalf + c4]) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+      lds_barrier();  // partial totals visible
+      float before[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) z = mfma4(a[kk], b[kk], z);
+      for (int q2 = 0; q2 < NPART; ++q2) {
+        const f32x4 tq = *reinterpret_cast<const f32x4*>(&sm.x[XL::tot + q2 * kHalf + c4]);
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) tij = mfma4(t[kk], z[kk], tij);
+        for (int jj = 0; jj < 4; ++jj) {
+          if (q2 < part) before[jj] += tq[jj];
+          gl[jj] += tq[jj];
+        }
+      }
+      if (hf == 0 && tid < C) sm.at[sw32<C>(tid, tid)] = beta_t;  // beta on the diagonal of at
 #pragma unroll
-      for (int j = 0; j < 4; ++j) sm.at[sw32<C>(16 * I + 4 * g + j, 16 * J + m)] = -tij[j];
+      for (int i = 0; i < PP; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) gm[i][jj] += before[jj];
+      // Block w's bound gam(16 w) is row 0 of the wave's first part (lanes
+      // 0 .. NQ-1); its row 15 is the last row of the wave's last part.
+      float d = 0.f;
+      {
+        float last[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) last[jj] = __shfl_xor(gm[PP - 1][jj], 64 - NQ);
+        if (lane < NQ) {
+          *reinterpret_cast<f32x4*>(&sm.x[XL::bnd + w * kHalf + c4]) = f32x4{gm[0][0], gm[0][1], gm[0][2], gm[0][3]};
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) d = fmaxf(d, gm[0][jj] - last[jj]);
+        }
+      }
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) d = fmaxf(d, __shfl_xor(d, off));
+      if (lane == 0) sm.x[XL::dmax + w] = d;
+      if (part == 0)
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(rec + R::Eg) + ch0 + c4) =
+            f32x4{__expf(gl[0]), __expf(gl[1]), __expf(gl[2]), __expf(gl[3])};
+    }
+    wait_vmem();  // this half's k and q copies (and every load before them) have landed
+    lds_barrier();
+    bool fast = true;
+#pragma unroll
+    for (int I = 0; I < 4; ++I) fast = fast && sm.x[XL::dmax + I] <= kMaxBlockDecay;
+    if (!fast) {  // uniform: the exact kernel takes the whole chunk
+      if (tid == 0) *flag = 1;
+      return;
+    }
+    // ---- factored operands of the half (see the exact kernel's notes) -----
+    for (int e = tid; e < 10 * kHalf; e += kThreads) {
+      const int pr = e / kHalf, cc = e % kHalf;
+      const int I = pr < 1 ? 0 : pr < 3 ? 1 : pr < 6 ? 2 : 3;
+      const int J = pr - I * (I + 1) / 2;
+      sm.x[XL::cij + e] = __expf(sm.x[XL::bnd + I * kHalf + cc] - sm.x[XL::bnd + J * kHalf + cc]);
+    }
+    const f32x4 rho = *reinterpret_cast<const f32x4*>(&sm.x[XL::bnd + w * kHalf + c4]);
+    float E[4], sE[4], G[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      E[jj] = __expf(rho[jj]);
+      sE[jj] = p.scale * E[jj];
+      G[jj] = __expf(gl[jj] - rho[jj]);
+    }
+    const int cg4 = ch0 + c4;  // the thread's first channel of the head
+    const int r8 = (cg4 & 31) >> 2;
+    const int qcol = 32 * (cg4 >> 5) + 8 * (r8 & 3) + 4 * (r8 >> 2);
+    uint2 kq[PP], qq[PP];
+#pragma unroll
+    for (int i = 0; i < PP; ++i) {
+      const int o = sw16<kHalf>(part * PP + i, c4);
+      kq[i] = *reinterpret_cast<const uint2*>(&sm.u.t.k[o]);
+      qq[i] = *reinterpret_cast<const uint2*>(&sm.u.t.q[o]);
+    }
+    float wk_even[4] = {0.f, 0.f, 0.f, 0.f};
+    float kgv[4][PP];  // [channel][position]
+#pragma unroll
+    for (int i = 0; i < PP; ++i) {
+      const int t = part * PP + i;
+      const int o = sw16<kHalf>(t, c4);
+      const float kv[4] = {__uint_as_float(kq[i].x << 16), __uint_as_float(kq[i].x & 0xffff0000u),
+                           __uint_as_float(kq[i].y << 16), __uint_as_float(kq[i].y & 0xffff0000u)};
+      const float qv[4] = {__uint_as_float(qq[i].x << 16), __uint_as_float(qq[i].x & 0xffff0000u),
+                           __uint_as_float(qq[i].y << 16), __uint_as_float(qq[i].y & 0xffff0000u)};
+      float kr[4], qr[4], kf[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const float Rt = __expf(gm[i][jj] - rho[jj]), Ft = __builtin_amdgcn_rcpf(Rt);  // Rt >= e^-80
+        kr[jj] = kv[jj] * Rt;
+        qr[jj] = qv[jj] * Rt;
+        kf[jj] = kv[jj] * Ft;
+        kgv[jj][i] = kf[jj] * G[jj];
+        if (i & 1) wkp[hf][jj][i >> 1] = pack_bf16x2(wk_even[jj], kr[jj] * E[jj]);
+        else wk_even[jj] = kr[jj] * E[jj];
+      }
+      *reinterpret_cast<uint2*>(&sm.u.t.k[o]) = uint2{pack_bf16x2(kr[0], kr[1]), pack_bf16x2(kr[2], kr[3])};
+      *reinterpret_cast<uint2*>(&sm.u.t.q[o]) = uint2{pack_bf16x2(qr[0], qr[1]), pack_bf16x2(qr[2], qr[3])};
+      *reinterpret_cast<uint2*>(&sm.u.t.kf[o]) = uint2{pack_bf16x2(kf[0], kf[1]), pack_bf16x2(kf[2], kf[3])};
+      const u32x2 qs = {pack_bf16x2(qr[0] * sE[0], qr[1] * sE[1]), pack_bf16x2(qr[2] * sE[2], qr[3] * sE[3])};
+      __builtin_amdgcn_raw_buffer_store_b64(qs, rqg, rec_elem<K>(t, qcol) * 2, 0, 0);
+    }
+    {
+      // (K o e^{gl - gam})^T: the 4 positions are 8 contiguous bytes of the
+      // permuted order.
+      const int tp = part * PP;
+      const int pin = tp & 31;
+      const int slot0 = pin < 16 ? 2 * pin : 2 * (pin - 16) + 4;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const u32x2 v = {pack_bf16x2(kgv[jj][0], kgv[jj][1]), pack_bf16x2(kgv[jj][2], kgv[jj][3])};
+        __builtin_amdgcn_raw_buffer_store_b64(v, rkg, rec_elem<C>(cg4 + jj, 32 * (tp >> 5) + slot0) * 2, 0, 0);
+      }
     }
     lds_barrier();
-    {
-      const int I = 2 + (w >> 1), J = w & 1;
-      float a2[2][4], a3[2][4], b[2][4], t2[4], t3[4];
+    // ---- A and P over the half's channels, accumulated --------------------
 #pragma unroll
-      for (int M = 0; M < 2; ++M)
+    for (int bi = 0; bi < 3; ++bi) {
+      const int I = blocks[w][bi][0], J = blocks[w][bi][1];
+      if (I >= 0) {  // wave-uniform
+        const float* cv = sm.x + XL::cij + (I * (I + 1) / 2 + J) * kHalf;
+        bf16x8 ak[kHalf / 32], aq[kHalf / 32], b[kHalf / 32];
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          b[M][kk] = Tget(16 * M + 4 * g + kk, 16 * J + m);  // zero for M < J
-          a2[M][kk] = Aget(32 + m, 16 * M + 4 * g + kk);
-          a3[M][kk] = Aget(48 + m, 16 * M + 4 * g + kk);
+        for (int kb = 0; kb < kHalf / 32; ++kb) {
+          const int c0 = 32 * kb + 8 * g;
+          ak[kb] = lds_frag(&sm.u.t.k[sw16<kHalf>(16 * I + m, c0)]);
+          aq[kb] = lds_frag(&sm.u.t.q[sw16<kHalf>(16 * I + m, c0)]);
+          b[kb] = lds_frag(&sm.u.t.kf[sw16<kHalf>(16 * J + m, c0)]);
+        }
+        if (J < I) {
+#pragma unroll
+          for (int kb = 0; kb < kHalf / 32; ++kb) {
+            const f32x4 c0v = *reinterpret_cast<const f32x4*>(cv + 32 * kb + 8 * g);
+            const f32x4 c1v = *reinterpret_cast<const f32x4*>(cv + 32 * kb + 8 * g + 4);
+            float sc[8];
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) sc[jj] = static_cast<float>(b[kb][jj]) * (jj < 4 ? c0v[jj] : c1v[jj - 4]);
+            b[kb] = to_bf16x8(sc);
+          }
         }
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        t2[kk] = Tget(16 * I + m, 32 + 4 * g + kk);
-        t3[kk] = Tget(48 + m, 48 + 4 * g + kk);
-      }
-      f32x4 y2 = {0.f, 0.f, 0.f, 0.f}, y3 = {0.f, 0.f, 0.f, 0.f}, tij = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int M = 0; M < 2; ++M)
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          y2 = mfma4(a2[M][kk], b[M][kk], y2);
-          y3 = mfma4(a3[M][kk], b[M][kk], y3);
+        for (int kb = 0; kb < kHalf / 32; ++kb) {
+          dA[bi] = mfma16(ak[kb], b[kb], dA[bi]);
+          dPt[bi] = mfma16(b[kb], aq[kb], dPt[bi]);
         }
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) tij = mfma4(t2[kk], y2[kk], tij);
-      if (I == 3) {
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) tij = mfma4(t3[kk], y3[kk], tij);
       }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) sm.at[sw32<C>(16 * I + 4 * g + j, 16 * J + m)] = -tij[j];
     }
-    lds_barrier();
   }
+  if (tid == 0) *flag = 0;
 
-  // ---- 7. W = T diag(beta)(K o e^gam), U = T diag(beta) V on MFMA -------
-  // beta is folded into the fp32 columns of T before the bf16 cast, so V
-  // enters the product exactly as given. T is lower triangular, so rows
-  // 0..31 need only positions 0..31.
+  // ---- A^T into at, scale P into the record -------------------------------
   {
-    // T diag(beta) as bf16 fragments: row 16 pb + m, positions 32 kb + 8 g
-    // .. +7, read as two 16-byte pieces of at (T strictly below the
-    // diagonal; the diagonal and above are masked by index).
-    bf16x8 Tf[4][2];
+    const __amdgpu_buffer_rsrc_t rpm = make_rsrc(rec + R::Pm, static_cast<uint32_t>(C * C * 2));
 #pragma unroll
-    for (int pb = 0; pb < 4; ++pb)
+    for (int bi = 0; bi < 3; ++bi) {
+      const int I = blocks[w][bi][0], J = blocks[w][bi][1];
+      if (I >= 0) {
+        float bt[4];  // beta of the lane's rows (on the diagonal of at)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int row = 16 * pb + m;
-        const int c0 = 32 * kb + 8 * g;
-        const f32x4 t0 = *reinterpret_cast<const f32x4*>(&sm.at[sw32<C>(row, c0)]);
-        const f32x4 t1 = *reinterpret_cast<const f32x4*>(&sm.at[sw32<C>(row, c0 + 4)]);
-        const f32x4 b0 = *reinterpret_cast<const f32x4*>(&beta_l[c0]);
-        const f32x4 b1 = *reinterpret_cast<const f32x4*>(&beta_l[c0 + 4]);
-        float tv[8];
+        for (int jj = 0; jj < 4; ++jj) bt[jj] = sm.at[sw32<C>(16 * I + 4 * g + jj, 16 * I + 4 * g + jj)];
+        const int s2 = 16 * J + m;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int col = c0 + j;
-          const float tval = j < 4 ? t0[j] : t1[j - 4];
-          const float bcol = j < 4 ? b0[j] : b1[j - 4];
-          tv[j] = (col < row ? tval : (col == row ? 1.f : 0.f)) * bcol;
+        for (int jj = 0; jj < 4; ++jj) {
+          const int row = 16 * I + 4 * g + jj;
+          sm.at[sw32<C>(s2, row)] = s2 == row ? bt[jj] : bt[jj] * dA[bi][jj];
         }
-        Tf[pb][kb] = to_bf16x8(tv);
-      }
-    // -W^T = -(K o e^gam)^T (T diag(beta))^T: the same fragments with the
-    // operands swapped leave lane (m, g) four consecutive channels
-    // 16 nb + 4 g .. +3 of position 16 pb + m, which are four consecutive
-    // slots of the record's permuted channel order: one 8-byte store each.
-    {
-      const __amdgpu_buffer_rsrc_t rwn = make_rsrc(rec + R::Wn, static_cast<uint32_t>(C * K * 2));
-      typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-      for (int nb = w; nb < K / 16; nb += 4) {
-        bf16x8 Bf[2];
+        const int prow = 16 * I + m;
+        float pv[4];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) Bf[kb] = frag<C>(wkt, 16 * nb + m, 32 * kb + 8 * g);
-        const int col = 32 * (nb >> 1) + 8 * g + 4 * (nb & 1);
-#pragma unroll
-        for (int pb = 0; pb < 4; ++pb) {
-          f32x4 D = mfma16(Bf[0], Tf[pb][0], f32x4{0.f, 0.f, 0.f, 0.f});
-          if (pb >= 2) D = mfma16(Bf[1], Tf[pb][1], D);
-          const u32x2 v = {pack_bf16x2(-D[0], -D[1]), pack_bf16x2(-D[2], -D[3])};
-          __builtin_amdgcn_raw_buffer_store_b64(v, rwn, rec_elem<K>(16 * pb + m, col) * 2, 0, 0);
-        }
+        for (int jj = 0; jj < 4; ++jj) pv[jj] = 16 * J + 4 * g + jj <= prow ? p.scale * dPt[bi][jj] : 0.f;
+        const u32x2 v = {pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])};
+        __builtin_amdgcn_raw_buffer_store_b64(v, rpm, rec_elem<C>(prow, 32 * (J >> 1) + 8 * g + 4 * (J & 1)) * 2, 0, 0);
       }
     }
-    // U written straight out in accumulator fragment order.
-    f32x4* uf = reinterpret_cast<f32x4*>(rec + R::Uf);
+    if (w == 3) {
+      const u32x2 z = {0u, 0u};
+      __builtin_amdgcn_raw_buffer_store_b64(z, rpm, rec_elem<C>(m, 8 * g + 4) * 2, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b64(z, rpm, rec_elem<C>(32 + m, 32 + 8 * g + 4) * 2, 0, 0);
+    }
+  }
+  // v for the U phase, fetched now so its latency hides behind the inverse.
+  constexpr int NBU = (V / 16 + 3) / 4;
+  static_assert(V / 16 <= 4 * NBU && V / 16 > 4 * (NBU - 1), "every wave has NBU column blocks");
+  uint16_t vpre[NBU][2][8];
+  {
+    const int vlane = (2 * H * K + h * V + m) * 2 + 8 * g * rs;
 #pragma unroll
-    for (int u = 0; u < NBU; ++u) {
-      const int nb = w + 4 * u;
-      if (nb >= V / 16) break;
-      bf16x8 Bv[2];
+    for (int u = 0; u < NBU; ++u)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) Bv[kb][j] = __builtin_bit_cast(__bf16, vpre[u][kb][j]);
-#pragma unroll
-      for (int pb = 0; pb < 4; ++pb) {
-        f32x4 D = mfma16(Tf[pb][0], Bv[0], f32x4{0.f, 0.f, 0.f, 0.f});
-        if (pb >= 2) D = mfma16(Tf[pb][1], Bv[1], D);
-        uf[(pb * (V / 16) + nb) * 64 + lane] = D;
-      }
-    }
+        for (int jj = 0; jj < 8; ++jj) {
+          const int nb = w + 4 * u;
+          vpre[u][kb][jj] = __builtin_amdgcn_raw_buffer_load_b16(rq, vlane + 32 * nb, (32 * kb + jj) * rs, 0);
+        }
   }
+  lds_barrier();  // A^T complete; tiles and x no longer read
+
+  float* beta_l = sm.x;
+  if (tid < C) beta_l[tid] = beta_t;
+  uint16_t* wkt = sm.u.wkt;
+  // (K o e^gam)^T: 8 bytes (4 positions) per channel and half.
+#pragma unroll
+  for (int hf = 0; hf < NH; ++hf)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+      *reinterpret_cast<uint2*>(wkt + rec_elem<C>(kHalf * hf + c4 + jj, part * PP)) = uint2{wkp[hf][jj][0], wkp[hf][jj][1]};
+
+  intra_inverse_wu<K, V>(p, sm.at, wkt, beta_l, vpre, rec, w, lane);
 }
 
 template <int K, int V>
-__global__ __launch_bounds__(kThreads, 2) void chunk_intra_kernel(const PrefillParams p,
+__global__ __launch_bounds__(kThreads, 3) void chunk_intra_kernel(const PrefillParams p,
                                                                   const int4* chunk_info,
                                                                   char* recs, uint8_t* exact_flags) {
-  intra_body<K, V, false>(p, chunk_info, recs, exact_flags);
+  intra_factored<K, V>(p, chunk_info, recs, exact_flags);
 }
 
 template <int K, int V>
 __global__ __launch_bounds__(kThreads, 2) void chunk_intra_exact_kernel(const PrefillParams p,
                                                                         const int4* chunk_info,
                                                                         char* recs, uint8_t* exact_flags) {
-  intra_body<K, V, true>(p, chunk_info, recs, exact_flags);
+  intra_exact<K, V>(p, chunk_info, recs, exact_flags);
 }
 
 
