@@ -1562,60 +1562,130 @@ __global__ __launch_bounds__(kThreads, NB == 1 ? 2 : 1) void chunk_state_kernel(
   // into bf16 hi + lo parts and the product is hi*hi + hi*lo + lo*hi (about
   // 16 significant bits, fp32 accumulation).
   if (li >= 0 && sg > 0) {
-    // Flattened over (step j, row tile rt); tile i + 1's operands are loaded
-    // while tile i computes (the scheduling barriers keep that order).
     const int mi0 = seg0 - seq;  // the sequence's first map item
     const int64_t item = static_cast<int64_t>(K) * K + static_cast<int64_t>(K) * V;
     constexpr int RT = K / 16, KB = K / 32;
-    auto load_tile = [&](int i, f32x4 (&a)[KB][2], f32x4& b) {
-      const float* M = pl.maps + map_index(h, mi0 + i / RT, pl) * item;
-      const int rt = i % RT;
-      const float* row = M + (16 * rt + m) * K + 4 * g;
+    if constexpr (NB == 2) {
+      // M goes through the idle second record buffer, 32 rows (two row
+      // tiles) per stage, two stages in flight: the workgroup reads M from
+      // L2 once instead of once per wave. Stage rows are stored with their
+      // 16-byte pieces XOR-swizzled by the row (piece p of row r at p ^ (r &
+      // 15)), so the 16 rows a fragment read touches fall in different banks.
+      constexpr int QR = 32;                 // rows per stage
+      constexpr int PPR = K / 4;             // 16-byte pieces per row
+      constexpr int SBYTES = QR * K * 4;
+      constexpr int SPS = K / QR;            // stages per map step
+      static_assert(2 * SBYTES <= static_cast<int>(sizeof(B)), "two stages fit the idle buffer");
+      static_assert((QR * PPR) % kThreads == 0, "whole DMA rounds");
+      float* stage_buf = reinterpret_cast<float*>(&buf[1]);
+      auto dma_stage = [&](int st) {  // stage st of the walk into its half of the buffer
+        const float* M = pl.maps + map_index(h, mi0 + st / SPS, pl) * item + static_cast<int64_t>(st % SPS) * QR * K;
+        const __amdgpu_buffer_rsrc_t rr = make_rsrc(M, static_cast<uint32_t>(SBYTES));
+        uint4* dst = reinterpret_cast<uint4*>(stage_buf + (st & 1) * (SBYTES / 4));
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        a[kb][0] = *reinterpret_cast<const f32x4*>(row + 32 * kb);
-        a[kb][1] = *reinterpret_cast<const f32x4*>(row + 32 * kb + 16);
-      }
-      const float* Bm = M + static_cast<int64_t>(K) * K;
+        for (int r = 0; r < QR * PPR / kThreads; ++r) {
+          const int ps = r * kThreads + tid;  // physical piece of the stage
+          const int row = ps / PPR, pp = ps % PPR;
+          const int pl = pp ^ (row & 15);     // logical piece stored there
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, dst + r * kThreads + (tid & ~63), 16,
+                                                   (row * PPR + pl) * 16, 0, 0, 0);
+        }
+      };
+      bf16x8 Sh[KB], Sl[KB];
+      const int stages = sg * SPS;
+      dma_stage(0);
+      for (int st = 0; st < stages; ++st) {
+        // Stage st has landed in every thread's pieces, and every wave is
+        // done with the half stage st + 1 overwrites.
+        wait_vmem();
+        lds_barrier();
+        if (st + 1 < stages) dma_stage(st + 1);
+        const float* sb = stage_buf + (st & 1) * (SBYTES / 4);
+        const float* Bm = pl.maps + map_index(h, mi0 + st / SPS, pl) * item + static_cast<int64_t>(K) * K;
+        if (st % SPS == 0) {
+          // Operands of this step: the state before it, as bf16 hi + lo.
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) b[jj] = Bm[(16 * rt + 4 * g + jj) * V + col0 + m];
-    };
-    f32x4 a_cur[KB][2], a_nxt[KB][2], b_cur, b_nxt;
-    bf16x8 Sh[KB], Sl[KB];
-    load_tile(0, a_cur, b_cur);
-    const int tiles = sg * RT;
-    for (int i = 0; i < tiles; ++i) {
-      const int rt = i % RT;
-      if (rt == 0) {
-        // Operands of this step: the state before it, as bf16 hi + lo.
+          for (int kb = 0; kb < KB; ++kb) {
+            Sh[kb] = pack_acc(S[2 * kb], S[2 * kb + 1]);
+            Sl[kb] = pack_lo(S[2 * kb], S[2 * kb + 1], Sh[kb]);
+          }
+        }
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          Sh[kb] = pack_acc(S[2 * kb], S[2 * kb + 1]);
-          Sl[kb] = pack_lo(S[2 * kb], S[2 * kb + 1], Sh[kb]);
+        for (int t2 = 0; t2 < QR / 16; ++t2) {
+          const int rt = (st % SPS) * (QR / 16) + t2;
+          f32x4 acc;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) acc[jj] = Bm[(16 * rt + 4 * g + jj) * V + col0 + m];
+          const float* row = sb + (16 * t2 + m) * K;
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) {
+            const f32x4 a0 = *reinterpret_cast<const f32x4*>(row + 4 * ((8 * kb + g) ^ m));
+            const f32x4 a1 = *reinterpret_cast<const f32x4*>(row + 4 * ((8 * kb + 4 + g) ^ m));
+            const bf16x8 ah = pack_acc(a0, a1);
+            const bf16x8 al = pack_lo(a0, a1, ah);
+            acc = mfma16(ah, Sh[kb], acc);
+            acc = mfma16(ah, Sl[kb], acc);
+            acc = mfma16(al, Sh[kb], acc);
+          }
+          // Row tile rt of the new state (the old tiles live on in Sh/Sl).
+#pragma unroll
+          for (int r2 = 0; r2 < RT; ++r2)
+            if (r2 == rt) S[r2] = acc;
         }
       }
-      __builtin_amdgcn_sched_barrier(0);
-      if (i + 1 < tiles) load_tile(i + 1, a_nxt, b_nxt);
-      __builtin_amdgcn_sched_barrier(0);
-      f32x4 acc = b_cur;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const bf16x8 ah = pack_acc(a_cur[kb][0], a_cur[kb][1]);
-        const bf16x8 al = pack_lo(a_cur[kb][0], a_cur[kb][1], ah);
-        acc = mfma16(ah, Sh[kb], acc);
-        acc = mfma16(ah, Sl[kb], acc);
-        acc = mfma16(al, Sh[kb], acc);
+    } else {
+      // Flattened over (step j, row tile rt); tile i + 1's operands are loaded
+      // while tile i computes (the scheduling barriers keep that order).
+      auto load_tile = [&](int i, f32x4 (&a)[KB][2], f32x4& b) {
+        const float* M = pl.maps + map_index(h, mi0 + i / RT, pl) * item;
+        const int rt = i % RT;
+        const float* row = M + (16 * rt + m) * K + 4 * g;
+  #pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          a[kb][0] = *reinterpret_cast<const f32x4*>(row + 32 * kb);
+          a[kb][1] = *reinterpret_cast<const f32x4*>(row + 32 * kb + 16);
+        }
+        const float* Bm = M + static_cast<int64_t>(K) * K;
+  #pragma unroll
+        for (int jj = 0; jj < 4; ++jj) b[jj] = Bm[(16 * rt + 4 * g + jj) * V + col0 + m];
+      };
+      f32x4 a_cur[KB][2], a_nxt[KB][2], b_cur, b_nxt;
+      bf16x8 Sh[KB], Sl[KB];
+      load_tile(0, a_cur, b_cur);
+      const int tiles = sg * RT;
+      for (int i = 0; i < tiles; ++i) {
+        const int rt = i % RT;
+        if (rt == 0) {
+          // Operands of this step: the state before it, as bf16 hi + lo.
+  #pragma unroll
+          for (int kb = 0; kb < KB; ++kb) {
+            Sh[kb] = pack_acc(S[2 * kb], S[2 * kb + 1]);
+            Sl[kb] = pack_lo(S[2 * kb], S[2 * kb + 1], Sh[kb]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (i + 1 < tiles) load_tile(i + 1, a_nxt, b_nxt);
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4 acc = b_cur;
+  #pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const bf16x8 ah = pack_acc(a_cur[kb][0], a_cur[kb][1]);
+          const bf16x8 al = pack_lo(a_cur[kb][0], a_cur[kb][1], ah);
+          acc = mfma16(ah, Sh[kb], acc);
+          acc = mfma16(ah, Sl[kb], acc);
+          acc = mfma16(al, Sh[kb], acc);
+        }
+        // Row tile rt of the new state (the old tiles live on in Sh/Sl).
+  #pragma unroll
+        for (int r2 = 0; r2 < RT; ++r2)
+          if (r2 == rt) S[r2] = acc;
+  #pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          a_cur[kb][0] = a_nxt[kb][0];
+          a_cur[kb][1] = a_nxt[kb][1];
+        }
+        b_cur = b_nxt;
       }
-      // Row tile rt of the new state (the old tiles live on in Sh/Sl).
-#pragma unroll
-      for (int r2 = 0; r2 < RT; ++r2)
-        if (r2 == rt) S[r2] = acc;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        a_cur[kb][0] = a_nxt[kb][0];
-        a_cur[kb][1] = a_nxt[kb][1];
-      }
-      b_cur = b_nxt;
     }
   }
   // Lane (m, g) of the transposed output tile of position block pb holds
