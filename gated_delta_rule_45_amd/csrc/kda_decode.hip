@@ -40,6 +40,9 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kMaxTokens = 8;
+// Requests of at least this many tokens on tiles of at most 32 columns take
+// the block (WY) form of the token chain.
+constexpr int kBlockMinTokens = 3;
 
 // Sum of x over the lanes that share lane % CG (CG = 4, 8, 16 or 32): a
 // butterfly on VALU lane permutations, no LDS traffic. Inside a 16-lane row
@@ -302,11 +305,360 @@ void decode_kernel(const DecodeParams p) {
   }
 }
 
+namespace {
+
+// x rotated right by N lanes inside each 16-lane row (DPP row_ror).
+template <int N>
+__device__ __forceinline__ float row_ror(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + N, 0xf, 0xf, false));
+}
+
+// One step of a recursive halving over the row-group bits of the lane
+// index: lanes with bit B clear keep the lower HALF of their value list and
+// lanes with it set the upper half, each adding the partner's copy of the
+// half it keeps. Bits 2 and 3 pair lanes by DPP rotations inside a 16-lane
+// row (a rotation by 4 or 8 flips that bit; the step for the next bit
+// completes the coverage); bits 4 and 5 by v_permlane16_swap /
+// v_permlane32_swap, which leave the kept half's two copies in the two
+// operands. Every lane must be active.
+template <int B, int HALF, int N>
+__device__ __forceinline__ void halve_step(float (&x)[N], int lane) {
+  if constexpr (B < 4) {
+    const bool hi = (lane >> B) & 1;
+#pragma unroll
+    for (int v = 0; v < HALF; ++v) {
+      const float keep = hi ? x[HALF + v] : x[v];
+      const float send = hi ? x[v] : x[HALF + v];
+      x[v] = keep + row_ror<(B == 2 ? 4 : 8)>(send);
+    }
+  } else {
+#pragma unroll
+    for (int v = 0; v < HALF; ++v) {
+      const uint32_t lo = __float_as_uint(x[v]), up = __float_as_uint(x[HALF + v]);
+      const auto r = B == 4 ? __builtin_amdgcn_permlane16_swap(lo, up, false, false)
+                            : __builtin_amdgcn_permlane32_swap(lo, up, false, false);
+      x[v] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+  }
+}
+
+// Sums of the N values over the wave's row groups (lanes that share
+// lane % CG), N / (64 / CG) of them left per lane: block B of the list, the
+// lowest row-group bit being B's most significant bit.
+template <int CG, int N>
+__device__ __forceinline__ void halve_row_groups(float (&x)[N], int lane) {
+  constexpr int first = CG == 4 ? 2 : CG == 8 ? 3 : CG == 16 ? 4 : 5;
+  static_assert((64 / CG) <= N, "fewer values than row groups");
+  if constexpr (first <= 2) halve_step<2, (N >> (3 - first))>(x, lane);
+  if constexpr (first <= 3) halve_step<3, (N >> (4 - first))>(x, lane);
+  if constexpr (first <= 4) halve_step<4, (N >> (5 - first))>(x, lane);
+  halve_step<5, (N >> (6 - first))>(x, lane);
+}
+
+}  // namespace
+
+// Spec-verify blocks of 3..8 tokens on narrow column tiles (the latency
+// case: few requests, one workgroup per CU). The per-token chain of the
+// decode kernel (a K-reduction, a cross-wave exchange and a barrier per
+// token) is replaced by the WY form of the block. With G_t the running sum
+// of the log decays through token t (per key channel):
+//   S'_t^T k_t = X_t + sum_{s<t} A_ts u_s,   X_t = S0^T (e^{G_t} * k_t),
+//   S_t^T q_t  = Y_t + sum_{s<=t} P_ts u_s,  Y_t = S0^T (e^{G_t} * q_t),
+//   A_ts = sum_i k_s[i] k_t[i] e^{G_t[i] - G_s[i]},  P_ts likewise with q_t,
+// so u_t = beta_t (v_t - X_t - sum_{s<t} A_ts u_s) and
+// o_t = scale (Y_t + sum_{s<=t} P_ts u_s). Every reduction against the state
+// is taken at once from S0 (one halving over the wave's row groups, one
+// exchange through LDS); the scalars A and P are formed while the state
+// loads are in flight; the u recurrence is per-column scalar work; and the
+// state then takes its tokens in registers, S = diag(e^{g_t}) S + k_t u_t^T
+// (stored after every token with a state per token). The exponents
+// G_t - G_s are never positive. NT is the token capacity (4 or 8).
+template <int K, int V, int VT, int NT>
+__global__ __launch_bounds__(256) void spec_block_kernel(const DecodeParams p) {
+  constexpr int RW = K / kWaves;
+  constexpr int CG = VT / 4;
+  constexpr int RG = 64 / CG;
+  constexpr int RPL = RW / RG;
+  constexpr int NVAL = 8 * NT;       // X and Y for NT tokens and 4 columns
+  constexpr int NKEEP = NVAL / RG;   // of them held by a lane after the halving
+  static_assert(CG * RG == 64 && RPL * RG == RW && RPL >= 1 && NKEEP >= 1, "tile does not fit");
+  static_assert(NT * (NT + 1) / 2 + NT * (NT - 1) / 2 <= 64, "one quad per A/P entry");
+
+  __shared__ __align__(16) float s_q[NT][K];
+  __shared__ __align__(16) float s_k[NT][K];
+  __shared__ __align__(16) float s_a[NT][K];   // e^{g_t}
+  __shared__ __align__(16) float s_G[NT][K];   // G_t
+  __shared__ __align__(16) float s_ck[NT][K];  // e^{G_t} k_t
+  __shared__ __align__(16) float s_cq[NT][K];  // e^{G_t} q_t
+  __shared__ __align__(16) float s_v[NT][VT];
+  __shared__ __align__(16) float s_u[NT][VT];
+  __shared__ float s_b[NT];
+  __shared__ float s_A[NT][NT];
+  __shared__ float s_P[NT][NT];
+  __shared__ __align__(16) float s_xy[kWaves][CG][NVAL];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int H = p.H;
+  const int T = p.tokens_per_seq;
+  constexpr int tiles = V / VT;
+  const int64_t bid = blockIdx.x;
+  const int tile = static_cast<int>(bid % tiles);
+  const int64_t nh = bid / tiles;
+  const int h = static_cast<int>(nh % H);
+  const int n = static_cast<int>(nh / H);
+  const int64_t row0 = static_cast<int64_t>(n) * T;
+  const int cg = lane % CG;
+  const int rg = lane / CG;
+  const int col = tile * VT + cg * 4;
+
+  const int32_t* irow = p.indices + static_cast<int64_t>(n) * p.index_stride;
+  const bool per_token = p.num_accepted != nullptr;
+  int init_col = 0;
+  if (per_token) init_col = min(max(uniform(p.num_accepted[n]), 1), T) - 1;
+  const int64_t slot = uniform(static_cast<int64_t>(irow[init_col * p.index_col_stride]));
+
+  if (slot < 0) {
+    for (int e = tid; e < T * VT; e += blockDim.x) {
+      const int t = e / VT, j = e % VT;
+      p.out[((row0 + t) * H + h) * static_cast<int64_t>(V) + tile * VT + j] = 0;
+    }
+    return;
+  }
+
+  // 1. Per-token input loads, then the state loads: the inputs arrive
+  //    first (loads complete in order) and the A/P work below overlaps the
+  //    state's memory latency. Thread i < K owns key channel i for every
+  //    token (the running sum G runs down its tokens); the others stage v
+  //    and beta. Loads past the request's rows read zero, so padded tokens
+  //    carry q = k = 0 and g = 0.
+  constexpr int NVE = (NT * VT + 255 - K) / (256 - K);  // v elements per staging thread
+  const int rs = static_cast<int>(p.qkv_row_stride) * 2;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.qkv + row0 * p.qkv_row_stride, static_cast<uint32_t>(T * rs));
+  uint16_t qb[NT], kb[NT], gb[NT], vb[NVE], bb = 0;
+  float db = 0.f;
+  if (tid < K) {
+    const int i = tid;
+    const __amdgpu_buffer_rsrc_t rgt = make_rsrc(p.raw_g + row0 * (H * K), static_cast<uint32_t>(T * H * K * 2));
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      qb[t] = __builtin_amdgcn_raw_buffer_load_b16(rq, t * rs + (h * K + i) * 2, 0, 0);
+      kb[t] = __builtin_amdgcn_raw_buffer_load_b16(rq, t * rs + (H * K + h * K + i) * 2, 0, 0);
+      gb[t] = __builtin_amdgcn_raw_buffer_load_b16(rgt, (t * H * K + h * K + i) * 2, 0, 0);
+    }
+    db = p.dt_bias[h * K + i];
+  } else {
+    const int j0 = tid - K;
+#pragma unroll
+    for (int u = 0; u < NVE; ++u) {
+      const int e = j0 + u * (256 - K);
+      const int t = e / VT, j = e % VT;
+      vb[u] = __builtin_amdgcn_raw_buffer_load_b16(rq, (e < NT * VT ? t * rs : T * rs) + (2 * H * K + h * V + tile * VT + j) * 2, 0, 0);
+    }
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.raw_beta + row0 * H, static_cast<uint32_t>(T * H * 2));
+    bb = __builtin_amdgcn_raw_buffer_load_b16(rb, (min(j0, NT) * H + h) * 2, 0, 0);
+  }
+  const __amdgpu_buffer_rsrc_t tile_rsrc =
+      make_rsrc(p.pool + slot * p.slot_stride + static_cast<int64_t>(h) * K * V, K * V * 4);
+  const int voff = ((w * RW + rg * RPL) * V + col) * 4;
+  f32x4 S[RPL];
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) S[r] = buffer_load_f32x4<kStreamPolicy>(tile_rsrc, voff, r * V * 4);
+
+  // 2. Inputs to LDS: q, k, e^{g}, G and the weighted rows e^{G} k, e^{G} q.
+  {
+    if (tid < K) {
+      const int i = tid;
+      const float a = __expf(p.A_log[h]);
+      const bool has_lb = p.has_lb != 0;
+      float G = 0.f;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const float q = bf16_to_f32(qb[t]);
+        const float k = bf16_to_f32(kb[t]);
+        const float g = t < T ? gate_log_decay(bf16_to_f32(gb[t]), db, a, has_lb, p.lower_bound) : 0.f;
+        G += g;
+        const float eG = __expf(G);
+        s_q[t][i] = q;
+        s_k[t][i] = k;
+        s_a[t][i] = __expf(g);
+        s_G[t][i] = G;
+        s_ck[t][i] = eG * k;
+        s_cq[t][i] = eG * q;
+      }
+    } else {
+      const int j0 = tid - K;
+#pragma unroll
+      for (int u = 0; u < NVE; ++u) {
+        const int e = j0 + u * (256 - K);
+        if (e < NT * VT) s_v[e / VT][e % VT] = bf16_to_f32(vb[u]);
+      }
+      if (j0 < NT) s_b[j0] = j0 < T ? sigmoid_f32(bf16_to_f32(bb)) : 0.f;
+    }
+  }
+  lds_barrier();
+
+  // 3. A and P: one quad of lanes per entry, each lane a quarter of the key
+  //    channels. Entries 0 .. NT(NT+1)/2 - 1 are P_ts (s <= t) row by row,
+  //    the next NT(NT-1)/2 are A_ts (s < t).
+  {
+    const int j = tid >> 2, quarter = tid & 3;
+    int rem = j, te = -1, se = 0;
+    bool isP = true;
+#pragma unroll
+    for (int x = 0; x < NT; ++x)
+      if (te < 0) {
+        if (rem <= x) { te = x; se = rem; } else { rem -= x + 1; }
+      }
+    if (te < 0) {
+      isP = false;
+#pragma unroll
+      for (int x = 1; x < NT; ++x)
+        if (te < 0) {
+          if (rem < x) { te = x; se = rem; } else { rem -= x; }
+        }
+    }
+    float acc = 0.f;
+    if (te >= 0 && te < T) {
+      // The quad reads four neighbouring float4s, and each entry starts at
+      // its own offset, so the quads of a wave spread over the LDS banks.
+      const float* lhs = isP ? s_q[te] : s_k[te];
+#pragma unroll 4
+      for (int m = 0; m < K / 16; ++m) {
+        const int i = (((m + j) % (K / 16)) * 4 + quarter) * 4;
+        const float4 ks = *reinterpret_cast<const float4*>(&s_k[se][i]);
+        const float4 lt = *reinterpret_cast<const float4*>(lhs + i);
+        const float4 gt = *reinterpret_cast<const float4*>(&s_G[te][i]);
+        const float4 gs = *reinterpret_cast<const float4*>(&s_G[se][i]);
+        acc = fmaf(ks.x * lt.x, __expf(gt.x - gs.x), acc);
+        acc = fmaf(ks.y * lt.y, __expf(gt.y - gs.y), acc);
+        acc = fmaf(ks.z * lt.z, __expf(gt.z - gs.z), acc);
+        acc = fmaf(ks.w * lt.w, __expf(gt.w - gs.w), acc);
+      }
+    }
+    acc += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(acc), 0xB1, 0xf, 0xf, false));  // quad [1,0,3,2]
+    acc += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(acc), 0x4E, 0xf, 0xf, false));  // quad [2,3,0,1]
+    if (quarter == 0 && te >= 0) (isP ? s_P : s_A)[te][se] = acc;
+  }
+
+  // 4. X_t and Y_t from S0: per-lane partials over the lane's rows, halved
+  //    over the wave's row groups, then summed over the waves through LDS.
+  {
+    float xy[NVAL];
+#pragma unroll
+    for (int v = 0; v < NVAL; ++v) xy[v] = 0.f;
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+      const int row = w * RW + rg * RPL + r;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const float ck = s_ck[t][row], cq = s_cq[t][row];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          xy[t * 4 + c] = fmaf(ck, S[r][c], xy[t * 4 + c]);
+          xy[(NT + t) * 4 + c] = fmaf(cq, S[r][c], xy[(NT + t) * 4 + c]);
+        }
+      }
+    }
+    halve_row_groups<CG>(xy, lane);
+    int blk = 0;
+#pragma unroll
+    for (int b = 2; b < 6; ++b)
+      if ((1 << b) >= CG) blk = blk * 2 + ((lane >> b) & 1);
+#pragma unroll
+    for (int v = 0; v < NKEEP; ++v) s_xy[w][cg][blk * NKEEP + v] = xy[v];
+  }
+  lds_barrier();
+
+  // 5. u and o, one thread per column of the tile.
+  if (tid < VT) {
+    // Every operand is read before the first result is written.
+    const int j = tid, jg = j / 4, jc = j % 4;
+    float X[NT], Y[NT], u[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      X[t] = s_v[t][j];
+      Y[t] = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) {
+        X[t] -= s_xy[ww][jg][t * 4 + jc];
+        Y[t] += s_xy[ww][jg][(NT + t) * 4 + jc];
+      }
+    }
+    float A[NT][NT], P[NT][NT], b[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      b[t] = s_b[t];
+#pragma unroll
+      for (int s2 = 0; s2 < NT; ++s2) {
+        A[t][s2] = s2 < t ? s_A[t][s2] : 0.f;
+        P[t][s2] = s2 <= t ? s_P[t][s2] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      float x = X[t];
+#pragma unroll
+      for (int s2 = 0; s2 < t; ++s2) x = fmaf(-A[t][s2], u[s2], x);
+      u[t] = b[t] * x;
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (t < T) {
+        float y = Y[t];
+#pragma unroll
+        for (int s2 = 0; s2 <= t; ++s2) y = fmaf(P[t][s2], u[s2], y);
+        p.out[((row0 + t) * H + h) * static_cast<int64_t>(V) + tile * VT + j] = f32_to_bf16_rne(p.scale * y);
+        s_u[t][j] = u[t];
+      }
+    }
+  }
+  lds_barrier();
+
+  // 6. The state takes the block's tokens in registers.
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    if (t < T) {
+      const f32x4 ut = *reinterpret_cast<const f32x4*>(&s_u[t][cg * 4]);
+#pragma unroll
+      for (int r = 0; r < RPL; ++r) {
+        const int row = w * RW + rg * RPL + r;
+        S[r] = S[r] * s_a[t][row] + s_k[t][row] * ut;
+      }
+      if (per_token) {
+        const int64_t st = uniform(static_cast<int64_t>(irow[t * p.index_col_stride]));
+        if (st >= 0) {
+          const __amdgpu_buffer_rsrc_t tr =
+              make_rsrc(p.pool + st * p.slot_stride + static_cast<int64_t>(h) * K * V, K * V * 4);
+#pragma unroll
+          for (int r = 0; r < RPL; ++r) buffer_store_f32x4<kStreamPolicy>(S[r], tr, voff, r * V * 4);
+        }
+      }
+    }
+  }
+  if (!per_token) {
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) buffer_store_f32x4<kStreamPolicy>(S[r], tile_rsrc, voff, r * V * 4);
+  }
+}
+
 template <int K, int V>
 static hipError_t launch_kv(const DecodeParams& p, int vt, hipStream_t stream) {
   const int64_t blocks = static_cast<int64_t>(p.num_seqs) * p.H * (V / vt);
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   dim3 grid(static_cast<unsigned>(blocks)), block(64 * kWaves);
+  if (p.tokens_per_seq >= kBlockMinTokens && vt <= 32) {
+    const bool nt4 = p.tokens_per_seq <= 4;
+    if (vt == 16) {
+      if (nt4) spec_block_kernel<K, V, 16, 4><<<grid, block, 0, stream>>>(p);
+      else spec_block_kernel<K, V, 16, 8><<<grid, block, 0, stream>>>(p);
+    } else {
+      if (nt4) spec_block_kernel<K, V, 32, 4><<<grid, block, 0, stream>>>(p);
+      else spec_block_kernel<K, V, 32, 8><<<grid, block, 0, stream>>>(p);
+    }
+    return hipGetLastError();
+  }
   switch (vt) {
     case 16: decode_kernel<K, V, 16><<<grid, block, 0, stream>>>(p); break;
     case 32: decode_kernel<K, V, 32><<<grid, block, 0, stream>>>(p); break;
@@ -332,7 +684,8 @@ hipError_t launch_decode(DecodeParams p, int K, hipStream_t stream) {
   // The output epilogue runs inside the kernel when a workgroup holds whole
   // rows; otherwise as a pass over the output after it.
   const OutNorm norm = p.norm;
-  const bool separate = norm.gate != nullptr && vt != p.V;
+  const bool block_form = p.tokens_per_seq >= kBlockMinTokens && vt <= 32;
+  const bool separate = norm.gate != nullptr && (vt != p.V || block_form);
   if (separate) p.norm.gate = nullptr;
   hipError_t e;
   if (K == 64)

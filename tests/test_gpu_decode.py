@@ -35,6 +35,21 @@ def test_spec_verify(layout, lower_bound):
     check_case(W.spec_verify(layout, lower_bound), DECODE_TOL_O, DECODE_TOL_S)
 
 
+@pytest.mark.parametrize("H,K,V,n,tps,lower_bound", [
+    (32, 128, 128, 5, 6, -5.0),  # 160 (request, head) pairs: 32-column tiles, 6 of 8 token places
+    (32, 128, 128, 2, 5, None),  # 16-column tiles, 5 of 8 token places
+    (16, 64, 128, 3, 7, -5.0),
+    (8, 128, 64, 4, 3, None),    # 3 of 4 token places
+])
+def test_spec_verify_ragged_token_blocks(H, K, V, n, tps, lower_bound):
+    """Requests of 3..8 tokens on tiles of at most 32 columns, which take the
+    block form of the token chain, with token counts that leave places of
+    the 4- or 8-token block empty, and a padded request on a null slot."""
+    case = W.decode_case(f"block_h{H}_k{K}_v{V}_{n}x{tps}", H, K, V, n, tps, 64, 2, lower_bound,
+                         seed=560 + tps, std=0.1, null_rows=(1,))
+    check_case(case, DECODE_TOL_O, DECODE_TOL_S)
+
+
 @pytest.mark.parametrize("K,V", [(64, 128), (128, 64), (64, 64)])
 def test_other_head_dims(K, V):
     case = W.decode_case(f"dims_k{K}_v{V}", 3, K, V, 5, 3, 17, 2, None, seed=501, std=0.2,

@@ -67,6 +67,14 @@ def test_spec_decode_per_token_states(layout, lower_bound):
     _check(case)
 
 
+def test_spec_decode_per_token_states_seven_tokens():
+    # 128 (request, head) pairs (32-column tiles), 7 of 8 token places, a
+    # padded request.
+    case = W.spec_decode_case("spec_states_4x7_h32", 32, 128, 128, 4, 7, num_slots=64,
+                              lower_bound=-5.0, seed=5400, null_rows=(3,), pool_seed=2999)
+    _check(case)
+
+
 def test_spec_decode_null_columns_strided_table_and_small_heads():
     # Every other column of a wider table (column stride 2), some null entries,
     # K = V = 64.
