@@ -382,7 +382,13 @@ __global__ __launch_bounds__(256) void spec_block_kernel(const DecodeParams p) {
   constexpr int NVAL = 8 * NT;       // X and Y for NT tokens and 4 columns
   constexpr int NKEEP = NVAL / RG;   // of them held by a lane after the halving
   static_assert(CG * RG == 64 && RPL * RG == RW && RPL >= 1 && NKEEP >= 1, "tile does not fit");
-  static_assert(NT * (NT + 1) / 2 + NT * (NT - 1) / 2 <= 64, "one quad per A/P entry");
+  // A/P work split: LO lanes per entry (t, s), s < t, and LD per diagonal.
+  constexpr int NO = NT * (NT - 1) / 2;
+  constexpr int LO = NT == 8 ? 8 : 16;
+  constexpr int LD = NT == 8 ? 4 : 16;
+  static_assert(NO * LO + NT * LD <= 256 && (NO * LO) % LD == 0 && K % (4 * LO) == 0 && K % (4 * LD) == 0,
+                "A/P lanes");
+  constexpr int SS = 2 * NT + 4;  // row stride of the wave-summed X/Y (padded against bank conflicts)
 
   __shared__ __align__(16) float s_q[NT][K];
   __shared__ __align__(16) float s_k[NT][K];
@@ -392,10 +398,11 @@ __global__ __launch_bounds__(256) void spec_block_kernel(const DecodeParams p) {
   __shared__ __align__(16) float s_cq[NT][K];  // e^{G_t} q_t
   __shared__ __align__(16) float s_v[NT][VT];
   __shared__ __align__(16) float s_u[NT][VT];
-  __shared__ float s_b[NT];
-  __shared__ float s_A[NT][NT];
-  __shared__ float s_P[NT][NT];
+  __shared__ __align__(16) float s_b[NT];
+  __shared__ __align__(16) float s_A[NT][NT];
+  __shared__ __align__(16) float s_P[NT][NT];
   __shared__ __align__(16) float s_xy[kWaves][CG][NVAL];
+  __shared__ __align__(16) float s_sum[VT][SS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -413,23 +420,9 @@ __global__ __launch_bounds__(256) void spec_block_kernel(const DecodeParams p) {
   const int rg = lane / CG;
   const int col = tile * VT + cg * 4;
 
-  const int32_t* irow = p.indices + static_cast<int64_t>(n) * p.index_stride;
-  const bool per_token = p.num_accepted != nullptr;
-  int init_col = 0;
-  if (per_token) init_col = min(max(uniform(p.num_accepted[n]), 1), T) - 1;
-  const int64_t slot = uniform(static_cast<int64_t>(irow[init_col * p.index_col_stride]));
-
-  if (slot < 0) {
-    for (int e = tid; e < T * VT; e += blockDim.x) {
-      const int t = e / VT, j = e % VT;
-      p.out[((row0 + t) * H + h) * static_cast<int64_t>(V) + tile * VT + j] = 0;
-    }
-    return;
-  }
-
-  // 1. Per-token input loads, then the state loads: the inputs arrive
-  //    first (loads complete in order) and the A/P work below overlaps the
-  //    state's memory latency. Thread i < K owns key channel i for every
+  // 1. Per-token input loads, then the slot and the state loads: the inputs
+  //    arrive first (loads complete in order), the slot lookup overlaps
+  //    them, and the A/P work below overlaps the state's memory latency. Thread i < K owns key channel i for every
   //    token (the running sum G runs down its tokens); the others stage v
   //    and beta. Loads past the request's rows read zero, so padded tokens
   //    carry q = k = 0 and g = 0.
@@ -459,6 +452,22 @@ __global__ __launch_bounds__(256) void spec_block_kernel(const DecodeParams p) {
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.raw_beta + row0 * H, static_cast<uint32_t>(T * H * 2));
     bb = __builtin_amdgcn_raw_buffer_load_b16(rb, (min(j0, NT) * H + h) * 2, 0, 0);
   }
+
+  const int32_t* irow = p.indices + static_cast<int64_t>(n) * p.index_stride;
+  const bool per_token = p.num_accepted != nullptr;
+  int init_col = 0;
+  if (per_token) init_col = min(max(uniform(p.num_accepted[n]), 1), T) - 1;
+  const int64_t slot = uniform(static_cast<int64_t>(irow[init_col * p.index_col_stride]));
+  if (slot < 0) {
+    // Null slot: zero rows; the input loads are drained before the exit.
+    __builtin_amdgcn_s_waitcnt(0);
+    for (int e = tid; e < T * VT; e += blockDim.x) {
+      const int t = e / VT, j = e % VT;
+      p.out[((row0 + t) * H + h) * static_cast<int64_t>(V) + tile * VT + j] = 0;
+    }
+    return;
+  }
+
   const __amdgpu_buffer_rsrc_t tile_rsrc =
       make_rsrc(p.pool + slot * p.slot_stride + static_cast<int64_t>(h) * K * V, K * V * 4);
   const int voff = ((w * RW + rg * RPL) * V + col) * 4;
@@ -499,47 +508,86 @@ __global__ __launch_bounds__(256) void spec_block_kernel(const DecodeParams p) {
   }
   lds_barrier();
 
-  // 3. A and P: one quad of lanes per entry, each lane a quarter of the key
-  //    channels. Entries 0 .. NT(NT+1)/2 - 1 are P_ts (s <= t) row by row,
-  //    the next NT(NT-1)/2 are A_ts (s < t).
+  // 3. A and P. For s < t, A_ts and P_ts share the factor e^{G_t - G_s}
+  //    (one exponential per channel for both): LO lanes per such entry, the
+  //    entries row by row; then LD lanes per diagonal entry P_tt = k_t . q_t.
+  //    The lanes of an entry read neighbouring float4s, and each entry
+  //    starts at its own offset, so the entries of a wave spread over the
+  //    LDS banks.
   {
-    const int j = tid >> 2, quarter = tid & 3;
-    int rem = j, te = -1, se = 0;
-    bool isP = true;
-#pragma unroll
-    for (int x = 0; x < NT; ++x)
-      if (te < 0) {
-        if (rem <= x) { te = x; se = rem; } else { rem -= x + 1; }
-      }
-    if (te < 0) {
-      isP = false;
+    int te = -1, se = 0, part = 0, ent = 0;
+    bool diag = false;
+    if (tid < NO * LO) {
+      ent = tid / LO;
+      part = tid % LO;
+      int rem = ent;
 #pragma unroll
       for (int x = 1; x < NT; ++x)
         if (te < 0) {
           if (rem < x) { te = x; se = rem; } else { rem -= x; }
         }
+    } else if (tid < NO * LO + NT * LD) {
+      te = se = (tid - NO * LO) / LD;
+      part = (tid - NO * LO) % LD;
+      diag = true;
     }
-    float acc = 0.f;
+    float accA = 0.f, accP = 0.f;
     if (te >= 0 && te < T) {
-      // The quad reads four neighbouring float4s, and each entry starts at
-      // its own offset, so the quads of a wave spread over the LDS banks.
-      const float* lhs = isP ? s_q[te] : s_k[te];
-#pragma unroll 4
-      for (int m = 0; m < K / 16; ++m) {
-        const int i = (((m + j) % (K / 16)) * 4 + quarter) * 4;
-        const float4 ks = *reinterpret_cast<const float4*>(&s_k[se][i]);
-        const float4 lt = *reinterpret_cast<const float4*>(lhs + i);
-        const float4 gt = *reinterpret_cast<const float4*>(&s_G[te][i]);
-        const float4 gs = *reinterpret_cast<const float4*>(&s_G[se][i]);
-        acc = fmaf(ks.x * lt.x, __expf(gt.x - gs.x), acc);
-        acc = fmaf(ks.y * lt.y, __expf(gt.y - gs.y), acc);
-        acc = fmaf(ks.z * lt.z, __expf(gt.z - gs.z), acc);
-        acc = fmaf(ks.w * lt.w, __expf(gt.w - gs.w), acc);
+      if (!diag) {
+        constexpr int NF = K / (4 * LO);  // float4s per lane
+#pragma unroll
+        for (int m = 0; m < NF; ++m) {
+          const int i = (((m + ent) % NF) * LO + part) * 4;
+          const float4 ks = *reinterpret_cast<const float4*>(&s_k[se][i]);
+          const float4 kt = *reinterpret_cast<const float4*>(&s_k[te][i]);
+          const float4 qt = *reinterpret_cast<const float4*>(&s_q[te][i]);
+          const float4 gt = *reinterpret_cast<const float4*>(&s_G[te][i]);
+          const float4 gs = *reinterpret_cast<const float4*>(&s_G[se][i]);
+          const float e0 = ks.x * __expf(gt.x - gs.x), e1 = ks.y * __expf(gt.y - gs.y);
+          const float e2 = ks.z * __expf(gt.z - gs.z), e3 = ks.w * __expf(gt.w - gs.w);
+          accA = fmaf(e0, kt.x, fmaf(e1, kt.y, fmaf(e2, kt.z, fmaf(e3, kt.w, accA))));
+          accP = fmaf(e0, qt.x, fmaf(e1, qt.y, fmaf(e2, qt.z, fmaf(e3, qt.w, accP))));
+        }
+      } else {
+        constexpr int NF = K / (4 * LD);
+#pragma unroll
+        for (int m = 0; m < NF; ++m) {
+          const int i = (m * LD + part) * 4;
+          const float4 kt = *reinterpret_cast<const float4*>(&s_k[te][i]);
+          const float4 qt = *reinterpret_cast<const float4*>(&s_q[te][i]);
+          accP = fmaf(kt.x, qt.x, fmaf(kt.y, qt.y, fmaf(kt.z, qt.z, fmaf(kt.w, qt.w, accP))));
+        }
       }
     }
-    acc += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(acc), 0xB1, 0xf, 0xf, false));  // quad [1,0,3,2]
-    acc += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(acc), 0x4E, 0xf, 0xf, false));  // quad [2,3,0,1]
-    if (quarter == 0 && te >= 0) (isP ? s_P : s_A)[te][se] = acc;
+    // Sums over an entry's lanes (aligned groups of 4, 8 or 16): the quad,
+    // then the other quad of the half row, then the other half of the row.
+    auto dpp = [](float x, int ctrl_id) {
+      switch (ctrl_id) {
+        case 0: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xf, 0xf, false));  // quad [1,0,3,2]
+        case 1: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xf, 0xf, false));  // quad [2,3,0,1]
+        case 2: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xf, 0xf, false));  // row_half_mirror
+        default: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xf, 0xf, false));  // row_mirror
+      }
+    };
+    float sA[3], sP[3];  // sums over 4, 8 and 16 lanes
+    accA += dpp(accA, 0);
+    accP += dpp(accP, 0);
+    sA[0] = accA + dpp(accA, 1);
+    sP[0] = accP + dpp(accP, 1);
+    sA[1] = sA[0] + dpp(sA[0], 2);
+    sP[1] = sP[0] + dpp(sP[0], 2);
+    sA[2] = sA[1] + dpp(sA[1], 3);
+    sP[2] = sP[1] + dpp(sP[1], 3);
+    constexpr int lo = LO == 4 ? 0 : LO == 8 ? 1 : 2;
+    constexpr int ld = LD == 4 ? 0 : LD == 8 ? 1 : 2;
+    if (part == 0 && te >= 0) {
+      if (diag) {
+        s_P[te][te] = sP[ld];
+      } else {
+        s_A[te][se] = sA[lo];
+        s_P[te][se] = sP[lo];
+      }
+    }
   }
 
   // 4. X_t and Y_t from S0: per-lane partials over the lane's rows, halved
@@ -571,34 +619,40 @@ __global__ __launch_bounds__(256) void spec_block_kernel(const DecodeParams p) {
   }
   lds_barrier();
 
-  // 5. u and o, one thread per column of the tile.
+  // 5. Sums over the waves (every thread), then u and o, one thread per
+  //    column of the tile.
+  for (int e = tid; e < VT * 2 * NT; e += 256) {
+    const int jj = e / (2 * NT), v = e % (2 * NT);
+    float x = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) x += s_xy[ww][jj / 4][v * 4 + jj % 4];
+    s_sum[jj][v] = x;
+  }
+  lds_barrier();
   if (tid < VT) {
     // Every operand is read before the first result is written.
-    const int j = tid, jg = j / 4, jc = j % 4;
-    float X[NT], Y[NT], u[NT];
+    const int j = tid;
+    float X[NT], Y[NT], A[NT][NT], P[NT][NT], b[NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      X[t] = s_v[t][j];
-      Y[t] = 0.f;
+    for (int t4 = 0; t4 < NT; t4 += 4) {
+      const float4 xv = *reinterpret_cast<const float4*>(&s_sum[j][t4]);
+      const float4 yv = *reinterpret_cast<const float4*>(&s_sum[j][NT + t4]);
+      const float4 bv = *reinterpret_cast<const float4*>(&s_b[t4]);
+      X[t4] = xv.x; X[t4 + 1] = xv.y; X[t4 + 2] = xv.z; X[t4 + 3] = xv.w;
+      Y[t4] = yv.x; Y[t4 + 1] = yv.y; Y[t4 + 2] = yv.z; Y[t4 + 3] = yv.w;
+      b[t4] = bv.x; b[t4 + 1] = bv.y; b[t4 + 2] = bv.z; b[t4 + 3] = bv.w;
 #pragma unroll
-      for (int ww = 0; ww < kWaves; ++ww) {
-        X[t] -= s_xy[ww][jg][t * 4 + jc];
-        Y[t] += s_xy[ww][jg][(NT + t) * 4 + jc];
+      for (int t = 0; t < NT; ++t) {
+        const float4 av = *reinterpret_cast<const float4*>(&s_A[t][t4]);
+        const float4 pv = *reinterpret_cast<const float4*>(&s_P[t][t4]);
+        A[t][t4] = av.x; A[t][t4 + 1] = av.y; A[t][t4 + 2] = av.z; A[t][t4 + 3] = av.w;
+        P[t][t4] = pv.x; P[t][t4 + 1] = pv.y; P[t][t4 + 2] = pv.z; P[t][t4 + 3] = pv.w;
       }
     }
-    float A[NT][NT], P[NT][NT], b[NT];
+    float u[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      b[t] = s_b[t];
-#pragma unroll
-      for (int s2 = 0; s2 < NT; ++s2) {
-        A[t][s2] = s2 < t ? s_A[t][s2] : 0.f;
-        P[t][s2] = s2 <= t ? s_P[t][s2] : 0.f;
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      float x = X[t];
+      float x = s_v[t][j] - X[t];
 #pragma unroll
       for (int s2 = 0; s2 < t; ++s2) x = fmaf(-A[t][s2], u[s2], x);
       u[t] = b[t] * x;
