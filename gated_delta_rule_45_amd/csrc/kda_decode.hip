@@ -42,7 +42,7 @@ constexpr int kWaves = 4;
 constexpr int kMaxTokens = 8;
 // Requests of at least this many tokens on tiles of at most 32 columns take
 // the block (WY) form of the token chain.
-constexpr int kBlockMinTokens = 3;
+constexpr int kBlockMinTokens = 2;
 
 // Sum of x over the lanes that share lane % CG (CG = 4, 8, 16 or 32): a
 // butterfly on VALU lane permutations, no LDS traffic. Inside a 16-lane row
@@ -357,7 +357,7 @@ __device__ __forceinline__ void halve_row_groups(float (&x)[N], int lane) {
 
 }  // namespace
 
-// Spec-verify blocks of 3..8 tokens on narrow column tiles (the latency
+// Spec-verify blocks of 2..8 tokens on narrow column tiles (the latency
 // case: few requests, one workgroup per CU). The per-token chain of the
 // decode kernel (a K-reduction, a cross-wave exchange and a barrier per
 // token) is replaced by the WY form of the block. With G_t the running sum

@@ -42,7 +42,7 @@ def test_spec_verify(layout, lower_bound):
     (8, 128, 64, 4, 3, None),    # 3 of 4 token places
 ])
 def test_spec_verify_ragged_token_blocks(H, K, V, n, tps, lower_bound):
-    """Requests of 3..8 tokens on tiles of at most 32 columns, which take the
+    """Requests of 2..8 tokens on tiles of at most 32 columns, which take the
     block form of the token chain, with token counts that leave places of
     the 4- or 8-token block empty, and a padded request on a null slot."""
     case = W.decode_case(f"block_h{H}_k{K}_v{V}_{n}x{tps}", H, K, V, n, tps, 64, 2, lower_bound,
