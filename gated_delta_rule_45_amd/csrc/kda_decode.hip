@@ -367,41 +367,59 @@ __device__ __forceinline__ void halve_row_groups(float (&x)[N], int lane) {
 //   A_ts = sum_i k_s[i] k_t[i] e^{G_t[i] - G_s[i]},  P_ts likewise with q_t,
 // so u_t = beta_t (v_t - X_t - sum_{s<t} A_ts u_s) and
 // o_t = scale (Y_t + sum_{s<=t} P_ts u_s). Every reduction against the state
-// is taken at once from S0 (one halving over the wave's row groups, one
-// exchange through LDS); the scalars A and P are formed while the state
-// loads are in flight; the u recurrence is per-column scalar work; and the
+// is taken at once from S0, then summed over the waves through LDS. On
+// 16-column tiles [X | Y] is a 16-column by 16-entry product over the K
+// rows, run on fp32 MFMA with the state held in the operand layout; on
+// 32-column tiles it is one recursive halving over the wave's row groups,
+// with the state held as float4 rows. The scalars A and P are formed while
+// the state loads are in flight; the u recurrence is per-column scalar work; and the
 // state then takes its tokens in registers, S = diag(e^{g_t}) S + k_t u_t^T
 // (stored after every token with a state per token). The exponents
 // G_t - G_s are never positive. NT is the token capacity (4 or 8).
 template <int K, int V, int VT, int NT>
 __global__ __launch_bounds__(256) void spec_block_kernel(const DecodeParams p) {
   constexpr int RW = K / kWaves;
+  // MFMA layout (VT = 16): lane (g, m) = (lane / 16, lane % 16) of wave w
+  // holds rows w RW + g NSTEP + s, s < NSTEP, of column m. Step s of the
+  // [X | Y] product takes from it the A element S0[row][m] and the B element
+  // ckq[row][m] of contraction index g (v_mfma_f32_16x16x4_f32).
+  constexpr bool kMfma = VT == 16;
+  constexpr int NSTEP = RW / 4;
+  // Row-group layout (VT = 32): lane (rg, cg) = (lane / CG, lane % CG)
+  // holds rows w RW + rg RPL + r, r < RPL, of columns 4cg .. 4cg + 3.
   constexpr int CG = VT / 4;
   constexpr int RG = 64 / CG;
   constexpr int RPL = RW / RG;
   constexpr int NVAL = 8 * NT;       // X and Y for NT tokens and 4 columns
   constexpr int NKEEP = NVAL / RG;   // of them held by a lane after the halving
-  static_assert(CG * RG == 64 && RPL * RG == RW && RPL >= 1 && NKEEP >= 1, "tile does not fit");
+  static_assert(kMfma ? NSTEP % 4 == 0 : (CG * RG == 64 && RPL * RG == RW && RPL >= 1 && NKEEP >= 1),
+                "tile does not fit");
+  constexpr int NS = kMfma ? NSTEP : 4 * RPL;  // state floats per lane
   // A/P work split: LO lanes per entry (t, s), s < t, and LD per diagonal.
   constexpr int NO = NT * (NT - 1) / 2;
   constexpr int LO = NT == 8 ? 8 : 16;
   constexpr int LD = NT == 8 ? 4 : 16;
   static_assert(NO * LO + NT * LD <= 256 && (NO * LO) % LD == 0 && K % (4 * LO) == 0 && K % (4 * LD) == 0,
                 "A/P lanes");
-  constexpr int SS = 2 * NT + 4;  // row stride of the wave-summed X/Y (padded against bank conflicts)
+  // Wave-summed [X | Y] per column: entry t is X_t and 8 + t is Y_t. Row
+  // strides are padded against LDS bank conflicts.
+  constexpr int SS = 20;
+  constexpr int QS = 17;  // MFMA B rows: e^{G_t} k_t at t, e^{G_t} q_t at 8 + t
 
   __shared__ __align__(16) float s_q[NT][K];
   __shared__ __align__(16) float s_k[NT][K];
   __shared__ __align__(16) float s_a[NT][K];   // e^{g_t}
   __shared__ __align__(16) float s_G[NT][K];   // G_t
-  __shared__ __align__(16) float s_ck[NT][K];  // e^{G_t} k_t
-  __shared__ __align__(16) float s_cq[NT][K];  // e^{G_t} q_t
+  __shared__ __align__(16) float s_ck[kMfma ? 1 : NT][kMfma ? 1 : K];  // e^{G_t} k_t
+  __shared__ __align__(16) float s_cq[kMfma ? 1 : NT][kMfma ? 1 : K];  // e^{G_t} q_t
+  __shared__ float s_ckq[kMfma ? K : 1][kMfma ? QS : 1];
   __shared__ __align__(16) float s_v[NT][VT];
   __shared__ __align__(16) float s_u[NT][VT];
   __shared__ __align__(16) float s_b[NT];
   __shared__ __align__(16) float s_A[NT][NT];
   __shared__ __align__(16) float s_P[NT][NT];
-  __shared__ __align__(16) float s_xy[kWaves][CG][NVAL];
+  __shared__ __align__(16) float s_xy[kWaves][kMfma ? 1 : CG][kMfma ? 1 : NVAL];
+  __shared__ float s_xym[kWaves][kMfma ? VT : 1][kMfma ? QS : 1];
   __shared__ __align__(16) float s_sum[VT][SS];
 
   const int tid = threadIdx.x;
@@ -419,6 +437,8 @@ __global__ __launch_bounds__(256) void spec_block_kernel(const DecodeParams p) {
   const int cg = lane % CG;
   const int rg = lane / CG;
   const int col = tile * VT + cg * 4;
+  const int g4 = lane >> 4, m16 = lane & 15;
+  const int srow = w * RW + g4 * NSTEP;  // MFMA layout: the lane's first row
 
   // 1. Per-token input loads, then the slot and the state loads: the inputs
   //    arrive first (loads complete in order), the slot lookup overlaps
@@ -470,10 +490,21 @@ __global__ __launch_bounds__(256) void spec_block_kernel(const DecodeParams p) {
 
   const __amdgpu_buffer_rsrc_t tile_rsrc =
       make_rsrc(p.pool + slot * p.slot_stride + static_cast<int64_t>(h) * K * V, K * V * 4);
-  const int voff = ((w * RW + rg * RPL) * V + col) * 4;
-  f32x4 S[RPL];
+  const int voff = kMfma ? (srow * V + tile * VT + m16) * 4 : ((w * RW + rg * RPL) * V + col) * 4;
+  float S[NS];
+  if constexpr (kMfma) {
 #pragma unroll
-  for (int r = 0; r < RPL; ++r) S[r] = buffer_load_f32x4<kStreamPolicy>(tile_rsrc, voff, r * V * 4);
+    for (int st = 0; st < NSTEP; ++st)
+      S[st] = __builtin_bit_cast(float,
+                                 __builtin_amdgcn_raw_buffer_load_b32(tile_rsrc, voff, st * V * 4, kStreamPolicy));
+  } else {
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+      const f32x4 x = buffer_load_f32x4<kStreamPolicy>(tile_rsrc, voff, r * V * 4);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) S[4 * r + c] = x[c];
+    }
+  }
 
   // 2. Inputs to LDS: q, k, e^{g}, G and the weighted rows e^{G} k, e^{G} q.
   {
@@ -493,8 +524,20 @@ __global__ __launch_bounds__(256) void spec_block_kernel(const DecodeParams p) {
         s_k[t][i] = k;
         s_a[t][i] = __expf(g);
         s_G[t][i] = G;
-        s_ck[t][i] = eG * k;
-        s_cq[t][i] = eG * q;
+        if constexpr (kMfma) {
+          s_ckq[i][t] = eG * k;
+          s_ckq[i][8 + t] = eG * q;
+        } else {
+          s_ck[t][i] = eG * k;
+          s_cq[t][i] = eG * q;
+        }
+      }
+      if constexpr (kMfma) {
+#pragma unroll
+        for (int t = NT; t < 8; ++t) {
+          s_ckq[i][t] = 0.f;
+          s_ckq[i][8 + t] = 0.f;
+        }
       }
     } else {
       const int j0 = tid - K;
@@ -590,9 +633,18 @@ __global__ __launch_bounds__(256) void spec_block_kernel(const DecodeParams p) {
     }
   }
 
-  // 4. X_t and Y_t from S0: per-lane partials over the lane's rows, halved
-  //    over the wave's row groups, then summed over the waves through LDS.
-  {
+  // 4. X_t and Y_t from S0, per wave, then to LDS for the sum over the
+  //    waves. MFMA layout: NSTEP fp32 MFMA steps over the wave's rows (lane
+  //    (g, m) ends with entry m of columns 4g .. 4g + 3). Row-group layout:
+  //    per-lane partials over the lane's rows, halved over the row groups.
+  if constexpr (kMfma) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < NSTEP; ++st)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(S[st], s_ckq[srow + st][m16], acc, 0, 0, 0);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) s_xym[w][4 * g4 + jj][m16] = acc[jj];
+  } else {
     float xy[NVAL];
 #pragma unroll
     for (int v = 0; v < NVAL; ++v) xy[v] = 0.f;
@@ -604,8 +656,8 @@ __global__ __launch_bounds__(256) void spec_block_kernel(const DecodeParams p) {
         const float ck = s_ck[t][row], cq = s_cq[t][row];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          xy[t * 4 + c] = fmaf(ck, S[r][c], xy[t * 4 + c]);
-          xy[(NT + t) * 4 + c] = fmaf(cq, S[r][c], xy[(NT + t) * 4 + c]);
+          xy[t * 4 + c] = fmaf(ck, S[4 * r + c], xy[t * 4 + c]);
+          xy[(NT + t) * 4 + c] = fmaf(cq, S[4 * r + c], xy[(NT + t) * 4 + c]);
         }
       }
     }
@@ -623,10 +675,16 @@ __global__ __launch_bounds__(256) void spec_block_kernel(const DecodeParams p) {
   //    column of the tile.
   for (int e = tid; e < VT * 2 * NT; e += 256) {
     const int jj = e / (2 * NT), v = e % (2 * NT);
+    const int kind = v / NT, t = v % NT;
     float x = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) x += s_xy[ww][jj / 4][v * 4 + jj % 4];
-    s_sum[jj][v] = x;
+    for (int ww = 0; ww < kWaves; ++ww) {
+      if constexpr (kMfma)
+        x += s_xym[ww][jj][kind * 8 + t];
+      else
+        x += s_xy[ww][jj / 4][v * 4 + jj % 4];
+    }
+    s_sum[jj][kind * 8 + t] = x;
   }
   lds_barrier();
   if (tid < VT) {
@@ -636,7 +694,7 @@ __global__ __launch_bounds__(256) void spec_block_kernel(const DecodeParams p) {
 #pragma unroll
     for (int t4 = 0; t4 < NT; t4 += 4) {
       const float4 xv = *reinterpret_cast<const float4*>(&s_sum[j][t4]);
-      const float4 yv = *reinterpret_cast<const float4*>(&s_sum[j][NT + t4]);
+      const float4 yv = *reinterpret_cast<const float4*>(&s_sum[j][8 + t4]);
       const float4 bv = *reinterpret_cast<const float4*>(&s_b[t4]);
       X[t4] = xv.x; X[t4 + 1] = xv.y; X[t4 + 2] = xv.z; X[t4 + 3] = xv.w;
       Y[t4] = yv.x; Y[t4 + 1] = yv.y; Y[t4 + 2] = yv.z; Y[t4 + 3] = yv.w;
@@ -671,30 +729,50 @@ __global__ __launch_bounds__(256) void spec_block_kernel(const DecodeParams p) {
   lds_barrier();
 
   // 6. The state takes the block's tokens in registers.
+  auto store_state = [&](const __amdgpu_buffer_rsrc_t r) {
+    if constexpr (kMfma) {
+#pragma unroll
+      for (int st = 0; st < NSTEP; ++st)
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, S[st]), r, voff, st * V * 4,
+                                              kStreamPolicy);
+    } else {
+#pragma unroll
+      for (int r2 = 0; r2 < RPL; ++r2)
+        buffer_store_f32x4<kStreamPolicy>(f32x4{S[4 * r2], S[4 * r2 + 1], S[4 * r2 + 2], S[4 * r2 + 3]}, r, voff,
+                                          r2 * V * 4);
+    }
+  };
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     if (t < T) {
-      const f32x4 ut = *reinterpret_cast<const f32x4*>(&s_u[t][cg * 4]);
+      if constexpr (kMfma) {
+        const float ut = s_u[t][m16];
 #pragma unroll
-      for (int r = 0; r < RPL; ++r) {
-        const int row = w * RW + rg * RPL + r;
-        S[r] = S[r] * s_a[t][row] + s_k[t][row] * ut;
+        for (int q4 = 0; q4 < NSTEP; q4 += 4) {
+          const float4 av = *reinterpret_cast<const float4*>(&s_a[t][srow + q4]);
+          const float4 kv = *reinterpret_cast<const float4*>(&s_k[t][srow + q4]);
+          S[q4] = fmaf(kv.x, ut, S[q4] * av.x);
+          S[q4 + 1] = fmaf(kv.y, ut, S[q4 + 1] * av.y);
+          S[q4 + 2] = fmaf(kv.z, ut, S[q4 + 2] * av.z);
+          S[q4 + 3] = fmaf(kv.w, ut, S[q4 + 3] * av.w);
+        }
+      } else {
+        const f32x4 ut = *reinterpret_cast<const f32x4*>(&s_u[t][cg * 4]);
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) {
+          const int row = w * RW + rg * RPL + r;
+          const float al = s_a[t][row], kr = s_k[t][row];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) S[4 * r + c] = fmaf(kr, ut[c], S[4 * r + c] * al);
+        }
       }
       if (per_token) {
         const int64_t st = uniform(static_cast<int64_t>(irow[t * p.index_col_stride]));
-        if (st >= 0) {
-          const __amdgpu_buffer_rsrc_t tr =
-              make_rsrc(p.pool + st * p.slot_stride + static_cast<int64_t>(h) * K * V, K * V * 4);
-#pragma unroll
-          for (int r = 0; r < RPL; ++r) buffer_store_f32x4<kStreamPolicy>(S[r], tr, voff, r * V * 4);
-        }
+        if (st >= 0) store_state(make_rsrc(p.pool + st * p.slot_stride + static_cast<int64_t>(h) * K * V, K * V * 4));
       }
     }
   }
-  if (!per_token) {
-#pragma unroll
-    for (int r = 0; r < RPL; ++r) buffer_store_f32x4<kStreamPolicy>(S[r], tile_rsrc, voff, r * V * 4);
-  }
+  if (!per_token) store_state(tile_rsrc);
 }
 
 template <int K, int V>
