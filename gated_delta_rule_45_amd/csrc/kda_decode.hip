@@ -395,6 +395,9 @@ __global__ __launch_bounds__(256) void spec_block_kernel(const DecodeParams p) {
   static_assert(kMfma ? NSTEP % 4 == 0 : (CG * RG == 64 && RPL * RG == RW && RPL >= 1 && NKEEP >= 1),
                 "tile does not fit");
   constexpr int NS = kMfma ? NSTEP : 4 * RPL;  // state floats per lane
+  // Factored A/P (below) on the MFMA layout with 8 token places; with 4 the
+  // per-channel form has only 16 entries and costs less.
+  constexpr bool kApMfma = kMfma && NT == 8;
   // A/P work split: LO lanes per entry (t, s), s < t, and LD per diagonal.
   constexpr int NO = NT * (NT - 1) / 2;
   constexpr int LO = NT == 8 ? 8 : 16;
@@ -413,6 +416,7 @@ __global__ __launch_bounds__(256) void spec_block_kernel(const DecodeParams p) {
   __shared__ __align__(16) float s_ck[kMfma ? 1 : NT][kMfma ? 1 : K];  // e^{G_t} k_t
   __shared__ __align__(16) float s_cq[kMfma ? 1 : NT][kMfma ? 1 : K];  // e^{G_t} q_t
   __shared__ float s_ckq[kMfma ? K : 1][kMfma ? QS : 1];
+  __shared__ float s_kinv[kApMfma ? K : 1][kApMfma ? QS : 1];  // e^{-G_s} k_s at s (factored A/P)
   __shared__ __align__(16) float s_v[NT][VT];
   __shared__ __align__(16) float s_u[NT][VT];
   __shared__ __align__(16) float s_b[NT];
@@ -420,6 +424,7 @@ __global__ __launch_bounds__(256) void spec_block_kernel(const DecodeParams p) {
   __shared__ __align__(16) float s_P[NT][NT];
   __shared__ __align__(16) float s_xy[kWaves][kMfma ? 1 : CG][kMfma ? 1 : NVAL];
   __shared__ float s_xym[kWaves][kMfma ? VT : 1][kMfma ? QS : 1];
+  __shared__ float s_apm[kWaves][kApMfma ? 16 : 1][kApMfma ? QS : 1];
   __shared__ __align__(16) float s_sum[VT][SS];
 
   const int tid = threadIdx.x;
@@ -439,6 +444,11 @@ __global__ __launch_bounds__(256) void spec_block_kernel(const DecodeParams p) {
   const int col = tile * VT + cg * 4;
   const int g4 = lane >> 4, m16 = lane & 15;
   const int srow = w * RW + g4 * NSTEP;  // MFMA layout: the lane's first row
+  // Factored A/P on the MFMA layout: with a lower bound lb every running sum
+  // satisfies -NT |lb| <= G <= 0, so e^{G_t} and e^{-G_s} stay within
+  // [e^-80, e^80] when NT |lb| <= 80, and e^{G_t - G_s} = e^{G_t} e^{-G_s}
+  // makes [A | P] the product [e^G k | e^G q]^T (e^{-G} k) over the keys.
+  const bool ap_mfma = kApMfma && p.has_lb != 0 && -p.lower_bound * NT <= 80.f;
 
   // 1. Per-token input loads, then the slot and the state loads: the inputs
   //    arrive first (loads complete in order), the slot lookup overlaps
@@ -527,6 +537,9 @@ __global__ __launch_bounds__(256) void spec_block_kernel(const DecodeParams p) {
         if constexpr (kMfma) {
           s_ckq[i][t] = eG * k;
           s_ckq[i][8 + t] = eG * q;
+          if constexpr (kApMfma) {
+            if (ap_mfma) s_kinv[i][t] = k * __expf(-G);
+          }
         } else {
           s_ck[t][i] = eG * k;
           s_cq[t][i] = eG * q;
@@ -537,6 +550,12 @@ __global__ __launch_bounds__(256) void spec_block_kernel(const DecodeParams p) {
         for (int t = NT; t < 8; ++t) {
           s_ckq[i][t] = 0.f;
           s_ckq[i][8 + t] = 0.f;
+        }
+        if constexpr (kApMfma) {
+          if (ap_mfma) {
+#pragma unroll
+            for (int t = NT; t < 16; ++t) s_kinv[i][t] = 0.f;
+          }
         }
       }
     } else {
@@ -556,8 +575,8 @@ __global__ __launch_bounds__(256) void spec_block_kernel(const DecodeParams p) {
   //    entries row by row; then LD lanes per diagonal entry P_tt = k_t . q_t.
   //    The lanes of an entry read neighbouring float4s, and each entry
   //    starts at its own offset, so the entries of a wave spread over the
-  //    LDS banks.
-  {
+  //    LDS banks. (The factored form takes A and P from MFMA in step 4.)
+  if (!ap_mfma) {
     int te = -1, se = 0, part = 0, ent = 0;
     bool diag = false;
     if (tid < NO * LO) {
@@ -644,6 +663,18 @@ __global__ __launch_bounds__(256) void spec_block_kernel(const DecodeParams p) {
       acc = __builtin_amdgcn_mfma_f32_16x16x4f32(S[st], s_ckq[srow + st][m16], acc, 0, 0, 0);
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) s_xym[w][4 * g4 + jj][m16] = acc[jj];
+    if constexpr (kApMfma) {
+      if (ap_mfma) {
+        // [A | P] partials over the wave's keys: lane (g, m) ends with
+        // column s = m of rows 4g .. 4g + 3 (rows t: A_ts, 8 + t: P_ts).
+        f32x4 ap = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < NSTEP; ++st)
+          ap = __builtin_amdgcn_mfma_f32_16x16x4f32(s_ckq[srow + st][m16], s_kinv[srow + st][m16], ap, 0, 0, 0);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) s_apm[w][4 * g4 + jj][m16] = ap[jj];
+      }
+    }
   } else {
     float xy[NVAL];
 #pragma unroll
@@ -685,6 +716,19 @@ __global__ __launch_bounds__(256) void spec_block_kernel(const DecodeParams p) {
         x += s_xy[ww][jj / 4][v * 4 + jj % 4];
     }
     s_sum[jj][kind * 8 + t] = x;
+  }
+  if constexpr (kApMfma) {
+    if (ap_mfma && tid < NT * NT) {
+      const int t = tid / NT, s2 = tid % NT;
+      float a = 0.f, pp = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) {
+        a += s_apm[ww][t][s2];
+        pp += s_apm[ww][8 + t][s2];
+      }
+      s_A[t][s2] = a;
+      s_P[t][s2] = pp;
+    }
   }
   lds_barrier();
   if (tid < VT) {
