@@ -50,6 +50,16 @@ def test_spec_verify_ragged_token_blocks(H, K, V, n, tps, lower_bound):
     check_case(case, DECODE_TOL_O, DECODE_TOL_S)
 
 
+@pytest.mark.parametrize("lower_bound", [-7.5, -12.0])
+def test_spec_verify_steep_lower_bounds(lower_bound):
+    """One request of 8 tokens on 16-column tiles: at lb = -7.5 the factored
+    form of the token-pair tables runs at its bound (running decays down to
+    e^-60), at lb = -12 the per-channel form takes over."""
+    case = W.decode_case(f"block_lb{lower_bound}", 32, 128, 128, 1, 8, 64, 2, lower_bound,
+                         seed=590, std=0.1)
+    check_case(case, DECODE_TOL_O, DECODE_TOL_S)
+
+
 @pytest.mark.parametrize("K,V", [(64, 128), (128, 64), (64, 64)])
 def test_other_head_dims(K, V):
     case = W.decode_case(f"dims_k{K}_v{V}", 3, K, V, 5, 3, 17, 2, None, seed=501, std=0.2,
