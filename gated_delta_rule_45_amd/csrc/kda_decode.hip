@@ -408,6 +408,8 @@ __global__ __launch_bounds__(256) void spec_block_kernel(const DecodeParams p) {
   // strides are padded against LDS bank conflicts.
   constexpr int SS = 20;
   constexpr int QS = 17;  // MFMA B rows: e^{G_t} k_t at t, e^{G_t} q_t at 8 + t
+  constexpr int kUParts = 4;  // threads per column in the u/o phase
+  static_assert(VT * kUParts <= 256 && NT % kUParts == 0, "u/o threads");
 
   __shared__ __align__(16) float s_q[NT][K];
   __shared__ __align__(16) float s_k[NT][K];
@@ -732,26 +734,33 @@ __global__ __launch_bounds__(256) void spec_block_kernel(const DecodeParams p) {
     }
   }
   lds_barrier();
-  if (tid < VT) {
-    // Every operand is read before the first result is written.
-    const int j = tid;
-    float X[NT], Y[NT], A[NT][NT], P[NT][NT], b[NT];
+  if (tid < VT * kUParts) {
+    // kUParts threads per column: each runs the column's u recurrence (a
+    // short dependent chain) and forms o and stores u for the token places
+    // t = part (mod kUParts). Every operand is read before the first result
+    // is written.
+    const int j = tid / kUParts, part = tid % kUParts;
+    constexpr int NOWN = NT / kUParts;
+    float X[NT], A[NT][NT], b[NT], Yo[NOWN], Po[NOWN][NT];
 #pragma unroll
     for (int t4 = 0; t4 < NT; t4 += 4) {
       const float4 xv = *reinterpret_cast<const float4*>(&s_sum[j][t4]);
-      const float4 yv = *reinterpret_cast<const float4*>(&s_sum[j][8 + t4]);
       const float4 bv = *reinterpret_cast<const float4*>(&s_b[t4]);
       X[t4] = xv.x; X[t4 + 1] = xv.y; X[t4 + 2] = xv.z; X[t4 + 3] = xv.w;
-      Y[t4] = yv.x; Y[t4 + 1] = yv.y; Y[t4 + 2] = yv.z; Y[t4 + 3] = yv.w;
       b[t4] = bv.x; b[t4 + 1] = bv.y; b[t4 + 2] = bv.z; b[t4 + 3] = bv.w;
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const float4 av = *reinterpret_cast<const float4*>(&s_A[t][t4]);
-        const float4 pv = *reinterpret_cast<const float4*>(&s_P[t][t4]);
         A[t][t4] = av.x; A[t][t4 + 1] = av.y; A[t][t4 + 2] = av.z; A[t][t4 + 3] = av.w;
-        P[t][t4] = pv.x; P[t][t4 + 1] = pv.y; P[t][t4 + 2] = pv.z; P[t][t4 + 3] = pv.w;
+      }
+#pragma unroll
+      for (int i = 0; i < NOWN; ++i) {
+        const float4 pv = *reinterpret_cast<const float4*>(&s_P[part + kUParts * i][t4]);
+        Po[i][t4] = pv.x; Po[i][t4 + 1] = pv.y; Po[i][t4 + 2] = pv.z; Po[i][t4 + 3] = pv.w;
       }
     }
+#pragma unroll
+    for (int i = 0; i < NOWN; ++i) Yo[i] = s_sum[j][8 + part + kUParts * i];
     float u[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -761,13 +770,17 @@ __global__ __launch_bounds__(256) void spec_block_kernel(const DecodeParams p) {
       u[t] = b[t] * x;
     }
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
+    for (int i = 0; i < NOWN; ++i) {
+      const int t = part + kUParts * i;
       if (t < T) {
-        float y = Y[t];
+        float y = Yo[i];
 #pragma unroll
-        for (int s2 = 0; s2 <= t; ++s2) y = fmaf(P[t][s2], u[s2], y);
+        for (int s2 = 0; s2 < NT; ++s2) y = fmaf(s2 <= t ? Po[i][s2] : 0.f, u[s2], y);
         p.out[((row0 + t) * H + h) * static_cast<int64_t>(V) + tile * VT + j] = f32_to_bf16_rne(p.scale * y);
-        s_u[t][j] = u[t];
+        float ut = u[0];
+#pragma unroll
+        for (int s2 = 1; s2 < NT; ++s2) ut = s2 == t ? u[s2] : ut;
+        s_u[t][j] = ut;
       }
     }
   }
