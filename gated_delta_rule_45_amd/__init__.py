@@ -7,7 +7,9 @@ package only marshals torch tensors into that ABI.
 from ._binding import (  # noqa: F401
     GatedRMSNorm,
     KdaError,
+    NOALLOC_SCRATCH_BYTES,
     kda_chunk_prefill,
+    kda_chunk_prefill_noalloc,
     kda_chunk_prefill_workspace_size,
     kda_decode_packed,
     kda_mixed_batch,
@@ -20,7 +22,9 @@ from ._binding import (  # noqa: F401
 __all__ = [
     "GatedRMSNorm",
     "KdaError",
+    "NOALLOC_SCRATCH_BYTES",
     "kda_chunk_prefill",
+    "kda_chunk_prefill_noalloc",
     "kda_chunk_prefill_workspace_size",
     "kda_decode_packed",
     "kda_mixed_batch",

@@ -17,6 +17,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libkda.so")
 
 KDA_OK = 0
+NOALLOC_SCRATCH_BYTES = 64 << 20  # KDA_NOALLOC_SCRATCH_BYTES in kda.h
 STATUS_NAMES = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARGUMENT", 2: "KDA_ERR_UNSUPPORTED",
                 3: "KDA_ERR_WORKSPACE", 4: "KDA_ERR_HIP"}
 
@@ -90,6 +91,9 @@ def lib() -> ctypes.CDLL:
         L.kda_chunk_prefill.argtypes = [i32, i64, vp, vp, i32, i32, i32, vp, i64, vp, vp, gp, spn,
                                         npn, vp, vp, sz, vp]
         L.kda_chunk_prefill.restype = i32
+        L.kda_chunk_prefill_noalloc.argtypes = [i32, i64, vp, vp, i32, i32, i32, vp, i64, vp, vp, gp,
+                                                spn, npn, vp, vp]
+        L.kda_chunk_prefill_noalloc.restype = i32
         L.kda_mixed_batch_workspace_size.argtypes = [i32, i32, i64, i32, i32, i32]
         L.kda_mixed_batch_workspace_size.restype = sz
         L.kda_mixed_batch.argtypes = [i32, i32, i64, vp, vp, i32, i32, i32, vp, i64, vp, vp, gp,
@@ -345,6 +349,38 @@ def kda_chunk_prefill(mixed_qkv, raw_g, raw_beta, A_log, dt_bias, lower_bound, i
                                  H, K, V, _ptr(mixed_qkv), mixed_qkv.stride(0), _ptr(raw_g),
                                  _ptr(raw_beta), ctypes.byref(g), ctypes.byref(s), _byref(nm),
                                  _ptr(out), _ptr(ws), ws.numel(), _stream(mixed_qkv.device))
+    _raise_if(st)
+    return out, initial_state
+
+
+def kda_chunk_prefill_noalloc(mixed_qkv, raw_g, raw_beta, A_log, dt_bias, lower_bound, initial_state,
+                              state_indices, cu_seqlens, *, has_initial_state=None, scale: float = 1.0,
+                              out=None, norm: GatedRMSNorm | None = None):
+    """kda_chunk_prefill on the library's static per-GPU scratch instead of a
+    workspace (no device allocation in the library; ``out`` is allocated
+    here only when not given). Sizes whose workspace would exceed
+    ``NOALLOC_SCRATCH_BYTES`` are rejected. Returns ``(out, initial_state)``."""
+    m = _Marshal()
+    H, K, V = _common(m, mixed_qkv, raw_g, raw_beta, A_log, dt_bias, initial_state, state_indices)
+    m.tensor("cu_seqlens", cu_seqlens, torch.int32, 1)
+    m.tensor("has_initial_state", has_initial_state, torch.uint8, 1, optional=True)
+    m.raise_if_any()
+    num_seqs = cu_seqlens.shape[0] - 1
+    num_tokens = mixed_qkv.shape[0]
+    m.check(cu_seqlens.is_contiguous(), "cu_seqlens must be contiguous")
+    m.check(state_indices.shape[0] == num_seqs, "state_indices needs one entry per sequence")
+    if has_initial_state is not None:
+        m.check(has_initial_state.shape[0] == num_seqs and has_initial_state.is_contiguous(),
+                "has_initial_state must be contiguous with one entry per sequence")
+    m.raise_if_any()
+    out = _out(out, num_tokens, H, V, mixed_qkv.device, m)
+    nm = _norm(norm, num_tokens, H, V, m)
+    g, s = _gate(A_log, dt_bias, lower_bound, scale), _state(initial_state, state_indices)
+    st = lib().kda_chunk_prefill_noalloc(num_seqs, num_tokens, _ptr(cu_seqlens),
+                                         _ptr(has_initial_state), H, K, V, _ptr(mixed_qkv),
+                                         mixed_qkv.stride(0), _ptr(raw_g), _ptr(raw_beta),
+                                         ctypes.byref(g), ctypes.byref(s), _byref(nm), _ptr(out),
+                                         _stream(mixed_qkv.device))
     _raise_if(st)
     return out, initial_state
 

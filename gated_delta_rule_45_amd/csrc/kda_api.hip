@@ -39,6 +39,55 @@ class Checks {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// Workspace of kda_chunk_prefill_noalloc: one static buffer per GPU, held
+// until the process ends. In host code `scratch` names a host-side stand-in,
+// not device memory; its device address on each GPU comes from
+// hipGetSymbolAddress (looked up once per device, with that device current)
+// and only that address is ever handed to kernels.
+constexpr size_t kNoallocScratchBytes = KDA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kNoallocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device a call's work runs on: the stream's (the current device for
+// the null stream).
+hipError_t stream_device(hipStream_t stream, int* dev) {
+  if (stream == nullptr) return hipGetDevice(dev);
+  hipDevice_t d = 0;
+  const hipError_t e = hipStreamGetDevice(stream, &d);
+  if (e == hipSuccess) *dev = static_cast<int>(d);
+  return e;
+}
+
+// Device address of the scratch on the GPU that `stream` runs on, looked up
+// on the first call for that GPU with that GPU current (and the caller's
+// current device restored).
+hipError_t noalloc_scratch(hipStream_t stream, void** out) {
+  int dev = 0;
+  hipError_t e = stream_device(stream, &dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    int cur = 0;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t er = hipSetDevice(cur);
+      if (e == hipSuccess) e = er;
+    }
+    if (e != hipSuccess) return e;
+    if (ptr == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 // Per-device side stream of the mixed-batch router, with the two events that
 // fork it from the caller's stream and join it back. Created on a device's
 // first mixed batch with decode and prefill rows, kept until the process
@@ -312,6 +361,37 @@ kda_status_t kda_chunk_prefill(int32_t num_seqs, int64_t num_tokens, const int32
                      qkv_row_stride, raw_g, raw_beta, gate, state, out, workspace, workspace_bytes);
   p.norm = out_norm(norm, 0);
   return hip_status(kda::launch_prefill(p, stream), "prefill launch");
+}
+
+kda_status_t kda_chunk_prefill_noalloc(int32_t num_seqs, int64_t num_tokens,
+                                       const int32_t* cu_seqlens,
+                                       const uint8_t* has_initial_state, int32_t H, int32_t K,
+                                       int32_t V, const void* mixed_qkv, int64_t qkv_row_stride,
+                                       const void* raw_g, const void* raw_beta,
+                                       const kda_gate_t* gate, const kda_state_t* state,
+                                       const kda_out_norm_t* norm, void* out,
+                                       hipStream_t stream) {
+  Checks c;
+  check_common(c, num_tokens, H, K, V, mixed_qkv, qkv_row_stride, raw_g, raw_beta, gate, state, out);
+  size_t need = 0;
+  if (num_seqs > 0 && num_tokens > 0 && H >= 1 && (K == 64 || K == 128) && (V == 64 || V == 128))
+    need = kda::prefill_workspace_bytes(num_seqs, num_tokens, H, K, V);
+  c.require(need <= kNoallocScratchBytes, KDA_ERR_WORKSPACE,
+            "these sizes need " + std::to_string(need) + " bytes of workspace, more than the " +
+                std::to_string(kNoallocScratchBytes) + " bytes of the static scratch (KDA_NOALLOC_SCRATCH_BYTES)");
+  // The size check above stands in for the workspace argument's checks.
+  void* ws = reinterpret_cast<void*>(uintptr_t{256});
+  check_prefill_specific(c, num_seqs, num_tokens, cu_seqlens, H, K, V, ws, SIZE_MAX);
+  check_norm(c, num_tokens, H, V, norm);
+  if (!c.ok()) return c.finish();
+  if (num_seqs == 0 || num_tokens == 0) return c.finish();
+  const hipError_t e = noalloc_scratch(stream, &ws);
+  if (e != hipSuccess) return hip_status(e, "prefill (no-alloc): scratch address");
+  kda::PrefillParams p =
+      prefill_params(num_seqs, num_tokens, cu_seqlens, has_initial_state, H, K, V, mixed_qkv,
+                     qkv_row_stride, raw_g, raw_beta, gate, state, out, ws, kNoallocScratchBytes);
+  p.norm = out_norm(norm, 0);
+  return hip_status(kda::launch_prefill(p, stream), "prefill (no-alloc) launch");
 }
 
 size_t kda_mixed_batch_workspace_size(int32_t num_decodes, int32_t num_prefills,

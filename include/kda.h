@@ -193,6 +193,36 @@ kda_status_t kda_chunk_prefill(int32_t num_seqs, int64_t num_tokens,
                                void* workspace, size_t workspace_bytes,
                                hipStream_t stream);
 
+/* Size of the static device scratch of kda_chunk_prefill_noalloc, per GPU. */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * kda_chunk_prefill without any allocation, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc. Same arguments, semantics and errors as
+ * kda_chunk_prefill, minus the workspace: the call uses the library's own
+ * static device buffer of KDA_NOALLOC_SCRATCH_BYTES (64 MiB), one per GPU,
+ * which each GPU the library runs on holds until the process ends. Sizes
+ * whose kda_chunk_prefill_workspace_size() exceeds it are rejected with
+ * KDA_ERR_WORKSPACE before anything is launched. The call allocates and frees
+ * nothing (no hipMalloc, no allocating library routine); the first call for a
+ * GPU looks up the buffer's device address (hipGetSymbolAddress), so make that
+ * first call outside graph capture. The kernels write every scratch word they
+ * read, so the buffer needs no clearing between calls, but every call on one
+ * GPU shares it: calls that overlap in time on one GPU (on different streams
+ * or from different host threads) race on it and must be ordered by the
+ * caller.
+ */
+kda_status_t kda_chunk_prefill_noalloc(int32_t num_seqs, int64_t num_tokens,
+                                       const int32_t* cu_seqlens,
+                                       const uint8_t* has_initial_state,
+                                       int32_t H, int32_t K, int32_t V,
+                                       const void* mixed_qkv, int64_t qkv_row_stride,
+                                       const void* raw_g, const void* raw_beta,
+                                       const kda_gate_t* gate, const kda_state_t* state,
+                                       const kda_out_norm_t* norm, void* out,
+                                       hipStream_t stream);
+
 /* Bytes of device workspace kda_mixed_batch needs. */
 size_t kda_mixed_batch_workspace_size(int32_t num_decodes, int32_t num_prefills,
                                       int64_t num_prefill_tokens, int32_t H,

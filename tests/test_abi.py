@@ -180,6 +180,23 @@ def test_prefill_rejects_missing_workspace_and_cu_seqlens():
     assert st == 3 and "workspace" in L.kda_last_error().decode()
 
 
+def test_noalloc_prefill_rejects_sizes_beyond_its_scratch():
+    """The no-alloc prefill has no workspace argument; a call whose workspace
+    would exceed the static scratch is refused on the host, with every
+    other failed check listed beside it."""
+    L = kda.lib()
+    g, s = _gate(), _state(index_stride=1)
+    assert L.kda_chunk_prefill_workspace_size(1, 8192, 32, 128, 128) > B.NOALLOC_SCRATCH_BYTES
+    st = L.kda_chunk_prefill_noalloc(1, 8192, FAKE, None, 32, 128, 128, FAKE, 3 * 32 * 128, FAKE,
+                                     FAKE, ctypes.byref(g), ctypes.byref(s), None, FAKE, None)
+    msg = L.kda_last_error().decode()
+    assert st == 3 and "static scratch" in msg, msg
+    st = L.kda_chunk_prefill_noalloc(2, 100, None, None, 32, 128, 128, FAKE, 3 * 32 * 128, FAKE,
+                                     FAKE, ctypes.byref(g), ctypes.byref(s), None, None, None)
+    msg = L.kda_last_error().decode()
+    assert st == 1 and "cu_seqlens must not be NULL" in msg and "out must not be NULL" in msg
+
+
 def test_mixed_rejects_negative_decodes():
     L = kda.lib()
     g, s = _gate(), _state()
