@@ -387,11 +387,12 @@ def leg_mixed(steps, warmup):
     out = torch.empty(T, H, V, dtype=torch.bfloat16, device=dev)
     ws = torch.empty(kda.kda_mixed_batch_workspace_size(D, 5, T - D, H, K, V), dtype=torch.uint8,
                      device=dev)
+    ov = kda.Overlap()  # decode rows on a caller-owned side stream beside the prefill
 
     def step(i):
         kda.kda_mixed_batch(inp["mixed_qkv"], inp["raw_g"], inp["raw_beta"], inp["A_log"],
                             inp["dt_bias"], -5.0, pool, tables[i % sets][:, 0], D, cu, out=out,
-                            workspace=ws)
+                            workspace=ws, overlap=ov)
 
     ms, _ = graph_time(step, sets, steps, warmup)
     return {"workload": "mixed_d96_p4000_h32_k128", "ms_per_step": round(ms, 4),

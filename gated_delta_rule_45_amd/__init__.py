@@ -7,6 +7,7 @@ package only marshals torch tensors into that ABI.
 from ._binding import (  # noqa: F401
     GatedRMSNorm,
     KdaError,
+    Overlap,
     NOALLOC_SCRATCH_BYTES,
     kda_chunk_prefill,
     kda_chunk_prefill_noalloc,
@@ -22,6 +23,7 @@ from ._binding import (  # noqa: F401
 __all__ = [
     "GatedRMSNorm",
     "KdaError",
+    "Overlap",
     "NOALLOC_SCRATCH_BYTES",
     "kda_chunk_prefill",
     "kda_chunk_prefill_noalloc",

@@ -58,6 +58,30 @@ class KdaShortConv(ctypes.Structure):
                 ("conv_slot_stride", ctypes.c_int64), ("num_slots", ctypes.c_int64)]
 
 
+class Overlap:
+    """Caller-owned overlap resources of ``kda_mixed_batch`` (a side stream
+    and two events on the current device, kda_overlap_create). Create it once,
+    outside graph capture, and pass it as ``overlap=`` so that the decode rows
+    of a mixed batch run beside the prefill's chunk passes. One handle serves
+    one call at a time; concurrent callers need their own."""
+
+    def __init__(self):
+        h = ctypes.c_void_p()
+        _raise_if(lib().kda_overlap_create(ctypes.byref(h)))
+        self.handle = h
+
+    def close(self):
+        if self.handle is not None and self.handle.value:
+            _raise_if(lib().kda_overlap_destroy(self.handle))
+        self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # interpreter shutdown
+            pass
+
+
 class KdaError(ValueError):
     """A call was rejected. ``status`` is the C status code, ``reasons`` the
     list of every failed check."""
@@ -97,8 +121,12 @@ def lib() -> ctypes.CDLL:
         L.kda_mixed_batch_workspace_size.argtypes = [i32, i32, i64, i32, i32, i32]
         L.kda_mixed_batch_workspace_size.restype = sz
         L.kda_mixed_batch.argtypes = [i32, i32, i64, vp, vp, i32, i32, i32, vp, i64, vp, vp, gp,
-                                      spn, npn, vp, vp, sz, vp]
+                                      spn, npn, vp, vp, sz, vp, vp]
         L.kda_mixed_batch.restype = i32
+        L.kda_overlap_create.argtypes = [ctypes.POINTER(vp)]
+        L.kda_overlap_create.restype = i32
+        L.kda_overlap_destroy.argtypes = [vp]
+        L.kda_overlap_destroy.restype = i32
         L.kda_short_conv.argtypes = [i32, i64, vp, vp, i32, i32, i32, vp, i64,
                                      ctypes.POINTER(KdaShortConv), vp, i64, vp, i64, vp]
         L.kda_short_conv.restype = i32
@@ -387,11 +415,14 @@ def kda_chunk_prefill_noalloc(mixed_qkv, raw_g, raw_beta, A_log, dt_bias, lower_
 
 def kda_mixed_batch(mixed_qkv, raw_g, raw_beta, A_log, dt_bias, lower_bound, initial_state,
                     state_indices, num_decodes: int, prefill_cu_seqlens, *, has_initial_state=None,
-                    scale: float = 1.0, out=None, workspace=None, norm: GatedRMSNorm | None = None):
+                    scale: float = 1.0, out=None, workspace=None, norm: GatedRMSNorm | None = None,
+                    overlap: Overlap | None = None):
     """Mixed batch: rows [0, num_decodes) are single-token decodes (recurrent
     kernel), the rest are prefill sequences given by ``prefill_cu_seqlens``
     (relative to ``num_decodes``; chunk pipeline). ``state_indices`` has the
-    decodes' entries first, then the prefills'. Returns ``(out, initial_state)``."""
+    decodes' entries first, then the prefills'. With ``overlap`` (an
+    ``Overlap``) the decode rows run on its side stream beside the prefill.
+    Returns ``(out, initial_state)``."""
     m = _Marshal()
     H, K, V = _common(m, mixed_qkv, raw_g, raw_beta, A_log, dt_bias, initial_state, state_indices)
     m.tensor("prefill_cu_seqlens", prefill_cu_seqlens, torch.int32, 1)
@@ -415,7 +446,8 @@ def kda_mixed_batch(mixed_qkv, raw_g, raw_beta, A_log, dt_bias, lower_bound, ini
                                _ptr(prefill_cu_seqlens), _ptr(has_initial_state), H, K, V,
                                _ptr(mixed_qkv), mixed_qkv.stride(0), _ptr(raw_g), _ptr(raw_beta),
                                ctypes.byref(g), ctypes.byref(s), _byref(nm), _ptr(out), _ptr(ws),
-                               ws.numel(), _stream(mixed_qkv.device))
+                               ws.numel(), overlap.handle if overlap is not None else None,
+                               _stream(mixed_qkv.device))
     _raise_if(st)
     return out, initial_state
 

@@ -6,12 +6,21 @@
 // memory from the host.
 #include <cmath>
 #include <cstdio>
-#include <map>
 #include <mutex>
+#include <new>
 #include <string>
 
 #include "kda.h"
 #include "kda_internal.h"
+
+// Overlap resources of kda_mixed_batch, created and owned by the caller: a
+// side stream for the decode rows and the two events that fork it from the
+// caller's stream and join it back, all on one device.
+struct kda_overlap_s {
+  int device;
+  hipStream_t stream;
+  hipEvent_t fork, join;
+};
 
 namespace {
 
@@ -85,34 +94,6 @@ hipError_t noalloc_scratch(hipStream_t stream, void** out) {
     g_scratch_ptr[dev] = ptr;
   }
   *out = g_scratch_ptr[dev];
-  return hipSuccess;
-}
-
-// Per-device side stream of the mixed-batch router, with the two events that
-// fork it from the caller's stream and join it back. Created on a device's
-// first mixed batch with decode and prefill rows, kept until the process
-// ends, and used under g_side_mu so that concurrent callers cannot interleave
-// their records and waits.
-struct SideStream {
-  hipStream_t stream = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-};
-std::mutex g_side_mu;
-std::map<int, SideStream> g_side;
-
-hipError_t side_stream_locked(SideStream** out) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  SideStream& ss = g_side[dev];
-  if (ss.stream == nullptr) {
-    SideStream fresh;
-    if ((e = hipStreamCreateWithFlags(&fresh.stream, hipStreamNonBlocking)) != hipSuccess) return e;
-    if ((e = hipEventCreateWithFlags(&fresh.fork, hipEventDisableTiming)) != hipSuccess) return e;
-    if ((e = hipEventCreateWithFlags(&fresh.join, hipEventDisableTiming)) != hipSuccess) return e;
-    ss = fresh;
-  }
-  *out = &ss;
   return hipSuccess;
 }
 
@@ -401,13 +382,46 @@ size_t kda_mixed_batch_workspace_size(int32_t num_decodes, int32_t num_prefills,
   return kda_chunk_prefill_workspace_size(num_prefills, num_prefill_tokens, H, K, V);
 }
 
+kda_status_t kda_overlap_create(kda_overlap_t* overlap) {
+  Checks c;
+  c.require(overlap != nullptr, KDA_ERR_INVALID_ARGUMENT, "overlap must not be NULL");
+  if (!c.ok()) return c.finish();
+  *overlap = nullptr;
+  kda_overlap_s* o = new (std::nothrow) kda_overlap_s{0, nullptr, nullptr, nullptr};
+  if (o == nullptr) {
+    g_last_error = "kda_overlap_create: out of host memory";
+    return KDA_ERR_HIP;
+  }
+  hipError_t e = hipGetDevice(&o->device);
+  if (e == hipSuccess) e = hipStreamCreateWithFlags(&o->stream, hipStreamNonBlocking);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&o->fork, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&o->join, hipEventDisableTiming);
+  if (e != hipSuccess) {
+    kda_overlap_destroy(o);
+    return hip_status(e, "kda_overlap_create");
+  }
+  *overlap = o;
+  g_last_error.clear();
+  return KDA_OK;
+}
+
+kda_status_t kda_overlap_destroy(kda_overlap_t overlap) {
+  if (overlap == nullptr) return KDA_OK;
+  hipError_t e = hipSuccess, ei;
+  if (overlap->join && (ei = hipEventDestroy(overlap->join)) != hipSuccess) e = ei;
+  if (overlap->fork && (ei = hipEventDestroy(overlap->fork)) != hipSuccess) e = ei;
+  if (overlap->stream && (ei = hipStreamDestroy(overlap->stream)) != hipSuccess) e = ei;
+  delete overlap;
+  return hip_status(e, "kda_overlap_destroy");
+}
+
 kda_status_t kda_mixed_batch(int32_t num_decodes, int32_t num_prefills, int64_t num_prefill_tokens,
                              const int32_t* prefill_cu_seqlens, const uint8_t* has_initial_state,
                              int32_t H, int32_t K, int32_t V, const void* mixed_qkv,
                              int64_t qkv_row_stride, const void* raw_g, const void* raw_beta,
                              const kda_gate_t* gate, const kda_state_t* state,
                              const kda_out_norm_t* norm, void* out, void* workspace,
-                             size_t workspace_bytes, hipStream_t stream) {
+                             size_t workspace_bytes, kda_overlap_t overlap, hipStream_t stream) {
   Checks c;
   const auto INV = KDA_ERR_INVALID_ARGUMENT;
   c.require(num_decodes >= 0, INV, "num_decodes must be >= 0");
@@ -417,16 +431,22 @@ kda_status_t kda_mixed_batch(int32_t num_decodes, int32_t num_prefills, int64_t 
   check_prefill_specific(c, num_prefills, num_prefill_tokens, prefill_cu_seqlens, H, K, V,
                          workspace, workspace_bytes);
   check_norm(c, rows, H, V, norm);
+  if (overlap != nullptr) {
+    int dev = -1;
+    const hipError_t e = stream_device(stream, &dev);
+    c.require(e == hipSuccess && dev == overlap->device, INV,
+              "overlap was created on another device than the one `stream` runs on");
+  }
   if (!c.ok()) return c.finish();
 
   // Decode rows [0, D) go to the recurrent kernel, one token per request;
   // prefill rows [D, D + P) to the chunk pipeline on the shifted views (only
   // host pointer arithmetic; device data is never read here). The two parts
-  // touch disjoint slots and rows, so with both present the decode rows run
-  // on a side stream forked from `stream` once the prefill's intra-chunk
-  // kernels are launched, and joined back after its last kernel: the
-  // HBM-bound decode kernel overlaps the latency-bound map and state passes,
-  // which leave LDS free beside their one workgroup per CU.
+  // touch disjoint slots and rows. With the caller's overlap resources the
+  // decode rows run on its side stream, forked from `stream` once the
+  // prefill's plan kernel is launched and joined back after the decode
+  // kernel: the HBM-bound decode kernel then shares the chip with the
+  // prefill's chunk passes. Without them both run on `stream`, decode first.
   const bool has_decode = num_decodes > 0;
   const bool has_prefill = num_prefills > 0 && num_prefill_tokens > 0;
   auto launch_decode_rows = [&](hipStream_t s) -> hipError_t {
@@ -435,7 +455,7 @@ kda_status_t kda_mixed_batch(int32_t num_decodes, int32_t num_prefills, int64_t 
     p.norm = out_norm(norm, 0);
     return kda::launch_decode(p, K, s);
   };
-  auto launch_prefill_rows = [&](hipStream_t s, hipEvent_t after_intra) -> hipError_t {
+  auto launch_prefill_rows = [&](hipStream_t s, hipEvent_t after_plan) -> hipError_t {
     const int64_t D = num_decodes;
     const uint16_t* qkv = static_cast<const uint16_t*>(mixed_qkv) + D * qkv_row_stride;
     const uint16_t* rg = static_cast<const uint16_t*>(raw_g) + D * H * K;
@@ -447,31 +467,31 @@ kda_status_t kda_mixed_batch(int32_t num_decodes, int32_t num_prefills, int64_t 
         prefill_params(num_prefills, num_prefill_tokens, prefill_cu_seqlens, has_initial_state, H,
                        K, V, qkv, qkv_row_stride, rg, rb, gate, &st, o, workspace, workspace_bytes);
     p.norm = out_norm(norm, D);
-    return kda::launch_prefill(p, s, after_intra);
+    return kda::launch_prefill(p, s, after_plan);
   };
-  if (has_decode && has_prefill) {
-    std::lock_guard<std::mutex> lock(g_side_mu);
-    SideStream* side = nullptr;
-    hipError_t e = side_stream_locked(&side);
-    if (e != hipSuccess) return hip_status(e, "mixed batch: side stream");
-    // The fork is recorded inside the prefill launch, after its intra
-    // kernels; once the side stream waits on it, it is joined back whatever
+  if (has_decode && has_prefill && overlap != nullptr) {
+    // The fork is recorded inside the prefill launch, after its plan
+    // kernel; once the side stream waits on it, it is joined back whatever
     // fails in between, so it never outlives the call's work on `stream`
     // (and a capture of `stream` stays joined).
-    const hipError_t ep = launch_prefill_rows(stream, side->fork);
+    const hipError_t ep = launch_prefill_rows(stream, overlap->fork);
     if (ep != hipSuccess) return hip_status(ep, "mixed batch: prefill launch");
-    if ((e = hipStreamWaitEvent(side->stream, side->fork, 0)) != hipSuccess)
+    hipError_t e;
+    if ((e = hipStreamWaitEvent(overlap->stream, overlap->fork, 0)) != hipSuccess)
       return hip_status(e, "mixed batch: fork");
-    const hipError_t ed = launch_decode_rows(side->stream);
-    if ((e = hipEventRecord(side->join, side->stream)) != hipSuccess) return hip_status(e, "mixed batch: join");
-    if ((e = hipStreamWaitEvent(stream, side->join, 0)) != hipSuccess) return hip_status(e, "mixed batch: join");
+    const hipError_t ed = launch_decode_rows(overlap->stream);
+    if ((e = hipEventRecord(overlap->join, overlap->stream)) != hipSuccess) return hip_status(e, "mixed batch: join");
+    if ((e = hipStreamWaitEvent(stream, overlap->join, 0)) != hipSuccess) return hip_status(e, "mixed batch: join");
     if (ed != hipSuccess) return hip_status(ed, "mixed batch: decode launch");
-  } else if (has_decode) {
-    const hipError_t e = launch_decode_rows(stream);
-    if (e != hipSuccess) return hip_status(e, "mixed batch: decode launch");
-  } else if (has_prefill) {
-    const hipError_t e = launch_prefill_rows(stream, nullptr);
-    if (e != hipSuccess) return hip_status(e, "mixed batch: prefill launch");
+  } else {
+    if (has_decode) {
+      const hipError_t e = launch_decode_rows(stream);
+      if (e != hipSuccess) return hip_status(e, "mixed batch: decode launch");
+    }
+    if (has_prefill) {
+      const hipError_t e = launch_prefill_rows(stream, nullptr);
+      if (e != hipSuccess) return hip_status(e, "mixed batch: prefill launch");
+    }
   }
   g_last_error.clear();
   return KDA_OK;

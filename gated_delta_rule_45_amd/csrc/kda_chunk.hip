@@ -12,27 +12,23 @@
 //   O       = scale [ (Q o e^gam) S + P V' ]
 //   S      <- diag(e^{gam_last}) S + (K o e^{gam_last - gam})^T V'
 //
-// Launches on one stream, no host synchronisation (the map pass only when a
-// call of these sizes can cut a sequence; see "segments" below):
-//  1. plan:  chunk offsets and segments per sequence from the device
-//            cu_seqlens.
-//  2. intra: one workgroup per (chunk, head), all chunks in parallel (last
-//            to first). Builds gam in registers, then A and P on bf16 MFMA
-//            from factored operand tiles, the key channels in halves of 64
-//            (or, in a second kernel for a chunk with a block that decays
-//            too steeply, with pairwise fp32 exponentials on the diagonal
-//            blocks), T by forward substitution plus fp32-MFMA block
-//            products, then W and U on MFMA. It stores -W, scale Q o e^gam,
-//            scale P, (K o e^{gam_last-gam})^T (bf16, laid out as MFMA A
-//            operands), e^{gam_last} and U (fp32, in accumulator fragment
-//            order) in the workspace.
-//  3. map:   per non-final segment of a cut sequence, the affine map of
-//            its chunks (below).
-//  4. state: one workgroup per (segment, head, 64 value columns), looping over
-//            the segment's chunks in order. The state lives in MFMA
-//            accumulators (fp32) for the whole sequence; each chunk's A
-//            operands are double-buffered in LDS, and the next chunk's are
-//            copied in while the current one computes.
+// Fused design: one workgroup owns one (segment of a sequence, head) and all
+// of its V value columns. For each chunk in order it builds the chunk's WY
+// operands (gate scan, A, P, T, W, U: the "intra" part) in LDS and registers
+// and then advances the state by them, writing the chunk's output. The
+// operands never leave the workgroup, so the HBM traffic is the inputs read
+// once, the outputs written once and the state read and written once; the
+// next chunk's inputs are loaded while the current one computes.
+//
+// Launches on one stream, no host synchronisation:
+//  1. plan:  validates cu_seqlens and splits long sequences into segments.
+//  2. map:   (only when some sequence is cut) per non-final segment and head,
+//            the affine map S_out = M S_in + B of the segment's chunks, with
+//            the same per-chunk intra part (without the query operands).
+//  3. scan:  (idem) per cut sequence and head, composes the maps in order
+//            into every segment's initial state.
+//  4. state: per segment and head: the segment's chunks from its initial
+//            state, writing the outputs and (last segment) the final state.
 //
 // Accumulator reuse. The bf16 16x16x32 MFMA leaves lane l with rows
 // 4(l/16)+j (j < 4) of column l%16; its B operand wants rows 8(l/16)+j
@@ -51,13 +47,20 @@ namespace kda {
 
 namespace {
 
-constexpr int C = 64;          // chunk size
-constexpr int kThreads = 256;  // 4 waves per workgroup
+constexpr int C = 64;              // chunk size
+constexpr int kWaves = 8;          // waves per fused workgroup (two per SIMD)
+constexpr int kThreads = 64 * kWaves;
+constexpr int kPlanThreads = 256;  // plan kernel
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
 // Index held in permuted storage slot s (0..31) of a 32-block.
@@ -107,13 +110,13 @@ __device__ __forceinline__ bf16x8 lds_frag(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
 }
 
-// Piece swizzle of the record's bf16 tiles. A row of N bf16 elements is
-// N/8 16-byte pieces; piece p of row r is stored at piece p ^ swz<N>(r). The
-// state kernel copies the record to LDS byte for byte and reads MFMA
-// fragments of 16 consecutive rows at one logical piece: the swizzle puts
-// those 16 reads in 16 different 16-byte bank groups (and any 8 consecutive
-// rows in 8), for 256-byte rows (r & 15) and for 128-byte rows, whose odd
-// rows start half way round the banks (r ^ r >> 3) & 7.
+// Piece swizzle of the operand tiles the state step reads. A row of N bf16
+// elements is N/8 16-byte pieces; piece p of row r is stored at piece
+// p ^ swz<N>(r). MFMA fragments read 16 consecutive rows at one logical
+// piece: the swizzle puts those 16 reads in 16 different 16-byte bank groups
+// (and any 8 consecutive rows in 8), for 256-byte rows (r & 15) and for
+// 128-byte rows, whose odd rows start half way round the banks
+// (r ^ r >> 3) & 7.
 template <int N>
 __device__ __forceinline__ int swz(int r) {
   static_assert(N / 8 >= 8, "rows of at least 8 pieces");
@@ -132,80 +135,93 @@ __device__ __forceinline__ bf16x8 frag(const uint16_t* tile, int r, int c) {
   return lds_frag(tile + rec_elem<N>(r, c));
 }
 
-// Per-(chunk, head) record in the workspace. The first five fields are
-// copied to LDS as one contiguous block by the state kernel; its bf16 tiles
-// are stored with the swizzle above.
-template <int K, int V>
-struct Rec {
-  static constexpr size_t Wn = 0;                      // bf16 [C][K], -W, channels permuted
-  static constexpr size_t Qg = Wn + C * K * 2;         // bf16 [C][K], scale Q o e^gam, channels permuted
-  static constexpr size_t Pm = Qg + C * K * 2;         // bf16 [C][C], scale P, positions permuted
-  static constexpr size_t KgT = Pm + C * C * 2;        // bf16 [K][C], positions permuted
-  static constexpr size_t Eg = KgT + K * C * 2;        // fp32 [K], e^{gam_last}
-  static constexpr size_t lds_part = Eg + K * 4;       // bytes copied to LDS
-  static constexpr size_t Uf = (lds_part + 255) / 256 * 256;  // fp32 fragments [C/16][V/16][64][4]
-  static constexpr size_t bytes = (Uf + C * V * 4 + 255) / 256 * 256;
-};
+// Element offsets in XOR-swizzled row-major LDS tiles of the intra part: the
+// 16-byte pieces of row t are permuted by t, so the 16 rows an MFMA fragment
+// touches fall in different banks.
+template <int N>  // bf16 tile [C][N]: 8 elements per piece
+__device__ __forceinline__ int sw16(int t, int c) {
+  constexpr int PM = (N / 8 > 16 ? 16 : N / 8) - 1;
+  return t * N + ((((c >> 3) ^ (t & PM)) << 3) | (c & 7));
+}
+template <int N>  // fp32 tile [C][N]: 4 elements per piece
+__device__ __forceinline__ int sw32(int t, int c) {
+  constexpr int PM = (N / 4 > 16 ? 16 : N / 4) - 1;
+  return t * N + ((((c >> 2) ^ (t & PM)) << 2) | (c & 3));
+}
+
+// The thread index, hidden from the optimiser at each use. Inside the chunk
+// loops every LDS and buffer address is a function of it; without this the
+// compiler hoists all of those addresses out of the loop and keeps them live
+// for its whole length, which runs the workgroup out of registers.
+__device__ __forceinline__ int opaque_tid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
 
 // Waits until this wave's outstanding vector-memory operations (including
 // LDS DMA) have completed: vmcnt = 0, other counters unconstrained.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-__host__ __device__ inline int64_t max_chunks_for(int64_t num_tokens, int32_t num_seqs) {
-  return num_tokens / C + num_seqs;
-}
-
-// Records, maps and starting states are laid out head-major: the chunks of
-// one head follow each other, so a workgroup walking a head's chunks reads
-// one contiguous stream.
-__device__ __forceinline__ int64_t rec_index(int h, int c, const PrefillParams& p) {
-  return static_cast<int64_t>(h) * max_chunks_for(p.num_tokens, p.num_seqs) + c;
+// Top of a chunk: this wave's vector-memory operations have completed except
+// the last `Pending` (the previous chunk's output stores, issued after the
+// loads of this chunk's inputs; they complete in issue order), its LDS
+// operations are done, and all waves meet. Unlike __syncthreads this leaves
+// the output stores in flight.
+template <int Pending>
+__device__ __forceinline__ void chunk_barrier() {
+  static_assert(Pending >= 0 && Pending < 64, "vmcnt field");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0070 | (Pending & 15) | ((Pending >> 4) << 14));  // expcnt 7, lgkmcnt 0
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // ------------------------------------------------------------- segments --
 //
-// The inter-chunk pass carries one state per (sequence, head) through the
-// sequence's chunks, so a long sequence is a chain of dependent steps on a
-// few workgroups. The chunk recurrence is affine in the state: after a run
-// of chunks, S_out = M S_in + B with
+// The state pass carries one state per (sequence, head) through the
+// sequence's chunks, so a long sequence is a chain of dependent steps on one
+// workgroup. The chunk recurrence is affine in the state: after a run of
+// chunks, S_out = M S_in + B with
 //   M = prod_c (diag(e^{gam_last}) - (K o e^{gam_last - gam})^T W)   (K x K)
 //   B = the state reached from S_in = 0                                (K x V)
-// so a long sequence is cut into segments: a map pass computes (M, B) of
-// every segment but the last in parallel, and in the state pass every
-// segment first walks the maps of the segments before it
-// (S_{j+1} = M_j S_j + B_j, a K x K by K x 16 product per wave and step)
-// and then runs its own chunks, all segments in parallel.
+// so a long sequence is cut into segments: the map pass computes (M, B) of
+// every segment but the last in parallel, the scan pass composes them in
+// order into each segment's initial state (S_{j+1} = M_j S_j + B_j, stored
+// over B_j), and the state pass runs every segment's chunks in parallel.
 //
 // A sequence is cut into at most ceil(chunks / kSegMinChunks) segments of
 // equal length (the last may be shorter), into no more segments than it
-// takes for the cut sequences' state-pass workgroups to occupy kChipSlots
-// slots (one per compute unit: its LDS image allows one workgroup per CU),
-// and only into kMinCut segments or more: a map chunk costs about as much as
-// a state chunk, so two segments would not shorten the chain.
+// takes for the cut sequences' workgroups to occupy kChipSlots slots (one
+// per compute unit: a workgroup's LDS takes most of a CU), and only into
+// kMinCut segments or more: a map chunk costs about as much as a state
+// chunk, so two segments would not shorten the chain.
 constexpr int kSegMinChunks = 16;
 constexpr int kMaxSegs = 16;  // <= kSegMinChunks: keeps the last segment non-empty
 constexpr int kMinCut = 3;
 constexpr int kChipSlots = 256;
 static_assert(kMaxSegs <= kSegMinChunks, "segment count bound");
 
-// Device-side plan of one prefill call, written by plan_kernel.
+// Device-side plan of one prefill call, written by plan_kernel. counts[0]
+// is the call's status word (workspace offset 0): 0 when cu_seqlens keep to
+// the contract, else KDA_PREFILL_BAD_CU_SEQLENS.
 struct SegPlan {
-  int32_t* chunk_start;  // [N+1] first chunk slot of each sequence
-  int4* chunk_info;      // [max_chunks] per intra workgroup row j: {chunk slot, first token, tokens, 0}
-                         // of chunk slot (chunks - 1 - j); tokens = 0 past the last chunk
+  int32_t* counts;       // [4]: status, segments, maps, cut sequences
+  int32_t* chunk_start;  // [N+1] first chunk of each sequence (in chunk units of the call)
   int32_t* seg_start;    // [N+1] first segment of each sequence
-  int32_t* counts;       // [4]: segments, maps, long sequences, plan fits its bounds
   int32_t* seg_seq;      // [seg_bound] sequence of each segment
   int32_t* seg_long;     // [seg_bound] index of a cut sequence among the cut ones, else -1
   int32_t* map_seg;      // [map_bound] segment of each map item (a non-final segment)
-  float* maps;           // [H][map_bound]: M (fp32 [K][K]) then B (fp32 [K][V])
+  int32_t* long_seq;     // [long_bound] sequence of each cut sequence
+  float* maps;           // [H][map_bound]: M (fp32 [K][K]) then B (fp32 [K][V]); after the
+                         // scan pass, B of map item j holds the initial state of segment j + 1
   float* s0;             // [H][long_bound]: fp32 [K][V] initial state of each cut sequence
   int32_t seg_bound, map_bound, long_bound;
   int32_t max_segs;      // segments per sequence at most (host bound)
-  int32_t fill_units;    // state-pass workgroups per segment (H * V / 64)
-  int32_t max_chunks;    // chunk slots the records are sized for
   int32_t num_tokens;    // rows of the call (validated to fit in int32)
 };
+
+constexpr int32_t kBadCuSeqlens = 1;
 
 __device__ __forceinline__ int64_t map_index(int h, int mi, const SegPlan& pl) {
   return static_cast<int64_t>(h) * pl.map_bound + mi;
@@ -219,41 +235,28 @@ __device__ __forceinline__ int64_t s0_index(int h, int li, const SegPlan& pl) {
 // segments, so a call has at most num_tokens / (64 kSegMinChunks) of them
 // (and at most num_seqs (max_segs - 1)); each cut sequence has at least one.
 struct Layout {
-  int64_t seg_bound, map_bound, long_bound, max_segs, fill_units;
-  size_t chunk_start, seg_start, counts, seg_seq, seg_long, map_seg, chunk_info;
-  size_t flags, recs, maps, s0, total;
+  int64_t seg_bound, map_bound, long_bound, max_segs;
+  size_t counts, chunk_start, seg_start, seg_seq, seg_long, map_seg, long_seq, maps, s0, total;
 };
 
 inline size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
-inline size_t rec_bytes_for(int32_t K, int32_t V) {
-  if (K == 64 && V == 64) return Rec<64, 64>::bytes;
-  if (K == 64 && V == 128) return Rec<64, 128>::bytes;
-  if (K == 128 && V == 64) return Rec<128, 64>::bytes;
-  return Rec<128, 128>::bytes;
-}
-
 inline Layout layout_for(int32_t num_seqs, int64_t num_tokens, int32_t H, int32_t K, int32_t V) {
   Layout L{};
   const int64_t N = num_seqs;
-  L.fill_units = static_cast<int64_t>(H) * (V / 64);
-  L.max_segs = std::min<int64_t>(kMaxSegs, std::max<int64_t>(1, (kChipSlots + L.fill_units - 1) / L.fill_units));
+  L.max_segs = std::min<int64_t>(kMaxSegs, std::max<int64_t>(1, (kChipSlots + H - 1) / H));
   L.map_bound = L.max_segs < kMinCut ? 0 : std::min<int64_t>(num_tokens / (C * kSegMinChunks), N * (L.max_segs - 1));
   L.long_bound = L.map_bound;
   L.seg_bound = N + L.map_bound;
   size_t o = 0;
+  L.counts = o;      o += 16;
   L.chunk_start = o; o += (N + 1) * 4;
   L.seg_start = o;   o += (N + 1) * 4;
-  L.counts = o;      o += 16;
   L.seg_seq = o;     o += L.seg_bound * 4;
   L.seg_long = o;    o += L.seg_bound * 4;
   L.map_seg = o;     o += L.map_bound * 4;
-  const int64_t maxc = max_chunks_for(num_tokens, num_seqs);
-  L.chunk_info = (o + 15) / 16 * 16;
-  o = L.chunk_info + static_cast<size_t>(maxc) * 16;
-  L.flags = round256(o);
-  L.recs = L.flags + round256(static_cast<size_t>(maxc) * H);
-  L.maps = L.recs + static_cast<size_t>(maxc) * H * rec_bytes_for(K, V);
+  L.long_seq = o;    o += L.long_bound * 4;
+  L.maps = round256(o);
   L.s0 = L.maps + static_cast<size_t>(L.map_bound) * H * (static_cast<size_t>(K) * K + static_cast<size_t>(K) * V) * 4;
   L.total = L.s0 + static_cast<size_t>(L.long_bound) * H * static_cast<size_t>(K) * V * 4;
   return L;
@@ -261,7 +264,7 @@ inline Layout layout_for(int32_t num_seqs, int64_t num_tokens, int32_t H, int32_
 
 // ------------------------------------------------------------------ plan --
 
-// Exclusive prefix sum of x over the workgroup (kThreads threads, 64-lane
+// Exclusive prefix sum of x over the workgroup (kPlanThreads threads, 64-lane
 // waves); `total` receives the sum. Every thread must call it.
 __device__ __forceinline__ int block_exclusive_scan(int x, int* part, int& total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -276,7 +279,7 @@ __device__ __forceinline__ int block_exclusive_scan(int x, int* part, int& total
   int before = 0;
   total = 0;
 #pragma unroll
-  for (int k = 0; k < kThreads / 64; ++k) {
+  for (int k = 0; k < kPlanThreads / 64; ++k) {
     const int t = part[k];
     if (k < w) before += t;
     total += t;
@@ -294,20 +297,29 @@ __device__ __forceinline__ int segments_of(int nch, int target) {
   return ns >= kMinCut ? ns : 1;
 }
 
-// Chunk slots and segments of every sequence. The segment target is the
+// Checks cu_seqlens (starts at 0, non-decreasing, ends at num_tokens) and
+// plans chunks and segments of every sequence. The segment target is the
 // number of segments each cut sequence needs for the cut sequences together
-// to occupy the chip.
-__global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t* cu, int32_t N, SegPlan pl) {
-  __shared__ int part[kThreads / 64];
+// to occupy the chip. With cu_seqlens outside the contract the status word
+// is set and no segment exists: the state pass then writes NaN to every
+// output row and touches no state.
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* cu, int32_t N, int32_t H, SegPlan pl) {
+  __shared__ int part[kPlanThreads / 64];
   const int tid = threadIdx.x;
-  const int per = (N + kThreads - 1) / kThreads;
+  const int per = (N + kPlanThreads - 1) / kPlanThreads;
   const int b = tid * per;
   const int e = min(N, b + per);
-  int nl = 0;
-  for (int i = b; i < e; ++i) nl += chunks_of(cu, i) > (kMinCut - 1) * kSegMinChunks;  // can be cut
+  int bad = 0, nl = 0;
+  for (int i = b; i < e; ++i) {
+    bad |= cu[i + 1] < cu[i];
+    nl += chunks_of(cu, i) > (kMinCut - 1) * kSegMinChunks;  // can be cut
+  }
+  if (tid == 0) bad |= cu[0] != 0 || cu[N] != pl.num_tokens;
+  int nbad;
+  block_exclusive_scan(bad, part, nbad);
   int n_long;
   block_exclusive_scan(nl, part, n_long);
-  const int units = pl.fill_units * max(n_long, 1);
+  const int units = H * max(n_long, 1);
   const int target = min(pl.max_segs, max(1, (kChipSlots + units - 1) / units));
 
   int cc = 0, sc = 0, lc = 0;
@@ -323,19 +335,14 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t* cu, int32
   int sb = block_exclusive_scan(sc, part, stot);
   int lb = block_exclusive_scan(lc, part, ltot);
   const int mtot = stot - N;
-  // Holds for cu_seqlens that keep to the contract; otherwise no segment
-  // tables are written and the state pass does nothing.
-  const bool fits = stot <= pl.seg_bound && mtot <= pl.map_bound && ltot <= pl.long_bound;
-  // Intra rows past the last chunk do nothing (so do all rows if the
-  // chunks outgrow the records).
-  for (int jj = (ctot <= pl.max_chunks ? ctot : 0) + tid; jj < pl.max_chunks; jj += kThreads)
-    pl.chunk_info[jj] = int4{0, 0, 0, 0};
+  // The bounds hold for cu_seqlens that keep to the contract.
+  const bool ok = nbad == 0 && stot <= pl.seg_bound && mtot <= pl.map_bound && ltot <= pl.long_bound;
   for (int i = b; i < e; ++i) {
     const int nch = chunks_of(cu, i);
     const int ns = segments_of(nch, target);
     pl.chunk_start[i] = cb;
     pl.seg_start[i] = sb;
-    if (fits) {
+    if (ok) {
       // Map items of sequence i start at sb - i (each earlier sequence has
       // one fewer than its segments); lb counts the earlier cut sequences.
       for (int s = 0; s < ns; ++s) {
@@ -343,204 +350,837 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t* cu, int32
         pl.seg_long[sb + s] = ns > 1 ? lb : -1;
       }
       for (int s = 0; s + 1 < ns; ++s) pl.map_seg[sb - i + s] = sb + s;
+      if (ns > 1) pl.long_seq[lb] = i;
     }
     cb += nch;
     sb += ns;
     lb += ns > 1;
   }
-  __syncthreads();  // chunk_start[0 .. N-1] visible to every thread
-  if (ctot <= pl.max_chunks) {
-    // Intra row j takes chunk slot ctot - 1 - j (the chunks last to first);
-    // slot c belongs to the last sequence whose first slot is <= c.
-    for (int c = tid; c < ctot; c += kThreads) {
-      int lo = 0, hi = N;
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (pl.chunk_start[mid] <= c) lo = mid; else hi = mid;
-      }
-      const int k = c - pl.chunk_start[lo];
-      const int bos = cu[lo], eos = cu[lo + 1];
-      const bool ok = bos >= 0 && eos <= pl.num_tokens;
-      pl.chunk_info[ctot - 1 - c] = ok ? int4{c, bos + C * k, min(C, eos - bos - C * k), 0} : int4{0, 0, 0, 0};
-    }
-  }
   if (tid == 0) {
     pl.chunk_start[N] = ctot;
     pl.seg_start[N] = stot;
-    pl.counts[0] = stot;
-    pl.counts[1] = mtot;
-    pl.counts[2] = ltot;
-    pl.counts[3] = fits ? 1 : 0;
+    pl.counts[0] = ok ? 0 : kBadCuSeqlens;
+    pl.counts[1] = ok ? stot : 0;
+    pl.counts[2] = ok ? mtot : 0;
+    pl.counts[3] = ok ? ltot : 0;
   }
 }
 
-// --------------------------------------------------------------- intra --
-
-// Element offsets in XOR-swizzled row-major LDS tiles: the 16-byte pieces of
-// row t are permuted by t, so the 16 rows an MFMA fragment touches fall in
-// different banks (no padding, which keeps two workgroups per CU).
-template <int N>  // bf16 tile [C][N]: 8 elements per piece
-__device__ __forceinline__ int sw16(int t, int c) {
-  constexpr int PM = (N / 8 > 16 ? 16 : N / 8) - 1;
-  return t * N + ((((c >> 3) ^ (t & PM)) << 3) | (c & 7));
-}
-template <int N>  // fp32 tile [C][N]: 4 elements per piece
-__device__ __forceinline__ int sw32(int t, int c) {
-  constexpr int PM = (N / 4 > 16 ? 16 : N / 4) - 1;
-  return t * N + ((((c >> 2) ^ (t & PM)) << 2) | (c & 3));
-}
-
-// Exact intra kernel LDS: 80 KiB at K = 128, two workgroups per CU.
-//  k   bf16 [C][K] (sw16)  keys (zero rows past the chunk end)
-//  q   bf16 [C][K] (sw16)  queries
-//  u   union of
-//        gam  fp32 [C][K] (sw32)  cumulative log-decay, and
-//        kf   bf16 [C][K] space, placing x over gam's second half; its
-//             first bytes hold beta after A/P, and
-//        x    fp32 scratch: part totals, gam at block starts and per-block
-//             decay ranges until gam is written; then (K o e^gam)^T, bf16
-//             [K][C] (swz<C>), the B operand of W
-//  at  fp32 [C][C] (sw32)  A^T
-//                          strictly above the diagonal (at(s,t) = A[t][s]),
-//                          T = (I + A)^{-1} strictly below it (unit
-//                          diagonal implicit), beta on it
-template <int K, int V>
-struct IntraSmem {
-  uint16_t k[C * K];
-  uint16_t q[C * K];
-  union {
-    float gam[C * K];
-    struct {
-      uint16_t kf[C * K];
-      float x[C * K / 2];
-    } f;
-  } u;
-  float at[C * C];
-};
-
-// Layout of the x scratch (in floats).
-template <int K>
-struct XLayout {
-  static constexpr int PARTS = kThreads / (K / 4);  // threads per channel quad in the gate scan
-  static constexpr int tot = 0;               // [PARTS][K] partial sums of the gate scan
-  static constexpr int bnd = tot + PARTS * K; // [4][K] gam at rows 16 I
-  static constexpr int dmax = bnd + 4 * K;    // [4 blocks] largest decay range
-  static constexpr int cij = dmax + 16;       // [10][K] e^{gam(16 I) - gam(16 J)}, J <= I
-  static constexpr int end = cij + 10 * K;
-  static_assert(end <= C * K / 2, "x scratch overflows its area");
-};
+// ------------------------------------------------------- the intra part --
 
 // Factored-path bound on a 16-row block's decay range: every factored
 // operand then lies in [e^-80, e^80], inside bf16/fp32 range.
 constexpr float kMaxBlockDecay = 80.f;
 
-__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+// Thread roles of the intra part: thread (q4, part) owns channels 4 q4 ..
+// 4 q4 + 3 at positions part PP .. part PP + PP - 1, so its tile reads and
+// writes are 8 bytes wide and wave w holds rows 8 w .. 8 w + 7, half of the
+// 16-row block w / 2.
+template <int K>
+struct Roles {
+  static constexpr int NQ = K / 4;              // channel quads
+  static constexpr int NPART = kThreads / NQ;   // 16 at K = 128, 32 at K = 64
+  static constexpr int PP = C / NPART;          // positions per thread: 4 or 2
+  static constexpr int KP8 = K / 8;             // 16-byte pieces per bf16 row
+  static constexpr int RW = C / kWaves;         // rows per wave
+  static_assert(NPART * PP == C && (64 / NQ) * PP == RW && RW == 8, "a wave holds 8 consecutive rows");
+};
+
+// fp32 scratch of the intra part (in floats). The 16-row blocks of a chunk
+// are factored against rho_I = gam just before block I (the sum of the log
+// decays of rows 0 .. 16 I - 1; rho_0 = 0), which every thread can form from
+// the gate scan's partial totals without another exchange.
+template <int K>
+struct XLayout {
+  static constexpr int NP = Roles<K>::NPART;
+  static constexpr int tot = 0;                              // [NPART][K] partial sums of the gate scan
+  static constexpr int cij = tot + NP * K;                   // [10][K] e^{rho_I - rho_J}, J <= I
+  static constexpr int drange = cij + 10 * K;                // [4] largest decay over a block (rho_I - gam(16 I + 15))
+  static constexpr int beta = drange + 16;                   // [C] beta per position
+  static constexpr int end = beta + C;
+};
+
+// Factor pairs (I, J), J <= I, in the order of x.cij: pair pr = I (I+1)/2 + J.
+__device__ __forceinline__ void cij_pair(int pr, int& I, int& J) {
+  I = pr < 1 ? 0 : pr < 3 ? 1 : pr < 6 ? 2 : 3;
+  J = pr - I * (I + 1) / 2;
 }
 
-// Steps common to both intra kernels once A^T (with beta on its diagonal)
-// is in at, (K o e^gam)^T in wkt, beta in beta_l and the lane's v operands
-// in vpre: T = (I + A)^{-1} in at, then W and U into the record.
+// Operand tiles the state (or map) step reads, built per chunk. The bf16
+// tiles are swizzled (rec_elem) for fragment reads.
+template <int K, bool Q>
+struct ChunkOps {
+  uint16_t wn[C * K];            // -W, channels permuted
+  uint16_t qg[Q ? C * K : 8];    // scale Q o e^gam, channels permuted
+  uint16_t pm[Q ? C * C : 8];    // scale P, positions permuted
+  uint16_t kgt[K * C];           // (K o e^{gam_last - gam})^T, positions permuted
+  float eg[K];                   // e^{gam_last}
+};
+
+// LDS of a fused workgroup. Q: the state kernel (query operands and
+// output); EXACT: chunks whose 16-row blocks decay too steeply for the
+// factored operands take the pairwise path (only launched when the gate's
+// bound does not rule them out).
+template <int K, bool Q, bool EXACT>
+struct FusedSmem {
+  struct {
+    ChunkOps<K, Q> ops;
+  } r;
+  union {
+    struct {                     // factored path: raw keys and queries (copied in), then K o R and Q o R; K o F
+      uint16_t k[C * K];
+      uint16_t q[Q ? C * K : 8];
+      uint16_t kf[C * K];
+    } f;
+    struct {                     // exact path: raw keys and queries, gam
+      uint16_t k[C * K];
+      uint16_t q[Q ? C * K : 8];
+      float gam[EXACT ? C * K : 4];
+    } e;
+    uint16_t wkt[K * C];         // (K o e^gam)^T, bf16 [K][C] (swz<C>), after A/P (EXACT)
+  } t;
+  // Without the exact path (K o e^gam)^T has its own area, so the next
+  // chunk's keys and queries can be copied into the tile area right after A/P.
+  uint16_t wkt_own[EXACT ? 8 : K * C];
+  float at[C * C];               // A^T strictly above the diagonal, then T = (I+A)^{-1} below it
+  float x[XLayout<K>::end];
+  __device__ uint16_t* wkt() {
+    if constexpr (EXACT) return t.wkt;
+    else return wkt_own;
+  }
+};
+
+// One chunk's register-held inputs, loaded a chunk ahead.
 template <int K, int V>
-__device__ __forceinline__ void intra_inverse_wu(const PrefillParams& p, float* at, const uint16_t* wkt,
-                                                 const float* beta_l,
-                                                 const uint16_t (&vpre)[(V / 16 + 3) / 4][2][8],
-                                                 char* rec, int w, int lane) {
-  using R = Rec<K, V>;
-  constexpr int NBU = (V / 16 + 3) / 4;
-  const int m = lane & 15;
-  const int g = lane >> 4;
-  // ---- 5. T = (I + A)^{-1}: diagonal blocks by forward substitution -----
-  // at(s, t) = A[t][s] for s < t; T strictly below the diagonal of at.
+struct ChunkIn {
+  static constexpr int PP = Roles<K>::PP;
+  u32x2 rgw[PP];                      // raw_g of the thread's 4 channels at its PP positions
+  uint16_t rb;                        // raw beta of position tid
+  uint16_t vpre[2][8];                // v operands of U (waves w < V / 16): lane (m, g) needs
+                                      // v[32 kb + 8 g + j][16 w + m]
+};
+
+// Where one chunk's rows are: first token and token count (n <= 64).
+struct ChunkPos {
+  int64_t t0;
+  int n;
+};
+
+// Issues the register loads of chunk (t0, n) that the gate scan consumes:
+// raw_g and raw beta. Rows past the chunk end read zero (buffer range).
+template <int K, int V>
+__device__ __forceinline__ void load_chunk_gate_regs(const PrefillParams& p, int h, ChunkPos cp, ChunkIn<K, V>& in) {
+  using Ro = Roles<K>;
+  const int H = p.H;
+  const int tid = opaque_tid();
+  const int q4 = tid % Ro::NQ, part = tid / Ro::NQ;
+  const int c4 = 4 * q4;
+  const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.raw_g + cp.t0 * (H * K), static_cast<uint32_t>(cp.n * H * K * 2));
+#pragma unroll
+  for (int i = 0; i < Ro::PP; ++i)
+    in.rgw[i] = __builtin_amdgcn_raw_buffer_load_b64(rg, ((part * Ro::PP + i) * H * K + h * K + c4) * 2, 0, 0);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.raw_beta + cp.t0 * H, static_cast<uint32_t>(cp.n * H * 2));
+  in.rb = __builtin_amdgcn_raw_buffer_load_b16(rb, (tid * H + h) * 2, 0, 0);
+}
+
+// Issues the loads of the v operands of chunk (t0, n) (waves w < V / 16).
+template <int K, int V>
+__device__ __forceinline__ void load_chunk_v_regs(const PrefillParams& p, int h, ChunkPos cp, ChunkIn<K, V>& in) {
+  const int H = p.H;
+  const int tid = opaque_tid(), lane = tid & 63, w = uniform(tid >> 6);
+  const int m = lane & 15, g = lane >> 4;
+  if (w < V / 16) {  // wave-uniform
+    const int rs = static_cast<int>(p.qkv_row_stride * 2);  // bytes per mixed_qkv row
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.qkv + cp.t0 * p.qkv_row_stride, static_cast<uint32_t>(cp.n * rs));
+    const int vlane = (2 * H * K + h * V + 16 * w + m) * 2 + 8 * g * rs;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        in.vpre[kb][j] = __builtin_amdgcn_raw_buffer_load_b16(rv, vlane, (32 * kb + j) * rs, 0);
+  }
+}
+
+// All register loads of chunk (t0, n).
+template <int K, int V>
+__device__ __forceinline__ void load_chunk_regs(const PrefillParams& p, int h, ChunkPos cp, ChunkIn<K, V>& in) {
+  load_chunk_gate_regs<K, V>(p, h, cp, in);
+  load_chunk_v_regs<K, V>(p, h, cp, in);
+}
+
+// Copies chunk (t0, n)'s keys (and queries when Q) into the tile area by
+// buffer-to-LDS DMA, 16-byte pieces XOR-swizzled by the row (sw16<K>); rows
+// past the chunk end read zero.
+template <int K, bool Q>
+__device__ __forceinline__ void dma_chunk_tiles(const PrefillParams& p, int h, ChunkPos cp, uint16_t* k_lds,
+                                                uint16_t* q_lds) {
+  using Ro = Roles<K>;
+  const int tid = opaque_tid();
+  const int64_t rs = p.qkv_row_stride * 2;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.qkv + cp.t0 * p.qkv_row_stride, static_cast<uint32_t>(cp.n * rs));
+  constexpr int KPM = (Ro::KP8 > 16 ? 16 : Ro::KP8) - 1;
+  static_assert((C * Ro::KP8) % kThreads == 0, "whole DMA rounds");
+#pragma unroll
+  for (int r = 0; r < C * Ro::KP8 / kThreads; ++r) {
+    const int ps = r * kThreads + tid;          // physical piece in the tile
+    const int t = ps / Ro::KP8;
+    const int pl = (ps % Ro::KP8) ^ (t & KPM);  // logical piece stored there
+    const int slot = r * kThreads + (tid & ~63);
+    const int qoff = static_cast<int>(t * rs) + (h * K + pl * 8) * 2;
+    if constexpr (Q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, reinterpret_cast<uint4*>(q_lds) + slot, 16, qoff, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, reinterpret_cast<uint4*>(k_lds) + slot, 16, qoff + p.H * K * 2, 0, 0, 0);
+  }
+}
+
+// Gate and cumulative log-decay of the chunk, in registers: gm[i][j] = gam
+// at the thread's position i and channel j, gl[j] = gam_last of channel j,
+// rho[j] = rho of the thread's block. Writes beta to x.beta, e^{gam_last} to
+// ops.eg, the factors c_IJ to x.cij and the blocks' decay ranges to
+// x.drange; returns whether every block's range is within kMaxBlockDecay
+// (the same value in every thread). Only the partial totals are exchanged
+// (one barrier); the other outputs become visible at the next barrier.
+template <int K, int V, bool Q, bool EXACT>
+__device__ __forceinline__ bool gate_scan(const PrefillParams& p, int h, int n, const ChunkIn<K, V>& in,
+                                          FusedSmem<K, Q, EXACT>& sm, float (&gm)[Roles<K>::PP][4],
+                                          float (&gl)[4], float (&rho)[4]) {
+  using Ro = Roles<K>;
+  using XL = XLayout<K>;
+  constexpr int PP = Ro::PP, NQ = Ro::NQ, NPART = Ro::NPART;
+  constexpr int PB = NPART / 4;  // parts per 16-row block
+  const int tid = opaque_tid(), lane = tid & 63, w = uniform(tid >> 6);
+  const int q4 = tid % NQ, part = tid / NQ;
+  const int c4 = 4 * q4;
+  float* x = sm.x;
+  const float a_h = __expf(p.A_log[h]);
+  float dtb[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) dtb[j] = p.dt_bias[h * K + c4 + j];
+  const float beta_t = (tid < n) ? sigmoid_f32(bf16_to_f32(in.rb)) : 0.f;
+  const bool has_lb = p.has_lb != 0;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < PP; ++i) {
+    // Padded positions do not decay, so row 63 holds gam_last.
+    const bool live = part * PP + i < n;
+    const float rg4[4] = {__uint_as_float(in.rgw[i][0] << 16), __uint_as_float(in.rgw[i][0] & 0xffff0000u),
+                          __uint_as_float(in.rgw[i][1] << 16), __uint_as_float(in.rgw[i][1] & 0xffff0000u)};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float gv = gate_log_decay(rg4[j], dtb[j], a_h, has_lb, p.lower_bound);
+      acc[j] += live ? gv : 0.f;
+      gm[i][j] = acc[j];
+    }
+  }
+  *reinterpret_cast<f32x4*>(&x[XL::tot + part * K + c4]) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+  lds_barrier();  // partial totals visible
+  // Prefix sums over the parts: before this thread's part, before each
+  // block (rho_I), and the total (gam_last).
+  float before[4] = {0.f, 0.f, 0.f, 0.f}, pb[5][4], run[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int q2 = 0; q2 < NPART; ++q2) {
+    if (q2 % PB == 0) {  // a block boundary: rho of block q2 / PB
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pb[q2 / PB][j] = run[j];
+    }
+    if (q2 == part) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) before[j] = run[j];
+    }
+    const f32x4 tq = *reinterpret_cast<const f32x4*>(&x[XL::tot + q2 * K + c4]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) run[j] += tq[j];
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) pb[4][j] = run[j];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    gl[j] = pb[4][j];
+    rho[j] = pb[0][j];
+  }
+#pragma unroll
+  for (int I = 1; I < 4; ++I)
+    if ((w >> 1) == I) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) rho[j] = pb[I][j];
+    }
+#pragma unroll
+  for (int i = 0; i < PP; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) gm[i][j] += before[j];
+  if (tid < C) x[XL::beta + tid] = beta_t;
+  if (part == 0)
+    *reinterpret_cast<f32x4*>(&sm.r.ops.eg[c4]) = f32x4{__expf(gl[0]), __expf(gl[1]), __expf(gl[2]), __expf(gl[3])};
+  // c_IJ of the thread's channels for one pair (I, J) per part.
+  if (part < 10) {
+    int I, J;
+    cij_pair(part, I, J);
+    float c[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float rI = pb[0][j], rJ = pb[0][j];
+#pragma unroll
+      for (int b2 = 1; b2 < 4; ++b2) {
+        if (I == b2) rI = pb[b2][j];
+        if (J == b2) rJ = pb[b2][j];
+      }
+      c[j] = __expf(rI - rJ);
+    }
+    *reinterpret_cast<f32x4*>(&x[XL::cij + part * K + c4]) = f32x4{c[0], c[1], c[2], c[3]};
+  }
+  if constexpr (!EXACT) {
+    return true;
+  } else {
+    // Each wave's lanes cover every channel: the largest range of each
+    // block by a butterfly, identical in every wave.
+    bool fast = true;
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+      float d = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) d = fmaxf(d, pb[I][j] - pb[I + 1][j]);
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) d = fmaxf(d, __shfl_xor(d, off));
+      if (tid == 0) x[XL::drange + I] = d;
+      fast = fast && d <= kMaxBlockDecay;
+    }
+    return fast;
+  }
+}
+
+// Off-diagonal blocks of A and P: waves 4..7 take (1,0) and (3,2), (2,1)
+// and (3,0), (2,0), (3,1); waves 0..3 take the diagonal block (w, w).
+__device__ __forceinline__ void offdiag_block(int w, int bi, int& I, int& J) {
+  if (bi == 1 && w >= 6) {
+    I = J = -1;
+    return;
+  }
+  if (w == 4) { I = bi ? 3 : 1; J = bi ? 2 : 0; }
+  else if (w == 5) { I = bi ? 3 : 2; J = bi ? 0 : 1; }
+  else if (w == 6) { I = 2; J = 0; }
+  else { I = 3; J = 1; }
+}
+
+// Inverse of the unit lower-triangular diagonal block blk of (I + A) by
+// forward substitution on lanes 0..15 of the calling wave (lane jc solves
+// column jc): at(s, t) = A[t][s] for s < t in, T strictly below the
+// diagonal of the block out. Each row's sum runs over the earlier rows in
+// order, so when x_{t-1} lands only one FMA of row t is left.
+__device__ __forceinline__ void diag_inverse(float* at, int blk, int lane) {
   if (lane < 16) {
-    const int blk = w, jc = lane;
-    float x[16];
+    const int jc = lane;
+    float xs[16];
 #pragma unroll
     for (int tt = 0; tt < 16; ++tt) {
       float v = (tt == jc) ? 1.f : 0.f;
 #pragma unroll
-      for (int s3 = 0; s3 < tt; ++s3) v = fmaf(-at[sw32<C>(16 * blk + s3, 16 * blk + tt)], x[s3], v);
-      x[tt] = v;
+      for (int s3 = 0; s3 < tt; ++s3) v = fmaf(-at[sw32<C>(16 * blk + s3, 16 * blk + tt)], xs[s3], v);
+      xs[tt] = v;
     }
 #pragma unroll
     for (int tt = 0; tt < 16; ++tt)
-      if (tt > jc) at[sw32<C>(16 * blk + tt, 16 * blk + jc)] = x[tt];
+      if (tt > jc) at[sw32<C>(16 * blk + tt, 16 * blk + jc)] = xs[tt];
+  }
+}
+
+// Zero P blocks above the diagonal that the state step reads: rows 0..15 x
+// cols 16..31 and rows 32..47 x cols 48..63.
+template <int K, bool Q>
+__device__ __forceinline__ void zero_p_blocks(ChunkOps<K, Q>& ops, int m, int g) {
+  *reinterpret_cast<u32x2*>(&ops.pm[rec_elem<C>(m, 8 * g + 4)]) = u32x2{0u, 0u};
+  *reinterpret_cast<u32x2*>(&ops.pm[rec_elem<C>(32 + m, 32 + 8 * g + 4)]) = u32x2{0u, 0u};
+}
+
+// Factored path (every 16-row block decays by <= kMaxBlockDecay on every
+// channel, always so with a lower bound >= -5): with rho_I = gam just before
+// block I, e^{gam_t - gam_s} = R_t F_s c_IJ with R_t = e^{gam_t - rho_I},
+// F_s = e^{rho_J - gam_s}, c_IJ = e^{rho_I - rho_J} <= 1. One elementwise
+// pass writes K o R, Q o R and K o F tiles, scale Q o e^gam and
+// (K o e^{gam_last - gam})^T; A and P then run on bf16 MFMA from the tiles.
+// Waves 0..3 take the diagonal blocks and invert theirs in (I + A) at once
+// (forward substitution), waves 4..7 the off-diagonal blocks. Leaves A^T
+// (times beta) strictly above the diagonal of at and the diagonal blocks of
+// T below it, scale P in ops.pm, and K o e^gam of the thread's elements in
+// wkp; ends with the workgroup met.
+template <int K, int V, bool Q, bool EXACT>
+__device__ __forceinline__ void intra_factored(const PrefillParams& p, FusedSmem<K, Q, EXACT>& sm,
+                                               const float (&gm)[Roles<K>::PP][4], const float (&gl)[4],
+                                               const float (&rho)[4], uint32_t (&wkp)[4][Roles<K>::PP / 2]) {
+  using Ro = Roles<K>;
+  using XL = XLayout<K>;
+  constexpr int PP = Ro::PP, NQ = Ro::NQ;
+  const int tid = opaque_tid(), lane = tid & 63, w = uniform(tid >> 6);
+  const int m = lane & 15, g = lane >> 4;
+  const int q4 = tid % NQ, part = tid / NQ;
+  const int c4 = 4 * q4;
+  float* x = sm.x;
+  auto& ops = sm.r.ops;
+  float E[4], sE[4], G[4];
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    E[jj] = __expf(rho[jj]);
+    sE[jj] = p.scale * E[jj];
+    G[jj] = __expf(gl[jj] - rho[jj]);
+  }
+  const int r8 = (c4 & 31) >> 2;
+  const int qcol = 32 * (c4 >> 5) + 8 * (r8 & 3) + 4 * (r8 >> 2);  // permuted slot of channel c4
+  uint2 kq[PP], qq[PP];
+#pragma unroll
+  for (int i = 0; i < PP; ++i) {
+    const int o = sw16<K>(part * PP + i, c4);
+    kq[i] = *reinterpret_cast<const uint2*>(&sm.t.f.k[o]);
+    if constexpr (Q) qq[i] = *reinterpret_cast<const uint2*>(&sm.t.f.q[o]);
+  }
+  float wk_even[4] = {0.f, 0.f, 0.f, 0.f};
+  float kgv[4][PP];  // [channel][position]
+#pragma unroll
+  for (int i = 0; i < PP; ++i) {
+    const int t = part * PP + i;
+    const int o = sw16<K>(t, c4);
+    const float kv[4] = {__uint_as_float(kq[i].x << 16), __uint_as_float(kq[i].x & 0xffff0000u),
+                         __uint_as_float(kq[i].y << 16), __uint_as_float(kq[i].y & 0xffff0000u)};
+    float Rt[4], kr[4], kf[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      Rt[jj] = __expf(gm[i][jj] - rho[jj]);
+      const float Ft = __builtin_amdgcn_rcpf(Rt[jj]);  // Rt >= e^-80
+      kr[jj] = kv[jj] * Rt[jj];
+      kf[jj] = kv[jj] * Ft;
+      kgv[jj][i] = kf[jj] * G[jj];
+      if (i & 1) wkp[jj][i >> 1] = pack_bf16x2(wk_even[jj], kr[jj] * E[jj]);
+      else wk_even[jj] = kr[jj] * E[jj];
+    }
+    *reinterpret_cast<uint2*>(&sm.t.f.k[o]) = uint2{pack_bf16x2(kr[0], kr[1]), pack_bf16x2(kr[2], kr[3])};
+    *reinterpret_cast<uint2*>(&sm.t.f.kf[o]) = uint2{pack_bf16x2(kf[0], kf[1]), pack_bf16x2(kf[2], kf[3])};
+    if constexpr (Q) {
+      const float qv[4] = {__uint_as_float(qq[i].x << 16), __uint_as_float(qq[i].x & 0xffff0000u),
+                           __uint_as_float(qq[i].y << 16), __uint_as_float(qq[i].y & 0xffff0000u)};
+      float qr[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) qr[jj] = qv[jj] * Rt[jj];
+      *reinterpret_cast<uint2*>(&sm.t.f.q[o]) = uint2{pack_bf16x2(qr[0], qr[1]), pack_bf16x2(qr[2], qr[3])};
+      *reinterpret_cast<u32x2*>(&ops.qg[rec_elem<K>(t, qcol)]) =
+          u32x2{pack_bf16x2(qr[0] * sE[0], qr[1] * sE[1]), pack_bf16x2(qr[2] * sE[2], qr[3] * sE[3])};
+    }
+  }
+  // (K o e^{gl - gam})^T: the thread's PP positions are PP consecutive slots
+  // of the permuted order (PP <= 4, aligned).
+  {
+    static_assert(PP == 4 || PP == 2, "positions per thread");
+    const int tp = part * PP;
+    const int slot0 = 32 * (tp >> 5) + perm_slot(tp & 31);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      uint16_t* dst = &ops.kgt[rec_elem<C>(c4 + jj, slot0)];
+      if constexpr (PP == 4)
+        *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(kgv[jj][0], kgv[jj][1]), pack_bf16x2(kgv[jj][2], kgv[jj][3])};
+      else
+        *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(kgv[jj][0], kgv[jj][1]);
+    }
+  }
+  lds_barrier();
+  // ---- A and P over all channels ----------------------------------------
+  // Block (I, J): lane (m, g) holds rows 16 I + 4 g + j of column 16 J + m.
+  auto ap_block = [&](int I, int J, f32x4& dA, f32x4& dPt) {
+    dA = f32x4{0.f, 0.f, 0.f, 0.f};
+    dPt = f32x4{0.f, 0.f, 0.f, 0.f};
+    const float* cv = x + XL::cij + (I * (I + 1) / 2 + J) * K;
+#pragma unroll
+    for (int kb = 0; kb < K / 32; ++kb) {
+      const int c0 = 32 * kb + 8 * g;
+      const bf16x8 ak = lds_frag(&sm.t.f.k[sw16<K>(16 * I + m, c0)]);
+      bf16x8 b = lds_frag(&sm.t.f.kf[sw16<K>(16 * J + m, c0)]);
+      if (J < I) {
+        const f32x4 c0v = *reinterpret_cast<const f32x4*>(cv + c0);
+        const f32x4 c1v = *reinterpret_cast<const f32x4*>(cv + c0 + 4);
+        float sc[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) sc[jj] = static_cast<float>(b[jj]) * (jj < 4 ? c0v[jj] : c1v[jj - 4]);
+        b = to_bf16x8(sc);
+      }
+      dA = mfma16(ak, b, dA);
+      if constexpr (Q) {
+        const bf16x8 aq = lds_frag(&sm.t.f.q[sw16<K>(16 * I + m, c0)]);
+        dPt = mfma16(b, aq, dPt);
+      }
+    }
+  };
+  // A^T (times beta) into at, scale P into ops.pm.
+  auto store_block = [&](int I, int J, const f32x4& dA, const f32x4& dPt) {
+    const int s2 = 16 * J + m;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int row = 16 * I + 4 * g + jj;
+      if (s2 < row) sm.at[sw32<C>(s2, row)] = x[XL::beta + row] * dA[jj];
+    }
+    if constexpr (Q) {
+      const int prow = 16 * I + m;
+      float pv[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) pv[jj] = 16 * J + 4 * g + jj <= prow ? p.scale * dPt[jj] : 0.f;
+      *reinterpret_cast<u32x2*>(&ops.pm[rec_elem<C>(prow, 32 * (J >> 1) + 8 * g + 4 * (J & 1))]) =
+          u32x2{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])};
+    }
+  };
+  if (w < 4) {
+    f32x4 dA, dPt;
+    ap_block(w, w, dA, dPt);
+    store_block(w, w, dA, dPt);
+    // The block's A^T entries were written by this wave's own lanes: LDS
+    // operations of one wave complete in order, so no barrier is needed.
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt = 0
+    __builtin_amdgcn_wave_barrier();
+    diag_inverse(sm.at, w, lane);
+  } else {
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi) {
+      int I, J;
+      offdiag_block(w, bi, I, J);
+      if (I >= 0) {  // wave-uniform
+        f32x4 dA, dPt;
+        ap_block(I, J, dA, dPt);
+        store_block(I, J, dA, dPt);
+      }
+    }
+    if constexpr (Q) {
+      if (w == kWaves - 1) zero_p_blocks<K, Q>(ops, m, g);
+    }
+  }
+  lds_barrier();  // A^T and the diagonal blocks of T complete; the tiles are no longer read
+}
+
+// Exact path (some 16-row block decays by more than kMaxBlockDecay): gam in
+// LDS, A and P by 16x16 blocks with a reference row per block: off-diagonal
+// blocks and diagonal blocks with a small decay range on bf16 MFMA (every
+// factor <= 1 or within e^{+-80}), the other diagonal blocks pairwise in
+// fp32. Same outputs as intra_factored (with the same block split).
+template <int K, int V, bool Q, bool EXACT>
+__device__ __forceinline__ void intra_exact(const PrefillParams& p, FusedSmem<K, Q, EXACT>& sm,
+                                            const float (&gm)[Roles<K>::PP][4],
+                                            uint32_t (&wkp)[4][Roles<K>::PP / 2]) {
+  using Ro = Roles<K>;
+  using XL = XLayout<K>;
+  constexpr int PP = Ro::PP, NQ = Ro::NQ, KP8 = Ro::KP8;
+  const int tid = opaque_tid(), lane = tid & 63, w = uniform(tid >> 6);
+  const int m = lane & 15, g = lane >> 4;
+  const int q4 = tid % NQ, part = tid / NQ;
+  const int c4 = 4 * q4;
+  float* x = sm.x;
+  auto& ops = sm.r.ops;
+  float* gam = sm.t.e.gam;
+#pragma unroll
+  for (int i = 0; i < PP; ++i)
+    *reinterpret_cast<f32x4*>(&gam[sw32<K>(part * PP + i, c4)]) = f32x4{gm[i][0], gm[i][1], gm[i][2], gm[i][3]};
+  lds_barrier();
+  // Elementwise outputs: scale Q o e^gam and (K o e^{gl - gam})^T.
+  if constexpr (Q) {
+    for (int e = tid; e < C * KP8; e += kThreads) {
+      const int t = e / KP8, pc = e % KP8;
+      const int cb = (pc >> 2) * 32 + 4 * (pc & 3);  // storage piece pc holds channels cb..cb+3, cb+16..cb+19
+      float qv[8], vals[8];
+      {
+        const uint2 w0 = *reinterpret_cast<const uint2*>(&sm.t.e.q[sw16<K>(t, cb)]);
+        const uint2 w1 = *reinterpret_cast<const uint2*>(&sm.t.e.q[sw16<K>(t, cb + 16)]);
+        qv[0] = __uint_as_float(w0.x << 16); qv[1] = __uint_as_float(w0.x & 0xffff0000u);
+        qv[2] = __uint_as_float(w0.y << 16); qv[3] = __uint_as_float(w0.y & 0xffff0000u);
+        qv[4] = __uint_as_float(w1.x << 16); qv[5] = __uint_as_float(w1.x & 0xffff0000u);
+        qv[6] = __uint_as_float(w1.y << 16); qv[7] = __uint_as_float(w1.y & 0xffff0000u);
+      }
+      const f32x4 g0 = *reinterpret_cast<const f32x4*>(&gam[sw32<K>(t, cb)]);
+      const f32x4 g1 = *reinterpret_cast<const f32x4*>(&gam[sw32<K>(t, cb + 16)]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        vals[j] = p.scale * qv[j] * __expf(g0[j]);
+        vals[4 + j] = p.scale * qv[4 + j] * __expf(g1[j]);
+      }
+      uint4 o;
+      o.x = pack_bf16x2(vals[0], vals[1]); o.y = pack_bf16x2(vals[2], vals[3]);
+      o.z = pack_bf16x2(vals[4], vals[5]); o.w = pack_bf16x2(vals[6], vals[7]);
+      *reinterpret_cast<uint4*>(&ops.qg[rec_elem<K>(t, pc * 8)]) = o;
+    }
+  }
+  for (int e = tid; e < K * (C / 8); e += kThreads) {
+    const int ch = e / (C / 8), pc = e % (C / 8);
+    const int base = (pc >> 2) * 32;
+    const float glast = gam[sw32<K>(C - 1, ch)];
+    float vals[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int t = base + perm_phys((pc & 3) * 8 + j);
+      vals[j] = bf16_to_f32(sm.t.e.k[sw16<K>(t, ch)]) * __expf(glast - gam[sw32<K>(t, ch)]);
+    }
+    uint4 o;
+    o.x = pack_bf16x2(vals[0], vals[1]); o.y = pack_bf16x2(vals[2], vals[3]);
+    o.z = pack_bf16x2(vals[4], vals[5]); o.w = pack_bf16x2(vals[6], vals[7]);
+    *reinterpret_cast<uint4*>(&ops.kgt[rec_elem<C>(ch, pc * 8)]) = o;
+  }
+  // A and P by 16x16 blocks (I, J), J <= I. For block-row I the reference
+  // row r = 16 I + 7 when the block decays by at most 80 on every channel:
+  // then every factor fits bf16 and every product with s <= t equals
+  // e^{gam_t - gam_s} <= 1. Otherwise reference 16 I for J < I (both
+  // factors <= 1) and pairwise fp32 exponentials on the diagonal block.
+  // A goes transposed into at (strictly above the diagonal); P into ops.pm
+  // (positions permuted), including the zero blocks above the diagonal that
+  // the state step reads.
+  auto do_block = [&](int I, int J) {
+    const bool fast = x[XL::drange + I] <= kMaxBlockDecay;  // uniform
+    if (J < I || fast) {
+      const int r = fast ? 16 * I + 7 : 16 * I;
+      f32x4 dA = {0.f, 0.f, 0.f, 0.f}, dP = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < K / 32; ++kb) {
+        const int c0 = 32 * kb + 8 * g;
+        const uint4 ka = *reinterpret_cast<const uint4*>(&sm.t.e.k[sw16<K>(16 * I + m, c0)]);
+        const uint4 kbv = *reinterpret_cast<const uint4*>(&sm.t.e.k[sw16<K>(16 * J + m, c0)]);
+        const f32x4 gt0 = *reinterpret_cast<const f32x4*>(&gam[sw32<K>(16 * I + m, c0)]);
+        const f32x4 gt1 = *reinterpret_cast<const f32x4*>(&gam[sw32<K>(16 * I + m, c0 + 4)]);
+        const f32x4 gr0 = *reinterpret_cast<const f32x4*>(&gam[sw32<K>(r, c0)]);
+        const f32x4 gr1 = *reinterpret_cast<const f32x4*>(&gam[sw32<K>(r, c0 + 4)]);
+        const f32x4 gs0 = *reinterpret_cast<const f32x4*>(&gam[sw32<K>(16 * J + m, c0)]);
+        const f32x4 gs1 = *reinterpret_cast<const f32x4*>(&gam[sw32<K>(16 * J + m, c0 + 4)]);
+        const uint32_t kaw[4] = {ka.x, ka.y, ka.z, ka.w};
+        const uint32_t kbw[4] = {kbv.x, kbv.y, kbv.z, kbv.w};
+        uint32_t qaw[4] = {0u, 0u, 0u, 0u};
+        if constexpr (Q) {
+          const uint4 qav = *reinterpret_cast<const uint4*>(&sm.t.e.q[sw16<K>(16 * I + m, c0)]);
+          qaw[0] = qav.x; qaw[1] = qav.y; qaw[2] = qav.z; qaw[3] = qav.w;
+        }
+        float ak[8], aq[8], bk[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float gt = j < 4 ? gt0[j] : gt1[j - 4];
+          const float gr = j < 4 ? gr0[j] : gr1[j - 4];
+          const float gs = j < 4 ? gs0[j] : gs1[j - 4];
+          const float kav = __uint_as_float(j & 1 ? (kaw[j >> 1] & 0xffff0000u) : (kaw[j >> 1] << 16));
+          const float kbf = __uint_as_float(j & 1 ? (kbw[j >> 1] & 0xffff0000u) : (kbw[j >> 1] << 16));
+          const float ea = __expf(gt - gr);
+          ak[j] = kav * ea;
+          aq[j] = __uint_as_float(j & 1 ? (qaw[j >> 1] & 0xffff0000u) : (qaw[j >> 1] << 16)) * ea;
+          bk[j] = kbf * __expf(gr - gs);
+        }
+        const bf16x8 b = to_bf16x8(bk);
+        dA = mfma16(to_bf16x8(ak), b, dA);
+        if constexpr (Q) dP = mfma16(to_bf16x8(aq), b, dP);
+      }
+      // Lane holds rows 16 I + 4 g + j of column s = 16 J + m. Entries above
+      // the diagonal are dropped (they may be huge or non-finite).
+      const int s2 = 16 * J + m;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = 16 * I + 4 * g + j;
+        if (s2 < row) sm.at[sw32<C>(s2, row)] = x[XL::beta + row] * dA[j];
+        if constexpr (Q)
+          ops.pm[rec_elem<C>(row, 32 * (s2 >> 5) + perm_slot(s2 & 31))] = bf16_bits(s2 <= row ? p.scale * dP[j] : 0.f);
+      }
+    } else {
+      // Diagonal block pairwise: lane (t, cq) = (m, g) covers row t and a
+      // quarter of the channels; partial sums are reduced over quarters.
+      constexpr int CQ = K / 4;
+      const int t = m, cq = g, row = 16 * I + t;
+      float ares[16], pres[16];
+#pragma unroll
+      for (int s3 = 0; s3 < 16; ++s3) {
+        ares[s3] = 0.f;
+        pres[s3] = 0.f;
+      }
+      for (int i8 = 0; i8 < CQ; i8 += 8) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int ch = cq * CQ + i8 + i;
+          const float gt = gam[sw32<K>(row, ch)];
+          const float kt = bf16_to_f32(sm.t.e.k[sw16<K>(row, ch)]);
+          float qti = 0.f;
+          if constexpr (Q) qti = bf16_to_f32(sm.t.e.q[sw16<K>(row, ch)]);
+#pragma unroll
+          for (int s3 = 0; s3 < 16; ++s3) {
+            const int srow = 16 * I + s3;
+            // gam is non-increasing, so for s <= t the exponent is <= 0;
+            // the min only keeps the masked s > t entries finite.
+            const float ke = bf16_to_f32(sm.t.e.k[sw16<K>(srow, ch)]) *
+                             __expf(fminf(gt - gam[sw32<K>(srow, ch)], 0.f));
+            ares[s3] = fmaf(kt, ke, ares[s3]);
+            if constexpr (Q) pres[s3] = fmaf(qti, ke, pres[s3]);
+          }
+        }
+      }
+#pragma unroll
+      for (int s3 = 0; s3 < 16; ++s3) {
+        ares[s3] += __shfl_xor(ares[s3], 16);
+        ares[s3] += __shfl_xor(ares[s3], 32);
+        if constexpr (Q) {
+          pres[s3] += __shfl_xor(pres[s3], 16);
+          pres[s3] += __shfl_xor(pres[s3], 32);
+        }
+      }
+      if (cq == 0) {
+        const float bt = x[XL::beta + row];
+#pragma unroll
+        for (int s3 = 0; s3 < 16; ++s3) {
+          const int col = 16 * I + s3;
+          if (s3 < t) sm.at[sw32<C>(col, row)] = bt * ares[s3];
+          if constexpr (Q)
+            ops.pm[rec_elem<C>(row, 32 * (col >> 5) + perm_slot(col & 31))] = bf16_bits(s3 <= t ? p.scale * pres[s3] : 0.f);
+        }
+      }
+    }
+  };
+  if (w < 4) {
+    do_block(w, w);
+    // The block's A^T entries were written by this wave's own lanes: LDS
+    // operations of one wave complete in order, so no barrier is needed.
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt = 0
+    __builtin_amdgcn_wave_barrier();
+    diag_inverse(sm.at, w, lane);
+  } else {
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi) {
+      int I, J;
+      offdiag_block(w, bi, I, J);
+      if (I >= 0) do_block(I, J);  // wave-uniform
+    }
+    if constexpr (Q) {
+      if (w == kWaves - 1) zero_p_blocks<K, Q>(ops, m, g);
+    }
+  }
+  // K o e^gam of this thread's channels and positions, from the tiles.
+  float wk_even[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < PP; ++i) {
+    const int t = part * PP + i;
+    const uint2 kv = *reinterpret_cast<const uint2*>(&sm.t.e.k[sw16<K>(t, c4)]);
+    const f32x4 gv = *reinterpret_cast<const f32x4*>(&gam[sw32<K>(t, c4)]);
+    const float kf[4] = {__uint_as_float(kv.x << 16), __uint_as_float(kv.x & 0xffff0000u),
+                         __uint_as_float(kv.y << 16), __uint_as_float(kv.y & 0xffff0000u)};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float val = kf[j] * __expf(gv[j]);
+      if (i & 1) wkp[j][i >> 1] = pack_bf16x2(wk_even[j], val);
+      else wk_even[j] = val;
+    }
+  }
+  lds_barrier();  // A^T complete; the tiles and gam are no longer read
+}
+
+// The rest of T = (I + A)^{-1} in at (its diagonal blocks are there
+// already), then W = T diag(beta)(K o e^gam) (as -W into ops.wn) and
+// U = T diag(beta) V (into registers of waves w < V / 16: lane (m, g) holds
+// rows 16 pb + 4 g + j of value columns 16 w + m in U[pb]). Starts with
+// K o e^gam of the thread's elements in wkp (written here to the wkt tile)
+// and the v operands in `in`; ends with the workgroup met.
+template <int K, int V, bool Q, bool EXACT>
+__device__ __forceinline__ void intra_inverse_wu(FusedSmem<K, Q, EXACT>& sm,
+                                                 const uint32_t (&wkp)[4][Roles<K>::PP / 2],
+                                                 const ChunkIn<K, V>& in, f32x4 (&U)[4]) {
+  using Ro = Roles<K>;
+  using XL = XLayout<K>;
+  constexpr int PP = Ro::PP, NQ = Ro::NQ;
+  const int tid = opaque_tid(), lane = tid & 63, w = uniform(tid >> 6);
+  const int m = lane & 15, g = lane >> 4;
+  const int q4 = tid % NQ, part = tid / NQ;
+  const int c4 = 4 * q4;
+  float* at = sm.at;
+  const float* beta_l = sm.x + XL::beta;
+  uint16_t* wkt = sm.wkt();
+  // (K o e^gam)^T into its tile: PP positions of a channel are 2 PP
+  // contiguous bytes.
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if constexpr (PP == 4)
+      *reinterpret_cast<uint2*>(wkt + rec_elem<C>(c4 + j, part * PP)) = uint2{wkp[j][0], wkp[j][1]};
+    else
+      *reinterpret_cast<uint32_t*>(wkt + rec_elem<C>(c4 + j, part * PP)) = wkp[j][0];
+  }
+
+  // ---- off-diagonal blocks of T on fp32 MFMA, in one phase ----------------
+  // For J < I, T_IJ = -T_II sum_{J <= L < I} A_IL T_LJ. Wave w < 6 computes
+  // block (I, J) = (1,0), (2,1), (3,2), (2,0), (3,1), (3,0) and, in its
+  // registers, the lower-order blocks that one needs (every wave forms them
+  // with the same operations, so the copies agree). The 16x16x4 product
+  // pairs lane group g of step kk with contraction index 4 g + kk, so an
+  // accumulator tile (rows 4 g + j) is the B operand of the next product as
+  // it stands: step kk takes its element j = kk.
+  if (w < 6) {
+    auto Tget = [&](int r, int cc) { return r > cc ? at[sw32<C>(r, cc)] : (r == cc ? 1.f : 0.f); };  // diagonal blocks
+    auto Aget = [&](int t, int s2) { return s2 < t ? at[sw32<C>(s2, t)] : 0.f; };                     // A[t][s]
+    // Every operand of the wave's chain is read first (only the MFMAs are
+    // then dependent): A-operand values of block (I, L) of A or of a
+    // diagonal block of T (negated ones carry the minus signs of the
+    // recurrence), and B-operand values of the diagonal blocks T_LL.
+    auto a_op = [&](bool of_a, int I, int L, bool negate, float (&a)[4]) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const float v = of_a ? Aget(16 * I + m, 16 * L + 4 * g + kk) : Tget(16 * I + m, 16 * L + 4 * g + kk);
+        a[kk] = negate ? -v : v;
+      }
+    };
+    auto b_tdiag = [&](int L, float (&b)[4]) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) b[kk] = Tget(16 * L + 4 * g + kk, 16 * L + m);
+    };
+    auto mm = [&](const float (&a)[4], const float (&b)[4], f32x4 acc) {  // both from registers
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) acc = mfma4(a[kk], b[kk], acc);
+      return acc;
+    };
+    auto mm_acc = [&](const float (&a)[4], const f32x4& y, f32x4 acc) {   // B operand an accumulator tile
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) acc = mfma4(a[kk], y[kk], acc);
+      return acc;
+    };
+    const f32x4 z0 = {0.f, 0.f, 0.f, 0.f};
+    int I, J;
+    f32x4 t;
+    if (w < 3) {  // the first sub-diagonal: T_{J+1,J} = -T_{J+1,J+1} A_{J+1,J} T_JJ
+      J = w;
+      I = w + 1;
+      float aIJ[4], bJJ[4], nTII[4];
+      a_op(true, I, J, false, aIJ);
+      b_tdiag(J, bJJ);
+      a_op(false, I, I, true, nTII);
+      t = mm_acc(nTII, mm(aIJ, bJJ, z0), z0);
+    } else if (w < 5) {  // T_20 (w = 3) and T_31 (w = 4), through T_{J+1,J}
+      J = w - 3;
+      I = J + 2;
+      float a10[4], bJJ[4], nT11[4], a20[4], a21[4], nT22[4];
+      a_op(true, J + 1, J, false, a10);
+      b_tdiag(J, bJJ);
+      a_op(false, J + 1, J + 1, true, nT11);
+      a_op(true, I, J, false, a20);
+      a_op(true, I, J + 1, false, a21);
+      a_op(false, I, I, true, nT22);
+      const f32x4 t_mid = mm_acc(nT11, mm(a10, bJJ, z0), z0);  // T_{J+1,J}
+      t = mm_acc(nT22, mm_acc(a21, t_mid, mm(a20, bJJ, z0)), z0);
+    } else {  // T_30, through T_10 and T_20
+      I = 3;
+      J = 0;
+      float a10[4], b00[4], nT11[4], a20[4], a21[4], nT22[4], a30[4], a31[4], a32[4], nT33[4];
+      a_op(true, 1, 0, false, a10);
+      b_tdiag(0, b00);
+      a_op(false, 1, 1, true, nT11);
+      a_op(true, 2, 0, false, a20);
+      a_op(true, 2, 1, false, a21);
+      a_op(false, 2, 2, true, nT22);
+      a_op(true, 3, 0, false, a30);
+      a_op(true, 3, 1, false, a31);
+      a_op(true, 3, 2, false, a32);
+      a_op(false, 3, 3, true, nT33);
+      const f32x4 p20 = mm(a20, b00, z0), p30 = mm(a30, b00, z0);  // independent of the chain
+      const f32x4 t10 = mm_acc(nT11, mm(a10, b00, z0), z0);
+      const f32x4 t20 = mm_acc(nT22, mm_acc(a21, t10, p20), z0);
+      t = mm_acc(nT33, mm_acc(a32, t20, mm_acc(a31, t10, p30)), z0);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) at[sw32<C>(16 * I + 4 * g + j, 16 * J + m)] = t[j];
   }
   lds_barrier();
 
-  // ---- 6. off-diagonal blocks of T on fp32 MFMA ---------------------------
-  // With the 32-row halves t (blocks 0, 1) and b (blocks 2, 3):
-  //   T_10 = -T_11 A_10 T_00,  T_32 = -T_33 A_32 T_22,  T_bt = -T_bb (A_bt T_tt).
-  // The 16x16x4 product pairs lane group g of step kk with contraction index
-  // 4 g + kk, so an accumulator tile (rows 4 g + j) is the B operand of the
-  // next product as it stands: step kk takes its element j = kk.
-  {
-    auto Tget = [&](int r, int cc) { return r > cc ? at[sw32<C>(r, cc)] : (r == cc ? 1.f : 0.f); };
-    auto Aget = [&](int t, int s) { return s < t ? at[sw32<C>(s, t)] : 0.f; };  // A[t][s]
-    // Operands are read into registers before their products (no LDS
-    // writes intervene), so the reads overlap.
-    if (w < 2) {
-      const int I = 1 + 2 * w, J = 2 * w;
-      float a[4], b[4], t[4];
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        a[kk] = Aget(16 * I + m, 16 * J + 4 * g + kk);
-        b[kk] = Tget(16 * J + 4 * g + kk, 16 * J + m);
-        t[kk] = Tget(16 * I + m, 16 * I + 4 * g + kk);
-      }
-      f32x4 z = {0.f, 0.f, 0.f, 0.f}, tij = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) z = mfma4(a[kk], b[kk], z);
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) tij = mfma4(t[kk], z[kk], tij);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) at[sw32<C>(16 * I + 4 * g + j, 16 * J + m)] = -tij[j];
-    }
-    lds_barrier();
-    {
-      const int I = 2 + (w >> 1), J = w & 1;
-      float a2[2][4], a3[2][4], b[2][4], t2[4], t3[4];
-#pragma unroll
-      for (int M = 0; M < 2; ++M)
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          b[M][kk] = Tget(16 * M + 4 * g + kk, 16 * J + m);  // zero for M < J
-          a2[M][kk] = Aget(32 + m, 16 * M + 4 * g + kk);
-          a3[M][kk] = Aget(48 + m, 16 * M + 4 * g + kk);
-        }
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        t2[kk] = Tget(16 * I + m, 32 + 4 * g + kk);
-        t3[kk] = Tget(48 + m, 48 + 4 * g + kk);
-      }
-      f32x4 y2 = {0.f, 0.f, 0.f, 0.f}, y3 = {0.f, 0.f, 0.f, 0.f}, tij = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int M = 0; M < 2; ++M)
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          y2 = mfma4(a2[M][kk], b[M][kk], y2);
-          y3 = mfma4(a3[M][kk], b[M][kk], y3);
-        }
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) tij = mfma4(t2[kk], y2[kk], tij);
-      if (I == 3) {
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) tij = mfma4(t3[kk], y3[kk], tij);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) at[sw32<C>(16 * I + 4 * g + j, 16 * J + m)] = -tij[j];
-    }
-    lds_barrier();
-  }
-
-  // ---- 7. W = T diag(beta)(K o e^gam), U = T diag(beta) V on MFMA -------
+  // ---- W = T diag(beta)(K o e^gam), U = T diag(beta) V on MFMA -----------
   // beta is folded into the fp32 columns of T before the bf16 cast, so V
   // enters the product exactly as given. T is lower triangular, so rows
-  // 0..31 need only positions 0..31.
-  {
-    // T diag(beta) as bf16 fragments: row 16 pb + m, positions 32 kb + 8 g
-    // .. +7, read as two 16-byte pieces of at (T strictly below the
-    // diagonal; the diagonal and above are masked by index).
+  // 0..31 need only positions 0..31. Wave w takes channel block w of W and
+  // value block w of U.
+  const bool does_w = w < K / 16, does_u = w < V / 16;  // wave-uniform
+  if (does_w || does_u) {
     bf16x8 Tf[4][2];
 #pragma unroll
     for (int pb = 0; pb < 4; ++pb)
@@ -565,972 +1205,161 @@ __device__ __forceinline__ void intra_inverse_wu(const PrefillParams& p, float* 
     // -W^T = -(K o e^gam)^T (T diag(beta))^T: the same fragments with the
     // operands swapped leave lane (m, g) four consecutive channels
     // 16 nb + 4 g .. +3 of position 16 pb + m, which are four consecutive
-    // slots of the record's permuted channel order: one 8-byte store each.
-    {
-      const __amdgpu_buffer_rsrc_t rwn = make_rsrc(rec + R::Wn, static_cast<uint32_t>(C * K * 2));
-      typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-      for (int nb = w; nb < K / 16; nb += 4) {
-        bf16x8 Bf[2];
+    // slots of the permuted channel order: one 8-byte store each.
+    if (does_w) {
+      const int nb = w;
+      bf16x8 Bf[2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) Bf[kb] = frag<C>(wkt, 16 * nb + m, 32 * kb + 8 * g);
-        const int col = 32 * (nb >> 1) + 8 * g + 4 * (nb & 1);
+      for (int kb = 0; kb < 2; ++kb) Bf[kb] = frag<C>(wkt, 16 * nb + m, 32 * kb + 8 * g);
+      const int col = 32 * (nb >> 1) + 8 * g + 4 * (nb & 1);
 #pragma unroll
-        for (int pb = 0; pb < 4; ++pb) {
-          f32x4 D = mfma16(Bf[0], Tf[pb][0], f32x4{0.f, 0.f, 0.f, 0.f});
-          if (pb >= 2) D = mfma16(Bf[1], Tf[pb][1], D);
-          const u32x2 v = {pack_bf16x2(-D[0], -D[1]), pack_bf16x2(-D[2], -D[3])};
-          __builtin_amdgcn_raw_buffer_store_b64(v, rwn, rec_elem<K>(16 * pb + m, col) * 2, 0, 0);
-        }
+      for (int pb = 0; pb < 4; ++pb) {
+        f32x4 D = mfma16(Bf[0], Tf[pb][0], f32x4{0.f, 0.f, 0.f, 0.f});
+        if (pb >= 2) D = mfma16(Bf[1], Tf[pb][1], D);
+        *reinterpret_cast<u32x2*>(&sm.r.ops.wn[rec_elem<K>(16 * pb + m, col)]) =
+            u32x2{pack_bf16x2(-D[0], -D[1]), pack_bf16x2(-D[2], -D[3])};
       }
     }
-    // U written straight out in accumulator fragment order.
-    f32x4* uf = reinterpret_cast<f32x4*>(rec + R::Uf);
-#pragma unroll
-    for (int u = 0; u < NBU; ++u) {
-      const int nb = w + 4 * u;
-      if (nb >= V / 16) break;
+    if (does_u) {
       bf16x8 Bv[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) Bv[kb][j] = __builtin_bit_cast(__bf16, vpre[u][kb][j]);
+        for (int j = 0; j < 8; ++j) Bv[kb][j] = __builtin_bit_cast(__bf16, in.vpre[kb][j]);
 #pragma unroll
       for (int pb = 0; pb < 4; ++pb) {
         f32x4 D = mfma16(Tf[pb][0], Bv[0], f32x4{0.f, 0.f, 0.f, 0.f});
         if (pb >= 2) D = mfma16(Tf[pb][1], Bv[1], D);
-        uf[(pb * (V / 16) + nb) * 64 + lane] = D;
+        U[pb] = D;
       }
     }
   }
+  lds_barrier();  // -W complete; at and wkt no longer read
 }
 
-// One workgroup of the exact intra kernel, launched after the factored one
-// on the same grid: it takes only the chunks the factored kernel flagged
-// (some 16-row block decays by more than kMaxBlockDecay), with gam in LDS
-// and pairwise exponentials on the diagonal blocks. Separate kernels keep
-// the factored path's registers and LDS free of the exact path's.
-template <int K, int V>
-__device__ __forceinline__ void intra_exact(const PrefillParams& p, const int4* chunk_info,
-                                            char* recs, uint8_t* exact_flags) {
-  using R = Rec<K, V>;
-  using SM = IntraSmem<K, V>;
-  using XL = XLayout<K>;
-  __shared__ SM sm;
-
-  const int H = p.H;
-  // Chunks are taken last to first: the state pass reads them first to
-  // last, so its early chunks are the most recently written (still in the
-  // memory-side cache when the records outgrow it). The plan gives row j
-  // its chunk slot, first token and token count in one load (zero tokens
-  // past the last chunk, or for cu_seqlens outside the contract).
-  const int j = static_cast<int>(blockIdx.x / H);
-  const int h = static_cast<int>(blockIdx.x % H);
-  const int4 info = chunk_info[j];
-  const int n = uniform(info.z);
-  if (n <= 0) return;  // uniform
-  const int c = uniform(info.x);
-  const int64_t t0 = uniform(info.y);
-  uint8_t* flag = exact_flags + static_cast<int64_t>(c) * H + h;
-  if (*flag == 0) return;  // uniform: the factored kernel took this chunk
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = uniform(tid >> 6);  // wave index, in a scalar register
-  const int m = lane & 15;
-  const int g = lane >> 4;
-  constexpr int KP8 = K / 8;                     // 16-byte pieces per bf16 row
-  constexpr int KPM = (KP8 > 16 ? 16 : KP8) - 1;
-
-  char* rec = recs + rec_index(h, c, p) * static_cast<int64_t>(R::bytes);
-  float* x = sm.u.f.x;
-  uint16_t* wkt = reinterpret_cast<uint16_t*>(sm.u.f.x);
-
-  // ---- 1. raw_g into registers, k and q tiles by LDS DMA -----------------
-  // Rows past the chunk end read 0. The thread's raw_g arrives in its own
-  // registers, so the gate scan waits only for those loads while the k and
-  // q copies keep landing under it.
-  // Thread (q4, part) owns channels 4 q4 .. 4 q4 + 3 at positions
-  // part PP .. part PP + PP - 1: its tile reads and writes are 8 bytes wide,
-  // and wave w holds exactly the 16-row block w.
-  constexpr int NQ = K / 4;              // channel quads
-  constexpr int NPART = XL::PARTS;       // 8 at K = 128, 16 at K = 64
-  constexpr int PP = C / NPART;          // positions per thread: 8 or 4
-  static_assert(NPART * PP == C && (64 / NQ) * PP == 16 && PP % 4 == 0, "a wave holds one 16-row block");
-  const int q4 = tid % NQ, part = tid / NQ;
-  const int c4 = 4 * q4;                 // the thread's first channel
-  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-  u32x2 rgw[PP];
-  float a_h, dtb[4];
-  uint16_t rb_bits = 0;
-  {
-    const int64_t rs = p.qkv_row_stride * 2;  // bytes per mixed_qkv row
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.qkv + t0 * p.qkv_row_stride, static_cast<uint32_t>(n * rs));
-    const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.raw_g + t0 * (H * K), static_cast<uint32_t>(n * H * K * 2));
-#pragma unroll
-    for (int i = 0; i < PP; ++i)
-      rgw[i] = __builtin_amdgcn_raw_buffer_load_b64(rg, ((part * PP + i) * H * K + h * K + c4) * 2, 0, 0);
-    // Per-head gate parameters and beta.
-    a_h = __expf(p.A_log[h]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) dtb[j] = p.dt_bias[h * K + c4 + j];
-    // beta of position tid (rows past the chunk end read 0; only tid < n is used).
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.raw_beta + t0 * H, static_cast<uint32_t>(n * H * 2));
-    rb_bits = __builtin_amdgcn_raw_buffer_load_b16(rb, (tid * H + h) * 2, 0, 0);
-    // Keep these loads ahead of the copies: loads complete in issue order,
-    // so anything issued after the copies would wait for them.
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int r = 0; r < C * KP8 / kThreads; ++r) {
-      const int ps = r * kThreads + tid;          // physical piece in the tile
-      const int t = ps / KP8;
-      const int pl = (ps % KP8) ^ (t & KPM);      // logical piece stored there
-      const int slot = r * kThreads + (tid & ~63);
-      const int qoff = static_cast<int>(t * rs) + (h * K + pl * 8) * 2;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, reinterpret_cast<uint4*>(sm.q) + slot, 16, qoff, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, reinterpret_cast<uint4*>(sm.k) + slot, 16, qoff + H * K * 2, 0, 0, 0);
-    }
+// The whole intra part of one chunk whose inputs have landed (tiles in LDS,
+// the rest in `in`): operand tiles in sm.r.ops, U in registers. With
+// has_next (`next` the following chunk of the same workgroup), its raw_g and
+// beta loads go out as soon as the gate scan has consumed this chunk's, and
+// (without the exact path) its keys and queries as soon as A/P is done. Ends
+// with the workgroup met and the tile area free.
+template <int K, int V, bool Q, bool EXACT>
+__device__ __forceinline__ void intra_part(const PrefillParams& p, int h, int n, ChunkIn<K, V>& in,
+                                           bool has_next, ChunkPos next, FusedSmem<K, Q, EXACT>& sm,
+                                           f32x4 (&U)[4]) {
+  using Ro = Roles<K>;
+  float gm[Ro::PP][4], gl[4], rho[4];
+  const bool fast = gate_scan<K, V, Q, EXACT>(p, h, n, in, sm, gm, gl, rho);
+  if (has_next) load_chunk_gate_regs<K, V>(p, h, next, in);
+  uint32_t wkp[4][Ro::PP / 2];
+  if (fast) intra_factored<K, V, Q, EXACT>(p, sm, gm, gl, rho, wkp);  // uniform
+  else if constexpr (EXACT) intra_exact<K, V, Q, EXACT>(p, sm, gm, wkp);
+  // The tile area is free from here on (EXACT: after W, see the caller).
+  if constexpr (!EXACT) {
+    if (has_next) dma_chunk_tiles<K, Q>(p, h, next, sm.t.f.k, sm.t.f.q);
   }
-
-  // ---- 2. gate and cumulative log-decay, in registers ---------------------
-  const float beta_t = (tid < n) ? sigmoid_f32(bf16_to_f32(rb_bits)) : 0.f;
-  // Each thread scans its PP positions; partial totals are added across
-  // parts through x.
-  float gm[PP][4];
-  float gl[4] = {0.f, 0.f, 0.f, 0.f};
-  {
-    const float a = a_h;
-    const bool has_lb = p.has_lb != 0;
-    // All reads first (rows past the chunk end hold zeros), then a
-    // branch-free scan; padded positions do not decay, so row 63 holds
-    // gam_last.
-    float rg[PP][4];
-#pragma unroll
-    for (int i = 0; i < PP; ++i) {
-      rg[i][0] = __uint_as_float(rgw[i][0] << 16);
-      rg[i][1] = __uint_as_float(rgw[i][0] & 0xffff0000u);
-      rg[i][2] = __uint_as_float(rgw[i][1] << 16);
-      rg[i][3] = __uint_as_float(rgw[i][1] & 0xffff0000u);
-    }
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    if (has_lb) {
-#pragma unroll
-      for (int i = 0; i < PP; ++i) {
-        const bool live = part * PP + i < n;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float gv = p.lower_bound * sigmoid_f32(a * (rg[i][j] + dtb[j]));
-          acc[j] += live ? gv : 0.f;
-          gm[i][j] = acc[j];
-        }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < PP; ++i) {
-        const bool live = part * PP + i < n;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float gv = -a * softplus_f32(rg[i][j] + dtb[j]);
-          acc[j] += live ? gv : 0.f;
-          gm[i][j] = acc[j];
-        }
-      }
-    }
-    *reinterpret_cast<f32x4*>(&x[XL::tot + part * K + c4]) = f32x4{acc[0], acc[1], acc[2], acc[3]};
-    lds_barrier();  // partial totals visible
-    float before[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int q2 = 0; q2 < NPART; ++q2) {
-      const f32x4 tq = *reinterpret_cast<const f32x4*>(&x[XL::tot + q2 * K + c4]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (q2 < part) before[j] += tq[j];
-        gl[j] += tq[j];
-      }
-    }
-    if (tid < C) sm.at[sw32<C>(tid, tid)] = beta_t;  // beta on the diagonal of at
-#pragma unroll
-    for (int i = 0; i < PP; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) gm[i][j] += before[j];
-    // Block w's bound gam(16 w) is row 0 of the wave's first part (lanes
-    // 0 .. NQ-1); its row 15 is the last row of the wave's last part, in
-    // lane + 64 - NQ. The decay range is gam(16 w) - gam(16 w + 15).
-    float d = 0.f;
-    {
-      float last[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) last[j] = __shfl_xor(gm[PP - 1][j], 64 - NQ);
-      if (lane < NQ) {
-        *reinterpret_cast<f32x4*>(&x[XL::bnd + w * K + c4]) = f32x4{gm[0][0], gm[0][1], gm[0][2], gm[0][3]};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) d = fmaxf(d, gm[0][j] - last[j]);
-      }
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) d = fmaxf(d, __shfl_xor(d, off));
-    if (lane == 0) x[XL::dmax + w] = d;
-    if (part == 0)
-      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(rec + R::Eg) + c4) =
-          f32x4{__expf(gl[0]), __expf(gl[1]), __expf(gl[2]), __expf(gl[3])};
-  }
-  wait_vmem();  // this thread's k and q copies (and every load before them) have landed
-  lds_barrier();
-  bool fast = true;
-#pragma unroll
-  for (int I = 0; I < 4; ++I) fast = fast && x[XL::dmax + I] <= kMaxBlockDecay;
-
-  // K o e^gam of this thread's channels and positions, as bf16 pairs, kept
-  // in registers until x is free.
-  uint32_t wkp[4][PP / 2];
-
-  {
-    // ---- 3e/4e. exact path (a block decays by more than the bound) --------
-    (void)fast;
-    lds_barrier();  // every thread has read the decay ranges (gam overlays x)
-#pragma unroll
-    for (int i = 0; i < PP; ++i)
-      *reinterpret_cast<f32x4*>(&sm.u.gam[sw32<K>(part * PP + i, c4)]) = f32x4{gm[i][0], gm[i][1], gm[i][2], gm[i][3]};
-    lds_barrier();
-    // Exact path, elementwise outputs: Q o e^gam and (K o e^{gl-gam})^T.
-    {
-      uint16_t* qg = reinterpret_cast<uint16_t*>(rec + R::Qg);
-      for (int e = tid; e < C * KP8; e += kThreads) {
-        const int t = e / KP8, pc = e % KP8;
-        const int cb = (pc >> 2) * 32 + 4 * (pc & 3);  // storage piece pc holds channels cb..cb+3, cb+16..cb+19
-        float qv[8], vals[8];
-        {
-          const uint2 w0 = *reinterpret_cast<const uint2*>(&sm.q[sw16<K>(t, cb)]);
-          const uint2 w1 = *reinterpret_cast<const uint2*>(&sm.q[sw16<K>(t, cb + 16)]);
-          qv[0] = __uint_as_float(w0.x << 16); qv[1] = __uint_as_float(w0.x & 0xffff0000u);
-          qv[2] = __uint_as_float(w0.y << 16); qv[3] = __uint_as_float(w0.y & 0xffff0000u);
-          qv[4] = __uint_as_float(w1.x << 16); qv[5] = __uint_as_float(w1.x & 0xffff0000u);
-          qv[6] = __uint_as_float(w1.y << 16); qv[7] = __uint_as_float(w1.y & 0xffff0000u);
-        }
-        const f32x4 g0 = *reinterpret_cast<const f32x4*>(&sm.u.gam[sw32<K>(t, cb)]);
-        const f32x4 g1 = *reinterpret_cast<const f32x4*>(&sm.u.gam[sw32<K>(t, cb + 16)]);
-  #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          vals[j] = p.scale * qv[j] * __expf(g0[j]);
-          vals[4 + j] = p.scale * qv[4 + j] * __expf(g1[j]);
-        }
-        uint4 o;
-        o.x = pack_bf16x2(vals[0], vals[1]); o.y = pack_bf16x2(vals[2], vals[3]);
-        o.z = pack_bf16x2(vals[4], vals[5]); o.w = pack_bf16x2(vals[6], vals[7]);
-        *reinterpret_cast<uint4*>(qg + rec_elem<K>(t, pc * 8)) = o;
-      }
-      uint16_t* kgt = reinterpret_cast<uint16_t*>(rec + R::KgT);
-      for (int e = tid; e < K * (C / 8); e += kThreads) {
-        const int ch = e / (C / 8), pc = e % (C / 8);
-        const int base = (pc >> 2) * 32;
-        const float gl = sm.u.gam[sw32<K>(C - 1, ch)];
-        float vals[8];
-  #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int t = base + perm_phys((pc & 3) * 8 + j);
-          vals[j] = bf16_to_f32(sm.k[sw16<K>(t, ch)]) * __expf(gl - sm.u.gam[sw32<K>(t, ch)]);
-        }
-        uint4 o;
-        o.x = pack_bf16x2(vals[0], vals[1]); o.y = pack_bf16x2(vals[2], vals[3]);
-        o.z = pack_bf16x2(vals[4], vals[5]); o.w = pack_bf16x2(vals[6], vals[7]);
-        *reinterpret_cast<uint4*>(kgt + rec_elem<C>(ch, pc * 8)) = o;
-      }
-    }
-
-
-    // Exact path, A and P by 16x16 blocks (I, J), J <= I.
-    // Fast path for block-row I: one reference row r = 16 I + 7. For s in an
-    // earlier block e^{gam_r - gam_s} <= 1; inside block I every factor lies
-    // within e^{+-D}, D = the block's largest decay range over channels. If
-    // D <= 80 every factor fits bf16 and every product with s <= t equals
-    // e^{gam_t - gam_s} <= 1, so the whole block-row runs on MFMA. Otherwise
-    // the exact scheme: reference 16 I for J < I (both factors <= 1) and
-    // pairwise fp32 exponentials on the diagonal block.
-    // A goes transposed into at (strictly above the diagonal); P goes straight
-    // to the workspace (bf16, positions permuted), including the zero blocks
-    // above the diagonal that the state kernel reads.
-    {
-      uint16_t* pm = reinterpret_cast<uint16_t*>(rec + R::Pm);
-      const int blocks[4][3][2] = {{{3, 3}, {3, 0}, {0, 0}},
-                                   {{2, 2}, {3, 1}, {1, 0}},
-                                   {{1, 1}, {3, 2}, {-1, -1}},
-                                   {{2, 1}, {2, 0}, {-1, -1}}};
-      for (int bi = 0; bi < 3; ++bi) {
-        const int I = blocks[w][bi][0], J = blocks[w][bi][1];
-        if (I < 0) break;
-        float dloc = 0.f;
-        for (int ch = lane; ch < K; ch += 64)
-          dloc = fmaxf(dloc, sm.u.gam[sw32<K>(16 * I, ch)] - sm.u.gam[sw32<K>(16 * I + 15, ch)]);
-  #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) dloc = fmaxf(dloc, __shfl_xor(dloc, off));
-        const bool fast = dloc <= 80.f;  // wave-uniform after the butterfly
-        if (J < I || fast) {
-          const int r = fast ? 16 * I + 7 : 16 * I;
-          f32x4 dA = {0.f, 0.f, 0.f, 0.f}, dP = {0.f, 0.f, 0.f, 0.f};
-  #pragma unroll
-          for (int kb = 0; kb < K / 32; ++kb) {
-            const int c0 = 32 * kb + 8 * g;
-            const uint4 ka = *reinterpret_cast<const uint4*>(&sm.k[sw16<K>(16 * I + m, c0)]);
-            const uint4 kbv = *reinterpret_cast<const uint4*>(&sm.k[sw16<K>(16 * J + m, c0)]);
-            const uint4 qav = *reinterpret_cast<const uint4*>(&sm.q[sw16<K>(16 * I + m, c0)]);
-            const uint32_t qaw[4] = {qav.x, qav.y, qav.z, qav.w};
-            const f32x4 gt0 = *reinterpret_cast<const f32x4*>(&sm.u.gam[sw32<K>(16 * I + m, c0)]);
-            const f32x4 gt1 = *reinterpret_cast<const f32x4*>(&sm.u.gam[sw32<K>(16 * I + m, c0 + 4)]);
-            const f32x4 gr0 = *reinterpret_cast<const f32x4*>(&sm.u.gam[sw32<K>(r, c0)]);
-            const f32x4 gr1 = *reinterpret_cast<const f32x4*>(&sm.u.gam[sw32<K>(r, c0 + 4)]);
-            const f32x4 gs0 = *reinterpret_cast<const f32x4*>(&sm.u.gam[sw32<K>(16 * J + m, c0)]);
-            const f32x4 gs1 = *reinterpret_cast<const f32x4*>(&sm.u.gam[sw32<K>(16 * J + m, c0 + 4)]);
-            const uint32_t kaw[4] = {ka.x, ka.y, ka.z, ka.w};
-            const uint32_t kbw[4] = {kbv.x, kbv.y, kbv.z, kbv.w};
-            float ak[8], aq[8], bk[8];
-  #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              const float gt = j < 4 ? gt0[j] : gt1[j - 4];
-              const float gr = j < 4 ? gr0[j] : gr1[j - 4];
-              const float gs = j < 4 ? gs0[j] : gs1[j - 4];
-              const float kav = __uint_as_float(j & 1 ? (kaw[j >> 1] & 0xffff0000u) : (kaw[j >> 1] << 16));
-              const float kbf = __uint_as_float(j & 1 ? (kbw[j >> 1] & 0xffff0000u) : (kbw[j >> 1] << 16));
-              const float ea = __expf(gt - gr);
-              ak[j] = kav * ea;
-              aq[j] = __uint_as_float(j & 1 ? (qaw[j >> 1] & 0xffff0000u) : (qaw[j >> 1] << 16)) * ea;
-              bk[j] = kbf * __expf(gr - gs);
-            }
-            const bf16x8 b = to_bf16x8(bk);
-            dA = mfma16(to_bf16x8(ak), b, dA);
-            dP = mfma16(to_bf16x8(aq), b, dP);
-          }
-          // Lane holds rows 16 I + 4 g + j of column s = 16 J + m. Entries
-          // above the diagonal are dropped (they may be huge or non-finite).
-          const int s2 = 16 * J + m;
-  #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int row = 16 * I + 4 * g + j;
-            if (s2 < row) sm.at[sw32<C>(s2, row)] = sm.at[sw32<C>(row, row)] * dA[j];
-            pm[rec_elem<C>(row, 32 * (s2 >> 5) + perm_slot(s2 & 31))] = bf16_bits(s2 <= row ? p.scale * dP[j] : 0.f);
-          }
-        } else {
-          // Diagonal block pairwise: lane (t, cq) = (m, g) covers row t and a
-          // quarter of the channels; partial sums are reduced over quarters.
-          constexpr int CQ = K / 4;
-          const int t = m, cq = g, row = 16 * I + t;
-          float ares[16], pres[16];
-#pragma unroll
-          for (int s3 = 0; s3 < 16; ++s3) {
-            ares[s3] = 0.f;
-            pres[s3] = 0.f;
-          }
-          for (int i8 = 0; i8 < CQ; i8 += 8) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              const int ch = cq * CQ + i8 + i;
-              const float gt = sm.u.gam[sw32<K>(row, ch)];
-              const float kt = bf16_to_f32(sm.k[sw16<K>(row, ch)]);
-              const float qti = bf16_to_f32(sm.q[sw16<K>(row, ch)]);
-#pragma unroll
-              for (int s3 = 0; s3 < 16; ++s3) {
-                const int srow = 16 * I + s3;
-                // gam is non-increasing, so for s <= t the exponent is <= 0;
-                // the min only keeps the masked s > t entries finite.
-                const float ke = bf16_to_f32(sm.k[sw16<K>(srow, ch)]) *
-                                 __expf(fminf(gt - sm.u.gam[sw32<K>(srow, ch)], 0.f));
-                ares[s3] = fmaf(kt, ke, ares[s3]);
-                pres[s3] = fmaf(qti, ke, pres[s3]);
-              }
-            }
-          }
-#pragma unroll
-          for (int s3 = 0; s3 < 16; ++s3) {
-            ares[s3] += __shfl_xor(ares[s3], 16);
-            ares[s3] += __shfl_xor(ares[s3], 32);
-            pres[s3] += __shfl_xor(pres[s3], 16);
-            pres[s3] += __shfl_xor(pres[s3], 32);
-          }
-          if (cq == 0) {
-            const float bt = sm.at[sw32<C>(row, row)];
-#pragma unroll
-            for (int s3 = 0; s3 < 16; ++s3) {
-              const int col = 16 * I + s3;
-              if (s3 < t) sm.at[sw32<C>(col, row)] = bt * ares[s3];
-              pm[rec_elem<C>(row, 32 * (col >> 5) + perm_slot(col & 31))] = bf16_bits(s3 <= t ? p.scale * pres[s3] : 0.f);
-            }
-          }
-        }
-      }
-      if (w == 3) {
-        // Zero P blocks above the diagonal that the state kernel reads:
-        // rows 0..15 x cols 16..31 and rows 32..47 x cols 48..63.
-  #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int row = 4 * g + j;
-          pm[rec_elem<C>(row, perm_slot(16 + m))] = 0;
-          pm[rec_elem<C>(32 + row, 32 + perm_slot(16 + m))] = 0;
-        }
-      }
-    }
-
-    // K o e^gam from the LDS tiles (k is unchanged on this path).
-    float wk_even[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < PP; ++i) {
-      const int t = part * PP + i;
-      const uint2 kv = *reinterpret_cast<const uint2*>(&sm.k[sw16<K>(t, c4)]);
-      const f32x4 gv = *reinterpret_cast<const f32x4*>(&sm.u.gam[sw32<K>(t, c4)]);
-      const float kf[4] = {__uint_as_float(kv.x << 16), __uint_as_float(kv.x & 0xffff0000u),
-                           __uint_as_float(kv.y << 16), __uint_as_float(kv.y & 0xffff0000u)};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float val = kf[j] * __expf(gv[j]);
-        if (i & 1) wkp[j][i >> 1] = pack_bf16x2(wk_even[j], val);
-        else wk_even[j] = val;
-      }
-    }
-  }
-  // v for the U phase, fetched now so its latency hides behind the inverse:
-  // lane (m, g) needs v[t][16 nb + m] for t = 32 kb + 8 g + j, nb = w, w + 4.
-  // 16-bit buffer loads over the chunk's rows: rows past its end read zero,
-  // the lane part of the offset is fixed and the row part is scalar.
-  constexpr int NBU = (V / 16 + 3) / 4;
-  static_assert(V / 16 <= 4 * NBU && V / 16 > 4 * (NBU - 1), "every wave has NBU column blocks");
-  uint16_t vpre[NBU][2][8];
-  {
-    const int rs = static_cast<int>(p.qkv_row_stride * 2);  // bytes per mixed_qkv row
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.qkv + t0 * p.qkv_row_stride, static_cast<uint32_t>(n * rs));
-    const int vlane = (2 * H * K + h * V + m) * 2 + 8 * g * rs;
-#pragma unroll
-    for (int u = 0; u < NBU; ++u)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int nb = w + 4 * u;
-          vpre[u][kb][j] = __builtin_amdgcn_raw_buffer_load_b16(rv, vlane + 32 * nb, (32 * kb + j) * rs, 0);
-        }
-  }
-
-
-  lds_barrier();  // A^T complete; x (or gam) no longer read
-
-  // beta of every position as a plain array in the first bytes of the kf
-  // area (dead from here), for 16-byte reads in the W/U step.
-  float* beta_l = reinterpret_cast<float*>(sm.u.f.kf);
-  if (tid < C) beta_l[tid] = beta_t;
-
-  // ---- 4. (K o e^gam)^T into x: 16-byte pieces of 8 positions -----------
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    if constexpr (PP == 8)
-      *reinterpret_cast<uint4*>(wkt + rec_elem<C>(c4 + j, part * PP)) = uint4{wkp[j][0], wkp[j][1], wkp[j][2], wkp[j][3]};
-    else
-      *reinterpret_cast<uint2*>(wkt + rec_elem<C>(c4 + j, part * PP)) = uint2{wkp[j][0], wkp[j][1]};
-  }
-
-  intra_inverse_wu<K, V>(p, sm.at, wkt, beta_l, vpre, rec, w, lane);
+  intra_inverse_wu<K, V, Q, EXACT>(sm, wkp, in, U);
 }
 
-
-// ------------------------------------------------------ intra, factored --
-//
-// The factored path works through the key channels in halves of 64, so one
-// half's k, q and K o F tiles (24 KiB) are all the tile space it needs: 47
-// KiB of LDS in all, three workgroups per CU. A and P accumulate over the
-// halves in registers; after the last half the tile space holds
-// (K o e^gam)^T for W. Chunks with a block that decays too steeply are
-// flagged for the exact kernel (which recomputes the whole chunk).
-constexpr int kHalf = 64;  // channels per half
-
-template <int K, int V>
-struct IntraHalfSmem {
-  union {
-    struct {
-      uint16_t k[C * kHalf];   // keys, then K o R (sw16<kHalf>)
-      uint16_t q[C * kHalf];   // queries, then Q o R
-      uint16_t kf[C * kHalf];  // K o F
-    } t;
-    uint16_t wkt[K * C];       // (K o e^gam)^T, bf16 [K][C] (swz<C>), after A/P
-  } u;
-  float x[XLayout<kHalf>::end];  // one half's scan totals, bounds, ranges, c_IJ; then beta
-  float at[C * C];               // as in the exact kernel: A^T, T, beta on the diagonal
+// Which chunks a segment runs: from the plan, for segment gs of the call.
+struct SegRange {
+  int seq, seg0, nseg, sg, c0;  // c0: the segment's first chunk within its sequence
+  int nch;
+  int64_t bos, eos;             // the sequence's rows
 };
 
-template <int K, int V>
-__device__ __forceinline__ void intra_factored(const PrefillParams& p, const int4* chunk_info,
-                                               char* recs, uint8_t* exact_flags) {
-  using R = Rec<K, V>;
-  using SM = IntraHalfSmem<K, V>;
-  using XL = XLayout<kHalf>;
-  constexpr int NH = K / kHalf;  // halves
-  __shared__ SM sm;
+__device__ __forceinline__ SegRange segment_range(const PrefillParams& p, const SegPlan& pl, int gs) {
+  SegRange r;
+  r.seq = uniform(pl.seg_seq[gs]);
+  r.seg0 = uniform(pl.seg_start[r.seq]);
+  r.nseg = uniform(pl.seg_start[r.seq + 1]) - r.seg0;
+  r.sg = gs - r.seg0;
+  const int nch_seq = uniform(pl.chunk_start[r.seq + 1]) - uniform(pl.chunk_start[r.seq]);
+  const int seg_len = (nch_seq + r.nseg - 1) / r.nseg;
+  r.c0 = r.sg * seg_len;
+  r.nch = min(nch_seq, r.c0 + seg_len) - r.c0;
+  r.bos = uniform(static_cast<int64_t>(p.cu_seqlens[r.seq]));
+  r.eos = uniform(static_cast<int64_t>(p.cu_seqlens[r.seq + 1]));
+  return r;
+}
 
+__device__ __forceinline__ ChunkPos chunk_pos(const SegRange& r, int cc) {
+  ChunkPos cp;
+  cp.t0 = r.bos + static_cast<int64_t>(C) * (r.c0 + cc);
+  cp.n = static_cast<int>(min<int64_t>(C, r.eos - cp.t0));
+  return cp;
+}
+
+// --------------------------------------------------------------- state --
+
+// With cu_seqlens outside the contract, every output row of the call is set
+// to NaN (no state is touched); the workgroups share the rows.
+__device__ __forceinline__ void poison_output(const PrefillParams& p) {
+  const int64_t total = p.num_tokens * p.H * p.V;  // bf16 elements
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < total; i += stride)
+    p.out[i] = 0x7FC0;  // bf16 quiet NaN
+}
+
+// One workgroup per (segment, head), 8 waves; wave w < V / 16 owns value
+// columns 16 w .. 16 w + 15 of the state, kept in MFMA accumulators for the
+// whole segment.
+template <int K, int V, bool EXACT>
+__global__ __launch_bounds__(kThreads, 1) void chunk_state_kernel(const PrefillParams p, const SegPlan pl) {
+  using SM = FusedSmem<K, true, EXACT>;
+  __shared__ SM sm;
   const int H = p.H;
-  const int j = static_cast<int>(blockIdx.x / H);
-  const int h = static_cast<int>(blockIdx.x % H);
-  const int4 info = chunk_info[j];
-  const int n = uniform(info.z);
-  if (n <= 0) return;  // uniform
-  const int c = uniform(info.x);
-  const int64_t t0 = uniform(info.y);
-  uint8_t* flag = exact_flags + static_cast<int64_t>(c) * H + h;
+  if (uniform(pl.counts[0]) != 0) {
+    poison_output(p);
+    return;
+  }
+  const int gs = static_cast<int>(blockIdx.x) / H, h = static_cast<int>(blockIdx.x) % H;
+  if (gs >= uniform(pl.counts[1])) return;
+  const SegRange sr = segment_range(p, pl, gs);
+  if (sr.nch <= 0) return;
+  const bool last_seg = sr.sg == sr.nseg - 1;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = uniform(tid >> 6);
   const int m = lane & 15;
   const int g = lane >> 4;
-  char* rec = recs + rec_index(h, c, p) * static_cast<int64_t>(R::bytes);
-
-  // Thread (q4, part) owns channels ch0 + 4 q4 .. + 3 of each half at
-  // positions part PP .. part PP + PP - 1; wave w holds the 16-row block w.
-  constexpr int NQ = kHalf / 4;         // 16 channel quads per half
-  constexpr int NPART = XL::PARTS;      // 16 parts
-  constexpr int PP = C / NPART;         // 4 positions per thread
-  static_assert(NPART * PP == C && (64 / NQ) * PP == 16 && PP == 4, "a wave holds one 16-row block");
-  constexpr int KP8 = kHalf / 8;        // 16-byte pieces per tile row
-  const int q4 = tid % NQ, part = tid / NQ;
-  const int c4 = 4 * q4;
-  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-
-  // raw_g of both halves, gate parameters and beta into registers first.
-  const int rs = static_cast<int>(p.qkv_row_stride * 2);  // bytes per mixed_qkv row
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.qkv + t0 * p.qkv_row_stride, static_cast<uint32_t>(n * rs));
-  u32x2 rgw[NH][PP];
-  float dtb[NH][4];
-  {
-    const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.raw_g + t0 * (H * K), static_cast<uint32_t>(n * H * K * 2));
-#pragma unroll
-    for (int hf = 0; hf < NH; ++hf)
-#pragma unroll
-      for (int i = 0; i < PP; ++i)
-        rgw[hf][i] = __builtin_amdgcn_raw_buffer_load_b64(rg, ((part * PP + i) * H * K + h * K + kHalf * hf + c4) * 2, 0, 0);
-#pragma unroll
-    for (int hf = 0; hf < NH; ++hf)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) dtb[hf][jj] = p.dt_bias[h * K + kHalf * hf + c4 + jj];
-  }
-  const float a_h = __expf(p.A_log[h]);
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.raw_beta + t0 * H, static_cast<uint32_t>(n * H * 2));
-  const uint16_t rb_bits = __builtin_amdgcn_raw_buffer_load_b16(rb, (tid * H + h) * 2, 0, 0);
-  auto copy_tiles = [&](int hf) {  // one half's q and k columns by LDS DMA
-#pragma unroll
-    for (int r = 0; r < C * KP8 / kThreads; ++r) {
-      const int ps = r * kThreads + tid;
-      const int t = ps / KP8;
-      const int pl = (ps % KP8) ^ (t & (KP8 - 1));
-      const int slot = r * kThreads + (tid & ~63);
-      const int qoff = t * rs + (h * K + kHalf * hf + pl * 8) * 2;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, reinterpret_cast<uint4*>(sm.u.t.q) + slot, 16, qoff, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, reinterpret_cast<uint4*>(sm.u.t.k) + slot, 16, qoff + H * K * 2, 0, 0, 0);
-    }
-  };
-  __builtin_amdgcn_sched_barrier(0);
-  copy_tiles(0);
-  const float beta_t = (tid < n) ? sigmoid_f32(bf16_to_f32(rb_bits)) : 0.f;
-
-  // The blocks (I, J), J <= I, of A and P each wave computes, with their
-  // accumulators kept over the halves.
-  const int blocks[4][3][2] = {{{3, 3}, {3, 0}, {0, 0}},
-                               {{2, 2}, {3, 1}, {1, 0}},
-                               {{1, 1}, {3, 2}, {-1, -1}},
-                               {{2, 1}, {2, 0}, {-1, -1}}};
-  f32x4 dA[3], dPt[3];
-#pragma unroll
-  for (int bi = 0; bi < 3; ++bi) {
-    dA[bi] = f32x4{0.f, 0.f, 0.f, 0.f};
-    dPt[bi] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  uint32_t wkp[NH][4][PP / 2];  // K o e^gam of the thread's channels, bf16 pairs
-  const __amdgpu_buffer_rsrc_t rqg = make_rsrc(rec + R::Qg, static_cast<uint32_t>(C * K * 2));
-  const __amdgpu_buffer_rsrc_t rkg = make_rsrc(rec + R::KgT, static_cast<uint32_t>(K * C * 2));
-
-#pragma unroll
-  for (int hf = 0; hf < NH; ++hf) {
-    const int ch0 = kHalf * hf;
-    if (hf > 0) {
-      // Every wave is done with the previous half's tiles.
-      lds_barrier();
-      copy_tiles(hf);
-    }
-    // ---- gate and cumulative log-decay of the half, in registers ---------
-    float gm[PP][4];
-    float gl[4] = {0.f, 0.f, 0.f, 0.f};
-    {
-      const bool has_lb = p.has_lb != 0;
-      float acc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int i = 0; i < PP; ++i) {
-        const bool live = part * PP + i < n;
-        const float rg4[4] = {__uint_as_float(rgw[hf][i][0] << 16), __uint_as_float(rgw[hf][i][0] & 0xffff0000u),
-                              __uint_as_float(rgw[hf][i][1] << 16), __uint_as_float(rgw[hf][i][1] & 0xffff0000u)};
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const float gv = gate_log_decay(rg4[jj], dtb[hf][jj], a_h, has_lb, p.lower_bound);
-          acc[jj] += live ? gv : 0.f;
-          gm[i][jj] = acc[jj];
-        }
-      }
-      *reinterpret_cast<f32x4*>(&sm.x[XL::tot + part * kHalf + c4]) = f32x4{acc[0], acc[1], acc[2], acc[3]};
-      lds_barrier();  // partial totals visible
-      float before[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int q2 = 0; q2 < NPART; ++q2) {
-        const f32x4 tq = *reinterpret_cast<const f32x4*>(&sm.x[XL::tot + q2 * kHalf + c4]);
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          if (q2 < part) before[jj] += tq[jj];
-          gl[jj] += tq[jj];
-        }
-      }
-      if (hf == 0 && tid < C) sm.at[sw32<C>(tid, tid)] = beta_t;  // beta on the diagonal of at
-#pragma unroll
-      for (int i = 0; i < PP; ++i)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) gm[i][jj] += before[jj];
-      // Block w's bound gam(16 w) is row 0 of the wave's first part (lanes
-      // 0 .. NQ-1); its row 15 is the last row of the wave's last part.
-      float d = 0.f;
-      {
-        float last[4];
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) last[jj] = __shfl_xor(gm[PP - 1][jj], 64 - NQ);
-        if (lane < NQ) {
-          *reinterpret_cast<f32x4*>(&sm.x[XL::bnd + w * kHalf + c4]) = f32x4{gm[0][0], gm[0][1], gm[0][2], gm[0][3]};
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) d = fmaxf(d, gm[0][jj] - last[jj]);
-        }
-      }
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) d = fmaxf(d, __shfl_xor(d, off));
-      if (lane == 0) sm.x[XL::dmax + w] = d;
-      if (part == 0)
-        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(rec + R::Eg) + ch0 + c4) =
-            f32x4{__expf(gl[0]), __expf(gl[1]), __expf(gl[2]), __expf(gl[3])};
-    }
-    wait_vmem();  // this half's k and q copies (and every load before them) have landed
-    lds_barrier();
-    bool fast = true;
-#pragma unroll
-    for (int I = 0; I < 4; ++I) fast = fast && sm.x[XL::dmax + I] <= kMaxBlockDecay;
-    if (!fast) {  // uniform: the exact kernel takes the whole chunk
-      if (tid == 0) *flag = 1;
-      return;
-    }
-    // ---- factored operands of the half (see the exact kernel's notes) -----
-    for (int e = tid; e < 10 * kHalf; e += kThreads) {
-      const int pr = e / kHalf, cc = e % kHalf;
-      const int I = pr < 1 ? 0 : pr < 3 ? 1 : pr < 6 ? 2 : 3;
-      const int J = pr - I * (I + 1) / 2;
-      sm.x[XL::cij + e] = __expf(sm.x[XL::bnd + I * kHalf + cc] - sm.x[XL::bnd + J * kHalf + cc]);
-    }
-    const f32x4 rho = *reinterpret_cast<const f32x4*>(&sm.x[XL::bnd + w * kHalf + c4]);
-    float E[4], sE[4], G[4];
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      E[jj] = __expf(rho[jj]);
-      sE[jj] = p.scale * E[jj];
-      G[jj] = __expf(gl[jj] - rho[jj]);
-    }
-    const int cg4 = ch0 + c4;  // the thread's first channel of the head
-    const int r8 = (cg4 & 31) >> 2;
-    const int qcol = 32 * (cg4 >> 5) + 8 * (r8 & 3) + 4 * (r8 >> 2);
-    uint2 kq[PP], qq[PP];
-#pragma unroll
-    for (int i = 0; i < PP; ++i) {
-      const int o = sw16<kHalf>(part * PP + i, c4);
-      kq[i] = *reinterpret_cast<const uint2*>(&sm.u.t.k[o]);
-      qq[i] = *reinterpret_cast<const uint2*>(&sm.u.t.q[o]);
-    }
-    float wk_even[4] = {0.f, 0.f, 0.f, 0.f};
-    float kgv[4][PP];  // [channel][position]
-#pragma unroll
-    for (int i = 0; i < PP; ++i) {
-      const int t = part * PP + i;
-      const int o = sw16<kHalf>(t, c4);
-      const float kv[4] = {__uint_as_float(kq[i].x << 16), __uint_as_float(kq[i].x & 0xffff0000u),
-                           __uint_as_float(kq[i].y << 16), __uint_as_float(kq[i].y & 0xffff0000u)};
-      const float qv[4] = {__uint_as_float(qq[i].x << 16), __uint_as_float(qq[i].x & 0xffff0000u),
-                           __uint_as_float(qq[i].y << 16), __uint_as_float(qq[i].y & 0xffff0000u)};
-      float kr[4], qr[4], kf[4];
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const float Rt = __expf(gm[i][jj] - rho[jj]), Ft = __builtin_amdgcn_rcpf(Rt);  // Rt >= e^-80
-        kr[jj] = kv[jj] * Rt;
-        qr[jj] = qv[jj] * Rt;
-        kf[jj] = kv[jj] * Ft;
-        kgv[jj][i] = kf[jj] * G[jj];
-        if (i & 1) wkp[hf][jj][i >> 1] = pack_bf16x2(wk_even[jj], kr[jj] * E[jj]);
-        else wk_even[jj] = kr[jj] * E[jj];
-      }
-      *reinterpret_cast<uint2*>(&sm.u.t.k[o]) = uint2{pack_bf16x2(kr[0], kr[1]), pack_bf16x2(kr[2], kr[3])};
-      *reinterpret_cast<uint2*>(&sm.u.t.q[o]) = uint2{pack_bf16x2(qr[0], qr[1]), pack_bf16x2(qr[2], qr[3])};
-      *reinterpret_cast<uint2*>(&sm.u.t.kf[o]) = uint2{pack_bf16x2(kf[0], kf[1]), pack_bf16x2(kf[2], kf[3])};
-      const u32x2 qs = {pack_bf16x2(qr[0] * sE[0], qr[1] * sE[1]), pack_bf16x2(qr[2] * sE[2], qr[3] * sE[3])};
-      __builtin_amdgcn_raw_buffer_store_b64(qs, rqg, rec_elem<K>(t, qcol) * 2, 0, 0);
-    }
-    {
-      // (K o e^{gl - gam})^T: the 4 positions are 8 contiguous bytes of the
-      // permuted order.
-      const int tp = part * PP;
-      const int pin = tp & 31;
-      const int slot0 = pin < 16 ? 2 * pin : 2 * (pin - 16) + 4;
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const u32x2 v = {pack_bf16x2(kgv[jj][0], kgv[jj][1]), pack_bf16x2(kgv[jj][2], kgv[jj][3])};
-        __builtin_amdgcn_raw_buffer_store_b64(v, rkg, rec_elem<C>(cg4 + jj, 32 * (tp >> 5) + slot0) * 2, 0, 0);
-      }
-    }
-    lds_barrier();
-    // ---- A and P over the half's channels, accumulated --------------------
-#pragma unroll
-    for (int bi = 0; bi < 3; ++bi) {
-      const int I = blocks[w][bi][0], J = blocks[w][bi][1];
-      if (I >= 0) {  // wave-uniform
-        const float* cv = sm.x + XL::cij + (I * (I + 1) / 2 + J) * kHalf;
-        bf16x8 ak[kHalf / 32], aq[kHalf / 32], b[kHalf / 32];
-#pragma unroll
-        for (int kb = 0; kb < kHalf / 32; ++kb) {
-          const int c0 = 32 * kb + 8 * g;
-          ak[kb] = lds_frag(&sm.u.t.k[sw16<kHalf>(16 * I + m, c0)]);
-          aq[kb] = lds_frag(&sm.u.t.q[sw16<kHalf>(16 * I + m, c0)]);
-          b[kb] = lds_frag(&sm.u.t.kf[sw16<kHalf>(16 * J + m, c0)]);
-        }
-        if (J < I) {
-#pragma unroll
-          for (int kb = 0; kb < kHalf / 32; ++kb) {
-            const f32x4 c0v = *reinterpret_cast<const f32x4*>(cv + 32 * kb + 8 * g);
-            const f32x4 c1v = *reinterpret_cast<const f32x4*>(cv + 32 * kb + 8 * g + 4);
-            float sc[8];
-#pragma unroll
-            for (int jj = 0; jj < 8; ++jj) sc[jj] = static_cast<float>(b[kb][jj]) * (jj < 4 ? c0v[jj] : c1v[jj - 4]);
-            b[kb] = to_bf16x8(sc);
-          }
-        }
-#pragma unroll
-        for (int kb = 0; kb < kHalf / 32; ++kb) {
-          dA[bi] = mfma16(ak[kb], b[kb], dA[bi]);
-          dPt[bi] = mfma16(b[kb], aq[kb], dPt[bi]);
-        }
-      }
-    }
-  }
-  if (tid == 0) *flag = 0;
-
-  // ---- A^T into at, scale P into the record -------------------------------
-  {
-    const __amdgpu_buffer_rsrc_t rpm = make_rsrc(rec + R::Pm, static_cast<uint32_t>(C * C * 2));
-#pragma unroll
-    for (int bi = 0; bi < 3; ++bi) {
-      const int I = blocks[w][bi][0], J = blocks[w][bi][1];
-      if (I >= 0) {
-        float bt[4];  // beta of the lane's rows (on the diagonal of at)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) bt[jj] = sm.at[sw32<C>(16 * I + 4 * g + jj, 16 * I + 4 * g + jj)];
-        const int s2 = 16 * J + m;
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int row = 16 * I + 4 * g + jj;
-          sm.at[sw32<C>(s2, row)] = s2 == row ? bt[jj] : bt[jj] * dA[bi][jj];
-        }
-        const int prow = 16 * I + m;
-        float pv[4];
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) pv[jj] = 16 * J + 4 * g + jj <= prow ? p.scale * dPt[bi][jj] : 0.f;
-        const u32x2 v = {pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])};
-        __builtin_amdgcn_raw_buffer_store_b64(v, rpm, rec_elem<C>(prow, 32 * (J >> 1) + 8 * g + 4 * (J & 1)) * 2, 0, 0);
-      }
-    }
-    if (w == 3) {
-      const u32x2 z = {0u, 0u};
-      __builtin_amdgcn_raw_buffer_store_b64(z, rpm, rec_elem<C>(m, 8 * g + 4) * 2, 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b64(z, rpm, rec_elem<C>(32 + m, 32 + 8 * g + 4) * 2, 0, 0);
-    }
-  }
-  // v for the U phase, fetched now so its latency hides behind the inverse.
-  constexpr int NBU = (V / 16 + 3) / 4;
-  static_assert(V / 16 <= 4 * NBU && V / 16 > 4 * (NBU - 1), "every wave has NBU column blocks");
-  uint16_t vpre[NBU][2][8];
-  {
-    const int vlane = (2 * H * K + h * V + m) * 2 + 8 * g * rs;
-#pragma unroll
-    for (int u = 0; u < NBU; ++u)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          const int nb = w + 4 * u;
-          vpre[u][kb][jj] = __builtin_amdgcn_raw_buffer_load_b16(rq, vlane + 32 * nb, (32 * kb + jj) * rs, 0);
-        }
-  }
-  lds_barrier();  // A^T complete; tiles and x no longer read
-
-  float* beta_l = sm.x;
-  if (tid < C) beta_l[tid] = beta_t;
-  uint16_t* wkt = sm.u.wkt;
-  // (K o e^gam)^T: 8 bytes (4 positions) per channel and half.
-#pragma unroll
-  for (int hf = 0; hf < NH; ++hf)
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj)
-      *reinterpret_cast<uint2*>(wkt + rec_elem<C>(kHalf * hf + c4 + jj, part * PP)) = uint2{wkp[hf][jj][0], wkp[hf][jj][1]};
-
-  intra_inverse_wu<K, V>(p, sm.at, wkt, beta_l, vpre, rec, w, lane);
-}
-
-template <int K, int V>
-__global__ __launch_bounds__(kThreads, 3) void chunk_intra_kernel(const PrefillParams p,
-                                                                  const int4* chunk_info,
-                                                                  char* recs, uint8_t* exact_flags) {
-  intra_factored<K, V>(p, chunk_info, recs, exact_flags);
-}
-
-template <int K, int V>
-__global__ __launch_bounds__(kThreads, 2) void chunk_intra_exact_kernel(const PrefillParams p,
-                                                                        const int4* chunk_info,
-                                                                        char* recs, uint8_t* exact_flags) {
-  intra_exact<K, V>(p, chunk_info, recs, exact_flags);
-}
-
-
-
-// --------------------------------------------------------------- state --
-
-// The LDS image of one record: the record's first lds_part bytes, byte for
-// byte (tiles swizzled as written by the intra kernel).
-template <int K, int V>
-struct StateBuf {
-  uint16_t wn[C * K];
-  uint16_t qg[C * K];
-  uint16_t pm[C * C];
-  uint16_t kgt[K * C];
-  float eg[K];
-};
-
-// Copy `Bytes` bytes (whole 16-byte pieces) from `src` to LDS at `dst` by
-// buffer-to-LDS DMA: lane l of a wave writes its 16 bytes at the wave's LDS
-// base + 16 l, so slot i takes piece i. Nothing passes through registers and
-// no per-lane address math is needed; the copy runs until the next vmcnt
-// wait. `wave` is the wave index in a scalar register.
-template <int Bytes, int NT>
-__device__ __forceinline__ void dma_copy(const char* src, void* dst_lds, int tid, int wave) {
-  static_assert(Bytes % 16 == 0, "whole 16-byte pieces");
-  constexpr int total = Bytes / 16;
-  constexpr int full = total / NT, rem = total % NT;
-  const __amdgpu_buffer_rsrc_t rr = make_rsrc(src, static_cast<uint32_t>(Bytes));
-  uint4* dst = reinterpret_cast<uint4*>(dst_lds) + wave * 64;
-  const int voff = tid * 16;
-#pragma unroll
-  for (int r = 0; r < full; ++r)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, dst + r * NT, 16, voff, r * NT * 16, 0, 0);
-  if constexpr (rem > 0) {
-    // Only lanes whose slot lies inside the range take part (inactive lanes
-    // write nothing).
-    if (tid < rem)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, dst + full * NT, 16, voff, full * NT * 16, 0, 0);
-  }
-}
-
-// Copy record `rec`'s LDS part into `b` with NT threads.
-template <int K, int V, int NT>
-__device__ __forceinline__ void dma_chunk(const char* rec, StateBuf<K, V>* b, int tid, int wave) {
-  dma_copy<static_cast<int>(sizeof(StateBuf<K, V>)), NT>(rec, b, tid, wave);
-}
-
-// Output stores per lane per chunk: one 8-byte store per 16-position block.
-constexpr int kOutStores = C / 16;
-
-// Top of a chunk: this wave's copies and U loads for the chunk have landed
-// (every vector-memory operation except the kOutStores output stores issued
-// after them; they complete in order), its LDS reads are done, and all waves
-// meet. Unlike __syncthreads this leaves the output stores in flight.
-__device__ __forceinline__ void chunk_barrier() {
-  static_assert(kOutStores < 16, "vmcnt field");
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0x0070 | kOutStores);  // vmcnt = kOutStores, expcnt = 7, lgkmcnt = 0
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// NB = 2: the next chunk's record is copied into the second LDS buffer while
-// the current one computes (one workgroup per CU at K = V = 128). NB = 1: one
-// buffer, refilled once every wave has read it, so two workgroups share a CU
-// and each one's copies overlap the other's MFMA phases; the host takes it
-// when there are enough workgroups to give every CU two.
-template <int K, int V, int NB>
-__global__ __launch_bounds__(kThreads, NB == 1 ? 2 : 1) void chunk_state_kernel(const PrefillParams p,
-                                                                                const SegPlan pl,
-                                                                                const char* recs) {
-  using R = Rec<K, V>;
-  using B = StateBuf<K, V>;
-  static_assert(sizeof(B) == R::lds_part, "LDS image is the record's first lds_part bytes");
-  static_assert(R::lds_part % 16 == 0, "record LDS part must be whole 16-byte pieces");
-  static_assert(NB == 1 || NB == 2, "one or two record buffers");
-  constexpr int NVH = V / 64;  // workgroups per (segment, head): 64 columns each
-  __shared__ B buf[NB];
-
-  // The NVH workgroups of one (segment, head) read the same records: give
-  // them indices that are equal modulo 8 so they run on the same XCD (one L2).
-  // (Four waves per workgroup: every wave reads the whole of each record's
-  // tiles from LDS, so more waves per workgroup would make LDS reads, not
-  // the record copies, the bound.)
-  const int bidx = blockIdx.x;
-  int pair, vh;
-  if constexpr (NVH == 2) {
-    pair = (bidx / 16) * 8 + (bidx % 8);
-    vh = (bidx / 8) % 2;
-  } else {
-    pair = bidx;
-    vh = 0;
-  }
-  const int H = p.H;
-  if (uniform(pl.counts[3]) == 0) return;  // cu_seqlens outside the contract
-  const int gs = pair / H, h = pair % H;
-  if (gs >= uniform(pl.counts[0])) return;
-  // Records exist for at most max_chunks chunks (sized from the host's token
-  // count); inconsistent cu_seqlens must not send us past them.
-  if (pl.chunk_start[p.num_seqs] > max_chunks_for(p.num_tokens, p.num_seqs)) return;
-  // Values loaded from wave-uniform addresses, kept in scalar registers.
-  const int seq = uniform(pl.seg_seq[gs]);
-  const int seg0 = uniform(pl.seg_start[seq]);
-  const int nseg = uniform(pl.seg_start[seq + 1]) - seg0;
-  const int sg = gs - seg0;
-  const int cbase = uniform(pl.chunk_start[seq]);
-  const int nch_seq = uniform(pl.chunk_start[seq + 1]) - cbase;
-  const int seg_len = (nch_seq + nseg - 1) / nseg;
-  const int cfirst = sg * seg_len;
-  const int nch = min(nch_seq, cfirst + seg_len) - cfirst;
-  const int c0 = cbase + cfirst;
-  const bool last_seg = sg == nseg - 1;
-  const int64_t bos = uniform(static_cast<int64_t>(p.cu_seqlens[seq]));
-  const int64_t eos = uniform(static_cast<int64_t>(p.cu_seqlens[seq + 1]));
-  if (nch <= 0 || eos > p.num_tokens || bos < 0) return;
-  const int64_t tfirst = bos + static_cast<int64_t>(C) * cfirst;
-  const int64_t tend = min<int64_t>(eos, tfirst + static_cast<int64_t>(C) * nch);
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = tid >> 6;
-  const int wave = uniform(w);
-  const int m = lane & 15;
-  const int g = lane >> 4;
-  const int col0 = vh * 64 + 16 * w;
+  const bool has_cols = w < V / 16;  // wave-uniform
+  const int col0 = 16 * w;
   const int64_t HV = static_cast<int64_t>(H) * V;
+  const int64_t tfirst = sr.bos + static_cast<int64_t>(C) * sr.c0;
+  const int64_t tend = min<int64_t>(sr.eos, tfirst + static_cast<int64_t>(C) * sr.nch);
 
-  const int64_t slot = uniform(static_cast<int64_t>(p.indices[static_cast<int64_t>(seq) * p.index_stride]));
+  const int64_t slot = uniform(static_cast<int64_t>(p.indices[static_cast<int64_t>(sr.seq) * p.index_stride]));
   if (slot < 0) {
     // Null slot: zero output rows, no state traffic.
     for (int64_t t = tfirst; t < tend; ++t)
-      if (tid < 64) p.out[t * HV + h * V + vh * 64 + tid] = 0;
+      for (int c = tid; c < V; c += kThreads) p.out[t * HV + h * V + c] = 0;
     return;
   }
 
+  // The first chunk's inputs go out first, so the state loads below hide
+  // their latency.
+  ChunkIn<K, V> in;
+  load_chunk_regs<K, V>(p, h, chunk_pos(sr, 0), in);
+  dma_chunk_tiles<K, true>(p, h, chunk_pos(sr, 0), sm.t.f.k, sm.t.f.q);
+
   float* st = p.pool + slot * p.slot_stride + static_cast<int64_t>(h) * K * V;
-  // Every segment of a cut sequence starts from the copy of the slot's state
-  // that the map pass made (the slot itself is written by the last segment
-  // of this same launch); an uncut sequence from its slot.
+  // Segment 0 of a cut sequence starts from the copy of the slot's state that
+  // the map pass made (the slot itself is written by the last segment of this
+  // same launch), segment sg > 0 from the state the scan pass left in B of
+  // map item sg - 1; an uncut sequence from its slot.
   const int li = uniform(pl.seg_long[gs]);
-  const float* s_in = li >= 0 ? pl.s0 + s0_index(h, li, pl) * K * V : st;
+  const float* s_in = st;
+  if (li >= 0)
+    s_in = sr.sg == 0 ? pl.s0 + s0_index(h, li, pl) * K * V
+                      : pl.maps + map_index(h, sr.seg0 - sr.seq + sr.sg - 1, pl) *
+                                      (static_cast<int64_t>(K) * K + static_cast<int64_t>(K) * V) + K * K;
   const bool init = li >= 0 || p.has_initial_state == nullptr ||
-                    uniform(static_cast<int32_t>(p.has_initial_state[seq])) != 0;
-  // Without an initial state the range is empty and every load reads zero;
-  // all loads are issued before the first use.
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(s_in, init ? static_cast<uint32_t>(K * V * 4) : 0u);
+                    uniform(static_cast<int32_t>(p.has_initial_state[sr.seq])) != 0;
+  // Without an initial state (or without columns) the range is empty and
+  // every load reads zero.
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(s_in, init && has_cols ? static_cast<uint32_t>(K * V * 4) : 0u);
   f32x4 S[K / 16];
 #pragma unroll
   for (int cb = 0; cb < K / 16; ++cb)
@@ -1538,179 +1367,35 @@ __global__ __launch_bounds__(kThreads, NB == 1 ? 2 : 1) void chunk_state_kernel(
     for (int j = 0; j < 4; ++j)
       S[cb][j] = __builtin_bit_cast(
           float, __builtin_amdgcn_raw_buffer_load_b32(rs, ((16 * cb + 4 * g + j) * V + col0 + m) * 4, 0, 0));
-  f32x4 Upre[4];
-  auto rec_of = [&](int cc) {
-    return recs + rec_index(h, c0 + cc, p) * static_cast<int64_t>(R::bytes);
-  };
-  // U fragments: lane's 16 bytes of tile (pb, col0 / 16) at a fixed offset.
-  const int u_lane = ((col0 / 16) * 64 + lane) * 16;
-  auto load_u = [&](int cc) {
-    const __amdgpu_buffer_rsrc_t ru = make_rsrc(rec_of(cc) + R::Uf, static_cast<uint32_t>(C * V * 4));
-#pragma unroll
-    for (int pb = 0; pb < 4; ++pb) Upre[pb] = buffer_load_f32x4<0>(ru, u_lane, pb * (V / 16) * 64 * 16);
-  };
-  // The first chunk's copy and U loads go out first, so the walk below
-  // hides their latency.
-  dma_chunk<K, V, kThreads>(rec_of(0), &buf[0], tid, wave);
-  load_u(0);
-  // Segment sg > 0 of a cut sequence walks the maps of the segments before
-  // it: S <- M_j S + B_j. The wave holds all K rows of its 16 columns, so
-  // two accumulator tiles form a bf16 B operand as in the chunk loop (the
-  // contraction index permuted within each 32-block); lane (m, g)'s A
-  // operand is then M[row m][32 kb + 4 g .. +3] and M[row m][32 kb + 16 +
-  // 4 g .. +3], two float4s of the row-major fp32 M. Both operands are split
-  // into bf16 hi + lo parts and the product is hi*hi + hi*lo + lo*hi (about
-  // 16 significant bits, fp32 accumulation).
-  if (li >= 0 && sg > 0) {
-    const int mi0 = seg0 - seq;  // the sequence's first map item
-    const int64_t item = static_cast<int64_t>(K) * K + static_cast<int64_t>(K) * V;
-    constexpr int RT = K / 16, KB = K / 32;
-    if constexpr (NB == 2) {
-      // M goes through the idle second record buffer, 32 rows (two row
-      // tiles) per stage, two stages in flight: the workgroup reads M from
-      // L2 once instead of once per wave. Stage rows are stored with their
-      // 16-byte pieces XOR-swizzled by the row (piece p of row r at p ^ (r &
-      // 15)), so the 16 rows a fragment read touches fall in different banks.
-      constexpr int QR = 32;                 // rows per stage
-      constexpr int PPR = K / 4;             // 16-byte pieces per row
-      constexpr int SBYTES = QR * K * 4;
-      constexpr int SPS = K / QR;            // stages per map step
-      static_assert(2 * SBYTES <= static_cast<int>(sizeof(B)), "two stages fit the idle buffer");
-      static_assert((QR * PPR) % kThreads == 0, "whole DMA rounds");
-      float* stage_buf = reinterpret_cast<float*>(&buf[1]);
-      auto dma_stage = [&](int st) {  // stage st of the walk into its half of the buffer
-        const float* M = pl.maps + map_index(h, mi0 + st / SPS, pl) * item + static_cast<int64_t>(st % SPS) * QR * K;
-        const __amdgpu_buffer_rsrc_t rr = make_rsrc(M, static_cast<uint32_t>(SBYTES));
-        uint4* dst = reinterpret_cast<uint4*>(stage_buf + (st & 1) * (SBYTES / 4));
-#pragma unroll
-        for (int r = 0; r < QR * PPR / kThreads; ++r) {
-          const int ps = r * kThreads + tid;  // physical piece of the stage
-          const int row = ps / PPR, pp = ps % PPR;
-          const int pl = pp ^ (row & 15);     // logical piece stored there
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, dst + r * kThreads + (tid & ~63), 16,
-                                                   (row * PPR + pl) * 16, 0, 0, 0);
-        }
-      };
-      bf16x8 Sh[KB], Sl[KB];
-      const int stages = sg * SPS;
-      dma_stage(0);
-      for (int st = 0; st < stages; ++st) {
-        // Stage st has landed in every thread's pieces, and every wave is
-        // done with the half stage st + 1 overwrites.
-        wait_vmem();
-        lds_barrier();
-        if (st + 1 < stages) dma_stage(st + 1);
-        const float* sb = stage_buf + (st & 1) * (SBYTES / 4);
-        const float* Bm = pl.maps + map_index(h, mi0 + st / SPS, pl) * item + static_cast<int64_t>(K) * K;
-        if (st % SPS == 0) {
-          // Operands of this step: the state before it, as bf16 hi + lo.
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb) {
-            Sh[kb] = pack_acc(S[2 * kb], S[2 * kb + 1]);
-            Sl[kb] = pack_lo(S[2 * kb], S[2 * kb + 1], Sh[kb]);
-          }
-        }
-#pragma unroll
-        for (int t2 = 0; t2 < QR / 16; ++t2) {
-          const int rt = (st % SPS) * (QR / 16) + t2;
-          f32x4 acc;
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) acc[jj] = Bm[(16 * rt + 4 * g + jj) * V + col0 + m];
-          const float* row = sb + (16 * t2 + m) * K;
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb) {
-            const f32x4 a0 = *reinterpret_cast<const f32x4*>(row + 4 * ((8 * kb + g) ^ m));
-            const f32x4 a1 = *reinterpret_cast<const f32x4*>(row + 4 * ((8 * kb + 4 + g) ^ m));
-            const bf16x8 ah = pack_acc(a0, a1);
-            const bf16x8 al = pack_lo(a0, a1, ah);
-            acc = mfma16(ah, Sh[kb], acc);
-            acc = mfma16(ah, Sl[kb], acc);
-            acc = mfma16(al, Sh[kb], acc);
-          }
-          // Row tile rt of the new state (the old tiles live on in Sh/Sl).
-#pragma unroll
-          for (int r2 = 0; r2 < RT; ++r2)
-            if (r2 == rt) S[r2] = acc;
-        }
-      }
-    } else {
-      // Flattened over (step j, row tile rt); tile i + 1's operands are loaded
-      // while tile i computes (the scheduling barriers keep that order).
-      auto load_tile = [&](int i, f32x4 (&a)[KB][2], f32x4& b) {
-        const float* M = pl.maps + map_index(h, mi0 + i / RT, pl) * item;
-        const int rt = i % RT;
-        const float* row = M + (16 * rt + m) * K + 4 * g;
-  #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          a[kb][0] = *reinterpret_cast<const f32x4*>(row + 32 * kb);
-          a[kb][1] = *reinterpret_cast<const f32x4*>(row + 32 * kb + 16);
-        }
-        const float* Bm = M + static_cast<int64_t>(K) * K;
-  #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) b[jj] = Bm[(16 * rt + 4 * g + jj) * V + col0 + m];
-      };
-      f32x4 a_cur[KB][2], a_nxt[KB][2], b_cur, b_nxt;
-      bf16x8 Sh[KB], Sl[KB];
-      load_tile(0, a_cur, b_cur);
-      const int tiles = sg * RT;
-      for (int i = 0; i < tiles; ++i) {
-        const int rt = i % RT;
-        if (rt == 0) {
-          // Operands of this step: the state before it, as bf16 hi + lo.
-  #pragma unroll
-          for (int kb = 0; kb < KB; ++kb) {
-            Sh[kb] = pack_acc(S[2 * kb], S[2 * kb + 1]);
-            Sl[kb] = pack_lo(S[2 * kb], S[2 * kb + 1], Sh[kb]);
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        if (i + 1 < tiles) load_tile(i + 1, a_nxt, b_nxt);
-        __builtin_amdgcn_sched_barrier(0);
-        f32x4 acc = b_cur;
-  #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          const bf16x8 ah = pack_acc(a_cur[kb][0], a_cur[kb][1]);
-          const bf16x8 al = pack_lo(a_cur[kb][0], a_cur[kb][1], ah);
-          acc = mfma16(ah, Sh[kb], acc);
-          acc = mfma16(ah, Sl[kb], acc);
-          acc = mfma16(al, Sh[kb], acc);
-        }
-        // Row tile rt of the new state (the old tiles live on in Sh/Sl).
-  #pragma unroll
-        for (int r2 = 0; r2 < RT; ++r2)
-          if (r2 == rt) S[r2] = acc;
-  #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          a_cur[kb][0] = a_nxt[kb][0];
-          a_cur[kb][1] = a_nxt[kb][1];
-        }
-        b_cur = b_nxt;
-      }
-    }
-  }
+
   // Lane (m, g) of the transposed output tile of position block pb holds
   // channels col0 + 4 g .. + 3 of position 16 pb + m: 8 contiguous bytes.
-  const int out_lane = static_cast<int>(m * HV + h * V + col0 + 4 * g) * 2;
-  for (int cc = 0; cc < nch; ++cc) {
-    const B& bf = buf[NB == 2 ? (cc & 1) : 0];
-    // Chunk cc's buffer is complete once every wave's copy has landed; with
-    // two buffers the barrier also means every wave is done with chunk
-    // cc-1's buffer, which the next copy overwrites.
-    chunk_barrier();
+  const auto& ops = sm.r.ops;
+  for (int cc = 0; cc < sr.nch; ++cc) {
+    const ChunkPos cp = chunk_pos(sr, cc);
+    // This chunk's inputs have landed (the previous chunk's 4 output stores
+    // per lane, issued after them, may still be in flight) and every wave is
+    // done with the previous chunk's operands.
+    if (has_cols) chunk_barrier<4>();
+    else chunk_barrier<0>();
     f32x4 Vp[4];
-#pragma unroll
-    for (int pb = 0; pb < 4; ++pb) Vp[pb] = Upre[pb];
-    if (NB == 2 && cc + 1 < nch) {
-      dma_chunk<K, V, kThreads>(rec_of(cc + 1), &buf[(cc + 1) & 1], tid, wave);
-      load_u(cc + 1);
+    const bool more = cc + 1 < sr.nch;
+    const ChunkPos np = chunk_pos(sr, more ? cc + 1 : cc);
+    intra_part<K, V, true, EXACT>(p, h, cp.n, in, more, np, sm, Vp);
+    // The rest of the next chunk's inputs go out now: the registers and the
+    // tile area are free, and the state step below hides their latency.
+    if (more) {
+      load_chunk_v_regs<K, V>(p, h, np, in);
+      if constexpr (EXACT) dma_chunk_tiles<K, true>(p, h, np, sm.t.f.k, sm.t.f.q);
     }
-
-    const int64_t t0 = tfirst + static_cast<int64_t>(C) * cc;
-    const int n = static_cast<int>(min<int64_t>(C, eos - t0));
+    if (!has_cols) continue;
+    const int m = opaque_tid() & 15, g = (opaque_tid() & 63) >> 4;
+    const int out_lane = static_cast<int>(m * HV + h * V + col0 + 4 * g) * 2;
 
     // V' = U - W S (rows: positions) and O^T = S^T (Q o e^gam)^T (rows:
     // value channels), both contracting over key channels. S as a bf16
-    // fragment is the B operand of the first and the A operand of the second.
+    // fragment is the B operand of the first and the A operand of the
+    // second.
     bf16x8 Sb[K / 32];
 #pragma unroll
     for (int kb = 0; kb < K / 32; ++kb) Sb[kb] = pack_acc(S[2 * kb], S[2 * kb + 1]);
@@ -1720,8 +1405,8 @@ __global__ __launch_bounds__(kThreads, NB == 1 ? 2 : 1) void chunk_state_kernel(
     bf16x8 wf[2][K / 32], qf[2][K / 32];
 #pragma unroll
     for (int kb = 0; kb < K / 32; ++kb) {
-      wf[0][kb] = frag<K>(bf.wn, m, 32 * kb + 8 * g);
-      qf[0][kb] = frag<K>(bf.qg, m, 32 * kb + 8 * g);
+      wf[0][kb] = frag<K>(ops.wn, m, 32 * kb + 8 * g);
+      qf[0][kb] = frag<K>(ops.qg, m, 32 * kb + 8 * g);
     }
     bf16x8 pf[4][2];
     f32x4 Ot[4];
@@ -1731,14 +1416,14 @@ __global__ __launch_bounds__(kThreads, NB == 1 ? 2 : 1) void chunk_state_kernel(
       if (pb + 1 < 4) {
 #pragma unroll
         for (int kb = 0; kb < K / 32; ++kb) {
-          wf[(pb + 1) & 1][kb] = frag<K>(bf.wn, 16 * (pb + 1) + m, 32 * kb + 8 * g);
-          qf[(pb + 1) & 1][kb] = frag<K>(bf.qg, 16 * (pb + 1) + m, 32 * kb + 8 * g);
+          wf[(pb + 1) & 1][kb] = frag<K>(ops.wn, 16 * (pb + 1) + m, 32 * kb + 8 * g);
+          qf[(pb + 1) & 1][kb] = frag<K>(ops.qg, 16 * (pb + 1) + m, 32 * kb + 8 * g);
         }
       } else {
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-          pf[b][0] = frag<C>(bf.pm, 16 * b + m, 8 * g);
-          if (b >= 2) pf[b][1] = frag<C>(bf.pm, 16 * b + m, 32 + 8 * g);
+          pf[b][0] = frag<C>(ops.pm, 16 * b + m, 8 * g);
+          if (b >= 2) pf[b][1] = frag<C>(ops.pm, 16 * b + m, 32 + 8 * g);
         }
       }
       Ot[pb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1749,12 +1434,6 @@ __global__ __launch_bounds__(kThreads, NB == 1 ? 2 : 1) void chunk_state_kernel(
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    bf16x8 kf[K / 16][2];
-#pragma unroll
-    for (int cb = 0; cb < K / 16; ++cb) {
-      kf[cb][0] = frag<C>(bf.kgt, 16 * cb + m, 8 * g);
-      kf[cb][1] = frag<C>(bf.kgt, 16 * cb + m, 32 + 8 * g);
-    }
     // V' over positions: the output product takes it as hi + lo bf16 parts
     // (the rounding of V' would otherwise dominate the output error); the
     // state update takes the hi part.
@@ -1774,292 +1453,321 @@ __global__ __launch_bounds__(kThreads, NB == 1 ? 2 : 1) void chunk_state_kernel(
       }
     }
     // Rows of the chunk as one buffer range: positions past its end fall
-    // outside and their stores are dropped, so every lane issues exactly
-    // kOutStores stores, the last vector-memory operations of the chunk.
-    auto store_out = [&]() {
-      const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.out + t0 * HV, static_cast<uint32_t>(n * HV * 2));
+    // outside and their stores are dropped, so every lane issues exactly 4
+    // stores, the last vector-memory operations of the chunk.
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.out + cp.t0 * HV, static_cast<uint32_t>(cp.n * HV * 2));
 #pragma unroll
-      for (int pb = 0; pb < 4; ++pb) {
-        const uint32_t lo = pack_bf16x2(Ot[pb][0], Ot[pb][1]);
-        const uint32_t hi = pack_bf16x2(Ot[pb][2], Ot[pb][3]);
-        typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-        __builtin_amdgcn_raw_buffer_store_b64(u32x2{lo, hi}, ro, out_lane + static_cast<int>(16 * pb * HV * 2), 0, 0);
-      }
-    };
-    if constexpr (NB == 2) store_out();
+    for (int pb = 0; pb < 4; ++pb)
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf16x2(Ot[pb][0], Ot[pb][1]), pack_bf16x2(Ot[pb][2], Ot[pb][3])},
+                                            ro, out_lane + static_cast<int>(16 * pb * HV * 2), 0, 0);
     // S <- diag(e^{gam_last}) S + (K o e^{gam_last - gam})^T V'.
+    bf16x8 kf[2][2];
+    kf[0][0] = frag<C>(ops.kgt, m, 8 * g);
+    kf[0][1] = frag<C>(ops.kgt, m, 32 + 8 * g);
 #pragma unroll
     for (int cb = 0; cb < K / 16; ++cb) {
-      const f32x4 e = *reinterpret_cast<const f32x4*>(&bf.eg[16 * cb + 4 * g]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (cb + 1 < K / 16) {
+        kf[(cb + 1) & 1][0] = frag<C>(ops.kgt, 16 * (cb + 1) + m, 8 * g);
+        kf[(cb + 1) & 1][1] = frag<C>(ops.kgt, 16 * (cb + 1) + m, 32 + 8 * g);
+      }
+      const f32x4 e = *reinterpret_cast<const f32x4*>(&ops.eg[16 * cb + 4 * g]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) S[cb][j] *= e[j];
-      S[cb] = mfma16(kf[cb][0], Vb0, S[cb]);
-      S[cb] = mfma16(kf[cb][1], Vb1, S[cb]);
+      S[cb] = mfma16(kf[cb & 1][0], Vb0, S[cb]);
+      S[cb] = mfma16(kf[cb & 1][1], Vb1, S[cb]);
     }
-    if constexpr (NB == 1) {
-      // Every wave's reads of the buffer are done: refill it with the next
-      // chunk, then store this chunk's output rows.
-      if (cc + 1 < nch) {
-        lds_barrier();
-        dma_chunk<K, V, kThreads>(rec_of(cc + 1), &buf[0], tid, wave);
-        load_u(cc + 1);
-      }
-      store_out();
-    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 
-  if (!last_seg) return;
+  if (!last_seg || !has_cols) return;
 #pragma unroll
   for (int cb = 0; cb < K / 16; ++cb)
 #pragma unroll
     for (int j = 0; j < 4; ++j) st[(16 * cb + 4 * g + j) * V + col0 + m] = S[cb][j];
 }
 
+// ---------------------------------------------------------------- scan --
+
+// One workgroup per (cut sequence, head), 8 waves; wave w < V / 16 owns
+// value columns 16 w .. 16 w + 15. Composes the segment maps in order:
+// S_0 = the copy of the slot's state, S_{j+1} = M_j S_j + B_j, stored over
+// B_j for segment j + 1 of the state pass. The wave holds all K rows of its
+// columns, so two accumulator tiles form a bf16 B operand as in the chunk
+// loop (the contraction index permuted within each 32-block); lane (m, g)'s
+// A operand is M[row m][32 kb + 4 g .. +3] and M[row m][32 kb + 16 + 4 g ..
+// +3], two float4s of the row-major fp32 M. Both operands are split into
+// bf16 hi + lo parts and the product is hi*hi + hi*lo + lo*hi (about 16
+// significant bits, fp32 accumulation). Each M goes through LDS once for the
+// workgroup (double-buffered: the next map's copy runs under the current
+// product), its rows' 16-byte pieces XOR-swizzled by the row (piece p of row
+// r at p ^ (r & 15)) so the 16 rows a fragment read touches fall in
+// different banks.
+template <int K, int V>
+__global__ __launch_bounds__(kThreads, 1) void chunk_scan_kernel(const PrefillParams p, const SegPlan pl) {
+  constexpr int KB = K / 32;
+  constexpr int PPR = K / 4;                     // 16-byte pieces per row of M
+  constexpr int ROUNDS = K * PPR / kThreads;     // DMA rounds per M
+  static_assert((K * PPR) % kThreads == 0, "whole DMA rounds");
+  __shared__ float mbuf[2][K * K];
+  const int H = p.H;
+  if (uniform(pl.counts[0]) != 0) return;
+  const int li = static_cast<int>(blockIdx.x) / H, h = static_cast<int>(blockIdx.x) % H;
+  if (li >= uniform(pl.counts[3])) return;
+  const int seq = uniform(pl.long_seq[li]);
+  const int64_t slot = uniform(static_cast<int64_t>(p.indices[static_cast<int64_t>(seq) * p.index_stride]));
+  if (slot < 0) return;  // no maps were made for a null slot
+  const int seg0 = uniform(pl.seg_start[seq]);
+  const int nmap = uniform(pl.seg_start[seq + 1]) - seg0 - 1;
+  const int mi0 = seg0 - seq;
+  const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
+  const int m = lane & 15, g = lane >> 4;
+  const bool has_cols = w < V / 16;
+  const int col0 = 16 * w;
+  const int64_t item = static_cast<int64_t>(K) * K + static_cast<int64_t>(K) * V;
+  auto dma_map = [&](int j) {
+    const __amdgpu_buffer_rsrc_t rr = make_rsrc(pl.maps + map_index(h, mi0 + j, pl) * item, static_cast<uint32_t>(K * K * 4));
+    uint4* dst = reinterpret_cast<uint4*>(mbuf[j & 1]);
+#pragma unroll
+    for (int r = 0; r < ROUNDS; ++r) {
+      const int ps = r * kThreads + tid;  // physical piece
+      const int row = ps / PPR, pp = ps % PPR;
+      const int lp = pp ^ (row & 15);     // logical piece stored there
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, dst + r * kThreads + (tid & ~63), 16, (row * PPR + lp) * 16, 0, 0, 0);
+    }
+  };
+  dma_map(0);
+  f32x4 S[K / 16];
+  {
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(pl.s0 + s0_index(h, li, pl) * K * V, has_cols ? static_cast<uint32_t>(K * V * 4) : 0u);
+#pragma unroll
+    for (int cb = 0; cb < K / 16; ++cb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        S[cb][j] = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(rs, ((16 * cb + 4 * g + j) * V + col0 + m) * 4, 0, 0));
+  }
+  // B_j of the wave's columns, loaded a step ahead.
+  auto load_b = [&](int j, f32x4 (&b)[K / 16]) {
+    const float* Bm = pl.maps + map_index(h, mi0 + j, pl) * item + static_cast<int64_t>(K) * K;
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bm, has_cols ? static_cast<uint32_t>(K * V * 4) : 0u);
+#pragma unroll
+    for (int cb = 0; cb < K / 16; ++cb)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        b[cb][jj] = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(rb, ((16 * cb + 4 * g + jj) * V + col0 + m) * 4, 0, 0));
+  };
+  f32x4 Bn[K / 16];
+  load_b(0, Bn);
+  for (int j = 0; j < nmap; ++j) {
+    float* Bm = pl.maps + map_index(h, mi0 + j, pl) * item + static_cast<int64_t>(K) * K;
+    // M_j has landed in every thread's pieces (wait for everything: the
+    // copy of M_{j+1} is issued only below), and every wave is done with the
+    // buffer M_{j+1} overwrites.
+    wait_vmem();
+    lds_barrier();
+    f32x4 Bc[K / 16];
+#pragma unroll
+    for (int cb = 0; cb < K / 16; ++cb) Bc[cb] = Bn[cb];
+    if (j + 1 < nmap) {
+      dma_map(j + 1);
+      load_b(j + 1, Bn);
+    }
+    if (!has_cols) continue;
+    bf16x8 Sh[KB], Sl[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      Sh[kb] = pack_acc(S[2 * kb], S[2 * kb + 1]);
+      Sl[kb] = pack_lo(S[2 * kb], S[2 * kb + 1], Sh[kb]);
+    }
+    const float* mb = mbuf[j & 1];
+#pragma unroll
+    for (int rt = 0; rt < K / 16; ++rt) {
+      f32x4 acc = Bc[rt];
+      const float* row = mb + (16 * rt + m) * K;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const f32x4 a0 = *reinterpret_cast<const f32x4*>(row + 4 * ((8 * kb + g) ^ m));
+        const f32x4 a1 = *reinterpret_cast<const f32x4*>(row + 4 * ((8 * kb + 4 + g) ^ m));
+        const bf16x8 ah = pack_acc(a0, a1);
+        const bf16x8 al = pack_lo(a0, a1, ah);
+        acc = mfma16(ah, Sh[kb], acc);
+        acc = mfma16(ah, Sl[kb], acc);
+        acc = mfma16(al, Sh[kb], acc);
+      }
+      S[rt] = acc;
+    }
+    // The state that segment j + 1 starts from, over B_j (this wave's
+    // columns only; B_j's other columns belong to other waves).
+#pragma unroll
+    for (int cb = 0; cb < K / 16; ++cb)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) Bm[(16 * cb + 4 * g + jj) * V + col0 + m] = S[cb][jj];
+  }
+}
+
 // ----------------------------------------------------------------- map --
 
-// LDS image of the record parts the map pass reads: -W, and the
-// contiguous (K o e^{gam_last - gam})^T and e^{gam_last}.
-template <int K, int V>
-struct MapBuf {
-  uint16_t wn[C * K];
-  uint16_t kgt[K * C];
-  float eg[K];
-};
-
-// One workgroup per (map item, head, 64 columns of [M | B]), one 16-column
-// MFMA tile per wave. (Two tiles per wave, each LDS fragment feeding two
-// MFMAs, measured 5 % slower: half as many workgroups, each with longer
-// chains per chunk.) Runs the chunk recurrence of one non-final segment
-// (all of its chunks are full) from S = the identity's columns with U = 0
-// (columns of M) or from S = 0 with the chunk's U (columns of B). There is
-// no output; the rounding is the state pass's (bf16 S into W S, bf16 V' into
-// the update, fp32 accumulation). Waves past column K + V only take part in
-// the copies and barriers (K and V are multiples of 64, so a wave's columns
-// all belong to M or all to B).
-constexpr int kMapWaves = 4;
-constexpr int kMapThreads = kMapWaves * 64;
-constexpr int kMapCT = 1;  // 16-column tiles per wave
-
-template <int K, int V>
-__global__ __launch_bounds__(kMapThreads, 2) void chunk_map_kernel(const PrefillParams p,
-                                                                   const SegPlan pl,
-                                                                   const char* recs) {
-  using R = Rec<K, V>;
-  using B = MapBuf<K, V>;
-  static_assert(R::Eg == R::KgT + static_cast<size_t>(K) * C * 2, "e^{gam_last} follows K^T in the record");
-  static_assert(sizeof(B) == static_cast<size_t>(C) * K * 2 + static_cast<size_t>(K) * C * 2 + K * 4, "packed");
-  constexpr int WCOLS = 16 * kMapCT;                                   // columns per wave
-  constexpr int NW = (K + V + kMapWaves * WCOLS - 1) / (kMapWaves * WCOLS);  // workgroups per (item, head)
-  constexpr int kKgtBytes = K * C * 2 + K * 4;
-  __shared__ B buf[2];
-
-  // The NW workgroups of one (item, head) read the same records: indices
-  // equal modulo 8 put them on one XCD.
-  const int bidx = blockIdx.x;
-  const int pair = (bidx / (8 * NW)) * 8 + bidx % 8;
-  const int sub = (bidx / 8) % NW;
+// One workgroup per (map item = a non-final segment of a cut sequence,
+// head), 8 waves. Runs the segment's chunks (all full) from X = [I | 0]
+// (the identity's columns, and zero) with U = 0 for the columns of M and the
+// chunk's U for those of B: X <- e^{gam_last} o X + (K o e^{gam_last-gam})^T
+// ([0 | U] - W X). Wave w owns M's column tile w (w < K / 16) and B's (w <
+// V / 16). No output; the rounding is the state pass's (bf16 X into W X,
+// bf16 V' into the update, fp32 accumulation).
+template <int K, int V, bool EXACT>
+__global__ __launch_bounds__(kThreads, 1) void chunk_map_kernel(const PrefillParams p, const SegPlan pl) {
+  using SM = FusedSmem<K, false, EXACT>;
+  __shared__ SM sm;
   const int H = p.H;
-  if (uniform(pl.counts[3]) == 0) return;
-  const int mi = pair / H, h = pair % H;
-  if (mi >= uniform(pl.counts[1])) return;
-  if (pl.chunk_start[p.num_seqs] > max_chunks_for(p.num_tokens, p.num_seqs)) return;
+  if (uniform(pl.counts[0]) != 0) return;
+  const int mi = static_cast<int>(blockIdx.x) / H, h = static_cast<int>(blockIdx.x) % H;
+  if (mi >= uniform(pl.counts[2])) return;
   const int gs = uniform(pl.map_seg[mi]);
-  const int seq = uniform(pl.seg_seq[gs]);
-  const int seg0 = uniform(pl.seg_start[seq]);
-  const int nseg = uniform(pl.seg_start[seq + 1]) - seg0;
-  const int cbase = uniform(pl.chunk_start[seq]);
-  const int nch_seq = uniform(pl.chunk_start[seq + 1]) - cbase;
-  const int nch = (nch_seq + nseg - 1) / nseg;  // a non-final segment is full length
-  const int c0 = cbase + (gs - seg0) * nch;
-  const int64_t eos = uniform(static_cast<int64_t>(p.cu_seqlens[seq + 1]));
-  if (eos > p.num_tokens) return;
-  const int64_t slot = uniform(static_cast<int64_t>(p.indices[static_cast<int64_t>(seq) * p.index_stride]));
+  const SegRange sr = segment_range(p, pl, gs);
+  const int64_t slot = uniform(static_cast<int64_t>(p.indices[static_cast<int64_t>(sr.seq) * p.index_stride]));
   if (slot < 0) return;  // a null slot carries no state
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
-  const int wave = uniform(w);
+  const int w = uniform(tid >> 6);
   const int m = lane & 15;
   const int g = lane >> 4;
-  const int gcol = sub * kMapWaves * WCOLS + WCOLS * wave;  // this wave's first column of [M | B]
-  const bool active = gcol < K + V;
-  const bool is_m = gcol < K;
-  const int col0 = is_m ? gcol : gcol - K;
+  const bool act[2] = {w < K / 16, w < V / 16};  // the wave's tile of M, of B (wave-uniform)
 
-  f32x4 S[kMapCT][K / 16];
-#pragma unroll
-  for (int ct = 0; ct < kMapCT; ++ct)
-#pragma unroll
-    for (int cb = 0; cb < K / 16; ++cb)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) S[ct][cb][j] = (is_m && 16 * cb + 4 * g + j == col0 + 16 * ct + m) ? 1.f : 0.f;
+  ChunkIn<K, V> in;
+  load_chunk_regs<K, V>(p, h, chunk_pos(sr, 0), in);
+  dma_chunk_tiles<K, false>(p, h, chunk_pos(sr, 0), sm.t.f.k, nullptr);
 
-  auto rec_of = [&](int cc) {
-    return recs + rec_index(h, c0 + cc, p) * static_cast<int64_t>(R::bytes);
-  };
-  auto dma = [&](int cc, B* b) {
-    dma_copy<C * K * 2, kMapThreads>(rec_of(cc) + R::Wn, b->wn, tid, wave);
-    dma_copy<kKgtBytes, kMapThreads>(rec_of(cc) + R::KgT, b->kgt, tid, wave);
-  };
-  f32x4 Upre[kMapCT][4];
-  auto load_u = [&](int cc) {
-    const __amdgpu_buffer_rsrc_t ru = make_rsrc(rec_of(cc) + R::Uf, static_cast<uint32_t>(C * V * 4));
-#pragma unroll
-    for (int ct = 0; ct < kMapCT; ++ct)
-#pragma unroll
-      for (int pb = 0; pb < 4; ++pb)
-        Upre[ct][pb] = buffer_load_f32x4<0>(ru, (((col0 + 16 * ct) / 16) * 64 + lane) * 16, pb * (V / 16) * 64 * 16);
-  };
-  const bool takes_u = active && !is_m;
   // The first map item of a cut sequence copies the slot's initial state
   // (zero without one) for the state pass: its segments then never read the
-  // slot that the last of them writes. The waves with columns of B cover
-  // every value column once.
-  if (takes_u && mi == seg0 - seq) {
-    // Lane l copies 4 consecutive columns of the wave's WCOLS columns in
-    // every 64 / (WCOLS / 4)-th row; every load is issued before the first
-    // store.
+  // slot that the last of them writes. Every load is issued before the
+  // first store.
+  if (mi == sr.seg0 - sr.seq) {
     const int li = uniform(pl.seg_long[gs]);
-    const bool init = p.has_initial_state == nullptr || uniform(static_cast<int32_t>(p.has_initial_state[seq])) != 0;
+    const bool init = p.has_initial_state == nullptr || uniform(static_cast<int32_t>(p.has_initial_state[sr.seq])) != 0;
     const float* src = p.pool + slot * p.slot_stride + static_cast<int64_t>(h) * K * V;
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, init ? static_cast<uint32_t>(K * V * 4) : 0u);
+    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(src, init ? static_cast<uint32_t>(K * V * 4) : 0u);
     const __amdgpu_buffer_rsrc_t rd = make_rsrc(pl.s0 + s0_index(h, li, pl) * K * V, static_cast<uint32_t>(K * V * 4));
-    constexpr int LPR = WCOLS / 4;  // lanes per row
-    constexpr int RPP = 64 / LPR;   // rows per pass
-    static_assert(K % RPP == 0, "whole passes");
-    const int lane_off = ((lane / LPR) * V + col0 + 4 * (lane % LPR)) * 4;
-    f32x4 cp[K / RPP];
+    constexpr int N4 = K * V / 4 / kThreads;  // float4s per thread
+    static_assert(N4 * 4 * kThreads == K * V, "whole float4s");
+    f32x4 cp[N4];
 #pragma unroll
-    for (int i = 0; i < K / RPP; ++i) cp[i] = buffer_load_f32x4<0>(rs, lane_off, i * RPP * V * 4);
+    for (int i = 0; i < N4; ++i) cp[i] = buffer_load_f32x4<0>(rsrc, (i * kThreads + tid) * 16, 0);
 #pragma unroll
-    for (int i = 0; i < K / RPP; ++i) buffer_store_f32x4<0>(cp[i], rd, lane_off, i * RPP * V * 4);
+    for (int i = 0; i < N4; ++i) buffer_store_f32x4<0>(cp[i], rd, (i * kThreads + tid) * 16, 0);
   }
-  dma(0, &buf[0]);
-  if (takes_u) load_u(0);
-  for (int cc = 0; cc < nch; ++cc) {
-    const B& bf = buf[cc & 1];
-    // Chunk cc's copy and U have landed in every wave, every wave's LDS
-    // reads of chunk cc-1's buffer (which the next copy overwrites) are done,
-    // and all waves meet.
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt = 0, expcnt = 7, lgkmcnt = 0
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    f32x4 Vp[kMapCT][4];
+
+  // X[0]: the wave's column tile of M (from the identity), X[1]: of B.
+  f32x4 X[2][K / 16];
 #pragma unroll
-    for (int ct = 0; ct < kMapCT; ++ct)
+  for (int cb = 0; cb < K / 16; ++cb)
 #pragma unroll
-      for (int pb = 0; pb < 4; ++pb) Vp[ct][pb] = is_m ? f32x4{0.f, 0.f, 0.f, 0.f} : Upre[ct][pb];
-    if (cc + 1 < nch) {
-      dma(cc + 1, &buf[(cc + 1) & 1]);
-      if (takes_u) load_u(cc + 1);
+    for (int j = 0; j < 4; ++j) {
+      X[0][cb][j] = (16 * cb + 4 * g + j == 16 * w + m) ? 1.f : 0.f;
+      X[1][cb][j] = 0.f;
     }
-    if (!active) continue;
-    // V' = U - W S over positions.
-    bf16x8 Sh[kMapCT][K / 32];
+  const auto& ops = sm.r.ops;
+  for (int cc = 0; cc < sr.nch; ++cc) {
+    chunk_barrier<0>();
+    f32x4 U[4];
+    const bool more = cc + 1 < sr.nch;
+    const ChunkPos np = chunk_pos(sr, more ? cc + 1 : cc);
+    intra_part<K, V, false, EXACT>(p, h, C, in, more, np, sm, U);
+    if (more) {
+      load_chunk_v_regs<K, V>(p, h, np, in);
+      if constexpr (EXACT) dma_chunk_tiles<K, false>(p, h, np, sm.t.f.k, nullptr);
+    }
+    if (!act[0] && !act[1]) continue;
+    const int m = opaque_tid() & 15, g = (opaque_tid() & 63) >> 4;
+    // V' = [0 | U] - W X over positions.
+    f32x4 Vp[2][4];
 #pragma unroll
-    for (int ct = 0; ct < kMapCT; ++ct)
+    for (int pb = 0; pb < 4; ++pb) {
+      Vp[0][pb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      Vp[1][pb] = U[pb];
+    }
+    bf16x8 Xb[2][K / 32];
 #pragma unroll
-      for (int kb = 0; kb < K / 32; ++kb) Sh[ct][kb] = pack_acc(S[ct][2 * kb], S[ct][2 * kb + 1]);
-    // Fragments are read one position block (or channel block) ahead of the
-    // MFMAs that use them; the scheduling barriers keep that order, so LDS
-    // latency hides behind the previous block's MFMAs.
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int kb = 0; kb < K / 32; ++kb) Xb[x][kb] = pack_acc(X[x][2 * kb], X[x][2 * kb + 1]);
     bf16x8 wf[2][K / 32];
 #pragma unroll
-    for (int kb = 0; kb < K / 32; ++kb) wf[0][kb] = frag<K>(bf.wn, m, 32 * kb + 8 * g);
+    for (int kb = 0; kb < K / 32; ++kb) wf[0][kb] = frag<K>(ops.wn, m, 32 * kb + 8 * g);
 #pragma unroll
     for (int pb = 0; pb < 4; ++pb) {
       __builtin_amdgcn_sched_barrier(0);
       if (pb + 1 < 4) {
 #pragma unroll
-        for (int kb = 0; kb < K / 32; ++kb) wf[(pb + 1) & 1][kb] = frag<K>(bf.wn, 16 * (pb + 1) + m, 32 * kb + 8 * g);
+        for (int kb = 0; kb < K / 32; ++kb) wf[(pb + 1) & 1][kb] = frag<K>(ops.wn, 16 * (pb + 1) + m, 32 * kb + 8 * g);
       }
 #pragma unroll
       for (int kb = 0; kb < K / 32; ++kb)
 #pragma unroll
-        for (int ct = 0; ct < kMapCT; ++ct) Vp[ct][pb] = mfma16(wf[pb & 1][kb], Sh[ct][kb], Vp[ct][pb]);
+        for (int x = 0; x < 2; ++x)
+          if (act[x]) Vp[x][pb] = mfma16(wf[pb & 1][kb], Xb[x][kb], Vp[x][pb]);
     }
     __builtin_amdgcn_sched_barrier(0);
-    bf16x8 Vb[kMapCT][2];
+    bf16x8 Vb[2][2];
 #pragma unroll
-    for (int ct = 0; ct < kMapCT; ++ct) {
-      Vb[ct][0] = pack_acc(Vp[ct][0], Vp[ct][1]);
-      Vb[ct][1] = pack_acc(Vp[ct][2], Vp[ct][3]);
+    for (int x = 0; x < 2; ++x) {
+      Vb[x][0] = pack_acc(Vp[x][0], Vp[x][1]);
+      Vb[x][1] = pack_acc(Vp[x][2], Vp[x][3]);
     }
-    // S <- diag(e^{gam_last}) S + (K o e^{gam_last - gam})^T V'.
-    bf16x8 kf[2][2];
-    f32x4 ef[2];
-    kf[0][0] = frag<C>(bf.kgt, m, 8 * g);
-    kf[0][1] = frag<C>(bf.kgt, m, 32 + 8 * g);
-    ef[0] = *reinterpret_cast<const f32x4*>(&bf.eg[4 * g]);
+    // X <- diag(e^{gam_last}) X + (K o e^{gam_last - gam})^T V'.
 #pragma unroll
     for (int cb = 0; cb < K / 16; ++cb) {
-      __builtin_amdgcn_sched_barrier(0);
-      if (cb + 1 < K / 16) {
-        kf[(cb + 1) & 1][0] = frag<C>(bf.kgt, 16 * (cb + 1) + m, 8 * g);
-        kf[(cb + 1) & 1][1] = frag<C>(bf.kgt, 16 * (cb + 1) + m, 32 + 8 * g);
-        ef[(cb + 1) & 1] = *reinterpret_cast<const f32x4*>(&bf.eg[16 * (cb + 1) + 4 * g]);
-      }
+      const bf16x8 kf0 = frag<C>(ops.kgt, 16 * cb + m, 8 * g);
+      const bf16x8 kf1 = frag<C>(ops.kgt, 16 * cb + m, 32 + 8 * g);
+      const f32x4 e = *reinterpret_cast<const f32x4*>(&ops.eg[16 * cb + 4 * g]);
 #pragma unroll
-      for (int ct = 0; ct < kMapCT; ++ct) {
+      for (int x = 0; x < 2; ++x) {
+        if (!act[x]) continue;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) S[ct][cb][j] *= ef[cb & 1][j];
-        S[ct][cb] = mfma16(kf[cb & 1][0], Vb[ct][0], S[ct][cb]);
-        S[ct][cb] = mfma16(kf[cb & 1][1], Vb[ct][1], S[ct][cb]);
+        for (int j = 0; j < 4; ++j) X[x][cb][j] *= e[j];
+        X[x][cb] = mfma16(kf0, Vb[x][0], X[x][cb]);
+        X[x][cb] = mfma16(kf1, Vb[x][1], X[x][cb]);
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
   }
-  if (!active) return;
-  const int64_t item = map_index(h, mi, pl) * (static_cast<int64_t>(K) * K + static_cast<int64_t>(K) * V);
-  float* dst = pl.maps + item + (is_m ? 0 : K * K);
-  const int ld = is_m ? K : V;
+  float* dst = pl.maps + map_index(h, mi, pl) * (static_cast<int64_t>(K) * K + static_cast<int64_t>(K) * V);
 #pragma unroll
-  for (int ct = 0; ct < kMapCT; ++ct)
+  for (int x = 0; x < 2; ++x) {
+    if (!act[x]) continue;
+    float* d = x == 0 ? dst : dst + K * K;
+    const int ld = x == 0 ? K : V;
 #pragma unroll
     for (int cb = 0; cb < K / 16; ++cb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) dst[(16 * cb + 4 * g + j) * ld + col0 + 16 * ct + m] = S[ct][cb][j];
+      for (int j = 0; j < 4; ++j) d[(16 * cb + 4 * g + j) * ld + 16 * w + m] = X[x][cb][j];
+  }
+}
+
+template <int K, int V, bool EXACT>
+hipError_t launch_kv(const PrefillParams& p, const Layout& L, const SegPlan& pl, hipStream_t stream) {
+  const int64_t state_blocks = L.seg_bound * p.H;
+  const int64_t map_blocks = L.map_bound * p.H;
+  if (state_blocks > 0x7fffffff || map_blocks > 0x7fffffff) return hipErrorInvalidValue;
+  if (map_blocks > 0) {
+    chunk_map_kernel<K, V, EXACT><<<dim3(static_cast<unsigned>(map_blocks)), dim3(kThreads), 0, stream>>>(p, pl);
+    chunk_scan_kernel<K, V><<<dim3(static_cast<unsigned>(L.long_bound * p.H)), dim3(kThreads), 0, stream>>>(p, pl);
+  }
+  chunk_state_kernel<K, V, EXACT><<<dim3(static_cast<unsigned>(state_blocks)), dim3(kThreads), 0, stream>>>(p, pl);
+  return hipGetLastError();
 }
 
 template <int K, int V>
-hipError_t launch_kv(const PrefillParams& p, const Layout& L, const SegPlan& pl, uint8_t* exact_flags,
-                     char* recs, hipStream_t stream, hipEvent_t after_intra) {
-  const int64_t maxc = max_chunks_for(p.num_tokens, p.num_seqs);
-  const int64_t intra_blocks = maxc * p.H;
-  const int64_t seg_pairs = L.seg_bound * p.H;
-  const int64_t state_blocks = (V / 64 == 2) ? (seg_pairs + 7) / 8 * 16 : seg_pairs;
-  const int64_t map_blocks = (L.map_bound * p.H + 7) / 8 * 8 * ((K + V + 16 * kMapCT * kMapWaves - 1) / (16 * kMapCT * kMapWaves));
-  if (intra_blocks > 0x7fffffff || state_blocks > 0x7fffffff || map_blocks > 0x7fffffff)
-    return hipErrorInvalidValue;
-  chunk_intra_kernel<K, V><<<dim3(static_cast<unsigned>(intra_blocks)), dim3(kThreads), 0, stream>>>(
-      p, pl.chunk_info, recs, exact_flags);
-  // With a lower bound lb every per-token log-decay lies in [lb, 0], so a
-  // 16-row block decays by at most 15 |lb| and the factored kernel takes
-  // every chunk once 15 |lb| <= kMaxBlockDecay: the exact kernel would only
-  // read its flags and return.
-  const bool all_factored = p.has_lb != 0 && 15.f * -p.lower_bound <= kMaxBlockDecay - 1.f;
-  if (!all_factored)
-    chunk_intra_exact_kernel<K, V><<<dim3(static_cast<unsigned>(intra_blocks)), dim3(kThreads), 0, stream>>>(
-        p, pl.chunk_info, recs, exact_flags);
-  if (after_intra != nullptr) {
-    const hipError_t e = hipEventRecord(after_intra, stream);
-    if (e != hipSuccess) return e;
-  }
-  if (L.map_bound > 0) {
-    chunk_map_kernel<K, V><<<dim3(static_cast<unsigned>(map_blocks)), dim3(kMapThreads), 0, stream>>>(p, pl, recs);
-  }
-  // Every sequence is at least one segment: with enough of them for two
-  // state workgroups per CU, one record buffer per workgroup lets two share
-  // a CU.
-  if (static_cast<int64_t>(p.num_seqs) * p.H * (V / 64) >= 2 * kChipSlots)
-    chunk_state_kernel<K, V, 1><<<dim3(static_cast<unsigned>(state_blocks)), dim3(kThreads), 0, stream>>>(
-        p, pl, recs);
-  else
-    chunk_state_kernel<K, V, 2><<<dim3(static_cast<unsigned>(state_blocks)), dim3(kThreads), 0, stream>>>(
-        p, pl, recs);
-  return hipGetLastError();
+hipError_t launch_k(const PrefillParams& p, const Layout& L, const SegPlan& pl, hipStream_t stream) {
+  // With a lower bound lb every per-token log-decay lies in (lb, 0), so a
+  // block's factors (over its 16 rows from the gam just before it) span
+  // less than 16 |lb| and every chunk takes the factored path once
+  // 16 |lb| <= kMaxBlockDecay: the kernels without the exact path (less LDS)
+  // then suffice.
+  const bool all_factored = p.has_lb != 0 && 16.f * -p.lower_bound <= kMaxBlockDecay;
+  return all_factored ? launch_kv<K, V, false>(p, L, pl, stream) : launch_kv<K, V, true>(p, L, pl, stream);
 }
 
 }  // namespace
@@ -2069,38 +1777,36 @@ size_t prefill_workspace_bytes(int32_t num_seqs, int64_t num_tokens, int32_t H, 
   return layout_for(num_seqs, num_tokens, H, K, V).total;
 }
 
-hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream, hipEvent_t after_intra) {
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream, hipEvent_t after_plan) {
   const Layout L = layout_for(p.num_seqs, p.num_tokens, p.H, p.K, p.V);
   if (L.seg_bound > 0x7fffffff) return hipErrorInvalidValue;
   char* ws = static_cast<char*>(p.workspace);
   SegPlan pl;
+  pl.counts = reinterpret_cast<int32_t*>(ws + L.counts);
   pl.chunk_start = reinterpret_cast<int32_t*>(ws + L.chunk_start);
   pl.seg_start = reinterpret_cast<int32_t*>(ws + L.seg_start);
-  pl.counts = reinterpret_cast<int32_t*>(ws + L.counts);
   pl.seg_seq = reinterpret_cast<int32_t*>(ws + L.seg_seq);
   pl.seg_long = reinterpret_cast<int32_t*>(ws + L.seg_long);
   pl.map_seg = reinterpret_cast<int32_t*>(ws + L.map_seg);
+  pl.long_seq = reinterpret_cast<int32_t*>(ws + L.long_seq);
   pl.maps = reinterpret_cast<float*>(ws + L.maps);
   pl.s0 = reinterpret_cast<float*>(ws + L.s0);
   pl.seg_bound = static_cast<int32_t>(L.seg_bound);
   pl.map_bound = static_cast<int32_t>(L.map_bound);
   pl.long_bound = static_cast<int32_t>(L.long_bound);
   pl.max_segs = static_cast<int32_t>(L.max_segs);
-  pl.fill_units = static_cast<int32_t>(L.fill_units);
-  pl.chunk_info = reinterpret_cast<int4*>(ws + L.chunk_info);
-  pl.max_chunks = static_cast<int32_t>(max_chunks_for(p.num_tokens, p.num_seqs));
   pl.num_tokens = static_cast<int32_t>(p.num_tokens);
-  uint8_t* flags = reinterpret_cast<uint8_t*>(ws + L.flags);
-  char* recs = ws + L.recs;
-  plan_kernel<<<1, kThreads, 0, stream>>>(p.cu_seqlens, p.num_seqs, pl);
+  plan_kernel<<<1, kPlanThreads, 0, stream>>>(p.cu_seqlens, p.num_seqs, p.H, pl);
+  if (after_plan != nullptr) {
+    const hipError_t e = hipEventRecord(after_plan, stream);
+    if (e != hipSuccess) return e;
+  }
   hipError_t e;
-  if (p.K == 64 && p.V == 64) e = launch_kv<64, 64>(p, L, pl, flags, recs, stream, after_intra);
-  else if (p.K == 64 && p.V == 128) e = launch_kv<64, 128>(p, L, pl, flags, recs, stream, after_intra);
-  else if (p.K == 128 && p.V == 64) e = launch_kv<128, 64>(p, L, pl, flags, recs, stream, after_intra);
-  else e = launch_kv<128, 128>(p, L, pl, flags, recs, stream, after_intra);
-  // Output epilogue: a head's columns are spread over the state pass's waves
-  // (and, at V = 128, over two workgroups), so the norm is a pass over the
-  // output.
+  if (p.K == 64 && p.V == 64) e = launch_k<64, 64>(p, L, pl, stream);
+  else if (p.K == 64 && p.V == 128) e = launch_k<64, 128>(p, L, pl, stream);
+  else if (p.K == 128 && p.V == 64) e = launch_k<128, 64>(p, L, pl, stream);
+  else e = launch_k<128, 128>(p, L, pl, stream);
+  // Output epilogue: applied as a pass over the output.
   if (e != hipSuccess || p.norm.gate == nullptr) return e;
   return launch_gated_rmsnorm(p.norm, p.out, p.num_tokens, p.H, p.V, stream);
 }

@@ -110,8 +110,8 @@ struct PrefillParams {
 
 size_t prefill_workspace_bytes(int32_t num_seqs, int64_t num_tokens, int32_t H,
                                int32_t K, int32_t V);
-// after_intra (optional) is recorded on the stream once the intra-chunk
-// kernels are launched, before the map and state passes.
-hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream, hipEvent_t after_intra = nullptr);
+// after_plan (optional) is recorded on the stream once the plan kernel is
+// launched, before the map and state passes.
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream, hipEvent_t after_plan = nullptr);
 
 }  // namespace kda

@@ -22,15 +22,19 @@
  * Conventions for every entry point:
  *  - All data pointers are DEVICE pointers owned by the caller. Inputs are only
  *    read, the state pool is read and written in place, outputs are written.
- *  - No call allocates or frees memory, synchronises the host, or reads device
- *    memory from the host; every launch goes on `stream` (NULL = the default
- *    stream). Calls can therefore be captured in a HIP graph.
+ *  - No computing call allocates or frees memory, synchronises the host, or
+ *    reads device memory from the host; every launch goes on `stream` (NULL =
+ *    the default stream). Calls can therefore be captured in a HIP graph. (Only
+ *    kda_overlap_create and kda_overlap_destroy, which manage a caller-owned
+ *    handle, create or free anything.)
  *  - Arguments are validated on the host before anything is launched. On any
  *    failed check nothing is launched, the call returns a non-zero status, and
  *    kda_last_error() lists every failed check (not just the first).
- *  - Device-side values are the caller's guarantee and are not checked: slot
- *    numbers must be < num_slots, slots must be unique within one call, and
- *    cu_seqlens must start at 0, be non-decreasing and end at num_tokens.
+ *  - Device-side values are the caller's guarantee: slot numbers must be
+ *    < num_slots and unique within one call (not checked), and cu_seqlens
+ *    must start at 0, be non-decreasing and end at num_tokens (checked on the
+ *    device by the prefill, which then writes NaN rows and sets its status
+ *    word instead of computing).
  *  - bf16 outputs are rounded to nearest even; the state stays fp32.
  *  - Supported head dims: K, V in {64, 128}. Layout alignment: mixed_qkv, raw_g,
  *    out and the pool must be 16-byte aligned, qkv_row_stride a multiple of 8
@@ -159,6 +163,10 @@ kda_status_t kda_spec_decode(int32_t num_seqs, int32_t tokens_per_seq,
                              const kda_out_norm_t* norm, void* out,
                              hipStream_t stream);
 
+/* Value of a prefill call's status word (workspace offset 0) when its
+ * cu_seqlens break the contract. */
+#define KDA_PREFILL_BAD_CU_SEQLENS 1
+
 /* Bytes of device workspace kda_chunk_prefill needs for these sizes (a pure
  * host computation; returns 0 for invalid sizes). */
 size_t kda_chunk_prefill_workspace_size(int32_t num_seqs, int64_t num_tokens,
@@ -178,7 +186,11 @@ size_t kda_chunk_prefill_workspace_size(int32_t num_seqs, int64_t num_tokens,
  * Row formats and norm as for kda_decode_packed; out is bf16 [num_tokens][H][V].
  * workspace: device scratch of at least kda_chunk_prefill_workspace_size()
  * bytes, 256-byte aligned, owned by the caller; its contents are not needed
- * before or after the call.
+ * before the call. After the call (in stream order) the int32 at workspace
+ * offset 0 is a status word: 0 when cu_seqlens kept to the contract
+ * (cu_seqlens[0] == 0, non-decreasing, cu_seqlens[num_seqs] == num_tokens),
+ * else KDA_PREFILL_BAD_CU_SEQLENS; in that case every output row of the call
+ * is set to NaN and no state slot is read or written.
  * Errors: KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE,
  * KDA_ERR_HIP.
  */
@@ -229,6 +241,20 @@ size_t kda_mixed_batch_workspace_size(int32_t num_decodes, int32_t num_prefills,
                                       int32_t K, int32_t V);
 
 /*
+ * Overlap resources of kda_mixed_batch, created and owned by the caller: a
+ * side stream (default priority, non-blocking) and two events on the device
+ * current at creation. kda_overlap_create allocates them, so call it once,
+ * outside graph capture, and keep the handle; kda_overlap_destroy frees them
+ * (NULL is a no-op). A handle serves one call at a time: callers that issue
+ * mixed batches concurrently (several host threads, or a capture beside
+ * eager calls) each need their own.
+ * Errors: KDA_ERR_INVALID_ARGUMENT (NULL out pointer), KDA_ERR_HIP.
+ */
+typedef struct kda_overlap_s* kda_overlap_t;
+kda_status_t kda_overlap_create(kda_overlap_t* overlap);
+kda_status_t kda_overlap_destroy(kda_overlap_t overlap);
+
+/*
  * Mixed decode + prefill batch in one call (vLLM PR #50649, Purpose: the
  * decode rows of a mixed non-speculative batch go to the recurrent kernel,
  * never to the chunk kernel, which returned NaN for them).
@@ -240,17 +266,15 @@ size_t kda_mixed_batch_workspace_size(int32_t num_decodes, int32_t num_prefills,
  * indices[(num_decodes+i)*index_stride] and has_initial_state[i] (NULL = all
  * 1). Decode rows go to the recurrent decode kernel, prefill rows to the chunk
  * pipeline, with no host synchronisation. The call is ordered on `stream` as
- * a whole; when it has both kinds of rows, the decode kernel runs on a
- * library-owned side stream (one per device, created with two events on the
- * device's first such call and kept until the process ends) that is forked
- * from `stream` after the prefill's intra-chunk kernels and joined back
- * before the call's work on `stream` ends, so it overlaps the prefill's
- * state pass. A capture of `stream` captures both branches; make the first
- * such call on a device outside capture, since it creates the side stream.
- * Calls on one device from several host threads are serialised while they
- * enqueue. out is bf16
+ * a whole. With overlap == NULL both parts run on `stream`. With a handle from
+ * kda_overlap_create (same device as `stream`, else KDA_ERR_INVALID_ARGUMENT)
+ * and both kinds of rows, the decode kernel runs on the handle's side stream,
+ * forked from `stream` after the prefill's plan kernel and joined back before
+ * the call's work on `stream` ends, so it shares the chip with the prefill's
+ * chunk passes; a capture of `stream` captures both branches. out is bf16
  * [num_decodes+num_prefill_tokens][H][V]; norm (optional) as for
- * kda_decode_packed, its gate rows paired with the output rows.
+ * kda_decode_packed, its gate rows paired with the output rows; the
+ * workspace's status word as for kda_chunk_prefill.
  * Errors: as kda_chunk_prefill.
  */
 kda_status_t kda_mixed_batch(int32_t num_decodes, int32_t num_prefills,
@@ -263,7 +287,7 @@ kda_status_t kda_mixed_batch(int32_t num_decodes, int32_t num_prefills,
                              const kda_gate_t* gate, const kda_state_t* state,
                              const kda_out_norm_t* norm, void* out,
                              void* workspace, size_t workspace_bytes,
-                             hipStream_t stream);
+                             kda_overlap_t overlap, hipStream_t stream);
 
 /* Short causal conv prologue (vLLM PR #60683, Purpose: in the decode
  * kernels a conv step precedes the KDA recurrence; the page prints no

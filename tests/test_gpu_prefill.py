@@ -240,10 +240,11 @@ def test_prefill_split_equals_whole():
 
 
 def test_mixed_batches_from_two_host_threads():
-    """The router runs a batch's decode rows on a side stream forked from the
-    caller's stream and joined back. Two host threads, each on its own
-    stream with its own pool, call it repeatedly at the same time; every
-    output and final state must still match the oracle."""
+    """With an overlap handle the router runs a batch's decode rows on the
+    handle's side stream, forked from the caller's stream after the plan and
+    joined back. Two host threads, each on its own stream with its own pool
+    and its own handle, call it repeatedly at the same time; every output and
+    final state must still match the oracle."""
     import threading
 
     cases = [W.mixed_case(f"threads_{n}", 4, 128, 128, 7, [90, 1, 40], 16, -5.0, seed=671 + n)
@@ -256,6 +257,7 @@ def test_mixed_batches_from_two_host_threads():
         try:
             c = cases[n]
             s = torch.cuda.Stream()
+            ov = kda.Overlap()
             with torch.cuda.stream(s):
                 outs = []
                 for _ in range(4):
@@ -263,9 +265,10 @@ def test_mixed_batches_from_two_host_threads():
                     i = dc.inputs
                     o, _ = kda.kda_mixed_batch(i["mixed_qkv"], i["raw_g"], i["raw_beta"], i["A_log"],
                                                i["dt_bias"], -5.0, dc.pool, dc.state_indices,
-                                               c.num_decodes, dc.cu_seqlens)
+                                               c.num_decodes, dc.cu_seqlens, overlap=ov)
                     outs.append((o, dc))
                 s.synchronize()
+            ov.close()
             results[n] = outs
         except Exception as exc:  # reported on the main thread
             errors.append(repr(exc))

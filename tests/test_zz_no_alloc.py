@@ -61,14 +61,24 @@ def test_noalloc_prefill_matches_workspace_prefill_twice():
 
 
 def test_noalloc_prefill_rejects_sizes_beyond_the_scratch():
-    H, K, V, T = 32, 128, 128, 8192
-    need = kda.kda_chunk_prefill_workspace_size(1, T, H, K, V)
+    # Two 8192-token sequences at H = 32 need more segment maps than the
+    # scratch holds; the call is refused on the host, so the inputs' values
+    # do not matter.
+    H, K, V, T = 32, 128, 128, 16384
+    need = kda.kda_chunk_prefill_workspace_size(2, T, H, K, V)
     assert need > kda.NOALLOC_SCRATCH_BYTES
-    case = W.prefill_case("noalloc_too_big", H, K, V, [T], 2, -5.0, seed=803)
-    dc = to_device(case)
-    before = dc.pool.clone()
+    dev = torch.device("cuda")
+    qkv = torch.zeros(T, 2 * H * K + H * V, dtype=torch.bfloat16, device=dev)
+    raw_g = torch.zeros(T, H * K, dtype=torch.bfloat16, device=dev)
+    raw_beta = torch.zeros(T, H, dtype=torch.bfloat16, device=dev)
+    A_log = torch.zeros(H, device=dev)
+    dt_bias = torch.zeros(H * K, device=dev)
+    pool = torch.ones(2, H, K, V, device=dev)
+    idx = torch.tensor([0, 1], dtype=torch.int32, device=dev)
+    cu = torch.tensor([0, 8192, T], dtype=torch.int32, device=dev)
     with pytest.raises(kda.KdaError) as ei:
-        _call(kda.kda_chunk_prefill_noalloc, dc)
+        kda.kda_chunk_prefill_noalloc(qkv, raw_g, raw_beta, A_log, dt_bias, -5.0, pool, idx, cu)
+    torch.cuda.synchronize()
     assert ei.value.status == 3 and any("static scratch" in r for r in ei.value.reasons)
-    assert torch.equal(dc.pool, before)
-    log("[case] no-alloc: an 8192-token call at H=32 is rejected before any launch")
+    assert bool((pool == 1).all())
+    log(f"[case] no-alloc: two 8192-token sequences at H=32 ({need} B of workspace) are rejected before any launch")
