@@ -156,7 +156,50 @@ __device__ __forceinline__ int sw32(int t, int c) {
 __device__ __forceinline__ int opaque_tid() {
   int t = threadIdx.x;
   asm volatile("" : "+v"(t));
+  // The range survives, so divisions and remainders by powers of two stay
+  // single shifts and masks.
+  __builtin_assume(t >= 0 && t < kThreads);
   return t;
+}
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// The words of the buffer resource make_rsrc builds, for the LDS copies
+// below (wave-uniform: scalar registers).
+__device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return u32x4{static_cast<uint32_t>(uniform(static_cast<int32_t>(a))),
+               static_cast<uint32_t>(uniform(static_cast<int32_t>(a >> 32))) & 0xffffu,
+               static_cast<uint32_t>(uniform(static_cast<int32_t>(bytes))), 0x00020000u};
+}
+
+// Buffer-to-LDS copy of one 16-byte piece per lane: lane l's piece at byte
+// offset voff + soff of the buffer lands at LDS byte lds_wave + 16 l
+// (lds_wave and soff the same in every lane); offsets past the buffer's
+// range land as zeros. The
+// compiler is not told that this writes LDS: with the builtin form it makes
+// the next LDS access of the wave wait until the copy has landed (it cannot
+// tell the copy's tile from the others), which would serialise every
+// prefetch. Each caller instead waits for its copies explicitly (vmcnt)
+// before a barrier, ahead of any read of the tile, and issues them only
+// after a barrier that ends every read of the tile's previous contents. M0
+// is restored, so the compiler's own uses of it are unaffected.
+__device__ __forceinline__ void lds_copy16(u32x4 rsrc, uint32_t lds_wave, int voff, uint32_t soff = 0) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_wave), "v"(voff), "s"(rsrc), "s"(soff)
+      : "memory");
+}
+
+// LDS byte address of a shared-memory pointer, read from lane 0.
+__device__ __forceinline__ uint32_t lds_addr(const void* ptr) {
+  return static_cast<uint32_t>(uniform(static_cast<int32_t>(reinterpret_cast<uintptr_t>(ptr))));
 }
 
 // Waits until this wave's outstanding vector-memory operations (including
@@ -213,8 +256,9 @@ struct SegPlan {
   int32_t* seg_long;     // [seg_bound] index of a cut sequence among the cut ones, else -1
   int32_t* map_seg;      // [map_bound] segment of each map item (a non-final segment)
   int32_t* long_seq;     // [long_bound] sequence of each cut sequence
-  float* maps;           // [H][map_bound]: M (fp32 [K][K]) then B (fp32 [K][V]); after the
-                         // scan pass, B of map item j holds the initial state of segment j + 1
+  float* maps;           // [H][map_bound]: M (as the scan's bf16 hi and lo A fragments, the
+                         // size of fp32 [K][K]) then B (fp32 [K][V]); after the scan pass, B
+                         // of map item j holds the initial state of segment j + 1
   float* s0;             // [H][long_bound]: fp32 [K][V] initial state of each cut sequence
   int32_t seg_bound, map_bound, long_bound;
   int32_t max_segs;      // segments per sequence at most (host bound)
@@ -397,7 +441,8 @@ struct XLayout {
   static constexpr int cij = tot + NP * K;                   // [10][K] e^{rho_I - rho_J}, J <= I
   static constexpr int drange = cij + 10 * K;                // [4] largest decay over a block (rho_I - gam(16 I + 15))
   static constexpr int beta = drange + 16;                   // [C] beta per position
-  static constexpr int end = beta + C;
+  static constexpr int gconst = beta + C;                    // [K] dt_bias, then e^{A_log} (fixed per head)
+  static constexpr int end = gconst + K + 4;
 };
 
 // Factor pairs (I, J), J <= I, in the order of x.cij: pair pr = I (I+1)/2 + J.
@@ -448,6 +493,9 @@ struct FusedSmem {
     if constexpr (EXACT) return t.wkt;
     else return wkt_own;
   }
+  // bf16 T diag(beta), [C][C] (rec_elem<C>), for the W and U products: built
+  // after A/P over K o F (or gam), which A/P was the last to read.
+  __device__ uint16_t* tf() { return t.f.kf; }
 };
 
 // One chunk's register-held inputs, loaded a chunk ahead.
@@ -455,8 +503,8 @@ template <int K, int V>
 struct ChunkIn {
   static constexpr int PP = Roles<K>::PP;
   u32x2 rgw[PP];                      // raw_g of the thread's 4 channels at its PP positions
-  uint16_t rb;                        // raw beta of position tid
-  uint16_t vpre[2][8];                // v operands of U (waves w < V / 16): lane (m, g) needs
+  uint32_t rb;                        // raw beta (bf16 bits, zero-extended) of position tid
+  uint32_t vpre[2][8];                // v operands of U (waves w < V / 16, zero-extended): lane (m, g) needs
                                       // v[32 kb + 8 g + j][16 w + m]
 };
 
@@ -501,6 +549,40 @@ __device__ __forceinline__ void load_chunk_v_regs(const PrefillParams& p, int h,
   }
 }
 
+// Makes the registers of a tile array look freshly written (waiting for
+// any loads into them to land, here).
+template <int N>
+__device__ __forceinline__ void pin_regs(f32x4 (&a)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(a[i][j]));
+}
+
+// Holds the v operands as the 16 registers their loads write, late in a
+// chunk: without this the compiler pairs them into bf16x2 right after the
+// loads, which makes the wave wait there for the loads to land.
+template <int K, int V>
+__device__ __forceinline__ void pin_v_regs(ChunkIn<K, V>& in) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) asm volatile("" : "+v"(in.vpre[kb][j]));
+}
+
+// The same for the gate inputs (raw_g, raw beta), so that the next gate
+// scan does not wait on whatever memory operations precede it.
+template <int K, int V>
+__device__ __forceinline__ void pin_gate_regs(ChunkIn<K, V>& in) {
+#pragma unroll
+  for (int i = 0; i < Roles<K>::PP; ++i) {
+    uint32_t a = in.rgw[i][0], b = in.rgw[i][1];
+    asm volatile("" : "+v"(a), "+v"(b));
+    in.rgw[i] = u32x2{a, b};
+  }
+  asm volatile("" : "+v"(in.rb));
+}
+
 // All register loads of chunk (t0, n).
 template <int K, int V>
 __device__ __forceinline__ void load_chunk_regs(const PrefillParams& p, int h, ChunkPos cp, ChunkIn<K, V>& in) {
@@ -517,7 +599,7 @@ __device__ __forceinline__ void dma_chunk_tiles(const PrefillParams& p, int h, C
   using Ro = Roles<K>;
   const int tid = opaque_tid();
   const int64_t rs = p.qkv_row_stride * 2;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.qkv + cp.t0 * p.qkv_row_stride, static_cast<uint32_t>(cp.n * rs));
+  const u32x4 rq = rsrc_words(p.qkv + cp.t0 * p.qkv_row_stride, static_cast<uint32_t>(cp.n * rs));
   constexpr int KPM = (Ro::KP8 > 16 ? 16 : Ro::KP8) - 1;
   static_assert((C * Ro::KP8) % kThreads == 0, "whole DMA rounds");
 #pragma unroll
@@ -527,10 +609,18 @@ __device__ __forceinline__ void dma_chunk_tiles(const PrefillParams& p, int h, C
     const int pl = (ps % Ro::KP8) ^ (t & KPM);  // logical piece stored there
     const int slot = r * kThreads + (tid & ~63);
     const int qoff = static_cast<int>(t * rs) + (h * K + pl * 8) * 2;
-    if constexpr (Q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, reinterpret_cast<uint4*>(q_lds) + slot, 16, qoff, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, reinterpret_cast<uint4*>(k_lds) + slot, 16, qoff + p.H * K * 2, 0, 0, 0);
+    if constexpr (Q) lds_copy16(rq, lds_addr(reinterpret_cast<uint4*>(q_lds) + slot), qoff);
+    lds_copy16(rq, lds_addr(reinterpret_cast<uint4*>(k_lds) + slot), qoff + p.H * K * 2);
   }
+}
+
+// The head's gate constants (dt_bias per channel, then e^{A_log}) into
+// x.gconst, once per workgroup, ahead of the first barrier of the chunk loop.
+template <int K>
+__device__ __forceinline__ void stage_gate_consts(const PrefillParams& p, int h, float* x) {
+  const int tid = threadIdx.x;
+  if (tid < K) x[XLayout<K>::gconst + tid] = p.dt_bias[h * K + tid];
+  if (tid == K) x[XLayout<K>::gconst + K] = __expf(p.A_log[h]);
 }
 
 // Gate and cumulative log-decay of the chunk, in registers: gm[i][j] = gam
@@ -541,7 +631,7 @@ __device__ __forceinline__ void dma_chunk_tiles(const PrefillParams& p, int h, C
 // (the same value in every thread). Only the partial totals are exchanged
 // (one barrier); the other outputs become visible at the next barrier.
 template <int K, int V, bool Q, bool EXACT>
-__device__ __forceinline__ bool gate_scan(const PrefillParams& p, int h, int n, const ChunkIn<K, V>& in,
+__device__ __forceinline__ bool gate_scan(const PrefillParams& p, int n, const ChunkIn<K, V>& in,
                                           FusedSmem<K, Q, EXACT>& sm, float (&gm)[Roles<K>::PP][4],
                                           float (&gl)[4], float (&rho)[4]) {
   using Ro = Roles<K>;
@@ -552,11 +642,9 @@ __device__ __forceinline__ bool gate_scan(const PrefillParams& p, int h, int n, 
   const int q4 = tid % NQ, part = tid / NQ;
   const int c4 = 4 * q4;
   float* x = sm.x;
-  const float a_h = __expf(p.A_log[h]);
-  float dtb[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) dtb[j] = p.dt_bias[h * K + c4 + j];
-  const float beta_t = (tid < n) ? sigmoid_f32(bf16_to_f32(in.rb)) : 0.f;
+  const float a_h = x[XL::gconst + K];
+  const f32x4 dtb = *reinterpret_cast<const f32x4*>(&x[XL::gconst + c4]);
+  const float beta_t = (tid < n) ? sigmoid_f32(bf16_to_f32(static_cast<uint16_t>(in.rb))) : 0.f;
   const bool has_lb = p.has_lb != 0;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -683,6 +771,41 @@ __device__ __forceinline__ void diag_inverse(float* at, int blk, int lane) {
   }
 }
 
+// 16x16x16 fp32 product on the 16x16x4 MFMA: a = X^T and b = Y in
+// accumulator form (lane (m, g) element j holds row 4 g + j of column m)
+// give X Y in accumulator form. Step kk pairs lane group g with contraction
+// index 4 g + kk, so an accumulator tile is a B operand as it stands and the
+// accumulator form of X^T is the A operand of X.
+__device__ __forceinline__ f32x4 mm16(const f32x4& a, const f32x4& b) {
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) acc = mfma4(a[kk], b[kk], acc);
+  return acc;
+}
+
+// s I + x for a 16x16 tile x in accumulator form.
+__device__ __forceinline__ f32x4 add_identity(f32x4 x, float s, int m, int g) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (4 * g + j == m) x[j] += s;
+  return x;
+}
+
+// (I + N)^{-1} of a strictly lower triangular 16x16 block N, from N and N^T
+// in accumulator form. N is nilpotent (N^16 = 0), so the Neumann series
+// stops and factors into
+//   (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8),
+// five levels of fp32 MFMA products instead of a 16-step substitution.
+__device__ __forceinline__ f32x4 unit_lower_inverse(const f32x4& n, const f32x4& nt, int m, int g) {
+  const f32x4 n2 = mm16(nt, n), n2t = mm16(n, nt);
+  // ((I - N)(I + N^2))^T = (I + N^2)^T (I - N)^T
+  const f32x4 w1t = mm16(add_identity(n2, 1.f, m, g), add_identity(-nt, 1.f, m, g));
+  const f32x4 n4 = mm16(n2t, n2), n4t = mm16(n2, n2t);
+  const f32x4 n8 = mm16(n4t, n4);
+  const f32x4 y = mm16(add_identity(n4t, 1.f, m, g), add_identity(n8, 1.f, m, g));  // (I + N^4)(I + N^8)
+  return mm16(w1t, y);
+}
+
 // Zero P blocks above the diagonal that the state step reads: rows 0..15 x
 // cols 16..31 and rows 32..47 x cols 48..63.
 template <int K, bool Q>
@@ -698,10 +821,10 @@ __device__ __forceinline__ void zero_p_blocks(ChunkOps<K, Q>& ops, int m, int g)
 // pass writes K o R, Q o R and K o F tiles, scale Q o e^gam and
 // (K o e^{gam_last - gam})^T; A and P then run on bf16 MFMA from the tiles.
 // Waves 0..3 take the diagonal blocks and invert theirs in (I + A) at once
-// (forward substitution), waves 4..7 the off-diagonal blocks. Leaves A^T
-// (times beta) strictly above the diagonal of at and the diagonal blocks of
-// T below it, scale P in ops.pm, and K o e^gam of the thread's elements in
-// wkp; ends with the workgroup met.
+// (in registers, unit_lower_inverse), waves 4..7 the off-diagonal blocks.
+// Leaves A^T (times beta) of the off-diagonal blocks strictly above the
+// diagonal of at and the diagonal blocks of T below it, scale P in ops.pm,
+// and K o e^gam of the thread's elements in wkp; ends with the workgroup met.
 template <int K, int V, bool Q, bool EXACT>
 __device__ __forceinline__ void intra_factored(const PrefillParams& p, FusedSmem<K, Q, EXACT>& sm,
                                                const float (&gm)[Roles<K>::PP][4], const float (&gl)[4],
@@ -781,9 +904,11 @@ __device__ __forceinline__ void intra_factored(const PrefillParams& p, FusedSmem
   lds_barrier();
   // ---- A and P over all channels ----------------------------------------
   // Block (I, J): lane (m, g) holds rows 16 I + 4 g + j of column 16 J + m.
-  auto ap_block = [&](int I, int J, f32x4& dA, f32x4& dPt) {
+  // On a diagonal block (I == J) also A^T (dAt), for the inverse.
+  auto ap_block = [&](int I, int J, f32x4& dA, f32x4& dPt, f32x4& dAt) {
     dA = f32x4{0.f, 0.f, 0.f, 0.f};
     dPt = f32x4{0.f, 0.f, 0.f, 0.f};
+    dAt = f32x4{0.f, 0.f, 0.f, 0.f};
     const float* cv = x + XL::cij + (I * (I + 1) / 2 + J) * K;
 #pragma unroll
     for (int kb = 0; kb < K / 32; ++kb) {
@@ -799,20 +924,24 @@ __device__ __forceinline__ void intra_factored(const PrefillParams& p, FusedSmem
         b = to_bf16x8(sc);
       }
       dA = mfma16(ak, b, dA);
+      if (I == J) dAt = mfma16(b, ak, dAt);  // wave-uniform
       if constexpr (Q) {
         const bf16x8 aq = lds_frag(&sm.t.f.q[sw16<K>(16 * I + m, c0)]);
         dPt = mfma16(b, aq, dPt);
       }
     }
   };
-  // A^T (times beta) into at, scale P into ops.pm.
-  auto store_block = [&](int I, int J, const f32x4& dA, const f32x4& dPt) {
+  // A^T (times beta) of an off-diagonal block into at.
+  auto store_a = [&](int I, int J, const f32x4& dA) {
     const int s2 = 16 * J + m;
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const int row = 16 * I + 4 * g + jj;
-      if (s2 < row) sm.at[sw32<C>(s2, row)] = x[XL::beta + row] * dA[jj];
+      sm.at[sw32<C>(s2, row)] = x[XL::beta + row] * dA[jj];
     }
+  };
+  // Scale P into ops.pm.
+  auto store_p = [&](int I, int J, const f32x4& dPt) {
     if constexpr (Q) {
       const int prow = 16 * I + m;
       float pv[4];
@@ -823,23 +952,33 @@ __device__ __forceinline__ void intra_factored(const PrefillParams& p, FusedSmem
     }
   };
   if (w < 4) {
-    f32x4 dA, dPt;
-    ap_block(w, w, dA, dPt);
-    store_block(w, w, dA, dPt);
-    // The block's A^T entries were written by this wave's own lanes: LDS
-    // operations of one wave complete in order, so no barrier is needed.
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt = 0
-    __builtin_amdgcn_wave_barrier();
-    diag_inverse(sm.at, w, lane);
+    // Diagonal block: N = diag(beta) A below the diagonal, inverted in
+    // registers; T_II goes strictly below the diagonal of at.
+    f32x4 dA, dPt, dAt;
+    ap_block(w, w, dA, dPt, dAt);
+    store_p(w, w, dPt);
+    const float beta_m = x[XL::beta + 16 * w + m];
+    const f32x4 beta_r = *reinterpret_cast<const f32x4*>(&x[XL::beta + 16 * w + 4 * g]);
+    f32x4 n, nt;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      n[jj] = m < 4 * g + jj ? beta_r[jj] * dA[jj] : 0.f;   // N[4 g + jj][m]
+      nt[jj] = 4 * g + jj < m ? beta_m * dAt[jj] : 0.f;     // N[m][4 g + jj]
+    }
+    const f32x4 tb = unit_lower_inverse(n, nt, m, g);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+      if (4 * g + jj > m) sm.at[sw32<C>(16 * w + 4 * g + jj, 16 * w + m)] = tb[jj];
   } else {
 #pragma unroll
     for (int bi = 0; bi < 2; ++bi) {
       int I, J;
       offdiag_block(w, bi, I, J);
       if (I >= 0) {  // wave-uniform
-        f32x4 dA, dPt;
-        ap_block(I, J, dA, dPt);
-        store_block(I, J, dA, dPt);
+        f32x4 dA, dPt, dAt;
+        ap_block(I, J, dA, dPt, dAt);
+        store_a(I, J, dA);
+        store_p(I, J, dPt);
       }
     }
     if constexpr (Q) {
@@ -1061,8 +1200,9 @@ __device__ __forceinline__ void intra_exact(const PrefillParams& p, FusedSmem<K,
   lds_barrier();  // A^T complete; the tiles and gam are no longer read
 }
 
-// The rest of T = (I + A)^{-1} in at (its diagonal blocks are there
-// already), then W = T diag(beta)(K o e^gam) (as -W into ops.wn) and
+// The rest of T = (I + A)^{-1} (its diagonal blocks are in at already),
+// as the bf16 tile of T diag(beta) (sm.tf()), then
+// W = T diag(beta)(K o e^gam) (as -W into ops.wn) and
 // U = T diag(beta) V (into registers of waves w < V / 16: lane (m, g) holds
 // rows 16 pb + 4 g + j of value columns 16 w + m in U[pb]). Starts with
 // K o e^gam of the thread's elements in wkp (written here to the wkt tile)
@@ -1081,6 +1221,7 @@ __device__ __forceinline__ void intra_inverse_wu(FusedSmem<K, Q, EXACT>& sm,
   float* at = sm.at;
   const float* beta_l = sm.x + XL::beta;
   uint16_t* wkt = sm.wkt();
+  uint16_t* tf = sm.tf();
   // (K o e^gam)^T into its tile: PP positions of a channel are 2 PP
   // contiguous bytes.
 #pragma unroll
@@ -1169,8 +1310,28 @@ __device__ __forceinline__ void intra_inverse_wu(FusedSmem<K, Q, EXACT>& sm,
       const f32x4 t20 = mm_acc(nT22, mm_acc(a21, t10, p20), z0);
       t = mm_acc(nT33, mm_acc(a32, t20, mm_acc(a31, t10, p30)), z0);
     }
+    // T_IJ diag(beta) in bf16 into the T tile (lane: rows 16 I + 4 g + j of
+    // column 16 J + m).
+    const float bc = beta_l[16 * J + m];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) at[sw32<C>(16 * I + 4 * g + j, 16 * J + m)] = t[j];
+    for (int j = 0; j < 4; ++j) tf[rec_elem<C>(16 * I + 4 * g + j, 16 * J + m)] = bf16_bits(t[j] * bc);
+  } else {
+    // Waves 6 and 7: the diagonal blocks of T diag(beta) (blocks 2 (w - 6)
+    // and 2 (w - 6) + 1, from at) and the zero blocks above the diagonal that
+    // the products read, (0, 1) and (2, 3).
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int I = 2 * (w - 6) + b;
+      const float bc = beta_l[16 * I + m];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 4 * g + j;
+        const float tv = r > m ? at[sw32<C>(16 * I + r, 16 * I + m)] : (r == m ? 1.f : 0.f);
+        tf[rec_elem<C>(16 * I + r, 16 * I + m)] = bf16_bits(tv * bc);
+      }
+    }
+    const int zr = 32 * (w - 6) + (lane >> 1), zp = 4 * (w - 6) + 2 + (lane & 1);
+    if (lane < 32) *reinterpret_cast<uint4*>(&tf[rec_elem<C>(zr, zp * 8)]) = uint4{0u, 0u, 0u, 0u};
   }
   lds_barrier();
 
@@ -1178,30 +1339,18 @@ __device__ __forceinline__ void intra_inverse_wu(FusedSmem<K, Q, EXACT>& sm,
   // beta is folded into the fp32 columns of T before the bf16 cast, so V
   // enters the product exactly as given. T is lower triangular, so rows
   // 0..31 need only positions 0..31. Wave w takes channel block w of W and
-  // value block w of U.
+  // value block w of U. Each block of the tile was written by the wave that
+  // formed it.
   const bool does_w = w < K / 16, does_u = w < V / 16;  // wave-uniform
   if (does_w || does_u) {
+    // Rows 16 pb + m of T diag(beta) at columns 32 kb + 8 g .. + 7 (rows
+    // 0..31 need only columns 0..31).
     bf16x8 Tf[4][2];
 #pragma unroll
     for (int pb = 0; pb < 4; ++pb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int row = 16 * pb + m;
-        const int c0 = 32 * kb + 8 * g;
-        const f32x4 t0 = *reinterpret_cast<const f32x4*>(&at[sw32<C>(row, c0)]);
-        const f32x4 t1 = *reinterpret_cast<const f32x4*>(&at[sw32<C>(row, c0 + 4)]);
-        const f32x4 b0 = *reinterpret_cast<const f32x4*>(&beta_l[c0]);
-        const f32x4 b1 = *reinterpret_cast<const f32x4*>(&beta_l[c0 + 4]);
-        float tv[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int col = c0 + j;
-          const float tval = j < 4 ? t0[j] : t1[j - 4];
-          const float bcol = j < 4 ? b0[j] : b1[j - 4];
-          tv[j] = (col < row ? tval : (col == row ? 1.f : 0.f)) * bcol;
-        }
-        Tf[pb][kb] = to_bf16x8(tv);
-      }
+      for (int kb = 0; kb < 2; ++kb)
+        if (kb == 0 || pb >= 2) Tf[pb][kb] = frag<C>(tf, 16 * pb + m, 32 * kb + 8 * g);
     // -W^T = -(K o e^gam)^T (T diag(beta))^T: the same fragments with the
     // operands swapped leave lane (m, g) four consecutive channels
     // 16 nb + 4 g .. +3 of position 16 pb + m, which are four consecutive
@@ -1225,7 +1374,7 @@ __device__ __forceinline__ void intra_inverse_wu(FusedSmem<K, Q, EXACT>& sm,
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) Bv[kb][j] = __builtin_bit_cast(__bf16, in.vpre[kb][j]);
+        for (int j = 0; j < 8; ++j) Bv[kb][j] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(in.vpre[kb][j]));
 #pragma unroll
       for (int pb = 0; pb < 4; ++pb) {
         f32x4 D = mfma16(Tf[pb][0], Bv[0], f32x4{0.f, 0.f, 0.f, 0.f});
@@ -1249,7 +1398,7 @@ __device__ __forceinline__ void intra_part(const PrefillParams& p, int h, int n,
                                            f32x4 (&U)[4]) {
   using Ro = Roles<K>;
   float gm[Ro::PP][4], gl[4], rho[4];
-  const bool fast = gate_scan<K, V, Q, EXACT>(p, h, n, in, sm, gm, gl, rho);
+  const bool fast = gate_scan<K, V, Q, EXACT>(p, n, in, sm, gm, gl, rho);
   if (has_next) load_chunk_gate_regs<K, V>(p, h, next, in);
   uint32_t wkp[4][Ro::PP / 2];
   if (fast) intra_factored<K, V, Q, EXACT>(p, sm, gm, gl, rho, wkp);  // uniform
@@ -1367,7 +1516,11 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_state_kernel(const PrefillP
     for (int j = 0; j < 4; ++j)
       S[cb][j] = __builtin_bit_cast(
           float, __builtin_amdgcn_raw_buffer_load_b32(rs, ((16 * cb + 4 * g + j) * V + col0 + m) * 4, 0, 0));
+  // Wait for the state here, once: the compiler cannot tell inside the loop
+  // that these loads are long done and would wait for every later load.
+  pin_regs(S);
 
+  stage_gate_consts<K>(p, h, sm.x);
   // Lane (m, g) of the transposed output tile of position block pb holds
   // channels col0 + 4 g .. + 3 of position 16 pb + m: 8 contiguous bytes.
   const auto& ops = sm.r.ops;
@@ -1388,7 +1541,10 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_state_kernel(const PrefillP
       load_chunk_v_regs<K, V>(p, h, np, in);
       if constexpr (EXACT) dma_chunk_tiles<K, true>(p, h, np, sm.t.f.k, sm.t.f.q);
     }
-    if (!has_cols) continue;
+    if (!has_cols) {
+      if (more) pin_gate_regs<K, V>(in);  // (no v operands without columns)
+      continue;
+    }
     const int m = opaque_tid() & 15, g = (opaque_tid() & 63) >> 4;
     const int out_lane = static_cast<int>(m * HV + h * V + col0 + 4 * g) * 2;
 
@@ -1455,6 +1611,12 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_state_kernel(const PrefillP
     // Rows of the chunk as one buffer range: positions past its end fall
     // outside and their stores are dropped, so every lane issues exactly 4
     // stores, the last vector-memory operations of the chunk.
+    // The next chunk's v operands have had the products above to land; held
+    // here, ahead of the stores, so that nothing later waits on them.
+    if (more) {
+      pin_v_regs<K, V>(in);
+      pin_gate_regs<K, V>(in);
+    }
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.out + cp.t0 * HV, static_cast<uint32_t>(cp.n * HV * 2));
 #pragma unroll
     for (int pb = 0; pb < 4; ++pb)
@@ -1489,30 +1651,51 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_state_kernel(const PrefillP
 
 // ---------------------------------------------------------------- scan --
 
-// One workgroup per (cut sequence, head), 8 waves; wave w < V / 16 owns
-// value columns 16 w .. 16 w + 15. Composes the segment maps in order:
-// S_0 = the copy of the slot's state, S_{j+1} = M_j S_j + B_j, stored over
-// B_j for segment j + 1 of the state pass. The wave holds all K rows of its
-// columns, so two accumulator tiles form a bf16 B operand as in the chunk
-// loop (the contraction index permuted within each 32-block); lane (m, g)'s
-// A operand is M[row m][32 kb + 4 g .. +3] and M[row m][32 kb + 16 + 4 g ..
-// +3], two float4s of the row-major fp32 M. Both operands are split into
-// bf16 hi + lo parts and the product is hi*hi + hi*lo + lo*hi (about 16
-// significant bits, fp32 accumulation). Each M goes through LDS once for the
-// workgroup (double-buffered: the next map's copy runs under the current
-// product), its rows' 16-byte pieces XOR-swizzled by the row (piece p of row
-// r at p ^ (r & 15)) so the 16 rows a fragment read touches fall in
-// different banks.
+// The A operand fragments of M for S <- M S + B: fragment (rt, kb) of lane
+// (m, g) is row 16 rt + m at the permuted channel slots 8 g .. 8 g + 7 of
+// block kb (channels 32 kb + 4 g + 0..3 and 32 kb + 16 + 4 g + 0..3), so an
+// accumulator-held S is the B operand as it stands. Stored as bf16 hi parts
+// ([RT][KB][64] fragments of 16 bytes) and then lo parts (the bf16 rounding
+// of M - hi), together the size of M in fp32. From M in LDS (fp32 [K][K],
+// pieces swizzled by row); all threads of the workgroup take part.
+template <int K>
+__device__ __forceinline__ void store_map_fragments(const float* mt, uint4* dst) {
+  constexpr int NF = (K / 16) * (K / 32) * 64;  // fragments per part
+  static_assert(NF % kThreads == 0, "whole rounds");
+#pragma unroll
+  for (int r0 = 0; r0 < NF / kThreads; ++r0) {
+    const int f = r0 * kThreads + static_cast<int>(threadIdx.x);
+    const int l = f & 63, kb = (f >> 6) % (K / 32), rt = (f >> 6) / (K / 32);
+    const int row = 16 * rt + (l & 15), g = l >> 4;
+    const int p0 = 8 * kb + g, p1 = 8 * kb + 4 + g;  // pieces of channels 32 kb + 4 g and 32 kb + 16 + 4 g
+    const f32x4 a0 = *reinterpret_cast<const f32x4*>(&mt[row * K + ((p0 ^ (row & 15)) << 2)]);
+    const f32x4 a1 = *reinterpret_cast<const f32x4*>(&mt[row * K + ((p1 ^ (row & 15)) << 2)]);
+    const bf16x8 hi = pack_acc(a0, a1);
+    const bf16x8 lo = pack_lo(a0, a1, hi);
+    dst[f] = __builtin_bit_cast(uint4, hi);
+    dst[NF + f] = __builtin_bit_cast(uint4, lo);
+  }
+}
+
+// One single-wave workgroup per (cut sequence, value column block of 16,
+// head); the blocks of a head share an XCD (the index is head-fastest, so
+// with H a multiple of 8 they fall on one L2 and each M is fetched once).
+// Composes the segment maps in order: S_0 = the copy of the slot's state,
+// S_{j+1} = M_j S_j + B_j, stored over B_j (the wave's columns) for segment
+// j + 1 of the state pass. S is held in accumulators; M_{j+1}'s fragments
+// are copied into LDS while step j computes.
+constexpr int kScanThreads = 64;
+
 template <int K, int V>
-__global__ __launch_bounds__(kThreads, 1) void chunk_scan_kernel(const PrefillParams p, const SegPlan pl) {
-  constexpr int KB = K / 32;
-  constexpr int PPR = K / 4;                     // 16-byte pieces per row of M
-  constexpr int ROUNDS = K * PPR / kThreads;     // DMA rounds per M
-  static_assert((K * PPR) % kThreads == 0, "whole DMA rounds");
-  __shared__ float mbuf[2][K * K];
+__global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(const PrefillParams p, const SegPlan pl) {
+  constexpr int KB = K / 32, RT = K / 16, NCB = V / 16;
+  constexpr int NF = RT * KB * 64;               // fragments per part of M
+  constexpr int NSTORE = RT * 4;                 // stores per lane per step
+  __shared__ uint4 mbuf[2][2 * NF];
   const int H = p.H;
   if (uniform(pl.counts[0]) != 0) return;
-  const int li = static_cast<int>(blockIdx.x) / H, h = static_cast<int>(blockIdx.x) % H;
+  const int h = static_cast<int>(blockIdx.x) % H, rest = static_cast<int>(blockIdx.x) / H;
+  const int cbk = rest % NCB, li = rest / NCB;
   if (li >= uniform(pl.counts[3])) return;
   const int seq = uniform(pl.long_seq[li]);
   const int64_t slot = uniform(static_cast<int64_t>(p.indices[static_cast<int64_t>(seq) * p.index_stride]));
@@ -1520,89 +1703,70 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_scan_kernel(const PrefillPa
   const int seg0 = uniform(pl.seg_start[seq]);
   const int nmap = uniform(pl.seg_start[seq + 1]) - seg0 - 1;
   const int mi0 = seg0 - seq;
-  const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
-  const int m = lane & 15, g = lane >> 4;
-  const bool has_cols = w < V / 16;
-  const int col0 = 16 * w;
+  const int lane = threadIdx.x, m = lane & 15, g = lane >> 4;
+  const int col0 = 16 * cbk;
   const int64_t item = static_cast<int64_t>(K) * K + static_cast<int64_t>(K) * V;
   auto dma_map = [&](int j) {
-    const __amdgpu_buffer_rsrc_t rr = make_rsrc(pl.maps + map_index(h, mi0 + j, pl) * item, static_cast<uint32_t>(K * K * 4));
-    uint4* dst = reinterpret_cast<uint4*>(mbuf[j & 1]);
+    const u32x4 rr = rsrc_words(pl.maps + map_index(h, mi0 + j, pl) * item, static_cast<uint32_t>(K * K * 4));
+    const uint32_t base = lds_addr(mbuf[j & 1]);
 #pragma unroll
-    for (int r = 0; r < ROUNDS; ++r) {
-      const int ps = r * kThreads + tid;  // physical piece
-      const int row = ps / PPR, pp = ps % PPR;
-      const int lp = pp ^ (row & 15);     // logical piece stored there
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, dst + r * kThreads + (tid & ~63), 16, (row * PPR + lp) * 16, 0, 0, 0);
-    }
+    for (int r = 0; r < 2 * NF / 64; ++r) lds_copy16(rr, base + r * 1024, lane * 16, r * 1024);
   };
-  dma_map(0);
-  f32x4 S[K / 16];
-  {
-    const __amdgpu_buffer_rsrc_t rs =
-        make_rsrc(pl.s0 + s0_index(h, li, pl) * K * V, has_cols ? static_cast<uint32_t>(K * V * 4) : 0u);
+  // The wave's columns of B_j (and of S_0): lane (m, g) holds rows
+  // 16 cb + 4 g + jj of column col0 + m.
+  auto load_cols = [&](const float* src, f32x4 (&b)[RT]) {
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(src, static_cast<uint32_t>(K * V * 4));
 #pragma unroll
-    for (int cb = 0; cb < K / 16; ++cb)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        S[cb][j] = __builtin_bit_cast(
-            float, __builtin_amdgcn_raw_buffer_load_b32(rs, ((16 * cb + 4 * g + j) * V + col0 + m) * 4, 0, 0));
-  }
-  // B_j of the wave's columns, loaded a step ahead.
-  auto load_b = [&](int j, f32x4 (&b)[K / 16]) {
-    const float* Bm = pl.maps + map_index(h, mi0 + j, pl) * item + static_cast<int64_t>(K) * K;
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bm, has_cols ? static_cast<uint32_t>(K * V * 4) : 0u);
-#pragma unroll
-    for (int cb = 0; cb < K / 16; ++cb)
+    for (int cb = 0; cb < RT; ++cb)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj)
         b[cb][jj] = __builtin_bit_cast(
             float, __builtin_amdgcn_raw_buffer_load_b32(rb, ((16 * cb + 4 * g + jj) * V + col0 + m) * 4, 0, 0));
   };
-  f32x4 Bn[K / 16];
-  load_b(0, Bn);
+  auto b_of = [&](int j) { return pl.maps + map_index(h, mi0 + j, pl) * item + static_cast<int64_t>(K) * K; };
+  dma_map(0);
+  f32x4 S[RT], Bn[RT];
+  load_cols(pl.s0 + s0_index(h, li, pl) * K * V, S);
+  load_cols(b_of(0), Bn);
+  pin_regs(S);
   for (int j = 0; j < nmap; ++j) {
-    float* Bm = pl.maps + map_index(h, mi0 + j, pl) * item + static_cast<int64_t>(K) * K;
-    // M_j has landed in every thread's pieces (wait for everything: the
-    // copy of M_{j+1} is issued only below), and every wave is done with the
-    // buffer M_{j+1} overwrites.
-    wait_vmem();
-    lds_barrier();
-    f32x4 Bc[K / 16];
+    // M_j's fragments and B_j have landed (only the previous step's stores,
+    // the last vector-memory operations, may be in flight).
+    if (j == 0) wait_vmem();
+    else __builtin_amdgcn_s_waitcnt(0x0F70 & ~0x000F | (NSTORE & 15) | ((NSTORE >> 4) << 14));
+    asm volatile("" ::: "memory");
+    f32x4 Bc[RT];
 #pragma unroll
-    for (int cb = 0; cb < K / 16; ++cb) Bc[cb] = Bn[cb];
+    for (int cb = 0; cb < RT; ++cb) Bc[cb] = Bn[cb];
     if (j + 1 < nmap) {
       dma_map(j + 1);
-      load_b(j + 1, Bn);
+      load_cols(b_of(j + 1), Bn);
     }
-    if (!has_cols) continue;
     bf16x8 Sh[KB], Sl[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       Sh[kb] = pack_acc(S[2 * kb], S[2 * kb + 1]);
       Sl[kb] = pack_lo(S[2 * kb], S[2 * kb + 1], Sh[kb]);
     }
-    const float* mb = mbuf[j & 1];
+    const uint4* mh = mbuf[j & 1];
 #pragma unroll
-    for (int rt = 0; rt < K / 16; ++rt) {
+    for (int rt = 0; rt < RT; ++rt) {
       f32x4 acc = Bc[rt];
-      const float* row = mb + (16 * rt + m) * K;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        const f32x4 a0 = *reinterpret_cast<const f32x4*>(row + 4 * ((8 * kb + g) ^ m));
-        const f32x4 a1 = *reinterpret_cast<const f32x4*>(row + 4 * ((8 * kb + 4 + g) ^ m));
-        const bf16x8 ah = pack_acc(a0, a1);
-        const bf16x8 al = pack_lo(a0, a1, ah);
+        const bf16x8 ah = __builtin_bit_cast(bf16x8, mh[(rt * KB + kb) * 64 + lane]);
+        const bf16x8 al = __builtin_bit_cast(bf16x8, mh[NF + (rt * KB + kb) * 64 + lane]);
         acc = mfma16(ah, Sh[kb], acc);
         acc = mfma16(ah, Sl[kb], acc);
         acc = mfma16(al, Sh[kb], acc);
       }
       S[rt] = acc;
     }
-    // The state that segment j + 1 starts from, over B_j (this wave's
-    // columns only; B_j's other columns belong to other waves).
+    // The state that segment j + 1 starts from, over B_j (the wave's
+    // columns; the other columns belong to the head's other workgroups).
+    float* Bm = b_of(j);
 #pragma unroll
-    for (int cb = 0; cb < K / 16; ++cb)
+    for (int cb = 0; cb < RT; ++cb)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) Bm[(16 * cb + 4 * g + jj) * V + col0 + m] = S[cb][jj];
   }
@@ -1669,8 +1833,10 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_map_kernel(const PrefillPar
       X[0][cb][j] = (16 * cb + 4 * g + j == 16 * w + m) ? 1.f : 0.f;
       X[1][cb][j] = 0.f;
     }
+  stage_gate_consts<K>(p, h, sm.x);
   const auto& ops = sm.r.ops;
   for (int cc = 0; cc < sr.nch; ++cc) {
+    pin_v_regs<K, V>(in);
     chunk_barrier<0>();
     f32x4 U[4];
     const bool more = cc + 1 < sr.nch;
@@ -1734,16 +1900,30 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_map_kernel(const PrefillPar
     }
   }
   float* dst = pl.maps + map_index(h, mi, pl) * (static_cast<int64_t>(K) * K + static_cast<int64_t>(K) * V);
-#pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    if (!act[x]) continue;
-    float* d = x == 0 ? dst : dst + K * K;
-    const int ld = x == 0 ? K : V;
+  // B as fp32 [K][V].
+  if (act[1]) {
 #pragma unroll
     for (int cb = 0; cb < K / 16; ++cb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) d[(16 * cb + 4 * g + j) * ld + 16 * w + m] = X[x][cb][j];
+      for (int j = 0; j < 4; ++j) dst[K * K + (16 * cb + 4 * g + j) * V + 16 * w + m] = X[1][cb][j];
   }
+  // M as the scan's MFMA A operands, split into bf16 hi and lo parts: a
+  // waves' column tiles go through LDS (fp32 [K][K], 16-byte pieces of row
+  // r XOR-swizzled by r) and come back as row fragments.
+  float* mt = reinterpret_cast<float*>(&sm);
+  static_assert(sizeof(SM) >= sizeof(float) * K * K, "M fits the workgroup's LDS");
+  __syncthreads();  // every wave is done with the last chunk's operands
+  if (act[0]) {
+#pragma unroll
+    for (int cb = 0; cb < K / 16; ++cb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 16 * cb + 4 * g + j, c = 16 * w + m;
+        mt[r * K + ((((c >> 2) ^ (r & 15)) << 2) | (c & 3))] = X[0][cb][j];
+      }
+  }
+  __syncthreads();
+  store_map_fragments<K>(mt, reinterpret_cast<uint4*>(dst));
 }
 
 template <int K, int V, bool EXACT>
@@ -1753,7 +1933,8 @@ hipError_t launch_kv(const PrefillParams& p, const Layout& L, const SegPlan& pl,
   if (state_blocks > 0x7fffffff || map_blocks > 0x7fffffff) return hipErrorInvalidValue;
   if (map_blocks > 0) {
     chunk_map_kernel<K, V, EXACT><<<dim3(static_cast<unsigned>(map_blocks)), dim3(kThreads), 0, stream>>>(p, pl);
-    chunk_scan_kernel<K, V><<<dim3(static_cast<unsigned>(L.long_bound * p.H)), dim3(kThreads), 0, stream>>>(p, pl);
+    chunk_scan_kernel<K, V><<<dim3(static_cast<unsigned>(L.long_bound * p.H * (V / 16))), dim3(kScanThreads), 0,
+                               stream>>>(p, pl);
   }
   chunk_state_kernel<K, V, EXACT><<<dim3(static_cast<unsigned>(state_blocks)), dim3(kThreads), 0, stream>>>(p, pl);
   return hipGetLastError();
