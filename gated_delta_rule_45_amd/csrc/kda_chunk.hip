@@ -228,22 +228,25 @@ __device__ __forceinline__ void chunk_barrier() {
 // chunks, S_out = M S_in + B with
 //   M = prod_c (diag(e^{gam_last}) - (K o e^{gam_last - gam})^T W)   (K x K)
 //   B = the state reached from S_in = 0                                (K x V)
-// so a long sequence is cut into segments: the map pass computes (M, B) of
-// every segment but the last in parallel, the scan pass composes them in
-// order into each segment's initial state (S_{j+1} = M_j S_j + B_j, stored
-// over B_j), and the state pass runs every segment's chunks in parallel.
+// so a long sequence is cut into segments and run in two launches. The
+// first runs segment 0's state pass (from the slot's state; its final state
+// goes to B of map item 0) beside the maps (M, B) of segments 1 .. n - 2; the
+// scan pass composes them in order into each later segment's initial state
+// (S_{j+1} = M_j S_j + B_j, stored over B_j); the second launch runs the
+// state pass of segments 1 .. n - 1 in parallel. Each launch has n - 1
+// workgroups per cut (sequence, head).
 //
 // A sequence is cut into at most ceil(chunks / kSegMinChunks) segments of
 // equal length (the last may be shorter), into no more segments than it
-// takes for the cut sequences' workgroups to occupy kChipSlots slots (one
-// per compute unit: a workgroup's LDS takes most of a CU), and only into
-// kMinCut segments or more: a map chunk costs about as much as a state
-// chunk, so two segments would not shorten the chain.
-constexpr int kSegMinChunks = 16;
-constexpr int kMaxSegs = 16;  // <= kSegMinChunks: keeps the last segment non-empty
+// takes for the cut sequences' workgroups of one launch to occupy
+// kChipSlots slots (one per compute unit: a workgroup's LDS takes most of a
+// CU), and only into kMinCut segments or more: a map chunk costs about as
+// much as a state chunk, so two segments would not shorten the chain.
+constexpr int kSegMinChunks = 12;
+constexpr int kMaxSegs = 13;  // <= kSegMinChunks + 1: keeps the last segment non-empty
 constexpr int kMinCut = 3;
 constexpr int kChipSlots = 256;
-static_assert(kMaxSegs <= kSegMinChunks, "segment count bound");
+static_assert(kMaxSegs <= kSegMinChunks + 1, "segment count bound");
 
 // Device-side plan of one prefill call, written by plan_kernel. counts[0]
 // is the call's status word (workspace offset 0): 0 when cu_seqlens keep to
@@ -254,12 +257,12 @@ struct SegPlan {
   int32_t* seg_start;    // [N+1] first segment of each sequence
   int32_t* seg_seq;      // [seg_bound] sequence of each segment
   int32_t* seg_long;     // [seg_bound] index of a cut sequence among the cut ones, else -1
-  int32_t* map_seg;      // [map_bound] segment of each map item (a non-final segment)
+  int32_t* map_seg;      // [map_bound] segment of each map item (a non-final segment; the
+                         // item of segment 0 runs that segment's state pass instead)
   int32_t* long_seq;     // [long_bound] sequence of each cut sequence
   float* maps;           // [H][map_bound]: M (as the scan's bf16 hi and lo A fragments, the
-                         // size of fp32 [K][K]) then B (fp32 [K][V]); after the scan pass, B
-                         // of map item j holds the initial state of segment j + 1
-  float* s0;             // [H][long_bound]: fp32 [K][V] initial state of each cut sequence
+                         // size of fp32 [K][K]) then B (fp32 [K][V]); B of map item j ends up
+                         // holding the initial state of segment j + 1
   int32_t seg_bound, map_bound, long_bound;
   int32_t max_segs;      // segments per sequence at most (host bound)
   int32_t num_tokens;    // rows of the call (validated to fit in int32)
@@ -270,9 +273,6 @@ constexpr int32_t kBadCuSeqlens = 1;
 __device__ __forceinline__ int64_t map_index(int h, int mi, const SegPlan& pl) {
   return static_cast<int64_t>(h) * pl.map_bound + mi;
 }
-__device__ __forceinline__ int64_t s0_index(int h, int li, const SegPlan& pl) {
-  return static_cast<int64_t>(h) * pl.long_bound + li;
-}
 
 // Workspace layout (byte offsets) for one call's sizes. Bounds: a cut
 // sequence of len tokens has fewer than len / (64 kSegMinChunks) non-final
@@ -280,7 +280,7 @@ __device__ __forceinline__ int64_t s0_index(int h, int li, const SegPlan& pl) {
 // (and at most num_seqs (max_segs - 1)); each cut sequence has at least one.
 struct Layout {
   int64_t seg_bound, map_bound, long_bound, max_segs;
-  size_t counts, chunk_start, seg_start, seg_seq, seg_long, map_seg, long_seq, maps, s0, total;
+  size_t counts, chunk_start, seg_start, seg_seq, seg_long, map_seg, long_seq, maps, total;
 };
 
 inline size_t round256(size_t x) { return (x + 255) / 256 * 256; }
@@ -288,7 +288,7 @@ inline size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 inline Layout layout_for(int32_t num_seqs, int64_t num_tokens, int32_t H, int32_t K, int32_t V) {
   Layout L{};
   const int64_t N = num_seqs;
-  L.max_segs = std::min<int64_t>(kMaxSegs, std::max<int64_t>(1, (kChipSlots + H - 1) / H));
+  L.max_segs = std::min<int64_t>(kMaxSegs, (kChipSlots + H - 1) / H + 1);
   L.map_bound = L.max_segs < kMinCut ? 0 : std::min<int64_t>(num_tokens / (C * kSegMinChunks), N * (L.max_segs - 1));
   L.long_bound = L.map_bound;
   L.seg_bound = N + L.map_bound;
@@ -301,8 +301,7 @@ inline Layout layout_for(int32_t num_seqs, int64_t num_tokens, int32_t H, int32_
   L.map_seg = o;     o += L.map_bound * 4;
   L.long_seq = o;    o += L.long_bound * 4;
   L.maps = round256(o);
-  L.s0 = L.maps + static_cast<size_t>(L.map_bound) * H * (static_cast<size_t>(K) * K + static_cast<size_t>(K) * V) * 4;
-  L.total = L.s0 + static_cast<size_t>(L.long_bound) * H * static_cast<size_t>(K) * V * 4;
+  L.total = L.maps + static_cast<size_t>(L.map_bound) * H * (static_cast<size_t>(K) * K + static_cast<size_t>(K) * V) * 4;
   return L;
 }
 
@@ -343,8 +342,8 @@ __device__ __forceinline__ int segments_of(int nch, int target) {
 
 // Checks cu_seqlens (starts at 0, non-decreasing, ends at num_tokens) and
 // plans chunks and segments of every sequence. The segment target is the
-// number of segments each cut sequence needs for the cut sequences together
-// to occupy the chip. With cu_seqlens outside the contract the status word
+// number of segments each cut sequence needs for the cut sequences' n - 1
+// workgroups per launch together to occupy the chip. With cu_seqlens outside the contract the status word
 // is set and no segment exists: the state pass then writes NaN to every
 // output row and touches no state.
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* cu, int32_t N, int32_t H, SegPlan pl) {
@@ -364,7 +363,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* cu, i
   int n_long;
   block_exclusive_scan(nl, part, n_long);
   const int units = H * max(n_long, 1);
-  const int target = min(pl.max_segs, max(1, (kChipSlots + units - 1) / units));
+  const int target = min(pl.max_segs, (kChipSlots + units - 1) / units + 1);
 
   int cc = 0, sc = 0, lc = 0;
   for (int i = b; i < e; ++i) {
@@ -904,31 +903,57 @@ __device__ __forceinline__ void intra_factored(const PrefillParams& p, FusedSmem
   lds_barrier();
   // ---- A and P over all channels ----------------------------------------
   // Block (I, J): lane (m, g) holds rows 16 I + 4 g + j of column 16 J + m.
-  // On a diagonal block (I == J) also A^T (dAt), for the inverse.
-  auto ap_block = [&](int I, int J, f32x4& dA, f32x4& dPt, f32x4& dAt) {
+  // Diagonal block (I, I): A, A^T (for the inverse) and P^T. Every
+  // fragment is read before the products (the scheduling barrier keeps the
+  // reads together, so their latencies overlap).
+  auto ap_diag = [&](int I, f32x4& dA, f32x4& dPt, f32x4& dAt) {
+    constexpr int KB = K / 32;
+    bf16x8 ak[KB], bk[KB], aq[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const int c0 = 32 * kb + 8 * g;
+      ak[kb] = lds_frag(&sm.t.f.k[sw16<K>(16 * I + m, c0)]);
+      bk[kb] = lds_frag(&sm.t.f.kf[sw16<K>(16 * I + m, c0)]);
+      if constexpr (Q) aq[kb] = lds_frag(&sm.t.f.q[sw16<K>(16 * I + m, c0)]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     dA = f32x4{0.f, 0.f, 0.f, 0.f};
     dPt = f32x4{0.f, 0.f, 0.f, 0.f};
     dAt = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      dA = mfma16(ak[kb], bk[kb], dA);
+      dAt = mfma16(bk[kb], ak[kb], dAt);
+      if constexpr (Q) dPt = mfma16(bk[kb], aq[kb], dPt);
+    }
+  };
+  // Off-diagonal block (I, J), J < I: the B operand (K o F rows of block J)
+  // scaled by c_IJ per channel. All reads first, as above.
+  auto ap_off = [&](int I, int J, f32x4& dA, f32x4& dPt) {
+    constexpr int KB = K / 32;
     const float* cv = x + XL::cij + (I * (I + 1) / 2 + J) * K;
+    bf16x8 ak[KB], bk[KB], aq[KB];
+    f32x4 cs[KB][2];
 #pragma unroll
-    for (int kb = 0; kb < K / 32; ++kb) {
+    for (int kb = 0; kb < KB; ++kb) {
       const int c0 = 32 * kb + 8 * g;
-      const bf16x8 ak = lds_frag(&sm.t.f.k[sw16<K>(16 * I + m, c0)]);
-      bf16x8 b = lds_frag(&sm.t.f.kf[sw16<K>(16 * J + m, c0)]);
-      if (J < I) {
-        const f32x4 c0v = *reinterpret_cast<const f32x4*>(cv + c0);
-        const f32x4 c1v = *reinterpret_cast<const f32x4*>(cv + c0 + 4);
-        float sc[8];
+      ak[kb] = lds_frag(&sm.t.f.k[sw16<K>(16 * I + m, c0)]);
+      bk[kb] = lds_frag(&sm.t.f.kf[sw16<K>(16 * J + m, c0)]);
+      cs[kb][0] = *reinterpret_cast<const f32x4*>(cv + c0);
+      cs[kb][1] = *reinterpret_cast<const f32x4*>(cv + c0 + 4);
+      if constexpr (Q) aq[kb] = lds_frag(&sm.t.f.q[sw16<K>(16 * I + m, c0)]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    dA = f32x4{0.f, 0.f, 0.f, 0.f};
+    dPt = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) sc[jj] = static_cast<float>(b[jj]) * (jj < 4 ? c0v[jj] : c1v[jj - 4]);
-        b = to_bf16x8(sc);
-      }
-      dA = mfma16(ak, b, dA);
-      if (I == J) dAt = mfma16(b, ak, dAt);  // wave-uniform
-      if constexpr (Q) {
-        const bf16x8 aq = lds_frag(&sm.t.f.q[sw16<K>(16 * I + m, c0)]);
-        dPt = mfma16(b, aq, dPt);
-      }
+    for (int kb = 0; kb < KB; ++kb) {
+      float sc[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) sc[jj] = static_cast<float>(bk[kb][jj]) * cs[kb][jj >> 2][jj & 3];
+      const bf16x8 b = to_bf16x8(sc);
+      dA = mfma16(ak[kb], b, dA);
+      if constexpr (Q) dPt = mfma16(b, aq[kb], dPt);
     }
   };
   // A^T (times beta) of an off-diagonal block into at.
@@ -955,7 +980,7 @@ __device__ __forceinline__ void intra_factored(const PrefillParams& p, FusedSmem
     // Diagonal block: N = diag(beta) A below the diagonal, inverted in
     // registers; T_II goes strictly below the diagonal of at.
     f32x4 dA, dPt, dAt;
-    ap_block(w, w, dA, dPt, dAt);
+    ap_diag(w, dA, dPt, dAt);
     store_p(w, w, dPt);
     const float beta_m = x[XL::beta + 16 * w + m];
     const f32x4 beta_r = *reinterpret_cast<const f32x4*>(&x[XL::beta + 16 * w + 4 * g]);
@@ -975,8 +1000,8 @@ __device__ __forceinline__ void intra_factored(const PrefillParams& p, FusedSmem
       int I, J;
       offdiag_block(w, bi, I, J);
       if (I >= 0) {  // wave-uniform
-        f32x4 dA, dPt, dAt;
-        ap_block(I, J, dA, dPt, dAt);
+        f32x4 dA, dPt;
+        ap_off(I, J, dA, dPt);
         store_a(I, J, dA);
         store_p(I, J, dPt);
       }
@@ -1241,22 +1266,35 @@ __device__ __forceinline__ void intra_inverse_wu(FusedSmem<K, Q, EXACT>& sm,
   // accumulator tile (rows 4 g + j) is the B operand of the next product as
   // it stands: step kk takes its element j = kk.
   if (w < 6) {
-    auto Tget = [&](int r, int cc) { return r > cc ? at[sw32<C>(r, cc)] : (r == cc ? 1.f : 0.f); };  // diagonal blocks
-    auto Aget = [&](int t, int s2) { return s2 < t ? at[sw32<C>(s2, t)] : 0.f; };                     // A[t][s]
-    // Every operand of the wave's chain is read first (only the MFMAs are
-    // then dependent): A-operand values of block (I, L) of A or of a
-    // diagonal block of T (negated ones carry the minus signs of the
-    // recurrence), and B-operand values of the diagonal blocks T_LL.
-    auto a_op = [&](bool of_a, int I, int L, bool negate, float (&a)[4]) {
+    // Operand values are read unconditionally (all in bounds), pinned, and
+    // only then selected: a read under a lane-dependent condition becomes a
+    // branch that waits for it on the spot. Every operand of the wave's
+    // chain is read first (only the MFMAs are then dependent).
+    auto pin4 = [](float (&v)[4]) { asm volatile("" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3])); };
+    // A-operand values of block (I, L), L < I, of A: A[16 I + m][16 L + 4 g + kk]
+    // (at holds A^T above the diagonal; no mask needed off the diagonal).
+    auto a_blk = [&](int I, int L, float (&a)[4]) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) a[kk] = at[sw32<C>(16 * L + 4 * g + kk, 16 * I + m)];
+    };
+    // Raw values of the diagonal block T_LL as an A operand (row m, column
+    // 4 g + kk) and as a B operand (row 4 g + kk, column m).
+    auto t_raw_a = [&](int L, float (&v)[4]) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) v[kk] = at[sw32<C>(16 * L + m, 16 * L + 4 * g + kk)];
+    };
+    auto t_raw_b = [&](int L, float (&v)[4]) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) v[kk] = at[sw32<C>(16 * L + 4 * g + kk, 16 * L + m)];
+    };
+    // Unit lower triangular selection of a raw diagonal-block value at local
+    // (row r, column c); sgn = -1 negates (the minus sign of the recurrence).
+    auto t_sel = [](float (&v)[4], bool as_a, int m_, int g_, float sgn) {
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const float v = of_a ? Aget(16 * I + m, 16 * L + 4 * g + kk) : Tget(16 * I + m, 16 * L + 4 * g + kk);
-        a[kk] = negate ? -v : v;
+        const int r = as_a ? m_ : 4 * g_ + kk, c = as_a ? 4 * g_ + kk : m_;
+        v[kk] = sgn * (r > c ? v[kk] : (r == c ? 1.f : 0.f));
       }
-    };
-    auto b_tdiag = [&](int L, float (&b)[4]) {
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) b[kk] = Tget(16 * L + 4 * g + kk, 16 * L + m);
     };
     auto mm = [&](const float (&a)[4], const float (&b)[4], f32x4 acc) {  // both from registers
 #pragma unroll
@@ -1275,36 +1313,49 @@ __device__ __forceinline__ void intra_inverse_wu(FusedSmem<K, Q, EXACT>& sm,
       J = w;
       I = w + 1;
       float aIJ[4], bJJ[4], nTII[4];
-      a_op(true, I, J, false, aIJ);
-      b_tdiag(J, bJJ);
-      a_op(false, I, I, true, nTII);
+      a_blk(I, J, aIJ);
+      t_raw_b(J, bJJ);
+      t_raw_a(I, nTII);
+      pin4(aIJ); pin4(bJJ); pin4(nTII);
+      t_sel(bJJ, false, m, g, 1.f);
+      t_sel(nTII, true, m, g, -1.f);
       t = mm_acc(nTII, mm(aIJ, bJJ, z0), z0);
     } else if (w < 5) {  // T_20 (w = 3) and T_31 (w = 4), through T_{J+1,J}
       J = w - 3;
       I = J + 2;
       float a10[4], bJJ[4], nT11[4], a20[4], a21[4], nT22[4];
-      a_op(true, J + 1, J, false, a10);
-      b_tdiag(J, bJJ);
-      a_op(false, J + 1, J + 1, true, nT11);
-      a_op(true, I, J, false, a20);
-      a_op(true, I, J + 1, false, a21);
-      a_op(false, I, I, true, nT22);
+      a_blk(J + 1, J, a10);
+      t_raw_b(J, bJJ);
+      t_raw_a(J + 1, nT11);
+      a_blk(I, J, a20);
+      a_blk(I, J + 1, a21);
+      t_raw_a(I, nT22);
+      pin4(a10); pin4(bJJ); pin4(nT11); pin4(a20); pin4(a21); pin4(nT22);
+      t_sel(bJJ, false, m, g, 1.f);
+      t_sel(nT11, true, m, g, -1.f);
+      t_sel(nT22, true, m, g, -1.f);
       const f32x4 t_mid = mm_acc(nT11, mm(a10, bJJ, z0), z0);  // T_{J+1,J}
       t = mm_acc(nT22, mm_acc(a21, t_mid, mm(a20, bJJ, z0)), z0);
     } else {  // T_30, through T_10 and T_20
       I = 3;
       J = 0;
       float a10[4], b00[4], nT11[4], a20[4], a21[4], nT22[4], a30[4], a31[4], a32[4], nT33[4];
-      a_op(true, 1, 0, false, a10);
-      b_tdiag(0, b00);
-      a_op(false, 1, 1, true, nT11);
-      a_op(true, 2, 0, false, a20);
-      a_op(true, 2, 1, false, a21);
-      a_op(false, 2, 2, true, nT22);
-      a_op(true, 3, 0, false, a30);
-      a_op(true, 3, 1, false, a31);
-      a_op(true, 3, 2, false, a32);
-      a_op(false, 3, 3, true, nT33);
+      a_blk(1, 0, a10);
+      t_raw_b(0, b00);
+      t_raw_a(1, nT11);
+      a_blk(2, 0, a20);
+      a_blk(2, 1, a21);
+      t_raw_a(2, nT22);
+      a_blk(3, 0, a30);
+      a_blk(3, 1, a31);
+      a_blk(3, 2, a32);
+      t_raw_a(3, nT33);
+      pin4(a10); pin4(b00); pin4(nT11); pin4(a20); pin4(a21);
+      pin4(nT22); pin4(a30); pin4(a31); pin4(a32); pin4(nT33);
+      t_sel(b00, false, m, g, 1.f);
+      t_sel(nT11, true, m, g, -1.f);
+      t_sel(nT22, true, m, g, -1.f);
+      t_sel(nT33, true, m, g, -1.f);
       const f32x4 p20 = mm(a20, b00, z0), p30 = mm(a30, b00, z0);  // independent of the chain
       const f32x4 t10 = mm_acc(nT11, mm(a10, b00, z0), z0);
       const f32x4 t20 = mm_acc(nT22, mm_acc(a21, t10, p20), z0);
@@ -1319,6 +1370,13 @@ __device__ __forceinline__ void intra_inverse_wu(FusedSmem<K, Q, EXACT>& sm,
     // Waves 6 and 7: the diagonal blocks of T diag(beta) (blocks 2 (w - 6)
     // and 2 (w - 6) + 1, from at) and the zero blocks above the diagonal that
     // the products read, (0, 1) and (2, 3).
+    float tv[2][4];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) tv[b][j] = at[sw32<C>(16 * (2 * (w - 6) + b) + 4 * g + j, 16 * (2 * (w - 6) + b) + m)];
+    asm volatile("" : "+v"(tv[0][0]), "+v"(tv[0][1]), "+v"(tv[0][2]), "+v"(tv[0][3]));
+    asm volatile("" : "+v"(tv[1][0]), "+v"(tv[1][1]), "+v"(tv[1][2]), "+v"(tv[1][3]));
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       const int I = 2 * (w - 6) + b;
@@ -1326,8 +1384,8 @@ __device__ __forceinline__ void intra_inverse_wu(FusedSmem<K, Q, EXACT>& sm,
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = 4 * g + j;
-        const float tv = r > m ? at[sw32<C>(16 * I + r, 16 * I + m)] : (r == m ? 1.f : 0.f);
-        tf[rec_elem<C>(16 * I + r, 16 * I + m)] = bf16_bits(tv * bc);
+        const float v = r > m ? tv[b][j] : (r == m ? 1.f : 0.f);  // read above, selected here
+        tf[rec_elem<C>(16 * I + r, 16 * I + m)] = bf16_bits(v * bc);
       }
     }
     const int zr = 32 * (w - 6) + (lane >> 1), zp = 4 * (w - 6) + 2 + (lane & 1);
@@ -1450,22 +1508,16 @@ __device__ __forceinline__ void poison_output(const PrefillParams& p) {
     p.out[i] = 0x7FC0;  // bf16 quiet NaN
 }
 
-// One workgroup per (segment, head), 8 waves; wave w < V / 16 owns value
-// columns 16 w .. 16 w + 15 of the state, kept in MFMA accumulators for the
-// whole segment.
+// The state pass of segment gs (rows sr) of head h on one workgroup, 8
+// waves; wave w < V / 16 owns value columns 16 w .. 16 w + 15 of the state,
+// kept in MFMA accumulators for the whole segment. Starts from the slot's
+// state (segment 0 or an uncut sequence) or from B of map item sg - 1 (the
+// scan's result); the final state goes to the slot (last segment) or, for
+// segment 0 of a cut sequence, to B of map item 0.
 template <int K, int V, bool EXACT>
-__global__ __launch_bounds__(kThreads, 1) void chunk_state_kernel(const PrefillParams p, const SegPlan pl) {
-  using SM = FusedSmem<K, true, EXACT>;
-  __shared__ SM sm;
+__device__ __forceinline__ void state_segment(const PrefillParams& p, const SegPlan& pl, int gs,
+                                              const SegRange& sr, int h, FusedSmem<K, true, EXACT>& sm) {
   const int H = p.H;
-  if (uniform(pl.counts[0]) != 0) {
-    poison_output(p);
-    return;
-  }
-  const int gs = static_cast<int>(blockIdx.x) / H, h = static_cast<int>(blockIdx.x) % H;
-  if (gs >= uniform(pl.counts[1])) return;
-  const SegRange sr = segment_range(p, pl, gs);
-  if (sr.nch <= 0) return;
   const bool last_seg = sr.sg == sr.nseg - 1;
 
   const int tid = threadIdx.x;
@@ -1494,17 +1546,15 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_state_kernel(const PrefillP
   dma_chunk_tiles<K, true>(p, h, chunk_pos(sr, 0), sm.t.f.k, sm.t.f.q);
 
   float* st = p.pool + slot * p.slot_stride + static_cast<int64_t>(h) * K * V;
-  // Segment 0 of a cut sequence starts from the copy of the slot's state that
-  // the map pass made (the slot itself is written by the last segment of this
-  // same launch), segment sg > 0 from the state the scan pass left in B of
-  // map item sg - 1; an uncut sequence from its slot.
-  const int li = uniform(pl.seg_long[gs]);
-  const float* s_in = st;
-  if (li >= 0)
-    s_in = sr.sg == 0 ? pl.s0 + s0_index(h, li, pl) * K * V
-                      : pl.maps + map_index(h, sr.seg0 - sr.seq + sr.sg - 1, pl) *
-                                      (static_cast<int64_t>(K) * K + static_cast<int64_t>(K) * V) + K * K;
-  const bool init = li >= 0 || p.has_initial_state == nullptr ||
+  // B of the sequence's map item j (fp32 [K][V]).
+  auto map_b = [&](int j) {
+    return pl.maps + map_index(h, sr.seg0 - sr.seq + j, pl) * (static_cast<int64_t>(K) * K + static_cast<int64_t>(K) * V) +
+           K * K;
+  };
+  const bool cut = uniform(pl.seg_long[gs]) >= 0;
+  const bool from_scan = cut && sr.sg > 0;
+  const float* s_in = from_scan ? map_b(sr.sg - 1) : st;
+  const bool init = from_scan || p.has_initial_state == nullptr ||
                     uniform(static_cast<int32_t>(p.has_initial_state[sr.seq])) != 0;
   // Without an initial state (or without columns) the range is empty and
   // every load reads zero.
@@ -1642,11 +1692,31 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_state_kernel(const PrefillP
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  if (!last_seg || !has_cols) return;
+  if (!has_cols) return;
+  float* fin = last_seg ? st : (cut && sr.sg == 0 ? map_b(0) : nullptr);
+  if (fin == nullptr) return;
 #pragma unroll
   for (int cb = 0; cb < K / 16; ++cb)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) st[(16 * cb + 4 * g + j) * V + col0 + m] = S[cb][j];
+    for (int j = 0; j < 4; ++j) fin[(16 * cb + 4 * g + j) * V + col0 + m] = S[cb][j];
+}
+
+// Second launch: one workgroup per (segment, head), every segment but
+// segment 0 of a cut sequence (run by the first launch).
+template <int K, int V, bool EXACT>
+__global__ __launch_bounds__(kThreads, 1) void chunk_state_kernel(const PrefillParams p, const SegPlan pl) {
+  __shared__ FusedSmem<K, true, EXACT> sm;
+  const int H = p.H;
+  if (uniform(pl.counts[0]) != 0) {
+    poison_output(p);
+    return;
+  }
+  const int gs = static_cast<int>(blockIdx.x) / H, h = static_cast<int>(blockIdx.x) % H;
+  if (gs >= uniform(pl.counts[1])) return;
+  const SegRange sr = segment_range(p, pl, gs);
+  if (sr.nch <= 0) return;
+  if (sr.sg == 0 && uniform(pl.seg_long[gs]) >= 0) return;
+  state_segment<K, V, EXACT>(p, pl, gs, sr, h, sm);
 }
 
 // ---------------------------------------------------------------- scan --
@@ -1680,7 +1750,7 @@ __device__ __forceinline__ void store_map_fragments(const float* mt, uint4* dst)
 // One single-wave workgroup per (cut sequence, value column block of 16,
 // head); the blocks of a head share an XCD (the index is head-fastest, so
 // with H a multiple of 8 they fall on one L2 and each M is fetched once).
-// Composes the segment maps in order: S_0 = the copy of the slot's state,
+// Composes the segment maps in order: S_1 = B_0 (segment 0's final state),
 // S_{j+1} = M_j S_j + B_j, stored over B_j (the wave's columns) for segment
 // j + 1 of the state pass. S is held in accumulators; M_{j+1}'s fragments
 // are copied into LDS while step j computes.
@@ -1724,15 +1794,16 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(const Prefi
             float, __builtin_amdgcn_raw_buffer_load_b32(rb, ((16 * cb + 4 * g + jj) * V + col0 + m) * 4, 0, 0));
   };
   auto b_of = [&](int j) { return pl.maps + map_index(h, mi0 + j, pl) * item + static_cast<int64_t>(K) * K; };
-  dma_map(0);
+  if (nmap < 2) return;
+  dma_map(1);
   f32x4 S[RT], Bn[RT];
-  load_cols(pl.s0 + s0_index(h, li, pl) * K * V, S);
-  load_cols(b_of(0), Bn);
+  load_cols(b_of(0), S);
+  load_cols(b_of(1), Bn);
   pin_regs(S);
-  for (int j = 0; j < nmap; ++j) {
+  for (int j = 1; j < nmap; ++j) {
     // M_j's fragments and B_j have landed (only the previous step's stores,
     // the last vector-memory operations, may be in flight).
-    if (j == 0) wait_vmem();
+    if (j == 1) wait_vmem();
     else __builtin_amdgcn_s_waitcnt(0x0F70 & ~0x000F | (NSTORE & 15) | ((NSTORE >> 4) << 14));
     asm volatile("" ::: "memory");
     f32x4 Bc[RT];
@@ -1774,8 +1845,9 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(const Prefi
 
 // ----------------------------------------------------------------- map --
 
-// One workgroup per (map item = a non-final segment of a cut sequence,
-// head), 8 waves. Runs the segment's chunks (all full) from X = [I | 0]
+// First launch: one workgroup per (map item = a non-final segment of a cut
+// sequence, head), 8 waves. Segment 0 runs its state pass (state_segment);
+// segments 1 .. n - 2 their maps: the segment's chunks (all full) from X = [I | 0]
 // (the identity's columns, and zero) with U = 0 for the columns of M and the
 // chunk's U for those of B: X <- e^{gam_last} o X + (K o e^{gam_last-gam})^T
 // ([0 | U] - W X). Wave w owns M's column tile w (w < K / 16) and B's (w <
@@ -1784,13 +1856,21 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(const Prefi
 template <int K, int V, bool EXACT>
 __global__ __launch_bounds__(kThreads, 1) void chunk_map_kernel(const PrefillParams p, const SegPlan pl) {
   using SM = FusedSmem<K, false, EXACT>;
-  __shared__ SM sm;
+  __shared__ union {
+    FusedSmem<K, true, EXACT> state;
+    SM map;
+  } smu;
+  SM& sm = smu.map;
   const int H = p.H;
   if (uniform(pl.counts[0]) != 0) return;
   const int mi = static_cast<int>(blockIdx.x) / H, h = static_cast<int>(blockIdx.x) % H;
   if (mi >= uniform(pl.counts[2])) return;
   const int gs = uniform(pl.map_seg[mi]);
   const SegRange sr = segment_range(p, pl, gs);
+  if (sr.sg == 0) {  // segment 0's state pass instead of its map
+    state_segment<K, V, EXACT>(p, pl, gs, sr, h, smu.state);
+    return;
+  }
   const int64_t slot = uniform(static_cast<int64_t>(p.indices[static_cast<int64_t>(sr.seq) * p.index_stride]));
   if (slot < 0) return;  // a null slot carries no state
 
@@ -1804,25 +1884,6 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_map_kernel(const PrefillPar
   ChunkIn<K, V> in;
   load_chunk_regs<K, V>(p, h, chunk_pos(sr, 0), in);
   dma_chunk_tiles<K, false>(p, h, chunk_pos(sr, 0), sm.t.f.k, nullptr);
-
-  // The first map item of a cut sequence copies the slot's initial state
-  // (zero without one) for the state pass: its segments then never read the
-  // slot that the last of them writes. Every load is issued before the
-  // first store.
-  if (mi == sr.seg0 - sr.seq) {
-    const int li = uniform(pl.seg_long[gs]);
-    const bool init = p.has_initial_state == nullptr || uniform(static_cast<int32_t>(p.has_initial_state[sr.seq])) != 0;
-    const float* src = p.pool + slot * p.slot_stride + static_cast<int64_t>(h) * K * V;
-    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(src, init ? static_cast<uint32_t>(K * V * 4) : 0u);
-    const __amdgpu_buffer_rsrc_t rd = make_rsrc(pl.s0 + s0_index(h, li, pl) * K * V, static_cast<uint32_t>(K * V * 4));
-    constexpr int N4 = K * V / 4 / kThreads;  // float4s per thread
-    static_assert(N4 * 4 * kThreads == K * V, "whole float4s");
-    f32x4 cp[N4];
-#pragma unroll
-    for (int i = 0; i < N4; ++i) cp[i] = buffer_load_f32x4<0>(rsrc, (i * kThreads + tid) * 16, 0);
-#pragma unroll
-    for (int i = 0; i < N4; ++i) buffer_store_f32x4<0>(cp[i], rd, (i * kThreads + tid) * 16, 0);
-  }
 
   // X[0]: the wave's column tile of M (from the identity), X[1]: of B.
   f32x4 X[2][K / 16];
@@ -1971,7 +2032,6 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream, hipEvent_t
   pl.map_seg = reinterpret_cast<int32_t*>(ws + L.map_seg);
   pl.long_seq = reinterpret_cast<int32_t*>(ws + L.long_seq);
   pl.maps = reinterpret_cast<float*>(ws + L.maps);
-  pl.s0 = reinterpret_cast<float*>(ws + L.s0);
   pl.seg_bound = static_cast<int32_t>(L.seg_bound);
   pl.map_bound = static_cast<int32_t>(L.map_bound);
   pl.long_bound = static_cast<int32_t>(L.long_bound);

@@ -159,7 +159,7 @@ def test_workspace_size_query():
     a = L.kda_chunk_prefill_workspace_size(1, 8192, 32, 128, 128)
     b = L.kda_chunk_prefill_workspace_size(64, 8192, 32, 128, 128)
     c = L.kda_chunk_prefill_workspace_size(1, 65536, 32, 128, 128)
-    assert 0 < a < b and a <= c  # a sequence has at most 7 segment maps at H=32
+    assert 0 < a < b and a <= c  # a sequence has at most 8 map items at H=32
     assert L.kda_chunk_prefill_workspace_size(1, 10, 32, 96, 128) == 0
     assert L.kda_chunk_prefill_workspace_size(-1, 10, 32, 128, 128) == 0
     assert L.kda_mixed_batch_workspace_size(96, 5, 4000, 32, 128, 128) == \
