@@ -9,8 +9,10 @@ from ._binding import (  # noqa: F401
     KdaError,
     Overlap,
     NOALLOC_SCRATCH_BYTES,
+    PREFILL_BAD_CU_SEQLENS,
     kda_chunk_prefill,
     kda_chunk_prefill_noalloc,
+    kda_chunk_prefill_workspace_maps,
     kda_chunk_prefill_workspace_size,
     kda_decode_packed,
     kda_mixed_batch,
@@ -18,6 +20,7 @@ from ._binding import (  # noqa: F401
     kda_short_conv,
     kda_spec_decode,
     lib,
+    prefill_status,
 )
 
 __all__ = [
@@ -25,8 +28,10 @@ __all__ = [
     "KdaError",
     "Overlap",
     "NOALLOC_SCRATCH_BYTES",
+    "PREFILL_BAD_CU_SEQLENS",
     "kda_chunk_prefill",
     "kda_chunk_prefill_noalloc",
+    "kda_chunk_prefill_workspace_maps",
     "kda_chunk_prefill_workspace_size",
     "kda_decode_packed",
     "kda_mixed_batch",
@@ -34,4 +39,5 @@ __all__ = [
     "kda_short_conv",
     "kda_spec_decode",
     "lib",
+    "prefill_status",
 ]

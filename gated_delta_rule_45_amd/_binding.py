@@ -18,6 +18,15 @@ LIB_PATH = os.path.join(_PKG, "libkda.so")
 
 KDA_OK = 0
 NOALLOC_SCRATCH_BYTES = 64 << 20  # KDA_NOALLOC_SCRATCH_BYTES in kda.h
+PREFILL_BAD_CU_SEQLENS = 1        # KDA_PREFILL_BAD_CU_SEQLENS in kda.h
+
+
+def prefill_status(workspace) -> int:
+    """The status word a prefill (or mixed) call left at offset 0 of its
+    workspace: 0, or PREFILL_BAD_CU_SEQLENS when its cu_seqlens broke the
+    contract (then its output rows are NaN and no slot was touched). Reads
+    device memory, so it waits for the workspace's stream."""
+    return int(workspace[:4].view(torch.int32).item())
 STATUS_NAMES = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARGUMENT", 2: "KDA_ERR_UNSUPPORTED",
                 3: "KDA_ERR_WORKSPACE", 4: "KDA_ERR_HIP"}
 
@@ -112,6 +121,9 @@ def lib() -> ctypes.CDLL:
         L.kda_spec_decode.restype = i32
         L.kda_chunk_prefill_workspace_size.argtypes = [i32, i64, i32, i32, i32]
         L.kda_chunk_prefill_workspace_size.restype = sz
+        L.kda_chunk_prefill_workspace_maps.argtypes = [i32, i64, i32, i32, i32, ctypes.POINTER(sz),
+                                                       ctypes.POINTER(sz), ctypes.POINTER(i64)]
+        L.kda_chunk_prefill_workspace_maps.restype = i32
         L.kda_chunk_prefill.argtypes = [i32, i64, vp, vp, i32, i32, i32, vp, i64, vp, vp, gp, spn,
                                         npn, vp, vp, sz, vp]
         L.kda_chunk_prefill.restype = i32
@@ -332,6 +344,15 @@ def kda_spec_decode(mixed_qkv, raw_g, raw_beta, A_log, dt_bias, lower_bound, ini
 
 def kda_chunk_prefill_workspace_size(num_seqs: int, num_tokens: int, H: int, K: int, V: int) -> int:
     return int(lib().kda_chunk_prefill_workspace_size(num_seqs, num_tokens, H, K, V))
+
+
+def kda_chunk_prefill_workspace_maps(num_seqs: int, num_tokens: int, H: int, K: int, V: int):
+    """(offset, item_bytes, items) of the segment-map area of a prefill
+    workspace of these sizes (kda_chunk_prefill_workspace_maps)."""
+    off, item, n = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_int64()
+    _raise_if(lib().kda_chunk_prefill_workspace_maps(num_seqs, num_tokens, H, K, V, ctypes.byref(off),
+                                                     ctypes.byref(item), ctypes.byref(n)))
+    return int(off.value), int(item.value), int(n.value)
 
 
 def kda_mixed_batch_workspace_size(num_decodes: int, num_prefills: int, num_prefill_tokens: int,

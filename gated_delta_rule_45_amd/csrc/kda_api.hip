@@ -325,6 +325,20 @@ size_t kda_chunk_prefill_workspace_size(int32_t num_seqs, int64_t num_tokens, in
   return kda::prefill_workspace_bytes(num_seqs, num_tokens, H, K, V);
 }
 
+kda_status_t kda_chunk_prefill_workspace_maps(int32_t num_seqs, int64_t num_tokens, int32_t H, int32_t K,
+                                              int32_t V, size_t* offset, size_t* item_bytes,
+                                              int64_t* items) {
+  Checks c;
+  c.require(num_seqs >= 0 && num_tokens >= 0 && H >= 1, KDA_ERR_INVALID_ARGUMENT,
+            "num_seqs, num_tokens must be >= 0 and H >= 1");
+  c.require((K == 64 || K == 128) && (V == 64 || V == 128), KDA_ERR_UNSUPPORTED, "K and V must be 64 or 128");
+  c.require(offset != nullptr && item_bytes != nullptr && items != nullptr, KDA_ERR_INVALID_ARGUMENT,
+            "offset, item_bytes and items are required");
+  if (!c.ok()) return c.finish();
+  kda::prefill_workspace_maps(num_seqs, num_tokens, H, K, V, offset, item_bytes, items);
+  return c.finish();
+}
+
 kda_status_t kda_chunk_prefill(int32_t num_seqs, int64_t num_tokens, const int32_t* cu_seqlens,
                                const uint8_t* has_initial_state, int32_t H, int32_t K, int32_t V,
                                const void* mixed_qkv, int64_t qkv_row_stride, const void* raw_g,

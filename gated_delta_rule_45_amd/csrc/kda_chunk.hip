@@ -2019,6 +2019,14 @@ size_t prefill_workspace_bytes(int32_t num_seqs, int64_t num_tokens, int32_t H, 
   return layout_for(num_seqs, num_tokens, H, K, V).total;
 }
 
+void prefill_workspace_maps(int32_t num_seqs, int64_t num_tokens, int32_t H, int32_t K, int32_t V,
+                            size_t* offset, size_t* item_bytes, int64_t* items) {
+  const Layout L = layout_for(num_seqs, num_tokens, H, K, V);
+  *offset = L.maps;
+  *item_bytes = (static_cast<size_t>(K) * K + static_cast<size_t>(K) * V) * 4;
+  *items = L.map_bound * H;
+}
+
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream, hipEvent_t after_plan) {
   const Layout L = layout_for(p.num_seqs, p.num_tokens, p.H, p.K, p.V);
   if (L.seg_bound > 0x7fffffff) return hipErrorInvalidValue;

@@ -110,6 +110,11 @@ struct PrefillParams {
 
 size_t prefill_workspace_bytes(int32_t num_seqs, int64_t num_tokens, int32_t H,
                                int32_t K, int32_t V);
+// The segment-map area of that workspace: its byte offset, the bytes of one
+// map item (M as bf16 hi then lo MFMA fragments, K*K*4 bytes, then B as
+// fp32 [K][V]) and the number of items (H times the map bound).
+void prefill_workspace_maps(int32_t num_seqs, int64_t num_tokens, int32_t H, int32_t K, int32_t V,
+                            size_t* offset, size_t* item_bytes, int64_t* items);
 // after_plan (optional) is recorded on the stream once the plan kernel is
 // launched, before the map and state passes.
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream, hipEvent_t after_plan = nullptr);

@@ -172,6 +172,23 @@ kda_status_t kda_spec_decode(int32_t num_seqs, int32_t tokens_per_seq,
 size_t kda_chunk_prefill_workspace_size(int32_t num_seqs, int64_t num_tokens,
                                         int32_t H, int32_t K, int32_t V);
 
+/* Diagnostics (a pure host computation): where the segment maps of a
+ * long-sequence prefill live in a workspace of these sizes. *offset is the
+ * byte offset of the map area, *item_bytes the size of one map item (the
+ * affine map S_out = M S_in + B of one segment of one head, chunked form of
+ * the delta rule in the vLLM PR #50649 kernel, Purpose: M as bf16 MFMA
+ * fragments, a hi part then a lo part, K*K*4 bytes together, then B as
+ * fp32 [K][V]; after the call B holds the next segment's initial state),
+ * *items the number of items the area holds (items beyond the ones a call
+ * plans are left as they were). All three outputs are host pointers owned
+ * by the caller. Errors: KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED. */
+kda_status_t kda_chunk_prefill_workspace_maps(int32_t num_seqs,
+                                              int64_t num_tokens, int32_t H,
+                                              int32_t K, int32_t V,
+                                              size_t* offset,
+                                              size_t* item_bytes,
+                                              int64_t* items);
+
 /*
  * Chunked prefill at chunk size 64 (vLLM PR #50649, Purpose:
  * chunk_kda_with_fused_gate and recompute_w_u).

@@ -214,3 +214,17 @@ def test_binding_refuses_host_tensors_listing_each():
                               torch.zeros(4, dtype=torch.int32))
     reasons = ei.value.reasons
     assert sum("must be on a GPU" in r for r in reasons) == 7
+
+
+def test_workspace_maps_query():
+    """The segment-map area lies inside the workspace; one item is M (K*K*4
+    bytes of bf16 hi/lo fragments) plus B (fp32 K*V); an 8192-token sequence
+    at H = 32 has 8 map items per head."""
+    off, item, n = kda.kda_chunk_prefill_workspace_maps(1, 8192, 32, 128, 128)
+    assert item == (128 * 128 + 128 * 128) * 4 and n == 8 * 32
+    assert off % 256 == 0 and off + n * item <= kda.kda_chunk_prefill_workspace_size(1, 8192, 32, 128, 128)
+    off2, item2, n2 = kda.kda_chunk_prefill_workspace_maps(64, 8192, 32, 64, 128)
+    assert item2 == (64 * 64 + 64 * 128) * 4 and off2 + n2 * item2 <= \
+        kda.kda_chunk_prefill_workspace_size(64, 8192, 32, 64, 128)
+    with pytest.raises(kda.KdaError):
+        kda.kda_chunk_prefill_workspace_maps(1, 8192, 32, 96, 128)

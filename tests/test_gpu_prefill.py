@@ -15,8 +15,8 @@ import torch
 
 import gated_delta_rule_45_amd as kda
 import workloads as W
-from kda_testlib import (DECODE_TOL_O, DECODE_TOL_S, PREFILL_TOL_O, PREFILL_TOL_S, check_case, log,
-                         rel_err, run_gpu, run_oracle, to_device)
+from kda_testlib import (DECODE_TOL_O, DECODE_TOL_S, PREFILL_TOL_O, PREFILL_TOL_S, cast_aware_err,
+                         check_case, log, rel_err, run_gpu, run_oracle, to_device)
 from oracle import oracle as O
 
 pytestmark = pytest.mark.gpu
@@ -123,7 +123,28 @@ def test_prefill_is_deterministic():
 
 
 def test_mixed_batch_4096():
-    check_case(W.mixed_4096(), PREFILL_TOL_O, PREFILL_TOL_S)
+    """cfg4 at full size: the batch at the prefill bars, and its 96 decode
+    rows (recurrent kernel, 128-column tiles) also at the decode bars
+    (cast-aware output error <= 2e-3, state <= 1e-3) and bit-identical to a
+    plain decode call on the same rows."""
+    case = W.mixed_4096()
+    ref_out, ref_fs = run_oracle(case)
+    check_case(case, PREFILL_TOL_O, PREFILL_TOL_S, oracle=(ref_out, ref_fs))
+    D = case.num_decodes
+    dc = to_device(case)
+    out = run_gpu(dc)
+    got = out[:D].float().cpu().numpy().astype(np.float64)
+    e_oc = cast_aware_err(got, ref_out[:D])
+    slots = case.state_indices[:D].tolist()
+    got_s = dc.pool[torch.tensor(slots, device=dc.pool.device)].cpu().numpy().astype(np.float64)
+    e_s = rel_err(got_s, np.stack([ref_fs[i] for i in range(D)]))
+    log(f"[case] mixed_4096 decode rows: e_o_cast={e_oc:.3e} e_S={e_s:.3e}")
+    assert e_oc <= DECODE_TOL_O and e_s <= DECODE_TOL_S
+    dc2 = to_device(case)
+    i = dc2.inputs
+    out_dec, _ = kda.kda_decode_packed(i["mixed_qkv"][:D], i["raw_g"][:D], i["raw_beta"][:D], i["A_log"],
+                                       i["dt_bias"], case.lower_bound, dc2.pool, dc2.state_indices[:D])
+    assert torch.equal(out[:D], out_dec)
 
 
 def test_mixed_batch_decode_rows_match_decode_kernel():
@@ -288,3 +309,57 @@ def test_mixed_batches_from_two_host_threads():
                      for i, s in enumerate(idx) if s >= 0)
             log(f"[case] thread {n}: e_o={e:.3e} e_S={es:.3e}")
             assert e <= PREFILL_TOL_O and es <= PREFILL_TOL_S
+
+
+@pytest.mark.parametrize("cu", [[0, 100, 50, 200], [0, 100, 150, 190], [5, 100, 150, 200]],
+                         ids=["decreasing", "short_of_num_tokens", "not_from_zero"])
+def test_prefill_bad_cu_seqlens_sets_status_and_nan_rows(cu):
+    """cu_seqlens outside the contract (the host never reads them, so the
+    call itself succeeds): the workspace's status word becomes
+    KDA_PREFILL_BAD_CU_SEQLENS, every output row is NaN and no slot changes.
+    A valid call on the same workspace then clears the status."""
+    case = W.prefill_case("bad_cu", 4, 128, 128, [100, 50, 50], 8, -5.0, seed=641)
+    dc = to_device(case)
+    i = dc.inputs
+    snapshot = dc.pool.clone()
+    T = 200
+    ws = torch.empty(kda.kda_chunk_prefill_workspace_size(3, T, 4, 128, 128), dtype=torch.uint8,
+                     device="cuda")
+    bad = torch.tensor(cu, dtype=torch.int32, device="cuda")
+    out, _ = kda.kda_chunk_prefill(i["mixed_qkv"], i["raw_g"], i["raw_beta"], i["A_log"], i["dt_bias"],
+                                   -5.0, dc.pool, dc.state_indices, bad, workspace=ws)
+    torch.cuda.synchronize()
+    assert kda.prefill_status(ws) == kda.PREFILL_BAD_CU_SEQLENS
+    assert torch.isnan(out.float()).all()
+    assert torch.equal(dc.pool, snapshot)
+    out2, _ = kda.kda_chunk_prefill(i["mixed_qkv"], i["raw_g"], i["raw_beta"], i["A_log"], i["dt_bias"],
+                                    -5.0, dc.pool, dc.state_indices, dc.cu_seqlens, workspace=ws)
+    torch.cuda.synchronize()
+    assert kda.prefill_status(ws) == 0
+    assert torch.isfinite(out2.float()).all()
+    log(f"[case] bad cu_seqlens {cu}: status word set, {out.numel()} NaN outputs, slots untouched")
+
+
+@pytest.mark.parametrize("lower_bound", [-5.0, None])
+def test_prefill_cut_sequence_weak_decay(lower_bound):
+    """With dt_bias shifted down by 10 the per-token decay is close to 1
+    (|g| ~ 1e-4), so a segment's map M stays far from zero and the scan's
+    composition S_{j+1} = M_j S_j + B_j carries real weight (with the pages'
+    gate inputs M underflows to zero over a segment). A 4096-token sequence
+    at H = 8 is cut into segments; parity at the prefill bars, and the
+    workspace maps must hold a sizeable M."""
+    case = W.prefill_case("cut_weak_decay", 8, 128, 128, [4096, 300], 8, lower_bound, seed=821)
+    case.inputs["dt_bias"] = case.inputs["dt_bias"] - 10.0
+    check_case(case, PREFILL_TOL_O, PREFILL_TOL_S)
+    dc = to_device(case)
+    T, H, K, V = 4396, 8, 128, 128
+    ws = torch.zeros(kda.kda_chunk_prefill_workspace_size(2, T, H, K, V), dtype=torch.uint8, device="cuda")
+    i = dc.inputs
+    kda.kda_chunk_prefill(i["mixed_qkv"], i["raw_g"], i["raw_beta"], i["A_log"], i["dt_bias"],
+                          lower_bound, dc.pool, dc.state_indices, dc.cu_seqlens, workspace=ws)
+    torch.cuda.synchronize()
+    off, item, n = kda.kda_chunk_prefill_workspace_maps(2, T, H, K, V)
+    m = ws[off:off + n * item].view(n, item)[:, :K * K * 4].contiguous().view(torch.bfloat16).float()
+    m_max = float(m.abs().max())
+    log(f"[case] cut_weak_decay lb={lower_bound}: max|M| = {m_max:.3e}")
+    assert m_max > 0.05
