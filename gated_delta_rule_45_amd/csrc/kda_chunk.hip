@@ -488,6 +488,7 @@ struct FusedSmem {
   uint16_t wkt_own[EXACT ? 8 : K * C];
   float at[C * C];               // A^T strictly above the diagonal, then T = (I+A)^{-1} below it
   float x[XLayout<K>::end];
+  float nrm[Q ? C * 8 : 1];      // output epilogue: sum of squares of each position over each wave's columns
   __device__ uint16_t* wkt() {
     if constexpr (EXACT) return t.wkt;
     else return wkt_own;
@@ -503,6 +504,7 @@ struct ChunkIn {
   static constexpr int PP = Roles<K>::PP;
   u32x2 rgw[PP];                      // raw_g of the thread's 4 channels at its PP positions
   uint32_t rb;                        // raw beta (bf16 bits, zero-extended) of position tid
+  u32x2 zg[4];                        // output epilogue gate of the lane's output elements (state pass)
   uint32_t vpre[2][8];                // v operands of U (waves w < V / 16, zero-extended): lane (m, g) needs
                                       // v[32 kb + 8 g + j][16 w + m]
 };
@@ -548,6 +550,17 @@ __device__ __forceinline__ void load_chunk_v_regs(const PrefillParams& p, int h,
   }
 }
 
+// Sum of x over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lane groups of a
+// wave), in every lane and in the same order everywhere: the row swaps
+// v_permlane16_swap / v_permlane32_swap with both operands x leave x of
+// the partner row (group) in the second result.
+__device__ __forceinline__ float sum_lane_groups(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Makes the registers of a tile array look freshly written (waiting for
 // any loads into them to land, here).
 template <int N>
@@ -556,6 +569,22 @@ __device__ __forceinline__ void pin_regs(f32x4 (&a)[N]) {
   for (int i = 0; i < N; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(a[i][j]));
+}
+
+// Issues the loads of the output epilogue's gate for chunk (t0, n): lane
+// (m, g) of wave w takes channels 16 w + 4 g .. + 3 of positions 16 pb + m
+// (rows past the chunk end read zero). Issued at the top of the chunk, so
+// the intra part hides their latency.
+template <int K, int V>
+__device__ __forceinline__ void load_chunk_norm_regs(const PrefillParams& p, int h, ChunkPos cp, ChunkIn<K, V>& in) {
+  const int tid = opaque_tid(), lane = tid & 63, w = uniform(tid >> 6);
+  const int m = lane & 15, g = lane >> 4;
+  const int64_t grs = p.norm.gate_row_stride;
+  const __amdgpu_buffer_rsrc_t rz = make_rsrc(p.norm.gate + cp.t0 * grs, static_cast<uint32_t>(cp.n * grs * 2));
+  const int zl = static_cast<int>(m * grs + h * V + 16 * w + 4 * g) * 2;
+#pragma unroll
+  for (int pb = 0; pb < 4; ++pb)
+    in.zg[pb] = __builtin_amdgcn_raw_buffer_load_b64(rz, zl + static_cast<int>(16 * pb * grs * 2), 0, 0);
 }
 
 // Holds the v operands as the 16 registers their loads write, late in a
@@ -1571,6 +1600,14 @@ __device__ __forceinline__ void state_segment(const PrefillParams& p, const SegP
   pin_regs(S);
 
   stage_gate_consts<K>(p, h, sm.x);
+  // Gated RMSNorm output epilogue (optional; vLLM PR #60683, Purpose, places
+  // it after the recurrence): y = o / sqrt(mean over the head's V channels
+  // of o^2 + eps) * weight * act(gate), applied to the fp32 output before
+  // its bf16 store. The workgroup holds every value column of its
+  // positions, so one exchange of per-wave sums of squares per chunk does.
+  const bool has_norm = p.norm.gate != nullptr;  // uniform
+  f32x4 nw = {1.f, 1.f, 1.f, 1.f};               // the norm weights of the lane's four channels
+  if (has_norm && has_cols) nw = *reinterpret_cast<const f32x4*>(p.norm.weight + col0 + 4 * g);
   // Lane (m, g) of the transposed output tile of position block pb holds
   // channels col0 + 4 g .. + 3 of position 16 pb + m: 8 contiguous bytes.
   const auto& ops = sm.r.ops;
@@ -1581,6 +1618,7 @@ __device__ __forceinline__ void state_segment(const PrefillParams& p, const SegP
     // done with the previous chunk's operands.
     if (has_cols) chunk_barrier<4>();
     else chunk_barrier<0>();
+    if (has_norm && has_cols) load_chunk_norm_regs<K, V>(p, h, cp, in);
     f32x4 Vp[4];
     const bool more = cc + 1 < sr.nch;
     const ChunkPos np = chunk_pos(sr, more ? cc + 1 : cc);
@@ -1592,7 +1630,8 @@ __device__ __forceinline__ void state_segment(const PrefillParams& p, const SegP
       if constexpr (EXACT) dma_chunk_tiles<K, true>(p, h, np, sm.t.f.k, sm.t.f.q);
     }
     if (!has_cols) {
-      if (more) pin_gate_regs<K, V>(in);  // (no v operands without columns)
+      pin_gate_regs<K, V>(in);            // (no v operands without columns)
+      if (has_norm) lds_barrier();        // the epilogue's exchange below
       continue;
     }
     const int m = opaque_tid() & 15, g = (opaque_tid() & 63) >> 4;
@@ -1661,12 +1700,46 @@ __device__ __forceinline__ void state_segment(const PrefillParams& p, const SegP
     // Rows of the chunk as one buffer range: positions past its end fall
     // outside and their stores are dropped, so every lane issues exactly 4
     // stores, the last vector-memory operations of the chunk.
+    if (has_norm) {
+      // Sum of squares of each position over the wave's 16 columns (lanes
+      // m, m + 16, m + 32, m + 48 hold one position), posted per wave by
+      // lanes 0..15.
+      float ss[4];
+#pragma unroll
+      for (int pb = 0; pb < 4; ++pb)
+        ss[pb] = sum_lane_groups(Ot[pb][0] * Ot[pb][0] + Ot[pb][1] * Ot[pb][1] + Ot[pb][2] * Ot[pb][2] +
+                                 Ot[pb][3] * Ot[pb][3]);
+      if (g == 0) {
+#pragma unroll
+        for (int pb = 0; pb < 4; ++pb) sm.nrm[(16 * pb + m) * 8 + w] = ss[pb];
+      }
+      lds_barrier();
+#pragma unroll
+      for (int pb = 0; pb < 4; ++pb) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(&sm.nrm[(16 * pb + m) * 8]);
+        float tot = a[0] + a[1] + a[2] + a[3];
+        if constexpr (V / 16 > 4) {
+          const f32x4 b = *reinterpret_cast<const f32x4*>(&sm.nrm[(16 * pb + m) * 8 + 4]);
+          tot += b[0] + b[1] + b[2] + b[3];
+        }
+        // Hardware reciprocal square root (about 1 ulp; the result is cast to bf16).
+        const float inv = __builtin_amdgcn_rsqf(tot * (1.0f / V) + p.norm.eps);
+        const float z[4] = {__uint_as_float(in.zg[pb][0] << 16), __uint_as_float(in.zg[pb][0] & 0xffff0000u),
+                            __uint_as_float(in.zg[pb][1] << 16), __uint_as_float(in.zg[pb][1] & 0xffff0000u)};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float sg = sigmoid_f32(z[j]);
+          const float act = p.norm.activation == 1 ? z[j] * sg : sg;
+          Ot[pb][j] = Ot[pb][j] * inv * nw[j] * act;
+        }
+      }
+    }
     // The next chunk's v operands have had the products above to land; held
     // here, ahead of the stores, so that nothing later waits on them.
-    if (more) {
-      pin_v_regs<K, V>(in);
-      pin_gate_regs<K, V>(in);
-    }
+    // (Unconditional: the last chunk's pins are no-ops, but every path
+    // through the loop then carries them.)
+    pin_v_regs<K, V>(in);
+    pin_gate_regs<K, V>(in);
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.out + cp.t0 * HV, static_cast<uint32_t>(cp.n * HV * 2));
 #pragma unroll
     for (int pb = 0; pb < 4; ++pb)
@@ -2055,9 +2128,8 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream, hipEvent_t
   else if (p.K == 64 && p.V == 128) e = launch_k<64, 128>(p, L, pl, stream);
   else if (p.K == 128 && p.V == 64) e = launch_k<128, 64>(p, L, pl, stream);
   else e = launch_k<128, 128>(p, L, pl, stream);
-  // Output epilogue: applied as a pass over the output.
-  if (e != hipSuccess || p.norm.gate == nullptr) return e;
-  return launch_gated_rmsnorm(p.norm, p.out, p.num_tokens, p.H, p.V, stream);
+  // The output epilogue (p.norm) is applied inside the state passes.
+  return e;
 }
 
 }  // namespace kda

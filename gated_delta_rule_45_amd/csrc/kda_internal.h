@@ -96,7 +96,7 @@ struct PrefillParams {
   const int32_t* indices;
   int64_t index_stride;
   uint16_t* out;
-  OutNorm norm;             // applied to out after the state pass
+  OutNorm norm;             // output epilogue, applied in the state passes (gate null: none)
   const int32_t* cu_seqlens;
   const uint8_t* has_initial_state;  // may be null
   int32_t num_seqs;

@@ -4,8 +4,8 @@
 //   y_j = o_j / sqrt(mean_j' o_j'^2 + eps) * weight[j] * act(gate_j)
 // per row and head over the head's V channels, act(z) = sigmoid(z) or
 // z * sigmoid(z). Used where no workgroup of the producing kernel holds a
-// head's whole row (narrow decode column tiles, the prefill state pass, whose
-// two workgroups per head each hold half of the columns).
+// head's whole row (narrow decode column tiles); the prefill state pass
+// applies it itself.
 //
 // HBM-bound elementwise work with one reduction per (row, head): a group of
 // V/8 lanes owns a (row, head), each lane 8 consecutive channels (one 16-byte
