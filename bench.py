@@ -156,14 +156,18 @@ def measured_traffic():
     return d.get("hbm_bytes_per_launch")
 
 
-def leg_decode(steps, warmup, with_norm=False):
+def _lb(lower_bound) -> str:
+    return "None" if lower_bound is None else f"{lower_bound:g}"
+
+
+def leg_decode(steps, warmup, with_norm=False, stride=8, lower_bound=-5.0):
     import torch
 
     import gated_delta_rule_45_amd as kda
     import workloads as W
 
     dev = torch.device("cuda")
-    H, K, V, N, STRIDE, SETS = 32, 128, 128, 32, 8, 16
+    H, K, V, N, STRIDE, SETS = 32, 128, 128, 32, stride, 16
     pool = _device_pool(N * SETS, H, K, V, 0.05, 1999, dev)
     inp = _device_token_inputs(N, H, K, V, 1020, dev)
     perm = torch.randperm(N * SETS, generator=W._gen(1021)).to(torch.int32)
@@ -180,14 +184,15 @@ def leg_decode(steps, warmup, with_norm=False):
 
     def step(i):
         kda.kda_decode_packed(inp["mixed_qkv"], inp["raw_g"], inp["raw_beta"], inp["A_log"],
-                              inp["dt_bias"], -5.0, pool, tables[i % SETS][:, 0], out=out, norm=norm)
+                              inp["dt_bias"], lower_bound, pool, tables[i % SETS][:, 0], out=out, norm=norm)
 
     eager_ms = eager_time(step, steps, warmup)
     ms, timed = graph_time(step, SETS, steps, warmup)
     state_bytes = 2 * N * H * K * V * 4
     alg_bytes = state_bytes + token_io_bytes(N, H, K, V) + (N * H * V * 2 if with_norm else 0)
     return {
-        "workload": "batched_decode_h32_k128_n32_stride8_lb-5" + ("_gated_rmsnorm" if with_norm else ""),
+        "workload": f"batched_decode_h32_k128_n32_stride{stride}_lb{_lb(lower_bound)}" +
+                    ("_gated_rmsnorm" if with_norm else ""),
         "ms_per_step": ms, "eager_ms_per_step": eager_ms, "steps_timed": timed,
         "state_gbs": state_bytes / (ms * 1e-3) / 1e9,
         "alg_bytes_per_launch": alg_bytes,
@@ -292,7 +297,7 @@ def prefill_io_bytes(T, H, K, V, seqs):
     return token_io_bytes(T, H, K, V) + 2 * seqs * H * K * V * 4
 
 
-def leg_prefill(steps, warmup, lens, name, seed, with_norm=False):
+def leg_prefill(steps, warmup, lens, name, seed, with_norm=False, lower_bound=-5.0):
     import torch
 
     import gated_delta_rule_45_amd as kda
@@ -317,7 +322,7 @@ def leg_prefill(steps, warmup, lens, name, seed, with_norm=False):
     def step(i):
         inp = inps[i % copies]
         kda.kda_chunk_prefill(inp["mixed_qkv"], inp["raw_g"], inp["raw_beta"], inp["A_log"],
-                              inp["dt_bias"], -5.0, pool, idx[i % 2], cu, out=out, workspace=ws,
+                              inp["dt_bias"], lower_bound, pool, idx[i % 2], cu, out=out, workspace=ws,
                               norm=norm)
 
     ms, _ = graph_time(step, copies, steps, warmup)
@@ -334,6 +339,102 @@ def leg_prefill(steps, warmup, lens, name, seed, with_norm=False):
         "useful_flops_per_step": flops,
         "io_bytes_per_step": io,
     }
+
+
+PREFILL_COUNTERS_FILE = os.path.join(ROOT, "profiles", "chunk_prefill_kernels_counters.json")
+PREFILL_SOURCES = ("kda_chunk.hip", "kda_device.h", "kda_internal.h")
+
+
+def prefill_kernel_hash() -> str:
+    """Hash of every source the chunked-prefill kernels are compiled from."""
+    h = hashlib.sha256()
+    for name in PREFILL_SOURCES:
+        h.update(open(os.path.join(ROOT, "gated_delta_rule_45_amd", "csrc", name), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def prefill_counters(workload: str):
+    """The committed rocprofv3 counter summary of one prefill workload (per
+    kernel: mean duration, HBM bytes from FETCH_SIZE x 2 / WRITE_SIZE x 1, MFMA
+    busy and executed MFMA flops), only if it was taken on the current
+    prefill kernel sources."""
+    try:
+        d = json.load(open(PREFILL_COUNTERS_FILE))
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_sha256_16") != prefill_kernel_hash():
+        return None
+    return d.get("workloads", {}).get(workload)
+
+
+def prefill_roofline(leg: dict):
+    """Roofline of a prefill call: co-bound by bf16 MFMA (useful flops of the
+    chunked algorithm) and HBM (mandatory I/O), with the measured traffic and
+    the per-kernel counters when a matching summary is committed."""
+    ms = leg["ms_per_step"]
+    r = {"bound": "co-bound",
+         "mfma_frac": leg["mfma_frac"], "mfma_achieved_tflops": leg["useful_tflops"],
+         "mfma_peak_tflops": BF16_DENSE_TFLOPS,
+         "hbm_frac": leg["hbm_frac"], "hbm_achieved_gbs": leg["io_gbs"], "hbm_peak_gbs": HBM_PEAK_GBS,
+         "alg_flops_per_call": leg["useful_flops_per_step"], "alg_bytes_per_call": leg["io_bytes_per_step"],
+         "traffic": None}
+    c = prefill_counters(leg["workload"])
+    if c is not None:
+        kernels = c["kernels"]
+        dom = max(kernels, key=lambda k: kernels[k]["us"])
+        traffic = sum(k["hbm_bytes"] for k in kernels.values())
+        mops = sum(k.get("mfma_flops", 0) for k in kernels.values())
+        r.update({
+            "traffic": traffic,
+            "traffic_over_algorithmic": round(traffic / leg["io_bytes_per_step"], 3),
+            "dominant_kernel": dom, "dominant_kernel_us": kernels[dom]["us"],
+            "dominant_kernel_mfma_busy": kernels[dom].get("mfma_busy"),
+            "counter_mfma_tflops": round(mops / (ms * 1e-3) / 1e12, 2),
+            "counter_mfma_frac": round(mops / (ms * 1e-3) / 1e12 / BF16_DENSE_TFLOPS, 5),
+            "kernels": kernels, "counters_from": os.path.relpath(PREFILL_COUNTERS_FILE, ROOT),
+        })
+    return r
+
+
+def _cpu_threads() -> int:
+    """Cores the oracle may use: the OpenMP allowance if one is set (the
+    box's CPU share), else every core the process sees."""
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    return int(env) if env.isdigit() and int(env) > 0 else (os.cpu_count() or 1)
+
+
+def cpu_prefill_baseline(lens, full_tokens: int, seconds: float):
+    """The fp64 oracle (recurrent form, as it stands) on head samples of a
+    prefill config, single-threaded (one head) and on every core (one head
+    per core, OpenMP over (sequence, head) pairs), each repeated for about
+    ``seconds``; tokens/s scaled to the config's 32 heads and full_tokens
+    (heads are independent and the recurrence's cost is linear in tokens)."""
+    import workloads as W
+    from oracle import oracle as O
+
+    H, K, V = 32, 128, 128
+    T = sum(lens)
+    res = {}
+    for key, threads in (("single_thread", 1), ("all_core", _cpu_threads())):
+        heads = min(max(threads, 1), H)
+        case = W.prefill_case("cpu_sample", heads, K, V, lens, len(lens), -5.0, seed=3900)
+        O.set_threads(threads)
+        cu = case.cu_seqlens.tolist()
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            O.prefill(case.inputs, case.pool, case.state_indices, cu, heads, K, V, lower_bound=-5.0,
+                      return_pool=False)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+        per_call = el / reps * (H / heads) * (full_tokens / T)
+        res[key] = {"value": round(full_tokens / per_call, 1), "unit": "tokens/s", "cores": O.max_threads(),
+                    "kind": "oracle",
+                    "sample": f"{reps} x {heads} head(s) of {len(lens)} sequence(s), {T} tokens, K=V=128, "
+                              f"fp64 recurrent oracle, {el:.1f} s wall; scaled to 32 heads and "
+                              f"{full_tokens} tokens"}
+    return res
 
 
 def leg_conv(steps, warmup, lens, name, seed):
@@ -408,21 +509,28 @@ def cpu_baseline(seconds: float):
 
     H, K, V, N = 32, 128, 128, 32
     case = W.decode_case("cpu_sample", H, K, V, N, 1, N, 8, -5.0, seed=1020, pool_seed=77)
-    O.set_threads(os.cpu_count() or 1)
-    O.decode_packed(case.inputs, case.pool, case.state_indices, H, K, V, 1, -5.0)  # load, warm
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        O.decode_packed(case.inputs, case.pool, case.state_indices, H, K, V, 1, -5.0)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    state_bytes = 2 * N * H * K * V * 4 * reps
-    return {"value": round(state_bytes / el / 1e9, 3), "unit": "GB/s", "cores": O.max_threads(),
-            "kind": "oracle",
-            "sample": f"{reps} repeats of the 32-request batched decode (H=32, K=V=128) through "
-                      f"the fp64 recurrent oracle on a 32-slot pool, {el:.1f} s wall"}
+
+    def run(threads, secs):
+        O.set_threads(threads)
+        O.decode_packed(case.inputs, case.pool, case.state_indices, H, K, V, 1, -5.0)  # load, warm
+        reps = 0
+        t0 = time.perf_counter()
+        while True:
+            O.decode_packed(case.inputs, case.pool, case.state_indices, H, K, V, 1, -5.0)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= secs:
+                break
+        state_bytes = 2 * N * H * K * V * 4 * reps
+        return {"value": round(state_bytes / el / 1e9, 3), "unit": "GB/s", "cores": O.max_threads(),
+                "kind": "oracle",
+                "sample": f"{reps} repeats of the 32-request batched decode (H=32, K=V=128) through "
+                          f"the fp64 recurrent oracle on a 32-slot pool, {el:.1f} s wall"}
+
+    single = run(1, seconds / 4)
+    res = run(_cpu_threads(), seconds)
+    res["single_thread"] = single
+    return res
 
 
 def main():
@@ -444,17 +552,37 @@ def main():
 
     dec = leg_decode(args.steps, args.warmup)
     extra = {}
+    if "decode" in legs:
+        # The other decode variants of the configuration: stride 1, and no lower bound.
+        for key, kw in (("decode_stride1", {"stride": 1}), ("decode_lbNone", {"lower_bound": None})):
+            d = leg_decode(args.steps, args.warmup, **kw)
+            extra[key] = {k: (round(v, 5) if isinstance(v, float) else v) for k, v in d.items()
+                          if k != "steps_timed"}
+            extra[key]["hbm_frac"] = round(d["achieved_gbs"] / HBM_PEAK_GBS, 4)
     if "spec" in legs:
         extra["spec_verify"] = leg_spec(max(args.steps // 4, 64), 16)
         extra["spec_decode_per_token_states"] = leg_spec_states(max(args.steps // 4, 64), 16)
-    if "prefill" in legs:
-        import workloads as W
+    import workloads as W
 
-        pf_steps = max(args.steps // 32, 6)
-        extra["prefill_t8192"] = leg_prefill(pf_steps, 2, [8192], "prefill_t8192_h32_k128", 3000)
-        extra["prefill_varlen64"] = leg_prefill(pf_steps, 2, W.random_lengths(64, 1, 256, 3001, force_ones=2),
-                                                "prefill_varlen64_h32_k128", 3002)
-        extra["prefill_t65536"] = leg_prefill(max(pf_steps // 2, 4), 1, [65536], "prefill_t65536_h32_k128", 3004)
+    pf_steps = max(args.steps // 32, 6)
+    vl = W.random_lengths(64, 1, 256, 3001, force_ones=2)
+    # name -> (lengths, workload, seed, steps, warmup, lower bound, CPU sample lengths, full tokens);
+    # "--legs prefill" runs them all, "--legs prefill_t8192" (etc.) one of them.
+    prefill_legs = {
+        "prefill_t8192": ([8192], "prefill_t8192_h32_k128", 3000, pf_steps, 2, -5.0, [8192], 8192),
+        "prefill_varlen64": (vl, "prefill_varlen64_h32_k128", 3002, pf_steps, 2, -5.0, vl, sum(vl)),
+        "prefill_t65536": ([65536], "prefill_t65536_h32_k128", 3004, max(pf_steps // 2, 4), 1, -5.0,
+                           [8192], 65536),
+        "prefill_t8192_lbNone": ([8192], "prefill_t8192_h32_k128_lbNone", 3000, pf_steps, 2, None, None, 0),
+    }
+    for key, (lens, wl, seed, st, wu, lb, lens_s, full) in prefill_legs.items():
+        if "prefill" not in legs and key not in legs:
+            continue
+        leg = leg_prefill(st, wu, lens, wl, seed, lower_bound=lb)
+        leg["roofline"] = prefill_roofline(leg)
+        if lens_s is not None and not args.no_cpu_baseline:
+            leg["cpu_baseline"] = cpu_prefill_baseline(lens_s, full, args.cpu_seconds / 5)
+        extra[key] = leg
     if "mixed" in legs:
         extra["mixed_4096"] = leg_mixed(max(args.steps // 16, 9), 9)
     if "conv" in legs:
@@ -465,7 +593,7 @@ def main():
                                                 "conv_prologue_t8192_h32_k128_w4", 3101)
     if "norm" in legs:
         # Gated RMSNorm output epilogue: inside the decode kernel (whole-row
-        # tiles), and as a pass after the prefill state pass.
+        # tiles) and inside the prefill state pass.
         d = leg_decode(args.steps, args.warmup, with_norm=True)
         extra["decode_gated_rmsnorm"] = {k: (round(v, 5) if isinstance(v, float) else v)
                                          for k, v in d.items() if k != "steps_timed"}

@@ -237,16 +237,17 @@ __device__ __forceinline__ void chunk_barrier() {
 // workgroups per cut (sequence, head).
 //
 // A sequence is cut into at most ceil(chunks / kSegMinChunks) segments of
-// equal length (the last may be shorter), into no more segments than it
-// takes for the cut sequences' workgroups of one launch to occupy
-// kChipSlots slots (one per compute unit: a workgroup's LDS takes most of a
-// CU), and only into kMinCut segments or more: a map chunk costs about as
-// much as a state chunk, so two segments would not shorten the chain.
-constexpr int kSegMinChunks = 12;
-constexpr int kMaxSegs = 13;  // <= kSegMinChunks + 1: keeps the last segment non-empty
+// balanced lengths (they differ by at most one chunk; only the last chunk of
+// the sequence may be partial, so every segment but the last is made of
+// full chunks), into no more segments than it takes for the cut sequences'
+// workgroups of one launch to occupy kChipSlots slots (one per compute
+// unit: a workgroup's LDS takes most of a CU), and only into kMinCut
+// segments or more: a map chunk costs about as much as a state chunk, so two
+// segments would not shorten the chain.
+constexpr int kSegMinChunks = 6;
+constexpr int kMaxSegs = 16;
 constexpr int kMinCut = 3;
 constexpr int kChipSlots = 256;
-static_assert(kMaxSegs <= kSegMinChunks + 1, "segment count bound");
 
 // Device-side plan of one prefill call, written by plan_kernel. counts[0]
 // is the call's status word (workspace offset 0): 0 when cu_seqlens keep to
@@ -343,7 +344,8 @@ __device__ __forceinline__ int segments_of(int nch, int target) {
 // Checks cu_seqlens (starts at 0, non-decreasing, ends at num_tokens) and
 // plans chunks and segments of every sequence. The segment target is the
 // number of segments each cut sequence needs for the cut sequences' n - 1
-// workgroups per launch together to occupy the chip. With cu_seqlens outside the contract the status word
+// workgroups per launch, with the uncut sequences' ones, to occupy the
+// chip. With cu_seqlens outside the contract the status word
 // is set and no segment exists: the state pass then writes NaN to every
 // output row and touches no state.
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* cu, int32_t N, int32_t H, SegPlan pl) {
@@ -352,18 +354,27 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* cu, i
   const int per = (N + kPlanThreads - 1) / kPlanThreads;
   const int b = tid * per;
   const int e = min(N, b + per);
-  int bad = 0, nl = 0;
+  int bad = 0, nl = 0, nw = 0;
   for (int i = b; i < e; ++i) {
     bad |= cu[i + 1] < cu[i];
-    nl += chunks_of(cu, i) > (kMinCut - 1) * kSegMinChunks;  // can be cut
+    const int nch = chunks_of(cu, i);
+    nl += nch > (kMinCut - 1) * kSegMinChunks;  // can be cut
+    nw += nch > 0 && nch <= (kMinCut - 1) * kSegMinChunks;  // stays whole
   }
   if (tid == 0) bad |= cu[0] != 0 || cu[N] != pl.num_tokens;
   int nbad;
   block_exclusive_scan(bad, part, nbad);
   int n_long;
   block_exclusive_scan(nl, part, n_long);
-  const int units = H * max(n_long, 1);
-  const int target = min(pl.max_segs, (kChipSlots + units - 1) / units + 1);
+  int n_whole;
+  block_exclusive_scan(nw, part, n_whole);
+  // Each launch holds a slot per (item, head); the uncut sequences' state
+  // passes run in the second launch beside the later segments, so they take
+  // slots from the cut sequences' budget there. Every cut sequence gets at
+  // least kMinCut segments.
+  const int slots = (kChipSlots + H - 1) / H;
+  const int budget = slots - n_whole;
+  const int target = min(pl.max_segs, 1 + max(kMinCut - 1, budget / max(n_long, 1)));
 
   int cc = 0, sc = 0, lc = 0;
   for (int i = b; i < e; ++i) {
@@ -1511,9 +1522,9 @@ __device__ __forceinline__ SegRange segment_range(const PrefillParams& p, const 
   r.nseg = uniform(pl.seg_start[r.seq + 1]) - r.seg0;
   r.sg = gs - r.seg0;
   const int nch_seq = uniform(pl.chunk_start[r.seq + 1]) - uniform(pl.chunk_start[r.seq]);
-  const int seg_len = (nch_seq + r.nseg - 1) / r.nseg;
-  r.c0 = r.sg * seg_len;
-  r.nch = min(nch_seq, r.c0 + seg_len) - r.c0;
+  // Balanced split: segment sg takes chunks [sg nch / nseg, (sg + 1) nch / nseg).
+  r.c0 = r.sg * nch_seq / r.nseg;
+  r.nch = (r.sg + 1) * nch_seq / r.nseg - r.c0;
   r.bos = uniform(static_cast<int64_t>(p.cu_seqlens[r.seq]));
   r.eos = uniform(static_cast<int64_t>(p.cu_seqlens[r.seq + 1]));
   return r;

@@ -64,10 +64,11 @@ def test_prefill_varlen_no_lower_bound():
 
 
 # Long sequences are cut into segments whose states are composed
-# (S_out = M S_in + B per segment) before every segment runs in parallel. At
-# H=3 these lengths cut three sequences into 3, 5 and 3 segments (shorter
-# than 16 chunks, the last ones ragged); the 1100-token sequence (18 chunks)
-# and the short ones stay whole.
+# (S_out = M S_in + B per segment) before every later segment runs in
+# parallel. At H=3 the sequences of more than 12 chunks (2100, 1100, 4200 and
+# 2500 tokens: 33, 18, 66 and 40 chunks) are cut into 6, 3, 11 and 7
+# segments of balanced lengths (the last chunks ragged); the short ones stay
+# whole.
 CUT = [2100, 5, 1100, 1, 4200, 64, 2500]
 
 
@@ -90,9 +91,8 @@ def test_prefill_cut_sequences_with_flags_and_null_slot():
 
 
 def test_prefill_many_sequences_with_a_cut_one():
-    """Enough sequences for the one-buffer state pass (16 sequences x 16
-    heads x 2 column halves = 512 workgroups, two per CU), one of them long
-    enough (47 chunks) to be cut into three segments."""
+    """Sixteen sequences at H = 16, one of them long enough (47 chunks) to
+    be cut (into 8 segments), beside short uncut ones."""
     lens = [3000, 1, 64, 65, 17, 130, 2, 90, 33, 127, 5, 64, 200, 1, 48, 77]
     case = W.prefill_case("one_buffer_cut", 16, 128, 128, lens, 24, -5.0, seed=681, std=0.1)
     check_case(case, PREFILL_TOL_O, PREFILL_TOL_S)
