@@ -27,19 +27,39 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
-    """Compiles every HIP source into one shared library and returns its path."""
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-I", CSRC, *sources(), "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
+def _run(cmd: list[str]) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "'-packed-fp32-ops' is not a recognized feature for this target (ignoring feature)"
     err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{err}")
-    if verbose and err.strip():
-        print(err)
+    return err
+
+
+def build(verbose: bool = False) -> str:
+    """Compiles every HIP source into an object (in parallel, one process
+    per source) and links them into one shared library; returns its path."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    srcs = sources()
+    objs = [os.path.join(objdir, os.path.basename(s)[:-4] + ".o") for s in srcs]
+    cmds = [[HIPCC, *FLAGS, "-c", "-I", INCLUDE, "-I", CSRC, s, "-o", o] for s, o in zip(srcs, objs)]
+    cmds = [[a for a in c if a != "-shared"] for c in cmds]
+    if verbose:
+        for c in cmds:
+            print(" ".join(c), flush=True)
+    workers = max(1, min(len(cmds), os.cpu_count() or 1, 8))
+    with ThreadPoolExecutor(workers) as ex:
+        errs = list(ex.map(_run, cmds))
+    tmp = LIB + ".tmp"
+    link = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
+    errs.append(_run(link))
+    if verbose:
+        for e in errs:
+            if e.strip():
+                print(e)
     os.replace(tmp, LIB)
     return LIB
 

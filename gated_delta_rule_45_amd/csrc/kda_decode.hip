@@ -40,8 +40,8 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kMaxTokens = 8;
-// Requests of at least this many tokens on tiles of at most 32 columns take
-// the block (WY) form of the token chain.
+// Requests of at least this many tokens in batches of fewer than 256
+// (request, head) pairs take the block (WY) form of the token chain.
 constexpr int kBlockMinTokens = 2;
 
 // Sum of x over the lanes that share lane % CG (CG = 4, 8, 16 or 32): a
@@ -307,127 +307,96 @@ void decode_kernel(const DecodeParams p) {
 
 namespace {
 
-// x rotated right by N lanes inside each 16-lane row (DPP row_ror).
-template <int N>
-__device__ __forceinline__ float row_ror(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + N, 0xf, 0xf, false));
-}
-
-// One step of a recursive halving over the row-group bits of the lane
-// index: lanes with bit B clear keep the lower HALF of their value list and
-// lanes with it set the upper half, each adding the partner's copy of the
-// half it keeps. Bits 2 and 3 pair lanes by DPP rotations inside a 16-lane
-// row (a rotation by 4 or 8 flips that bit; the step for the next bit
-// completes the coverage); bits 4 and 5 by v_permlane16_swap /
-// v_permlane32_swap, which leave the kept half's two copies in the two
-// operands. Every lane must be active.
-template <int B, int HALF, int N>
-__device__ __forceinline__ void halve_step(float (&x)[N], int lane) {
-  if constexpr (B < 4) {
-    const bool hi = (lane >> B) & 1;
-#pragma unroll
-    for (int v = 0; v < HALF; ++v) {
-      const float keep = hi ? x[HALF + v] : x[v];
-      const float send = hi ? x[v] : x[HALF + v];
-      x[v] = keep + row_ror<(B == 2 ? 4 : 8)>(send);
-    }
-  } else {
-#pragma unroll
-    for (int v = 0; v < HALF; ++v) {
-      const uint32_t lo = __float_as_uint(x[v]), up = __float_as_uint(x[HALF + v]);
-      const auto r = B == 4 ? __builtin_amdgcn_permlane16_swap(lo, up, false, false)
-                            : __builtin_amdgcn_permlane32_swap(lo, up, false, false);
-      x[v] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-    }
-  }
-}
-
-// Sums of the N values over the wave's row groups (lanes that share
-// lane % CG), N / (64 / CG) of them left per lane: block B of the list, the
-// lowest row-group bit being B's most significant bit.
-template <int CG, int N>
-__device__ __forceinline__ void halve_row_groups(float (&x)[N], int lane) {
-  constexpr int first = CG == 4 ? 2 : CG == 8 ? 3 : CG == 16 ? 4 : 5;
-  static_assert((64 / CG) <= N, "fewer values than row groups");
-  if constexpr (first <= 2) halve_step<2, (N >> (3 - first))>(x, lane);
-  if constexpr (first <= 3) halve_step<3, (N >> (4 - first))>(x, lane);
-  if constexpr (first <= 4) halve_step<4, (N >> (5 - first))>(x, lane);
-  halve_step<5, (N >> (6 - first))>(x, lane);
+// Orders this wave's LDS writes before its later LDS reads by other lanes
+// of the same wave (no other wave takes part).
+__device__ __forceinline__ void wave_lds_sync() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt = 0
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" ::: "memory");
 }
 
 }  // namespace
 
-// Spec-verify blocks of 2..8 tokens on narrow column tiles (the latency
-// case: few requests, one workgroup per CU). The per-token chain of the
-// decode kernel (a K-reduction, a cross-wave exchange and a barrier per
-// token) is replaced by the WY form of the block. With G_t the running sum
-// of the log decays through token t (per key channel):
+// Spec-verify blocks of 2..8 tokens on 16- or 32-column tiles (the latency
+// case: few requests, so a workgroup per (request, head, column tile)
+// spreads one step over the chip). The per-token chain of the decode kernel
+// (a K-reduction, a cross-wave exchange and a barrier per token) is replaced
+// by the WY form of the block. With G_t the running sum of the log decays
+// through token t (per key channel):
 //   S'_t^T k_t = X_t + sum_{s<t} A_ts u_s,   X_t = S0^T (e^{G_t} * k_t),
 //   S_t^T q_t  = Y_t + sum_{s<=t} P_ts u_s,  Y_t = S0^T (e^{G_t} * q_t),
 //   A_ts = sum_i k_s[i] k_t[i] e^{G_t[i] - G_s[i]},  P_ts likewise with q_t,
 // so u_t = beta_t (v_t - X_t - sum_{s<t} A_ts u_s) and
-// o_t = scale (Y_t + sum_{s<=t} P_ts u_s). Every reduction against the state
-// is taken at once from S0, then summed over the waves through LDS. On
-// 16-column tiles [X | Y] is a 16-column by 16-entry product over the K
-// rows, run on fp32 MFMA with the state held in the operand layout; on
-// 32-column tiles it is one recursive halving over the wave's row groups,
-// with the state held as float4 rows. The scalars A and P are formed while
-// the state loads are in flight; the u recurrence is per-column scalar work; and the
-// state then takes its tokens in registers, S = diag(e^{g_t}) S + k_t u_t^T
-// (stored after every token with a state per token). The exponents
-// G_t - G_s are never positive. NT is the token capacity (4 or 8).
-template <int K, int V, int VT, int NT>
+// o_t = scale (Y_t + sum_{s<=t} P_ts u_s): with M = I + diag(beta) A (unit
+// lower triangular) and d = v - X per column, u solves M u = diag(beta) d.
+// After the block, with C_t = e^{G_last - G_t} * k_t,
+//   S = diag(e^{G_last}) S0 + sum_t C_t u_t^T.
+// Schedule: the slot lookup goes out first, then every input load, then the
+// state loads; the decays (each channel's tokens split over lane groups of
+// one wave, their running sums joined by a lane swap) and the operand
+// tables are staged in LDS while the state is in flight. One barrier later
+// each wave forms its part of A and P (a fp32 MFMA product over its K/4
+// keys in the factored form) and of [X | Y] (a 16-column by 16-entry fp32
+// MFMA product over its rows, per column block); after a second barrier
+// every wave sums the partials it needs itself, so no further exchange
+// between the waves is needed: each lane solves M u = diag(beta) d for its
+// column by forward substitution, the state takes the whole block in one
+// more MFMA product (a rank-NT update) and is stored, and then o is formed
+// and stored. With a state per token (PT) the update instead runs token by
+// token, S = diag(e^{g_t}) S + k_t u_t^T, storing after every token.
+//
+// Lane (g, m) = (lane / 16, lane % 16) of wave w holds rows
+// w K/4 + g NSTEP + s (s < NSTEP) of column 16 cb + m of each column block
+// cb < NCB: the A operand of v_mfma_f32_16x16x4_f32 for [X | Y] and, in
+// groups of four rows, its accumulator for the update. The exponents
+// G_t - G_s and G_last - G_t are never positive. NT is the token capacity
+// (2, 4 or 8); FA selects the factored A/P form (below), LBG the gate form
+// (the lower-bound sigmoid form, else the softplus form), both fixed at
+// compile time so that the per-token work carries no branches.
+template <int K, int V, int NT, int NCB, bool PT, bool FA, bool LBG>
 __global__ __launch_bounds__(256) void spec_block_kernel(const DecodeParams p) {
-  constexpr int RW = K / kWaves;
-  // MFMA layout (VT = 16): lane (g, m) = (lane / 16, lane % 16) of wave w
-  // holds rows w RW + g NSTEP + s, s < NSTEP, of column m. Step s of the
-  // [X | Y] product takes from it the A element S0[row][m] and the B element
-  // ckq[row][m] of contraction index g (v_mfma_f32_16x16x4_f32).
-  constexpr bool kMfma = VT == 16;
-  constexpr int NSTEP = RW / 4;
-  // Row-group layout (VT = 32): lane (rg, cg) = (lane / CG, lane % CG)
-  // holds rows w RW + rg RPL + r, r < RPL, of columns 4cg .. 4cg + 3.
-  constexpr int CG = VT / 4;
-  constexpr int RG = 64 / CG;
-  constexpr int RPL = RW / RG;
-  constexpr int NVAL = 8 * NT;       // X and Y for NT tokens and 4 columns
-  constexpr int NKEEP = NVAL / RG;   // of them held by a lane after the halving
-  static_assert(kMfma ? NSTEP % 4 == 0 : (CG * RG == 64 && RPL * RG == RW && RPL >= 1 && NKEEP >= 1),
+  constexpr int VT = 16 * NCB;
+  constexpr int RW = K / kWaves;   // rows per wave
+  constexpr int NSTEP = RW / 4;    // rows per lane
+  constexpr int CPW = K / kWaves;  // key channels per wave in the gate work
+  constexpr int NP = 64 / CPW;     // token parts of a channel (lane groups of a wave)
+  constexpr int TPP = NT / NP;     // tokens per part
+  constexpr int NTP = NT < 4 ? 4 : NT;  // token places of the MFMA contraction (groups of 4)
+  static_assert(!FA || LBG, "the factored form needs a lower bound");
+  static_assert(NSTEP % 4 == 0 && TPP >= 1 && TPP * NP == NT && (NP == 2 || NP == 4) && NT * VT <= 256,
                 "tile does not fit");
-  constexpr int NS = kMfma ? NSTEP : 4 * RPL;  // state floats per lane
-  // Factored A/P (below) on the MFMA layout with 8 token places; with 4 the
-  // per-channel form has only 16 entries and costs less.
-  constexpr bool kApMfma = kMfma && NT == 8;
-  // A/P work split: LO lanes per entry (t, s), s < t, and LD per diagonal.
+  // Per-channel A/P work split: LO lanes per entry (t, s), s < t, and LD
+  // per diagonal entry.
   constexpr int NO = NT * (NT - 1) / 2;
   constexpr int LO = NT == 8 ? 8 : 16;
   constexpr int LD = NT == 8 ? 4 : 16;
   static_assert(NO * LO + NT * LD <= 256 && (NO * LO) % LD == 0 && K % (4 * LO) == 0 && K % (4 * LD) == 0,
                 "A/P lanes");
-  // Wave-summed [X | Y] per column: entry t is X_t and 8 + t is Y_t. Row
-  // strides are padded against LDS bank conflicts.
+  // Row strides against LDS bank conflicts: QS for the MFMA operand rows
+  // (e^{G_t} k_t at t, e^{G_t} q_t at 8 + t), SS (float4-aligned) for the
+  // per-wave [X | Y] partials.
+  constexpr int QS = 17;
   constexpr int SS = 20;
-  constexpr int QS = 17;  // MFMA B rows: e^{G_t} k_t at t, e^{G_t} q_t at 8 + t
-  constexpr int kUParts = 4;  // threads per column in the u/o phase
-  static_assert(VT * kUParts <= 256 && NT % kUParts == 0, "u/o threads");
 
-  __shared__ __align__(16) float s_q[NT][K];
-  __shared__ __align__(16) float s_k[NT][K];
-  __shared__ __align__(16) float s_a[NT][K];   // e^{g_t}
-  __shared__ __align__(16) float s_G[NT][K];   // G_t
-  __shared__ __align__(16) float s_ck[kMfma ? 1 : NT][kMfma ? 1 : K];  // e^{G_t} k_t
-  __shared__ __align__(16) float s_cq[kMfma ? 1 : NT][kMfma ? 1 : K];  // e^{G_t} q_t
-  __shared__ float s_ckq[kMfma ? K : 1][kMfma ? QS : 1];
-  __shared__ float s_kinv[kApMfma ? K : 1][kApMfma ? QS : 1];  // e^{-G_s} k_s at s (factored A/P)
-  __shared__ __align__(16) float s_v[NT][VT];
-  __shared__ __align__(16) float s_u[NT][VT];
-  __shared__ __align__(16) float s_b[NT];
-  __shared__ __align__(16) float s_A[NT][NT];
-  __shared__ __align__(16) float s_P[NT][NT];
-  __shared__ __align__(16) float s_xy[kWaves][kMfma ? 1 : CG][kMfma ? 1 : NVAL];
-  __shared__ float s_xym[kWaves][kMfma ? VT : 1][kMfma ? QS : 1];
-  __shared__ float s_apm[kWaves][kApMfma ? 16 : 1][kApMfma ? QS : 1];
-  __shared__ __align__(16) float s_sum[VT][SS];
+  __shared__ float s_ckq[K][QS];
+  __shared__ float s_kinv[FA ? K : 1][FA ? QS : 1];  // e^{-G_s} k_s at s (factored A/P)
+  __shared__ float s_c[K][NTP + 1];                  // C_t = e^{G_last - G_t} k_t at t (zero past NT)
+  __shared__ __align__(16) float s_egl[K];           // e^{G_last}
+  __shared__ __align__(16) float s_q[FA ? 1 : NT][FA ? 1 : K];            // per-channel A/P form
+  __shared__ __align__(16) float s_G[FA ? 1 : NT][FA ? 1 : K];            // per-channel A/P form
+  __shared__ __align__(16) float s_k[FA && !PT ? 1 : NT][FA && !PT ? 1 : K];
+  __shared__ __align__(16) float s_a[PT ? NT : 1][PT ? K : 1];            // e^{g_t}
+  __shared__ __align__(16) float s_vT[VT][8];        // v by column
+  __shared__ float s_b[8];
+  __shared__ float s_A[FA ? 1 : 8][FA ? 1 : 8];
+  __shared__ float s_P[FA ? 1 : 8][FA ? 1 : 8];
+  // Per wave: diag(beta) A strictly below the diagonal with beta on it,
+  // and P on and below it.
+  __shared__ __align__(16) float s_M[kWaves][8][8];
+  __shared__ __align__(16) float s_Pm[kWaves][8][8];
+  __shared__ __align__(16) float s_xym[kWaves][VT][SS];
+  __shared__ float s_apm[kWaves][FA ? 16 : 1][FA ? QS : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -441,58 +410,56 @@ __global__ __launch_bounds__(256) void spec_block_kernel(const DecodeParams p) {
   const int h = static_cast<int>(nh % H);
   const int n = static_cast<int>(nh / H);
   const int64_t row0 = static_cast<int64_t>(n) * T;
-  const int cg = lane % CG;
-  const int rg = lane / CG;
-  const int col = tile * VT + cg * 4;
   const int g4 = lane >> 4, m16 = lane & 15;
-  const int srow = w * RW + g4 * NSTEP;  // MFMA layout: the lane's first row
-  // Factored A/P on the MFMA layout: with a lower bound lb every running sum
-  // satisfies -NT |lb| <= G <= 0, so e^{G_t} and e^{-G_s} stay within
-  // [e^-60, e^60] when NT |lb| <= 60 (products with key components stay
-  // far above the fp32 denormal range), and e^{G_t - G_s} = e^{G_t} e^{-G_s}
-  // makes [A | P] the product [e^G k | e^G q]^T (e^{-G} k) over the keys.
-  const bool ap_mfma = kApMfma && p.has_lb != 0 && -p.lower_bound * NT <= 60.f;
+  const int srow = w * RW + g4 * NSTEP;  // the lane's first row
 
-  // 1. Per-token input loads, then the slot and the state loads: the inputs
-  //    arrive first (loads complete in order), the slot lookup overlaps
-  //    them, and the A/P work below overlaps the state's memory latency. Thread i < K owns key channel i for every
-  //    token (the running sum G runs down its tokens); the others stage v
-  //    and beta. Loads past the request's rows read zero, so padded tokens
-  //    carry q = k = 0 and g = 0.
-  constexpr int NVE = (NT * VT + 255 - K) / (256 - K);  // v elements per staging thread
+  // 1. The slot lookup, then every input load, then the state loads once the
+  //    slot is known: the inputs and the decay constant arrive while the
+  //    slot does, and the work on them below overlaps the state's memory
+  //    latency. Lane (part, c) = (lane / CPW, lane % CPW) of wave w owns key
+  //    channel i = w CPW + c for tokens part*TPP .. part*TPP + TPP - 1, so
+  //    that the parts of a channel meet inside one wave; threads below
+  //    NT*VT stage one v element, threads below 8 one beta. Loads past the
+  //    request's rows read zero, so padded tokens carry q = k = v = 0.
+  const int32_t* irow = p.indices + static_cast<int64_t>(n) * p.index_stride;
+  int init_col = 0;
+  if constexpr (PT) init_col = min(max(uniform(p.num_accepted[n]), 1), T) - 1;
+  const int64_t slot = uniform(static_cast<int64_t>(irow[init_col * p.index_col_stride]));
+  const float a_log = p.A_log[h];
+  __builtin_amdgcn_sched_barrier(0);  // both scalar loads go out first
+
+  const int part = lane / CPW;
+  const int i = w * CPW + lane % CPW;
   const int rs = static_cast<int>(p.qkv_row_stride) * 2;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.qkv + row0 * p.qkv_row_stride, static_cast<uint32_t>(T * rs));
-  uint16_t qb[NT], kb[NT], gb[NT], vb[NVE], bb = 0;
-  float db = 0.f;
-  if (tid < K) {
-    const int i = tid;
-    const __amdgpu_buffer_rsrc_t rgt = make_rsrc(p.raw_g + row0 * (H * K), static_cast<uint32_t>(T * H * K * 2));
+  const __amdgpu_buffer_rsrc_t rgt = make_rsrc(p.raw_g + row0 * (H * K), static_cast<uint32_t>(T * H * K * 2));
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.raw_beta + row0 * H, static_cast<uint32_t>(T * H * 2));
+  uint16_t qb[TPP], kb[TPP], gb[TPP], vb, bb;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      qb[t] = __builtin_amdgcn_raw_buffer_load_b16(rq, t * rs + (h * K + i) * 2, 0, 0);
-      kb[t] = __builtin_amdgcn_raw_buffer_load_b16(rq, t * rs + (H * K + h * K + i) * 2, 0, 0);
-      gb[t] = __builtin_amdgcn_raw_buffer_load_b16(rgt, (t * H * K + h * K + i) * 2, 0, 0);
-    }
-    db = p.dt_bias[h * K + i];
-  } else {
-    const int j0 = tid - K;
-#pragma unroll
-    for (int u = 0; u < NVE; ++u) {
-      const int e = j0 + u * (256 - K);
-      const int t = e / VT, j = e % VT;
-      vb[u] = __builtin_amdgcn_raw_buffer_load_b16(rq, (e < NT * VT ? t * rs : T * rs) + (2 * H * K + h * V + tile * VT + j) * 2, 0, 0);
-    }
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.raw_beta + row0 * H, static_cast<uint32_t>(T * H * 2));
-    bb = __builtin_amdgcn_raw_buffer_load_b16(rb, (min(j0, NT) * H + h) * 2, 0, 0);
+  for (int tt = 0; tt < TPP; ++tt) {
+    const int t = part * TPP + tt;
+    qb[tt] = __builtin_amdgcn_raw_buffer_load_b16(rq, t * rs + (h * K + i) * 2, 0, 0);
+    kb[tt] = __builtin_amdgcn_raw_buffer_load_b16(rq, t * rs + (H * K + h * K + i) * 2, 0, 0);
+    gb[tt] = __builtin_amdgcn_raw_buffer_load_b16(rgt, (t * H * K + h * K + i) * 2, 0, 0);
   }
+  {
+    // Unconditional loads: the threads past the staged elements read a row
+    // past the request (zero). A load under a lane mask would be followed by
+    // its conversion, and with it a wait for every earlier load, in front of
+    // the state loads.
+    const int ve = min(tid, NT * VT);
+    vb = __builtin_amdgcn_raw_buffer_load_b16(rq, (ve / VT) * rs + (2 * H * K + h * V + tile * VT + ve % VT) * 2, 0, 0);
+    bb = __builtin_amdgcn_raw_buffer_load_b16(rb, (min(tid, NT) * H + h) * 2, 0, 0);
+  }
+  const float db = p.dt_bias[h * K + i];
 
-  const int32_t* irow = p.indices + static_cast<int64_t>(n) * p.index_stride;
-  const bool per_token = p.num_accepted != nullptr;
-  int init_col = 0;
-  if (per_token) init_col = min(max(uniform(p.num_accepted[n]), 1), T) - 1;
-  const int64_t slot = uniform(static_cast<int64_t>(irow[init_col * p.index_col_stride]));
   if (slot < 0) {
     // Null slot: zero rows; the input loads are drained before the exit.
+    // (The empty asm uses every loaded value on this path too, so that no
+    // load sinks below the branch and behind the state loads.)
+#pragma unroll
+    for (int tt = 0; tt < TPP; ++tt) asm volatile("" ::"v"(qb[tt]), "v"(kb[tt]), "v"(gb[tt]));
+    asm volatile("" ::"v"(vb), "v"(bb), "v"(db), "s"(a_log));
     __builtin_amdgcn_s_waitcnt(0);
     for (int e = tid; e < T * VT; e += blockDim.x) {
       const int t = e / VT, j = e % VT;
@@ -503,88 +470,103 @@ __global__ __launch_bounds__(256) void spec_block_kernel(const DecodeParams p) {
 
   const __amdgpu_buffer_rsrc_t tile_rsrc =
       make_rsrc(p.pool + slot * p.slot_stride + static_cast<int64_t>(h) * K * V, K * V * 4);
-  const int voff = kMfma ? (srow * V + tile * VT + m16) * 4 : ((w * RW + rg * RPL) * V + col) * 4;
-  float S[NS];
-  if constexpr (kMfma) {
+  const int voff = (srow * V + tile * VT + m16) * 4;
+  float S[NCB][NSTEP];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
     for (int st = 0; st < NSTEP; ++st)
-      S[st] = __builtin_bit_cast(float,
-                                 __builtin_amdgcn_raw_buffer_load_b32(tile_rsrc, voff, st * V * 4, kStreamPolicy));
-  } else {
-#pragma unroll
-    for (int r = 0; r < RPL; ++r) {
-      const f32x4 x = buffer_load_f32x4<kStreamPolicy>(tile_rsrc, voff, r * V * 4);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) S[4 * r + c] = x[c];
-    }
-  }
+      S[cb][st] = __builtin_bit_cast(
+          float, __builtin_amdgcn_raw_buffer_load_b32(tile_rsrc, voff, st * V * 4 + cb * 64, kStreamPolicy));
 
-  // 2. Inputs to LDS: q, k, e^{g}, G and the weighted rows e^{G} k, e^{G} q.
-  {
-    if (tid < K) {
-      const int i = tid;
-      const float a = __expf(p.A_log[h]);
-      const bool has_lb = p.has_lb != 0;
-      float G = 0.f;
+  // 2. Decays: each part sums its own tokens' log decays, the parts' totals
+  //    meet across the wave's lane groups, and every running sum is then
+  //    the part's offset (the sum of the earlier parts) plus its local sum;
+  //    G_last, the sum of all parts in the same order, equals the last
+  //    part's last running sum exactly.
+  const float a = __expf(a_log);
+  float gv[TPP], L[TPP];
+  float run = 0.f;
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const float q = bf16_to_f32(qb[t]);
-        const float k = bf16_to_f32(kb[t]);
-        const float g = t < T ? gate_log_decay(bf16_to_f32(gb[t]), db, a, has_lb, p.lower_bound) : 0.f;
-        G += g;
-        const float eG = __expf(G);
-        s_q[t][i] = q;
-        s_k[t][i] = k;
-        s_a[t][i] = __expf(g);
-        s_G[t][i] = G;
-        if constexpr (kMfma) {
-          s_ckq[i][t] = eG * k;
-          s_ckq[i][8 + t] = eG * q;
-          if constexpr (kApMfma) {
-            if (ap_mfma) s_kinv[i][t] = k * __expf(-G);
-          }
-        } else {
-          s_ck[t][i] = eG * k;
-          s_cq[t][i] = eG * q;
-        }
-      }
-      if constexpr (kMfma) {
-#pragma unroll
-        for (int t = NT; t < 8; ++t) {
-          s_ckq[i][t] = 0.f;
-          s_ckq[i][8 + t] = 0.f;
-        }
-        if constexpr (kApMfma) {
-          if (ap_mfma) {
-#pragma unroll
-            for (int t = NT; t < 16; ++t) s_kinv[i][t] = 0.f;
-          }
-        }
-      }
-    } else {
-      const int j0 = tid - K;
-#pragma unroll
-      for (int u = 0; u < NVE; ++u) {
-        const int e = j0 + u * (256 - K);
-        if (e < NT * VT) s_v[e / VT][e % VT] = bf16_to_f32(vb[u]);
-      }
-      if (j0 < NT) s_b[j0] = j0 < T ? sigmoid_f32(bf16_to_f32(bb)) : 0.f;
-    }
+  for (int tt = 0; tt < TPP; ++tt) {
+    const int t = part * TPP + tt;
+    const float g = gate_log_decay(bf16_to_f32(gb[tt]), db, a, LBG, p.lower_bound);
+    gv[tt] = t < T ? g : 0.f;
+    run += gv[tt];
+    L[tt] = run;
   }
+  float off, Gl;
+  if constexpr (NP == 2) {
+    // v_permlane32_swap(x, x) leaves the lower half's x in the first
+    // result and the upper half's in the second, in every lane.
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(run), __float_as_uint(run), false, false);
+    const float t0 = __uint_as_float(r[0]);
+    const float t1 = __uint_as_float(r[1]);
+    off = part ? t0 : 0.f;
+    Gl = t0 + t1;
+  } else {
+    float pre = 0.f;
+    off = 0.f;
+#pragma unroll
+    for (int pp = 0; pp < NP; ++pp) {
+      const float x = __shfl(run, pp * CPW + lane % CPW);
+      if (pp == part) off = pre;
+      pre += x;
+    }
+    Gl = pre;
+  }
+  const float egl = __expf(Gl);
+#pragma unroll
+  for (int tt = 0; tt < TPP; ++tt) {
+    const int t = part * TPP + tt;
+    const float G = off + L[tt];
+    const float q = bf16_to_f32(qb[tt]);
+    const float k = bf16_to_f32(kb[tt]);
+    const float eG = __expf(G);
+    s_ckq[i][t] = eG * k;
+    s_ckq[i][8 + t] = eG * q;
+    if constexpr (FA) {
+      const float kinv = k * __expf(-G);
+      s_kinv[i][t] = kinv;
+      s_c[i][t] = kinv * egl;
+    } else {
+      s_c[i][t] = k * __expf(Gl - G);
+      s_q[t][i] = q;
+      s_G[t][i] = G;
+    }
+    if constexpr (!FA || PT) s_k[t][i] = k;
+    if constexpr (PT) s_a[t][i] = __expf(gv[tt]);
+  }
+  if (part == 0) {
+    s_egl[i] = egl;
+#pragma unroll
+    for (int t = NT; t < NTP; ++t) s_c[i][t] = 0.f;
+  }
+  if (tid < NT * VT) s_vT[tid % VT][tid / VT] = bf16_to_f32(vb);
+  if (tid < 8) s_b[tid] = tid < T ? sigmoid_f32(bf16_to_f32(bb)) : 0.f;
   lds_barrier();
 
-  // 3. A and P. For s < t, A_ts and P_ts share the factor e^{G_t - G_s}
-  //    (one exponential per channel for both): LO lanes per such entry, the
-  //    entries row by row; then LD lanes per diagonal entry P_tt = k_t . q_t.
-  //    The lanes of an entry read neighbouring float4s, and each entry
-  //    starts at its own offset, so the entries of a wave spread over the
-  //    LDS banks. (The factored form takes A and P from MFMA in step 4.)
-  if (!ap_mfma) {
-    int te = -1, se = 0, part = 0, ent = 0;
+  // 3. A and P. Factored: per-wave partials of the product over the wave's
+  //    keys (lane (g, m) ends with column s = m of rows 4g .. 4g + 3; rows
+  //    t: A_ts, 8 + t: P_ts). Per channel otherwise: for s < t, A_ts and
+  //    P_ts share the factor e^{G_t - G_s} (one exponential per channel for
+  //    both): LO lanes per such entry, the entries row by row; then LD lanes
+  //    per diagonal entry P_tt = k_t . q_t. The lanes of an entry read
+  //    neighbouring float4s, and each entry starts at its own offset, so the
+  //    entries of a wave spread over the LDS banks.
+  if constexpr (FA) {
+    f32x4 ap[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};  // two chains: even and odd steps
+#pragma unroll
+    for (int st = 0; st < NSTEP; ++st)
+      ap[st & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(s_ckq[srow + st][m16], s_kinv[srow + st][m16], ap[st & 1], 0, 0, 0);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) s_apm[w][4 * g4 + jj][m16] = ap[0][jj] + ap[1][jj];
+  } else {
+    int te = -1, se = 0, pe = 0, ent = 0;
     bool diag = false;
     if (tid < NO * LO) {
       ent = tid / LO;
-      part = tid % LO;
+      pe = tid % LO;
       int rem = ent;
 #pragma unroll
       for (int x = 1; x < NT; ++x)
@@ -593,7 +575,7 @@ __global__ __launch_bounds__(256) void spec_block_kernel(const DecodeParams p) {
         }
     } else if (tid < NO * LO + NT * LD) {
       te = se = (tid - NO * LO) / LD;
-      part = (tid - NO * LO) % LD;
+      pe = (tid - NO * LO) % LD;
       diag = true;
     }
     float accA = 0.f, accP = 0.f;
@@ -602,12 +584,12 @@ __global__ __launch_bounds__(256) void spec_block_kernel(const DecodeParams p) {
         constexpr int NF = K / (4 * LO);  // float4s per lane
 #pragma unroll
         for (int m = 0; m < NF; ++m) {
-          const int i = (((m + ent) % NF) * LO + part) * 4;
-          const float4 ks = *reinterpret_cast<const float4*>(&s_k[se][i]);
-          const float4 kt = *reinterpret_cast<const float4*>(&s_k[te][i]);
-          const float4 qt = *reinterpret_cast<const float4*>(&s_q[te][i]);
-          const float4 gt = *reinterpret_cast<const float4*>(&s_G[te][i]);
-          const float4 gs = *reinterpret_cast<const float4*>(&s_G[se][i]);
+          const int c = (((m + ent) % NF) * LO + pe) * 4;
+          const float4 ks = *reinterpret_cast<const float4*>(&s_k[se][c]);
+          const float4 kt = *reinterpret_cast<const float4*>(&s_k[te][c]);
+          const float4 qt = *reinterpret_cast<const float4*>(&s_q[te][c]);
+          const float4 gt = *reinterpret_cast<const float4*>(&s_G[te][c]);
+          const float4 gs = *reinterpret_cast<const float4*>(&s_G[se][c]);
           const float e0 = ks.x * __expf(gt.x - gs.x), e1 = ks.y * __expf(gt.y - gs.y);
           const float e2 = ks.z * __expf(gt.z - gs.z), e3 = ks.w * __expf(gt.w - gs.w);
           accA = fmaf(e0, kt.x, fmaf(e1, kt.y, fmaf(e2, kt.z, fmaf(e3, kt.w, accA))));
@@ -617,9 +599,9 @@ __global__ __launch_bounds__(256) void spec_block_kernel(const DecodeParams p) {
         constexpr int NF = K / (4 * LD);
 #pragma unroll
         for (int m = 0; m < NF; ++m) {
-          const int i = (m * LD + part) * 4;
-          const float4 kt = *reinterpret_cast<const float4*>(&s_k[te][i]);
-          const float4 qt = *reinterpret_cast<const float4*>(&s_q[te][i]);
+          const int c = (m * LD + pe) * 4;
+          const float4 kt = *reinterpret_cast<const float4*>(&s_k[te][c]);
+          const float4 qt = *reinterpret_cast<const float4*>(&s_q[te][c]);
           accP = fmaf(kt.x, qt.x, fmaf(kt.y, qt.y, fmaf(kt.z, qt.z, fmaf(kt.w, qt.w, accP))));
         }
       }
@@ -645,7 +627,7 @@ __global__ __launch_bounds__(256) void spec_block_kernel(const DecodeParams p) {
     sP[2] = sP[1] + dpp(sP[1], 3);
     constexpr int lo = LO == 4 ? 0 : LO == 8 ? 1 : 2;
     constexpr int ld = LD == 4 ? 0 : LD == 8 ? 1 : 2;
-    if (part == 0 && te >= 0) {
+    if (pe == 0 && te >= 0) {
       if (diag) {
         s_P[te][te] = sP[ld];
       } else {
@@ -655,197 +637,238 @@ __global__ __launch_bounds__(256) void spec_block_kernel(const DecodeParams p) {
     }
   }
 
-  // 4. X_t and Y_t from S0, per wave, then to LDS for the sum over the
-  //    waves. MFMA layout: NSTEP fp32 MFMA steps over the wave's rows (lane
-  //    (g, m) ends with entry m of columns 4g .. 4g + 3). Row-group layout:
-  //    per-lane partials over the lane's rows, halved over the row groups.
-  if constexpr (kMfma) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  // 4. X_t and Y_t from S0, per wave and column block: NSTEP fp32 MFMA
+  //    steps over the wave's rows, in two chains (lane (g, m) ends with
+  //    entry m of columns 4g .. 4g + 3 of the block). The update's operands
+  //    that do not depend on u are read here too.
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int st = 0; st < NSTEP; ++st)
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(S[st], s_ckq[srow + st][m16], acc, 0, 0, 0);
+      acc[st & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(S[cb][st], s_ckq[srow + st][m16], acc[st & 1], 0, 0, 0);
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) s_xym[w][4 * g4 + jj][m16] = acc[jj];
-    if constexpr (kApMfma) {
-      if (ap_mfma) {
-        // [A | P] partials over the wave's keys: lane (g, m) ends with
-        // column s = m of rows 4g .. 4g + 3 (rows t: A_ts, 8 + t: P_ts).
-        f32x4 ap = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int st = 0; st < NSTEP; ++st)
-          ap = __builtin_amdgcn_mfma_f32_16x16x4f32(s_ckq[srow + st][m16], s_kinv[srow + st][m16], ap, 0, 0, 0);
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) s_apm[w][4 * g4 + jj][m16] = ap[jj];
-      }
-    }
-  } else {
-    float xy[NVAL];
-#pragma unroll
-    for (int v = 0; v < NVAL; ++v) xy[v] = 0.f;
-#pragma unroll
-    for (int r = 0; r < RPL; ++r) {
-      const int row = w * RW + rg * RPL + r;
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const float ck = s_ck[t][row], cq = s_cq[t][row];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          xy[t * 4 + c] = fmaf(ck, S[4 * r + c], xy[t * 4 + c]);
-          xy[(NT + t) * 4 + c] = fmaf(cq, S[4 * r + c], xy[(NT + t) * 4 + c]);
-        }
-      }
-    }
-    halve_row_groups<CG>(xy, lane);
-    int blk = 0;
-#pragma unroll
-    for (int b = 2; b < 6; ++b)
-      if ((1 << b) >= CG) blk = blk * 2 + ((lane >> b) & 1);
-#pragma unroll
-    for (int v = 0; v < NKEEP; ++v) s_xy[w][cg][blk * NKEEP + v] = xy[v];
+    for (int jj = 0; jj < 4; ++jj) s_xym[w][16 * cb + 4 * g4 + jj][m16] = acc[0][jj] + acc[1][jj];
   }
-  lds_barrier();
+  constexpr int NHB = NSTEP / 4;  // 16-row blocks of the update
+  float4 eg[NHB];
+  float cf[NHB][NTP / 4];
+  if constexpr (!PT) {
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb) {
+      eg[hb] = *reinterpret_cast<const float4*>(&s_egl[srow + 4 * hb]);
+      const int arow = w * RW + (m16 >> 2) * NSTEP + 4 * hb + (m16 & 3);
+#pragma unroll
+      for (int ks = 0; ks < NTP / 4; ++ks) cf[hb][ks] = s_c[arow][4 * ks + g4];
+    }
+  }
+  lds_barrier();  // A, P and the [X | Y] partials complete
 
-  // 5. Sums over the waves (every thread), then u and o, one thread per
-  //    column of the tile.
-  for (int e = tid; e < VT * 2 * NT; e += 256) {
-    const int jj = e / (2 * NT), v = e % (2 * NT);
-    const int kind = v / NT, t = v % NT;
-    float x = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) {
-      if constexpr (kMfma)
-        x += s_xym[ww][jj][kind * 8 + t];
-      else
-        x += s_xy[ww][jj / 4][v * 4 + jj % 4];
-    }
-    s_sum[jj][kind * 8 + t] = x;
-  }
-  if constexpr (kApMfma) {
-    if (ap_mfma && tid < NT * NT) {
-      const int t = tid / NT, s2 = tid % NT;
-      float a = 0.f, pp = 0.f;
+  // 5. The token-pair tables, in every wave (its own copy, so that no
+  //    further exchange between the waves is needed): lane (r, c) =
+  //    (lane / 8, lane % 8) takes entry (r, c) of A and P (summing the
+  //    factored partials over the waves) and keeps what the recurrence
+  //    uses: M = diag(beta) A strictly below the diagonal, beta on it, and
+  //    P on and below it. Rows of padded token places are zero.
+  {
+    const int r = lane >> 3, c = lane & 7;
+    float arc = 0.f, prc = 0.f;
+    if constexpr (FA) {
 #pragma unroll
       for (int ww = 0; ww < kWaves; ++ww) {
-        a += s_apm[ww][t][s2];
-        pp += s_apm[ww][8 + t][s2];
+        arc += s_apm[ww][r][c];
+        prc += s_apm[ww][8 + r][c];
       }
-      s_A[t][s2] = a;
-      s_P[t][s2] = pp;
+    } else {
+      arc = s_A[r][c];
+      prc = s_P[r][c];
     }
+    const bool live = r < NT;
+    const float br = s_b[r];
+    s_M[w][r][c] = !live ? 0.f : c < r ? br * arc : c == r ? br : 0.f;
+    s_Pm[w][r][c] = live && c <= r ? prc : 0.f;
   }
-  lds_barrier();
-  if (tid < VT * kUParts) {
-    // kUParts threads per column: each runs the column's u recurrence (a
-    // short dependent chain) and forms o and stores u for the token places
-    // t = part (mod kUParts). Every operand is read before the first result
-    // is written.
-    const int j = tid / kUParts, part = tid % kUParts;
-    constexpr int NOWN = NT / kUParts;
-    float X[NT], A[NT][NT], b[NT], Yo[NOWN], Po[NOWN][NT];
+
+  // 6. Per lane (g, m), in every wave and column block: the wave sums of X
+  //    for column 16 cb + m, d = v - X, and u by forward substitution,
+  //    u_t = beta_t d_t - sum_{s<t} beta_t A_ts u_s.
+  float u[NCB][NTP];
+  {
+    float m[NT][NTP];
+    wave_lds_sync();
 #pragma unroll
-    for (int t4 = 0; t4 < NT; t4 += 4) {
-      const float4 xv = *reinterpret_cast<const float4*>(&s_sum[j][t4]);
-      const float4 bv = *reinterpret_cast<const float4*>(&s_b[t4]);
-      X[t4] = xv.x; X[t4 + 1] = xv.y; X[t4 + 2] = xv.z; X[t4 + 3] = xv.w;
-      b[t4] = bv.x; b[t4 + 1] = bv.y; b[t4 + 2] = bv.z; b[t4 + 3] = bv.w;
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int s4 = 0; s4 < NTP; s4 += 4) {
+        if (s4 <= t) {
+          const float4 x = *reinterpret_cast<const float4*>(&s_M[w][t][s4]);
+          m[t][s4] = x.x; m[t][s4 + 1] = x.y; m[t][s4 + 2] = x.z; m[t][s4 + 3] = x.w;
+        }
+      }
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      float d[NTP];
+#pragma unroll
+      for (int s4 = 0; s4 < NTP; s4 += 4) {
+        const int j = 16 * cb + m16;
+        float4 x = *reinterpret_cast<const float4*>(&s_xym[0][j][s4]);
+#pragma unroll
+        for (int ww = 1; ww < kWaves; ++ww) {
+          const float4 y = *reinterpret_cast<const float4*>(&s_xym[ww][j][s4]);
+          x.x += y.x; x.y += y.y; x.z += y.z; x.w += y.w;
+        }
+        const float4 v = *reinterpret_cast<const float4*>(&s_vT[j][s4]);
+        d[s4] = v.x - x.x;
+        d[s4 + 1] = v.y - x.y;
+        d[s4 + 2] = v.z - x.z;
+        d[s4 + 3] = v.w - x.w;
+      }
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const float4 av = *reinterpret_cast<const float4*>(&s_A[t][t4]);
-        A[t][t4] = av.x; A[t][t4 + 1] = av.y; A[t][t4 + 2] = av.z; A[t][t4 + 3] = av.w;
+        float acc = m[t][t] * d[t];
+#pragma unroll
+        for (int s2 = 0; s2 < t; ++s2) acc = fmaf(-m[t][s2], u[cb][s2], acc);
+        u[cb][t] = acc;
       }
 #pragma unroll
-      for (int i = 0; i < NOWN; ++i) {
-        const float4 pv = *reinterpret_cast<const float4*>(&s_P[part + kUParts * i][t4]);
-        Po[i][t4] = pv.x; Po[i][t4 + 1] = pv.y; Po[i][t4 + 2] = pv.z; Po[i][t4 + 3] = pv.w;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < NOWN; ++i) Yo[i] = s_sum[j][8 + part + kUParts * i];
-    float u[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      float x = s_v[t][j] - X[t];
-#pragma unroll
-      for (int s2 = 0; s2 < t; ++s2) x = fmaf(-A[t][s2], u[s2], x);
-      u[t] = b[t] * x;
-    }
-#pragma unroll
-    for (int i = 0; i < NOWN; ++i) {
-      const int t = part + kUParts * i;
-      if (t < T) {
-        float y = Yo[i];
-#pragma unroll
-        for (int s2 = 0; s2 < NT; ++s2) y = fmaf(s2 <= t ? Po[i][s2] : 0.f, u[s2], y);
-        p.out[((row0 + t) * H + h) * static_cast<int64_t>(V) + tile * VT + j] = f32_to_bf16_rne(p.scale * y);
-        float ut = u[0];
-#pragma unroll
-        for (int s2 = 1; s2 < NT; ++s2) ut = s2 == t ? u[s2] : ut;
-        s_u[t][j] = ut;
-      }
+      for (int t = NT; t < NTP; ++t) u[cb][t] = 0.f;
     }
   }
-  lds_barrier();
 
-  // 6. The state takes the block's tokens in registers.
+  // 7. The state takes the block and is stored.
   auto store_state = [&](const __amdgpu_buffer_rsrc_t r) {
-    if constexpr (kMfma) {
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
       for (int st = 0; st < NSTEP; ++st)
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, S[st]), r, voff, st * V * 4,
-                                              kStreamPolicy);
-    } else {
-#pragma unroll
-      for (int r2 = 0; r2 < RPL; ++r2)
-        buffer_store_f32x4<kStreamPolicy>(f32x4{S[4 * r2], S[4 * r2 + 1], S[4 * r2 + 2], S[4 * r2 + 3]}, r, voff,
-                                          r2 * V * 4);
-    }
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, S[cb][st]), r, voff,
+                                              st * V * 4 + cb * 64, kStreamPolicy);
   };
+  if constexpr (!PT) {
+    // S = diag(e^{G_last}) S0 + C U, in blocks of 16 rows: block hb holds
+    // lane (g, m)'s rows srow + 4hb .. srow + 4hb + 3, so its row r is
+    // w K/4 + (r / 4) NSTEP + 4hb + r % 4; the contraction runs over the
+    // token places, four per step (B operand: u_{4 ks + g} of the lane's
+    // column).
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    if (t < T) {
-      if constexpr (kMfma) {
-        const float ut = s_u[t][m16];
+    for (int cb = 0; cb < NCB; ++cb) {
+      float uk[NTP / 4];
 #pragma unroll
-        for (int q4 = 0; q4 < NSTEP; q4 += 4) {
-          const float4 av = *reinterpret_cast<const float4*>(&s_a[t][srow + q4]);
-          const float4 kv = *reinterpret_cast<const float4*>(&s_k[t][srow + q4]);
-          S[q4] = fmaf(kv.x, ut, S[q4] * av.x);
-          S[q4 + 1] = fmaf(kv.y, ut, S[q4 + 1] * av.y);
-          S[q4 + 2] = fmaf(kv.z, ut, S[q4 + 2] * av.z);
-          S[q4 + 3] = fmaf(kv.w, ut, S[q4 + 3] * av.w);
-        }
-      } else {
-        const f32x4 ut = *reinterpret_cast<const f32x4*>(&s_u[t][cg * 4]);
+      for (int ks = 0; ks < NTP / 4; ++ks) {
+        // u_{4 ks + g}: a chain of selects (branch-free).
+        float x = u[cb][4 * ks];
 #pragma unroll
-        for (int r = 0; r < RPL; ++r) {
-          const int row = w * RW + rg * RPL + r;
-          const float al = s_a[t][row], kr = s_k[t][row];
-#pragma unroll
-          for (int c = 0; c < 4; ++c) S[4 * r + c] = fmaf(kr, ut[c], S[4 * r + c] * al);
-        }
+        for (int gg = 1; gg < 4; ++gg) x = g4 == gg ? u[cb][4 * ks + gg] : x;
+        uk[ks] = x;
       }
-      if (per_token) {
+#pragma unroll
+      for (int hb = 0; hb < NHB; ++hb) {
+        f32x4 acc = {eg[hb].x * S[cb][4 * hb], eg[hb].y * S[cb][4 * hb + 1], eg[hb].z * S[cb][4 * hb + 2],
+                     eg[hb].w * S[cb][4 * hb + 3]};
+#pragma unroll
+        for (int ks = 0; ks < NTP / 4; ++ks)
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(cf[hb][ks], uk[ks], acc, 0, 0, 0);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) S[cb][4 * hb + jj] = acc[jj];
+      }
+    }
+    store_state(tile_rsrc);
+  } else {
+    // Token by token, storing after each.
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (t < T) {
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          const float ut = u[cb][t];
+#pragma unroll
+          for (int q4 = 0; q4 < NSTEP; q4 += 4) {
+            const float4 av = *reinterpret_cast<const float4*>(&s_a[t][srow + q4]);
+            const float4 kv = *reinterpret_cast<const float4*>(&s_k[t][srow + q4]);
+            S[cb][q4] = fmaf(kv.x, ut, S[cb][q4] * av.x);
+            S[cb][q4 + 1] = fmaf(kv.y, ut, S[cb][q4 + 1] * av.y);
+            S[cb][q4 + 2] = fmaf(kv.z, ut, S[cb][q4 + 2] * av.z);
+            S[cb][q4 + 3] = fmaf(kv.w, ut, S[cb][q4 + 3] * av.w);
+          }
+        }
         const int64_t st = uniform(static_cast<int64_t>(irow[t * p.index_col_stride]));
         if (st >= 0) store_state(make_rsrc(p.pool + st * p.slot_stride + static_cast<int64_t>(h) * K * V, K * V * 4));
       }
     }
   }
-  if (!per_token) store_state(tile_rsrc);
+
+  // 8. Outputs: waves w < NTP/4 form o_t = scale (Y_t + sum_{s<=t} P_ts u_s)
+  //    for t = 4 w + g of the lane's columns.
+  if (w < NTP / 4) {
+    const int t = 4 * w + g4;
+    float pr[NTP];
+#pragma unroll
+    for (int s4 = 0; s4 < NTP; s4 += 4) {
+      const float4 x = *reinterpret_cast<const float4*>(&s_Pm[w][t][s4]);
+      pr[s4] = x.x; pr[s4 + 1] = x.y; pr[s4 + 2] = x.z; pr[s4 + 3] = x.w;
+    }
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      const int j = 16 * cb + m16;
+      float y = s_xym[0][j][8 + t];
+#pragma unroll
+      for (int ww = 1; ww < kWaves; ++ww) y += s_xym[ww][j][8 + t];
+#pragma unroll
+      for (int s2 = 0; s2 < NTP; ++s2) y = fmaf(pr[s2], u[cb][s2], y);
+      if (t < T) p.out[((row0 + t) * H + h) * static_cast<int64_t>(V) + tile * VT + j] = f32_to_bf16_rne(p.scale * y);
+    }
+  }
+}
+
+template <int K, int V, int NT, int NCB, bool PT>
+static void launch_block_pt(const DecodeParams& p, dim3 grid, dim3 block, hipStream_t stream) {
+  // Factored A/P under a lower bound lb: every running sum satisfies
+  // -NT |lb| <= G <= 0, so e^{G_t} and e^{-G_s} stay within [e^-60, e^60]
+  // when NT |lb| <= 60 (products with key components stay far above the
+  // fp32 denormal range), and e^{G_t - G_s} = e^{G_t} e^{-G_s} makes
+  // [A | P] the product [e^G k | e^G q]^T (e^{-G} k) over the keys. With 2
+  // token places the per-channel form has 3 entries and costs less.
+  const bool lb = p.has_lb != 0;
+  const bool fa = NT > 2 && lb && -p.lower_bound * NT <= 60.f;
+  if (fa) {
+    if constexpr (NT > 2) spec_block_kernel<K, V, NT, NCB, PT, true, true><<<grid, block, 0, stream>>>(p);
+  } else if (lb) {
+    spec_block_kernel<K, V, NT, NCB, PT, false, true><<<grid, block, 0, stream>>>(p);
+  } else {
+    spec_block_kernel<K, V, NT, NCB, PT, false, false><<<grid, block, 0, stream>>>(p);
+  }
+}
+
+template <int K, int V, int NT, int NCB>
+static void launch_block(const DecodeParams& p, dim3 grid, dim3 block, hipStream_t stream) {
+  if (p.num_accepted != nullptr) launch_block_pt<K, V, NT, NCB, true>(p, grid, block, stream);
+  else launch_block_pt<K, V, NT, NCB, false>(p, grid, block, stream);
 }
 
 template <int K, int V>
-static hipError_t launch_kv(const DecodeParams& p, int vt, hipStream_t stream) {
+static hipError_t launch_kv(const DecodeParams& p, int vt, bool block_form, hipStream_t stream) {
   const int64_t blocks = static_cast<int64_t>(p.num_seqs) * p.H * (V / vt);
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   dim3 grid(static_cast<unsigned>(blocks)), block(64 * kWaves);
-  if (p.tokens_per_seq >= kBlockMinTokens && vt <= 32) {
-    const bool nt4 = p.tokens_per_seq <= 4;
+  if (block_form) {
+    // Token capacity: 2 (128 keys only: one token per part), 4 or 8.
+    const int nt = p.tokens_per_seq <= 2 && K == 128 ? 2 : p.tokens_per_seq <= 4 ? 4 : 8;
     if (vt == 16) {
-      if (nt4) spec_block_kernel<K, V, 16, 4><<<grid, block, 0, stream>>>(p);
-      else spec_block_kernel<K, V, 16, 8><<<grid, block, 0, stream>>>(p);
+      if (nt == 2) {
+        if constexpr (K == 128) launch_block<K, V, 2, 1>(p, grid, block, stream);
+      } else if (nt == 4) {
+        launch_block<K, V, 4, 1>(p, grid, block, stream);
+      } else {
+        launch_block<K, V, 8, 1>(p, grid, block, stream);
+      }
     } else {
-      if (nt4) spec_block_kernel<K, V, 32, 4><<<grid, block, 0, stream>>>(p);
-      else spec_block_kernel<K, V, 32, 8><<<grid, block, 0, stream>>>(p);
+      if (nt == 2) {
+        if constexpr (K == 128) launch_block<K, V, 2, 2>(p, grid, block, stream);
+      } else if (nt == 4) {
+        launch_block<K, V, 4, 2>(p, grid, block, stream);
+      } else {
+        launch_block<K, V, 8, 2>(p, grid, block, stream);
+      }
     }
     return hipGetLastError();
   }
@@ -863,25 +886,30 @@ static hipError_t launch_kv(const DecodeParams& p, int vt, hipStream_t stream) {
 // Column-tile choice: whole rows (VT = V) when there are enough (request,
 // head) pairs to fill the chip; narrower tiles for small batches, so that a
 // spec-verify step of a single request still spreads over the 256 CUs.
+// Requests of several tokens with fewer than 256 pairs take the block form
+// (on 16- or 32-column tiles).
 hipError_t launch_decode(DecodeParams p, int K, hipStream_t stream) {
   const int64_t pairs = static_cast<int64_t>(p.num_seqs) * p.H;
+  const bool block_form = p.tokens_per_seq >= kBlockMinTokens && pairs < 256;
   int vt = 128;
   if (pairs < 512) vt = 64;
   if (pairs < 256) vt = 32;
   if (pairs < 128) vt = 16;
+  // The block form: one workgroup per CU where possible (16 columns for up
+  // to 32 pairs, 32 beyond).
+  if (block_form) vt = pairs <= 32 ? 16 : 32;
   if (vt > p.V) vt = p.V;
   p.num_tiles = pairs * (p.V / vt);
   // The output epilogue runs inside the kernel when a workgroup holds whole
   // rows; otherwise as a pass over the output after it.
   const OutNorm norm = p.norm;
-  const bool block_form = p.tokens_per_seq >= kBlockMinTokens && vt <= 32;
   const bool separate = norm.gate != nullptr && (vt != p.V || block_form);
   if (separate) p.norm.gate = nullptr;
   hipError_t e;
   if (K == 64)
-    e = p.V == 64 ? launch_kv<64, 64>(p, vt, stream) : launch_kv<64, 128>(p, vt, stream);
+    e = p.V == 64 ? launch_kv<64, 64>(p, vt, block_form, stream) : launch_kv<64, 128>(p, vt, block_form, stream);
   else
-    e = p.V == 64 ? launch_kv<128, 64>(p, vt, stream) : launch_kv<128, 128>(p, vt, stream);
+    e = p.V == 64 ? launch_kv<128, 64>(p, vt, block_form, stream) : launch_kv<128, 128>(p, vt, block_form, stream);
   if (e != hipSuccess || !separate) return e;
   return launch_gated_rmsnorm(norm, p.out, static_cast<int64_t>(p.num_seqs) * p.tokens_per_seq, p.H,
                               p.V, stream);

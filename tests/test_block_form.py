@@ -7,10 +7,14 @@ initial state S0 alone,
     A_ts = sum_i k_s k_t e^{G_t - G_s}  (s < t),   P_ts likewise with q_t (s <= t),
 then u_t = beta_t (v_t - X_t - sum_{s<t} A_ts u_s), o_t = scale (Y_t + sum_{s<=t}
 P_ts u_s), and the state S_t = diag(e^{g_t}) S_{t-1} + k_t u_t^T. Under a lower
-bound it takes A and P from the factored product (e^{G} k)^T (e^{-G} k). These
-tests restate that algebra in numpy and check it against the oracle's
-token-by-token recurrence, so the reformulation itself is pinned apart from
-the GPU: a dropped term, a wrong sign, or an exclusive running sum fails them.
+bound it takes A and P from the factored product (e^{G} k)^T (e^{-G} k). The
+kernel evaluates the recurrence for u in matrix form: with
+M = I + diag(beta) A_strict and Tb = M^{-1} diag(beta), u = Tb (v - X) and
+o = scale (Y + P Tb (v - X)); the block's state is
+diag(e^{G_last}) S0 + sum_t (e^{G_last - G_t} k_t) u_t^T. These tests restate
+that algebra in numpy and check it against the oracle's token-by-token
+recurrence, so the reformulation itself is pinned apart from the GPU: a
+dropped term, a wrong sign, or an exclusive running sum fails them.
 """
 import numpy as np
 import pytest
@@ -45,6 +49,27 @@ def _block_form(q, k, v, g, b, S0, scale, factored=False):
     return o, S
 
 
+def _block_form_matrix(q, k, v, g, b, S0, scale):
+    """The matrix form: Tb and P Tb from the token-pair tables, u and o as
+    products with d = v - X, the state as one rank-T update of the decayed
+    initial state."""
+    T = q.shape[0]
+    G = np.cumsum(g, axis=0)
+    X = (np.exp(G) * k) @ S0
+    Y = (np.exp(G) * q) @ S0
+    A = (np.exp(G) * k) @ (np.exp(-G) * k).T
+    P = (np.exp(G) * q) @ (np.exp(-G) * k).T
+    M = np.eye(T) + np.diag(b) @ np.tril(A, -1)
+    Tb = np.linalg.solve(M, np.diag(b))
+    PT = np.tril(P) @ Tb
+    d = v - X
+    u = Tb @ d
+    o = scale * (Y + PT @ d)
+    C = np.exp(G[-1][None, :] - G) * k             # [T, K]
+    S = np.exp(G[-1])[:, None] * S0 + C.T @ u
+    return o, S
+
+
 def _case(T, K, V, lb, seed):
     r = np.random.default_rng(seed)
     q = r.standard_normal((T, K))
@@ -66,6 +91,28 @@ def test_block_form_equals_recurrence(T, lb):
     o, S = _block_form(q, k, v, g, b, S0, 0.7)
     np.testing.assert_allclose(o, o_ref, rtol=1e-11, atol=1e-12)
     np.testing.assert_allclose(S, S_ref, rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("T", [2, 4, 7, 8])
+@pytest.mark.parametrize("lb", [-5.0, None])
+def test_matrix_form_equals_recurrence(T, lb):
+    q, k, v, g, b, S0 = _case(T, 16, 8, lb, 320 + T)
+    o_ref, S_ref = O.recurrent_pregated(q, k, v, g, b, S0, scale=0.7)
+    o, S = _block_form_matrix(q, k, v, g, b, S0, 0.7)
+    np.testing.assert_allclose(o, o_ref, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(S, S_ref, rtol=1e-10, atol=1e-12)
+
+
+def test_matrix_form_padded_places_are_inert():
+    # Padded places (q = k = v = 0, g = 0, beta = 0) give zero rows and
+    # columns of Tb, zero u there, and leave the state that of the real tokens.
+    q, k, v, g, b, S0 = _case(3, 16, 8, -5.0, 431)
+    pad = lambda a: np.concatenate([a, np.zeros((5,) + a.shape[1:])])
+    o8, S8 = _block_form_matrix(pad(q), pad(k), pad(v), pad(g), pad(b), S0, 1.0)
+    o_ref, S_ref = O.recurrent_pregated(q, k, v, g, b, S0, scale=1.0)
+    np.testing.assert_allclose(o8[:3], o_ref, rtol=1e-10, atol=1e-12)
+    assert np.all(o8[3:] == 0.0)
+    np.testing.assert_allclose(S8, S_ref, rtol=1e-10, atol=1e-12)
 
 
 def test_factored_tables_under_a_bound_equal_the_recurrence():

@@ -91,8 +91,12 @@ def test_spec_decode_null_columns_strided_table_and_small_heads():
 @pytest.mark.parametrize("tps", [1, 4, 8])
 def test_one_accepted_token_matches_plain_decode(tps):
     """With one accepted token the initial state is column 0's, as in plain
-    decode; the state stored after the last token then equals plain decode's
-    final state, and the outputs agree, bit for bit (same kernel arithmetic)."""
+    decode; the outputs agree bit for bit (same kernel arithmetic), and the
+    state stored after the last token equals plain decode's final state: bit
+    for bit with one token, and up to fp32 rounding with several (plain
+    decode applies a block of tokens as one rank-T update, the per-token path
+    token by token, and e^{G} of a running sum G carries a relative error
+    of about |G| 2^-24 where the per-token products round eight times)."""
     n = 8 // tps
     case = W.spec_decode_case(f"spec_vs_decode_{tps}", 32, 128, 128, n, tps, num_slots=512,
                               lower_bound=-5.0, seed=5300 + tps, accepted=[1] * n, pool_seed=2999)
@@ -105,6 +109,13 @@ def test_one_accepted_token_matches_plain_decode(tps):
                                    tokens_per_seq=tps)
     torch.cuda.synchronize()
     assert np.array_equal(got, out.float().cpu().numpy().astype(np.float64))
+    worst = 0.0
     for r in range(n):
-        assert torch.equal(pool_spec[int(case.block_table[r, tps - 1])], pool.cpu()[int(case.block_table[r, 0])])
-    log(f"[case] spec vs plain decode, {n} x {tps}: outputs and final states bit-identical")
+        a = pool_spec[int(case.block_table[r, tps - 1])]
+        b = pool.cpu()[int(case.block_table[r, 0])]
+        if tps == 1:
+            assert torch.equal(a, b)
+        else:
+            worst = max(worst, float((a - b).abs().max() / b.abs().max()))
+    assert worst <= 1e-5, worst
+    log(f"[case] spec vs plain decode, {n} x {tps}: outputs bit-identical, final states rel diff {worst:.2e}")
