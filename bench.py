@@ -465,6 +465,47 @@ def leg_conv(steps, warmup, lens, name, seed):
             "io_gbs": round(io / (ms * 1e-3) / 1e9, 1), "io_bytes_per_step": io}
 
 
+def leg_conv_decode(steps, warmup, n=32):
+    """Decode of n one-token requests (H=32, K=V=128) with the width-4 conv
+    prologue fused (kda_conv_decode_packed), against the two-pass pipeline
+    (kda_short_conv, then kda_decode_packed) on the same inputs; 2 GiB of state
+    in rotation, as in the decode leg."""
+    import torch
+
+    import gated_delta_rule_45_amd as kda
+    import workloads as W
+
+    dev = torch.device("cuda")
+    H, K, V, Wd = 32, 128, 128, 4
+    slots = 1024
+    pool = _device_pool(slots, H, K, V, 0.05, 3200, dev)
+    inp = _device_token_inputs(n, H, K, V, 3201, dev)
+    ci = W.make_conv(n, H, K, V, Wd, slots, 3202)
+    x, w, b, cs = ci["x"].to(dev), ci["weight"].to(dev), ci["bias"].to(dev), ci["conv_state"].to(dev)
+    perm = torch.randperm(slots, generator=W._gen(3203)).to(torch.int32)
+    sets = slots // n
+    idx = [perm[i * n:(i + 1) * n].to(dev) for i in range(sets)]
+    cu = torch.arange(0, n + 1, dtype=torch.int32, device=dev)
+    out = torch.empty(n, H, V, dtype=torch.bfloat16, device=dev)
+    mixed = torch.empty(n, 2 * H * K + H * V, dtype=torch.bfloat16, device=dev)
+
+    def fused(i):
+        kda.kda_conv_decode_packed(x, w, b, cs, inp["raw_g"], inp["raw_beta"], inp["A_log"], inp["dt_bias"],
+                                   -5.0, pool, idx[i % sets], out=out)
+
+    def two_pass(i):
+        kda.kda_short_conv(x, w, b, cs, idx[i % sets], cu, H=H, K=K, V=V, out=mixed)
+        kda.kda_decode_packed(mixed, inp["raw_g"], inp["raw_beta"], inp["A_log"], inp["dt_bias"], -5.0,
+                              pool, idx[i % sets], out=out)
+
+    ms_f, _ = graph_time(fused, sets, steps, warmup)
+    ms_t, _ = graph_time(two_pass, sets, steps, warmup)
+    state_bytes = 2 * n * H * K * V * 4
+    return {"workload": f"conv_decode_h32_k128_n{n}_w4", "us_per_step_fused": round(ms_f * 1e3, 3),
+            "us_per_step_two_pass": round(ms_t * 1e3, 3),
+            "state_gbs_fused": round(state_bytes / (ms_f * 1e-3) / 1e9, 1)}
+
+
 def leg_mixed(steps, warmup):
     import torch
 
@@ -591,6 +632,7 @@ def main():
                                                      "conv_prologue_decode_h32_k128_n32_w4", 3100)
         extra["conv_prologue_t8192"] = leg_conv(max(args.steps // 8, 16), 4, [8192],
                                                 "conv_prologue_t8192_h32_k128_w4", 3101)
+        extra["conv_decode_fused_n32"] = leg_conv_decode(args.steps, args.warmup)
     if "norm" in legs:
         # Gated RMSNorm output epilogue: inside the decode kernel (whole-row
         # tiles) and inside the prefill state pass.

@@ -142,6 +142,10 @@ def lib() -> ctypes.CDLL:
         L.kda_short_conv.argtypes = [i32, i64, vp, vp, i32, i32, i32, vp, i64,
                                      ctypes.POINTER(KdaShortConv), vp, i64, vp, i64, vp]
         L.kda_short_conv.restype = i32
+        L.kda_conv_decode_packed.argtypes = [i32, i32, i32, i32, i32, vp, i64,
+                                             ctypes.POINTER(KdaShortConv), vp, vp, gp, spn, npn, vp,
+                                             vp]
+        L.kda_conv_decode_packed.restype = i32
         L.kda_status_string.argtypes = [i32]
         L.kda_status_string.restype = ctypes.c_char_p
         L.kda_last_error.argtypes = []
@@ -199,8 +203,9 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
 
-def _common(m: _Marshal, mixed_qkv, raw_g, raw_beta, A_log, dt_bias, initial_state, state_indices):
-    m.tensor("mixed_qkv", mixed_qkv, torch.bfloat16, 2)
+def _common(m: _Marshal, mixed_qkv, raw_g, raw_beta, A_log, dt_bias, initial_state, state_indices,
+            qkv_name: str = "mixed_qkv"):
+    m.tensor(qkv_name, mixed_qkv, torch.bfloat16, 2)
     m.tensor("raw_g", raw_g, torch.bfloat16, 2)
     m.tensor("raw_beta", raw_beta, torch.bfloat16, 2)
     m.tensor("A_log", A_log, torch.float32, 1)
@@ -212,7 +217,7 @@ def _common(m: _Marshal, mixed_qkv, raw_g, raw_beta, A_log, dt_bias, initial_sta
     slots, H, K, V = initial_state.shape
     st = initial_state.stride()
     m.check(st[1:] == (K * V, V, 1), "initial_state must be contiguous within a slot ([H][K][V])")
-    m.check(mixed_qkv.stride(1) == 1, "mixed_qkv rows must be unit-stride")
+    m.check(mixed_qkv.stride(1) == 1, f"{qkv_name} rows must be unit-stride")
     m.check(raw_g.is_contiguous(), "raw_g must be contiguous")
     m.check(raw_beta.is_contiguous(), "raw_beta must be contiguous")
     m.check(A_log.is_contiguous() and dt_bias.is_contiguous(), "A_log and dt_bias must be contiguous")
@@ -221,7 +226,7 @@ def _common(m: _Marshal, mixed_qkv, raw_g, raw_beta, A_log, dt_bias, initial_sta
     m.check(A_log.shape[0] == H, f"A_log must have H = {H} entries")
     m.check(dt_bias.shape[0] == H * K, f"dt_bias must have H*K = {H * K} entries")
     m.check(raw_g.shape[0] == mixed_qkv.shape[0] and raw_beta.shape[0] == mixed_qkv.shape[0],
-            "mixed_qkv, raw_g and raw_beta must have the same number of rows")
+            f"{qkv_name}, raw_g and raw_beta must have the same number of rows")
     m.raise_if_any()
     return H, K, V
 
@@ -524,3 +529,45 @@ def kda_short_conv(x, weight, bias, conv_state, state_indices, cu_seqlens, *, H:
                               state_indices.stride(0), _ptr(out), out.stride(0), _stream(x.device))
     _raise_if(st)
     return out, conv_state
+
+
+def kda_conv_decode_packed(x, weight, bias, conv_state, raw_g, raw_beta, A_log, dt_bias, lower_bound,
+                           initial_state, state_indices, *, tokens_per_seq: int = 1, scale: float = 1.0,
+                           l2_eps: float = 1e-6, out=None, norm: GatedRMSNorm | None = None):
+    """Packed decode with the short conv prologue fused: q, k and v come from
+    the pre-activations ``x`` (bf16 [num_seqs*tokens_per_seq, >= D], unit-stride
+    rows) through the conv (``weight`` fp32 [D, width], ``bias`` fp32 [D] or
+    None, ``conv_state`` bf16 [slots, width-1, D], updated in place on the
+    KDA state's slot numbers). ``initial_state`` is updated in place as for
+    kda_decode_packed. Returns ``(out, initial_state, conv_state)``."""
+    m = _Marshal()
+    m.tensor("x", x, torch.bfloat16, 2)
+    m.tensor("weight", weight, torch.float32, 2)
+    m.tensor("bias", bias, torch.float32, 1, optional=True)
+    m.tensor("conv_state", conv_state, torch.bfloat16, 3)
+    m.raise_if_any()
+    H, K, V = _common(m, x, raw_g, raw_beta, A_log, dt_bias, initial_state, state_indices, "x")
+    D = 2 * H * K + H * V
+    width = weight.shape[1]
+    num_seqs = state_indices.shape[0]
+    rows = num_seqs * int(tokens_per_seq)
+    m.check(x.shape[0] == rows, f"x has {x.shape[0]} rows, expected num_seqs*tokens_per_seq = {rows}")
+    m.check(x.shape[1] >= D, f"x must have >= {D} columns")
+    m.check(tuple(weight.shape) == (D, width) and weight.is_contiguous(),
+            f"weight must be a contiguous [{D}, width] tensor")
+    if bias is not None:
+        m.check(tuple(bias.shape) == (D,) and bias.is_contiguous(), f"bias must be a contiguous [{D}] tensor")
+    m.check(conv_state.shape[1:] == (width - 1, D) and conv_state.stride(1) == D and conv_state.stride(2) == 1,
+            f"conv_state must be [slots, {width - 1}, {D}] with contiguous slots")
+    m.raise_if_any()
+    out = _out(out, rows, H, V, x.device, m)
+    nm = _norm(norm, rows, H, V, m)
+    cv = KdaShortConv(weight=weight.data_ptr(), bias=bias.data_ptr() if bias is not None else None,
+                      width=int(width), l2_eps=float(l2_eps), conv_state=conv_state.data_ptr(),
+                      conv_slot_stride=conv_state.stride(0), num_slots=conv_state.shape[0])
+    g, s = _gate(A_log, dt_bias, lower_bound, scale), _state(initial_state, state_indices)
+    st = lib().kda_conv_decode_packed(num_seqs, int(tokens_per_seq), H, K, V, _ptr(x), x.stride(0),
+                                      ctypes.byref(cv), _ptr(raw_g), _ptr(raw_beta), ctypes.byref(g),
+                                      ctypes.byref(s), _byref(nm), _ptr(out), _stream(x.device))
+    _raise_if(st)
+    return out, initial_state, conv_state

@@ -98,10 +98,13 @@ hipError_t noalloc_scratch(hipStream_t stream, void** out) {
 }
 
 // Checks shared by all entry points. rows: number of token rows the call reads.
+// qkv_name and stride_name name the row input and its row stride in
+// messages (mixed_qkv, or x for the conv entry).
 void check_common(Checks& c, int64_t rows, int32_t H, int32_t K, int32_t V,
                   const void* mixed_qkv, int64_t qkv_row_stride, const void* raw_g,
                   const void* raw_beta, const kda_gate_t* gate, const kda_state_t* state,
-                  const void* out) {
+                  const void* out, const std::string& qkv_name = "mixed_qkv",
+                  const std::string& stride_name = "qkv_row_stride") {
   const auto INV = KDA_ERR_INVALID_ARGUMENT;
   const auto UNS = KDA_ERR_UNSUPPORTED;
   c.require(H >= 1, INV, "H must be >= 1");
@@ -131,17 +134,17 @@ void check_common(Checks& c, int64_t rows, int32_t H, int32_t K, int32_t V,
     c.require(state->slot_stride % 4 == 0, UNS, "state->slot_stride must be a multiple of 4");
   }
   if (rows > 0) {
-    c.require(mixed_qkv != nullptr, INV, "mixed_qkv must not be NULL");
+    c.require(mixed_qkv != nullptr, INV, qkv_name + " must not be NULL");
     c.require(raw_g != nullptr, INV, "raw_g must not be NULL");
     c.require(raw_beta != nullptr, INV, "raw_beta must not be NULL");
     c.require(out != nullptr, INV, "out must not be NULL");
     if (H >= 1 && K >= 1 && V >= 1)
       c.require(qkv_row_stride >= 2 * static_cast<int64_t>(H) * K + static_cast<int64_t>(H) * V, INV,
-                "qkv_row_stride must be >= 2*H*K + H*V");
-    c.require(qkv_row_stride % 8 == 0, UNS, "qkv_row_stride must be a multiple of 8");
+                stride_name + " must be >= 2*H*K + H*V");
+    c.require(qkv_row_stride % 8 == 0, UNS, stride_name + " must be a multiple of 8");
     c.require(qkv_row_stride <= (int64_t{1} << 24), UNS,
-              "qkv_row_stride must be <= 2^24 (kernels address 64 rows with 32-bit offsets)");
-    c.require(aligned(mixed_qkv, 16), UNS, "mixed_qkv must be 16-byte aligned");
+              stride_name + " must be <= 2^24 (kernels address 64 rows with 32-bit offsets)");
+    c.require(aligned(mixed_qkv, 16), UNS, qkv_name + " must be 16-byte aligned");
     c.require(aligned(raw_g, 16), UNS, "raw_g must be 16-byte aligned");
     c.require(aligned(raw_beta, 2), UNS, "raw_beta must be 2-byte aligned");
     c.require(aligned(out, 16), UNS, "out must be 16-byte aligned");
@@ -212,6 +215,27 @@ kda_status_t hip_status(hipError_t e, const char* what) {
   }
   g_last_error = std::string(what) + ": " + hipGetErrorString(e);
   return KDA_ERR_HIP;
+}
+
+// The conv weights, bias and state pool.
+void check_conv(Checks& c, const kda_short_conv_t* conv, int32_t H, int32_t K, int32_t V) {
+  const auto INV = KDA_ERR_INVALID_ARGUMENT;
+  const auto UNS = KDA_ERR_UNSUPPORTED;
+  c.require(conv != nullptr, INV, "conv must not be NULL");
+  if (conv == nullptr) return;
+  const int64_t D = 2 * static_cast<int64_t>(H) * K + static_cast<int64_t>(H) * V;
+  c.require(conv->width >= 2 && conv->width <= 4, UNS, "conv->width must be 2, 3 or 4");
+  c.require(std::isfinite(conv->l2_eps) && conv->l2_eps > 0.0f, INV, "conv->l2_eps must be finite and > 0");
+  c.require(conv->weight != nullptr, INV, "conv->weight must not be NULL");
+  c.require(aligned(conv->weight, 16), UNS, "conv->weight must be 16-byte aligned");
+  c.require(conv->bias == nullptr || aligned(conv->bias, 16), UNS, "conv->bias must be 16-byte aligned");
+  c.require(conv->conv_state != nullptr, INV, "conv->conv_state must not be NULL");
+  c.require(aligned(conv->conv_state, 16), UNS, "conv->conv_state must be 16-byte aligned");
+  c.require(conv->num_slots >= 1, INV, "conv->num_slots must be >= 1");
+  if (H >= 1)
+    c.require(conv->conv_slot_stride >= (conv->width - 1) * D, INV,
+              "conv->conv_slot_stride must be >= (width-1)*D");
+  c.require(conv->conv_slot_stride % 8 == 0, UNS, "conv->conv_slot_stride must be a multiple of 8");
 }
 
 kda::PrefillParams prefill_params(int32_t num_seqs, int64_t num_tokens, const int32_t* cu_seqlens,
@@ -289,6 +313,41 @@ kda_status_t kda_decode_packed(int32_t num_seqs, int32_t tokens_per_seq, int32_t
                                       raw_g, raw_beta, gate, state, out);
   p.norm = out_norm(norm, 0);
   return hip_status(kda::launch_decode(p, K, stream), "decode launch");
+}
+
+kda_status_t kda_conv_decode_packed(int32_t num_seqs, int32_t tokens_per_seq, int32_t H, int32_t K,
+                                    int32_t V, const void* x, int64_t x_row_stride,
+                                    const kda_short_conv_t* conv, const void* raw_g,
+                                    const void* raw_beta, const kda_gate_t* gate,
+                                    const kda_state_t* state, const kda_out_norm_t* norm, void* out,
+                                    hipStream_t stream) {
+  Checks c;
+  const auto INV = KDA_ERR_INVALID_ARGUMENT;
+  c.require(num_seqs >= 0, INV, "num_seqs must be >= 0");
+  c.require(tokens_per_seq >= 1 && tokens_per_seq <= 8, INV,
+            "tokens_per_seq must be in 1..8 (spec-verify steps have at most 8 rows per request)");
+  const int64_t rows = static_cast<int64_t>(num_seqs) * tokens_per_seq;
+  c.require(rows <= 0x7fffffffLL, INV, "num_seqs * tokens_per_seq must fit in int32");
+  check_common(c, rows, H, K, V, x, x_row_stride, raw_g, raw_beta, gate, state, out, "x", "x_row_stride");
+  check_norm(c, rows, H, V, norm);
+  check_conv(c, conv, H, K, V);
+  if (conv && state)
+    c.require(conv->num_slots >= state->num_slots, INV,
+              "conv->num_slots must be >= state->num_slots (the conv state shares the slot numbers)");
+  if (!c.ok()) return c.finish();
+  if (num_seqs == 0) return c.finish();
+  kda::DecodeParams p = decode_params(num_seqs, tokens_per_seq, H, V, nullptr, x_row_stride, raw_g,
+                                      raw_beta, gate, state, out);
+  p.norm = out_norm(norm, 0);
+  p.conv.x = static_cast<const uint16_t*>(x);
+  p.conv.x_row_stride = x_row_stride;
+  p.conv.weight = conv->weight;
+  p.conv.bias = conv->bias;
+  p.conv.width = conv->width;
+  p.conv.l2_eps = conv->l2_eps;
+  p.conv.conv_state = static_cast<uint16_t*>(conv->conv_state);
+  p.conv.conv_slot_stride = conv->conv_slot_stride;
+  return hip_status(kda::launch_decode(p, K, stream), "conv decode launch");
 }
 
 kda_status_t kda_spec_decode(int32_t num_seqs, int32_t tokens_per_seq, int32_t H, int32_t K,
@@ -526,24 +585,10 @@ kda_status_t kda_short_conv(int32_t num_seqs, int64_t num_rows, const int32_t* c
   c.require(H >= 1, INV, "H must be >= 1");
   c.require(K == 64 || K == 128, UNS, "K must be 64 or 128");
   c.require(V == 64 || V == 128, UNS, "V must be 64 or 128");
-  c.require(conv != nullptr, INV, "conv must not be NULL");
   c.require(indices != nullptr || num_seqs == 0, INV, "indices must not be NULL");
   c.require(index_stride >= 1, INV, "index_stride must be >= 1 (a non-positive stride is rejected)");
+  check_conv(c, conv, H, K, V);
   const int64_t D = 2 * static_cast<int64_t>(H) * K + static_cast<int64_t>(H) * V;
-  if (conv) {
-    c.require(conv->width >= 2 && conv->width <= 4, UNS, "conv->width must be 2, 3 or 4");
-    c.require(std::isfinite(conv->l2_eps) && conv->l2_eps > 0.0f, INV, "conv->l2_eps must be finite and > 0");
-    c.require(conv->weight != nullptr, INV, "conv->weight must not be NULL");
-    c.require(aligned(conv->weight, 16), UNS, "conv->weight must be 16-byte aligned");
-    c.require(conv->bias == nullptr || aligned(conv->bias, 16), UNS, "conv->bias must be 16-byte aligned");
-    c.require(conv->conv_state != nullptr, INV, "conv->conv_state must not be NULL");
-    c.require(aligned(conv->conv_state, 16), UNS, "conv->conv_state must be 16-byte aligned");
-    c.require(conv->num_slots >= 1, INV, "conv->num_slots must be >= 1");
-    if (H >= 1)
-      c.require(conv->conv_slot_stride >= (conv->width - 1) * D, INV,
-                "conv->conv_slot_stride must be >= (width-1)*D");
-    c.require(conv->conv_slot_stride % 8 == 0, UNS, "conv->conv_slot_stride must be a multiple of 8");
-  }
   if (num_rows > 0) {
     c.require(x != nullptr, INV, "x must not be NULL");
     c.require(mixed_qkv != nullptr, INV, "mixed_qkv must not be NULL");

@@ -163,8 +163,9 @@ template <int W>
 __global__ __launch_bounds__(kConvThreads) void conv_state_kernel(const ConvParams p, int Dn) {
   const int s = blockIdx.x;
   if (s >= p.num_seqs) return;
-  const int64_t bos = uniform(static_cast<int64_t>(p.cu_seqlens[s]));
-  const int64_t eos = uniform(static_cast<int64_t>(p.cu_seqlens[s + 1]));
+  const int64_t bos = p.uniform_len > 0 ? static_cast<int64_t>(s) * p.uniform_len
+                                        : uniform(static_cast<int64_t>(p.cu_seqlens[s]));
+  const int64_t eos = p.uniform_len > 0 ? bos + p.uniform_len : uniform(static_cast<int64_t>(p.cu_seqlens[s + 1]));
   const int64_t len = eos - bos;
   if (len <= 0 || bos < 0 || eos > p.num_rows) return;  // nothing to store
   const int64_t slot = uniform(static_cast<int64_t>(p.indices[static_cast<int64_t>(s) * p.index_stride]));
@@ -219,6 +220,18 @@ hipError_t launch_kv(const ConvParams& p, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t launch_conv_state(const ConvParams& p, hipStream_t stream) {
+  if (p.num_seqs <= 0) return hipSuccess;
+  const int Dn = 2 * p.H * p.K + p.H * p.V;
+  const dim3 seqs(static_cast<unsigned>(p.num_seqs));
+  switch (p.width) {
+    case 2: conv_state_kernel<2><<<seqs, kConvThreads, 0, stream>>>(p, Dn); break;
+    case 3: conv_state_kernel<3><<<seqs, kConvThreads, 0, stream>>>(p, Dn); break;
+    default: conv_state_kernel<4><<<seqs, kConvThreads, 0, stream>>>(p, Dn); break;
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_short_conv(const ConvParams& p, hipStream_t stream) {
   if (p.num_seqs <= 0) return hipSuccess;

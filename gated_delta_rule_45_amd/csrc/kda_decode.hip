@@ -31,6 +31,12 @@
 // groups (DPP rotations and lane swaps, no LDS traffic), and a sum of the
 // four waves' partials through LDS (one barrier per token; the partial
 // buffer alternates between tokens).
+//
+// With the short conv prologue fused (kda_conv_decode_packed; vLLM PR
+// #60683, Purpose, runs conv, recurrence and norm in one decode kernel), the
+// staging computes q, k and v from the pre-activations and the conv state
+// instead of reading mixed_qkv; a workgroup that holds whole heads also
+// writes the heads' new conv states.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -67,9 +73,150 @@ __device__ __forceinline__ float sum_row_groups(float x) {
 
 }  // namespace
 
-template <int K, int V, int VT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8)))
-void decode_kernel(const DecodeParams p) {
+// Fused short conv prologue (the conv of kda_conv.hip, same arithmetic and
+// rounding, so the staged q, k and v equal what the separate conv pass
+// would have written to mixed_qkv). Request n's tokens are one conv
+// sequence on conv-state slot `slot` (its state slot, never null here).
+// Waves 2p and 2p+1 take tokens t = p, p + 2, ...: in the first, lanes
+// 0 .. K/4-1 work on the head's q and the next K/4 on its k; in the second,
+// lanes 0 .. VT/4-1 on the tile's v columns; 4 channels per lane. The window
+// of CW inputs of a token comes from the request's x rows, or from the conv
+// state for positions before its first row. q and k are L2-normalised over
+// the head: the sum of squares of each 8 channels runs as one chain over a
+// lane pair (the even lane's 4 channels, continued by the odd lane), then a
+// butterfly over the head's odd lanes, in the order of the separate pass.
+// With one token per request and the whole head in the workgroup, each lane
+// also writes its channels' new conv state (taps 1 .. CW-1 of the token) at
+// once: no other lane reads those channels' old state.
+template <int K, int V, int VT, int CW>
+__device__ __forceinline__ void stage_conv_inputs(const DecodeParams& p, int64_t slot, int n, int h, int tile,
+                                                  float (*s_q)[K], float (*s_k)[K], float (*s_v)[VT]) {
+  constexpr int LQ = K / 4, LV = VT / 4;  // lanes per q (or k) head, per v tile
+  static_assert(2 * LQ <= 64 && LV <= 64, "conv lanes per wave");
+  const DecodeConv& cv = p.conv;
+  const int H = p.H, tps = p.tokens_per_seq;
+  const int Dn = 2 * H * K + H * V;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int pair = w >> 1, role = w & 1;  // role 0: q and k, 1: v
+  if (pair >= tps) return;  // no token for this wave (its taps would go unused)
+  const int64_t row0 = static_cast<int64_t>(n) * tps;
+  int c0 = 0, dst = 0, sec = 3;  // section: 0 q, 1 k, 2 v, 3 none
+  if (role == 0) {
+    if (lane < LQ) {
+      c0 = h * K + 4 * lane; dst = 4 * lane; sec = 0;
+    } else if (lane < 2 * LQ) {
+      c0 = H * K + h * K + 4 * (lane - LQ); dst = 4 * (lane - LQ); sec = 1;
+    }
+  } else if (lane < LV) {
+    c0 = 2 * H * K + h * V + tile * VT + 4 * lane; dst = 4 * lane; sec = 2;
+  }
+  const bool live = sec < 3;
+  // Taps and bias of the lane's 4 channels: w[c0 + j][i] at (c0 + j) * CW + i.
+  float wt[4 * CW], bias[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int q = 0; q < CW; ++q) {
+    const f32x4 v = live ? *reinterpret_cast<const f32x4*>(cv.weight + static_cast<int64_t>(c0) * CW + 4 * q)
+                         : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) wt[4 * q + j] = v[j];
+  }
+  if (live && cv.bias != nullptr) {
+    const f32x4 b = *reinterpret_cast<const f32x4*>(cv.bias + c0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bias[j] = b[j];
+  }
+  uint16_t* st = cv.conv_state + slot * cv.conv_slot_stride;
+  const bool write_now = VT == V && tps == 1 && live;
+  for (int t = pair; t < tps; t += kWaves / 2) {
+    uint2 raw[CW];  // the window, bf16 pairs (widened where used)
+#pragma unroll
+    for (int i = 0; i < CW; ++i) {
+      const int src = t - (CW - 1) + i;
+      raw[i] = uint2{0u, 0u};
+      if (live && src >= 0)
+        raw[i] = *reinterpret_cast<const uint2*>(cv.x + (row0 + src) * cv.x_row_stride + c0);
+      else if (live)
+        raw[i] = *reinterpret_cast<const uint2*>(st + static_cast<int64_t>(CW - 1 + src) * Dn + c0);
+    }
+    if (write_now) {
+#pragma unroll
+      for (int i = 1; i < CW; ++i) *reinterpret_cast<uint2*>(st + static_cast<int64_t>(i - 1) * Dn + c0) = raw[i];
+    }
+    float y[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float acc = bias[j];
+#pragma unroll
+      for (int i = 0; i < CW; ++i) {
+        const uint32_t wd = j < 2 ? raw[i].x : raw[i].y;
+        const float xv = __uint_as_float((j & 1) ? (wd & 0xffff0000u) : (wd << 16));
+        acc = fmaf(wt[j * CW + i], xv, acc);
+      }
+      y[j] = live ? acc * sigmoid_f32(acc) : 0.f;
+    }
+    // Sum of squares of the 8 channels of a lane pair, as one chain: the even
+    // lane's 4 from zero, continued by the odd lane (row_shr:1 brings the
+    // even lane's value); then the butterfly over the odd lanes of a head,
+    // and the odd lane's total back to the even one.
+    float e = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) e = fmaf(y[j], y[j], e);  // the even lanes' chain
+    float o = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(e), 0x111, 0xf, 0xf, false));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o = fmaf(y[j], y[j], o);  // continued by the odd lanes
+    float ss = (lane & 1) ? o : e;
+#pragma unroll
+    for (int off = 2; off < LQ; off <<= 1) ss += __shfl_xor(ss, off);
+    ss = __shfl(ss, lane | 1);
+    if (sec < 2) {
+      const float inv = 1.0f / sqrtf(ss + cv.l2_eps);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) y[j] *= inv;
+    }
+    if (live) {
+      float* d = sec == 0 ? &s_q[t][dst] : sec == 1 ? &s_k[t][dst] : &s_v[t][dst];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) d[j] = bf16_to_f32(f32_to_bf16_rne(y[j]));
+    }
+  }
+}
+
+// The new conv state of a request of several tokens, its last CW-1 inputs
+// (older ones from the old state for a shorter request), after the barrier
+// that ends every read of the old state: a workgroup that holds the whole
+// head owns these channels. Waves 0 and 1 take q and k, and v; each lane
+// reads all its rows before it writes any.
+template <int K, int V, int CW>
+__device__ __forceinline__ void store_conv_state(const DecodeParams& p, int64_t slot, int n, int h) {
+  constexpr int LQ = K / 4, LV = V / 4;
+  const DecodeConv& cv = p.conv;
+  const int H = p.H, tps = p.tokens_per_seq;
+  const int Dn = 2 * H * K + H * V;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int c0;
+  if (w == 0 && lane < 2 * LQ)
+    c0 = lane < LQ ? h * K + 4 * lane : H * K + h * K + 4 * (lane - LQ);
+  else if (w == 1 && lane < LV)
+    c0 = 2 * H * K + h * V + 4 * lane;
+  else
+    return;
+  const int64_t row0 = static_cast<int64_t>(n) * tps;
+  uint16_t* st = cv.conv_state + slot * cv.conv_slot_stride;
+  uint2 rows[CW - 1];
+#pragma unroll
+  for (int j = 0; j < CW - 1; ++j) {
+    const int q = tps - (CW - 1) + j;  // position of new row j
+    rows[j] = q >= 0 ? *reinterpret_cast<const uint2*>(cv.x + (row0 + q) * cv.x_row_stride + c0)
+                     : *reinterpret_cast<const uint2*>(st + static_cast<int64_t>(CW - 1 + q) * Dn + c0);
+  }
+#pragma unroll
+  for (int j = 0; j < CW - 1; ++j) *reinterpret_cast<uint2*>(st + static_cast<int64_t>(j) * Dn + c0) = rows[j];
+}
+
+// CW > 0: the short conv prologue of width CW is fused into the staging
+// (launched through decode_conv_kernel, which allows more registers).
+template <int K, int V, int VT, int CW>
+__device__ __forceinline__ void decode_body(const DecodeParams& p) {
   constexpr int RW = K / kWaves;   // rows per wave
   constexpr int CG = VT / 4;       // column groups of 4 columns
   constexpr int RG = 64 / CG;      // row groups per wave
@@ -134,7 +281,21 @@ void decode_kernel(const DecodeParams p) {
   {
     const float a = __expf(p.A_log[h]);
     const bool has_lb = p.has_lb != 0;
-    if (tps >= 3) {
+    if constexpr (CW > 0) {
+      // The gates first, on the threads from 128 on (so that with one or two
+      // tokens the waves that take the conv work have none), then the conv.
+      for (int e = (tid + 128) & 255; e < tps * K; e += 256) {
+        const int t = e / K, i = e % K;
+        const float g = gate_log_decay(bf16_to_f32(p.raw_g[(row0 + t) * (H * K) + h * K + i]),
+                                       p.dt_bias[h * K + i], a, has_lb, p.lower_bound);
+        s_a[t][i] = __expf(g);
+      }
+      if (tid >= 256 - kMaxTokens && tid - (256 - kMaxTokens) < tps) {
+        const int t = tid - (256 - kMaxTokens);
+        s_b[t] = sigmoid_f32(bf16_to_f32(p.raw_beta[(row0 + t) * H + h]));
+      }
+      stage_conv_inputs<K, V, VT, CW>(p, slot, n, h, tile, s_q, s_k, s_v);
+    } else if (tps >= 3) {
       // Long requests: every load is issued before the first use (buffer
       // loads over the request's rows; elements past its tokens read zero
       // and are not stored), one memory round trip instead of one per pass.
@@ -208,6 +369,9 @@ void decode_kernel(const DecodeParams p) {
     }
   }
   __syncthreads();
+  if constexpr (CW > 0 && VT == V) {
+    if (tps > 1) store_conv_state<K, V, CW>(p, slot, n, h);
+  }
 
   // 3. Token loop, all in registers.
   for (int t = 0; t < tps; ++t) {
@@ -303,6 +467,18 @@ void decode_kernel(const DecodeParams p) {
 #pragma unroll
     for (int r = 0; r < RPL; ++r) buffer_store_f32x4<kStreamPolicy>(S[r], tile_rsrc, voff, r * V * 4);
   }
+}
+
+template <int K, int V, int VT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8)))
+void decode_kernel(const DecodeParams p) {
+  decode_body<K, V, VT, 0>(p);
+}
+
+template <int K, int V, int VT, int CW>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8)))
+void decode_conv_kernel(const DecodeParams p) {
+  decode_body<K, V, VT, CW>(p);
 }
 
 namespace {
@@ -845,6 +1021,24 @@ static void launch_block(const DecodeParams& p, dim3 grid, dim3 block, hipStream
   else launch_block_pt<K, V, NT, NCB, false>(p, grid, block, stream);
 }
 
+template <int K, int V, int VT, int CW>
+static void launch_one(const DecodeParams& p, dim3 grid, dim3 block, hipStream_t stream) {
+  if constexpr (CW == 0) decode_kernel<K, V, VT><<<grid, block, 0, stream>>>(p);
+  else decode_conv_kernel<K, V, VT, CW><<<grid, block, 0, stream>>>(p);
+}
+
+template <int K, int V, int CW>
+static void launch_vt(const DecodeParams& p, int vt, dim3 grid, dim3 block, hipStream_t stream) {
+  switch (vt) {
+    case 16: launch_one<K, V, 16, CW>(p, grid, block, stream); break;
+    case 32: launch_one<K, V, 32, CW>(p, grid, block, stream); break;
+    case 64: launch_one<K, V, 64, CW>(p, grid, block, stream); break;
+    default:
+      if constexpr (V == 128) launch_one<K, V, 128, CW>(p, grid, block, stream);
+      break;
+  }
+}
+
 template <int K, int V>
 static hipError_t launch_kv(const DecodeParams& p, int vt, bool block_form, hipStream_t stream) {
   const int64_t blocks = static_cast<int64_t>(p.num_seqs) * p.H * (V / vt);
@@ -872,13 +1066,11 @@ static hipError_t launch_kv(const DecodeParams& p, int vt, bool block_form, hipS
     }
     return hipGetLastError();
   }
-  switch (vt) {
-    case 16: decode_kernel<K, V, 16><<<grid, block, 0, stream>>>(p); break;
-    case 32: decode_kernel<K, V, 32><<<grid, block, 0, stream>>>(p); break;
-    case 64: decode_kernel<K, V, 64><<<grid, block, 0, stream>>>(p); break;
-    default:
-      if constexpr (V == 128) decode_kernel<K, V, 128><<<grid, block, 0, stream>>>(p);
-      break;
+  switch (p.conv.x == nullptr ? 0 : p.conv.width) {
+    case 0: launch_vt<K, V, 0>(p, vt, grid, block, stream); break;
+    case 2: launch_vt<K, V, 2>(p, vt, grid, block, stream); break;
+    case 3: launch_vt<K, V, 3>(p, vt, grid, block, stream); break;
+    default: launch_vt<K, V, 4>(p, vt, grid, block, stream); break;
   }
   return hipGetLastError();
 }
@@ -890,7 +1082,8 @@ static hipError_t launch_kv(const DecodeParams& p, int vt, bool block_form, hipS
 // (on 16- or 32-column tiles).
 hipError_t launch_decode(DecodeParams p, int K, hipStream_t stream) {
   const int64_t pairs = static_cast<int64_t>(p.num_seqs) * p.H;
-  const bool block_form = p.tokens_per_seq >= kBlockMinTokens && pairs < 256;
+  const bool conv = p.conv.x != nullptr;
+  const bool block_form = !conv && p.tokens_per_seq >= kBlockMinTokens && pairs < 256;
   int vt = 128;
   if (pairs < 512) vt = 64;
   if (pairs < 256) vt = 32;
@@ -910,6 +1103,25 @@ hipError_t launch_decode(DecodeParams p, int K, hipStream_t stream) {
     e = p.V == 64 ? launch_kv<64, 64>(p, vt, block_form, stream) : launch_kv<64, 128>(p, vt, block_form, stream);
   else
     e = p.V == 64 ? launch_kv<128, 64>(p, vt, block_form, stream) : launch_kv<128, 128>(p, vt, block_form, stream);
+  if (e == hipSuccess && conv && vt != p.V) {
+    // Workgroups of one head share its q and k channels: the new conv
+    // states are written by a pass after every workgroup has read the old.
+    ConvParams c{};
+    c.x = p.conv.x;
+    c.x_row_stride = p.conv.x_row_stride;
+    c.width = p.conv.width;
+    c.conv_state = p.conv.conv_state;
+    c.conv_slot_stride = p.conv.conv_slot_stride;
+    c.indices = p.indices;
+    c.index_stride = p.index_stride;
+    c.uniform_len = p.tokens_per_seq;
+    c.num_seqs = p.num_seqs;
+    c.num_rows = static_cast<int64_t>(p.num_seqs) * p.tokens_per_seq;
+    c.H = p.H;
+    c.K = K;
+    c.V = p.V;
+    e = launch_conv_state(c, stream);
+  }
   if (e != hipSuccess || !separate) return e;
   return launch_gated_rmsnorm(norm, p.out, static_cast<int64_t>(p.num_seqs) * p.tokens_per_seq, p.H,
                               p.V, stream);

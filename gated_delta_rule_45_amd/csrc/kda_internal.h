@@ -23,6 +23,21 @@ hipError_t launch_gated_rmsnorm(const OutNorm& n, uint16_t* out, int64_t rows, i
                                 int32_t V, hipStream_t stream);
 
 // One packed-decode / spec-verify launch.
+// Short conv prologue fused into the decode staging (x null: none): q, k
+// and v come from the pre-activations x through the conv, request n's
+// tokens forming one conv sequence on conv-state slot indices[n] (its state
+// slot).
+struct DecodeConv {
+  const uint16_t* x;         // bf16 [rows][x_row_stride], channels [q | k | v]
+  int64_t x_row_stride;      // elements
+  const float* weight;       // [D][width]
+  const float* bias;         // [D] or null
+  int32_t width;             // 2..4
+  float l2_eps;
+  uint16_t* conv_state;      // bf16 pool; slot s at s*conv_slot_stride: [width-1][D]
+  int64_t conv_slot_stride;  // elements
+};
+
 struct DecodeParams {
   const uint16_t* qkv;      // bf16 [rows][qkv_row_stride]
   int64_t qkv_row_stride;   // elements
@@ -45,6 +60,7 @@ struct DecodeParams {
   int64_t index_col_stride;
   uint16_t* out;            // bf16 [rows][H][V]
   OutNorm norm;             // fused into the kernel when a workgroup holds whole rows
+  DecodeConv conv;          // x null: mixed_qkv holds q, k, v
   int32_t num_seqs;
   int32_t tokens_per_seq;
   int32_t H;
@@ -64,7 +80,8 @@ struct ConvParams {
   int64_t conv_slot_stride;     // elements
   const int32_t* indices;       // entry i at indices[i*index_stride]; < 0: null
   int64_t index_stride;
-  const int32_t* cu_seqlens;    // [num_seqs+1]
+  const int32_t* cu_seqlens;    // [num_seqs+1] (unused when uniform_len > 0)
+  int32_t uniform_len;          // > 0: sequence i is rows i*uniform_len .. (i+1)*uniform_len - 1
   const uint8_t* has_initial_state;  // may be null (all 1)
   uint16_t* out;                // bf16 [rows][out_row_stride] (mixed_qkv)
   int64_t out_row_stride;       // elements
@@ -76,6 +93,9 @@ struct ConvParams {
 };
 
 hipError_t launch_short_conv(const ConvParams& p, hipStream_t stream);
+// Only the conv-state pass of launch_short_conv (the new states from x and
+// the old states), for callers that computed the conv outputs themselves.
+hipError_t launch_conv_state(const ConvParams& p, hipStream_t stream);
 
 // Picks the column-tile width for a decode launch and launches it.
 hipError_t launch_decode(DecodeParams p, int K, hipStream_t stream);

@@ -351,6 +351,38 @@ kda_status_t kda_short_conv(int32_t num_seqs, int64_t num_rows,
                             void* mixed_qkv, int64_t qkv_row_stride,
                             hipStream_t stream);
 
+/*
+ * Packed decode with the short conv prologue fused (vLLM PR #60683, Purpose:
+ * its decode kernel runs the conv step, the KDA recurrence and the gated
+ * RMSNorm as one kernel). As kda_decode_packed, except that q, k and v come
+ * from the [q | k | v] pre-activations x through the conv of
+ * kda_short_conv, and mixed_qkv is never materialised:
+ *   x     bf16 [num_seqs*tokens_per_seq][x_row_stride], x_row_stride >= D
+ *         (D = 2*H*K + H*V), a multiple of 8, 16-byte aligned;
+ *   conv  weights, bias, width, l2_eps and the bf16 conv-state pool, as for
+ *         kda_short_conv; conv->num_slots >= state->num_slots.
+ * Request n's tokens form one conv sequence whose conv-state slot is its KDA
+ * state slot (state->indices); the conv state is read as the request's
+ * initial state and replaced by its last width-1 inputs. A null slot reads
+ * and writes neither state and yields zero output rows. The staged q, k and
+ * v are bit-identical to those a kda_short_conv call writes into mixed_qkv
+ * (same arithmetic, bf16 rounding included), and the decode kernel that
+ * consumes them is kda_decode_packed's per-token kernel, also for requests of
+ * several tokens (the spec-verify block form is not used on this path).
+ * One launch when a workgroup holds whole heads (num_seqs*H >= 512, or
+ * >= 256 with V = 64); otherwise the new conv states are written by a
+ * second, small launch after the decode kernel.
+ * Errors: as kda_decode_packed and kda_short_conv (row-input checks name x).
+ */
+kda_status_t kda_conv_decode_packed(int32_t num_seqs, int32_t tokens_per_seq,
+                                    int32_t H, int32_t K, int32_t V,
+                                    const void* x, int64_t x_row_stride,
+                                    const kda_short_conv_t* conv,
+                                    const void* raw_g, const void* raw_beta,
+                                    const kda_gate_t* gate, const kda_state_t* state,
+                                    const kda_out_norm_t* norm, void* out,
+                                    hipStream_t stream);
+
 /* Static name of a status code. */
 const char* kda_status_string(kda_status_t status);
 

@@ -117,6 +117,24 @@ def test_short_conv_rejects_and_lists_every_reason():
     assert st == 1 and "must not overlap x" in L.kda_last_error().decode()
 
 
+def test_conv_decode_rejects_and_lists_every_reason():
+    L = kda.lib()
+    g, s_ = _gate(), _state()
+    cv = B.KdaShortConv(weight=None, bias=FAKE, width=5, l2_eps=1e-6, conv_state=FAKE,
+                        conv_slot_stride=3 * 3 * 32 * 128, num_slots=2)
+    st = L.kda_conv_decode_packed(4, 1, 32, 128, 128, FAKE + 2, 3 * 32 * 128 + 4, ctypes.byref(cv), FAKE,
+                                  FAKE, ctypes.byref(g), ctypes.byref(s_), None, FAKE, None)
+    msg = L.kda_last_error().decode()
+    assert st == 1
+    for frag in ("conv->width must be 2, 3 or 4", "conv->weight must not be NULL",
+                 "conv->num_slots must be >= state->num_slots", "x must be 16-byte aligned",
+                 "x_row_stride must be a multiple of 8"):
+        assert frag in msg, msg
+    st = L.kda_conv_decode_packed(4, 1, 32, 128, 128, FAKE, 3 * 32 * 128, None, FAKE, FAKE,
+                                  ctypes.byref(g), ctypes.byref(s_), None, FAKE, None)
+    assert st == 1 and "conv must not be NULL" in L.kda_last_error().decode()
+
+
 def test_negative_index_stride_rejected():
     st, msg = _decode(s=_state(index_stride=-8))
     assert st == 1 and "index_stride" in msg
