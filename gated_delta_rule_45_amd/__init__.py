@@ -13,6 +13,7 @@ from ._binding import (  # noqa: F401
     kda_chunk_prefill,
     kda_chunk_prefill_noalloc,
     kda_chunk_prefill_workspace_maps,
+    kda_chunk_prefill_workspace_min_size,
     kda_chunk_prefill_workspace_size,
     kda_conv_decode_packed,
     kda_decode_packed,
@@ -33,6 +34,7 @@ __all__ = [
     "kda_chunk_prefill",
     "kda_chunk_prefill_noalloc",
     "kda_chunk_prefill_workspace_maps",
+    "kda_chunk_prefill_workspace_min_size",
     "kda_chunk_prefill_workspace_size",
     "kda_conv_decode_packed",
     "kda_decode_packed",

@@ -121,6 +121,8 @@ def lib() -> ctypes.CDLL:
         L.kda_spec_decode.restype = i32
         L.kda_chunk_prefill_workspace_size.argtypes = [i32, i64, i32, i32, i32]
         L.kda_chunk_prefill_workspace_size.restype = sz
+        L.kda_chunk_prefill_workspace_min_size.argtypes = [i32, i64, i32, i32, i32]
+        L.kda_chunk_prefill_workspace_min_size.restype = sz
         L.kda_chunk_prefill_workspace_maps.argtypes = [i32, i64, i32, i32, i32, ctypes.POINTER(sz),
                                                        ctypes.POINTER(sz), ctypes.POINTER(i64)]
         L.kda_chunk_prefill_workspace_maps.restype = i32
@@ -349,6 +351,11 @@ def kda_spec_decode(mixed_qkv, raw_g, raw_beta, A_log, dt_bias, lower_bound, ini
 
 def kda_chunk_prefill_workspace_size(num_seqs: int, num_tokens: int, H: int, K: int, V: int) -> int:
     return int(lib().kda_chunk_prefill_workspace_size(num_seqs, num_tokens, H, K, V))
+
+
+def kda_chunk_prefill_workspace_min_size(num_seqs: int, num_tokens: int, H: int, K: int, V: int) -> int:
+    """The smallest workspace kda_chunk_prefill accepts (no chunk records)."""
+    return int(lib().kda_chunk_prefill_workspace_min_size(num_seqs, num_tokens, H, K, V))
 
 
 def kda_chunk_prefill_workspace_maps(num_seqs: int, num_tokens: int, H: int, K: int, V: int):

@@ -281,9 +281,9 @@ void check_prefill_specific(Checks& c, int32_t num_seqs, int64_t num_tokens,
   if (num_seqs > 0) c.require(cu_seqlens != nullptr, INV, "cu_seqlens must not be NULL");
   c.require(num_tokens == 0 || num_seqs > 0, INV, "num_tokens > 0 needs num_seqs > 0");
   if (num_seqs > 0 && num_tokens > 0 && H >= 1 && (K == 64 || K == 128) && (V == 64 || V == 128)) {
-    const size_t need = kda::prefill_workspace_bytes(num_seqs, num_tokens, H, K, V);
+    const size_t need = kda::prefill_workspace_min_bytes(num_seqs, num_tokens, H, K, V);
     c.require(workspace != nullptr && workspace_bytes >= need, KDA_ERR_WORKSPACE,
-              "workspace must be at least kda_chunk_prefill_workspace_size() bytes (" +
+              "workspace must be at least kda_chunk_prefill_workspace_min_size() bytes (" +
                   std::to_string(need) + ")");
     c.require(aligned(workspace, 256), KDA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   }
@@ -384,6 +384,13 @@ size_t kda_chunk_prefill_workspace_size(int32_t num_seqs, int64_t num_tokens, in
   return kda::prefill_workspace_bytes(num_seqs, num_tokens, H, K, V);
 }
 
+size_t kda_chunk_prefill_workspace_min_size(int32_t num_seqs, int64_t num_tokens, int32_t H, int32_t K,
+                                            int32_t V) {
+  if (num_seqs < 0 || num_tokens < 0 || H < 1 || !(K == 64 || K == 128) || !(V == 64 || V == 128))
+    return 0;
+  return kda::prefill_workspace_min_bytes(num_seqs, num_tokens, H, K, V);
+}
+
 kda_status_t kda_chunk_prefill_workspace_maps(int32_t num_seqs, int64_t num_tokens, int32_t H, int32_t K,
                                               int32_t V, size_t* offset, size_t* item_bytes,
                                               int64_t* items) {
@@ -429,7 +436,7 @@ kda_status_t kda_chunk_prefill_noalloc(int32_t num_seqs, int64_t num_tokens,
   check_common(c, num_tokens, H, K, V, mixed_qkv, qkv_row_stride, raw_g, raw_beta, gate, state, out);
   size_t need = 0;
   if (num_seqs > 0 && num_tokens > 0 && H >= 1 && (K == 64 || K == 128) && (V == 64 || V == 128))
-    need = kda::prefill_workspace_bytes(num_seqs, num_tokens, H, K, V);
+    need = kda::prefill_workspace_min_bytes(num_seqs, num_tokens, H, K, V);
   c.require(need <= kNoallocScratchBytes, KDA_ERR_WORKSPACE,
             "these sizes need " + std::to_string(need) + " bytes of workspace, more than the " +
                 std::to_string(kNoallocScratchBytes) + " bytes of the static scratch (KDA_NOALLOC_SCRATCH_BYTES)");

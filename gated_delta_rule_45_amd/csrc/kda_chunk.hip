@@ -242,8 +242,9 @@ __device__ __forceinline__ void chunk_barrier() {
 // full chunks), into no more segments than it takes for the cut sequences'
 // workgroups of one launch to occupy kChipSlots slots (one per compute
 // unit: a workgroup's LDS takes most of a CU), and only into kMinCut
-// segments or more: a map chunk costs about as much as a state chunk, so two
-// segments would not shorten the chain.
+// segments or more without records: a map chunk costs about as much as a
+// state chunk, so two segments would not shorten the chain. With records
+// (the first launch keeps each chunk's operands for the second) two do.
 constexpr int kSegMinChunks = 6;
 constexpr int kMaxSegs = 16;
 constexpr int kMinCut = 3;
@@ -264,9 +265,12 @@ struct SegPlan {
   float* maps;           // [H][map_bound]: M (as the scan's bf16 hi and lo A fragments, the
                          // size of fp32 [K][K]) then B (fp32 [K][V]); B of map item j ends up
                          // holding the initial state of segment j + 1
+  uint8_t* recs;         // [H][rec_bound] chunk records (records mode only)
   int32_t seg_bound, map_bound, long_bound;
+  int32_t rec_bound;     // chunk slots of the call at most
   int32_t max_segs;      // segments per sequence at most (host bound)
   int32_t num_tokens;    // rows of the call (validated to fit in int32)
+  int32_t records;       // 1: the first launch writes chunk records, the second runs from them
 };
 
 constexpr int32_t kBadCuSeqlens = 1;
@@ -279,18 +283,26 @@ __device__ __forceinline__ int64_t map_index(int h, int mi, const SegPlan& pl) {
 // sequence of len tokens has fewer than len / (64 kSegMinChunks) non-final
 // segments, so a call has at most num_tokens / (64 kSegMinChunks) of them
 // (and at most num_seqs (max_segs - 1)); each cut sequence has at least one.
+// The chunk records follow the maps; a workspace that ends before them
+// (total_min bytes) runs without records.
 struct Layout {
-  int64_t seg_bound, map_bound, long_bound, max_segs;
-  size_t counts, chunk_start, seg_start, seg_seq, seg_long, map_seg, long_seq, maps, total;
+  int64_t seg_bound, map_bound, long_bound, max_segs, rec_bound;
+  size_t counts, chunk_start, seg_start, seg_seq, seg_long, map_seg, long_seq, maps, total_min, recs, total;
 };
 
 inline size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Bytes of one chunk record: -W, scale Q o e^gam, scale P, K~^T (bf16), e^{gam_last} (fp32 [K]), U (fp32 [C][V]).
+__host__ __device__ constexpr size_t rec_bytes(int K, int V) {
+  return static_cast<size_t>(C) * K * 2 * 2 + static_cast<size_t>(C) * C * 2 + static_cast<size_t>(K) * C * 2 +
+         static_cast<size_t>(K) * 4 + static_cast<size_t>(C) * V * 4;
+}
 
 inline Layout layout_for(int32_t num_seqs, int64_t num_tokens, int32_t H, int32_t K, int32_t V) {
   Layout L{};
   const int64_t N = num_seqs;
   L.max_segs = std::min<int64_t>(kMaxSegs, (kChipSlots + H - 1) / H + 1);
-  L.map_bound = L.max_segs < kMinCut ? 0 : std::min<int64_t>(num_tokens / (C * kSegMinChunks), N * (L.max_segs - 1));
+  L.map_bound = L.max_segs < 2 ? 0 : std::min<int64_t>(num_tokens / (C * kSegMinChunks), N * (L.max_segs - 1));
   L.long_bound = L.map_bound;
   L.seg_bound = N + L.map_bound;
   size_t o = 0;
@@ -302,7 +314,12 @@ inline Layout layout_for(int32_t num_seqs, int64_t num_tokens, int32_t H, int32_
   L.map_seg = o;     o += L.map_bound * 4;
   L.long_seq = o;    o += L.long_bound * 4;
   L.maps = round256(o);
-  L.total = L.maps + static_cast<size_t>(L.map_bound) * H * (static_cast<size_t>(K) * K + static_cast<size_t>(K) * V) * 4;
+  L.total_min = L.maps + static_cast<size_t>(L.map_bound) * H * (static_cast<size_t>(K) * K + static_cast<size_t>(K) * V) * 4;
+  // Records: one per chunk slot of a cut sequence (only those are written);
+  // the chunk slots of a call number at most num_tokens / C + num_seqs.
+  L.rec_bound = L.map_bound > 0 ? num_tokens / C + N : 0;
+  L.recs = round256(L.total_min);
+  L.total = L.recs + static_cast<size_t>(L.rec_bound) * H * rec_bytes(K, V);
   return L;
 }
 
@@ -336,9 +353,9 @@ __device__ __forceinline__ int chunks_of(const int32_t* cu, int i) {
   return (max(cu[i + 1] - cu[i], 0) + C - 1) / C;
 }
 
-__device__ __forceinline__ int segments_of(int nch, int target) {
+__device__ __forceinline__ int segments_of(int nch, int target, int min_cut) {
   const int ns = min((nch + kSegMinChunks - 1) / kSegMinChunks, target);
-  return ns >= kMinCut ? ns : 1;
+  return ns >= min_cut ? ns : 1;
 }
 
 // Checks cu_seqlens (starts at 0, non-decreasing, ends at num_tokens) and
@@ -354,12 +371,15 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* cu, i
   const int per = (N + kPlanThreads - 1) / kPlanThreads;
   const int b = tid * per;
   const int e = min(N, b + per);
+  // With records a second segment costs only its state steps in the second
+  // launch, so two segments already shorten the chain.
+  const int min_cut = pl.records ? 2 : kMinCut;
   int bad = 0, nl = 0, nw = 0;
   for (int i = b; i < e; ++i) {
     bad |= cu[i + 1] < cu[i];
     const int nch = chunks_of(cu, i);
-    nl += nch > (kMinCut - 1) * kSegMinChunks;  // can be cut
-    nw += nch > 0 && nch <= (kMinCut - 1) * kSegMinChunks;  // stays whole
+    nl += nch > (min_cut - 1) * kSegMinChunks;  // can be cut
+    nw += nch > 0 && nch <= (min_cut - 1) * kSegMinChunks;  // stays whole
   }
   if (tid == 0) bad |= cu[0] != 0 || cu[N] != pl.num_tokens;
   int nbad;
@@ -371,15 +391,19 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* cu, i
   // Each launch holds a slot per (item, head); the uncut sequences' state
   // passes run in the second launch beside the later segments, so they take
   // slots from the cut sequences' budget there. Every cut sequence gets at
-  // least kMinCut segments.
+  // least min_cut segments. With records the first launch also holds the
+  // last segment of every cut sequence (its records), so it has n workgroups
+  // per cut (sequence, head) and the second one n - 1.
   const int slots = (kChipSlots + H - 1) / H;
   const int budget = slots - n_whole;
-  const int target = min(pl.max_segs, 1 + max(kMinCut - 1, budget / max(n_long, 1)));
+  const int per_long = max(min_cut - 1, budget / max(n_long, 1));
+  const int target = pl.records ? min(pl.max_segs, max(min_cut, min(per_long + 1, slots / max(n_long, 1))))
+                                : min(pl.max_segs, 1 + per_long);
 
   int cc = 0, sc = 0, lc = 0;
   for (int i = b; i < e; ++i) {
     const int nch = chunks_of(cu, i);
-    const int ns = segments_of(nch, target);
+    const int ns = segments_of(nch, target, min_cut);
     cc += nch;
     sc += ns;
     lc += ns > 1;
@@ -393,7 +417,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* cu, i
   const bool ok = nbad == 0 && stot <= pl.seg_bound && mtot <= pl.map_bound && ltot <= pl.long_bound;
   for (int i = b; i < e; ++i) {
     const int nch = chunks_of(cu, i);
-    const int ns = segments_of(nch, target);
+    const int ns = segments_of(nch, target, min_cut);
     pl.chunk_start[i] = cb;
     pl.seg_start[i] = sb;
     if (ok) {
@@ -507,6 +531,37 @@ struct FusedSmem {
   // bf16 T diag(beta), [C][C] (rec_elem<C>), for the W and U products: built
   // after A/P over K o F (or gam), which A/P was the last to read.
   __device__ uint16_t* tf() { return t.f.kf; }
+};
+
+// Chunk records. When a sequence is cut into segments, the first launch
+// builds the intra part of every chunk of segments 1 .. n - 1 anyway (for the
+// segment maps); with records it also writes the chunk's state-step
+// operands to the workspace: the ChunkOps tiles byte for byte as they sit in
+// LDS, then U (fp32, lane (m, g) of wave w holding rows 16 pb + 4 g + j of
+// value columns 16 w + m, as 16 bytes at piece (4 w + pb) 64 + lane). The
+// second launch then runs those segments' state steps from the records
+// alone. Records are head-major ([H][chunk slot]), so a workgroup reads one
+// contiguous stream.
+template <int K, int V>
+struct Rec {
+  static constexpr int kOps = static_cast<int>(sizeof(ChunkOps<K, true>));  // bytes of the operand tiles
+  static constexpr int kPieces = kOps / 16;
+  static constexpr int kRounds = (kPieces + kThreads - 1) / kThreads;       // 16-byte pieces per thread
+  static constexpr int kBytes = kOps + C * V * 4;                           // one record
+  static constexpr int kBuf = kRounds * kThreads * 16;                      // LDS per record buffer
+  static_assert(kOps % 16 == 0, "whole 16-byte pieces");
+};
+
+// LDS of a state pass that runs from records: two record buffers (the DMA
+// rounds land whole, so each buffer is rounded up to them) and the output
+// epilogue's exchange.
+template <int K, int V>
+struct RecSmem {
+  uint4 ops[2][Rec<K, V>::kBuf / 16];
+  float nrm[C * 8];
+  __device__ const ChunkOps<K, true>& buf(int b) const {
+    return *reinterpret_cast<const ChunkOps<K, true>*>(&ops[b][0]);
+  }
 };
 
 // One chunk's register-held inputs, loaded a chunk ahead.
@@ -1548,6 +1603,150 @@ __device__ __forceinline__ void poison_output(const PrefillParams& p) {
     p.out[i] = 0x7FC0;  // bf16 quiet NaN
 }
 
+// One chunk's state step on the calling wave's value columns 16 w .. 16 w +
+// 15 (w < V / 16): V' = U - W S, the chunk's output (with the optional
+// gated RMSNorm epilogue) and S <- diag(e^{gam_last}) S + K~^T V', from the
+// operand tiles `ops` and U in Vp. zg holds the epilogue's gate of the
+// lane's output elements, nw its weights; nrm is the epilogue's LDS
+// exchange (all waves of the workgroup take part in its barrier, see the
+// callers). pin() runs just before the output stores.
+template <int K, int V, typename Pin>
+__device__ __forceinline__ void state_step(const PrefillParams& p, int h, int w, ChunkPos cp,
+                                           const ChunkOps<K, true>& ops, float* nrm, f32x4 (&S)[K / 16],
+                                           f32x4 (&Vp)[4], const u32x2 (&zg)[4], f32x4 nw, bool has_norm,
+                                           Pin&& pin) {
+  const int64_t HV = static_cast<int64_t>(p.H) * V;
+  const int col0 = 16 * w;
+  const int m = opaque_tid() & 15, g = (opaque_tid() & 63) >> 4;
+  // Lane (m, g) of the transposed output tile of position block pb holds
+  // channels col0 + 4 g .. + 3 of position 16 pb + m: 8 contiguous bytes.
+  const int out_lane = static_cast<int>(m * HV + h * V + col0 + 4 * g) * 2;
+
+  // V' = U - W S (rows: positions) and O^T = S^T (Q o e^gam)^T (rows:
+  // value channels), both contracting over key channels. S as a bf16
+  // fragment is the B operand of the first and the A operand of the
+  // second.
+  bf16x8 Sb[K / 32];
+#pragma unroll
+  for (int kb = 0; kb < K / 32; ++kb) Sb[kb] = pack_acc(S[2 * kb], S[2 * kb + 1]);
+  // Fragments are read one position block ahead of the MFMAs that use
+  // them (the scheduling barriers keep that order), so LDS latency hides
+  // behind the previous block's MFMAs.
+  bf16x8 wf[2][K / 32], qf[2][K / 32];
+#pragma unroll
+  for (int kb = 0; kb < K / 32; ++kb) {
+    wf[0][kb] = frag<K>(ops.wn, m, 32 * kb + 8 * g);
+    qf[0][kb] = frag<K>(ops.qg, m, 32 * kb + 8 * g);
+  }
+  bf16x8 pf[4][2];
+  f32x4 Ot[4];
+#pragma unroll
+  for (int pb = 0; pb < 4; ++pb) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (pb + 1 < 4) {
+#pragma unroll
+      for (int kb = 0; kb < K / 32; ++kb) {
+        wf[(pb + 1) & 1][kb] = frag<K>(ops.wn, 16 * (pb + 1) + m, 32 * kb + 8 * g);
+        qf[(pb + 1) & 1][kb] = frag<K>(ops.qg, 16 * (pb + 1) + m, 32 * kb + 8 * g);
+      }
+    } else {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        pf[b][0] = frag<C>(ops.pm, 16 * b + m, 8 * g);
+        if (b >= 2) pf[b][1] = frag<C>(ops.pm, 16 * b + m, 32 + 8 * g);
+      }
+    }
+    Ot[pb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < K / 32; ++kb) {
+      Vp[pb] = mfma16(wf[pb & 1][kb], Sb[kb], Vp[pb]);
+      Ot[pb] = mfma16(Sb[kb], qf[pb & 1][kb], Ot[pb]);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // V' over positions: the output product takes it as hi + lo bf16 parts
+  // (the rounding of V' would otherwise dominate the output error); the
+  // state update takes the hi part.
+  const bf16x8 Vb0 = pack_acc(Vp[0], Vp[1]);
+  const bf16x8 Vb1 = pack_acc(Vp[2], Vp[3]);
+  const bf16x8 Vl0 = pack_lo(Vp[0], Vp[1], Vb0);
+  const bf16x8 Vl1 = pack_lo(Vp[2], Vp[3], Vb1);
+  // O^T += V'^T P^T (P is lower triangular: positions 0..31 see only
+  // positions 0..31).
+#pragma unroll
+  for (int pb = 0; pb < 4; ++pb) {
+    Ot[pb] = mfma16(Vb0, pf[pb][0], Ot[pb]);
+    Ot[pb] = mfma16(Vl0, pf[pb][0], Ot[pb]);
+    if (pb >= 2) {
+      Ot[pb] = mfma16(Vb1, pf[pb][1], Ot[pb]);
+      Ot[pb] = mfma16(Vl1, pf[pb][1], Ot[pb]);
+    }
+  }
+  // Rows of the chunk as one buffer range: positions past its end fall
+  // outside and their stores are dropped, so every lane issues exactly 4
+  // stores, the last vector-memory operations of the chunk.
+  if (has_norm) {
+    // Sum of squares of each position over the wave's 16 columns (lanes
+    // m, m + 16, m + 32, m + 48 hold one position), posted per wave by
+    // lanes 0..15.
+    float ss[4];
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb)
+      ss[pb] = sum_lane_groups(Ot[pb][0] * Ot[pb][0] + Ot[pb][1] * Ot[pb][1] + Ot[pb][2] * Ot[pb][2] +
+                               Ot[pb][3] * Ot[pb][3]);
+    if (g == 0) {
+#pragma unroll
+      for (int pb = 0; pb < 4; ++pb) nrm[(16 * pb + m) * 8 + w] = ss[pb];
+    }
+    lds_barrier();
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(&nrm[(16 * pb + m) * 8]);
+      float tot = a[0] + a[1] + a[2] + a[3];
+      if constexpr (V / 16 > 4) {
+        const f32x4 b = *reinterpret_cast<const f32x4*>(&nrm[(16 * pb + m) * 8 + 4]);
+        tot += b[0] + b[1] + b[2] + b[3];
+      }
+      // Hardware reciprocal square root (about 1 ulp; the result is cast to bf16).
+      const float inv = __builtin_amdgcn_rsqf(tot * (1.0f / V) + p.norm.eps);
+      const float z[4] = {__uint_as_float(zg[pb][0] << 16), __uint_as_float(zg[pb][0] & 0xffff0000u),
+                          __uint_as_float(zg[pb][1] << 16), __uint_as_float(zg[pb][1] & 0xffff0000u)};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float sg = sigmoid_f32(z[j]);
+        const float act = p.norm.activation == 1 ? z[j] * sg : sg;
+        Ot[pb][j] = Ot[pb][j] * inv * nw[j] * act;
+      }
+    }
+  }
+  // The caller's registers for the next chunk (loads in flight) are held
+  // here, ahead of the stores, so that nothing later waits on them.
+  pin();
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.out + cp.t0 * HV, static_cast<uint32_t>(cp.n * HV * 2));
+#pragma unroll
+  for (int pb = 0; pb < 4; ++pb)
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf16x2(Ot[pb][0], Ot[pb][1]), pack_bf16x2(Ot[pb][2], Ot[pb][3])},
+                                          ro, out_lane + static_cast<int>(16 * pb * HV * 2), 0, 0);
+  // S <- diag(e^{gam_last}) S + (K o e^{gam_last - gam})^T V'.
+  bf16x8 kf[2][2];
+  kf[0][0] = frag<C>(ops.kgt, m, 8 * g);
+  kf[0][1] = frag<C>(ops.kgt, m, 32 + 8 * g);
+#pragma unroll
+  for (int cb = 0; cb < K / 16; ++cb) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (cb + 1 < K / 16) {
+      kf[(cb + 1) & 1][0] = frag<C>(ops.kgt, 16 * (cb + 1) + m, 8 * g);
+      kf[(cb + 1) & 1][1] = frag<C>(ops.kgt, 16 * (cb + 1) + m, 32 + 8 * g);
+    }
+    const f32x4 e = *reinterpret_cast<const f32x4*>(&ops.eg[16 * cb + 4 * g]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) S[cb][j] *= e[j];
+    S[cb] = mfma16(kf[cb & 1][0], Vb0, S[cb]);
+    S[cb] = mfma16(kf[cb & 1][1], Vb1, S[cb]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // The state pass of segment gs (rows sr) of head h on one workgroup, 8
 // waves; wave w < V / 16 owns value columns 16 w .. 16 w + 15 of the state,
 // kept in MFMA accumulators for the whole segment. Starts from the slot's
@@ -1619,8 +1818,6 @@ __device__ __forceinline__ void state_segment(const PrefillParams& p, const SegP
   const bool has_norm = p.norm.gate != nullptr;  // uniform
   f32x4 nw = {1.f, 1.f, 1.f, 1.f};               // the norm weights of the lane's four channels
   if (has_norm && has_cols) nw = *reinterpret_cast<const f32x4*>(p.norm.weight + col0 + 4 * g);
-  // Lane (m, g) of the transposed output tile of position block pb holds
-  // channels col0 + 4 g .. + 3 of position 16 pb + m: 8 contiguous bytes.
   const auto& ops = sm.r.ops;
   for (int cc = 0; cc < sr.nch; ++cc) {
     const ChunkPos cp = chunk_pos(sr, cc);
@@ -1645,135 +1842,13 @@ __device__ __forceinline__ void state_segment(const PrefillParams& p, const SegP
       if (has_norm) lds_barrier();        // the epilogue's exchange below
       continue;
     }
-    const int m = opaque_tid() & 15, g = (opaque_tid() & 63) >> 4;
-    const int out_lane = static_cast<int>(m * HV + h * V + col0 + 4 * g) * 2;
-
-    // V' = U - W S (rows: positions) and O^T = S^T (Q o e^gam)^T (rows:
-    // value channels), both contracting over key channels. S as a bf16
-    // fragment is the B operand of the first and the A operand of the
-    // second.
-    bf16x8 Sb[K / 32];
-#pragma unroll
-    for (int kb = 0; kb < K / 32; ++kb) Sb[kb] = pack_acc(S[2 * kb], S[2 * kb + 1]);
-    // Fragments are read one position block ahead of the MFMAs that use
-    // them (the scheduling barriers keep that order), so LDS latency hides
-    // behind the previous block's MFMAs.
-    bf16x8 wf[2][K / 32], qf[2][K / 32];
-#pragma unroll
-    for (int kb = 0; kb < K / 32; ++kb) {
-      wf[0][kb] = frag<K>(ops.wn, m, 32 * kb + 8 * g);
-      qf[0][kb] = frag<K>(ops.qg, m, 32 * kb + 8 * g);
-    }
-    bf16x8 pf[4][2];
-    f32x4 Ot[4];
-#pragma unroll
-    for (int pb = 0; pb < 4; ++pb) {
-      __builtin_amdgcn_sched_barrier(0);
-      if (pb + 1 < 4) {
-#pragma unroll
-        for (int kb = 0; kb < K / 32; ++kb) {
-          wf[(pb + 1) & 1][kb] = frag<K>(ops.wn, 16 * (pb + 1) + m, 32 * kb + 8 * g);
-          qf[(pb + 1) & 1][kb] = frag<K>(ops.qg, 16 * (pb + 1) + m, 32 * kb + 8 * g);
-        }
-      } else {
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          pf[b][0] = frag<C>(ops.pm, 16 * b + m, 8 * g);
-          if (b >= 2) pf[b][1] = frag<C>(ops.pm, 16 * b + m, 32 + 8 * g);
-        }
-      }
-      Ot[pb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < K / 32; ++kb) {
-        Vp[pb] = mfma16(wf[pb & 1][kb], Sb[kb], Vp[pb]);
-        Ot[pb] = mfma16(Sb[kb], qf[pb & 1][kb], Ot[pb]);
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // V' over positions: the output product takes it as hi + lo bf16 parts
-    // (the rounding of V' would otherwise dominate the output error); the
-    // state update takes the hi part.
-    const bf16x8 Vb0 = pack_acc(Vp[0], Vp[1]);
-    const bf16x8 Vb1 = pack_acc(Vp[2], Vp[3]);
-    const bf16x8 Vl0 = pack_lo(Vp[0], Vp[1], Vb0);
-    const bf16x8 Vl1 = pack_lo(Vp[2], Vp[3], Vb1);
-    // O^T += V'^T P^T (P is lower triangular: positions 0..31 see only
-    // positions 0..31).
-#pragma unroll
-    for (int pb = 0; pb < 4; ++pb) {
-      Ot[pb] = mfma16(Vb0, pf[pb][0], Ot[pb]);
-      Ot[pb] = mfma16(Vl0, pf[pb][0], Ot[pb]);
-      if (pb >= 2) {
-        Ot[pb] = mfma16(Vb1, pf[pb][1], Ot[pb]);
-        Ot[pb] = mfma16(Vl1, pf[pb][1], Ot[pb]);
-      }
-    }
-    // Rows of the chunk as one buffer range: positions past its end fall
-    // outside and their stores are dropped, so every lane issues exactly 4
-    // stores, the last vector-memory operations of the chunk.
-    if (has_norm) {
-      // Sum of squares of each position over the wave's 16 columns (lanes
-      // m, m + 16, m + 32, m + 48 hold one position), posted per wave by
-      // lanes 0..15.
-      float ss[4];
-#pragma unroll
-      for (int pb = 0; pb < 4; ++pb)
-        ss[pb] = sum_lane_groups(Ot[pb][0] * Ot[pb][0] + Ot[pb][1] * Ot[pb][1] + Ot[pb][2] * Ot[pb][2] +
-                                 Ot[pb][3] * Ot[pb][3]);
-      if (g == 0) {
-#pragma unroll
-        for (int pb = 0; pb < 4; ++pb) sm.nrm[(16 * pb + m) * 8 + w] = ss[pb];
-      }
-      lds_barrier();
-#pragma unroll
-      for (int pb = 0; pb < 4; ++pb) {
-        const f32x4 a = *reinterpret_cast<const f32x4*>(&sm.nrm[(16 * pb + m) * 8]);
-        float tot = a[0] + a[1] + a[2] + a[3];
-        if constexpr (V / 16 > 4) {
-          const f32x4 b = *reinterpret_cast<const f32x4*>(&sm.nrm[(16 * pb + m) * 8 + 4]);
-          tot += b[0] + b[1] + b[2] + b[3];
-        }
-        // Hardware reciprocal square root (about 1 ulp; the result is cast to bf16).
-        const float inv = __builtin_amdgcn_rsqf(tot * (1.0f / V) + p.norm.eps);
-        const float z[4] = {__uint_as_float(in.zg[pb][0] << 16), __uint_as_float(in.zg[pb][0] & 0xffff0000u),
-                            __uint_as_float(in.zg[pb][1] << 16), __uint_as_float(in.zg[pb][1] & 0xffff0000u)};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float sg = sigmoid_f32(z[j]);
-          const float act = p.norm.activation == 1 ? z[j] * sg : sg;
-          Ot[pb][j] = Ot[pb][j] * inv * nw[j] * act;
-        }
-      }
-    }
-    // The next chunk's v operands have had the products above to land; held
-    // here, ahead of the stores, so that nothing later waits on them.
-    // (Unconditional: the last chunk's pins are no-ops, but every path
-    // through the loop then carries them.)
-    pin_v_regs<K, V>(in);
-    pin_gate_regs<K, V>(in);
-    const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.out + cp.t0 * HV, static_cast<uint32_t>(cp.n * HV * 2));
-#pragma unroll
-    for (int pb = 0; pb < 4; ++pb)
-      __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf16x2(Ot[pb][0], Ot[pb][1]), pack_bf16x2(Ot[pb][2], Ot[pb][3])},
-                                            ro, out_lane + static_cast<int>(16 * pb * HV * 2), 0, 0);
-    // S <- diag(e^{gam_last}) S + (K o e^{gam_last - gam})^T V'.
-    bf16x8 kf[2][2];
-    kf[0][0] = frag<C>(ops.kgt, m, 8 * g);
-    kf[0][1] = frag<C>(ops.kgt, m, 32 + 8 * g);
-#pragma unroll
-    for (int cb = 0; cb < K / 16; ++cb) {
-      __builtin_amdgcn_sched_barrier(0);
-      if (cb + 1 < K / 16) {
-        kf[(cb + 1) & 1][0] = frag<C>(ops.kgt, 16 * (cb + 1) + m, 8 * g);
-        kf[(cb + 1) & 1][1] = frag<C>(ops.kgt, 16 * (cb + 1) + m, 32 + 8 * g);
-      }
-      const f32x4 e = *reinterpret_cast<const f32x4*>(&ops.eg[16 * cb + 4 * g]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) S[cb][j] *= e[j];
-      S[cb] = mfma16(kf[cb & 1][0], Vb0, S[cb]);
-      S[cb] = mfma16(kf[cb & 1][1], Vb1, S[cb]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
+    state_step<K, V>(p, h, w, cp, ops, sm.nrm, S, Vp, in.zg, nw, has_norm, [&] {
+      // The next chunk's v operands have had the products above to land.
+      // (Unconditional: the last chunk's pins are no-ops, but every path
+      // through the loop then carries them.)
+      pin_v_regs<K, V>(in);
+      pin_gate_regs<K, V>(in);
+    });
   }
 
   if (!has_cols) return;
@@ -1785,11 +1860,144 @@ __device__ __forceinline__ void state_segment(const PrefillParams& p, const SegP
     for (int j = 0; j < 4; ++j) fin[(16 * cb + 4 * g + j) * V + col0 + m] = S[cb][j];
 }
 
+// Address of the record of chunk cc of segment range sr, head h.
+template <int K, int V>
+__device__ __forceinline__ uint8_t* record_of(const SegPlan& pl, const SegRange& sr, int h, int cc) {
+  const int64_t slot = static_cast<int64_t>(uniform(pl.chunk_start[sr.seq])) + sr.c0 + cc;
+  return pl.recs + (static_cast<int64_t>(h) * pl.rec_bound + slot) * static_cast<int64_t>(rec_bytes(K, V));
+}
+
+// Buffer-to-LDS copy of a record's operand tiles into an LDS record buffer,
+// Rec::kRounds 16-byte pieces per thread; pieces past the tiles land as
+// zeros in the buffer's rounding.
+template <int K, int V>
+__device__ __forceinline__ void dma_record(const uint8_t* rec, const uint4* buf) {
+  const u32x4 rr = rsrc_words(rec, static_cast<uint32_t>(Rec<K, V>::kOps));
+  const int tid = opaque_tid();
+#pragma unroll
+  for (int r = 0; r < Rec<K, V>::kRounds; ++r)
+    lds_copy16(rr, lds_addr(buf + r * kThreads + (tid & ~63)), (r * kThreads + tid) * 16);
+}
+
+// U of a record (waves w < V / 16): lane (m, g) gets rows 16 pb + 4 g + j of
+// value columns 16 w + m.
+template <int K, int V>
+__device__ __forceinline__ void load_record_u(const uint8_t* rec, int w, f32x4 (&u)[4]) {
+  const __amdgpu_buffer_rsrc_t ru = make_rsrc(rec + Rec<K, V>::kOps, static_cast<uint32_t>(C * V * 4));
+  const int lane = opaque_tid() & 63;
+#pragma unroll
+  for (int pb = 0; pb < 4; ++pb)
+    u[pb] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ru, ((4 * w + pb) * 64 + lane) * 16, 0, 0));
+}
+
+// The state pass of segment sg >= 1 of a cut sequence from its chunk
+// records (records mode): the same state steps as state_segment, from the
+// scan's initial state, with the next chunk's record copied into the idle
+// LDS buffer (and its U and epilogue gate loaded) while the current one
+// computes. The final state goes to the slot (last segment).
+template <int K, int V>
+__device__ __forceinline__ void state_records(const PrefillParams& p, const SegPlan& pl, const SegRange& sr, int h,
+                                              RecSmem<K, V>& rm) {
+  const int H = p.H;
+  const bool last_seg = sr.sg == sr.nseg - 1;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = uniform(tid >> 6);
+  const int m = lane & 15;
+  const int g = lane >> 4;
+  const bool has_cols = w < V / 16;  // wave-uniform
+  const int col0 = 16 * w;
+  const int64_t HV = static_cast<int64_t>(H) * V;
+  const int64_t tfirst = sr.bos + static_cast<int64_t>(C) * sr.c0;
+  const int64_t tend = min<int64_t>(sr.eos, tfirst + static_cast<int64_t>(C) * sr.nch);
+
+  const int64_t slot = uniform(static_cast<int64_t>(p.indices[static_cast<int64_t>(sr.seq) * p.index_stride]));
+  if (slot < 0) {
+    // Null slot: zero output rows, no state traffic (and no records were written).
+    for (int64_t t = tfirst; t < tend; ++t)
+      for (int c = tid; c < V; c += kThreads) p.out[t * HV + h * V + c] = 0;
+    return;
+  }
+  const bool has_norm = p.norm.gate != nullptr;  // uniform
+  f32x4 Un[4] = {};
+  u32x2 zn[4] = {};
+  // The first chunk's record goes out first, so the state loads below hide
+  // its latency.
+  auto issue = [&](int cc) {
+    const uint8_t* rec = record_of<K, V>(pl, sr, h, cc);
+    dma_record<K, V>(rec, rm.ops[cc & 1]);
+    if (has_cols) {
+      load_record_u<K, V>(rec, w, Un);
+      if (has_norm) {
+        const ChunkPos cp = chunk_pos(sr, cc);
+        const int64_t grs = p.norm.gate_row_stride;
+        const __amdgpu_buffer_rsrc_t rz =
+            make_rsrc(p.norm.gate + cp.t0 * grs, static_cast<uint32_t>(cp.n * grs * 2));
+        const int zl = static_cast<int>(m * grs + h * V + col0 + 4 * g) * 2;
+#pragma unroll
+        for (int pb = 0; pb < 4; ++pb)
+          zn[pb] = __builtin_amdgcn_raw_buffer_load_b64(rz, zl + static_cast<int>(16 * pb * grs * 2), 0, 0);
+      }
+    }
+  };
+  issue(0);
+
+  // From B of the sequence's map item sg - 1: the scan's result.
+  const float* s_in = pl.maps + map_index(h, sr.seg0 - sr.seq + sr.sg - 1, pl) *
+                                    (static_cast<int64_t>(K) * K + static_cast<int64_t>(K) * V) +
+                      K * K;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(s_in, has_cols ? static_cast<uint32_t>(K * V * 4) : 0u);
+  f32x4 S[K / 16];
+#pragma unroll
+  for (int cb = 0; cb < K / 16; ++cb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      S[cb][j] = __builtin_bit_cast(
+          float, __builtin_amdgcn_raw_buffer_load_b32(rs, ((16 * cb + 4 * g + j) * V + col0 + m) * 4, 0, 0));
+  f32x4 nw = {1.f, 1.f, 1.f, 1.f};
+  if (has_norm && has_cols) nw = *reinterpret_cast<const f32x4*>(p.norm.weight + col0 + 4 * g);
+  pin_regs(S);
+
+  for (int cc = 0; cc < sr.nch; ++cc) {
+    const ChunkPos cp = chunk_pos(sr, cc);
+    // This chunk's record, U and gate have landed (the previous chunk's 4
+    // output stores per lane, issued after them, may still be in flight) and
+    // every wave is done with the other buffer.
+    if (cc > 0 && has_cols) chunk_barrier<4>();
+    else chunk_barrier<0>();
+    f32x4 Vp[4];
+    u32x2 zg[4];
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb) {
+      Vp[pb] = Un[pb];
+      zg[pb] = zn[pb];
+    }
+    if (cc + 1 < sr.nch) issue(cc + 1);
+    if (!has_cols) {
+      if (has_norm) lds_barrier();  // the epilogue's exchange in the state step
+      continue;
+    }
+    // (The next chunk's U and gate are first read at its top, after its
+    // barrier: nothing to hold here.)
+    state_step<K, V>(p, h, w, cp, rm.buf(cc & 1), rm.nrm, S, Vp, zg, nw, has_norm, [] {});
+  }
+  if (!has_cols || !last_seg) return;
+  float* st = p.pool + slot * p.slot_stride + static_cast<int64_t>(h) * K * V;
+#pragma unroll
+  for (int cb = 0; cb < K / 16; ++cb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) st[(16 * cb + 4 * g + j) * V + col0 + m] = S[cb][j];
+}
+
 // Second launch: one workgroup per (segment, head), every segment but
-// segment 0 of a cut sequence (run by the first launch).
-template <int K, int V, bool EXACT>
+// segment 0 of a cut sequence (run by the first launch). REC: the later
+// segments of cut sequences run from their chunk records.
+template <int K, int V, bool EXACT, bool REC>
 __global__ __launch_bounds__(kThreads, 1) void chunk_state_kernel(const PrefillParams p, const SegPlan pl) {
-  __shared__ FusedSmem<K, true, EXACT> sm;
+  __shared__ union {
+    FusedSmem<K, true, EXACT> fused;
+    RecSmem<K, V> rec;
+  } smu;
   const int H = p.H;
   if (uniform(pl.counts[0]) != 0) {
     poison_output(p);
@@ -1799,8 +2007,10 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_state_kernel(const PrefillP
   if (gs >= uniform(pl.counts[1])) return;
   const SegRange sr = segment_range(p, pl, gs);
   if (sr.nch <= 0) return;
-  if (sr.sg == 0 && uniform(pl.seg_long[gs]) >= 0) return;
-  state_segment<K, V, EXACT>(p, pl, gs, sr, h, sm);
+  const bool cut = uniform(pl.seg_long[gs]) >= 0;
+  if (sr.sg == 0 && cut) return;
+  if (REC && cut) state_records<K, V>(p, pl, sr, h, smu.rec);
+  else state_segment<K, V, EXACT>(p, pl, gs, sr, h, smu.fused);
 }
 
 // ---------------------------------------------------------------- scan --
@@ -1831,21 +2041,28 @@ __device__ __forceinline__ void store_map_fragments(const float* mt, uint4* dst)
   }
 }
 
-// One single-wave workgroup per (cut sequence, value column block of 16,
+// One workgroup of four waves per (cut sequence, value column block of 16,
 // head); the blocks of a head share an XCD (the index is head-fastest, so
 // with H a multiple of 8 they fall on one L2 and each M is fetched once).
 // Composes the segment maps in order: S_1 = B_0 (segment 0's final state),
-// S_{j+1} = M_j S_j + B_j, stored over B_j (the wave's columns) for segment
-// j + 1 of the state pass. S is held in accumulators; M_{j+1}'s fragments
-// are copied into LDS while step j computes.
-constexpr int kScanThreads = 64;
+// S_{j+1} = M_j S_j + B_j, stored over B_j (the workgroup's columns) for
+// segment j + 1 of the state pass. Wave w computes row tiles RPW w .. RPW w
+// + RPW - 1 of S_{j+1} (RPW = K / 64); S_j goes through LDS (one barrier
+// per step), and M_{j+1}'s fragments and B_{j+1} are loaded while step j
+// computes.
+constexpr int kScanWaves = 4;
+constexpr int kScanThreads = 64 * kScanWaves;
 
 template <int K, int V>
 __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(const PrefillParams p, const SegPlan pl) {
   constexpr int KB = K / 32, RT = K / 16, NCB = V / 16;
+  constexpr int RPW = RT / kScanWaves;           // row tiles per wave
   constexpr int NF = RT * KB * 64;               // fragments per part of M
-  constexpr int NSTORE = RT * 4;                 // stores per lane per step
+  constexpr int NSTORE = RPW * 4;                // stores per lane per step
+  constexpr int SST = K + 4;                     // S in LDS: [16 columns][K rows], rows padded
+  static_assert(RPW * kScanWaves == RT && (2 * NF) % kScanThreads == 0, "whole row tiles and DMA rounds");
   __shared__ uint4 mbuf[2][2 * NF];
+  __shared__ float sbuf[2][16 * SST];
   const int H = p.H;
   if (uniform(pl.counts[0]) != 0) return;
   const int h = static_cast<int>(blockIdx.x) % H, rest = static_cast<int>(blockIdx.x) / H;
@@ -1856,57 +2073,71 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(const Prefi
   if (slot < 0) return;  // no maps were made for a null slot
   const int seg0 = uniform(pl.seg_start[seq]);
   const int nmap = uniform(pl.seg_start[seq + 1]) - seg0 - 1;
+  if (nmap < 2) return;
   const int mi0 = seg0 - seq;
-  const int lane = threadIdx.x, m = lane & 15, g = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6), m = lane & 15, g = lane >> 4;
   const int col0 = 16 * cbk;
   const int64_t item = static_cast<int64_t>(K) * K + static_cast<int64_t>(K) * V;
   auto dma_map = [&](int j) {
     const u32x4 rr = rsrc_words(pl.maps + map_index(h, mi0 + j, pl) * item, static_cast<uint32_t>(K * K * 4));
-    const uint32_t base = lds_addr(mbuf[j & 1]);
 #pragma unroll
-    for (int r = 0; r < 2 * NF / 64; ++r) lds_copy16(rr, base + r * 1024, lane * 16, r * 1024);
-  };
-  // The wave's columns of B_j (and of S_0): lane (m, g) holds rows
-  // 16 cb + 4 g + jj of column col0 + m.
-  auto load_cols = [&](const float* src, f32x4 (&b)[RT]) {
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(src, static_cast<uint32_t>(K * V * 4));
-#pragma unroll
-    for (int cb = 0; cb < RT; ++cb)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        b[cb][jj] = __builtin_bit_cast(
-            float, __builtin_amdgcn_raw_buffer_load_b32(rb, ((16 * cb + 4 * g + jj) * V + col0 + m) * 4, 0, 0));
+    for (int r = 0; r < 2 * NF / kScanThreads; ++r)
+      lds_copy16(rr, lds_addr(&mbuf[j & 1][r * kScanThreads + (tid & ~63)]), (r * kScanThreads + tid) * 16);
   };
   auto b_of = [&](int j) { return pl.maps + map_index(h, mi0 + j, pl) * item + static_cast<int64_t>(K) * K; };
-  if (nmap < 2) return;
-  dma_map(1);
-  f32x4 S[RT], Bn[RT];
-  load_cols(b_of(0), S);
-  load_cols(b_of(1), Bn);
-  pin_regs(S);
-  for (int j = 1; j < nmap; ++j) {
-    // M_j's fragments and B_j have landed (only the previous step's stores,
-    // the last vector-memory operations, may be in flight).
-    if (j == 1) wait_vmem();
-    else __builtin_amdgcn_s_waitcnt(0x0F70 & ~0x000F | (NSTORE & 15) | ((NSTORE >> 4) << 14));
-    asm volatile("" ::: "memory");
-    f32x4 Bc[RT];
+  // The wave's row tiles of B_j's columns: lane (m, g) holds rows 16 rt + 4 g
+  // + jj of column col0 + m.
+  auto load_rows = [&](const float* src, f32x4 (&b)[RPW]) {
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(src, static_cast<uint32_t>(K * V * 4));
 #pragma unroll
-    for (int cb = 0; cb < RT; ++cb) Bc[cb] = Bn[cb];
+    for (int r = 0; r < RPW; ++r)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        b[r][jj] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                 rb, ((16 * (RPW * w + r) + 4 * g + jj) * V + col0 + m) * 4, 0, 0));
+  };
+  auto put_rows = [&](float* sb, const f32x4 (&b)[RPW]) {
+#pragma unroll
+    for (int r = 0; r < RPW; ++r)
+      *reinterpret_cast<f32x4*>(&sb[m * SST + 16 * (RPW * w + r) + 4 * g]) = b[r];
+  };
+  dma_map(1);
+  f32x4 S1[RPW], Bn[RPW];
+  load_rows(b_of(0), S1);
+  load_rows(b_of(1), Bn);
+  pin_regs(S1);
+  put_rows(sbuf[1], S1);
+  for (int j = 1; j < nmap; ++j) {
+    // M_j's fragments, B_j and every wave's rows of S_j have landed (only the
+    // previous step's stores, the last vector-memory operations, may be in
+    // flight), and every wave is done with step j - 1's buffers.
+    if (j == 1) __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt 0, lgkmcnt 0
+    else __builtin_amdgcn_s_waitcnt(0x0070 | (NSTORE & 15) | ((NSTORE >> 4) << 14));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    f32x4 Bc[RPW];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) Bc[r] = Bn[r];
     if (j + 1 < nmap) {
       dma_map(j + 1);
-      load_cols(b_of(j + 1), Bn);
+      load_rows(b_of(j + 1), Bn);
     }
+    // S_j as the B operand: lane (m, g) takes rows 16 cb + 4 g + jj.
+    const float* sb = sbuf[j & 1];
     bf16x8 Sh[KB], Sl[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      Sh[kb] = pack_acc(S[2 * kb], S[2 * kb + 1]);
-      Sl[kb] = pack_lo(S[2 * kb], S[2 * kb + 1], Sh[kb]);
+      const f32x4 s0 = *reinterpret_cast<const f32x4*>(&sb[m * SST + 32 * kb + 4 * g]);
+      const f32x4 s1 = *reinterpret_cast<const f32x4*>(&sb[m * SST + 32 * kb + 16 + 4 * g]);
+      Sh[kb] = pack_acc(s0, s1);
+      Sl[kb] = pack_lo(s0, s1, Sh[kb]);
     }
     const uint4* mh = mbuf[j & 1];
+    f32x4 Sn[RPW];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      f32x4 acc = Bc[rt];
+    for (int r = 0; r < RPW; ++r) {
+      const int rt = RPW * w + r;
+      f32x4 acc = Bc[r];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         const bf16x8 ah = __builtin_bit_cast(bf16x8, mh[(rt * KB + kb) * 64 + lane]);
@@ -1915,59 +2146,72 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(const Prefi
         acc = mfma16(ah, Sl[kb], acc);
         acc = mfma16(al, Sh[kb], acc);
       }
-      S[rt] = acc;
+      Sn[r] = acc;
     }
-    // The state that segment j + 1 starts from, over B_j (the wave's
+    put_rows(sbuf[(j + 1) & 1], Sn);
+    // The state that segment j + 1 starts from, over B_j (the workgroup's
     // columns; the other columns belong to the head's other workgroups).
     float* Bm = b_of(j);
 #pragma unroll
-    for (int cb = 0; cb < RT; ++cb)
+    for (int r = 0; r < RPW; ++r)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) Bm[(16 * cb + 4 * g + jj) * V + col0 + m] = S[cb][jj];
+      for (int jj = 0; jj < 4; ++jj) Bm[(16 * (RPW * w + r) + 4 * g + jj) * V + col0 + m] = Sn[r][jj];
   }
 }
 
 // ----------------------------------------------------------------- map --
 
-// First launch: one workgroup per (map item = a non-final segment of a cut
-// sequence, head), 8 waves. Segment 0 runs its state pass (state_segment);
-// segments 1 .. n - 2 their maps: the segment's chunks (all full) from X = [I | 0]
-// (the identity's columns, and zero) with U = 0 for the columns of M and the
-// chunk's U for those of B: X <- e^{gam_last} o X + (K o e^{gam_last-gam})^T
-// ([0 | U] - W X). Wave w owns M's column tile w (w < K / 16) and B's (w <
-// V / 16). No output; the rounding is the state pass's (bf16 X into W X,
-// bf16 V' into the update, fp32 accumulation).
-template <int K, int V, bool EXACT>
-__global__ __launch_bounds__(kThreads, 1) void chunk_map_kernel(const PrefillParams p, const SegPlan pl) {
-  using SM = FusedSmem<K, false, EXACT>;
-  __shared__ union {
-    FusedSmem<K, true, EXACT> state;
-    SM map;
-  } smu;
-  SM& sm = smu.map;
-  const int H = p.H;
-  if (uniform(pl.counts[0]) != 0) return;
-  const int mi = static_cast<int>(blockIdx.x) / H, h = static_cast<int>(blockIdx.x) % H;
-  if (mi >= uniform(pl.counts[2])) return;
-  const int gs = uniform(pl.map_seg[mi]);
-  const SegRange sr = segment_range(p, pl, gs);
-  if (sr.sg == 0) {  // segment 0's state pass instead of its map
-    state_segment<K, V, EXACT>(p, pl, gs, sr, h, smu.state);
-    return;
+// Writes chunk cc's record (records mode): the operand tiles from LDS, 16
+// bytes per piece (Rec::kRounds stores per thread; those past the tiles are
+// dropped by the buffer range), then U from the registers of waves w < V /
+// 16 (4 stores per lane).
+template <int K, int V>
+__device__ __forceinline__ void write_record(uint8_t* rec, const ChunkOps<K, true>& ops, const f32x4 (&U)[4], int w) {
+  using R = Rec<K, V>;
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(rec, static_cast<uint32_t>(R::kOps));
+  const int tid = opaque_tid();
+  const uint4* src = reinterpret_cast<const uint4*>(&ops);
+#pragma unroll
+  for (int r = 0; r < R::kRounds; ++r) {
+    const int piece = r * kThreads + tid;
+    const uint4 v = src[min(piece, R::kPieces - 1)];
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4{v.x, v.y, v.z, v.w}, ro, piece * 16, 0, 0);
   }
-  const int64_t slot = uniform(static_cast<int64_t>(p.indices[static_cast<int64_t>(sr.seq) * p.index_stride]));
-  if (slot < 0) return;  // a null slot carries no state
+  if (w < V / 16) {  // wave-uniform
+    const __amdgpu_buffer_rsrc_t ru = make_rsrc(rec + R::kOps, static_cast<uint32_t>(C * V * 4));
+    const int lane = tid & 63;
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, U[pb]), ru, ((4 * w + pb) * 64 + lane) * 16, 0,
+                                             0);
+  }
+}
 
+// A segment sg >= 1 of a cut sequence in the first launch: with do_map its
+// map (M, B) into map item mi; with REC the records of its chunks (then Q:
+// the intra part builds the query operands too). Every chunk of a map item's
+// segment is full; a records-only segment (the last) may end in a partial
+// chunk.
+//   X = [I | 0] (the identity's columns, and zero); per chunk, with U = 0
+//   for the columns of M and the chunk's U for those of B:
+//   X <- e^{gam_last} o X + (K o e^{gam_last-gam})^T ([0 | U] - W X).
+// Wave w owns M's column tile w (w < K / 16) and B's (w < V / 16). The
+// rounding is the state pass's (bf16 X into W X, bf16 V' into the update,
+// fp32 accumulation).
+template <int K, int V, bool Q, bool EXACT, bool REC>
+__device__ __forceinline__ void map_segment(const PrefillParams& p, const SegPlan& pl, int mi, const SegRange& sr,
+                                            int h, FusedSmem<K, Q, EXACT>& sm, bool do_map) {
+  static_assert(!REC || Q, "records carry the query operands");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = uniform(tid >> 6);
   const int m = lane & 15;
   const int g = lane >> 4;
-  const bool act[2] = {w < K / 16, w < V / 16};  // the wave's tile of M, of B (wave-uniform)
+  const bool act[2] = {do_map && w < K / 16, do_map && w < V / 16};  // the wave's tile of M, of B (wave-uniform)
 
   ChunkIn<K, V> in;
   load_chunk_regs<K, V>(p, h, chunk_pos(sr, 0), in);
-  dma_chunk_tiles<K, false>(p, h, chunk_pos(sr, 0), sm.t.f.k, nullptr);
+  dma_chunk_tiles<K, Q>(p, h, chunk_pos(sr, 0), sm.t.f.k, Q ? sm.t.f.q : nullptr);
 
   // X[0]: the wave's column tile of M (from the identity), X[1]: of B.
   f32x4 X[2][K / 16];
@@ -1982,15 +2226,24 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_map_kernel(const PrefillPar
   const auto& ops = sm.r.ops;
   for (int cc = 0; cc < sr.nch; ++cc) {
     pin_v_regs<K, V>(in);
-    chunk_barrier<0>();
+    // This chunk's inputs have landed; with records, the previous chunk's
+    // record stores (the last vector-memory operations) may be in flight.
+    if (REC && cc > 0) {
+      if (w < V / 16) chunk_barrier<Rec<K, V>::kRounds + 4>();
+      else chunk_barrier<Rec<K, V>::kRounds>();
+    } else {
+      chunk_barrier<0>();
+    }
     f32x4 U[4];
     const bool more = cc + 1 < sr.nch;
+    const ChunkPos cp = chunk_pos(sr, cc);
     const ChunkPos np = chunk_pos(sr, more ? cc + 1 : cc);
-    intra_part<K, V, false, EXACT>(p, h, C, in, more, np, sm, U);
+    intra_part<K, V, Q, EXACT>(p, h, cp.n, in, more, np, sm, U);
     if (more) {
       load_chunk_v_regs<K, V>(p, h, np, in);
-      if constexpr (EXACT) dma_chunk_tiles<K, false>(p, h, np, sm.t.f.k, nullptr);
+      if constexpr (EXACT) dma_chunk_tiles<K, Q>(p, h, np, sm.t.f.k, Q ? sm.t.f.q : nullptr);
     }
+    if constexpr (REC) write_record<K, V>(record_of<K, V>(pl, sr, h, cc), ops, U, w);
     if (!act[0] && !act[1]) continue;
     const int m = opaque_tid() & 15, g = (opaque_tid() & 63) >> 4;
     // V' = [0 | U] - W X over positions.
@@ -2044,6 +2297,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_map_kernel(const PrefillPar
       }
     }
   }
+  if (!do_map) return;  // uniform
   float* dst = pl.maps + map_index(h, mi, pl) * (static_cast<int64_t>(K) * K + static_cast<int64_t>(K) * V);
   // B as fp32 [K][V].
   if (act[1]) {
@@ -2056,7 +2310,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_map_kernel(const PrefillPar
   // waves' column tiles go through LDS (fp32 [K][K], 16-byte pieces of row
   // r XOR-swizzled by r) and come back as row fragments.
   float* mt = reinterpret_cast<float*>(&sm);
-  static_assert(sizeof(SM) >= sizeof(float) * K * K, "M fits the workgroup's LDS");
+  static_assert(sizeof(FusedSmem<K, Q, EXACT>) >= sizeof(float) * K * K, "M fits the workgroup's LDS");
   __syncthreads();  // every wave is done with the last chunk's operands
   if (act[0]) {
 #pragma unroll
@@ -2071,17 +2325,62 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_map_kernel(const PrefillPar
   store_map_fragments<K>(mt, reinterpret_cast<uint4*>(dst));
 }
 
+// First launch: one workgroup per (map item = a non-final segment of a cut
+// sequence, head), 8 waves, and with REC one more per (cut sequence, head)
+// for the sequence's last segment (records only). Segment 0 runs its state
+// pass (state_segment); segments 1 .. n - 2 their maps (map_segment), with
+// REC also their records.
+template <int K, int V, bool EXACT, bool REC>
+__global__ __launch_bounds__(kThreads, 1) void chunk_map_kernel(const PrefillParams p, const SegPlan pl) {
+  __shared__ union {
+    FusedSmem<K, true, EXACT> state;
+    FusedSmem<K, false, EXACT> map;
+  } smu;
+  const int H = p.H;
+  if (uniform(pl.counts[0]) != 0) return;
+  const int mi = static_cast<int>(blockIdx.x) / H, h = static_cast<int>(blockIdx.x) % H;
+  const int nmaps = uniform(pl.counts[2]);
+  int gs;
+  bool do_map = true;
+  if (mi < nmaps) {
+    gs = uniform(pl.map_seg[mi]);
+  } else {
+    if (!REC) return;
+    const int li = mi - nmaps;
+    if (li >= uniform(pl.counts[3])) return;
+    gs = uniform(pl.seg_start[uniform(pl.long_seq[li]) + 1]) - 1;
+    do_map = false;
+  }
+  const SegRange sr = segment_range(p, pl, gs);
+  if (sr.sg == 0) {  // segment 0's state pass instead of its map
+    state_segment<K, V, EXACT>(p, pl, gs, sr, h, smu.state);
+    return;
+  }
+  const int64_t slot = uniform(static_cast<int64_t>(p.indices[static_cast<int64_t>(sr.seq) * p.index_stride]));
+  if (slot < 0) return;  // a null slot carries no state
+  if constexpr (REC) map_segment<K, V, true, EXACT, true>(p, pl, mi, sr, h, smu.state, do_map);
+  else map_segment<K, V, false, EXACT, false>(p, pl, mi, sr, h, smu.map, true);
+}
+
 template <int K, int V, bool EXACT>
 hipError_t launch_kv(const PrefillParams& p, const Layout& L, const SegPlan& pl, hipStream_t stream) {
   const int64_t state_blocks = L.seg_bound * p.H;
-  const int64_t map_blocks = L.map_bound * p.H;
+  // With records the first launch also runs the last segment of every cut
+  // sequence (one item per cut sequence after the map items).
+  const int64_t map_blocks = (L.map_bound + (pl.records ? L.long_bound : 0)) * p.H;
   if (state_blocks > 0x7fffffff || map_blocks > 0x7fffffff) return hipErrorInvalidValue;
   if (map_blocks > 0) {
-    chunk_map_kernel<K, V, EXACT><<<dim3(static_cast<unsigned>(map_blocks)), dim3(kThreads), 0, stream>>>(p, pl);
+    if (pl.records)
+      chunk_map_kernel<K, V, EXACT, true><<<dim3(static_cast<unsigned>(map_blocks)), dim3(kThreads), 0, stream>>>(p, pl);
+    else
+      chunk_map_kernel<K, V, EXACT, false><<<dim3(static_cast<unsigned>(map_blocks)), dim3(kThreads), 0, stream>>>(p, pl);
     chunk_scan_kernel<K, V><<<dim3(static_cast<unsigned>(L.long_bound * p.H * (V / 16))), dim3(kScanThreads), 0,
                                stream>>>(p, pl);
   }
-  chunk_state_kernel<K, V, EXACT><<<dim3(static_cast<unsigned>(state_blocks)), dim3(kThreads), 0, stream>>>(p, pl);
+  if (pl.records)
+    chunk_state_kernel<K, V, EXACT, true><<<dim3(static_cast<unsigned>(state_blocks)), dim3(kThreads), 0, stream>>>(p, pl);
+  else
+    chunk_state_kernel<K, V, EXACT, false><<<dim3(static_cast<unsigned>(state_blocks)), dim3(kThreads), 0, stream>>>(p, pl);
   return hipGetLastError();
 }
 
@@ -2103,6 +2402,11 @@ size_t prefill_workspace_bytes(int32_t num_seqs, int64_t num_tokens, int32_t H, 
   return layout_for(num_seqs, num_tokens, H, K, V).total;
 }
 
+size_t prefill_workspace_min_bytes(int32_t num_seqs, int64_t num_tokens, int32_t H, int32_t K,
+                                   int32_t V) {
+  return layout_for(num_seqs, num_tokens, H, K, V).total_min;
+}
+
 void prefill_workspace_maps(int32_t num_seqs, int64_t num_tokens, int32_t H, int32_t K, int32_t V,
                             size_t* offset, size_t* item_bytes, int64_t* items) {
   const Layout L = layout_for(num_seqs, num_tokens, H, K, V);
@@ -2113,7 +2417,7 @@ void prefill_workspace_maps(int32_t num_seqs, int64_t num_tokens, int32_t H, int
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream, hipEvent_t after_plan) {
   const Layout L = layout_for(p.num_seqs, p.num_tokens, p.H, p.K, p.V);
-  if (L.seg_bound > 0x7fffffff) return hipErrorInvalidValue;
+  if (L.seg_bound > 0x7fffffff || L.rec_bound > 0x7fffffff) return hipErrorInvalidValue;
   char* ws = static_cast<char*>(p.workspace);
   SegPlan pl;
   pl.counts = reinterpret_cast<int32_t*>(ws + L.counts);
@@ -2124,6 +2428,11 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream, hipEvent_t
   pl.map_seg = reinterpret_cast<int32_t*>(ws + L.map_seg);
   pl.long_seq = reinterpret_cast<int32_t*>(ws + L.long_seq);
   pl.maps = reinterpret_cast<float*>(ws + L.maps);
+  // Records when the workspace holds them (a workspace of total_min bytes
+  // runs without) and some sequence can be cut.
+  pl.records = p.workspace_bytes >= L.total && L.rec_bound > 0 ? 1 : 0;
+  pl.recs = pl.records ? reinterpret_cast<uint8_t*>(ws + L.recs) : nullptr;
+  pl.rec_bound = static_cast<int32_t>(L.rec_bound);
   pl.seg_bound = static_cast<int32_t>(L.seg_bound);
   pl.map_bound = static_cast<int32_t>(L.map_bound);
   pl.long_bound = static_cast<int32_t>(L.long_bound);

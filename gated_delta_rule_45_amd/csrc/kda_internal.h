@@ -128,8 +128,13 @@ struct PrefillParams {
   size_t workspace_bytes;
 };
 
+// Workspace of a prefill call: the full size (plan, segment maps and chunk
+// records) and the smallest that runs (without records: long sequences then
+// run their intra part twice).
 size_t prefill_workspace_bytes(int32_t num_seqs, int64_t num_tokens, int32_t H,
                                int32_t K, int32_t V);
+size_t prefill_workspace_min_bytes(int32_t num_seqs, int64_t num_tokens, int32_t H,
+                                   int32_t K, int32_t V);
 // The segment-map area of that workspace: its byte offset, the bytes of one
 // map item (M as bf16 hi then lo MFMA fragments, K*K*4 bytes, then B as
 // fp32 [K][V]) and the number of items (H times the map bound).

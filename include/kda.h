@@ -167,10 +167,21 @@ kda_status_t kda_spec_decode(int32_t num_seqs, int32_t tokens_per_seq,
  * cu_seqlens break the contract. */
 #define KDA_PREFILL_BAD_CU_SEQLENS 1
 
-/* Bytes of device workspace kda_chunk_prefill needs for these sizes (a pure
- * host computation; returns 0 for invalid sizes). */
+/* Bytes of device workspace for kda_chunk_prefill at these sizes (a pure
+ * host computation; returns 0 for invalid sizes): the plan, the segment
+ * maps of long sequences and a record per chunk of them. With the records
+ * the second pass over a long sequence's later segments reads each chunk's
+ * WY operands (the chunked delta rule of the vLLM PR #50649 kernel,
+ * Purpose: W, U and the query operands) instead of building them again. */
 size_t kda_chunk_prefill_workspace_size(int32_t num_seqs, int64_t num_tokens,
                                         int32_t H, int32_t K, int32_t V);
+
+/* The smallest workspace kda_chunk_prefill accepts at these sizes: the plan
+ * and the segment maps, without the chunk records (long sequences then
+ * build their WY operands in both passes). Same results up to the rounding
+ * of the segment split; 0 for invalid sizes. */
+size_t kda_chunk_prefill_workspace_min_size(int32_t num_seqs, int64_t num_tokens,
+                                            int32_t H, int32_t K, int32_t V);
 
 /* Diagnostics (a pure host computation): where the segment maps of a
  * long-sequence prefill live in a workspace of these sizes. *offset is the
@@ -201,9 +212,10 @@ kda_status_t kda_chunk_prefill_workspace_maps(int32_t num_seqs,
  * zero-length sequence or a null slot touches no state (null: zero output).
  * Chunks never cross sequences; the last chunk of a sequence may be partial.
  * Row formats and norm as for kda_decode_packed; out is bf16 [num_tokens][H][V].
- * workspace: device scratch of at least kda_chunk_prefill_workspace_size()
- * bytes, 256-byte aligned, owned by the caller; its contents are not needed
- * before the call. After the call (in stream order) the int32 at workspace
+ * workspace: device scratch of kda_chunk_prefill_workspace_size() bytes
+ * (at least kda_chunk_prefill_workspace_min_size(); below the full size
+ * long sequences run without chunk records), 256-byte aligned, owned by the
+ * caller; its contents are not needed before the call. After the call (in stream order) the int32 at workspace
  * offset 0 is a status word: 0 when cu_seqlens kept to the contract
  * (cu_seqlens[0] == 0, non-decreasing, cu_seqlens[num_seqs] == num_tokens),
  * else KDA_PREFILL_BAD_CU_SEQLENS; in that case every output row of the call
@@ -232,8 +244,10 @@ kda_status_t kda_chunk_prefill(int32_t num_seqs, int64_t num_tokens,
  * kda_chunk_prefill, minus the workspace: the call uses the library's own
  * static device buffer of KDA_NOALLOC_SCRATCH_BYTES (64 MiB), one per GPU,
  * which each GPU the library runs on holds until the process ends. Sizes
- * whose kda_chunk_prefill_workspace_size() exceeds it are rejected with
- * KDA_ERR_WORKSPACE before anything is launched. The call allocates and frees
+ * whose kda_chunk_prefill_workspace_min_size() exceeds it are rejected with
+ * KDA_ERR_WORKSPACE before anything is launched; sizes whose
+ * kda_chunk_prefill_workspace_size() fits run exactly as kda_chunk_prefill
+ * with a full workspace, the others without chunk records. The call allocates and frees
  * nothing (no hipMalloc, no allocating library routine); the first call for a
  * GPU looks up the buffer's device address (hipGetSymbolAddress), so make that
  * first call outside graph capture. The kernels write every scratch word they

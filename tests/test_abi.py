@@ -182,6 +182,12 @@ def test_workspace_size_query():
     assert L.kda_chunk_prefill_workspace_size(-1, 10, 32, 128, 128) == 0
     assert L.kda_mixed_batch_workspace_size(96, 5, 4000, 32, 128, 128) == \
         L.kda_chunk_prefill_workspace_size(5, 4000, 32, 128, 128)
+    # The smallest accepted workspace leaves out the chunk records: one fp32
+    # U tile and the bf16/fp32 operand tiles per chunk slot and head.
+    lo = L.kda_chunk_prefill_workspace_min_size(1, 8192, 32, 128, 128)
+    rec = 64 * 128 * 2 * 2 + 64 * 64 * 2 + 128 * 64 * 2 + 128 * 4 + 64 * 128 * 4
+    assert 0 < lo < a and a - lo >= (8192 // 64 + 1) * 32 * rec
+    assert L.kda_chunk_prefill_workspace_min_size(1, 10, 32, 96, 128) == 0
 
 
 def test_prefill_rejects_missing_workspace_and_cu_seqlens():
@@ -192,7 +198,7 @@ def test_prefill_rejects_missing_workspace_and_cu_seqlens():
     msg = L.kda_last_error().decode()
     assert st == 1
     assert "cu_seqlens must not be NULL" in msg and "workspace" in msg
-    need = L.kda_chunk_prefill_workspace_size(2, 100, 32, 128, 128)
+    need = L.kda_chunk_prefill_workspace_min_size(2, 100, 32, 128, 128)
     st = L.kda_chunk_prefill(2, 100, FAKE, None, 32, 128, 128, FAKE, 3 * 32 * 128, FAKE, FAKE,
                              ctypes.byref(g), ctypes.byref(s), None, FAKE, FAKE, need - 1, None)
     assert st == 3 and "workspace" in L.kda_last_error().decode()

@@ -98,6 +98,54 @@ def test_prefill_many_sequences_with_a_cut_one():
     check_case(case, PREFILL_TOL_O, PREFILL_TOL_S)
 
 
+def _round256(x):
+    return (x + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("K,V,lower_bound", [(128, 128, -5.0), (128, 64, None), (64, 128, -5.0)])
+def test_prefill_records_and_min_workspace(K, V, lower_bound):
+    """Long sequences with chunk records (a full workspace: the first launch
+    keeps every chunk's state-step operands for the second) and without
+    them (the smallest accepted workspace: both launches build them), each
+    at the prefill bars. With records exactly the chunks of the cut
+    sequences' later segments get a record: at H = 8 the 3100-, 700- and
+    900-token sequences (49, 11 and 15 chunks) are cut into 9, 2 and 3
+    segments, the others stay whole."""
+    H = 8
+    lens = [3100, 64, 700, 1, 900]
+    case = W.prefill_case(f"records_k{K}_v{V}_lb{lower_bound}", H, K, V, lens, 8, lower_bound,
+                          seed=841 + K + V, std=0.1, scale=1.0 / math.sqrt(K))
+    N, T = len(lens), sum(lens)
+    full = kda.kda_chunk_prefill_workspace_size(N, T, H, K, V)
+    small = kda.kda_chunk_prefill_workspace_min_size(N, T, H, K, V)
+    assert 0 < small < full
+    ref = run_oracle(case)
+    ws = torch.full((full,), 0xA5, dtype=torch.uint8, device="cuda")
+    check_case(case, PREFILL_TOL_O, PREFILL_TOL_S, oracle=ref, workspace=ws)
+    # Chunk slots of the call (sequence by sequence) and the ones of
+    # segments 1 .. n - 1 of the cut sequences (balanced split).
+    rec = 64 * K * 2 * 2 + 64 * 64 * 2 + K * 64 * 2 + K * 4 + 64 * V * 4
+    rec_bound = T // 64 + N
+    base = _round256(small)
+    assert base + H * rec_bound * rec == full
+    segs = {0: 9, 2: 2, 4: 3}
+    expect, c0 = set(), 0
+    for i, n in enumerate(lens):
+        nch = (n + 63) // 64
+        if i in segs:
+            expect.update(range(c0 + nch // segs[i], c0 + nch))  # segment 0 is chunks [0, nch / ns)
+        c0 += nch
+    recs = ws[base:].view(H, rec_bound, rec).cpu()
+    written = (recs != 0xA5).any(dim=2)
+    got = {c for c in range(rec_bound) if bool(written[:, c].all())}
+    untouched = {c for c in range(rec_bound) if not bool(written[:, c].any())}
+    assert got == expect and untouched == set(range(rec_bound)) - expect, (sorted(got), sorted(expect))
+    ws_min = torch.full((small,), 0xA5, dtype=torch.uint8, device="cuda")
+    check_case(case, PREFILL_TOL_O, PREFILL_TOL_S, oracle=ref, workspace=ws_min)
+    log(f"[case] records k{K} v{V} lb={lower_bound}: {len(expect)} records per head written; "
+        f"both schedules at the prefill bars")
+
+
 def test_prefill_cut_sequence_is_deterministic():
     case = W.prefill_case("det_cut", 2, 128, 128, [4000, 40], 4, -5.0, seed=671)
     results = []

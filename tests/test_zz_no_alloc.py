@@ -2,8 +2,10 @@
 workspace entry point (kda_chunk_prefill) it mirrors: two calls in a row on
 the library's static scratch, the second with a smaller input, each
 bit-identical to the workspace call from the same starting state and within
-the prefill bar of the fp64 oracle. Sizes beyond the scratch are rejected
-before anything is launched."""
+the prefill bar of the fp64 oracle; a size whose chunk records do not fit
+the scratch, bit-identical to the workspace call with the smallest accepted
+workspace (no records). Sizes beyond the scratch are rejected before
+anything is launched."""
 import math
 
 import numpy as np
@@ -58,6 +60,33 @@ def test_noalloc_prefill_matches_workspace_prefill_twice():
     small = W.prefill_case("noalloc_small", 4, 128, 128, [1, 5, 63, 64, 65], 12, None, seed=802,
                            std=0.1, has_initial=[1, 0, 1, 1, 0])
     _check(small)
+
+
+def test_noalloc_prefill_without_records_matches_min_workspace_prefill():
+    # One 8192-token sequence at H = 8: the plan and maps fit the scratch,
+    # the chunk records (93 MB) do not, so the no-alloc call runs the
+    # schedule without records, as kda_chunk_prefill does with the smallest
+    # accepted workspace: bit-identical to that, and at the prefill bars.
+    case = W.prefill_case("noalloc_norec", 8, 128, 128, [8192], 4, -5.0, seed=803, std=0.1,
+                          scale=1.0 / math.sqrt(128))
+    N, T = 1, 8192
+    small = kda.kda_chunk_prefill_workspace_min_size(N, T, 8, 128, 128)
+    assert small <= kda.NOALLOC_SCRATCH_BYTES < kda.kda_chunk_prefill_workspace_size(N, T, 8, 128, 128)
+    log(f"[case] no-alloc noalloc_norec: rows={T} min workspace={small} B")
+    dc_ws = to_device(case)
+    ws = torch.empty(small, dtype=torch.uint8, device="cuda")
+    out_ws = _call(kda.kda_chunk_prefill, dc_ws, workspace=ws)
+    dc_na = to_device(case)
+    out_na = _call(kda.kda_chunk_prefill_noalloc, dc_na)
+    assert torch.equal(out_na, out_ws), "output differs from kda_chunk_prefill without records"
+    assert torch.equal(dc_na.pool, dc_ws.pool), "state pool differs from kda_chunk_prefill without records"
+    ref_out, ref_fs = run_oracle(case)
+    got = out_na.float().cpu().numpy().astype(np.float64)
+    e_o = rel_err(got, ref_out)
+    s = int(case.state_indices[0])
+    e_s = rel_err(dc_na.pool[s].cpu().numpy().astype(np.float64), ref_fs[0])
+    log(f"[case] no-alloc noalloc_norec: bit-identical to the smallest-workspace call; e_o={e_o:.3e} e_S={e_s:.3e}")
+    assert e_o <= PREFILL_TOL_O and e_s <= PREFILL_TOL_S
 
 
 def test_noalloc_prefill_rejects_sizes_beyond_the_scratch():
