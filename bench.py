@@ -297,7 +297,7 @@ def prefill_io_bytes(T, H, K, V, seqs):
     return token_io_bytes(T, H, K, V) + 2 * seqs * H * K * V * 4
 
 
-def leg_prefill(steps, warmup, lens, name, seed, with_norm=False, lower_bound=-5.0):
+def leg_prefill(steps, warmup, lens, name, seed, with_norm=False, lower_bound=-5.0, min_workspace=False):
     import torch
 
     import gated_delta_rule_45_amd as kda
@@ -313,7 +313,10 @@ def leg_prefill(steps, warmup, lens, name, seed, with_norm=False, lower_bound=-5
     idx = [torch.arange(c * n, (c + 1) * n, dtype=torch.int32, device=dev) for c in range(2)]
     cu = W.cu_from_lengths(lens).to(dev)
     out = torch.empty(T, H, V, dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(kda.kda_chunk_prefill_workspace_size(n, T, H, K, V), dtype=torch.uint8, device=dev)
+    # The full workspace runs long sequences with chunk records; the smallest
+    # accepted one without (both launches build every chunk's operands).
+    size = (kda.kda_chunk_prefill_workspace_min_size if min_workspace else kda.kda_chunk_prefill_workspace_size)
+    ws = torch.empty(size(n, T, H, K, V), dtype=torch.uint8, device=dev)
     norm = None
     if with_norm:
         nm = W.make_norm(T, H, V, seed + 20)
@@ -607,19 +610,23 @@ def main():
 
     pf_steps = max(args.steps // 32, 6)
     vl = W.random_lengths(64, 1, 256, 3001, force_ones=2)
-    # name -> (lengths, workload, seed, steps, warmup, lower bound, CPU sample lengths, full tokens);
-    # "--legs prefill" runs them all, "--legs prefill_t8192" (etc.) one of them.
+    # name -> (lengths, workload, seed, steps, warmup, lower bound, CPU sample lengths, full tokens,
+    # smallest workspace); "--legs prefill" runs them all, "--legs prefill_t8192" (etc.) one of them.
     prefill_legs = {
-        "prefill_t8192": ([8192], "prefill_t8192_h32_k128", 3000, pf_steps, 2, -5.0, [8192], 8192),
-        "prefill_varlen64": (vl, "prefill_varlen64_h32_k128", 3002, pf_steps, 2, -5.0, vl, sum(vl)),
+        "prefill_t8192": ([8192], "prefill_t8192_h32_k128", 3000, pf_steps, 2, -5.0, [8192], 8192, False),
+        "prefill_varlen64": (vl, "prefill_varlen64_h32_k128", 3002, pf_steps, 2, -5.0, vl, sum(vl), False),
         "prefill_t65536": ([65536], "prefill_t65536_h32_k128", 3004, max(pf_steps // 2, 4), 1, -5.0,
-                           [8192], 65536),
-        "prefill_t8192_lbNone": ([8192], "prefill_t8192_h32_k128_lbNone", 3000, pf_steps, 2, None, None, 0),
+                           [8192], 65536, False),
+        "prefill_t8192_lbNone": ([8192], "prefill_t8192_h32_k128_lbNone", 3000, pf_steps, 2, None, None, 0,
+                                 False),
+        # The same 8192-token call with the smallest accepted workspace (no chunk records).
+        "prefill_t8192_min_workspace": ([8192], "prefill_t8192_h32_k128_min_workspace", 3000, pf_steps, 2,
+                                        -5.0, None, 0, True),
     }
-    for key, (lens, wl, seed, st, wu, lb, lens_s, full) in prefill_legs.items():
+    for key, (lens, wl, seed, st, wu, lb, lens_s, full, minws) in prefill_legs.items():
         if "prefill" not in legs and key not in legs:
             continue
-        leg = leg_prefill(st, wu, lens, wl, seed, lower_bound=lb)
+        leg = leg_prefill(st, wu, lens, wl, seed, lower_bound=lb, min_workspace=minws)
         leg["roofline"] = prefill_roofline(leg)
         if lens_s is not None and not args.no_cpu_baseline:
             leg["cpu_baseline"] = cpu_prefill_baseline(lens_s, full, args.cpu_seconds / 5)
