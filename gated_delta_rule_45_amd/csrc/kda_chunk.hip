@@ -39,6 +39,7 @@
 // P and K^T along positions) are stored in that permuted order, so S and V'
 // never leave registers.
 #include <algorithm>
+#include <type_traits>
 
 #include "kda_device.h"
 #include "kda_internal.h"
@@ -739,18 +740,28 @@ __device__ __forceinline__ bool gate_scan(const PrefillParams& p, int n, const C
   const float a_h = x[XL::gconst + K];
   const f32x4 dtb = *reinterpret_cast<const f32x4*>(&x[XL::gconst + c4]);
   const float beta_t = (tid < n) ? sigmoid_f32(bf16_to_f32(static_cast<uint16_t>(in.rb))) : 0.f;
-  const bool has_lb = p.has_lb != 0;
+  // The thread's PP x 4 log-decays, with the gate form chosen once (the
+  // form is uniform), so the independent exponentials interleave.
+  float gv[PP][4];
+  auto gates = [&](auto lb_form) {
+#pragma unroll
+    for (int i = 0; i < PP; ++i) {
+      const float rg4[4] = {__uint_as_float(in.rgw[i][0] << 16), __uint_as_float(in.rgw[i][0] & 0xffff0000u),
+                            __uint_as_float(in.rgw[i][1] << 16), __uint_as_float(in.rgw[i][1] & 0xffff0000u)};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) gv[i][j] = gate_log_decay(rg4[j], dtb[j], a_h, decltype(lb_form)::value, p.lower_bound);
+    }
+  };
+  if (p.has_lb != 0) gates(std::true_type{});
+  else gates(std::false_type{});
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < PP; ++i) {
     // Padded positions do not decay, so row 63 holds gam_last.
     const bool live = part * PP + i < n;
-    const float rg4[4] = {__uint_as_float(in.rgw[i][0] << 16), __uint_as_float(in.rgw[i][0] & 0xffff0000u),
-                          __uint_as_float(in.rgw[i][1] << 16), __uint_as_float(in.rgw[i][1] & 0xffff0000u)};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float gv = gate_log_decay(rg4[j], dtb[j], a_h, has_lb, p.lower_bound);
-      acc[j] += live ? gv : 0.f;
+      acc[j] += live ? gv[i][j] : 0.f;
       gm[i][j] = acc[j];
     }
   }
