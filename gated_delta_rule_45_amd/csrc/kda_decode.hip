@@ -1079,11 +1079,15 @@ static hipError_t launch_kv(const DecodeParams& p, int vt, bool block_form, hipS
 // head) pairs to fill the chip; narrower tiles for small batches, so that a
 // spec-verify step of a single request still spreads over the 256 CUs.
 // Requests of several tokens with fewer than 256 pairs take the block form
-// (on 16- or 32-column tiles).
+// (on 16- or 32-column tiles), except two-token requests that store a state
+// per token: with two tokens the token loop forms and stores both states for
+// less than the block form's tables and per-token state updates.
 hipError_t launch_decode(DecodeParams p, int K, hipStream_t stream) {
   const int64_t pairs = static_cast<int64_t>(p.num_seqs) * p.H;
   const bool conv = p.conv.x != nullptr;
-  const bool block_form = !conv && p.tokens_per_seq >= kBlockMinTokens && pairs < 256;
+  const bool per_token = p.num_accepted != nullptr;
+  const bool block_form = !conv && p.tokens_per_seq >= kBlockMinTokens && pairs < 256 &&
+                          !(per_token && p.tokens_per_seq == 2);
   int vt = 128;
   if (pairs < 512) vt = 64;
   if (pairs < 256) vt = 32;
