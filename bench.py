@@ -136,12 +136,43 @@ def token_io_bytes(rows, H, K, V):
 DECODE_SOURCES = ("kda_decode.hip", "kda_device.h", "kda_internal.h")
 
 
-def decode_kernel_hash() -> str:
-    """Hash of every source the decode kernel is compiled from."""
+def source_code(text: str) -> str:
+    """The code of a C++/HIP source without its comments, trailing blanks and
+    blank lines (string and character literals kept as they are), so that a
+    counter summary stays valid across edits that change no code."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    lines = (line.rstrip() for line in "".join(out).split("\n"))
+    return "\n".join(line for line in lines if line)
+
+
+def sources_hash(names) -> str:
     h = hashlib.sha256()
-    for name in DECODE_SOURCES:
-        h.update(open(os.path.join(ROOT, "gated_delta_rule_45_amd", "csrc", name), "rb").read())
+    for name in names:
+        text = open(os.path.join(ROOT, "gated_delta_rule_45_amd", "csrc", name), encoding="utf-8").read()
+        h.update(source_code(text).encode())
     return h.hexdigest()[:16]
+
+
+def decode_kernel_hash() -> str:
+    """Hash of the code of every source the decode kernel is compiled from."""
+    return sources_hash(DECODE_SOURCES)
 
 
 def measured_traffic():
@@ -349,11 +380,8 @@ PREFILL_SOURCES = ("kda_chunk.hip", "kda_device.h", "kda_internal.h")
 
 
 def prefill_kernel_hash() -> str:
-    """Hash of every source the chunked-prefill kernels are compiled from."""
-    h = hashlib.sha256()
-    for name in PREFILL_SOURCES:
-        h.update(open(os.path.join(ROOT, "gated_delta_rule_45_amd", "csrc", name), "rb").read())
-    return h.hexdigest()[:16]
+    """Hash of the code of every source the chunked-prefill kernels are compiled from."""
+    return sources_hash(PREFILL_SOURCES)
 
 
 def prefill_counters(workload: str):

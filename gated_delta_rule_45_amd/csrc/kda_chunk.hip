@@ -535,14 +535,14 @@ struct FusedSmem {
 };
 
 // Chunk records. When a sequence is cut into segments, the first launch
-// builds the intra part of every chunk of segments 1 .. n - 1 anyway (for the
-// segment maps); with records it also writes the chunk's state-step
-// operands to the workspace: the ChunkOps tiles byte for byte as they sit in
-// LDS, then U (fp32, lane (m, g) of wave w holding rows 16 pb + 4 g + j of
-// value columns 16 w + m, as 16 bytes at piece (4 w + pb) 64 + lane). The
-// second launch then runs those segments' state steps from the records
-// alone. Records are head-major ([H][chunk slot]), so a workgroup reads one
-// contiguous stream.
+// builds the intra part of every chunk of segments 1 .. n - 2 anyway (for the
+// segment maps); with records it also builds the last segment's chunks, and
+// writes every such chunk's state-step operands to the workspace: the
+// ChunkOps tiles byte for byte as they sit in LDS, then U (fp32, lane (m, g)
+// of wave w holding rows 16 pb + 4 g + j of value columns 16 w + m, as 16
+// bytes at piece (4 w + pb) 64 + lane). The second launch then runs
+// segments 1 .. n - 1 from the records alone. Records are head-major ([H]
+// [chunk slot]), so a workgroup reads one contiguous stream.
 template <int K, int V>
 struct Rec {
   static constexpr int kOps = static_cast<int>(sizeof(ChunkOps<K, true>));  // bytes of the operand tiles
