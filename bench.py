@@ -608,7 +608,7 @@ def cpu_baseline(seconds: float):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the KDA library runs on one GPU per process (heads and sequences shard across GPUs with no exchange); --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
