@@ -163,10 +163,15 @@ def source_code(text: str) -> str:
 
 
 def sources_hash(names) -> str:
+    """Hash of the code of the named sources and of the compiler flags each
+    is built with (the same code under another schedule is another kernel)."""
+    from gated_delta_rule_45_amd import build as kb
+
     h = hashlib.sha256()
     for name in names:
         text = open(os.path.join(ROOT, "gated_delta_rule_45_amd", "csrc", name), encoding="utf-8").read()
         h.update(source_code(text).encode())
+        h.update(" ".join(kb.FLAGS + kb.SOURCE_FLAGS.get(name, [])).encode())
     return h.hexdigest()[:16]
 
 
@@ -376,7 +381,7 @@ def leg_prefill(steps, warmup, lens, name, seed, with_norm=False, lower_bound=-5
 
 
 PREFILL_COUNTERS_FILE = os.path.join(ROOT, "profiles", "chunk_prefill_kernels_counters.json")
-PREFILL_SOURCES = ("kda_chunk.hip", "kda_device.h", "kda_internal.h")
+PREFILL_SOURCES = ("kda_chunk.hip", "kda_chunk_exact.hip", "kda_device.h", "kda_internal.h")
 
 
 def prefill_kernel_hash() -> str:

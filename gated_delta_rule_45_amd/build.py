@@ -23,6 +23,17 @@ FLAGS = [
 ]
 
 
+# Per-source additions. The factored chunked-prefill kernels are
+# latency-bound chains of short phases at two waves per SIMD; the iterative
+# ILP scheduler orders them about 2 % faster (same instructions,
+# bit-identical results). The exact-path variants (kda_chunk_exact.hip) and
+# the decode and spec-verify kernels keep the default scheduler: the former
+# spill under it, the latter measured slower.
+SOURCE_FLAGS = {
+    "kda_chunk.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+}
+
+
 def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
@@ -45,7 +56,8 @@ def build(verbose: bool = False) -> str:
     os.makedirs(objdir, exist_ok=True)
     srcs = sources()
     objs = [os.path.join(objdir, os.path.basename(s)[:-4] + ".o") for s in srcs]
-    cmds = [[HIPCC, *FLAGS, "-c", "-I", INCLUDE, "-I", CSRC, s, "-o", o] for s, o in zip(srcs, objs)]
+    cmds = [[HIPCC, *FLAGS, *SOURCE_FLAGS.get(os.path.basename(s), []), "-c", "-I", INCLUDE, "-I", CSRC, s, "-o", o]
+            for s, o in zip(srcs, objs)]
     cmds = [[a for a in c if a != "-shared"] for c in cmds]
     if verbose:
         for c in cmds:

@@ -46,6 +46,11 @@
 
 namespace kda {
 
+// The launches of the exact path (kda_chunk_exact.hip): the map, scan and
+// state kernels of a prefill whose gates may be steeper than the factored
+// form allows, after the plan launch.
+hipError_t launch_prefill_exact(const PrefillParams& p, hipStream_t stream);
+
 namespace {
 
 constexpr int C = 64;              // chunk size
@@ -2395,18 +2400,49 @@ hipError_t launch_kv(const PrefillParams& p, const Layout& L, const SegPlan& pl,
   return hipGetLastError();
 }
 
-template <int K, int V>
-hipError_t launch_k(const PrefillParams& p, const Layout& L, const SegPlan& pl, hipStream_t stream) {
-  // With a lower bound lb every per-token log-decay lies in (lb, 0), so a
-  // block's factors (over its 16 rows from the gam just before it) span
-  // less than 16 |lb| and every chunk takes the factored path once
-  // 16 |lb| <= kMaxBlockDecay: the kernels without the exact path (less LDS)
-  // then suffice.
-  const bool all_factored = p.has_lb != 0 && 16.f * -p.lower_bound <= kMaxBlockDecay;
-  return all_factored ? launch_kv<K, V, false>(p, L, pl, stream) : launch_kv<K, V, true>(p, L, pl, stream);
+// With a lower bound lb every per-token log-decay lies in (lb, 0), so a
+// block's factors (over its 16 rows from the gam just before it) span less
+// than 16 |lb| and every chunk takes the factored path once
+// 16 |lb| <= kMaxBlockDecay: the kernels without the exact path (less LDS)
+// then suffice.
+bool all_factored(const PrefillParams& p) { return p.has_lb != 0 && 16.f * -p.lower_bound <= kMaxBlockDecay; }
+
+template <bool EXACT>
+hipError_t launch_kernels(const PrefillParams& p, const Layout& L, const SegPlan& pl, hipStream_t stream) {
+  if (p.K == 64 && p.V == 64) return launch_kv<64, 64, EXACT>(p, L, pl, stream);
+  if (p.K == 64 && p.V == 128) return launch_kv<64, 128, EXACT>(p, L, pl, stream);
+  if (p.K == 128 && p.V == 64) return launch_kv<128, 64, EXACT>(p, L, pl, stream);
+  return launch_kv<128, 128, EXACT>(p, L, pl, stream);
+}
+
+// The plan's pointers into the workspace.
+SegPlan plan_for(const PrefillParams& p, const Layout& L) {
+  char* ws = static_cast<char*>(p.workspace);
+  SegPlan pl;
+  pl.counts = reinterpret_cast<int32_t*>(ws + L.counts);
+  pl.chunk_start = reinterpret_cast<int32_t*>(ws + L.chunk_start);
+  pl.seg_start = reinterpret_cast<int32_t*>(ws + L.seg_start);
+  pl.seg_seq = reinterpret_cast<int32_t*>(ws + L.seg_seq);
+  pl.seg_long = reinterpret_cast<int32_t*>(ws + L.seg_long);
+  pl.map_seg = reinterpret_cast<int32_t*>(ws + L.map_seg);
+  pl.long_seq = reinterpret_cast<int32_t*>(ws + L.long_seq);
+  pl.maps = reinterpret_cast<float*>(ws + L.maps);
+  // Records when the workspace holds them (a workspace of total_min bytes
+  // runs without) and some sequence can be cut.
+  pl.records = p.workspace_bytes >= L.total && L.rec_bound > 0 ? 1 : 0;
+  pl.recs = pl.records ? reinterpret_cast<uint8_t*>(ws + L.recs) : nullptr;
+  pl.rec_bound = static_cast<int32_t>(L.rec_bound);
+  pl.seg_bound = static_cast<int32_t>(L.seg_bound);
+  pl.map_bound = static_cast<int32_t>(L.map_bound);
+  pl.long_bound = static_cast<int32_t>(L.long_bound);
+  pl.max_segs = static_cast<int32_t>(L.max_segs);
+  pl.num_tokens = static_cast<int32_t>(p.num_tokens);
+  return pl;
 }
 
 }  // namespace
+
+#ifndef KDA_CHUNK_EXACT_PART
 
 size_t prefill_workspace_bytes(int32_t num_seqs, int64_t num_tokens, int32_t H, int32_t K,
                                int32_t V) {
@@ -2429,38 +2465,23 @@ void prefill_workspace_maps(int32_t num_seqs, int64_t num_tokens, int32_t H, int
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream, hipEvent_t after_plan) {
   const Layout L = layout_for(p.num_seqs, p.num_tokens, p.H, p.K, p.V);
   if (L.seg_bound > 0x7fffffff || L.rec_bound > 0x7fffffff) return hipErrorInvalidValue;
-  char* ws = static_cast<char*>(p.workspace);
-  SegPlan pl;
-  pl.counts = reinterpret_cast<int32_t*>(ws + L.counts);
-  pl.chunk_start = reinterpret_cast<int32_t*>(ws + L.chunk_start);
-  pl.seg_start = reinterpret_cast<int32_t*>(ws + L.seg_start);
-  pl.seg_seq = reinterpret_cast<int32_t*>(ws + L.seg_seq);
-  pl.seg_long = reinterpret_cast<int32_t*>(ws + L.seg_long);
-  pl.map_seg = reinterpret_cast<int32_t*>(ws + L.map_seg);
-  pl.long_seq = reinterpret_cast<int32_t*>(ws + L.long_seq);
-  pl.maps = reinterpret_cast<float*>(ws + L.maps);
-  // Records when the workspace holds them (a workspace of total_min bytes
-  // runs without) and some sequence can be cut.
-  pl.records = p.workspace_bytes >= L.total && L.rec_bound > 0 ? 1 : 0;
-  pl.recs = pl.records ? reinterpret_cast<uint8_t*>(ws + L.recs) : nullptr;
-  pl.rec_bound = static_cast<int32_t>(L.rec_bound);
-  pl.seg_bound = static_cast<int32_t>(L.seg_bound);
-  pl.map_bound = static_cast<int32_t>(L.map_bound);
-  pl.long_bound = static_cast<int32_t>(L.long_bound);
-  pl.max_segs = static_cast<int32_t>(L.max_segs);
-  pl.num_tokens = static_cast<int32_t>(p.num_tokens);
+  const SegPlan pl = plan_for(p, L);
   plan_kernel<<<1, kPlanThreads, 0, stream>>>(p.cu_seqlens, p.num_seqs, p.H, pl);
   if (after_plan != nullptr) {
     const hipError_t e = hipEventRecord(after_plan, stream);
     if (e != hipSuccess) return e;
   }
-  hipError_t e;
-  if (p.K == 64 && p.V == 64) e = launch_k<64, 64>(p, L, pl, stream);
-  else if (p.K == 64 && p.V == 128) e = launch_k<64, 128>(p, L, pl, stream);
-  else if (p.K == 128 && p.V == 64) e = launch_k<128, 64>(p, L, pl, stream);
-  else e = launch_k<128, 128>(p, L, pl, stream);
   // The output epilogue (p.norm) is applied inside the state passes.
-  return e;
+  return all_factored(p) ? launch_kernels<false>(p, L, pl, stream) : launch_prefill_exact(p, stream);
 }
+
+#else  // KDA_CHUNK_EXACT_PART
+
+hipError_t launch_prefill_exact(const PrefillParams& p, hipStream_t stream) {
+  const Layout L = layout_for(p.num_seqs, p.num_tokens, p.H, p.K, p.V);
+  return launch_kernels<true>(p, L, plan_for(p, L), stream);
+}
+
+#endif  // KDA_CHUNK_EXACT_PART
 
 }  // namespace kda
