@@ -859,28 +859,6 @@ __device__ __forceinline__ void offdiag_block(int w, int bi, int& I, int& J) {
   else { I = 3; J = 1; }
 }
 
-// Inverse of the unit lower-triangular diagonal block blk of (I + A) by
-// forward substitution on lanes 0..15 of the calling wave (lane jc solves
-// column jc): at(s, t) = A[t][s] for s < t in, T strictly below the
-// diagonal of the block out. Each row's sum runs over the earlier rows in
-// order, so when x_{t-1} lands only one FMA of row t is left.
-__device__ __forceinline__ void diag_inverse(float* at, int blk, int lane) {
-  if (lane < 16) {
-    const int jc = lane;
-    float xs[16];
-#pragma unroll
-    for (int tt = 0; tt < 16; ++tt) {
-      float v = (tt == jc) ? 1.f : 0.f;
-#pragma unroll
-      for (int s3 = 0; s3 < tt; ++s3) v = fmaf(-at[sw32<C>(16 * blk + s3, 16 * blk + tt)], xs[s3], v);
-      xs[tt] = v;
-    }
-#pragma unroll
-    for (int tt = 0; tt < 16; ++tt)
-      if (tt > jc) at[sw32<C>(16 * blk + tt, 16 * blk + jc)] = xs[tt];
-  }
-}
-
 // 16x16x16 fp32 product on the 16x16x4 MFMA: a = X^T and b = Y in
 // accumulator form (lane (m, g) element j holds row 4 g + j of column m)
 // give X Y in accumulator form. Step kk pairs lane group g with contraction
@@ -1127,8 +1105,10 @@ __device__ __forceinline__ void intra_factored(const PrefillParams& p, FusedSmem
 // Exact path (some 16-row block decays by more than kMaxBlockDecay): gam in
 // LDS, A and P by 16x16 blocks with a reference row per block: off-diagonal
 // blocks and diagonal blocks with a small decay range on bf16 MFMA (every
-// factor <= 1 or within e^{+-80}), the other diagonal blocks pairwise in
-// fp32. Same outputs as intra_factored (with the same block split).
+// factor <= 1 or within e^{+-80}), the other diagonal blocks by 4-row
+// sub-blocks (between them on bf16 MFMA against a reference row per pass,
+// within them pairwise in fp32). Same outputs as intra_factored (with the
+// same block split), diagonal inverses included.
 template <int K, int V, bool Q, bool EXACT>
 __device__ __forceinline__ void intra_exact(const PrefillParams& p, FusedSmem<K, Q, EXACT>& sm,
                                             const float (&gm)[Roles<K>::PP][4],
@@ -1248,64 +1228,121 @@ __device__ __forceinline__ void intra_exact(const PrefillParams& p, FusedSmem<K,
           ops.pm[rec_elem<C>(row, 32 * (s2 >> 5) + perm_slot(s2 & 31))] = bf16_bits(s2 <= row ? p.scale * dP[j] : 0.f);
       }
     } else {
-      // Diagonal block pairwise: lane (t, cq) = (m, g) covers row t and a
-      // quarter of the channels; partial sums are reduced over quarters.
-      constexpr int CQ = K / 4;
-      const int t = m, cq = g, row = 16 * I + t;
-      float ares[16], pres[16];
+      // Diagonal block whose range exceeds kMaxBlockDecay, by 4-row
+      // sub-blocks. Between sub-blocks on bf16 MFMA: pass a = 1..3 takes
+      // reference row r = 16 I + 4 a, so rows t >= r carry e^{gam_t - gam_r}
+      // and columns s < r carry e^{gam_r - gam_s}, both <= 1; the other rows
+      // and columns of the pass are clamped to finite values and dropped.
+      // Lane group g keeps the rows 4 g .. 4 g + 3 of pass g. Within a
+      // sub-block pairwise in fp32: lane (sb, tt, ss) = (l / 16, l / 4 % 4,
+      // l % 4) forms entry (4 sb + tt, 4 sb + ss) over every channel.
+      f32x4 dA = {0.f, 0.f, 0.f, 0.f}, dP = {0.f, 0.f, 0.f, 0.f};
+      const int tm = 16 * I + m;
+#pragma unroll 1
+      for (int a = 1; a < 4; ++a) {
+        const int r = 16 * I + 4 * a;
+        const bool below = m >= 4 * a;  // row m of the block is at or after r
+        f32x4 pA = {0.f, 0.f, 0.f, 0.f}, pP = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s3 = 0; s3 < 16; ++s3) {
-        ares[s3] = 0.f;
-        pres[s3] = 0.f;
-      }
-      for (int i8 = 0; i8 < CQ; i8 += 8) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int ch = cq * CQ + i8 + i;
-          const float gt = gam[sw32<K>(row, ch)];
-          const float kt = bf16_to_f32(sm.t.e.k[sw16<K>(row, ch)]);
-          float qti = 0.f;
-          if constexpr (Q) qti = bf16_to_f32(sm.t.e.q[sw16<K>(row, ch)]);
-#pragma unroll
-          for (int s3 = 0; s3 < 16; ++s3) {
-            const int srow = 16 * I + s3;
-            // gam is non-increasing, so for s <= t the exponent is <= 0;
-            // the min only keeps the masked s > t entries finite.
-            const float ke = bf16_to_f32(sm.t.e.k[sw16<K>(srow, ch)]) *
-                             __expf(fminf(gt - gam[sw32<K>(srow, ch)], 0.f));
-            ares[s3] = fmaf(kt, ke, ares[s3]);
-            if constexpr (Q) pres[s3] = fmaf(qti, ke, pres[s3]);
+        for (int kb = 0; kb < K / 32; ++kb) {
+          const int c0 = 32 * kb + 8 * g;
+          const uint4 kv = *reinterpret_cast<const uint4*>(&sm.t.e.k[sw16<K>(tm, c0)]);
+          const f32x4 gt0 = *reinterpret_cast<const f32x4*>(&gam[sw32<K>(tm, c0)]);
+          const f32x4 gt1 = *reinterpret_cast<const f32x4*>(&gam[sw32<K>(tm, c0 + 4)]);
+          const f32x4 gr0 = *reinterpret_cast<const f32x4*>(&gam[sw32<K>(r, c0)]);
+          const f32x4 gr1 = *reinterpret_cast<const f32x4*>(&gam[sw32<K>(r, c0 + 4)]);
+          const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w};
+          uint32_t qw[4] = {0u, 0u, 0u, 0u};
+          if constexpr (Q) {
+            const uint4 qv = *reinterpret_cast<const uint4*>(&sm.t.e.q[sw16<K>(tm, c0)]);
+            qw[0] = qv.x; qw[1] = qv.y; qw[2] = qv.z; qw[3] = qv.w;
           }
+          float ak[8], aq[8], bk[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float d = (j < 4 ? gt0[j] : gt1[j - 4]) - (j < 4 ? gr0[j] : gr1[j - 4]);
+            const float e = __expf(-fabsf(d));  // e^{gam_t - gam_r} on rows after r, e^{gam_r - gam_s} before
+            const float kf = __uint_as_float(j & 1 ? (kw[j >> 1] & 0xffff0000u) : (kw[j >> 1] << 16));
+            const float qf = __uint_as_float(j & 1 ? (qw[j >> 1] & 0xffff0000u) : (qw[j >> 1] << 16));
+            ak[j] = below ? kf * e : kf;
+            aq[j] = below ? qf * e : qf;
+            bk[j] = below ? kf : kf * e;
+          }
+          const bf16x8 b = to_bf16x8(bk);
+          pA = mfma16(to_bf16x8(ak), b, pA);
+          if constexpr (Q) pP = mfma16(to_bf16x8(aq), b, pP);
+        }
+        if (g == a) {
+          dA = pA;
+          dP = pP;
         }
       }
+      // Lane (m, g) holds rows 16 I + 4 g + j of column s = 16 I + m: the
+      // sub-blocks before g from the passes, P's zeros after g.
+      const int s2 = 16 * I + m;
 #pragma unroll
-      for (int s3 = 0; s3 < 16; ++s3) {
-        ares[s3] += __shfl_xor(ares[s3], 16);
-        ares[s3] += __shfl_xor(ares[s3], 32);
+      for (int j = 0; j < 4; ++j) {
+        const int row = 16 * I + 4 * g + j;
+        if ((m >> 2) < g) sm.at[sw32<C>(s2, row)] = x[XL::beta + row] * dA[j];
         if constexpr (Q) {
-          pres[s3] += __shfl_xor(pres[s3], 16);
-          pres[s3] += __shfl_xor(pres[s3], 32);
+          if ((m >> 2) != g)
+            ops.pm[rec_elem<C>(row, 32 * (s2 >> 5) + perm_slot(s2 & 31))] = bf16_bits((m >> 2) < g ? p.scale * dP[j] : 0.f);
         }
       }
-      if (cq == 0) {
-        const float bt = x[XL::beta + row];
+      const int tt = (lane >> 2) & 3, ss = lane & 3, sb = lane >> 4;
+      const int rt = 16 * I + 4 * sb + tt, rsrc = 16 * I + 4 * sb + ss;
+      float aw = 0.f, pw = 0.f;
+#pragma unroll 2
+      for (int c0 = 0; c0 < K; c0 += 8) {
+        const uint4 kt = *reinterpret_cast<const uint4*>(&sm.t.e.k[sw16<K>(rt, c0)]);
+        const uint4 ks = *reinterpret_cast<const uint4*>(&sm.t.e.k[sw16<K>(rsrc, c0)]);
+        const f32x4 gt0 = *reinterpret_cast<const f32x4*>(&gam[sw32<K>(rt, c0)]);
+        const f32x4 gt1 = *reinterpret_cast<const f32x4*>(&gam[sw32<K>(rt, c0 + 4)]);
+        const f32x4 gs0 = *reinterpret_cast<const f32x4*>(&gam[sw32<K>(rsrc, c0)]);
+        const f32x4 gs1 = *reinterpret_cast<const f32x4*>(&gam[sw32<K>(rsrc, c0 + 4)]);
+        const uint32_t ktw[4] = {kt.x, kt.y, kt.z, kt.w};
+        const uint32_t ksw[4] = {ks.x, ks.y, ks.z, ks.w};
+        uint32_t qtw[4] = {0u, 0u, 0u, 0u};
+        if constexpr (Q) {
+          const uint4 qt = *reinterpret_cast<const uint4*>(&sm.t.e.q[sw16<K>(rt, c0)]);
+          qtw[0] = qt.x; qtw[1] = qt.y; qtw[2] = qt.z; qtw[3] = qt.w;
+        }
 #pragma unroll
-        for (int s3 = 0; s3 < 16; ++s3) {
-          const int col = 16 * I + s3;
-          if (s3 < t) sm.at[sw32<C>(col, row)] = bt * ares[s3];
+        for (int j = 0; j < 8; ++j) {
+          // gam is non-increasing, so for s <= t the exponent is <= 0; the
+          // min only keeps the dropped s > t entries finite.
+          const float d = fminf((j < 4 ? gt0[j] : gt1[j - 4]) - (j < 4 ? gs0[j] : gs1[j - 4]), 0.f);
+          const float ke = __uint_as_float(j & 1 ? (ksw[j >> 1] & 0xffff0000u) : (ksw[j >> 1] << 16)) * __expf(d);
+          aw = fmaf(__uint_as_float(j & 1 ? (ktw[j >> 1] & 0xffff0000u) : (ktw[j >> 1] << 16)), ke, aw);
           if constexpr (Q)
-            ops.pm[rec_elem<C>(row, 32 * (col >> 5) + perm_slot(col & 31))] = bf16_bits(s3 <= t ? p.scale * pres[s3] : 0.f);
+            pw = fmaf(__uint_as_float(j & 1 ? (qtw[j >> 1] & 0xffff0000u) : (qtw[j >> 1] << 16)), ke, pw);
         }
       }
+      if (ss < tt) sm.at[sw32<C>(rsrc, rt)] = x[XL::beta + rt] * aw;
+      if constexpr (Q)
+        ops.pm[rec_elem<C>(rt, 32 * (rsrc >> 5) + perm_slot(rsrc & 31))] = bf16_bits(ss <= tt ? p.scale * pw : 0.f);
     }
   };
   if (w < 4) {
     do_block(w, w);
     // The block's A^T entries were written by this wave's own lanes: LDS
     // operations of one wave complete in order, so no barrier is needed.
+    // N = diag(beta) A below the diagonal comes back in accumulator form
+    // and is inverted in registers as on the factored path; T_II goes
+    // strictly below the diagonal of at.
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt = 0
     __builtin_amdgcn_wave_barrier();
-    diag_inverse(sm.at, w, lane);
+    f32x4 n, nt;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int r = 4 * g + jj;
+      n[jj] = m < r ? sm.at[sw32<C>(16 * w + m, 16 * w + r)] : 0.f;    // N[r][m]
+      nt[jj] = r < m ? sm.at[sw32<C>(16 * w + r, 16 * w + m)] : 0.f;   // N[m][r]
+    }
+    const f32x4 tb = unit_lower_inverse(n, nt, m, g);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+      if (4 * g + jj > m) sm.at[sw32<C>(16 * w + 4 * g + jj, 16 * w + m)] = tb[jj];
   } else {
 #pragma unroll
     for (int bi = 0; bi < 2; ++bi) {
