@@ -1111,11 +1111,11 @@ __device__ __forceinline__ void intra_factored(const PrefillParams& p, FusedSmem
 // same block split), diagonal inverses included.
 template <int K, int V, bool Q, bool EXACT>
 __device__ __forceinline__ void intra_exact(const PrefillParams& p, FusedSmem<K, Q, EXACT>& sm,
-                                            const float (&gm)[Roles<K>::PP][4],
+                                            const float (&gm)[Roles<K>::PP][4], const float (&gl)[4],
                                             uint32_t (&wkp)[4][Roles<K>::PP / 2]) {
   using Ro = Roles<K>;
   using XL = XLayout<K>;
-  constexpr int PP = Ro::PP, NQ = Ro::NQ, KP8 = Ro::KP8;
+  constexpr int PP = Ro::PP, NQ = Ro::NQ;
   const int tid = opaque_tid(), lane = tid & 63, w = uniform(tid >> 6);
   const int m = lane & 15, g = lane >> 4;
   const int q4 = tid % NQ, part = tid / NQ;
@@ -1126,49 +1126,46 @@ __device__ __forceinline__ void intra_exact(const PrefillParams& p, FusedSmem<K,
 #pragma unroll
   for (int i = 0; i < PP; ++i)
     *reinterpret_cast<f32x4*>(&gam[sw32<K>(part * PP + i, c4)]) = f32x4{gm[i][0], gm[i][1], gm[i][2], gm[i][3]};
-  lds_barrier();
-  // Elementwise outputs: scale Q o e^gam and (K o e^{gl - gam})^T.
-  if constexpr (Q) {
-    for (int e = tid; e < C * KP8; e += kThreads) {
-      const int t = e / KP8, pc = e % KP8;
-      const int cb = (pc >> 2) * 32 + 4 * (pc & 3);  // storage piece pc holds channels cb..cb+3, cb+16..cb+19
-      float qv[8], vals[8];
-      {
-        const uint2 w0 = *reinterpret_cast<const uint2*>(&sm.t.e.q[sw16<K>(t, cb)]);
-        const uint2 w1 = *reinterpret_cast<const uint2*>(&sm.t.e.q[sw16<K>(t, cb + 16)]);
-        qv[0] = __uint_as_float(w0.x << 16); qv[1] = __uint_as_float(w0.x & 0xffff0000u);
-        qv[2] = __uint_as_float(w0.y << 16); qv[3] = __uint_as_float(w0.y & 0xffff0000u);
-        qv[4] = __uint_as_float(w1.x << 16); qv[5] = __uint_as_float(w1.x & 0xffff0000u);
-        qv[6] = __uint_as_float(w1.y << 16); qv[7] = __uint_as_float(w1.y & 0xffff0000u);
-      }
-      const f32x4 g0 = *reinterpret_cast<const f32x4*>(&gam[sw32<K>(t, cb)]);
-      const f32x4 g1 = *reinterpret_cast<const f32x4*>(&gam[sw32<K>(t, cb + 16)]);
+  // Elementwise outputs of the thread's own elements, from gam in registers
+  // (every factor <= 1): scale Q o e^gam and (K o e^{gl - gam})^T; the
+  // stores of gam above drain meanwhile.
+  {
+    const int r8 = (c4 & 31) >> 2;
+    const int qcol = 32 * (c4 >> 5) + 8 * (r8 & 3) + 4 * (r8 >> 2);  // permuted slot of channel c4
+    float kgv[4][PP];  // [channel][position]
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        vals[j] = p.scale * qv[j] * __expf(g0[j]);
-        vals[4 + j] = p.scale * qv[4 + j] * __expf(g1[j]);
+    for (int i = 0; i < PP; ++i) {
+      const int t = part * PP + i;
+      const int o = sw16<K>(t, c4);
+      const uint2 kq = *reinterpret_cast<const uint2*>(&sm.t.e.k[o]);
+      const float kf[4] = {__uint_as_float(kq.x << 16), __uint_as_float(kq.x & 0xffff0000u),
+                           __uint_as_float(kq.y << 16), __uint_as_float(kq.y & 0xffff0000u)};
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) kgv[jj][i] = kf[jj] * __expf(gl[jj] - gm[i][jj]);
+      if constexpr (Q) {
+        const uint2 qq = *reinterpret_cast<const uint2*>(&sm.t.e.q[o]);
+        const float qf[4] = {__uint_as_float(qq.x << 16), __uint_as_float(qq.x & 0xffff0000u),
+                             __uint_as_float(qq.y << 16), __uint_as_float(qq.y & 0xffff0000u)};
+        float qg[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) qg[jj] = p.scale * qf[jj] * __expf(gm[i][jj]);
+        *reinterpret_cast<u32x2*>(&ops.qg[rec_elem<K>(t, qcol)]) =
+            u32x2{pack_bf16x2(qg[0], qg[1]), pack_bf16x2(qg[2], qg[3])};
       }
-      uint4 o;
-      o.x = pack_bf16x2(vals[0], vals[1]); o.y = pack_bf16x2(vals[2], vals[3]);
-      o.z = pack_bf16x2(vals[4], vals[5]); o.w = pack_bf16x2(vals[6], vals[7]);
-      *reinterpret_cast<uint4*>(&ops.qg[rec_elem<K>(t, pc * 8)]) = o;
+    }
+    static_assert(PP == 4 || PP == 2, "positions per thread");
+    const int tp = part * PP;
+    const int slot0 = 32 * (tp >> 5) + perm_slot(tp & 31);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      uint16_t* dst = &ops.kgt[rec_elem<C>(c4 + jj, slot0)];
+      if constexpr (PP == 4)
+        *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(kgv[jj][0], kgv[jj][1]), pack_bf16x2(kgv[jj][2], kgv[jj][3])};
+      else
+        *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(kgv[jj][0], kgv[jj][1]);
     }
   }
-  for (int e = tid; e < K * (C / 8); e += kThreads) {
-    const int ch = e / (C / 8), pc = e % (C / 8);
-    const int base = (pc >> 2) * 32;
-    const float glast = gam[sw32<K>(C - 1, ch)];
-    float vals[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int t = base + perm_phys((pc & 3) * 8 + j);
-      vals[j] = bf16_to_f32(sm.t.e.k[sw16<K>(t, ch)]) * __expf(glast - gam[sw32<K>(t, ch)]);
-    }
-    uint4 o;
-    o.x = pack_bf16x2(vals[0], vals[1]); o.y = pack_bf16x2(vals[2], vals[3]);
-    o.z = pack_bf16x2(vals[4], vals[5]); o.w = pack_bf16x2(vals[6], vals[7]);
-    *reinterpret_cast<uint4*>(&ops.kgt[rec_elem<C>(ch, pc * 8)]) = o;
-  }
+  lds_barrier();  // gam visible
   // A and P by 16x16 blocks (I, J), J <= I. For block-row I the reference
   // row r = 16 I + 7 when the block decays by at most 80 on every channel:
   // then every factor fits bf16 and every product with s <= t equals
@@ -1608,7 +1605,7 @@ __device__ __forceinline__ void intra_part(const PrefillParams& p, int h, int n,
   if (has_next) load_chunk_gate_regs<K, V>(p, h, next, in);
   uint32_t wkp[4][Ro::PP / 2];
   if (fast) intra_factored<K, V, Q, EXACT>(p, sm, gm, gl, rho, wkp);  // uniform
-  else if constexpr (EXACT) intra_exact<K, V, Q, EXACT>(p, sm, gm, wkp);
+  else if constexpr (EXACT) intra_exact<K, V, Q, EXACT>(p, sm, gm, gl, wkp);
   // The tile area is free from here on (EXACT: after W, see the caller).
   if constexpr (!EXACT) {
     if (has_next) dma_chunk_tiles<K, Q>(p, h, next, sm.t.f.k, sm.t.f.q);
