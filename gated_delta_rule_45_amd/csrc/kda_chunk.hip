@@ -504,7 +504,7 @@ struct ChunkOps {
 
 // LDS of a fused workgroup. Q: the state kernel (query operands and
 // output); EXACT: chunks whose 16-row blocks decay too steeply for the
-// factored operands take the pairwise path (only launched when the gate's
+// factored operands take the exact path (only launched when the gate's
 // bound does not rule them out).
 template <int K, bool Q, bool EXACT>
 struct FusedSmem {
@@ -894,6 +894,18 @@ __device__ __forceinline__ f32x4 unit_lower_inverse(const f32x4& n, const f32x4&
   return mm16(w1t, y);
 }
 
+// P's block of rows 0..31 x columns 32..63 lies above the diagonal and is
+// never read or written by a chunk; it is zeroed once per workgroup so that
+// the chunk records, which copy the tiles byte for byte, carry no stale LDS
+// contents.
+template <int K, bool Q>
+__device__ __forceinline__ void zero_p_unread(ChunkOps<K, Q>& ops) {
+  if constexpr (Q) {
+    const int tid = threadIdx.x;
+    if (tid < 128) *reinterpret_cast<uint4*>(&ops.pm[rec_elem<C>(tid >> 2, 32 + 8 * (tid & 3))]) = uint4{0u, 0u, 0u, 0u};
+  }
+}
+
 // Zero P blocks above the diagonal that the state step reads: rows 0..15 x
 // cols 16..31 and rows 32..47 x cols 48..63.
 template <int K, bool Q>
@@ -1170,7 +1182,7 @@ __device__ __forceinline__ void intra_exact(const PrefillParams& p, FusedSmem<K,
   // row r = 16 I + 7 when the block decays by at most 80 on every channel:
   // then every factor fits bf16 and every product with s <= t equals
   // e^{gam_t - gam_s} <= 1. Otherwise reference 16 I for J < I (both
-  // factors <= 1) and pairwise fp32 exponentials on the diagonal block.
+  // factors <= 1) and 4-row sub-blocks on the diagonal block (below).
   // A goes transposed into at (strictly above the diagonal); P into ops.pm
   // (positions permuted), including the zero blocks above the diagonal that
   // the state step reads.
@@ -1860,6 +1872,7 @@ __device__ __forceinline__ void state_segment(const PrefillParams& p, const SegP
   pin_regs(S);
 
   stage_gate_consts<K>(p, h, sm.x);
+  zero_p_unread<K, true>(sm.r.ops);
   // Gated RMSNorm output epilogue (optional; vLLM PR #60683, Purpose, places
   // it after the recurrence): y = o / sqrt(mean over the head's V channels
   // of o^2 + eps) * weight * act(gate), applied to the fp32 output before
@@ -2273,6 +2286,7 @@ __device__ __forceinline__ void map_segment(const PrefillParams& p, const SegPla
       X[1][cb][j] = 0.f;
     }
   stage_gate_consts<K>(p, h, sm.x);
+  zero_p_unread<K, Q>(sm.r.ops);
   const auto& ops = sm.r.ops;
   for (int cc = 0; cc < sr.nch; ++cc) {
     pin_v_regs<K, V>(in);

@@ -136,3 +136,40 @@ def test_workspace_maps_finite_after_prefill(lower_bound):
     assert written > 0
     log(f"[case] workspace maps lb={lower_bound}: {n} items, {written} written, "
         f"max|M|={float(m.abs().max()):.3e} max|B|={float(b.abs().max()):.3e}")
+
+
+@pytest.mark.parametrize("lower_bound", [-5.0, None])
+def test_workspace_records_finite_after_prefill(lower_bound):
+    """Every chunk record a cut prefill writes with a full workspace (the
+    state step's operand tiles -W, scale Q o e^gam, scale P and
+    (K o e^{gam_last - gam})^T in bf16, then e^{gam_last} and U in fp32) is
+    finite and below 1e30. The workspace starts zeroed, so slots the call
+    does not fill stay zero; at 8192 tokens every head has records."""
+    case = W.prefill_8192(lower_bound)
+    dc = to_device(case)
+    T, H, K, V, C = 8192, 32, 128, 128, 64
+    full = kda.kda_chunk_prefill_workspace_size(1, T, H, K, V)
+    ws = torch.zeros(full, dtype=torch.uint8, device="cuda")
+    i = dc.inputs
+    kda.kda_chunk_prefill(i["mixed_qkv"], i["raw_g"], i["raw_beta"], i["A_log"], i["dt_bias"],
+                          lower_bound, dc.pool, dc.state_indices, dc.cu_seqlens, workspace=ws)
+    torch.cuda.synchronize()
+    assert kda.prefill_status(ws) == 0
+    # Records follow the rest of the workspace at the next 256-byte boundary,
+    # one per (head, chunk slot), T / C + num_seqs slots per head.
+    start = (kda.kda_chunk_prefill_workspace_min_size(1, T, H, K, V) + 255) // 256 * 256
+    tiles = (2 * C * K + C * C + K * C) * 2
+    rec = tiles + K * 4 + C * V * 4
+    slots = T // C + 1
+    assert start + H * slots * rec == full
+    area = ws[start:].view(H * slots, rec)
+    bf = area[:, :tiles].contiguous().view(torch.bfloat16).float()
+    f32 = area[:, tiles:].contiguous().view(torch.float32)
+    for name, x in (("operand tiles", bf), ("e^gam_last and U", f32)):
+        assert torch.isfinite(x).all(), f"non-finite {name} in the chunk records"
+        big = float(x.abs().max())
+        assert big < 1e30, f"garbage-sized {name} in the chunk records: {big:.3e}"
+    written = (area.view(H, slots, rec) != 0).any(dim=2).sum(dim=1)
+    assert int(written.min()) > 0, "a head without records"
+    log(f"[case] chunk records lb={lower_bound}: {int(written.sum())} of {H * slots} slots written, "
+        f"max|tiles|={float(bf.abs().max()):.3e} max|U|={float(f32.abs().max()):.3e}")
