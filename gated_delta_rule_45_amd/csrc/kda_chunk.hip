@@ -69,12 +69,6 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// Index held in permuted storage slot s (0..31) of a 32-block.
-__device__ __forceinline__ int perm_phys(int s) {
-  const int g = s >> 3, j = s & 7;
-  return j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4);
-}
-
 // Storage slot of index p (0..31) in a permuted 32-block.
 __device__ __forceinline__ int perm_slot(int p) {
   const int hi = p >> 4, r = p & 15;
@@ -207,10 +201,6 @@ __device__ __forceinline__ void lds_copy16(u32x4 rsrc, uint32_t lds_wave, int vo
 __device__ __forceinline__ uint32_t lds_addr(const void* ptr) {
   return static_cast<uint32_t>(uniform(static_cast<int32_t>(reinterpret_cast<uintptr_t>(ptr))));
 }
-
-// Waits until this wave's outstanding vector-memory operations (including
-// LDS DMA) have completed: vmcnt = 0, other counters unconstrained.
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Top of a chunk: this wave's vector-memory operations have completed except
 // the last `Pending` (the previous chunk's output stores, issued after the
@@ -364,6 +354,7 @@ __device__ __forceinline__ int segments_of(int nch, int target, int min_cut) {
   return ns >= min_cut ? ns : 1;
 }
 
+#ifndef KDA_CHUNK_EXACT_PART
 // Checks cu_seqlens (starts at 0, non-decreasing, ends at num_tokens) and
 // plans chunks and segments of every sequence. The segment target is the
 // number of segments each cut sequence needs for the cut sequences' n - 1
@@ -449,6 +440,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* cu, i
     pl.counts[3] = ok ? ltot : 0;
   }
 }
+#endif  // KDA_CHUNK_EXACT_PART
 
 // ------------------------------------------------------- the intra part --
 
@@ -738,7 +730,7 @@ __device__ __forceinline__ bool gate_scan(const PrefillParams& p, int n, const C
   using XL = XLayout<K>;
   constexpr int PP = Ro::PP, NQ = Ro::NQ, NPART = Ro::NPART;
   constexpr int PB = NPART / 4;  // parts per 16-row block
-  const int tid = opaque_tid(), lane = tid & 63, w = uniform(tid >> 6);
+  const int tid = opaque_tid(), w = uniform(tid >> 6);
   const int q4 = tid % NQ, part = tid / NQ;
   const int c4 = 4 * q4;
   float* x = sm.x;
@@ -2453,7 +2445,9 @@ hipError_t launch_kv(const PrefillParams& p, const Layout& L, const SegPlan& pl,
 // than 16 |lb| and every chunk takes the factored path once
 // 16 |lb| <= kMaxBlockDecay: the kernels without the exact path (less LDS)
 // then suffice.
+#ifndef KDA_CHUNK_EXACT_PART
 bool all_factored(const PrefillParams& p) { return p.has_lb != 0 && 16.f * -p.lower_bound <= kMaxBlockDecay; }
+#endif
 
 template <bool EXACT>
 hipError_t launch_kernels(const PrefillParams& p, const Layout& L, const SegPlan& pl, hipStream_t stream) {
