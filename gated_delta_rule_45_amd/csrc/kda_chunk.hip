@@ -2120,97 +2120,108 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(const Prefi
   __shared__ float sbuf[2][16 * SST];
   const int H = p.H;
   if (uniform(pl.counts[0]) != 0) return;
-  const int h = static_cast<int>(blockIdx.x) % H, rest = static_cast<int>(blockIdx.x) / H;
-  const int cbk = rest % NCB, li = rest / NCB;
-  if (li >= uniform(pl.counts[3])) return;
-  const int seq = uniform(pl.long_seq[li]);
-  const int64_t slot = uniform(static_cast<int64_t>(p.indices[static_cast<int64_t>(seq) * p.index_stride]));
-  if (slot < 0) return;  // no maps were made for a null slot
-  const int seg0 = uniform(pl.seg_start[seq]);
-  const int nmap = uniform(pl.seg_start[seq + 1]) - seg0 - 1;
-  if (nmap < 2) return;
-  const int mi0 = seg0 - seq;
-  const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6), m = lane & 15, g = lane >> 4;
-  const int col0 = 16 * cbk;
-  const int64_t item = static_cast<int64_t>(K) * K + static_cast<int64_t>(K) * V;
-  auto dma_map = [&](int j) {
-    const u32x4 rr = rsrc_words(pl.maps + map_index(h, mi0 + j, pl) * item, static_cast<uint32_t>(K * K * 4));
+  auto scan_item = [&](int bi) {
+    const int h = bi % H, rest = bi / H;
+    const int cbk = rest % NCB, li = rest / NCB;
+    if (li >= uniform(pl.counts[3])) return;
+    const int seq = uniform(pl.long_seq[li]);
+    const int64_t slot = uniform(static_cast<int64_t>(p.indices[static_cast<int64_t>(seq) * p.index_stride]));
+    if (slot < 0) return;  // no maps were made for a null slot
+    const int seg0 = uniform(pl.seg_start[seq]);
+    const int nmap = uniform(pl.seg_start[seq + 1]) - seg0 - 1;
+    if (nmap < 2) return;
+    const int mi0 = seg0 - seq;
+    const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6), m = lane & 15, g = lane >> 4;
+    const int col0 = 16 * cbk;
+    const int64_t item = static_cast<int64_t>(K) * K + static_cast<int64_t>(K) * V;
+    auto dma_map = [&](int j) {
+      const u32x4 rr = rsrc_words(pl.maps + map_index(h, mi0 + j, pl) * item, static_cast<uint32_t>(K * K * 4));
 #pragma unroll
-    for (int r = 0; r < 2 * NF / kScanThreads; ++r)
-      lds_copy16(rr, lds_addr(&mbuf[j & 1][r * kScanThreads + (tid & ~63)]), (r * kScanThreads + tid) * 16);
-  };
-  auto b_of = [&](int j) { return pl.maps + map_index(h, mi0 + j, pl) * item + static_cast<int64_t>(K) * K; };
-  // The wave's row tiles of B_j's columns: lane (m, g) holds rows 16 rt + 4 g
-  // + jj of column col0 + m.
-  auto load_rows = [&](const float* src, f32x4 (&b)[RPW]) {
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(src, static_cast<uint32_t>(K * V * 4));
+      for (int r = 0; r < 2 * NF / kScanThreads; ++r)
+        lds_copy16(rr, lds_addr(&mbuf[j & 1][r * kScanThreads + (tid & ~63)]), (r * kScanThreads + tid) * 16);
+    };
+    auto b_of = [&](int j) { return pl.maps + map_index(h, mi0 + j, pl) * item + static_cast<int64_t>(K) * K; };
+    // The wave's row tiles of B_j's columns: lane (m, g) holds rows 16 rt + 4 g
+    // + jj of column col0 + m.
+    auto load_rows = [&](const float* src, f32x4 (&b)[RPW]) {
+      const __amdgpu_buffer_rsrc_t rb = make_rsrc(src, static_cast<uint32_t>(K * V * 4));
 #pragma unroll
-    for (int r = 0; r < RPW; ++r)
+      for (int r = 0; r < RPW; ++r)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        b[r][jj] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                 rb, ((16 * (RPW * w + r) + 4 * g + jj) * V + col0 + m) * 4, 0, 0));
-  };
-  auto put_rows = [&](float* sb, const f32x4 (&b)[RPW]) {
+        for (int jj = 0; jj < 4; ++jj)
+          b[r][jj] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                   rb, ((16 * (RPW * w + r) + 4 * g + jj) * V + col0 + m) * 4, 0, 0));
+    };
+    auto put_rows = [&](float* sb, const f32x4 (&b)[RPW]) {
 #pragma unroll
-    for (int r = 0; r < RPW; ++r)
-      *reinterpret_cast<f32x4*>(&sb[m * SST + 16 * (RPW * w + r) + 4 * g]) = b[r];
-  };
-  dma_map(1);
-  f32x4 S1[RPW], Bn[RPW];
-  load_rows(b_of(0), S1);
-  load_rows(b_of(1), Bn);
-  pin_regs(S1);
-  put_rows(sbuf[1], S1);
-  for (int j = 1; j < nmap; ++j) {
-    // M_j's fragments, B_j and every wave's rows of S_j have landed (only the
-    // previous step's stores, the last vector-memory operations, may be in
-    // flight), and every wave is done with step j - 1's buffers.
-    if (j == 1) __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt 0, lgkmcnt 0
-    else __builtin_amdgcn_s_waitcnt(0x0070 | (NSTORE & 15) | ((NSTORE >> 4) << 14));
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    f32x4 Bc[RPW];
+      for (int r = 0; r < RPW; ++r)
+        *reinterpret_cast<f32x4*>(&sb[m * SST + 16 * (RPW * w + r) + 4 * g]) = b[r];
+    };
+    dma_map(1);
+    f32x4 S1[RPW], Bn[RPW];
+    load_rows(b_of(0), S1);
+    load_rows(b_of(1), Bn);
+    pin_regs(S1);
+    put_rows(sbuf[1], S1);
+    for (int j = 1; j < nmap; ++j) {
+      // M_j's fragments, B_j and every wave's rows of S_j have landed (only the
+      // previous step's stores, the last vector-memory operations, may be in
+      // flight), and every wave is done with step j - 1's buffers.
+      if (j == 1) __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt 0, lgkmcnt 0
+      else __builtin_amdgcn_s_waitcnt(0x0070 | (NSTORE & 15) | ((NSTORE >> 4) << 14));
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      f32x4 Bc[RPW];
 #pragma unroll
-    for (int r = 0; r < RPW; ++r) Bc[r] = Bn[r];
-    if (j + 1 < nmap) {
-      dma_map(j + 1);
-      load_rows(b_of(j + 1), Bn);
-    }
-    // S_j as the B operand: lane (m, g) takes rows 16 cb + 4 g + jj.
-    const float* sb = sbuf[j & 1];
-    bf16x8 Sh[KB], Sl[KB];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      const f32x4 s0 = *reinterpret_cast<const f32x4*>(&sb[m * SST + 32 * kb + 4 * g]);
-      const f32x4 s1 = *reinterpret_cast<const f32x4*>(&sb[m * SST + 32 * kb + 16 + 4 * g]);
-      Sh[kb] = pack_acc(s0, s1);
-      Sl[kb] = pack_lo(s0, s1, Sh[kb]);
-    }
-    const uint4* mh = mbuf[j & 1];
-    f32x4 Sn[RPW];
-#pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-      const int rt = RPW * w + r;
-      f32x4 acc = Bc[r];
+      for (int r = 0; r < RPW; ++r) Bc[r] = Bn[r];
+      if (j + 1 < nmap) {
+        dma_map(j + 1);
+        load_rows(b_of(j + 1), Bn);
+      }
+      // S_j as the B operand: lane (m, g) takes rows 16 cb + 4 g + jj.
+      const float* sb = sbuf[j & 1];
+      bf16x8 Sh[KB], Sl[KB];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        const bf16x8 ah = __builtin_bit_cast(bf16x8, mh[(rt * KB + kb) * 64 + lane]);
-        const bf16x8 al = __builtin_bit_cast(bf16x8, mh[NF + (rt * KB + kb) * 64 + lane]);
-        acc = mfma16(ah, Sh[kb], acc);
-        acc = mfma16(ah, Sl[kb], acc);
-        acc = mfma16(al, Sh[kb], acc);
+        const f32x4 s0 = *reinterpret_cast<const f32x4*>(&sb[m * SST + 32 * kb + 4 * g]);
+        const f32x4 s1 = *reinterpret_cast<const f32x4*>(&sb[m * SST + 32 * kb + 16 + 4 * g]);
+        Sh[kb] = pack_acc(s0, s1);
+        Sl[kb] = pack_lo(s0, s1, Sh[kb]);
       }
-      Sn[r] = acc;
+      const uint4* mh = mbuf[j & 1];
+      f32x4 Sn[RPW];
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        const int rt = RPW * w + r;
+        f32x4 acc = Bc[r];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const bf16x8 ah = __builtin_bit_cast(bf16x8, mh[(rt * KB + kb) * 64 + lane]);
+          const bf16x8 al = __builtin_bit_cast(bf16x8, mh[NF + (rt * KB + kb) * 64 + lane]);
+          acc = mfma16(ah, Sh[kb], acc);
+          acc = mfma16(ah, Sl[kb], acc);
+          acc = mfma16(al, Sh[kb], acc);
+        }
+        Sn[r] = acc;
+      }
+      put_rows(sbuf[(j + 1) & 1], Sn);
+      // The state that segment j + 1 starts from, over B_j (the workgroup's
+      // columns; the other columns belong to the head's other workgroups).
+      float* Bm = b_of(j);
+#pragma unroll
+      for (int r = 0; r < RPW; ++r)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) Bm[(16 * (RPW * w + r) + 4 * g + jj) * V + col0 + m] = Sn[r][jj];
     }
-    put_rows(sbuf[(j + 1) & 1], Sn);
-    // The state that segment j + 1 starts from, over B_j (the workgroup's
-    // columns; the other columns belong to the head's other workgroups).
-    float* Bm = b_of(j);
-#pragma unroll
-    for (int r = 0; r < RPW; ++r)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) Bm[(16 * (RPW * w + r) + 4 * g + jj) * V + col0 + m] = Sn[r][jj];
+  };
+  // One item per (cut sequence, 16 value columns, head). The grid holds at
+  // most one workgroup per CU (idle ones would each cost a dispatch round),
+  // so a workgroup steps through the items; a stride that is a multiple of
+  // 8 keeps every item of a head on one XCD.
+  const int items = uniform(pl.counts[3]) * H * NCB;
+  for (int bi = blockIdx.x; bi < items; bi += gridDim.x) {
+    if (bi != static_cast<int>(blockIdx.x)) __syncthreads();  // the previous item is done with the LDS
+    scan_item(bi);
   }
 }
 
@@ -2424,14 +2435,17 @@ hipError_t launch_kv(const PrefillParams& p, const Layout& L, const SegPlan& pl,
   // With records the first launch also runs the last segment of every cut
   // sequence (one item per cut sequence after the map items).
   const int64_t map_blocks = (L.map_bound + (pl.records ? L.long_bound : 0)) * p.H;
-  if (state_blocks > 0x7fffffff || map_blocks > 0x7fffffff) return hipErrorInvalidValue;
+  const int64_t scan_blocks = L.long_bound * p.H * (V / 16);
+  if (state_blocks > 0x7fffffff || map_blocks > 0x7fffffff || scan_blocks > 0x7fffffff) return hipErrorInvalidValue;
   if (map_blocks > 0) {
+    // The scan kernel steps through its items (one workgroup per CU at
+    // most): only the plan knows how many there are.
+    const unsigned scan_grid = static_cast<unsigned>(std::min<int64_t>(scan_blocks, kChipSlots));
     if (pl.records)
       chunk_map_kernel<K, V, EXACT, true><<<dim3(static_cast<unsigned>(map_blocks)), dim3(kThreads), 0, stream>>>(p, pl);
     else
       chunk_map_kernel<K, V, EXACT, false><<<dim3(static_cast<unsigned>(map_blocks)), dim3(kThreads), 0, stream>>>(p, pl);
-    chunk_scan_kernel<K, V><<<dim3(static_cast<unsigned>(L.long_bound * p.H * (V / 16))), dim3(kScanThreads), 0,
-                               stream>>>(p, pl);
+    chunk_scan_kernel<K, V><<<dim3(scan_grid), dim3(kScanThreads), 0, stream>>>(p, pl);
   }
   if (pl.records)
     chunk_state_kernel<K, V, EXACT, true><<<dim3(static_cast<unsigned>(state_blocks)), dim3(kThreads), 0, stream>>>(p, pl);

@@ -247,6 +247,44 @@ def test_prefill_65536_sampled_heads():
     assert e_o <= PREFILL_TOL_O and e_s <= PREFILL_TOL_S
 
 
+@pytest.mark.parametrize("records", [True, False])
+def test_prefill_two_cut_sequences_h32_sampled_heads(records):
+    """Two sequences cut into at least three segments each at H = 32 and
+    K = V = 128: the scan has 2 x 32 x 8 = 512 items on a grid of at most one
+    workgroup per CU, so each workgroup takes two (the second sequence's on
+    its second pass). With and without chunk records; the oracle checks a
+    sample of heads, outputs and both final states."""
+    lens = [2000, 2500, 300]
+    case = W.prefill_case(f"two_cut_h32_rec{records}", 32, 128, 128, lens, 8, -5.0, seed=691, std=0.1)
+    dc = to_device(case)
+    T, H, K, V, N = sum(lens), 32, 128, 128, len(lens)
+    size = (kda.kda_chunk_prefill_workspace_size if records else kda.kda_chunk_prefill_workspace_min_size)(
+        N, T, H, K, V)
+    ws = torch.zeros(size, dtype=torch.uint8, device="cuda")
+    i = dc.inputs
+    out, _ = kda.kda_chunk_prefill(i["mixed_qkv"], i["raw_g"], i["raw_beta"], i["A_log"], i["dt_bias"],
+                                   case.lower_bound, dc.pool, dc.state_indices, dc.cu_seqlens,
+                                   scale=case.scale, workspace=ws)
+    torch.cuda.synchronize()
+    plan = ws[:16 + 2 * (N + 1) * 4].view(torch.int32).cpu().tolist()
+    assert plan[0] == 0 and plan[3] == 2, f"expected two cut sequences, plan counts {plan[:4]}"
+    seg_start = plan[4 + N + 1:4 + 2 * (N + 1)]
+    nseg = [seg_start[k + 1] - seg_start[k] for k in range(N)]
+    assert nseg[0] >= 3 and nseg[1] >= 3 and nseg[2] == 1, nseg
+    heads = [0, 13, 31]
+    inp, pool = _head_slice(case, heads)
+    ref_out, ref_fs, _ = O.prefill(inp, pool, case.state_indices, case.cu_seqlens.tolist(), len(heads),
+                                   K, V, lower_bound=case.lower_bound, scale=case.scale, return_pool=False)
+    got = out[:, heads].float().cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got))
+    e_o = rel_err(got, ref_out)
+    e_s = max(rel_err(dc.pool[int(case.state_indices[k]), heads].cpu().numpy().astype(np.float64), ref_fs[k])
+              for k in range(N))
+    log(f"[case] two cut sequences H=32 records={records} segments {nseg} heads {heads}: "
+        f"e_o={e_o:.3e} e_S={e_s:.3e}")
+    assert e_o <= PREFILL_TOL_O and e_s <= PREFILL_TOL_S
+
+
 @pytest.mark.parametrize("T", [1, 3, 8])
 def test_cross_path_decodes_prefill_spec_verify(T):
     """T single-token decodes = one prefill of T = one spec-verify call of T
