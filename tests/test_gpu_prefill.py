@@ -247,6 +247,27 @@ def test_prefill_65536_sampled_heads():
     assert e_o <= PREFILL_TOL_O and e_s <= PREFILL_TOL_S
 
 
+@pytest.mark.parametrize("spread", ["uniform", "heavy"])
+def test_prefill_exact_path_extreme_decays(spread):
+    """Gates far past the factored limit, without a lower bound: e^{A_log} =
+    16 on every head and raw_g around 3 ("uniform": about 49 per token, so
+    every 16-row block and most 4-row sub-blocks decay by more than 80), or
+    raw_g with a heavy spread ("heavy": a mix of tiny and huge per-token
+    decays inside one block). Ragged lengths, one long enough to be cut."""
+    lens = [1, 37, 64, 130, 300, 1500]
+    case = W.prefill_case(f"extreme_{spread}", 4, 128, 128, lens, 8, None, seed=701, std=0.1,
+                          scale=1.0 / math.sqrt(128))
+    g = torch.Generator().manual_seed(702)
+    rows = case.inputs["raw_g"].shape[0]
+    if spread == "uniform":
+        raw = 3.0 + 0.3 * torch.randn(rows, 4 * 128, generator=g)
+    else:
+        raw = 4.0 * torch.randn(rows, 4 * 128, generator=g)
+    case.inputs["raw_g"] = raw.to(torch.bfloat16)
+    case.inputs["A_log"] = torch.full((4,), math.log(16.0), dtype=torch.float32)
+    check_case(case, PREFILL_TOL_O, PREFILL_TOL_S)
+
+
 @pytest.mark.parametrize("records", [True, False])
 def test_prefill_two_cut_sequences_h32_sampled_heads(records):
     """Two sequences cut into at least three segments each at H = 32 and
