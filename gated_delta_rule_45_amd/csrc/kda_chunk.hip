@@ -1232,8 +1232,9 @@ __device__ __forceinline__ void intra_exact(const PrefillParams& p, FusedSmem<K,
       // Diagonal block whose range exceeds kMaxBlockDecay, by 4-row
       // sub-blocks. Between sub-blocks on bf16 MFMA: pass a = 1..3 takes
       // reference row r = 16 I + 4 a, so rows t >= r carry e^{gam_t - gam_r}
-      // and columns s < r carry e^{gam_r - gam_s}, both <= 1; the other rows
-      // and columns of the pass are clamped to finite values and dropped.
+      // and columns s < r carry e^{gam_r - gam_s}, both <= 1; the pass's
+      // other rows and columns keep the unscaled (finite) keys and are
+      // dropped.
       // Lane group g keeps the rows 4 g .. 4 g + 3 of pass g. Within a
       // sub-block pairwise in fp32: lane (sb, tt, ss) = (l / 16, l / 4 % 4,
       // l % 4) forms entry (4 sb + tt, 4 sb + ss) over every channel.
